@@ -1,0 +1,219 @@
+/*
+ * mt.h — C ABI of libmt, the MI355X (gfx950) layer-streamed training step.
+ *
+ * What it computes: one full-batch training step of a pre-norm GQA decoder
+ * whose fp32 parameters and Adam states live in host memory, with the GPU
+ * used as a transient compute engine that receives each layer's weights,
+ * computes, and sends the layer's gradient back (MegaTrain listing page,
+ * Abstract; blog summary, sections 1 and 2).  Weights are bound into a
+ * stateless layer template at call time instead of living in a persistent
+ * autograd graph (Abstract; blog summary, section 4).  Activations are
+ * recomputed from checkpoints kept every K layers (blog summary, section 3).
+ * The optimizer step runs on the CPU (blog summary, section 1).
+ *
+ * Conventions for every call:
+ *  - Every call returns mt_status; no C++ exception crosses the ABI.  On a
+ *    non-OK return mt_last_error() gives a message (thread-local, valid
+ *    until the next failing call on the same thread).
+ *  - Arguments are validated before any GPU work is enqueued: a failed
+ *    validation enqueues nothing and leaves every buffer and model state as
+ *    it was.
+ *  - Device pointers are plain HIP device addresses (e.g. a torch tensor's
+ *    data_ptr()); streams are hipStream_t values passed as void*.  The
+ *    caller owns every pointer it passes and keeps it alive until the work
+ *    enqueued on the given stream(s) has finished.
+ *  - Activations are token-major row-major: a [D, C] matrix has D = B*T rows
+ *    (batch-major, then position) and C contiguous columns.  Weights are
+ *    [out, in] row-major, so a linear layer is y = x W^T.
+ *  - dtype: bf16 storage (round to nearest even) with fp32 accumulation,
+ *    unless a run config selects MT_PREC_FP32_DEBUG, in which case every
+ *    buffer the calls below describe as bf16 holds fp32 instead.
+ *  - A model handle is not thread-safe; distinct handles are independent.
+ */
+#ifndef MT_H
+#define MT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MT_OK = 0,
+  MT_E_INVALID = -1,    /* null pointer, bad enum or knob value */
+  MT_E_SHAPE = -2,      /* shape not supported or inconsistent */
+  MT_E_OOM_DEVICE = -3, /* caller buffer too small */
+  MT_E_OOM_HOST = -4,   /* host (pinned or pageable) allocation failed */
+  MT_E_HIP = -5,        /* a HIP runtime call failed */
+  MT_E_NONFINITE = -6,  /* loss or gradient not finite (nothing updated) */
+  MT_E_STATE = -7       /* model unusable after an earlier failure */
+} mt_status;
+
+enum { MT_DT_BF16 = 0, MT_DT_F32 = 1 };
+enum { MT_PREC_BF16 = 0, MT_PREC_FP32_DEBUG = 1 };
+enum { MT_HOST_PINNED = 0, MT_HOST_PAGEABLE = 1 };
+
+/* Decoder shape (Qwen2.5 shape, MegaTrain listing page, Table 2).
+ * Constraints: head_dim in {64, 128}; n_heads % n_kv_heads == 0;
+ * hidden, ffn, vocab multiples of 64. */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps;
+  double rope_theta;
+} mt_model_cfg;
+
+/* Knobs of one run.  The ablation of the listing page (Table 4) varies the
+ * checkpoint interval, double buffering (prefetch_depth 1 vs 2) and the
+ * gradient slab pool; chunked MLP execution is Table 7's note on the
+ * longest contexts.  Zero means "default" where a default is stated. */
+typedef struct {
+  int32_t ckpt_interval;     /* K >= 1 (default 4) */
+  int32_t prefetch_depth;    /* weight slots ahead of compute: 1, 2 or 3 (default 2) */
+  int32_t use_slab_pool;     /* 1: recycle pinned gradient slabs (default); 0: one slab per unit */
+  int32_t n_slabs;           /* pool size when use_slab_pool (default 4) */
+  int32_t mlp_chunk_tokens;  /* 0: whole token set; else MLP runs over chunks of this many tokens */
+  int32_t head_chunk_tokens; /* tokens per LM-head chunk (default 16384) */
+  int32_t precision;         /* MT_PREC_BF16 | MT_PREC_FP32_DEBUG */
+  int32_t host_threads;      /* CPU threads for Adam and embedding work (default 16) */
+  int32_t check_finite;      /* 1: refuse to update on a non-finite loss/gradient */
+  int32_t serialize;         /* 1: run W, C and G work on one stream (for invariance tests) */
+  int32_t host_alloc;        /* MT_HOST_PINNED (default) | MT_HOST_PAGEABLE (no GPU needed) */
+  int32_t keep_grads;        /* 1: keep each step's gradients on the host for mt_model_get_param */
+  int32_t time_kernels;      /* 1: bracket the dominant GEMM with HIP events (stats) */
+  float lr, beta1, beta2, eps, weight_decay; /* Adam (weight_decay must be 0) */
+} mt_run_cfg;
+
+/* Device pointers of one layer's weights: the stateless template's binding.
+ * Layouts (bf16): attn_norm [H]; w_qkv [Q+2Kv, H] = rows of W_q, then W_k,
+ * then W_v; w_o [H, Q]; mlp_norm [H]; w_gate_up [2F, H] = rows of W_gate
+ * then W_up; w_down [H, F].  Q = n_heads*head_dim, Kv = n_kv_heads*head_dim. */
+typedef struct {
+  const void *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate_up, *w_down;
+} mt_layer_view;
+
+/* Device pointers receiving one layer's gradients, same layouts as above. */
+typedef struct {
+  void *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate_up, *w_down;
+} mt_layer_grad_view;
+
+typedef struct {
+  double step_ms;           /* wall time of mt_stream_step */
+  double fwd_ms, head_ms, bwd_ms; /* compute-stream phase times (HIP events) */
+  double adam_ms;           /* summed host Adam time */
+  double tail_ms;           /* from the end of GPU work to return */
+  double h2d_bytes, d2h_bytes;
+  double h2d_ms, d2h_ms;    /* summed copy durations on the W and G streams */
+  double exposed_wait_fwd_ms, exposed_wait_bwd_ms; /* compute idle while waiting on weights */
+  double probe_kernel_ms;   /* summed duration of the timed GEMM launches */
+  double probe_kernel_flops;/* algorithmic FLOPs of those launches */
+  int64_t probe_kernel_launches;
+  int64_t pinned_host_bytes, pageable_host_bytes, device_arena_bytes;
+  int64_t units_updated;    /* units whose Adam update completed this step */
+} mt_step_stats;
+
+typedef struct mt_model mt_model;
+
+/* Thread-local text of the last non-OK status returned on this thread. */
+const char* mt_last_error(void);
+
+/* ---------------------------------------------------------------------
+ * Stateless layer template (blog summary, section 4: weights bound at call
+ * time, nothing kept between calls).  Enqueue-only on `stream`: never
+ * allocates, never synchronizes.  The caller provides a device workspace of
+ * at least mt_layer_workspace_bytes(...) bytes (256-B aligned).
+ * ------------------------------------------------------------------- */
+
+/* which: 0 = forward, 1 = recompute + backward. */
+size_t mt_layer_workspace_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                                int32_t batch, int32_t seq, int32_t which);
+
+/* Forward of one decoder layer: x_out = x_in + attn(...) + mlp(...).
+ * x_in, x_out: device bf16 [batch*seq, hidden]; x_out may not alias x_in. */
+mt_status mt_layer_fwd(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                       const mt_layer_view* w, const void* x_in, void* x_out,
+                       int32_t batch, int32_t seq, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Recompute the layer's internals from its input x_in (blog summary,
+ * section 3), then backward: given dy = dL/dx_out, write dx = dL/dx_in and
+ * every weight gradient into dw (bf16, overwritten, not accumulated).
+ * x_in, dy, dx: device bf16 [batch*seq, hidden]; dx may alias dy. */
+mt_status mt_layer_recompute_bwd(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                                 const mt_layer_view* w, const void* x_in,
+                                 const void* dy, void* dx,
+                                 const mt_layer_grad_view* dw, int32_t batch,
+                                 int32_t seq, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Host-resident model: the authoritative flat store (blog summary,
+ * "Performance and Capabilities": flat tensor layout, authoritative host
+ * storage).  One region per unit (each layer, the head = final norm + LM
+ * head, the embedding); fp32 master, m and v share one layout, and a bf16
+ * copy of the master (pinned) is what streams to the GPU.
+ * ------------------------------------------------------------------- */
+
+mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                          mt_model** out);
+void mt_model_destroy(mt_model* model);
+
+/* Parameter names: "embed", "layers.<l>.{attn_norm,w_q,w_k,w_v,w_o,
+ * mlp_norm,w_gate,w_up,w_down}", "final_norm", "lm_head"; shapes [out, in].
+ * set: copies n fp32 values into the master, writes the bf16 copy (RNE) and
+ * zeroes m and v.  n must equal the tensor's element count. */
+mt_status mt_model_set_param(mt_model* model, const char* name,
+                             const float* src, size_t n);
+
+enum { MT_GET_MASTER = 0, MT_GET_M = 1, MT_GET_V = 2, MT_GET_GRAD = 3,
+       MT_GET_SHADOW = 4 };
+/* get: copies a tensor out as fp32.  MT_GET_GRAD needs keep_grads = 1 and
+ * returns the last step's gradient as the optimizer saw it. */
+mt_status mt_model_get_param(const mt_model* model, const char* name,
+                             int32_t which, float* dst, size_t n);
+
+/* Adam step counter of the model (number of completed steps). */
+int64_t mt_model_step_count(const mt_model* model);
+
+/* Device arena the streamed step needs for batch x seq tokens. */
+size_t mt_stream_arena_bytes(const mt_model* model, int32_t batch, int32_t seq);
+
+/* One training step (blog summary, sections 1-4; listing page, Fig. 3):
+ * stream each layer's bf16 weights in on streams[0] (W), run forward,
+ * head, segment re-forward, recompute and backward on streams[1] (C), and
+ * offload each unit's bf16 gradient on streams[2] (G) into a pinned slab,
+ * where a CPU Adam step updates that unit while the GPU continues.
+ * tokens: host int32 [batch, seq], ids in [0, vocab).  arena: device, at
+ * least mt_stream_arena_bytes bytes.  Blocks until every unit is updated;
+ * writes the mean next-token loss to *loss_out and, if stats_out is not
+ * null, timings and byte counts.  With check_finite, a non-finite loss
+ * returns MT_E_NONFINITE before any update. */
+mt_status mt_stream_step(mt_model* model, const int32_t* tokens, int32_t batch,
+                         int32_t seq, void* arena, size_t arena_bytes,
+                         void* const streams[3], float* loss_out,
+                         mt_step_stats* stats_out);
+
+/* ---------------------------------------------------------------------
+ * CPU optimizer (blog summary, section 1: the optimizer step runs entirely
+ * on the CPU).  Synchronous, in place, on host memory the caller owns.
+ * Adam with bias correction: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+ * p -= lr * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps).  grad is bf16 or fp32
+ * per grad_dtype; bf16_shadow (nullable) receives RNE(bf16) of the new p.
+ * With hp->check_finite, a non-finite gradient returns MT_E_NONFINITE and
+ * leaves every array unchanged.  step >= 1.
+ * ------------------------------------------------------------------- */
+mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq,
+                       const void* grad, int32_t grad_dtype,
+                       uint16_t* bf16_shadow, size_t n, int64_t step,
+                       const mt_run_cfg* hp);
+
+/* Defaults for every knob (ckpt 4, depth 2, pool of 4, lr 1e-4, betas
+ * 0.9/0.999, eps 1e-8, bf16, 16 host threads, pinned host memory). */
+void mt_run_cfg_default(mt_run_cfg* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MT_H */

@@ -1,0 +1,371 @@
+// Row-wise and elementwise kernels of the decoder layer (gfx950):
+// RMSNorm forward/backward with deterministic gain-gradient partials, RoPE
+// tables and rotation, the LM-head cross-entropy rows, casts and fills.
+// All are HBM-bound; one wave64 owns one row so every reduction is a
+// register loop plus one wave butterfly, with 16-byte vector accesses.
+#include "common.h"
+#include "kernels.h"
+
+namespace mt {
+
+namespace {
+
+constexpr int RN_WAVES = 4;  // rows per workgroup in the forward
+
+__device__ __forceinline__ void unpack8(u32x4_t v, float* f) {
+  f[0] = lo_bf(v.x); f[1] = hi_bf(v.x); f[2] = lo_bf(v.y); f[3] = hi_bf(v.y);
+  f[4] = lo_bf(v.z); f[5] = hi_bf(v.z); f[6] = lo_bf(v.w); f[7] = hi_bf(v.w);
+}
+__device__ __forceinline__ u32x4_t pack8(const float* f) {
+  u32x4_t v;
+  v.x = pack_bf(f[0], f[1]); v.y = pack_bf(f[2], f[3]);
+  v.z = pack_bf(f[4], f[5]); v.w = pack_bf(f[6], f[7]);
+  return v;
+}
+
+// y = x * rsqrt(mean(x^2) + eps) * g.  One wave per row; cols % 8 == 0.
+__global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_fwd_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, uint16_t* __restrict__ y,
+    float* __restrict__ rstd_out, int rows, int cols, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * RN_WAVES + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* xr = x + (long)row * cols;
+  const int nch = cols / 8;
+  float ss = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    float f[8];
+    unpack8(*reinterpret_cast<const u32x4_t*>(xr + c * 8), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+  }
+  ss = wave_sum(ss);
+  const float r = 1.f / sqrtf(ss / (float)cols + eps);
+  if (lane == 0 && rstd_out) rstd_out[row] = r;
+  uint16_t* yr = y + (long)row * cols;
+  for (int c = lane; c < nch; c += 64) {
+    float f[8], gg[8];
+    unpack8(*reinterpret_cast<const u32x4_t*>(xr + c * 8), f);
+    unpack8(*reinterpret_cast<const u32x4_t*>(g + c * 8), gg);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] * r * gg[i];
+    *reinterpret_cast<u32x4_t*>(yr + c * 8) = pack8(f);
+  }
+}
+
+// Backward.  Each workgroup (4 waves) owns RB_ROWS consecutive rows; every
+// wave walks its rows and keeps per-column dg sums for its chunk columns in
+// registers; the 4 waves are combined in LDS in fixed order and written as
+// one partial row of dg_part.  MAXC = max chunk iterations per lane.
+constexpr int RB_ROWS = 64;
+
+template <int MAXC>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ g, const float* __restrict__ rstd,
+    const uint16_t* __restrict__ resid, uint16_t* __restrict__ dx, float* __restrict__ dg_part,
+    int rows, int cols) {
+  extern __shared__ float red[];  // [4][cols]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = cols / 8;
+  float acc[MAXC][8];
+#pragma unroll
+  for (int k = 0; k < MAXC; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[k][i] = 0.f;
+  const int r0 = blockIdx.x * RB_ROWS;
+  const float inv_cols = 1.f / (float)cols;
+  for (int rr = wave; rr < RB_ROWS; rr += 4) {
+    const int row = r0 + rr;
+    if (row >= rows) break;
+    const long off = (long)row * cols;
+    const float r = rstd[row];
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      const int c = lane + 64 * k;
+      if (c < nch) {
+        float fd[8], fx[8], fg[8];
+        unpack8(*reinterpret_cast<const u32x4_t*>(dy + off + c * 8), fd);
+        unpack8(*reinterpret_cast<const u32x4_t*>(x + off + c * 8), fx);
+        unpack8(*reinterpret_cast<const u32x4_t*>(g + c * 8), fg);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xh = fx[i] * r;
+          dot += fd[i] * fg[i] * xh;
+          acc[k][i] += fd[i] * xh;
+        }
+      }
+    }
+    dot = wave_sum(dot) * inv_cols;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      const int c = lane + 64 * k;
+      if (c < nch) {
+        float fd[8], fx[8], fg[8], fr[8];
+        unpack8(*reinterpret_cast<const u32x4_t*>(dy + off + c * 8), fd);
+        unpack8(*reinterpret_cast<const u32x4_t*>(x + off + c * 8), fx);
+        unpack8(*reinterpret_cast<const u32x4_t*>(g + c * 8), fg);
+        if (resid) unpack8(*reinterpret_cast<const u32x4_t*>(resid + off + c * 8), fr);
+        else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) fr[i] = 0.f;
+        }
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xh = fx[i] * r;
+          o[i] = fr[i] + r * (fd[i] * fg[i] - xh * dot);
+        }
+        *reinterpret_cast<u32x4_t*>(dx + off + c * 8) = pack8(o);
+      }
+    }
+  }
+  // combine the four waves' column sums in fixed order
+#pragma unroll
+  for (int k = 0; k < MAXC; ++k) {
+    const int c = lane + 64 * k;
+    if (c < nch)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wave * cols + c * 8 + i] = acc[k][i];
+  }
+  __syncthreads();
+  for (int col = threadIdx.x; col < cols; col += 256) {
+    const float s = ((red[col] + red[cols + col]) + red[2 * cols + col]) + red[3 * cols + col];
+    dg_part[(long)blockIdx.x * cols + col] = s;
+  }
+}
+
+__global__ void reduce_rows_kernel(const float* __restrict__ part, int nblk, int cols,
+                                   uint16_t* __restrict__ out) {
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  if (col >= cols) return;
+  float s = 0.f;
+  for (int b = 0; b < nblk; ++b) s += part[(long)b * cols + col];
+  out[col] = f2bf(s);
+}
+
+__global__ void rope_table_kernel(float* cos_t, float* sin_t, int seq, int half, int head_dim,
+                                  double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= seq * half) return;
+  const int t = idx / half, j = idx % half;
+  const double inv = pow(theta, -2.0 * (double)j / (double)head_dim);
+  const double ang = (double)t * inv;
+  cos_t[idx] = (float)cos(ang);
+  sin_t[idx] = (float)sin(ang);
+}
+
+// One thread per (token, head, pair j): rotates (x_j, x_{j+d/2}).
+__global__ void rope_kernel(uint16_t* __restrict__ qkv, long ldq, int tokens, int seq, int nh,
+                            int half, const float* __restrict__ cos_t,
+                            const float* __restrict__ sin_t, float sgn) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)tokens * nh * half;
+  if (idx >= total) return;
+  const int j = (int)(idx % half);
+  const long th = idx / half;
+  const int h = (int)(th % nh);
+  const int tok = (int)(th / nh);
+  const int t = tok % seq;
+  uint16_t* p = qkv + (long)tok * ldq + (long)h * 2 * half;
+  const float c = cos_t[t * half + j], sn = sgn * sin_t[t * half + j];
+  const float x1 = bf2f(p[j]), x2 = bf2f(p[j + half]);
+  p[j] = f2bf(x1 * c - x2 * sn);
+  p[j + half] = f2bf(x2 * c + x1 * sn);
+}
+
+// Cross-entropy over one row of fp32 logits per workgroup (256 threads):
+// pass 1 online max/sum, pass 2 writes (softmax - onehot) * inv_n as bf16.
+__global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ logits,
+                                                      const int32_t* __restrict__ target,
+                                                      uint16_t* __restrict__ dlogits,
+                                                      float* __restrict__ loss_part, int vocab,
+                                                      float inv_n) {
+  __shared__ float sm[2][4];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* lr = logits + (long)row * vocab;
+  uint16_t* dr = dlogits + (long)row * vocab;
+  const int tgt = target[row];
+  if (tgt < 0 || tgt >= vocab) {
+    for (int c = tid * 4; c < vocab; c += 1024)
+      *reinterpret_cast<u32x2_t*>(dr + c) = u32x2_t{0, 0};
+    if (tid == 0) loss_part[row] = 0.f;
+    return;
+  }
+  float m = -INFINITY, s = 0.f;
+  for (int c = tid * 4; c < vocab; c += 1024) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lr + c);
+    const float mv = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    const float nm = fmaxf(m, mv);
+    s = s * __expf(m - nm) + __expf(v.x - nm) + __expf(v.y - nm) + __expf(v.z - nm) +
+        __expf(v.w - nm);
+    m = nm;
+  }
+  // combine (m, s) across the wave, then across waves
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float om = __shfl_xor(m, o, 64), os = __shfl_xor(s, o, 64);
+    const float nm = fmaxf(m, om);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - nm)) + (om == -INFINITY ? 0.f : os * __expf(om - nm));
+    m = nm;
+  }
+  if (lane == 0) { sm[0][wave] = m; sm[1][wave] = s; }
+  __syncthreads();
+  float M = fmaxf(fmaxf(sm[0][0], sm[0][1]), fmaxf(sm[0][2], sm[0][3]));
+  float S = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) S += sm[1][w] * __expf(sm[0][w] - M);
+  const float inv_s = 1.f / S;
+  for (int c = tid * 4; c < vocab; c += 1024) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lr + c);
+    float p[4] = {__expf(v.x - M) * inv_s, __expf(v.y - M) * inv_s, __expf(v.z - M) * inv_s,
+                  __expf(v.w - M) * inv_s};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c + i == tgt) p[i] -= 1.f;
+    u32x2_t o;
+    o.x = pack_bf(p[0] * inv_n, p[1] * inv_n);
+    o.y = pack_bf(p[2] * inv_n, p[3] * inv_n);
+    *reinterpret_cast<u32x2_t*>(dr + c) = o;
+  }
+  if (tid == 0) loss_part[row] = (M + logf(S)) - lr[tgt];
+}
+
+// Fixed-order sum of n values by one workgroup: each thread sums a strided
+// slice in index order, then a fixed tree over the 256 partials.
+__global__ __launch_bounds__(256) void sum_kernel(const float* __restrict__ part, int n,
+                                                  float scale, float* __restrict__ out) {
+  __shared__ float sh[256];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) s += part[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = sh[0] * scale;
+}
+
+__global__ void cast_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = f2bf(in[i]);
+}
+
+__global__ void fill_kernel(float* __restrict__ p, float v, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void copy_rows_kernel(const uint16_t* __restrict__ src, long lds,
+                                 uint16_t* __restrict__ dst, long ldd, int rows, int cols8) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)rows * cols8) return;
+  const int r = (int)(idx / cols8), c = (int)(idx % cols8);
+  *reinterpret_cast<u32x4_t*>(dst + r * ldd + c * 8) =
+      *reinterpret_cast<const u32x4_t*>(src + r * lds + c * 8);
+}
+
+}  // namespace
+
+hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int rows,
+                       int cols, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((rows + RN_WAVES - 1) / RN_WAVES),
+                     dim3(RN_WAVES * 64), 0, s, x, g, y, rstd, rows, cols, eps);
+  return hipGetLastError();
+}
+
+int rmsnorm_bwd_blocks(int rows) { return (rows + RB_ROWS - 1) / RB_ROWS; }
+
+hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
+                       const float* rstd, const uint16_t* resid, uint16_t* dx, float* dg_part,
+                       int rows, int cols, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int nch = cols / 8;
+  const int iters = (nch + 63) / 64;
+  const dim3 grid(rmsnorm_bwd_blocks(rows)), block(256);
+  const size_t lds = 4 * (size_t)cols * sizeof(float);
+#define MT_RB(C)                                                                           \
+  if (iters <= C) {                                                                        \
+    static bool attr = false;                                                              \
+    if (!attr) {                                                                           \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rmsnorm_bwd_kernel<C>), \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,       \
+                                         4 * 8192 * (int)sizeof(float));                   \
+      if (e != hipSuccess) return e;                                                       \
+      attr = true;                                                                         \
+    }                                                                                      \
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<C>, grid, block, lds, s, dy, x, g, rstd, resid, dx, \
+                       dg_part, rows, cols);                                               \
+    return hipGetLastError();                                                              \
+  }
+  MT_RB(1) MT_RB(2) MT_RB(4) MT_RB(8) MT_RB(16)
+#undef MT_RB
+  return hipErrorInvalidValue;
+}
+
+hipError_t reduce_rows_to_bf16(const float* part, int nblk, int cols, uint16_t* out,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, part, nblk,
+                     cols, out);
+  return hipGetLastError();
+}
+
+hipError_t rope_table(float* cos_t, float* sin_t, int seq, int head_dim, double theta,
+                      hipStream_t s) {
+  const int half = head_dim / 2, n = seq * half;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cos_t, sin_t, seq,
+                     half, head_dim, theta);
+  return hipGetLastError();
+}
+
+hipError_t rope_apply(uint16_t* qkv, long ldq, int batch, int seq, int n_heads, int n_kv_heads,
+                      int head_dim, const float* cos_t, const float* sin_t, int inverse,
+                      hipStream_t s) {
+  const int tokens = batch * seq, nh = n_heads + n_kv_heads, half = head_dim / 2;
+  const long total = (long)tokens * nh * half;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, qkv,
+                     ldq, tokens, seq, nh, half, cos_t, sin_t, inverse ? -1.f : 1.f);
+  return hipGetLastError();
+}
+
+hipError_t ce_rows(const float* logits, const int32_t* target, uint16_t* dlogits,
+                   float* loss_part, int rows, int vocab, float inv_n, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_rows_kernel, dim3(rows), dim3(256), 0, s, logits, target, dlogits,
+                     loss_part, vocab, inv_n);
+  return hipGetLastError();
+}
+
+hipError_t sum_loss(const float* part, int n, float inv_n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(256), 0, s, part, n, inv_n, out);
+  return hipGetLastError();
+}
+
+hipError_t cast_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t fill_f32(float* p, float v, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t copy_rows_bf16(const uint16_t* src, long lds, uint16_t* dst, long ldd, int rows,
+                          int cols, hipStream_t s) {
+  const long total = (long)rows * (cols / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, src,
+                     lds, dst, ldd, rows, cols / 8);
+  return hipGetLastError();
+}
+
+}  // namespace mt

@@ -1,0 +1,96 @@
+// Internal launch API of libmt's HIP kernels (host side).  Every launcher
+// enqueues on the given stream and returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mt {
+
+// ---------------------------------------------------------------- GEMM
+// C[M, N] = op(A) * op(B) with fp32 accumulation on bf16 MFMA.
+//  NT: A [M, K] (row stride lda), B [N, K] (ldb)      C = A B^T
+//  NN: A [M, K],                  B [K, N]            C = A B
+//  TN: A [K, M],                  B [K, N]            C = A^T B
+enum GemmLayout { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
+
+enum GemmEpi {
+  EPI_BF16 = 0,        // C (bf16) = acc
+  EPI_F32 = 1,         // C (fp32) = acc
+  EPI_ACC_F32 = 2,     // C (fp32) += acc
+  EPI_RESID_BF16 = 3,  // C (bf16) = R (bf16) + acc
+  EPI_SWIGLU = 4,      // NT only; B = [W_gate; W_up] (2F rows); N = 2F:
+                       //   C (bf16) [M, F] = silu(gate) * up
+  EPI_SWIGLU_SAVE = 5, // as EPI_SWIGLU, and C2 (bf16) [M, 2F] = [gate | up]
+  EPI_SWIGLU_BWD = 6   // acc = dm [M, F]; G = [gate | up] (bf16, ldg);
+                       //   C2 (bf16) [M, 2F] = [dgate | dup]
+};
+
+struct GemmArgs {
+  int layout = GEMM_NT, epi = EPI_BF16;
+  int M = 0, N = 0, K = 0;
+  const uint16_t* A = nullptr; long lda = 0;
+  const uint16_t* B = nullptr; long ldb = 0;
+  void* C = nullptr; long ldc = 0;
+  const uint16_t* R = nullptr; long ldr = 0;
+  uint16_t* C2 = nullptr; long ldc2 = 0;
+  const uint16_t* G = nullptr; long ldg = 0;
+  int F = 0;  // FFN width for the SwiGLU epilogues
+};
+
+// Returns a message for unsupported arguments, or nullptr if OK.
+const char* gemm_check(const GemmArgs& a);
+hipError_t gemm_launch(const GemmArgs& a, hipStream_t s);
+const char* gemm_kernel_name(const GemmArgs& a);
+
+// ------------------------------------------------------------ elementwise
+// RMSNorm over rows of x [rows, cols] (bf16): y = x * rstd * g (bf16),
+// rstd [rows] fp32 (may be null).
+hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd,
+                       int rows, int cols, float eps, hipStream_t s);
+// dx = resid + rstd*(e - xh*mean(e*xh)), e = dy*g, xh = x*rstd  (bf16 out;
+// resid may be null).  Writes per-block partial gain gradients
+// dg_part [nblk, cols] fp32; nblk = rmsnorm_bwd_blocks(rows).
+int rmsnorm_bwd_blocks(int rows);
+hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
+                       const float* rstd, const uint16_t* resid, uint16_t* dx,
+                       float* dg_part, int rows, int cols, hipStream_t s);
+// out[c] = bf16(sum_b part[b, c]) in fixed block order.
+hipError_t reduce_rows_to_bf16(const float* part, int nblk, int cols, uint16_t* out,
+                               hipStream_t s);
+
+// cos/sin tables [seq, head_dim/2] fp32, angle = t * theta^(-2j/d) in fp64.
+hipError_t rope_table(float* cos_t, float* sin_t, int seq, int head_dim, double theta,
+                      hipStream_t s);
+// Rotate the q and k column blocks of qkv [B*T, ldq] in place (inverse=1
+// rotates by the negative angle: the backward).
+hipError_t rope_apply(uint16_t* qkv, long ldq, int batch, int seq, int n_heads,
+                      int n_kv_heads, int head_dim, const float* cos_t, const float* sin_t,
+                      int inverse, hipStream_t s);
+
+hipError_t cast_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
+hipError_t fill_f32(float* p, float v, size_t n, hipStream_t s);
+hipError_t copy_rows_bf16(const uint16_t* src, long lds, uint16_t* dst, long ldd, int rows,
+                          int cols, hipStream_t s);
+
+// ------------------------------------------------------------- attention
+// Causal GQA attention over q/k/v held in qkv [B*T, (Hq+2Hkv)*d] (bf16).
+// o [B*T, Hq*d] bf16; lse [B, Hq, T] fp32.
+hipError_t attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int seq,
+                    int n_heads, int n_kv_heads, int head_dim, hipStream_t s);
+// Backward: delta [B, Hq, T] fp32 workspace; dqkv [B*T, (Hq+2Hkv)*d] bf16 out.
+hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                    const uint16_t* dout, float* delta, uint16_t* dqkv, int batch, int seq,
+                    int n_heads, int n_kv_heads, int head_dim, hipStream_t s);
+
+// ------------------------------------------------------------------ head
+// Row-wise softmax cross-entropy on fp32 logits [rows, V] for next-token
+// targets: target[r] < 0 means no target (zero gradient, no loss).
+// dlogits (bf16) = (softmax - onehot) * inv_n; loss_part[r] = lse - picked.
+hipError_t ce_rows(const float* logits, const int32_t* target, uint16_t* dlogits,
+                   float* loss_part, int rows, int vocab, float inv_n, hipStream_t s);
+// loss = sum(loss_part[0..n)) * inv_n in fixed order -> out[0] (fp32).
+hipError_t sum_loss(const float* part, int n, float inv_n, float* out, hipStream_t s);
+
+}  // namespace mt

@@ -1,0 +1,214 @@
+"""ctypes binding of libmt (include/mt.h, include/mt_ops.h).
+
+Argument marshalling only: every step of the training path runs inside
+libmt.  Device buffers are passed as torch tensors (their data_ptr()),
+streams as torch.cuda.Stream (their hipStream_t handle).  A missing or
+unloadable library raises at import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmt.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libmt.so not found at {LIB_PATH}; build it with "
+        "`python -m layer_streamed_amd.build` (hipcc for gfx950)")
+_lib = C.CDLL(LIB_PATH)
+
+# ----------------------------------------------------------------- constants
+MT_OK, MT_E_INVALID, MT_E_SHAPE, MT_E_OOM_DEVICE, MT_E_OOM_HOST = 0, -1, -2, -3, -4
+MT_E_HIP, MT_E_NONFINITE, MT_E_STATE = -5, -6, -7
+DT_BF16, DT_F32 = 0, 1
+PREC_BF16, PREC_FP32_DEBUG = 0, 1
+HOST_PINNED, HOST_PAGEABLE = 0, 1
+GET_MASTER, GET_M, GET_V, GET_GRAD, GET_SHADOW = 0, 1, 2, 3, 4
+GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
+EPI_BF16, EPI_F32, EPI_ACC_F32, EPI_RESID_BF16 = 0, 1, 2, 3
+EPI_SWIGLU, EPI_SWIGLU_SAVE, EPI_SWIGLU_BWD = 4, 5, 6
+
+_STATUS = {0: "MT_OK", -1: "MT_E_INVALID", -2: "MT_E_SHAPE", -3: "MT_E_OOM_DEVICE",
+           -4: "MT_E_OOM_HOST", -5: "MT_E_HIP", -6: "MT_E_NONFINITE", -7: "MT_E_STATE"}
+
+
+class MTError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+# ------------------------------------------------------------------- structs
+class ModelCfg(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_double)]
+
+
+class RunCfg(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "ckpt_interval", "prefetch_depth", "use_slab_pool", "n_slabs", "mlp_chunk_tokens",
+        "head_chunk_tokens", "precision", "host_threads", "check_finite", "serialize",
+        "host_alloc", "keep_grads", "time_kernels")] + [
+        (n, C.c_float) for n in ("lr", "beta1", "beta2", "eps", "weight_decay")]
+
+
+class LayerView(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in
+                ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")]
+
+
+class StepStats(C.Structure):
+    _fields_ = [(n, C.c_double) for n in (
+        "step_ms", "fwd_ms", "head_ms", "bwd_ms", "adam_ms", "tail_ms", "h2d_bytes",
+        "d2h_bytes", "h2d_ms", "d2h_ms", "exposed_wait_fwd_ms", "exposed_wait_bwd_ms",
+        "probe_kernel_ms", "probe_kernel_flops")] + [(n, C.c_int64) for n in (
+            "probe_kernel_launches", "pinned_host_bytes", "pageable_host_bytes",
+            "device_arena_bytes", "units_updated")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+# ---------------------------------------------------------------- signatures
+_P, _I32, _I64, _SZ, _F, _D = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float, C.c_double
+
+
+def _fn(name, res, *args):
+    f = getattr(_lib, name, None)
+    if f is None:
+        return None
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_lib.mt_last_error.restype = C.c_char_p
+_lib.mt_last_error.argtypes = []
+
+_SIGS = {
+    "mt_op_gemm": (_I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                   _P, _I64, _P, _I64, _I32, _P),
+    "mt_op_rmsnorm_fwd": (_I32, _P, _P, _P, _P, _I32, _I32, _F, _P),
+    "mt_op_rmsnorm_bwd": (_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
+    "mt_op_rope_table": (_I32, _P, _P, _I32, _I32, _D, _P),
+    "mt_op_rope": (_I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _P),
+    "mt_op_attn_fwd": (_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
+    "mt_op_attn_bwd": (_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
+    "mt_op_ce_rows": (_I32, _P, _P, _P, _P, _I32, _I32, _F, _P),
+    "mt_layer_workspace_bytes": (_SZ, _P, _P, _I32, _I32, _I32),
+    "mt_layer_fwd": (_I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
+    "mt_layer_recompute_bwd": (_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
+    "mt_model_create": (_I32, _P, _P, _P),
+    "mt_model_destroy": (None, _P),
+    "mt_model_set_param": (_I32, _P, C.c_char_p, _P, _SZ),
+    "mt_model_get_param": (_I32, _P, C.c_char_p, _I32, _P, _SZ),
+    "mt_model_step_count": (_I64, _P),
+    "mt_stream_arena_bytes": (_SZ, _P, _I32, _I32),
+    "mt_stream_step": (_I32, _P, _P, _I32, _I32, _P, _SZ, _P, _P, _P),
+    "mt_host_adam": (_I32, _P, _P, _P, _P, _I32, _P, _SZ, _I64, _P),
+    "mt_run_cfg_default": (None, _P),
+    "mt_op_rmsnorm_bwd_workspace": (_SZ, _I32, _I32),
+}
+FN = {}
+for _name, (_res, *_args) in _SIGS.items():
+    FN[_name] = _fn(_name, _res, *_args)
+
+EXPORTED = sorted(n for n, f in FN.items() if f is not None) + ["mt_last_error"]
+
+
+def last_error() -> str:
+    return (_lib.mt_last_error() or b"").decode()
+
+
+def check(status: int, what: str = ""):
+    if status != MT_OK:
+        raise MTError(status, f"{what}: {last_error()}")
+
+
+def call(name, *args):
+    f = FN.get(name)
+    if f is None:
+        raise MTError(MT_E_INVALID, f"{name} is not exported by {LIB_PATH}")
+    return f(*args)
+
+
+# ------------------------------------------------------------------- helpers
+def ptr(t):
+    """Device or host address of a torch tensor / numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data  # numpy
+
+
+def stream_handle(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def run_cfg(**kw) -> RunCfg:
+    r = RunCfg()
+    call("mt_run_cfg_default", C.byref(r))
+    for k, v in kw.items():
+        if not hasattr(r, k):
+            raise AttributeError(k)
+        setattr(r, k, v)
+    return r
+
+
+def model_cfg(shape) -> ModelCfg:
+    return ModelCfg(shape.n_layers, shape.hidden, shape.n_heads, shape.n_kv_heads,
+                    shape.head_dim, shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta)
+
+
+# ----------------------------------------------------------------- op calls
+def gemm(layout, epi, M, N, K, A, lda, B, ldb, Cm, ldc, R=None, ldr=0, C2=None, ldc2=0,
+         G=None, ldg=0, F=0, stream=None):
+    check(call("mt_op_gemm", layout, epi, M, N, K, ptr(A), lda, ptr(B), ldb, ptr(Cm), ldc,
+               ptr(R), ldr, ptr(C2), ldc2, ptr(G), ldg, F, stream_handle(stream)), "mt_op_gemm")
+
+
+def rmsnorm_fwd(x, g, y, rstd, rows, cols, eps, stream=None):
+    check(call("mt_op_rmsnorm_fwd", ptr(x), ptr(g), ptr(y), ptr(rstd), rows, cols, eps,
+               stream_handle(stream)), "mt_op_rmsnorm_fwd")
+
+
+def rmsnorm_bwd(dy, x, g, rstd, resid, dx, dg, rows, cols, ws, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    check(call("mt_op_rmsnorm_bwd", ptr(dy), ptr(x), ptr(g), ptr(rstd), ptr(resid), ptr(dx),
+               ptr(dg), rows, cols, ptr(ws), nbytes, stream_handle(stream)), "mt_op_rmsnorm_bwd")
+
+
+def rmsnorm_bwd_workspace(rows, cols) -> int:
+    return call("mt_op_rmsnorm_bwd_workspace", rows, cols)
+
+
+def rope_table(cos_t, sin_t, seq, head_dim, theta, stream=None):
+    check(call("mt_op_rope_table", ptr(cos_t), ptr(sin_t), seq, head_dim, theta,
+               stream_handle(stream)), "mt_op_rope_table")
+
+
+def rope(qkv, batch, seq, n_heads, n_kv_heads, head_dim, cos_t, sin_t, inverse=0, stream=None):
+    check(call("mt_op_rope", ptr(qkv), batch, seq, n_heads, n_kv_heads, head_dim, ptr(cos_t),
+               ptr(sin_t), inverse, stream_handle(stream)), "mt_op_rope")
+
+
+def attn_fwd(qkv, o, lse, batch, seq, n_heads, n_kv_heads, head_dim, stream=None):
+    check(call("mt_op_attn_fwd", ptr(qkv), ptr(o), ptr(lse), batch, seq, n_heads, n_kv_heads,
+               head_dim, stream_handle(stream)), "mt_op_attn_fwd")
+
+
+def attn_bwd(qkv, o, lse, dout, delta, dqkv, batch, seq, n_heads, n_kv_heads, head_dim,
+             stream=None):
+    check(call("mt_op_attn_bwd", ptr(qkv), ptr(o), ptr(lse), ptr(dout), ptr(delta), ptr(dqkv),
+               batch, seq, n_heads, n_kv_heads, head_dim, stream_handle(stream)), "mt_op_attn_bwd")
+
+
+def ce_rows(logits, target, dlogits, loss_part, rows, vocab, inv_n, stream=None):
+    check(call("mt_op_ce_rows", ptr(logits), ptr(target), ptr(dlogits), ptr(loss_part), rows,
+               vocab, inv_n, stream_handle(stream)), "mt_op_ce_rows")

@@ -1,0 +1,219 @@
+"""Per-kernel parity on the GPU, through the C ABI, against the oracle's
+per-operation functions (NumPy), on seeded inputs.
+
+Sizes span several tiles plus ragged tails; the large cases use the real
+7B-shaped dimensions and compare sampled rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import decoder as D
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    return torch
+
+
+def _mt():
+    from layer_streamed_amd import mt
+    return mt
+
+
+def bf16_dev(a):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(torch.bfloat16)
+
+
+def to_np(t):
+    return t.float().cpu().numpy()
+
+
+def rel_fro(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def _rand(rng, shape, scale=1.0):
+    return (rng.standard_normal(shape) * scale).astype(np.float32)
+
+
+GEMM_CASES = [
+    # layout, M, N, K  (ragged M/N tails, K not a multiple of 64)
+    (0, 300, 200, 264), (1, 300, 200, 264), (2, 296, 200, 264),
+    (0, 256, 512, 256), (1, 256, 256, 1024), (2, 1024, 256, 256),
+    (0, 128, 128, 64), (1, 8, 8, 8), (2, 8, 8, 8),
+]
+
+
+@pytest.mark.parametrize("layout,M,N,K", GEMM_CASES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+def test_gemm_layouts_and_epilogues(layout, M, N, K, epi):
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(100 + layout * 7 + epi)
+    a = oracle.bf16_round(_rand(rng, (K, M) if layout == 2 else (M, K)))
+    b = oracle.bf16_round(_rand(rng, (N, K) if layout == 0 else (K, N)))
+    A, B = bf16_dev(a), bf16_dev(b)
+    af = a.astype(np.float64)
+    bf = b.astype(np.float64)
+    ref = (af.T if layout == 2 else af) @ (bf.T if layout == 0 else bf)
+    r = None
+    if epi == 3:
+        r = oracle.bf16_round(_rand(rng, (M, N)))
+        ref = ref + r
+    if epi in (1, 2):
+        Cm = torch.zeros((M, N), device="cuda", dtype=torch.float32)
+        if epi == 2:
+            init = _rand(rng, (M, N))
+            Cm.copy_(torch.from_numpy(init))
+            ref = ref + init
+    else:
+        Cm = torch.zeros((M, N), device="cuda", dtype=torch.bfloat16)
+    lda = M if layout == 2 else K
+    ldb = K if layout == 0 else N
+    mt.gemm(layout, epi, M, N, K, A, lda, B, ldb, Cm, N, R=None if r is None else bf16_dev(r), ldr=N)
+    torch.cuda.synchronize()
+    out = to_np(Cm)
+    tol = 1e-5 if epi in (1, 2) else 5e-3
+    assert rel_fro(out, ref) < tol
+    if epi not in (1, 2):
+        np.testing.assert_allclose(out, ref, rtol=1e-2, atol=1e-2 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("M,F,K", [(256, 1024, 256), (200, 96, 136)])
+def test_gemm_swiglu_forward_and_backward_epilogues(M, F, K):
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(7)
+    b = oracle.bf16_round(_rand(rng, (M, K)))
+    wg = oracle.bf16_round(_rand(rng, (F, K), 0.1))
+    wu = oracle.bf16_round(_rand(rng, (F, K), 0.1))
+    Bm, W = bf16_dev(b), bf16_dev(np.concatenate([wg, wu]))
+    m = torch.zeros((M, F), device="cuda", dtype=torch.bfloat16)
+    gu = torch.zeros((M, 2 * F), device="cuda", dtype=torch.bfloat16)
+    mt.gemm(0, 5, M, 2 * F, K, Bm, K, W, K, m, F, C2=gu, ldc2=2 * F, F=F)
+    torch.cuda.synchronize()
+    gt = b.astype(np.float64) @ wg.T.astype(np.float64)
+    ut = b.astype(np.float64) @ wu.T.astype(np.float64)
+    assert rel_fro(to_np(gu)[:, :F], gt) < 5e-3
+    assert rel_fro(to_np(gu)[:, F:], ut) < 5e-3
+    assert rel_fro(to_np(m), D.silu(gt) * ut) < 1e-2
+    # backward epilogue: dm = dy @ W_down (NN), fused into dgate/dup
+    H = K
+    dy = oracle.bf16_round(_rand(rng, (M, H)))
+    wd = oracle.bf16_round(_rand(rng, (H, F), 0.1))
+    dgu = torch.zeros((M, 2 * F), device="cuda", dtype=torch.bfloat16)
+    mt.gemm(1, 6, M, F, H, bf16_dev(dy), H, bf16_dev(wd), F, dgu, 2 * F, C2=dgu, ldc2=2 * F,
+            G=gu, ldg=2 * F, F=F)
+    torch.cuda.synchronize()
+    g_bf = to_np(gu)[:, :F].astype(np.float64)
+    u_bf = to_np(gu)[:, F:].astype(np.float64)
+    dm = dy.astype(np.float64) @ wd.astype(np.float64)
+    sg = 1 / (1 + np.exp(-g_bf))
+    assert rel_fro(to_np(dgu)[:, :F], dm * u_bf * sg * (1 + g_bf * (1 - sg))) < 1e-2
+    assert rel_fro(to_np(dgu)[:, F:], dm * D.silu(g_bf)) < 1e-2
+
+
+def test_gemm_7b_gate_up_shape_sampled_rows():
+    """Gate/up projection at the 7B shape (16384 x 37888 x 3584)."""
+    torch, mt = _torch(), _mt()
+    M, F, K = 16384, 18944, 3584
+    g = torch.Generator(device="cuda").manual_seed(3)
+    A = (torch.randn((M, K), device="cuda", generator=g) ).to(torch.bfloat16)
+    W = (torch.randn((2 * F, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    m = torch.empty((M, F), device="cuda", dtype=torch.bfloat16)
+    gu = torch.empty((M, 2 * F), device="cuda", dtype=torch.bfloat16)
+    mt.gemm(0, 5, M, 2 * F, K, A, K, W, K, m, F, C2=gu, ldc2=2 * F, F=F)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(M, 24, replace=False)
+    a = A[rows].float().cpu().numpy().astype(np.float64)
+    w = W.float().cpu().numpy().astype(np.float64)
+    ref = a @ w.T
+    out = gu[rows].float().cpu().numpy()
+    assert rel_fro(out, ref) < 5e-3
+    mref = D.silu(ref[:, :F]) * ref[:, F:]
+    assert rel_fro(m[rows].float().cpu().numpy(), mref) < 1e-2
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 256), (77, 3584), (130, 7168), (5, 8)])
+def test_rmsnorm_forward_backward(rows, cols):
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(rows + cols)
+    x = oracle.bf16_round(_rand(rng, (rows, cols), 2.0))
+    g = oracle.bf16_round(1 + 0.1 * _rand(rng, (cols,)))
+    dy = oracle.bf16_round(_rand(rng, (rows, cols)))
+    res = oracle.bf16_round(_rand(rng, (rows, cols)))
+    X, G, DY, RES = bf16_dev(x), bf16_dev(g), bf16_dev(dy), bf16_dev(res)
+    Y = torch.empty_like(X)
+    rstd = torch.empty(rows, device="cuda", dtype=torch.float32)
+    mt.rmsnorm_fwd(X, G, Y, rstd, rows, cols, 1e-6)
+    y_ref, r_ref = D.rms_norm(x, g, 1e-6)
+    dx_ref, dg_ref = D.rms_norm_backward(dy, x, g, r_ref)
+    ws = torch.empty(mt.rmsnorm_bwd_workspace(rows, cols) // 4 + 1, device="cuda", dtype=torch.float32)
+    DX = torch.empty_like(X)
+    DG = torch.empty(cols, device="cuda", dtype=torch.bfloat16)
+    mt.rmsnorm_bwd(DY, X, G, rstd, RES, DX, DG, rows, cols, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(rstd.cpu().numpy(), r_ref[:, 0], rtol=2e-6)
+    assert rel_fro(to_np(Y), y_ref) < 5e-3
+    assert rel_fro(to_np(DX), dx_ref + res) < 5e-3
+    assert rel_fro(to_np(DG), dg_ref) < 5e-3
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,d", [(2, 128, 4, 2, 64), (1, 77, 28, 4, 128)])
+def test_rope_table_and_rotation(B, T, Hq, Hkv, d):
+    torch, mt = _torch(), _mt()
+    cos_t = torch.empty((T, d // 2), device="cuda", dtype=torch.float32)
+    sin_t = torch.empty_like(cos_t)
+    mt.rope_table(cos_t, sin_t, T, d, 1e6)
+    c_ref, s_ref = D.rope_cos_sin(T, d, 1e6, np.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(cos_t.cpu().numpy(), c_ref, rtol=0, atol=1.2e-7)
+    np.testing.assert_allclose(sin_t.cpu().numpy(), s_ref, rtol=0, atol=1.2e-7)
+    rng = np.random.default_rng(T)
+    ld = (Hq + 2 * Hkv) * d
+    qkv = oracle.bf16_round(_rand(rng, (B * T, ld)))
+    Q = bf16_dev(qkv)
+    mt.rope(Q, B, T, Hq, Hkv, d, cos_t, sin_t, 0)
+    torch.cuda.synchronize()
+    out = to_np(Q)
+    nq = (Hq + Hkv) * d
+    ref = D.rope(qkv[:, :nq].reshape(B, T, Hq + Hkv, d), c_ref, s_ref).reshape(B * T, nq)
+    assert rel_fro(out[:, :nq], ref) < 5e-3
+    np.testing.assert_array_equal(out[:, nq:], qkv[:, nq:])
+    mt.rope(Q, B, T, Hq, Hkv, d, cos_t, sin_t, 1)
+    torch.cuda.synchronize()
+    ref_b = D.rope_backward(out[:, :nq].reshape(B, T, Hq + Hkv, d), c_ref, s_ref).reshape(B * T, nq)
+    assert rel_fro(to_np(Q)[:, :nq], ref_b) < 5e-3
+
+
+@pytest.mark.parametrize("rows,V", [(37, 1024), (8, 152064)])
+def test_cross_entropy_rows(rows, V):
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(V)
+    logits = _rand(rng, (rows, V), 3.0)
+    tgt = rng.integers(0, V, rows).astype(np.int32)
+    tgt[::5] = -1
+    L = torch.from_numpy(logits).cuda()
+    Tg = torch.from_numpy(tgt).cuda()
+    dl = torch.empty((rows, V), device="cuda", dtype=torch.bfloat16)
+    lp = torch.empty(rows, device="cuda", dtype=torch.float32)
+    inv_n = 1.0 / max(1, int((tgt >= 0).sum()))
+    mt.ce_rows(L, Tg, dl, lp, rows, V, inv_n)
+    torch.cuda.synchronize()
+    l64 = logits.astype(np.float64)
+    mx = l64.max(1, keepdims=True)
+    lse = mx[:, 0] + np.log(np.exp(l64 - mx).sum(1))
+    sm = np.exp(l64 - lse[:, None])
+    ref_d = np.zeros_like(sm)
+    ref_l = np.zeros(rows)
+    for r in range(rows):
+        if tgt[r] >= 0:
+            ref_d[r] = sm[r] * inv_n
+            ref_d[r, tgt[r]] -= inv_n
+            ref_l[r] = lse[r] - l64[r, tgt[r]]
+    np.testing.assert_allclose(lp.cpu().numpy(), ref_l, rtol=1e-5, atol=1e-5)
+    assert rel_fro(to_np(dl), ref_d) < 5e-3
+    assert not to_np(dl)[tgt < 0].any()
