@@ -82,7 +82,7 @@ typedef struct {
   int32_t host_alloc;        /* MT_HOST_PINNED (default) | MT_HOST_PAGEABLE (no GPU needed) */
   int32_t keep_grads;        /* 1: keep each step's gradients on the host for mt_model_get_param */
   int32_t time_kernels;      /* 1: bracket the dominant GEMM with HIP events (stats) */
-  float lr, beta1, beta2, eps, weight_decay; /* Adam (weight_decay must be 0) */
+  double lr, beta1, beta2, eps, weight_decay; /* Adam (weight_decay must be 0) */
 } mt_run_cfg;
 
 /* Device pointers of one layer's weights: the stateless template's binding.

@@ -28,7 +28,7 @@ HIP_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 CXX_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-march=x86-64-v3", "-pthread",
+    "-O3", "-std=c++17", "-fPIC", "-march=x86-64-v3", "-pthread", "-ffp-contract=off",
     "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
 ]

@@ -1,7 +1,655 @@
-// placeholder, replaced by the flash attention kernels
+// Causal grouped-query flash attention for gfx950 (forward and backward).
+//
+// Layout: q, k, v are column blocks of qkv [B*T, (Hq+2Hkv)*d] (bf16);
+// query head h reads key/value head h*Hkv/Hq.  Softmax in fp32, scores
+// scaled by 1/sqrt(d) and masked causally; the forward saves the row
+// log-sum-exp so the backward can rebuild P without storing it.
+//
+// MFMA mapping (v_mfma_f32_32x32x16_bf16, see common.h).  The forward
+// computes S^T = K Q^T with keys as rows, so in the result every lane holds
+// one query (lane % 32) and 16 of its 32 keys; the other 16 are in lane+32.
+// The online softmax therefore needs one cross-half exchange per tile, and
+// its per-row state (max, sum, rescale factor) is a per-lane scalar.  The
+// output is accumulated as O^T = V^T P^T: the P^T operand comes straight
+// from the lane's own score registers, because the k-slots an MFMA operand
+// lane supplies may be any fixed permutation of k as long as both operands
+// agree.  V (and, in the backward, Q, dO, K) is therefore stored in LDS
+// transposed, with rows of each 16-row group placed in that permuted order,
+// so each lane reads its 8 slots with one 16-byte LDS load.
+//
+// Backward (deterministic, no atomics): delta = rowsum(dO * O); a dK/dV
+// kernel owns 128 keys per workgroup and loops over every query head of the
+// GQA group and every query tile at or after its keys; a dQ kernel owns 128
+// queries and loops over key tiles up to the diagonal.
 #include "common.h"
 #include "kernels.h"
+
 namespace mt {
-hipError_t attn_fwd(const uint16_t*, uint16_t*, float*, int, int, int, int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t attn_bwd(const uint16_t*, const uint16_t*, const float*, const uint16_t*, float*, uint16_t*, int, int, int, int, int, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float NEG = -1e30f;
+
+struct AttnArgs {
+  const uint16_t* qkv;
+  uint16_t* o;
+  float* lse;
+  const uint16_t* dout;
+  const float* delta;
+  uint16_t* dqkv;
+  int B, T, Hq, Hkv;
+  long ldq, ldo;
+  float scale;       // 1/sqrt(d)
+  float scale_log2;  // scale * log2(e)
+};
+
+// Row r(s) of the 8-row set (group G of 16 rows, half hs) whose slot order
+// matches the MFMA accumulator: slots 0-3 -> rows 4hs..4hs+3, slots 4-7 ->
+// rows 8+4hs..8+4hs+3 of the group.
+__device__ __forceinline__ int perm_row(int G, int hs, int s) {
+  return 16 * G + (s < 4 ? 4 * hs + s : 8 + 4 * hs + (s - 4));
 }
+
+// Transpose 8 rows x 4 columns (u32x2 per row) into column di's 8 slots.
+__device__ __forceinline__ u32x4_t col_of(const u32x2_t* r, int di) {
+  uint32_t h[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const uint32_t w = (di < 2) ? r[s].x : r[s].y;
+    h[s] = (di & 1) ? (w >> 16) : (w & 0xFFFFu);
+  }
+  u32x4_t o;
+  o.x = h[0] | (h[1] << 16);
+  o.y = h[2] | (h[3] << 16);
+  o.z = h[4] | (h[5] << 16);
+  o.w = h[6] | (h[7] << 16);
+  return o;
+}
+
+__device__ __forceinline__ u32x4_t pack_p(const f32x16_t& acc, int jj) {
+  u32x4_t v;
+  v.x = pack_bf(acc[8 * jj + 0], acc[8 * jj + 1]);
+  v.y = pack_bf(acc[8 * jj + 2], acc[8 * jj + 3]);
+  v.z = pack_bf(acc[8 * jj + 4], acc[8 * jj + 5]);
+  v.w = pack_bf(acc[8 * jj + 6], acc[8 * jj + 7]);
+  return v;
+}
+
+__device__ __forceinline__ void zero16(f32x16_t& a) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a[e] = 0.f;
+}
+
+// A 64-row x D tile loaded as permuted 8x4 blocks: block b (< 16*D/8... )
+// covers rows perm_row(G, hs, 0..7) and columns 4*dq..4*dq+3.
+template <int D>
+struct PermTile {
+  static constexpr int NB = 8 * (D / 4);  // blocks per 64-row tile
+  u32x2_t r[8];
+  __device__ __forceinline__ void load(const uint16_t* base, long ld, int row0, int nrows,
+                                       int tid) {
+    if (tid < NB) {
+      const int kgrp = tid / (D / 4), dq = tid % (D / 4);
+      const int G = kgrp >> 1, hs = kgrp & 1;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int gr = row0 + perm_row(G, hs, s);
+        r[s] = gr < nrows ? *reinterpret_cast<const u32x2_t*>(base + (long)gr * ld + dq * 4)
+                          : u32x2_t{0, 0};
+      }
+    }
+  }
+  // natural layout [64][ld_nat]
+  __device__ __forceinline__ void store_nat(uint16_t* s_nat, int ld_nat, int tid) const {
+    if (tid < NB) {
+      const int kgrp = tid / (D / 4), dq = tid % (D / 4);
+      const int G = kgrp >> 1, hs = kgrp & 1;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        *reinterpret_cast<u32x2_t*>(s_nat + perm_row(G, hs, s) * ld_nat + dq * 4) = r[s];
+    }
+  }
+  // transposed, permuted layout [D][ld_t]
+  __device__ __forceinline__ void store_t(uint16_t* s_t, int ld_t, int tid) const {
+    if (tid < NB) {
+      const int kgrp = tid / (D / 4), dq = tid % (D / 4);
+      const int G = kgrp >> 1, hs = kgrp & 1;
+#pragma unroll
+      for (int di = 0; di < 4; ++di)
+        *reinterpret_cast<u32x4_t*>(s_t + (dq * 4 + di) * ld_t + G * 16 + hs * 8) = col_of(r, di);
+    }
+  }
+};
+
+// A 64-row x D tile loaded as 16-byte chunks for a natural LDS layout.
+template <int D>
+struct NatTile {
+  static constexpr int PER = 64 * (D / 8) / 256;
+  u32x4_t r[PER];
+  __device__ __forceinline__ void load(const uint16_t* base, long ld, int row0, int nrows,
+                                       int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int c = tid + p * 256;
+      const int row = c / (D / 8), dc = c % (D / 8);
+      const int gr = row0 + row;
+      r[p] = gr < nrows ? *reinterpret_cast<const u32x4_t*>(base + (long)gr * ld + dc * 8)
+                        : u32x4_t{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* s, int lds, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int c = tid + p * 256;
+      const int row = c / (D / 8), dc = c % (D / 8);
+      *reinterpret_cast<u32x4_t*>(s + row * lds + dc * 8) = r[p];
+    }
+  }
+};
+
+// ------------------------------------------------------------------ forward
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int BQ = 128, BKV = 64, KLD = D + 8, VLD = BKV + 8;
+  constexpr int STAGE = BKV * KLD + D * VLD;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int T = a.T;
+  const int nqb = (T + BQ - 1) / BQ;
+  const int per = a.Hq * a.B;
+  const int id = blockIdx.x;
+  const int qb = nqb - 1 - id / per;  // longest causal rows first
+  const int rest = id % per;
+  const int h = rest % a.Hq, b = rest / a.Hq;
+  const int g = (h * a.Hkv) / a.Hq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int q0 = qb * BQ;
+  const int qrow = q0 + 32 * w + n;
+  const long ldq = a.ldq;
+  const uint16_t* base = a.qkv + (long)b * T * ldq;
+  const uint16_t* kbase = base + (long)(a.Hq + g) * D;
+  const uint16_t* vbase = base + (long)(a.Hq + a.Hkv + g) * D;
+
+  u32x4_t qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = qrow < T ? *reinterpret_cast<const u32x4_t*>(base + (long)qrow * ldq + h * D + ks * 16 + hh * 8)
+                      : u32x4_t{0, 0, 0, 0};
+
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) zero16(oacc[dt]);
+  float m = NEG, l = 0.f;
+
+  const int kv_end = min(q0 + BQ, T);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int wave_qmax = q0 + 32 * w + 31;
+
+  NatTile<D> kt_ld;
+  PermTile<D> vt_ld;
+  kt_ld.load(kbase, ldq, 0, T, tid);
+  vt_ld.load(vbase, ldq, 0, T, tid);
+  kt_ld.store(smem, KLD, tid);
+  vt_ld.store_t(smem + BKV * KLD, VLD, tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * BKV;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      kt_ld.load(kbase, ldq, kv0 + BKV, T, tid);
+      vt_ld.load(vbase, ldq, kv0 + BKV, T, tid);
+    }
+    if (kv0 <= wave_qmax) {
+      const uint16_t* sk = smem + buf * STAGE;
+      const uint16_t* sv = sk + BKV * KLD;
+      f32x16_t sacc[2];
+      zero16(sacc[0]);
+      zero16(sacc[1]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4_t A = *reinterpret_cast<const u32x4_t*>(sk + (32 * kt + n) * KLD + ks * 16 + hh * 8);
+          sacc[kt] = mfma32(A, qf[ks], sacc[kt]);
+        }
+      float mx = NEG;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          float s = sacc[kt][e] * a.scale_log2;
+          if (key > qrow || key >= T) s = NEG;
+          sacc[kt][e] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2f(m - mnew);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(sacc[kt][e] - mnew);
+          sacc[kt][e] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l = l * alpha + rs;
+      m = mnew;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      u32x4_t pf[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) pf[kt][jj] = pack_p(sacc[kt], jj);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const u32x4_t A = *reinterpret_cast<const u32x4_t*>(sv + (32 * dt + n) * VLD + (2 * kt + jj) * 16 + hh * 8);
+            oacc[dt] = mfma32(A, pf[kt][jj], oacc[dt]);
+          }
+    }
+    if (t + 1 < ntiles) {
+      uint16_t* sk = smem + (buf ^ 1) * STAGE;
+      kt_ld.store(sk, KLD, tid);
+      vt_ld.store_t(sk + BKV * KLD, VLD, tid);
+    }
+    __syncthreads();
+  }
+
+  if (qrow < T) {
+    const float linv = 1.f / l;
+    uint16_t* orow = a.o + ((long)b * T + qrow) * a.ldo + h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * hh;
+        u32x2_t v;
+        v.x = pack_bf(oacc[dt][4 * j] * linv, oacc[dt][4 * j + 1] * linv);
+        v.y = pack_bf(oacc[dt][4 * j + 2] * linv, oacc[dt][4 * j + 3] * linv);
+        *reinterpret_cast<u32x2_t*>(orow + d) = v;
+      }
+    if (hh == 0) a.lse[((long)b * a.Hq + h) * T + qrow] = (m + log2f(l)) * LN2;
+  }
+}
+
+// ------------------------------------------------------------ backward prep
+template <int D>
+__global__ void attn_delta_kernel(const AttnArgs a) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)a.B * a.T * a.Hq;
+  if (idx >= total) return;
+  const int h = (int)(idx % a.Hq);
+  const long tok = idx / a.Hq;
+  const uint16_t* orow = a.o + tok * a.ldo + h * D;
+  const uint16_t* drow = a.dout + tok * a.ldo + h * D;
+  float s = 0.f;
+#pragma unroll 2
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(orow + c * 8);
+    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(drow + c * 8);
+    s += lo_bf(ov.x) * lo_bf(dv.x) + hi_bf(ov.x) * hi_bf(dv.x) + lo_bf(ov.y) * lo_bf(dv.y) +
+         hi_bf(ov.y) * hi_bf(dv.y) + lo_bf(ov.z) * lo_bf(dv.z) + hi_bf(ov.z) * hi_bf(dv.z) +
+         lo_bf(ov.w) * lo_bf(dv.w) + hi_bf(ov.w) * hi_bf(dv.w);
+  }
+  const int b = (int)(tok / a.T), t = (int)(tok % a.T);
+  const_cast<float*>(a.delta)[((long)b * a.Hq + h) * a.T + t] = s;
+}
+
+// ------------------------------------------------------------- dK and dV
+template <int D>
+__global__ __launch_bounds__(256) void attn_dkdv_kernel(const AttnArgs a) {
+  constexpr int BK = 128, BQ = 64, KLD = D + 8, VLD = BQ + 8;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* sQ = smem;
+  uint16_t* sdO = sQ + BQ * KLD;
+  uint16_t* sQt = sdO + BQ * KLD;
+  uint16_t* sdOt = sQt + D * VLD;
+  float* sL = reinterpret_cast<float*>(sdOt + D * VLD);
+  float* sDl = sL + BQ;
+
+  const int T = a.T;
+  const int nkb = (T + BK - 1) / BK;
+  const int per = a.Hkv * a.B;
+  const int kb = nkb - 1 - (int)blockIdx.x / per;
+  const int rest = blockIdx.x % per;
+  const int g = rest % a.Hkv, b = rest / a.Hkv;
+  const int rep = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int k0 = kb * BK;
+  const int key = k0 + 32 * w + n;
+  const long ldq = a.ldq;
+  const uint16_t* base = a.qkv + (long)b * T * ldq;
+  const uint16_t* dbase = a.dout + (long)b * T * a.ldo;
+
+  u32x4_t kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bool ok = key < T;
+    kf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + g) * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+    vf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + a.Hkv + g) * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+  }
+  f32x16_t dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    zero16(dk[dt]);
+    zero16(dv[dt]);
+  }
+
+  const int ntq = (T - k0 + BQ - 1) / BQ;  // query tiles from k0 to T
+  const int nit = rep * ntq;
+  PermTile<D> q_ld, d_ld;
+  float lse_r = 0.f, del_r = 0.f;
+  auto fetch = [&](int it) {
+    const int hq = g * rep + it / ntq;
+    const int qt0 = k0 + (it % ntq) * BQ;
+    q_ld.load(base + hq * D, ldq, qt0, T, tid);
+    d_ld.load(dbase + hq * D, a.ldo, qt0, T, tid);
+    if (tid < BQ) {
+      const int q = qt0 + tid;
+      const long li = ((long)b * a.Hq + hq) * T + q;
+      lse_r = q < T ? a.lse[li] * LOG2E : -NEG;  // +1e30 makes P = 0 for padding rows
+      del_r = q < T ? a.delta[li] : 0.f;
+    }
+  };
+  auto commit = [&]() {
+    q_ld.store_nat(sQ, KLD, tid);
+    q_ld.store_t(sQt, VLD, tid);
+    d_ld.store_nat(sdO, KLD, tid);
+    d_ld.store_t(sdOt, VLD, tid);
+    if (tid < BQ) {
+      sL[tid] = lse_r;
+      sDl[tid] = del_r;
+    }
+  };
+
+  if (nit > 0) {
+    fetch(0);
+    commit();
+  }
+  __syncthreads();
+  for (int it = 0; it < nit; ++it) {
+    const int qt0 = k0 + (it % ntq) * BQ;
+    if (it + 1 < nit) fetch(it + 1);
+    if (qt0 + BQ - 1 >= k0 + 32 * w) {  // some query of the tile sees this wave's keys
+      f32x16_t sacc[2], dpacc[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        zero16(sacc[qt]);
+        zero16(dpacc[qt]);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4_t Aq = *reinterpret_cast<const u32x4_t*>(sQ + (32 * qt + n) * KLD + ks * 16 + hh * 8);
+          sacc[qt] = mfma32(Aq, kf[ks], sacc[qt]);
+          const u32x4_t Ad = *reinterpret_cast<const u32x4_t*>(sdO + (32 * qt + n) * KLD + ks * 16 + hh * 8);
+          dpacc[qt] = mfma32(Ad, vf[ks], dpacc[qt]);
+        }
+      }
+      // P and dS, rows = queries (qt0 + 32qt + 8j + 4hh + i), column = key
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int qi = 32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const int q = qt0 + qi;
+          float p = exp2f(sacc[qt][e] * a.scale_log2 - sL[qi]);
+          if (key > q) p = 0.f;
+          sacc[qt][e] = p;
+          dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
+        }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4_t Pb = pack_p(sacc[qt], jj);
+          const u32x4_t Sb = pack_p(dpacc[qt], jj);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const int off = (32 * dt + n) * VLD + (2 * qt + jj) * 16 + hh * 8;
+            dv[dt] = mfma32(*reinterpret_cast<const u32x4_t*>(sdOt + off), Pb, dv[dt]);
+            dk[dt] = mfma32(*reinterpret_cast<const u32x4_t*>(sQt + off), Sb, dk[dt]);
+          }
+        }
+    }
+    __syncthreads();
+    if (it + 1 < nit) commit();
+    __syncthreads();
+  }
+
+  if (key < T) {
+    uint16_t* drow = a.dqkv + ((long)b * T + key) * ldq;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * hh;
+        u32x2_t vk, vv;
+        vk.x = pack_bf(dk[dt][4 * j] * a.scale, dk[dt][4 * j + 1] * a.scale);
+        vk.y = pack_bf(dk[dt][4 * j + 2] * a.scale, dk[dt][4 * j + 3] * a.scale);
+        vv.x = pack_bf(dv[dt][4 * j], dv[dt][4 * j + 1]);
+        vv.y = pack_bf(dv[dt][4 * j + 2], dv[dt][4 * j + 3]);
+        *reinterpret_cast<u32x2_t*>(drow + (a.Hq + g) * D + d) = vk;
+        *reinterpret_cast<u32x2_t*>(drow + (a.Hq + a.Hkv + g) * D + d) = vv;
+      }
+  }
+}
+
+// --------------------------------------------------------------------- dQ
+template <int D>
+__global__ __launch_bounds__(256) void attn_dq_kernel(const AttnArgs a) {
+  constexpr int BQ = 128, BKV = 64, KLD = D + 8, VLD = BKV + 8;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* sK = smem;
+  uint16_t* sV = sK + BKV * KLD;
+  uint16_t* sKt = sV + BKV * KLD;
+
+  const int T = a.T;
+  const int nqb = (T + BQ - 1) / BQ;
+  const int per = a.Hq * a.B;
+  const int qb = nqb - 1 - (int)blockIdx.x / per;
+  const int rest = blockIdx.x % per;
+  const int h = rest % a.Hq, b = rest / a.Hq;
+  const int g = (h * a.Hkv) / a.Hq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int q0 = qb * BQ;
+  const int qrow = q0 + 32 * w + n;
+  const long ldq = a.ldq;
+  const uint16_t* base = a.qkv + (long)b * T * ldq;
+  const uint16_t* kbase = base + (long)(a.Hq + g) * D;
+  const uint16_t* vbase = base + (long)(a.Hq + a.Hkv + g) * D;
+
+  u32x4_t qf[D / 16], df[D / 16];
+  const bool ok = qrow < T;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)qrow * ldq + h * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+    df[ks] = ok ? *reinterpret_cast<const u32x4_t*>(a.dout + ((long)b * T + qrow) * a.ldo + h * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+  }
+  const long li = ((long)b * a.Hq + h) * T + qrow;
+  const float lse2 = ok ? a.lse[li] * LOG2E : -NEG;
+  const float del = ok ? a.delta[li] : 0.f;
+
+  f32x16_t dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) zero16(dq[dt]);
+
+  const int kv_end = min(q0 + BQ, T);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int wave_qmax = q0 + 32 * w + 31;
+  PermTile<D> k_ld;
+  NatTile<D> v_ld;
+  auto fetch = [&](int kv0) {
+    k_ld.load(kbase, ldq, kv0, T, tid);
+    v_ld.load(vbase, ldq, kv0, T, tid);
+  };
+  auto commit = [&]() {
+    k_ld.store_nat(sK, KLD, tid);
+    k_ld.store_t(sKt, VLD, tid);
+    v_ld.store(sV, KLD, tid);
+  };
+  fetch(0);
+  commit();
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * BKV;
+    if (t + 1 < ntiles) fetch(kv0 + BKV);
+    if (kv0 <= wave_qmax) {
+      f32x16_t sacc[2], dpacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        zero16(sacc[kt]);
+        zero16(dpacc[kt]);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4_t Ak = *reinterpret_cast<const u32x4_t*>(sK + (32 * kt + n) * KLD + ks * 16 + hh * 8);
+          sacc[kt] = mfma32(Ak, qf[ks], sacc[kt]);
+          const u32x4_t Av = *reinterpret_cast<const u32x4_t*>(sV + (32 * kt + n) * KLD + ks * 16 + hh * 8);
+          dpacc[kt] = mfma32(Av, df[ks], dpacc[kt]);
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          float p = exp2f(sacc[kt][e] * a.scale_log2 - lse2);
+          if (kk > qrow || kk >= T) p = 0.f;
+          dpacc[kt][e] = p * (dpacc[kt][e] - del);
+        }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4_t Sb = pack_p(dpacc[kt], jj);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const u32x4_t A = *reinterpret_cast<const u32x4_t*>(sKt + (32 * dt + n) * VLD + (2 * kt + jj) * 16 + hh * 8);
+            dq[dt] = mfma32(A, Sb, dq[dt]);
+          }
+        }
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) commit();
+    __syncthreads();
+  }
+
+  if (ok) {
+    uint16_t* drow = a.dqkv + ((long)b * T + qrow) * ldq + h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * hh;
+        u32x2_t v;
+        v.x = pack_bf(dq[dt][4 * j] * a.scale, dq[dt][4 * j + 1] * a.scale);
+        v.y = pack_bf(dq[dt][4 * j + 2] * a.scale, dq[dt][4 * j + 3] * a.scale);
+        *reinterpret_cast<u32x2_t*>(drow + d) = v;
+      }
+  }
+}
+
+template <class K>
+hipError_t set_lds(K kern, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int D>
+hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
+  constexpr size_t lds = 2 * (64 * (D + 8) + D * (64 + 8)) * sizeof(uint16_t);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds(attn_fwd_kernel<D>, lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int nqb = (a.T + 127) / 128;
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
+  constexpr size_t lds_kv = (2 * 64 * (D + 8) + 2 * D * (64 + 8)) * sizeof(uint16_t) + 2 * 64 * sizeof(float);
+  constexpr size_t lds_q = (2 * 64 * (D + 8) + D * (64 + 8)) * sizeof(uint16_t);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds(attn_dkdv_kernel<D>, lds_kv);
+    if (e != hipSuccess) return e;
+    e = set_lds(attn_dq_kernel<D>, lds_q);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const long rows = (long)a.B * a.T * a.Hq;
+  hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (a.T + 127) / 128;
+  hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_kv, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (a.T + 127) / 128;
+  hipLaunchKernelGGL(attn_dq_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_q, s, a);
+  return hipGetLastError();
+}
+
+AttnArgs make_args(const uint16_t* qkv, int batch, int seq, int n_heads, int n_kv_heads,
+                   int head_dim) {
+  AttnArgs a{};
+  a.qkv = qkv;
+  a.B = batch;
+  a.T = seq;
+  a.Hq = n_heads;
+  a.Hkv = n_kv_heads;
+  a.ldq = (long)(n_heads + 2 * n_kv_heads) * head_dim;
+  a.ldo = (long)n_heads * head_dim;
+  a.scale = 1.f / sqrtf((float)head_dim);
+  a.scale_log2 = a.scale * LOG2E;
+  return a;
+}
+
+}  // namespace
+
+hipError_t attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int seq, int n_heads,
+                    int n_kv_heads, int head_dim, hipStream_t s) {
+  if (batch == 0 || seq == 0) return hipSuccess;
+  AttnArgs a = make_args(qkv, batch, seq, n_heads, n_kv_heads, head_dim);
+  a.o = o;
+  a.lse = lse;
+  if (head_dim == 128) return fwd_d<128>(a, s);
+  if (head_dim == 64) return fwd_d<64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                    const uint16_t* dout, float* delta, uint16_t* dqkv, int batch, int seq,
+                    int n_heads, int n_kv_heads, int head_dim, hipStream_t s) {
+  if (batch == 0 || seq == 0) return hipSuccess;
+  AttnArgs a = make_args(qkv, batch, seq, n_heads, n_kv_heads, head_dim);
+  a.o = const_cast<uint16_t*>(o);
+  a.lse = const_cast<float*>(lse);
+  a.dout = dout;
+  a.delta = delta;
+  a.dqkv = dqkv;
+  if (head_dim == 128) return bwd_d<128>(a, s);
+  if (head_dim == 64) return bwd_d<64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mt

@@ -1,0 +1,677 @@
+// The streamed training step (MegaTrain listing page, Abstract and Fig. 3;
+// blog summary, sections 1-4): weights stream in per layer on a W stream,
+// forward / recompute / backward run on a C stream, and each unit's
+// gradient streams out on a G stream into a pinned slab, where a CPU thread
+// runs Adam on that unit while the GPU goes on with the next layers.
+//
+// The schedule is built first as a pure plan (compute ops, weight loads,
+// slot assignment and dependencies) that has no HIP in it, so its hazards
+// can be checked on the CPU; one executor replays it with HIP events.
+//
+// Compute order: forward of every layer (keeping the input of layers
+// l = 0 mod K), the head (final norm, LM head, loss, its backward), then
+// the segments from the last: re-forward the segment's first K-1 layers
+// from its checkpoint to rebuild their inputs, then recompute+backward each
+// layer in reverse.  A weight slot is reused only after the last compute
+// op that reads it has finished, and a load may run at most `depth` compute
+// ops ahead of its first use (depth 2 = double buffering).
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <condition_variable>
+#include <deque>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "kernels.h"
+#include "layer.h"
+#include "model.h"
+#include "status.h"
+
+namespace mt {
+
+enum OpKind { OP_FWD = 0, OP_HEAD = 1, OP_REFWD = 2, OP_BWD = 3 };
+struct PlanOp {
+  int kind, layer, load;
+};
+struct PlanLoad {
+  int unit, slot, first_use, last_use, wait_use, gate_use;
+};
+struct Plan {
+  std::vector<PlanOp> ops;
+  std::vector<PlanLoad> loads;
+  int n_slots = 0;
+  const char* error = nullptr;
+};
+
+static int plan_slots(int K, int depth) { return std::max(2, K + depth); }
+
+Plan build_plan(int L, int K, int depth, int n_slots) {
+  Plan p;
+  p.n_slots = n_slots;
+  auto add_load = [&](int unit) {
+    p.loads.push_back({unit, -1, -1, -1, -1, -1});
+    return (int)p.loads.size() - 1;
+  };
+  auto add_op = [&](int kind, int layer, int load) {
+    const int i = (int)p.ops.size();
+    p.ops.push_back({kind, layer, load});
+    PlanLoad& ld = p.loads[load];
+    if (ld.first_use < 0) ld.first_use = i;
+    ld.last_use = i;
+  };
+  for (int l = 0; l < L; ++l) add_op(OP_FWD, l, add_load(l));
+  add_op(OP_HEAD, -1, add_load(L));
+  for (int a = ((L - 1) / K) * K; a >= 0; a -= K) {
+    const int e = std::min(a + K, L);
+    std::vector<int> ld(e - a);
+    for (int l = a; l < e; ++l) ld[l - a] = add_load(l);
+    for (int l = a; l < e - 1; ++l) add_op(OP_REFWD, l, ld[l - a]);
+    for (int l = e - 1; l >= a; --l) add_op(OP_BWD, l, ld[l - a]);
+  }
+  std::vector<int> free_after(n_slots, -1);
+  for (auto& ld : p.loads) {
+    ld.gate_use = ld.first_use - depth >= 0 ? ld.first_use - depth : -1;
+    if (ld.unit == L) {  // the head has a slot of its own
+      ld.slot = -2;
+      ld.wait_use = -1;
+      continue;
+    }
+    int best = 0;
+    for (int s = 1; s < n_slots; ++s)
+      if (free_after[s] < free_after[best]) best = s;
+    ld.slot = best;
+    ld.wait_use = free_after[best];
+    if (ld.wait_use >= ld.first_use && !p.error) p.error = "too few weight slots for this schedule";
+    free_after[best] = ld.last_use;
+  }
+  return p;
+}
+
+namespace {
+
+constexpr int NG = 3;  // device gradient ring depth
+
+struct Arena {
+  std::vector<uint16_t*> slot;
+  uint16_t* head_slot = nullptr;
+  uint16_t* gring[NG] = {};
+  uint16_t* head_grad = nullptr;
+  uint16_t* act[2] = {};
+  std::vector<uint16_t*> ckpt, seg;
+  uint16_t* dy = nullptr;
+  int32_t* tgt = nullptr;
+  float* loss = nullptr;
+  void* lws = nullptr;
+  size_t lws_bytes = 0;
+  void* hws = nullptr;
+  size_t hws_bytes = 0;
+};
+
+Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
+  Carve c{base};
+  Arena a;
+  const int L = M->cfg.n_layers, K = M->run.ckpt_interval;
+  const size_t lay = M->ll.total, head = M->hl.total, act = (size_t)d.D * d.H;
+  const int ns = plan_slots(K, M->run.prefetch_depth);
+  for (int i = 0; i < ns; ++i) a.slot.push_back(c.take<uint16_t>(lay));
+  a.head_slot = c.take<uint16_t>(head);
+  for (int i = 0; i < NG; ++i) a.gring[i] = c.take<uint16_t>(lay);
+  a.head_grad = c.take<uint16_t>(head);
+  a.act[0] = c.take<uint16_t>(act);
+  a.act[1] = c.take<uint16_t>(act);
+  for (int i = 0; i <= L / K; ++i) a.ckpt.push_back(c.take<uint16_t>(act));
+  for (int i = 0; i < K - 1; ++i) a.seg.push_back(c.take<uint16_t>(act));
+  a.dy = c.take<uint16_t>(act);
+  a.tgt = c.take<int32_t>(d.D);
+  a.loss = c.take<float>(64);
+  a.lws_bytes = layer_ws_bytes(d, 1);
+  a.lws = c.take<char>(a.lws_bytes);
+  a.hws_bytes = head_ws_bytes(d);
+  a.hws = c.take<char>(a.hws_bytes);
+  *bytes = c.off + 256;
+  return a;
+}
+
+mt_layer_view layer_view(const mt_model* M, const uint16_t* slab) {
+  const LayerLayout& l = M->ll;
+  mt_layer_view v;
+  v.attn_norm = slab + l.attn_norm;
+  v.w_qkv = slab + l.w_qkv;
+  v.w_o = slab + l.w_o;
+  v.mlp_norm = slab + l.mlp_norm;
+  v.w_gate_up = slab + l.w_gate_up;
+  v.w_down = slab + l.w_down;
+  return v;
+}
+
+mt_layer_grad_view grad_view(const mt_model* M, uint16_t* slab) {
+  const LayerLayout& l = M->ll;
+  mt_layer_grad_view v;
+  v.attn_norm = slab + l.attn_norm;
+  v.w_qkv = slab + l.w_qkv;
+  v.w_o = slab + l.w_o;
+  v.mlp_norm = slab + l.mlp_norm;
+  v.w_gate_up = slab + l.w_gate_up;
+  v.w_down = slab + l.w_down;
+  return v;
+}
+
+// Event pool handed out in order within one step.
+struct Events {
+  std::vector<hipEvent_t>* pool;
+  size_t next = 0;
+  mt_status err = MT_OK;
+  hipEvent_t get() {
+    if (next == pool->size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) {
+        err = MT_E_HIP;
+        return nullptr;
+      }
+      pool->push_back(e);
+    }
+    return (*pool)[next++];
+  }
+};
+
+float elapsed(hipEvent_t a, hipEvent_t b) {
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return 0.f;
+  return ms;
+}
+
+struct Offload {
+  int unit;          // -1 = dx0
+  const uint16_t* src;
+  size_t elems;
+  hipEvent_t after;  // compute event the copy waits for
+  int ring;          // gradient ring index or -1
+  bool end = false;
+};
+
+struct Landed {
+  int unit;
+  uint16_t* host;  // slab (or dx0 staging)
+  bool own_alloc;  // allocated for this transfer (no pool)
+  hipEvent_t ev;
+  bool end = false;
+};
+
+template <class T>
+struct Queue {
+  std::mutex mu;
+  std::condition_variable cv;
+  std::deque<T> q;
+  void push(T v) {
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      q.push_back(v);
+    }
+    cv.notify_one();
+  }
+  T pop() {
+    std::unique_lock<std::mutex> lk(mu);
+    cv.wait(lk, [&] { return !q.empty(); });
+    T v = q.front();
+    q.pop_front();
+    return v;
+  }
+};
+
+#define MT_STEP_HIP(expr)                                                                     \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) {                                                                   \
+      fail = set_error(MT_E_HIP, "mt_stream_step: %s failed: %s", #expr, hipGetErrorString(e_)); \
+      goto drain;                                                                             \
+    }                                                                                         \
+  } while (0)
+
+#define MT_STEP_RUN(expr)        \
+  do {                           \
+    mt_status s_ = (expr);       \
+    if (s_ != MT_OK) {           \
+      fail = s_;                 \
+      goto drain;                \
+    }                            \
+  } while (0)
+
+}  // namespace
+
+size_t stream_arena_bytes(const mt_model* M, const Dims& d) {
+  size_t b = 0;
+  carve_arena(M, d, nullptr, &b);
+  return b;
+}
+
+}  // namespace mt
+
+using namespace mt;
+
+extern "C" {
+
+size_t mt_stream_arena_bytes(const mt_model* model, int32_t batch, int32_t seq) {
+  if (!model) return 0;
+  Dims d;
+  if (make_dims(&model->cfg, &model->run, batch, seq, &d)) return 0;
+  return stream_arena_bytes(model, d);
+}
+
+// Diagnostic: the plan for L layers, checkpoint interval K and prefetch
+// depth.  out receives, for each compute op, (kind, layer, load) and then,
+// for each load, (unit, slot, first_use, last_use, wait_use, gate_use);
+// counts[0..2] = n_ops, n_loads, n_slots.  Returns MT_E_SHAPE if the plan is
+// invalid, MT_E_OOM_HOST if out is too small.
+mt_status mt_debug_plan(int32_t n_layers, int32_t ckpt_interval, int32_t prefetch_depth,
+                        int32_t* out, size_t cap, int32_t* counts) {
+  MT_CHECK(n_layers >= 1 && ckpt_interval >= 1 && prefetch_depth >= 1 && out && counts,
+           MT_E_INVALID, "mt_debug_plan: bad arguments");
+  Plan p = build_plan(n_layers, ckpt_interval, prefetch_depth,
+                      plan_slots(ckpt_interval, prefetch_depth));
+  counts[0] = (int32_t)p.ops.size();
+  counts[1] = (int32_t)p.loads.size();
+  counts[2] = p.n_slots;
+  const size_t need = 3 * p.ops.size() + 6 * p.loads.size();
+  MT_CHECK(cap >= need, MT_E_OOM_HOST, "mt_debug_plan: need %zu entries", need);
+  size_t k = 0;
+  for (auto& o : p.ops) {
+    out[k++] = o.kind;
+    out[k++] = o.layer;
+    out[k++] = o.load;
+  }
+  for (auto& l : p.loads) {
+    out[k++] = l.unit;
+    out[k++] = l.slot;
+    out[k++] = l.first_use;
+    out[k++] = l.last_use;
+    out[k++] = l.wait_use;
+    out[k++] = l.gate_use;
+  }
+  if (p.error) return set_error(MT_E_SHAPE, "mt_debug_plan: %s", p.error);
+  return MT_OK;
+}
+
+mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int32_t seq,
+                         void* arena, size_t arena_bytes, void* const streams[3],
+                         float* loss_out, mt_step_stats* stats_out) {
+  using clock = std::chrono::steady_clock;
+  const auto t_begin = clock::now();
+  MT_CHECK(M && tokens && arena && streams && loss_out, MT_E_INVALID,
+           "mt_stream_step: null argument");
+  MT_CHECK(!M->broken, MT_E_STATE, "mt_stream_step: the model was left inconsistent by an earlier failure");
+  MT_CHECK(streams[0] && streams[1] && streams[2], MT_E_INVALID, "mt_stream_step: null stream");
+  MT_CHECK(M->run.host_alloc == MT_HOST_PINNED, MT_E_INVALID,
+           "mt_stream_step: needs a model created with pinned host memory");
+  Dims d;
+  if (const char* msg = make_dims(&M->cfg, &M->run, batch, seq, &d))
+    return set_error(MT_E_SHAPE, "mt_stream_step: %s", msg);
+  MT_CHECK(seq >= 2, MT_E_SHAPE, "mt_stream_step: seq must be >= 2 (next-token targets)");
+  const int L = M->cfg.n_layers, K = M->run.ckpt_interval, V = d.V;
+  for (int i = 0; i < d.D; ++i)
+    MT_CHECK(tokens[i] >= 0 && tokens[i] < V, MT_E_INVALID,
+             "mt_stream_step: token %d at position %d is outside [0, %d)", tokens[i], i, V);
+  size_t need = 0;
+  Arena A = carve_arena(M, d, static_cast<char*>(arena), &need);
+  MT_CHECK(arena_bytes >= need, MT_E_OOM_DEVICE, "mt_stream_step: arena %zu < %zu bytes",
+           arena_bytes, need);
+  MT_CHECK(((uintptr_t)arena & 255) == 0, MT_E_INVALID, "mt_stream_step: arena must be 256-byte aligned");
+  Plan plan = build_plan(L, K, M->run.prefetch_depth, plan_slots(K, M->run.prefetch_depth));
+  MT_CHECK(!plan.error, MT_E_INVALID, "mt_stream_step: %s", plan.error);
+
+  // pinned per-step staging
+  if (M->staging_tokens < (size_t)d.D) {
+    const size_t nt = (size_t)d.D;
+    M->x0_host = static_cast<uint16_t*>(M->host_alloc(nt * d.H * 2, true));
+    M->dx0_host = static_cast<uint16_t*>(M->host_alloc(nt * d.H * 2, true));
+    M->tgt_host = static_cast<int32_t*>(M->host_alloc(nt * 4, true));
+    M->loss_host = static_cast<float*>(M->host_alloc(64, true));
+    MT_CHECK(M->x0_host && M->dx0_host && M->tgt_host && M->loss_host, MT_E_OOM_HOST,
+             "mt_stream_step: pinned staging allocation failed");
+    M->staging_tokens = nt;
+  }
+
+  const bool ser = M->run.serialize != 0;
+  hipStream_t sC = static_cast<hipStream_t>(streams[1]);
+  hipStream_t sW = ser ? sC : static_cast<hipStream_t>(streams[0]);
+  hipStream_t sG = ser ? sC : static_cast<hipStream_t>(streams[2]);
+  const int64_t t_step = M->step + 1;
+  const AdamHp hp = adam_hp(M->run, t_step);
+  Events ev{&M->events};
+  mt_status fail = MT_OK;
+  const size_t act = (size_t)d.D * d.H;
+
+  // host: targets and the embedding gather (from the bf16 copy)
+  const Unit& emb = M->units[L + 1];
+  for (int b = 0; b < d.B; ++b)
+    for (int t = 0; t < d.T; ++t)
+      M->tgt_host[(size_t)b * d.T + t] = t + 1 < d.T ? tokens[(size_t)b * d.T + t + 1] : -1;
+  embed_gather(emb.shadow, tokens, (size_t)d.D, (size_t)d.H, M->x0_host, M->pool.get());
+  const float inv_n = 1.f / (float)((size_t)d.B * (d.T - 1));
+
+  // thread state
+  Queue<Offload> offq;
+  Queue<Landed> landq;
+  std::mutex ring_mu;
+  std::condition_variable ring_cv;
+  long ring_enqueued = 0;  // offloads from the gradient ring already enqueued
+  std::atomic<bool> abort_all{false};
+  std::atomic<int> g_fail{0}, a_fail{0};
+  std::atomic<int64_t> units_updated{0};
+  double adam_ms = 0.0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> d2h_ev;
+  double d2h_bytes = 0;
+  hipEvent_t loss_ev = nullptr;
+  std::mutex ev_mu;  // guards the event pool across threads
+  auto get_ev = [&]() {
+    std::lock_guard<std::mutex> lk(ev_mu);
+    return ev.get();
+  };
+  bool nonfinite_loss = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> h2d_ev;
+  double h2d_bytes = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> wait_ev_f, wait_ev_b;
+  Probe probe;
+  hipEvent_t ph_start = nullptr, ph_fwd = nullptr, ph_head = nullptr, ph_end = nullptr;
+  std::vector<hipEvent_t> op_done(plan.ops.size(), nullptr), load_done(plan.loads.size(), nullptr);
+  size_t next_load = 0;
+  int bwd_count = 0;
+  std::thread gthr, athr;
+  std::mutex loss_mu;
+  std::condition_variable loss_cv;
+  bool loss_ready = false;
+
+  hipEvent_t gfree[NG] = {};  // ring buffer i may be overwritten once this fires
+
+  // --------------------------------------------------------- G thread
+  auto g_main = [&]() {
+    for (;;) {
+      Offload o = offq.pop();
+      if (o.end) {
+        landq.push(Landed{0, nullptr, false, nullptr, true});
+        return;
+      }
+      if (abort_all.load()) {
+        if (o.ring >= 0) {
+          std::lock_guard<std::mutex> lk(ring_mu);
+          ++ring_enqueued;
+          ring_cv.notify_all();
+        }
+        continue;
+      }
+      uint16_t* host = nullptr;
+      bool own = false;
+      if (o.unit < 0) {
+        host = M->dx0_host;
+      } else if (M->run.use_slab_pool) {
+        host = M->slabs.acquire();
+      } else {
+        if (hipHostMalloc(reinterpret_cast<void**>(&host), M->slab_elems * 2, hipHostMallocDefault) !=
+            hipSuccess) {
+          g_fail = 1;
+          abort_all = true;
+          continue;
+        }
+        own = true;
+      }
+      hipEvent_t e0 = get_ev(), e1 = get_ev(), landed = get_ev();
+      bool ok = e0 && e1 && landed && hipStreamWaitEvent(sG, o.after, 0) == hipSuccess &&
+                hipEventRecord(e0, sG) == hipSuccess &&
+                hipMemcpyAsync(host, o.src, o.elems * 2, hipMemcpyDeviceToHost, sG) == hipSuccess &&
+                hipEventRecord(e1, sG) == hipSuccess;
+      if (ok && o.ring >= 0) ok = hipEventRecord(gfree[o.ring], sG) == hipSuccess;
+      if (o.ring >= 0) {
+        std::lock_guard<std::mutex> lk(ring_mu);
+        ++ring_enqueued;
+        ring_cv.notify_all();
+      }
+      ok = ok && hipEventRecord(landed, sG) == hipSuccess;
+      if (!ok) {
+        g_fail = 1;
+        abort_all = true;
+        if (!own && o.unit >= 0) M->slabs.release(host);
+        if (own) hipHostFree(host);
+        continue;
+      }
+      d2h_ev.push_back({e0, e1});
+      d2h_bytes += (double)o.elems * 2;
+      landq.push(Landed{o.unit, host, own, landed, false});
+    }
+  };
+
+  // ------------------------------------------------------ Adam thread
+  auto a_main = [&]() {
+    // zero the embedding gradient while the GPU runs the forward
+    float* dE = M->dE;
+    M->pool->parallel_for((size_t)d.V * d.H,
+                          [&](size_t lo, size_t hi) { memset(dE + lo, 0, (hi - lo) * 4); });
+    bool checked = false;
+    bool skip = false;
+    for (;;) {
+      Landed x = landq.pop();
+      if (x.end) return;
+      if (hipEventSynchronize(x.ev) != hipSuccess) {
+        a_fail = 1;
+        abort_all = true;
+      }
+      if (!checked) {
+        std::unique_lock<std::mutex> lk(loss_mu);
+        loss_cv.wait(lk, [&] { return loss_ready; });
+        checked = true;
+        if (!loss_ev || hipEventSynchronize(loss_ev) != hipSuccess) {
+          a_fail = 1;
+          abort_all = true;
+        } else if (M->run.check_finite && !std::isfinite(*M->loss_host)) {
+          nonfinite_loss = true;
+          abort_all = true;
+        }
+      }
+      skip = skip || abort_all.load();
+      const auto t0 = clock::now();
+      if (!skip) {
+        if (x.unit >= 0) {
+          Unit& u = M->units[x.unit];
+          if (M->run.check_finite && !grad_finite(x.host, nullptr, u.n, M->pool.get())) {
+            a_fail = 2;
+            abort_all = true;
+            skip = true;
+          } else {
+            adam_parallel(u.master, u.m, u.v, x.host, nullptr, u.shadow, u.n, hp, M->pool.get());
+            if (u.kept) memcpy(u.kept, x.host, u.n * 2);
+            ++units_updated;
+          }
+        } else {
+          Unit& u = M->units[L + 1];
+          embed_scatter_add(x.host, tokens, (size_t)d.D, (size_t)d.H, dE, M->pool.get());
+          if (M->run.check_finite && !grad_finite(nullptr, dE, (size_t)d.V * d.H, M->pool.get())) {
+            a_fail = 2;
+            abort_all = true;
+            skip = true;
+          } else {
+            adam_parallel(u.master, u.m, u.v, nullptr, dE, u.shadow, (size_t)d.V * d.H, hp,
+                          M->pool.get());
+            ++units_updated;
+          }
+        }
+      }
+      adam_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+      if (x.unit >= 0) {
+        if (x.own_alloc) hipHostFree(x.host);
+        else M->slabs.release(x.host);
+      }
+    }
+  };
+
+  // ---------------------------------------------------- enqueue (main)
+  for (int i = 0; i < NG; ++i) gfree[i] = get_ev();
+  loss_ev = get_ev();
+  ph_start = get_ev();
+  ph_fwd = get_ev();
+  ph_head = get_ev();
+  ph_end = get_ev();
+  hipEvent_t x0_ready = get_ev();
+  for (auto& e : op_done) e = get_ev();
+  for (auto& e : load_done) e = get_ev();
+  if (M->run.time_kernels) {
+    probe.ev.resize(4 * (size_t)L + 8);
+    for (auto& e : probe.ev) e = get_ev();
+  }
+  if (ev.err != MT_OK) return set_error(MT_E_HIP, "mt_stream_step: event creation failed");
+
+  gthr = std::thread(g_main);
+  athr = std::thread(a_main);
+
+  {
+    // gradient buffers: pads must read as zero
+    MT_STEP_HIP(hipMemsetAsync(A.head_grad, 0, M->hl.total * 2, sC));
+    for (int i = 0; i < NG; ++i) MT_STEP_HIP(hipMemsetAsync(A.gring[i], 0, M->ll.total * 2, sC));
+    MT_STEP_HIP(hipEventRecord(ph_start, sC));
+    // inputs of the step
+    MT_STEP_HIP(hipMemcpyAsync(A.ckpt[0], M->x0_host, act * 2, hipMemcpyHostToDevice, sW));
+    MT_STEP_HIP(hipMemcpyAsync(A.tgt, M->tgt_host, (size_t)d.D * 4, hipMemcpyHostToDevice, sW));
+    MT_STEP_HIP(hipEventRecord(x0_ready, sW));
+    h2d_bytes += (double)act * 2 + (double)d.D * 4;
+    MT_STEP_HIP(hipStreamWaitEvent(sC, x0_ready, 0));
+
+    auto xloc = [&](int i) -> uint16_t* { return (i % K == 0) ? A.ckpt[i / K] : A.act[i % 2]; };
+
+    for (size_t i = 0; i < plan.ops.size(); ++i) {
+      // weight loads whose slot and look-ahead dependencies are enqueued
+      while (next_load < plan.loads.size()) {
+        const PlanLoad& ld = plan.loads[next_load];
+        if (std::max(ld.wait_use, ld.gate_use) >= (int)i) break;
+        if (ld.wait_use >= 0) MT_STEP_HIP(hipStreamWaitEvent(sW, op_done[ld.wait_use], 0));
+        if (ld.gate_use >= 0 && ld.gate_use != ld.wait_use)
+          MT_STEP_HIP(hipStreamWaitEvent(sW, op_done[ld.gate_use], 0));
+        const Unit& u = M->units[ld.unit];
+        uint16_t* dst = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+        hipEvent_t c0 = get_ev(), c1 = get_ev();
+        MT_STEP_HIP(hipEventRecord(c0, sW));
+        MT_STEP_HIP(hipMemcpyAsync(dst, u.shadow, u.n * 2, hipMemcpyHostToDevice, sW));
+        MT_STEP_HIP(hipEventRecord(c1, sW));
+        MT_STEP_HIP(hipEventRecord(load_done[next_load], sW));
+        h2d_ev.push_back({c0, c1});
+        h2d_bytes += (double)u.n * 2;
+        ++next_load;
+      }
+      const PlanOp& op = plan.ops[i];
+      const PlanLoad& ld = plan.loads[op.load];
+      const uint16_t* w = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+      // wait for this op's weights; the gap is the exposed transfer time
+      hipEvent_t w0 = get_ev(), w1 = get_ev();
+      MT_STEP_HIP(hipEventRecord(w0, sC));
+      MT_STEP_HIP(hipStreamWaitEvent(sC, load_done[op.load], 0));
+      MT_STEP_HIP(hipEventRecord(w1, sC));
+      (op.kind == OP_BWD ? wait_ev_b : wait_ev_f).push_back({w0, w1});
+      if (op.kind == OP_FWD) {
+        const int l = op.layer;
+        MT_STEP_RUN(layer_fwd_impl(d, layer_view(M, w), xloc(l), xloc(l + 1), A.lws, A.lws_bytes,
+                                   sC, M->run.time_kernels ? &probe : nullptr));
+        if (l == L - 1) MT_STEP_HIP(hipEventRecord(ph_fwd, sC));
+      } else if (op.kind == OP_HEAD) {
+        MT_STEP_RUN(head_impl(d, w + M->hl.final_norm, w + M->hl.lm_head, xloc(L), A.tgt, inv_n,
+                              A.dy, A.head_grad + M->hl.final_norm, A.head_grad + M->hl.lm_head,
+                              A.loss, A.hws, A.hws_bytes, sC));
+        MT_STEP_HIP(hipMemcpyAsync(M->loss_host, A.loss, 4, hipMemcpyDeviceToHost, sC));
+        MT_STEP_HIP(hipEventRecord(loss_ev, sC));
+        {
+          std::lock_guard<std::mutex> lk(loss_mu);
+          loss_ready = true;
+        }
+        loss_cv.notify_all();
+        MT_STEP_HIP(hipEventRecord(ph_head, sC));
+        MT_STEP_HIP(hipEventRecord(op_done[i], sC));
+        offq.push(Offload{L, A.head_grad, M->hl.total, op_done[i], -1});
+        continue;
+      } else if (op.kind == OP_REFWD) {
+        const int l = op.layer, a = (l / K) * K;
+        const uint16_t* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
+        MT_STEP_RUN(layer_fwd_impl(d, layer_view(M, w), in, A.seg[l - a], A.lws, A.lws_bytes, sC,
+                                   M->run.time_kernels ? &probe : nullptr));
+      } else {  // OP_BWD
+        const int l = op.layer, a = (l / K) * K;
+        const uint16_t* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
+        const int r = bwd_count % NG;
+        if (bwd_count >= NG) {
+          std::unique_lock<std::mutex> lk(ring_mu);
+          ring_cv.wait(lk, [&] { return ring_enqueued >= bwd_count - NG + 1 || abort_all.load(); });
+          if (abort_all.load()) {
+            fail = MT_E_HIP;
+            goto drain;
+          }
+          MT_STEP_HIP(hipStreamWaitEvent(sC, gfree[r], 0));
+        }
+        MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
+                                   A.lws, A.lws_bytes, sC, nullptr));
+        MT_STEP_HIP(hipEventRecord(op_done[i], sC));
+        Offload o{l, A.gring[r], M->ll.total, op_done[i], r};
+        offq.push(o);
+        ++bwd_count;
+        if (l == 0) MT_STEP_HIP(hipEventRecord(ph_end, sC));
+        continue;
+      }
+      MT_STEP_HIP(hipEventRecord(op_done[i], sC));
+    }
+    // dx0 = gradient of the embedding output
+    offq.push(Offload{-1, A.dy, act, ph_end, -1});
+  }
+drain:
+  if (fail != MT_OK) {
+    abort_all = true;
+    std::lock_guard<std::mutex> lk(loss_mu);
+    loss_ready = true;
+    loss_cv.notify_all();
+  }
+  offq.push(Offload{0, nullptr, 0, nullptr, -1, true});
+  if (gthr.joinable()) gthr.join();
+  if (athr.joinable()) athr.join();
+  const hipError_t e1 = hipStreamSynchronize(sW), e2 = hipStreamSynchronize(sC),
+                   e3 = hipStreamSynchronize(sG);
+  if (fail == MT_OK && (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess)) {
+    fail = set_error(MT_E_HIP, "mt_stream_step: asynchronous HIP error: %s",
+                     hipGetErrorString(e1 != hipSuccess ? e1 : e2 != hipSuccess ? e2 : e3));
+  }
+  if (fail == MT_OK && (g_fail.load() || a_fail.load() == 1))
+    fail = set_error(MT_E_HIP, "mt_stream_step: gradient offload or optimizer thread failed");
+  if (fail == MT_OK && nonfinite_loss)
+    fail = set_error(MT_E_NONFINITE, "mt_stream_step: loss is not finite; nothing was updated");
+  if (fail == MT_OK && a_fail.load() == 2)
+    fail = set_error(MT_E_NONFINITE, "mt_stream_step: a gradient is not finite; %lld units were updated",
+                     (long long)units_updated.load());
+  *loss_out = *M->loss_host;
+  if (fail != MT_OK) {
+    if (units_updated.load() > 0) M->broken = true;
+    return fail;
+  }
+  M->step = t_step;
+  if (stats_out) {
+    mt_step_stats& s = *stats_out;
+    memset(&s, 0, sizeof(s));
+    s.fwd_ms = elapsed(ph_start, ph_fwd);
+    s.head_ms = elapsed(ph_fwd, ph_head);
+    s.bwd_ms = elapsed(ph_head, ph_end);
+    s.adam_ms = adam_ms;
+    for (auto& p : h2d_ev) s.h2d_ms += elapsed(p.first, p.second);
+    for (auto& p : d2h_ev) s.d2h_ms += elapsed(p.first, p.second);
+    for (auto& p : wait_ev_f) s.exposed_wait_fwd_ms += elapsed(p.first, p.second);
+    for (auto& p : wait_ev_b) s.exposed_wait_bwd_ms += elapsed(p.first, p.second);
+    for (int i = 0; i + 1 < probe.used; i += 2) s.probe_kernel_ms += elapsed(probe.ev[i], probe.ev[i + 1]);
+    s.probe_kernel_launches = probe.used / 2;
+    s.probe_kernel_flops = probe.flops;
+    s.h2d_bytes = h2d_bytes;
+    s.d2h_bytes = d2h_bytes;
+    s.pinned_host_bytes = M->pinned_bytes;
+    s.pageable_host_bytes = M->pageable_bytes;
+    s.device_arena_bytes = (int64_t)need;
+    s.units_updated = units_updated.load();
+    s.step_ms = std::chrono::duration<double, std::milli>(clock::now() - t_begin).count();
+    s.tail_ms = s.step_ms - (s.fwd_ms + s.head_ms + s.bwd_ms);
+  }
+  return MT_OK;
+}
+
+}  // extern "C"

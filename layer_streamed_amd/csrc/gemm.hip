@@ -304,7 +304,7 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
 const char* gemm_check(const GemmArgs& a) {
   if (a.M < 0 || a.N < 0 || a.K < 0) return "negative GEMM size";
   if (!a.A || !a.B || !a.C) return "null GEMM operand";
-  if (a.K % 8) return "GEMM K must be a multiple of 8";
+  if (a.layout != GEMM_TN && a.K % 8) return "NT/NN GEMM K must be a multiple of 8";
   auto al16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
   if (!al16(a.A) || !al16(a.B)) return "GEMM operands must be 16-byte aligned";
   if (a.lda % 8 || a.ldb % 8) return "GEMM leading dimensions must be multiples of 8";

@@ -1,0 +1,219 @@
+// Host runtime: worker pool, CPU Adam (MegaTrain blog summary, section 1:
+// the optimizer step runs entirely on the CPU), embedding gather and
+// scatter-add.  Compiled with -ffp-contract=off so every fp32 operation is
+// rounded as written (no fused multiply-add), which keeps the update
+// bit-identical to a plain fp32 evaluation of the same formula.
+#include "host.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "status.h"
+
+namespace mt {
+
+ThreadPool::ThreadPool(int threads) {
+  const int n = std::max(1, threads) - 1;
+  for (int i = 0; i < n; ++i) workers_.emplace_back([this, i] { loop(i); });
+}
+
+ThreadPool::~ThreadPool() {
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    stop_ = true;
+  }
+  cv_.notify_all();
+  for (auto& t : workers_) t.join();
+}
+
+void ThreadPool::loop(int idx) {
+  uint64_t seen = 0;
+  for (;;) {
+    const std::function<void(size_t, size_t)>* job;
+    size_t n;
+    {
+      std::unique_lock<std::mutex> lk(mu_);
+      cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+      if (stop_) return;
+      seen = gen_;
+      job = job_;
+      n = n_;
+    }
+    const size_t parts = workers_.size() + 1;
+    const size_t lo = n * (idx + 1) / parts, hi = n * (idx + 2) / parts;
+    if (lo < hi) (*job)(lo, hi);
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      if (--pending_ == 0) done_cv_.notify_all();
+    }
+  }
+}
+
+void ThreadPool::parallel_for(size_t n, const std::function<void(size_t, size_t)>& fn,
+                              size_t grain) {
+  if (n == 0) return;
+  if (workers_.empty() || n < grain) {
+    fn(0, n);
+    return;
+  }
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    job_ = &fn;
+    n_ = n;
+    pending_ = (int)workers_.size();
+    ++gen_;
+  }
+  cv_.notify_all();
+  const size_t parts = workers_.size() + 1;
+  fn(0, n / parts);
+  std::unique_lock<std::mutex> lk(mu_);
+  done_cv_.wait(lk, [&] { return pending_ == 0; });
+}
+
+AdamHp adam_hp(const mt_run_cfg& hp, int64_t step) {
+  AdamHp h;
+  h.b1 = (float)hp.beta1;
+  h.omb1 = (float)(1.0 - hp.beta1);
+  h.b2 = (float)hp.beta2;
+  h.omb2 = (float)(1.0 - hp.beta2);
+  h.bc1 = (float)(1.0 - pow(hp.beta1, (double)step));
+  h.bc2 = (float)(1.0 - pow(hp.beta2, (double)step));
+  h.lr = (float)hp.lr;
+  h.eps = (float)hp.eps;
+  return h;
+}
+
+void adam_range(float* __restrict p, float* __restrict m, float* __restrict v,
+                const uint16_t* __restrict gb, const float* __restrict gf,
+                uint16_t* __restrict shadow, size_t lo, size_t hi, const AdamHp& h) {
+  const float b1 = h.b1, omb1 = h.omb1, b2 = h.b2, omb2 = h.omb2;
+  const float bc1 = h.bc1, bc2 = h.bc2, lr = h.lr, eps = h.eps;
+  for (size_t i = lo; i < hi; ++i) {
+    const float g = gb ? host_bf2f(gb[i]) : gf[i];
+    const float mi = b1 * m[i] + omb1 * g;
+    const float vi = b2 * v[i] + omb2 * (g * g);
+    const float mh = mi / bc1;
+    const float vh = vi / bc2;
+    const float pi = p[i] - lr * mh / (sqrtf(vh) + eps);
+    m[i] = mi;
+    v[i] = vi;
+    p[i] = pi;
+    if (shadow) shadow[i] = host_f2bf(pi);
+  }
+}
+
+bool grad_finite(const uint16_t* gb, const float* gf, size_t n, ThreadPool* pool) {
+  std::vector<char> bad(pool ? pool->size() + 1 : 1, 0);
+  std::mutex mu;
+  bool any_bad = false;
+  auto body = [&](size_t lo, size_t hi) {
+    bool b = false;
+    if (gb) {
+      for (size_t i = lo; i < hi; ++i) b |= ((gb[i] & 0x7F80u) == 0x7F80u);
+    } else {
+      for (size_t i = lo; i < hi; ++i) b |= !std::isfinite(gf[i]);
+    }
+    if (b) {
+      std::lock_guard<std::mutex> lk(mu);
+      any_bad = true;
+    }
+  };
+  if (pool) pool->parallel_for(n, body);
+  else body(0, n);
+  return !any_bad;
+}
+
+void adam_parallel(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
+                   uint16_t* shadow, size_t n, const AdamHp& h, ThreadPool* pool) {
+  auto body = [&](size_t lo, size_t hi) { adam_range(p, m, v, gb, gf, shadow, lo, hi, h); };
+  if (pool) pool->parallel_for(n, body);
+  else body(0, n);
+}
+
+void embed_gather(const uint16_t* table, const int32_t* ids, size_t n_tok, size_t H,
+                  uint16_t* out, ThreadPool* pool) {
+  auto body = [&](size_t lo, size_t hi) {
+    for (size_t t = lo; t < hi; ++t)
+      memcpy(out + t * H, table + (size_t)ids[t] * H, H * sizeof(uint16_t));
+  };
+  if (pool) pool->parallel_for(n_tok, body, 64);
+  else body(0, n_tok);
+}
+
+void embed_scatter_add(const uint16_t* dx0, const int32_t* ids, size_t n_tok, size_t H,
+                       float* dE, ThreadPool* pool) {
+  // each worker owns a column slice and walks every token in order, so the
+  // summation order per element is the token order regardless of threads
+  auto body = [&](size_t c0, size_t c1) {
+    for (size_t t = 0; t < n_tok; ++t) {
+      float* row = dE + (size_t)ids[t] * H;
+      const uint16_t* src = dx0 + t * H;
+      for (size_t c = c0; c < c1; ++c) row[c] += host_bf2f(src[c]);
+    }
+  };
+  if (pool) pool->parallel_for(H, body, 64);
+  else body(0, H);
+}
+
+}  // namespace mt
+
+using namespace mt;
+
+extern "C" {
+
+void mt_run_cfg_default(mt_run_cfg* r) {
+  if (!r) return;
+  memset(r, 0, sizeof(*r));
+  r->ckpt_interval = 4;
+  r->prefetch_depth = 2;
+  r->use_slab_pool = 1;
+  r->n_slabs = 4;
+  r->mlp_chunk_tokens = 0;
+  r->head_chunk_tokens = 16384;
+  r->precision = MT_PREC_BF16;
+  r->host_threads = 16;
+  r->check_finite = 1;
+  r->serialize = 0;
+  r->host_alloc = MT_HOST_PINNED;
+  r->keep_grads = 0;
+  r->time_kernels = 1;
+  r->lr = 1e-4;
+  r->beta1 = 0.9;
+  r->beta2 = 0.999;
+  r->eps = 1e-8;
+  r->weight_decay = 0.0;
+}
+
+mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq, const void* grad,
+                       int32_t grad_dtype, uint16_t* bf16_shadow, size_t n, int64_t step,
+                       const mt_run_cfg* hp) {
+  MT_CHECK(hp, MT_E_INVALID, "mt_host_adam: null hyperparameters");
+  MT_CHECK(n == 0 || (param && exp_avg && exp_avg_sq && grad), MT_E_INVALID,
+           "mt_host_adam: null array");
+  MT_CHECK(grad_dtype == MT_DT_BF16 || grad_dtype == MT_DT_F32, MT_E_INVALID,
+           "mt_host_adam: grad_dtype must be MT_DT_BF16 or MT_DT_F32");
+  MT_CHECK(step >= 1, MT_E_INVALID, "mt_host_adam: step must be >= 1");
+  MT_CHECK(hp->weight_decay == 0.0, MT_E_INVALID, "mt_host_adam: weight decay is not supported");
+  MT_CHECK(hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && hp->eps >= 0,
+           MT_E_INVALID, "mt_host_adam: betas must be in [0, 1), eps >= 0");
+  const uint16_t* gb = grad_dtype == MT_DT_BF16 ? static_cast<const uint16_t*>(grad) : nullptr;
+  const float* gf = grad_dtype == MT_DT_F32 ? static_cast<const float*>(grad) : nullptr;
+  static ThreadPool* pool = nullptr;
+  static int pool_threads = 0;
+  static std::mutex pool_mu;
+  std::lock_guard<std::mutex> lk(pool_mu);
+  const int want = hp->host_threads > 0 ? hp->host_threads : 1;
+  if (!pool || pool_threads != want) {
+    delete pool;
+    pool = new ThreadPool(want);
+    pool_threads = want;
+  }
+  if (hp->check_finite && !grad_finite(gb, gf, n, pool))
+    return set_error(MT_E_NONFINITE, "mt_host_adam: gradient has NaN or Inf; nothing updated");
+  adam_parallel(param, exp_avg, exp_avg_sq, gb, gf, bf16_shadow, n, adam_hp(*hp, step), pool);
+  return MT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Host-side runtime pieces of libmt: a persistent worker pool, the CPU Adam
+// kernel and the embedding gather / scatter-add.  Plain C++ (no HIP).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <condition_variable>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "mt.h"
+
+namespace mt {
+
+// Fixed set of worker threads; parallel_for splits [0, n) into contiguous
+// ranges, one per worker (plus the caller), and returns when all are done.
+class ThreadPool {
+ public:
+  explicit ThreadPool(int threads);
+  ~ThreadPool();
+  int size() const { return (int)workers_.size() + 1; }
+  // grain: below this many items the caller runs fn(0, n) alone
+  void parallel_for(size_t n, const std::function<void(size_t, size_t)>& fn, size_t grain = 4096);
+
+ private:
+  void loop(int idx);
+  std::vector<std::thread> workers_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_cv_;
+  const std::function<void(size_t, size_t)>* job_ = nullptr;
+  size_t n_ = 0;
+  uint64_t gen_ = 0;
+  int pending_ = 0;
+  bool stop_ = false;
+};
+
+struct AdamHp {
+  float b1, omb1, b2, omb2, bc1, bc2, lr, eps;
+};
+AdamHp adam_hp(const mt_run_cfg& hp, int64_t step);
+
+// One Adam update over [lo, hi): grad is bf16 (gb) or fp32 (gf).
+void adam_range(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
+                uint16_t* shadow, size_t lo, size_t hi, const AdamHp& h);
+// True if every gradient value in [0, n) is finite.
+bool grad_finite(const uint16_t* gb, const float* gf, size_t n, ThreadPool* pool);
+void adam_parallel(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
+                   uint16_t* shadow, size_t n, const AdamHp& h, ThreadPool* pool);
+
+inline uint16_t host_f2bf(float f) {
+  uint32_t u;
+  __builtin_memcpy(&u, &f, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+inline float host_bf2f(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return f;
+}
+
+// x0[t] = table[ids[t]] (bf16 rows of width H).
+void embed_gather(const uint16_t* table, const int32_t* ids, size_t n_tok, size_t H,
+                  uint16_t* out, ThreadPool* pool);
+// dE[ids[t]] += dx0[t] in token order (fp32 accumulate; dE pre-zeroed).
+void embed_scatter_add(const uint16_t* dx0, const int32_t* ids, size_t n_tok, size_t H,
+                       float* dE, ThreadPool* pool);
+
+}  // namespace mt

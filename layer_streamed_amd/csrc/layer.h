@@ -1,0 +1,77 @@
+// Internal API of the stateless decoder-layer template and the LM head.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "mt.h"
+
+namespace mt {
+
+struct Dims {
+  int B, T, D, H, Hq, Hkv, d, Qd, Kvd, NQKV, F, V;
+  float eps;
+  double theta;
+  int mlp_chunk;   // tokens per MLP chunk (== D when not chunked)
+  int head_chunk;  // tokens per LM-head chunk
+};
+
+// Validates the model shape and run knobs; fills dims.  Returns nullptr or
+// a message.
+const char* make_dims(const mt_model_cfg* cfg, const mt_run_cfg* run, int batch, int seq,
+                      Dims* out);
+
+// Optional timing of one GEMM class (the gate/up projection with its SwiGLU
+// epilogue, the largest product of the layer) with event pairs.
+struct Probe {
+  std::vector<hipEvent_t> ev;  // pairs
+  int used = 0;
+  double flops = 0;
+};
+
+// Bump allocator over a caller-provided device workspace; with base ==
+// nullptr it only measures.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+size_t layer_ws_bytes(const Dims& d, int which);
+mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* x_in,
+                         uint16_t* x_out, void* ws, size_t ws_bytes, hipStream_t s, Probe* probe);
+mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* x_in,
+                         const uint16_t* dy, uint16_t* dx, const mt_layer_grad_view& g, void* ws,
+                         size_t ws_bytes, hipStream_t s, Probe* probe);
+
+// LM head: h = rms(x_L) g_f; logits = h W_out^T per token chunk; next-token
+// cross-entropy; dh, dW_out, dg_f; dx_L = rmsnorm backward.  targets: device
+// int32 [D] (-1 = none).  loss_dev: device fp32 scalar (mean over targets).
+size_t head_ws_bytes(const Dims& d);
+mt_status head_impl(const Dims& d, const uint16_t* g_f, const uint16_t* w_out,
+                    const uint16_t* x_L, const int32_t* targets, float inv_n, uint16_t* dx_L,
+                    uint16_t* dg_f, uint16_t* dw_out, float* loss_dev, void* ws, size_t ws_bytes,
+                    hipStream_t s);
+
+// Element offsets of the tensors inside one layer's flat unit (bf16 slab
+// and fp32 store share them), each aligned to 128 elements.
+struct LayerLayout {
+  size_t attn_norm, w_qkv, w_q, w_k, w_v, w_o, mlp_norm, w_gate_up, w_gate, w_up, w_down, total;
+};
+LayerLayout layer_layout(const Dims& d);
+struct HeadLayout {
+  size_t final_norm, lm_head, total;
+};
+HeadLayout head_layout(const Dims& d);
+inline size_t align128(size_t n) { return (n + 127) & ~size_t(127); }
+
+}  // namespace mt

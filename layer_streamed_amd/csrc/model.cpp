@@ -1,0 +1,225 @@
+// Host store of the model (MegaTrain blog summary, section 1: parameters
+// and optimizer states live in host memory; "Performance and Capabilities":
+// a flat layout in authoritative host storage keeps host memory linear in
+// the parameter count).
+//
+// Per unit (a layer, the head, the embedding) the fp32 master, m and v are
+// three flat arrays with one shared layout; only the bf16 copy of the
+// master (what the GPU receives) and the gradient slabs (what it sends back)
+// are pinned, since only they are DMA endpoints: 2 B/param pinned plus the
+// slab pool, instead of 14 B/param.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "model.h"
+#include "status.h"
+
+namespace mt {
+
+uint16_t* SlabPool::acquire() {
+  std::unique_lock<std::mutex> lk(mu_);
+  cv_.wait(lk, [&] { return !free_.empty(); });
+  uint16_t* p = free_.back();
+  free_.pop_back();
+  return p;
+}
+
+void SlabPool::release(uint16_t* p) {
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    free_.push_back(p);
+  }
+  cv_.notify_one();
+}
+
+bool lookup_param(const mt_model* m, const char* name, TensorRef* out) {
+  if (!name) return false;
+  const Dims& d = m->shape;
+  const size_t H = d.H;
+  const int L = m->cfg.n_layers;
+  std::string s(name);
+  if (s == "embed") { *out = {L + 1, 0, (size_t)d.V * H}; return true; }
+  if (s == "final_norm") { *out = {L, m->hl.final_norm, H}; return true; }
+  if (s == "lm_head") { *out = {L, m->hl.lm_head, (size_t)d.V * H}; return true; }
+  if (s.rfind("layers.", 0) != 0) return false;
+  const size_t dot = s.find('.', 7);
+  if (dot == std::string::npos || dot == 7) return false;
+  const std::string num = s.substr(7, dot - 7);
+  if (num.find_first_not_of("0123456789") != std::string::npos || num.size() > 6) return false;
+  const int l = atoi(num.c_str());
+  if (l < 0 || l >= L) return false;
+  const std::string t = s.substr(dot + 1);
+  const LayerLayout& ll = m->ll;
+  if (t == "attn_norm") *out = {l, ll.attn_norm, H};
+  else if (t == "w_q") *out = {l, ll.w_q, (size_t)d.Qd * H};
+  else if (t == "w_k") *out = {l, ll.w_k, (size_t)d.Kvd * H};
+  else if (t == "w_v") *out = {l, ll.w_v, (size_t)d.Kvd * H};
+  else if (t == "w_o") *out = {l, ll.w_o, H * d.Qd};
+  else if (t == "mlp_norm") *out = {l, ll.mlp_norm, H};
+  else if (t == "w_gate") *out = {l, ll.w_gate, (size_t)d.F * H};
+  else if (t == "w_up") *out = {l, ll.w_up, (size_t)d.F * H};
+  else if (t == "w_down") *out = {l, ll.w_down, H * d.F};
+  else return false;
+  return true;
+}
+
+}  // namespace mt
+
+using namespace mt;
+
+void* mt_model::host_alloc(size_t bytes, bool pinned) {
+  bytes = (bytes + 4095) & ~size_t(4095);
+  void* p = nullptr;
+  if (pinned) {
+    if (hipHostMalloc(&p, bytes, hipHostMallocDefault) != hipSuccess) return nullptr;
+    pinned_bytes += (int64_t)bytes;
+  } else {
+    p = aligned_alloc(4096, bytes);
+    if (!p) return nullptr;
+    pageable_bytes += (int64_t)bytes;
+  }
+  blocks.push_back({p, bytes, pinned});
+  return p;
+}
+
+mt_model::~mt_model() {
+  for (auto& e : events) hipEventDestroy(e);
+  for (auto& b : blocks) {
+    if (b.pinned) hipHostFree(b.p);
+    else free(b.p);
+  }
+}
+
+extern "C" {
+
+mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_model** out) {
+  MT_CHECK(cfg && run && out, MT_E_INVALID, "mt_model_create: null argument");
+  *out = nullptr;
+  Dims d;
+  if (const char* msg = make_dims(cfg, run, 1, 1, &d))
+    return set_error(MT_E_SHAPE, "mt_model_create: %s", msg);
+  MT_CHECK(run->ckpt_interval >= 1, MT_E_INVALID, "ckpt_interval must be >= 1");
+  MT_CHECK(run->prefetch_depth >= 1 && run->prefetch_depth <= 3, MT_E_INVALID,
+           "prefetch_depth must be 1, 2 or 3");
+  MT_CHECK(!run->use_slab_pool || (run->n_slabs >= 1 && run->n_slabs <= 64), MT_E_INVALID,
+           "n_slabs must be in [1, 64]");
+  MT_CHECK(run->host_threads >= 1 && run->host_threads <= 256, MT_E_INVALID,
+           "host_threads must be in [1, 256]");
+  MT_CHECK(run->host_alloc == MT_HOST_PINNED || run->host_alloc == MT_HOST_PAGEABLE, MT_E_INVALID,
+           "bad host_alloc");
+  MT_CHECK(run->weight_decay == 0.0, MT_E_INVALID, "weight decay is not supported");
+  MT_CHECK(run->lr > 0 && run->beta1 >= 0 && run->beta1 < 1 && run->beta2 >= 0 &&
+               run->beta2 < 1 && run->eps >= 0,
+           MT_E_INVALID, "bad Adam hyperparameters");
+
+  std::unique_ptr<mt_model> m(new mt_model());
+  m->cfg = *cfg;
+  m->run = *run;
+  m->shape = d;
+  m->ll = layer_layout(d);
+  m->hl = head_layout(d);
+  const int L = cfg->n_layers;
+  m->units.resize(L + 2);
+  for (int l = 0; l < L; ++l) m->units[l].n = m->ll.total;
+  m->units[L].n = m->hl.total;
+  m->units[L + 1].n = align128((size_t)d.V * d.H);
+  const bool pinned = run->host_alloc == MT_HOST_PINNED;
+
+  // bf16 copy of every unit in one pinned region
+  size_t shadow_elems = 0;
+  for (auto& u : m->units) shadow_elems += u.n;
+  uint16_t* sh = static_cast<uint16_t*>(m->host_alloc(shadow_elems * 2, pinned));
+  if (!sh) return set_error(MT_E_OOM_HOST, "mt_model_create: %s allocation of %zu bytes failed",
+                            pinned ? "pinned" : "host", shadow_elems * 2);
+  m->pool.reset(new ThreadPool(run->host_threads));
+  size_t off = 0;
+  for (auto& u : m->units) {
+    u.shadow = sh + off;
+    off += u.n;
+    u.master = static_cast<float*>(m->host_alloc(u.n * 4, false));
+    u.m = static_cast<float*>(m->host_alloc(u.n * 4, false));
+    u.v = static_cast<float*>(m->host_alloc(u.n * 4, false));
+    if (!u.master || !u.m || !u.v)
+      return set_error(MT_E_OOM_HOST, "mt_model_create: host allocation of %zu bytes failed", u.n * 4);
+    if (run->keep_grads) {
+      u.kept = static_cast<uint16_t*>(m->host_alloc(u.n * 2, false));
+      if (!u.kept) return set_error(MT_E_OOM_HOST, "mt_model_create: keep_grads allocation failed");
+    }
+    // first touch in parallel (places pages, zeroes pads and moments)
+    float* ps[3] = {u.master, u.m, u.v};
+    uint16_t* shp = u.shadow;
+    uint16_t* kp = u.kept;
+    m->pool->parallel_for(u.n, [&](size_t lo, size_t hi) {
+      for (float* p : ps) memset(p + lo, 0, (hi - lo) * 4);
+      memset(shp + lo, 0, (hi - lo) * 2);
+      if (kp) memset(kp + lo, 0, (hi - lo) * 2);
+    });
+  }
+  m->dE = static_cast<float*>(m->host_alloc((size_t)d.V * d.H * 4, false));
+  if (!m->dE) return set_error(MT_E_OOM_HOST, "mt_model_create: embedding gradient allocation failed");
+
+  // gradient slab pool: each slab fits the largest streamed unit
+  m->slab_elems = std::max(m->ll.total, m->hl.total);
+  const int n_slabs = run->use_slab_pool ? run->n_slabs : 0;
+  for (int i = 0; i < n_slabs; ++i) {
+    uint16_t* s = static_cast<uint16_t*>(m->host_alloc(m->slab_elems * 2, pinned));
+    if (!s) return set_error(MT_E_OOM_HOST, "mt_model_create: slab allocation failed");
+    m->slab_list.push_back(s);
+  }
+  m->slabs.init(m->slab_list);
+  m->slabs.set_total(m->slab_list.size());
+  *out = m.release();
+  return MT_OK;
+}
+
+void mt_model_destroy(mt_model* model) { delete model; }
+
+int64_t mt_model_step_count(const mt_model* model) { return model ? model->step : -1; }
+
+mt_status mt_model_set_param(mt_model* m, const char* name, const float* src, size_t n) {
+  MT_CHECK(m && src, MT_E_INVALID, "mt_model_set_param: null argument");
+  TensorRef r;
+  MT_CHECK(lookup_param(m, name, &r), MT_E_INVALID, "mt_model_set_param: unknown parameter '%s'",
+           name ? name : "(null)");
+  MT_CHECK(n == r.n, MT_E_SHAPE, "mt_model_set_param: '%s' has %zu elements, got %zu", name, r.n, n);
+  Unit& u = m->units[r.unit];
+  m->pool->parallel_for(n, [&](size_t lo, size_t hi) {
+    memcpy(u.master + r.off + lo, src + lo, (hi - lo) * 4);
+    memset(u.m + r.off + lo, 0, (hi - lo) * 4);
+    memset(u.v + r.off + lo, 0, (hi - lo) * 4);
+    for (size_t i = lo; i < hi; ++i) u.shadow[r.off + i] = host_f2bf(src[i]);
+  });
+  return MT_OK;
+}
+
+mt_status mt_model_get_param(const mt_model* m, const char* name, int32_t which, float* dst,
+                             size_t n) {
+  MT_CHECK(m && dst, MT_E_INVALID, "mt_model_get_param: null argument");
+  TensorRef r;
+  MT_CHECK(lookup_param(m, name, &r), MT_E_INVALID, "mt_model_get_param: unknown parameter '%s'",
+           name ? name : "(null)");
+  MT_CHECK(n == r.n, MT_E_SHAPE, "mt_model_get_param: '%s' has %zu elements, got %zu", name, r.n, n);
+  const Unit& u = m->units[r.unit];
+  const bool embed = r.unit == m->cfg.n_layers + 1;
+  switch (which) {
+    case MT_GET_MASTER: memcpy(dst, u.master + r.off, n * 4); break;
+    case MT_GET_M: memcpy(dst, u.m + r.off, n * 4); break;
+    case MT_GET_V: memcpy(dst, u.v + r.off, n * 4); break;
+    case MT_GET_SHADOW:
+      for (size_t i = 0; i < n; ++i) dst[i] = host_bf2f(u.shadow[r.off + i]);
+      break;
+    case MT_GET_GRAD:
+      MT_CHECK(m->run.keep_grads, MT_E_STATE, "mt_model_get_param: gradients need keep_grads = 1");
+      if (embed) memcpy(dst, m->dE + r.off, n * 4);
+      else
+        for (size_t i = 0; i < n; ++i) dst[i] = host_bf2f(u.kept[r.off + i]);
+      break;
+    default: return set_error(MT_E_INVALID, "mt_model_get_param: bad 'which' %d", which);
+  }
+  return MT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// The host-resident model: the authoritative flat store of fp32 master
+// weights and Adam moments, the pinned bf16 copy that streams to the GPU,
+// the pinned gradient slab pool, and the per-step scratch the engine uses.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <condition_variable>
+#include <deque>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "host.h"
+#include "layer.h"
+#include "mt.h"
+
+namespace mt {
+
+// Units: 0..L-1 layers, L = head (final norm + LM head), L+1 = embedding.
+struct Unit {
+  size_t n = 0;               // elements (with alignment padding)
+  float* master = nullptr;    // fp32, pageable
+  float* m = nullptr;
+  float* v = nullptr;
+  uint16_t* shadow = nullptr; // bf16 copy, inside the pinned shadow region
+  uint16_t* kept = nullptr;   // last step's bf16 gradient (keep_grads)
+};
+
+struct TensorRef {
+  int unit;
+  size_t off, n;
+};
+
+// Pool of pinned gradient slabs shared by the offload and optimizer threads.
+class SlabPool {
+ public:
+  void init(std::vector<uint16_t*> slabs) { free_ = std::move(slabs); }
+  uint16_t* acquire();
+  void release(uint16_t* p);
+  size_t capacity() const { return total_; }
+  void set_total(size_t t) { total_ = t; }
+
+ private:
+  std::mutex mu_;
+  std::condition_variable cv_;
+  std::vector<uint16_t*> free_;
+  size_t total_ = 0;
+};
+
+struct HostBlock {  // one host allocation
+  void* p = nullptr;
+  size_t bytes = 0;
+  bool pinned = false;
+};
+
+}  // namespace mt
+
+struct mt_model {
+  mt_model_cfg cfg{};
+  mt_run_cfg run{};
+  mt::Dims shape{};  // model dims (B = T = 1); per-step dims are rebuilt
+  mt::LayerLayout ll{};
+  mt::HeadLayout hl{};
+  std::vector<mt::Unit> units;
+  std::vector<mt::HostBlock> blocks;
+  size_t slab_elems = 0;
+  mt::SlabPool slabs;
+  std::vector<uint16_t*> slab_list;
+  std::unique_ptr<mt::ThreadPool> pool;
+  float* dE = nullptr;          // fp32 embedding gradient [V, H]
+  // pinned per-step staging, grown on demand
+  uint16_t* x0_host = nullptr;
+  uint16_t* dx0_host = nullptr;
+  int32_t* tgt_host = nullptr;
+  float* loss_host = nullptr;
+  size_t staging_tokens = 0;
+  std::vector<hipEvent_t> events;  // grown on demand
+  int64_t step = 0;
+  bool broken = false;
+  int64_t pinned_bytes = 0, pageable_bytes = 0;
+
+  void* host_alloc(size_t bytes, bool pinned);
+  ~mt_model();
+};
+
+namespace mt {
+bool lookup_param(const mt_model* m, const char* name, TensorRef* out);
+}

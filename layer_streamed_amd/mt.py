@@ -52,7 +52,7 @@ class RunCfg(C.Structure):
         "ckpt_interval", "prefetch_depth", "use_slab_pool", "n_slabs", "mlp_chunk_tokens",
         "head_chunk_tokens", "precision", "host_threads", "check_finite", "serialize",
         "host_alloc", "keep_grads", "time_kernels")] + [
-        (n, C.c_float) for n in ("lr", "beta1", "beta2", "eps", "weight_decay")]
+        (n, C.c_double) for n in ("lr", "beta1", "beta2", "eps", "weight_decay")]
 
 
 class LayerView(C.Structure):
@@ -111,6 +111,7 @@ _SIGS = {
     "mt_host_adam": (_I32, _P, _P, _P, _P, _I32, _P, _SZ, _I64, _P),
     "mt_run_cfg_default": (None, _P),
     "mt_op_rmsnorm_bwd_workspace": (_SZ, _I32, _I32),
+    "mt_debug_plan": (_I32, _I32, _I32, _I32, _P, _SZ, _P),
 }
 FN = {}
 for _name, (_res, *_args) in _SIGS.items():
@@ -212,3 +213,103 @@ def attn_bwd(qkv, o, lse, dout, delta, dqkv, batch, seq, n_heads, n_kv_heads, he
 def ce_rows(logits, target, dlogits, loss_part, rows, vocab, inv_n, stream=None):
     check(call("mt_op_ce_rows", ptr(logits), ptr(target), ptr(dlogits), ptr(loss_part), rows,
                vocab, inv_n, stream_handle(stream)), "mt_op_ce_rows")
+
+
+# ------------------------------------------------------------- layer / model
+class GradView(C.Structure):
+    _fields_ = LayerView._fields_
+
+
+def layer_workspace_bytes(mcfg, rcfg, batch, seq, which) -> int:
+    return call("mt_layer_workspace_bytes", C.byref(mcfg), C.byref(rcfg), batch, seq, which)
+
+
+def layer_fwd(mcfg, rcfg, view, x_in, x_out, batch, seq, ws, stream=None):
+    check(call("mt_layer_fwd", C.byref(mcfg), C.byref(rcfg), C.byref(view), ptr(x_in),
+               ptr(x_out), batch, seq, ptr(ws), ws.numel() * ws.element_size(),
+               stream_handle(stream)), "mt_layer_fwd")
+
+
+def layer_recompute_bwd(mcfg, rcfg, view, x_in, dy, dx, gview, batch, seq, ws, stream=None):
+    check(call("mt_layer_recompute_bwd", C.byref(mcfg), C.byref(rcfg), C.byref(view), ptr(x_in),
+               ptr(dy), ptr(dx), C.byref(gview), batch, seq, ptr(ws),
+               ws.numel() * ws.element_size(), stream_handle(stream)), "mt_layer_recompute_bwd")
+
+
+def debug_plan(n_layers, ckpt_interval, prefetch_depth):
+    """The engine's schedule as (status, ops [n,3], loads [n,6], n_slots)."""
+    import numpy as np
+    cap = 64 * (n_layers + 2) * 4 + 64
+    out = np.zeros(cap, np.int32)
+    counts = np.zeros(3, np.int32)
+    st = call("mt_debug_plan", n_layers, ckpt_interval, prefetch_depth, ptr(out), cap, ptr(counts))
+    n_ops, n_loads, n_slots = (int(c) for c in counts)
+    ops = out[: 3 * n_ops].reshape(n_ops, 3).copy()
+    loads = out[3 * n_ops: 3 * n_ops + 6 * n_loads].reshape(n_loads, 6).copy()
+    return st, ops, loads, n_slots
+
+
+class Model:
+    """Host-resident model (mt_model) plus the streamed training step."""
+
+    def __init__(self, shape, **run_kw):
+        self.shape = shape
+        self.mcfg = model_cfg(shape)
+        kw = dict(ckpt_interval=shape.ckpt_interval, mlp_chunk_tokens=shape.mlp_chunk_tokens,
+                  lr=shape.lr, beta1=shape.beta1, beta2=shape.beta2, eps=shape.adam_eps)
+        kw.update(run_kw)
+        self.rcfg = run_cfg(**kw)
+        h = C.c_void_p()
+        check(call("mt_model_create", C.byref(self.mcfg), C.byref(self.rcfg), C.byref(h)),
+              "mt_model_create")
+        self.h = h
+
+    def close(self):
+        if self.h:
+            call("mt_model_destroy", self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_param(self, name, arr):
+        import numpy as np
+        a = np.ascontiguousarray(arr, dtype=np.float32).reshape(-1)
+        check(call("mt_model_set_param", self.h, name.encode(), ptr(a), a.size),
+              f"mt_model_set_param({name})")
+
+    def set_params(self, weights):
+        for n, a in weights.items():
+            self.set_param(n, a)
+
+    def get(self, name, which=GET_MASTER, shape=None):
+        import numpy as np
+        from synth import param_shapes
+        shp = shape or param_shapes(self.shape)[name]
+        out = np.empty(int(np.prod(shp)), np.float32)
+        check(call("mt_model_get_param", self.h, name.encode(), which, ptr(out), out.size),
+              f"mt_model_get_param({name})")
+        return out.reshape(shp)
+
+    @property
+    def step_count(self):
+        return call("mt_model_step_count", self.h)
+
+    def arena_bytes(self, batch, seq):
+        return call("mt_stream_arena_bytes", self.h, batch, seq)
+
+    def step(self, tokens, arena, streams):
+        """One streamed training step; returns (loss, stats dict)."""
+        import numpy as np
+        ids = np.ascontiguousarray(tokens, dtype=np.int32)
+        B, T = ids.shape
+        loss = C.c_float()
+        stats = StepStats()
+        handles = (C.c_void_p * 3)(*[s.cuda_stream for s in streams])
+        check(call("mt_stream_step", self.h, ptr(ids), B, T, ptr(arena),
+                   arena.numel() * arena.element_size(), handles, C.byref(loss),
+                   C.byref(stats)), "mt_stream_step")
+        return float(loss.value), stats.as_dict()

@@ -136,11 +136,14 @@ def _is_gain(name: str) -> bool:
 
 def make_weights(shape: ModelShape, seed: int = 0, std: float = 0.02,
                  names: list[str] | None = None,
-                 dtype=np.float32) -> dict[str, np.ndarray]:
+                 dtype=np.float32, bf16_exact: bool = False) -> dict[str, np.ndarray]:
     """Seeded weights: matrices ~ N(0, std^2), gains = 1.
 
     ``names`` restricts the draw to a subset (each tensor has its own stream,
     so a subset draws exactly the values the full set would).
+    ``bf16_exact`` clears the low 16 bits of every float32 draw (truncation
+    toward zero), so the values are exactly representable in bfloat16 and an
+    fp32 master and its 16-bit copy start out equal.
     """
     shapes = param_shapes(shape)
     order = param_names(shape)
@@ -153,7 +156,10 @@ def make_weights(shape: ModelShape, seed: int = 0, std: float = 0.02,
             out[n] = np.ones(shp, dtype=dtype)
         else:
             rng = np.random.default_rng([seed, index[n]])
-            out[n] = (rng.standard_normal(shp) * std).astype(dtype)
+            a = (rng.standard_normal(shp) * std).astype(np.float32)
+            if bf16_exact:
+                a = (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+            out[n] = a.astype(dtype)
     return out
 
 

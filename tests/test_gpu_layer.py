@@ -1,0 +1,104 @@
+"""Layer-template parity on the GPU: mt_layer_fwd and mt_layer_recompute_bwd
+against the oracle's layer_forward / layer_backward on the same seeded
+weights and inputs (bf16 on the GPU, fp32 in the oracle)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import decoder as D
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2  # relative Frobenius, bf16 storage with fp32 accumulation
+
+
+def _env():
+    import torch
+    from layer_streamed_amd import mt
+    assert torch.cuda.is_available()
+    return torch, mt
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def _layer_case(shape, B, T, seed, mlp_chunk=0, x_scale=1.0):
+    torch, mt = _env()
+    names = synth.layer_param_names(0)
+    w = synth.make_weights(shape, seed=seed, names=names)
+    w = {n.split(".")[-1]: v for n, v in w.items()}
+    rng = np.random.default_rng(seed + 1)
+    # gains away from 1 so their gradients are exercised
+    w["attn_norm"] = (1 + 0.1 * rng.standard_normal(shape.hidden)).astype(np.float32)
+    w["mlp_norm"] = (1 + 0.1 * rng.standard_normal(shape.hidden)).astype(np.float32)
+    wb = {k: oracle.bf16_round(v) for k, v in w.items()}  # the values the GPU holds
+    x = oracle.bf16_round((rng.standard_normal((B, T, shape.hidden)) * x_scale).astype(np.float32))
+    dy = oracle.bf16_round((rng.standard_normal((B, T, shape.hidden)) * 1e-2).astype(np.float32))
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+
+    W = {
+        "attn_norm": dev(wb["attn_norm"]),
+        "w_qkv": dev(np.concatenate([wb["w_q"], wb["w_k"], wb["w_v"]])),
+        "w_o": dev(wb["w_o"]),
+        "mlp_norm": dev(wb["mlp_norm"]),
+        "w_gate_up": dev(np.concatenate([wb["w_gate"], wb["w_up"]])),
+        "w_down": dev(wb["w_down"]),
+    }
+    view = mt.LayerView(*[W[k].data_ptr() for k, _ in mt.LayerView._fields_])
+    G = {k: torch.full_like(v, float("nan")) for k, v in W.items()}
+    gview = mt.GradView(*[G[k].data_ptr() for k, _ in mt.GradView._fields_])
+    mcfg = mt.model_cfg(shape)
+    rcfg = mt.run_cfg(mlp_chunk_tokens=mlp_chunk)
+    X = dev(x.reshape(B * T, -1))
+    Y = torch.empty_like(X)
+    ws = torch.empty(mt.layer_workspace_bytes(mcfg, rcfg, B, T, 1), dtype=torch.uint8, device="cuda")
+    mt.layer_fwd(mcfg, rcfg, view, X, Y, B, T, ws)
+    DX = dev(dy.reshape(B * T, -1))  # dy in, dx out (aliasing allowed)
+    mt.layer_recompute_bwd(mcfg, rcfg, view, X, DX, DX, gview, B, T, ws)
+    torch.cuda.synchronize()
+    cos, sin = D.rope_cos_sin(T, shape.head_dim, shape.rope_theta, np.float32)
+    y_ref, saved = D.layer_forward(wb, x, shape, cos, sin)
+    dx_ref, g_ref = D.layer_backward(wb, saved, dy, shape, cos, sin)
+    out = {
+        "y": (Y.float().cpu().numpy(), y_ref.reshape(B * T, -1)),
+        "dx": (DX.float().cpu().numpy(), dx_ref.reshape(B * T, -1)),
+        "attn_norm": (G["attn_norm"].float().cpu().numpy(), g_ref["attn_norm"]),
+        "w_qkv": (G["w_qkv"].float().cpu().numpy(),
+                  np.concatenate([g_ref["w_q"], g_ref["w_k"], g_ref["w_v"]])),
+        "w_o": (G["w_o"].float().cpu().numpy(), g_ref["w_o"]),
+        "mlp_norm": (G["mlp_norm"].float().cpu().numpy(), g_ref["mlp_norm"]),
+        "w_gate_up": (G["w_gate_up"].float().cpu().numpy(),
+                      np.concatenate([g_ref["w_gate"], g_ref["w_up"]])),
+        "w_down": (G["w_down"].float().cpu().numpy(), g_ref["w_down"]),
+    }
+    return out
+
+
+CASES = [
+    ("tiny", synth.CONFIGS["tiny-2l-h256"], 2, 128, 0),
+    ("tiny-ragged-T", synth.CONFIGS["tiny-2l-h256"], 3, 77, 0),
+    ("tiny-chunked-mlp", synth.CONFIGS["tiny-2l-h256"], 2, 100, 64),
+    ("gqa5-d128", synth.ModelShape(name="gqa5", n_layers=1, hidden=640, n_heads=10,
+                                   n_kv_heads=2, head_dim=128, ffn=1536, vocab=1024), 2, 192, 0),
+]
+
+
+@pytest.mark.parametrize("name,shape,B,T,chunk", CASES, ids=[c[0] for c in CASES])
+def test_layer_forward_and_recompute_backward(name, shape, B, T, chunk):
+    out = _layer_case(shape, B, T, seed=11, mlp_chunk=chunk)
+    for k, (gpu, ref) in out.items():
+        assert np.isfinite(gpu).all(), k
+        assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))
+
+
+def test_layer_7b_shape_one_sequence():
+    """One Qwen2.5-7B-shaped layer (H 3584, 28/4 heads, F 18944) on one
+    sequence of 256 tokens against the oracle."""
+    shape = synth.CONFIGS["qwen2.5-7b-b16-t1024"]
+    out = _layer_case(shape, 1, 256, seed=3)
+    for k, (gpu, ref) in out.items():
+        assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))

@@ -217,3 +217,82 @@ def test_cross_entropy_rows(rows, V):
     np.testing.assert_allclose(lp.cpu().numpy(), ref_l, rtol=1e-5, atol=1e-5)
     assert rel_fro(to_np(dl), ref_d) < 5e-3
     assert not to_np(dl)[tgt < 0].any()
+
+
+ATTN_CASES = [
+    # B, T, Hq, Hkv, d
+    (2, 128, 4, 2, 64),     # the small parity model
+    (1, 200, 6, 2, 128),    # ragged T, group 3
+    (2, 300, 10, 2, 64),    # ragged T, group 5
+    (1, 1024, 28, 4, 128),  # 7B heads, group 7
+    (3, 1, 4, 4, 128),      # single token
+]
+
+
+def _attn_inputs(B, T, Hq, Hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    qkv = oracle.bf16_round(_rand(rng, (B * T, (Hq + 2 * Hkv) * d)))
+    q = qkv[:, : Hq * d].reshape(B, T, Hq, d)
+    k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(B, T, Hkv, d)
+    v = qkv[:, (Hq + Hkv) * d:].reshape(B, T, Hkv, d)
+    return qkv, q, k, v
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,d", ATTN_CASES)
+def test_attention_forward_backward(B, T, Hq, Hkv, d):
+    torch, mt = _torch(), _mt()
+    qkv, q, k, v = _attn_inputs(B, T, Hq, Hkv, d, T + Hq)
+    QKV = bf16_dev(qkv)
+    O = torch.empty((B * T, Hq * d), device="cuda", dtype=torch.bfloat16)
+    LSE = torch.empty((B, Hq, T), device="cuda", dtype=torch.float32)
+    mt.attn_fwd(QKV, O, LSE, B, T, Hq, Hkv, d)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = D.causal_attention(q, k, v)
+    assert rel_fro(to_np(O), o_ref.reshape(B * T, Hq * d)) < 1e-2
+    np.testing.assert_allclose(LSE.cpu().numpy(), lse_ref, rtol=0, atol=2e-3)
+    rng = np.random.default_rng(T)
+    do = oracle.bf16_round(_rand(rng, (B * T, Hq * d)))
+    DO = bf16_dev(do)
+    delta = torch.empty((B, Hq, T), device="cuda", dtype=torch.float32)
+    DQKV = torch.full((B * T, (Hq + 2 * Hkv) * d), float("nan"), device="cuda", dtype=torch.bfloat16)
+    mt.attn_bwd(QKV, O, LSE, DO, delta, DQKV, B, T, Hq, Hkv, d)
+    torch.cuda.synchronize()
+    o_gpu = to_np(O).reshape(B, T, Hq, d)
+    dq, dk, dv = D.causal_attention_backward(q, k, v, o_gpu, LSE.cpu().numpy(),
+                                             do.reshape(B, T, Hq, d))
+    out = to_np(DQKV)
+    assert np.isfinite(out).all()
+    # exact dq and dk vanish at T = 1 (P = 1, dS = 0): floor the denominator
+    # at a small fraction of |dO| so rounding noise is compared absolutely
+    floor = 1e-2 * np.linalg.norm(do)
+
+    def err(a, b):
+        return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), floor))
+
+    assert err(out[:, : Hq * d], dq.reshape(B * T, -1)) < 2e-2
+    assert err(out[:, Hq * d:(Hq + Hkv) * d], dk.reshape(B * T, -1)) < 2e-2
+    assert err(out[:, (Hq + Hkv) * d:], dv.reshape(B * T, -1)) < 2e-2
+
+
+def test_attention_forward_32k_sampled_heads():
+    """Long-context shape (T = 32768, 7B heads): heads 0 and 27 against the
+    oracle computed on those heads alone."""
+    torch, mt = _torch(), _mt()
+    B, T, Hq, Hkv, d = 1, 32768, 28, 4, 128
+    g = torch.Generator(device="cuda").manual_seed(5)
+    QKV = torch.randn((T, (Hq + 2 * Hkv) * d), device="cuda", generator=g).to(torch.bfloat16)
+    O = torch.empty((T, Hq * d), device="cuda", dtype=torch.bfloat16)
+    LSE = torch.empty((1, Hq, T), device="cuda", dtype=torch.float32)
+    mt.attn_fwd(QKV, O, LSE, B, T, Hq, Hkv, d)
+    torch.cuda.synchronize()
+    qkv = QKV.float().cpu().numpy()
+    for h in (0, 27):
+        gkv = h * Hkv // Hq
+        q = qkv[:, h * d:(h + 1) * d].reshape(1, T, 1, d)
+        k = qkv[:, (Hq + gkv) * d:(Hq + gkv + 1) * d].reshape(1, T, 1, d)
+        v = qkv[:, (Hq + Hkv + gkv) * d:(Hq + Hkv + gkv + 1) * d].reshape(1, T, 1, d)
+        rows = np.r_[0:64, T - 2048:T]
+        # rows of a causal attention depend only on keys up to the row
+        o_ref, lse_ref = D.causal_attention(q, k, v, row_block=2048)
+        assert rel_fro(to_np(O)[rows, h * d:(h + 1) * d], o_ref[0, rows, 0]) < 1e-2
+        np.testing.assert_allclose(LSE[0, h].cpu().numpy()[rows], lse_ref[0, 0, rows], atol=2e-3)

@@ -1,0 +1,104 @@
+"""Host-side pieces of libmt that run without a GPU: the library loads and
+exports every entry point its headers declare, the CPU Adam matches the
+oracle's Adam bit for bit, and argument validation rejects bad calls
+without touching state."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import decoder as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _mt():
+    from layer_streamed_amd import mt
+    return mt
+
+
+def _declared():
+    names = set()
+    for h in ("mt.h", "mt_ops.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(mt_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    mt = _mt()
+    lib = C.CDLL(mt.LIB_PATH)
+    missing = [n for n in sorted(_declared()) if not hasattr(lib, n)]
+    assert not missing, missing
+    assert _declared() <= set(mt.EXPORTED)
+
+
+def _adam(p, m, v, g, step, dtype, shadow=True, **hp):
+    mt = _mt()
+    cfg = mt.run_cfg(**hp)
+    sh = np.zeros(p.size, np.uint16) if shadow else None
+    gbuf = D.bf16_bits(g) if dtype == mt.DT_BF16 else np.ascontiguousarray(g, np.float32)
+    st = mt.call("mt_host_adam", mt.ptr(p), mt.ptr(m), mt.ptr(v), mt.ptr(gbuf), dtype,
+                 mt.ptr(sh), p.size, step, C.byref(cfg))
+    return st, sh
+
+
+@pytest.mark.parametrize("dtype", [0, 1], ids=["bf16_grad", "f32_grad"])
+@pytest.mark.parametrize("threads", [1, 7])
+def test_host_adam_bitwise_equals_oracle(dtype, threads):
+    rng = np.random.default_rng(1 + dtype)
+    n = 100_003
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = (rng.random(n) * 1e-6).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    g[:50] = 0
+    if dtype == 0:
+        g = D.bf16_round(g)
+    for step in (1, 3):
+        rp, rm, rv = D.adam_update(p.copy(), m.copy(), v.copy(), g, step, 1e-4, 0.9, 0.999, 1e-8)
+        pp, mm, vv = p.copy(), m.copy(), v.copy()
+        st, sh = _adam(pp, mm, vv, g, step, dtype, host_threads=threads)
+        assert st == 0
+        np.testing.assert_array_equal(mm, rm)
+        np.testing.assert_array_equal(vv, rv)
+        np.testing.assert_array_equal(pp, rp)
+        np.testing.assert_array_equal(sh, D.bf16_bits(rp))
+
+
+def test_host_adam_refuses_nonfinite_and_leaves_state():
+    mt = _mt()
+    n = 9000
+    p = np.ones(n, np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    g = np.full(n, 0.5, np.float32)
+    g[4321] = np.nan
+    st, sh = _adam(p, m, v, g, 1, mt.DT_F32, check_finite=1)
+    assert st == mt.MT_E_NONFINITE
+    assert "NaN" in mt.last_error()
+    assert (p == 1).all() and not m.any() and not v.any() and not sh.any()
+
+
+def test_host_adam_validates_arguments():
+    mt = _mt()
+    p = np.ones(8, np.float32)
+    m = np.zeros(8, np.float32)
+    v = np.zeros(8, np.float32)
+    g = np.ones(8, np.float32)
+    st, _ = _adam(p, m, v, g, 0, mt.DT_F32)
+    assert st == mt.MT_E_INVALID
+    st, _ = _adam(p, m, v, g, 1, 7)
+    assert st == mt.MT_E_INVALID
+    cfg = mt.run_cfg()
+    assert mt.call("mt_host_adam", None, None, None, None, 1, None, 8, 1, C.byref(cfg)) == mt.MT_E_INVALID
+    assert (p == 1).all()
+
+
+def test_run_cfg_defaults():
+    r = _mt().run_cfg()
+    assert r.ckpt_interval == 4 and r.prefetch_depth == 2 and r.use_slab_pool == 1
+    assert r.lr == 1e-4 and r.beta1 == 0.9 and r.beta2 == 0.999 and r.eps == 1e-8

@@ -1,0 +1,90 @@
+"""The engine's stream schedule, checked on the CPU for hazards.
+
+The schedule (mt_debug_plan) is what mt_stream_step replays with HIP
+events.  These tests walk it as a discrete-event system: every layer runs
+forward once and backward once, every compute op finds its weights loaded,
+no weight slot is overwritten while an earlier occupant still has a reader,
+loads never wait on compute that comes after their own first use (no
+deadlock), and no load runs more than `depth` ops ahead.
+"""
+import pytest
+
+FWD, HEAD, REFWD, BWD = 0, 1, 2, 3
+
+
+def _plan(L, K, depth):
+    from layer_streamed_amd import mt
+    return mt.debug_plan(L, K, depth)
+
+
+@pytest.mark.parametrize("L", [1, 2, 5, 28])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 7, 28])
+@pytest.mark.parametrize("depth", [1, 2, 3])
+def test_plan_is_hazard_free(L, K, depth):
+    if K > L:
+        K = L
+    st, ops, loads, n_slots = _plan(L, K, depth)
+    assert st == 0
+    kinds = ops[:, 0].tolist()
+    # forward of every layer in order, then the head
+    assert kinds[:L] == [FWD] * L and ops[:L, 1].tolist() == list(range(L))
+    assert kinds[L] == HEAD
+    # backward: segments from the last, each re-forwarding all but its last
+    # layer from the checkpoint, then backward in reverse
+    rest = ops[L + 1:]
+    expect = []
+    for a in reversed(range(0, L, K)):
+        e = min(a + K, L)
+        expect += [(REFWD, l) for l in range(a, e - 1)]
+        expect += [(BWD, l) for l in reversed(range(a, e))]
+    assert [(int(k), int(l)) for k, l, _ in rest] == expect
+    # every op reads a load of its own unit, inside that load's live range
+    for i, (kind, layer, load) in enumerate(ops):
+        unit, slot, first, last, wait, gate = loads[load]
+        assert unit == (L if kind == HEAD else layer)
+        assert first <= i <= last
+    # loads are issued in order of first use; dependencies precede the use
+    firsts = loads[:, 2].tolist()
+    assert firsts == sorted(firsts)
+    for unit, slot, first, last, wait, gate in loads:
+        assert wait < first and gate < first
+        assert gate == (first - depth if first - depth >= 0 else -1)
+    # slot reuse: the next occupant waits for the last reader of the previous
+    by_slot = {}
+    for j, (unit, slot, first, last, wait, gate) in enumerate(loads):
+        if slot == -2:
+            assert unit == L
+            continue
+        assert 0 <= slot < n_slots
+        if slot in by_slot:
+            prev = loads[by_slot[slot]]
+            assert wait >= prev[3], (j, slot)
+            assert first > prev[3]
+        by_slot[slot] = j
+
+
+def test_plan_single_stream_replay_never_reads_stale_weights():
+    """Replay the plan as the executor does on one in-order stream and track
+    which unit each slot holds at every compute op."""
+    L, K, depth = 28, 4, 2
+    st, ops, loads, n_slots = _plan(L, K, depth)
+    assert st == 0
+    holds = {}
+    nxt = 0
+    for i, (kind, layer, load) in enumerate(ops):
+        while nxt < len(loads) and max(loads[nxt][4], loads[nxt][5]) < i:
+            unit, slot = loads[nxt][0], loads[nxt][1]
+            holds[slot] = (unit, nxt)
+            nxt += 1
+        unit, slot = loads[load][0], loads[load][1]
+        assert holds[slot] == (unit, load), (i, kind, layer)
+
+
+def test_plan_counts_match_the_method():
+    """Per step: L forward loads + head + L backward loads; the forward uses
+    each layer once, recompute+backward once, re-forward (K-1)/K of them."""
+    L, K = 28, 4
+    st, ops, loads, _ = _plan(L, K, 2)
+    assert len(loads) == 2 * L + 1
+    assert (ops[:, 0] == REFWD).sum() == L - L // K
+    assert (ops[:, 0] == BWD).sum() == L
