@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--prefetch-depth", type=int, default=2)
     ap.add_argument("--no-slab-pool", action="store_true")
     ap.add_argument("--ckpt-interval", type=int, default=0)
+    # Adam is host-memory-bandwidth bound from about 4 threads on; the rest
+    # of the cores stay free for the enqueue and offload threads
+    ap.add_argument("--host-threads", type=int, default=8)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the "
@@ -129,7 +132,7 @@ def main():
     t0 = time.perf_counter()
     model = mt.Model(shape, prefetch_depth=args.prefetch_depth,
                      use_slab_pool=0 if args.no_slab_pool else 1, check_finite=1,
-                     time_kernels=1, host_threads=min(16, os.cpu_count() or 16))
+                     time_kernels=1, host_threads=args.host_threads)
     log(f"model created in {time.perf_counter() - t0:.1f}s")
     t0 = time.perf_counter()
     init_weights(model, shape, seed=0)
@@ -154,7 +157,9 @@ def main():
         log(f"step {i}: loss {loss:.4f} {1e3 * (time.perf_counter() - ts):.0f} ms "
             f"fwd {st['fwd_ms']:.0f} head {st['head_ms']:.0f} bwd {st['bwd_ms']:.0f} "
             f"tail {st['tail_ms']:.0f} adam {st['adam_ms']:.0f} exposed "
-            f"{st['exposed_wait_fwd_ms']:.0f}/{st['exposed_wait_bwd_ms']:.0f} ms")
+            f"{st['exposed_wait_fwd_ms']:.0f}/{st['exposed_wait_bwd_ms']:.0f} ms; host waits "
+            f"ring {st['host_ring_wait_ms']:.0f} slab {st['host_slab_wait_ms']:.0f} "
+            f"op {st['host_op_wait_ms']:.0f} adam-idle {st['host_adam_idle_ms']:.0f} ms")
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = 1e3 * elapsed / args.steps
@@ -225,7 +230,8 @@ def main():
         "mfma_frac_executed": round(f_exec / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "phases_ms": {k: round(float(np.mean([s[k] for s in stats])), 2) for k in
                       ("fwd_ms", "head_ms", "bwd_ms", "tail_ms", "adam_ms",
-                       "exposed_wait_fwd_ms", "exposed_wait_bwd_ms")},
+                       "exposed_wait_fwd_ms", "exposed_wait_bwd_ms", "host_ring_wait_ms",
+                       "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms")},
         "link": {"h2d_bytes": h2d, "d2h_bytes": d2h,
                  "h2d_GBps_while_copying": round(h2d / max(h2d_ms, 1e-9) / 1e6, 2),
                  "d2h_GBps_while_copying": round(d2h / max(d2h_ms, 1e-9) / 1e6, 2),

@@ -72,7 +72,7 @@ typedef struct {
   int32_t ckpt_interval;     /* K >= 1 (default 4) */
   int32_t prefetch_depth;    /* weight slots ahead of compute: 1, 2 or 3 (default 2) */
   int32_t use_slab_pool;     /* 1: recycle pinned gradient slabs (default); 0: one slab per unit */
-  int32_t n_slabs;           /* pool size when use_slab_pool (default 4) */
+  int32_t n_slabs;           /* pool size when use_slab_pool (default 8) */
   int32_t mlp_chunk_tokens;  /* 0: whole token set; else MLP runs over chunks of this many tokens */
   int32_t head_chunk_tokens; /* tokens per LM-head chunk (default 16384) */
   int32_t precision;         /* MT_PREC_BF16 | MT_PREC_FP32_DEBUG */
@@ -111,6 +111,10 @@ typedef struct {
   int64_t probe_kernel_launches;
   int64_t pinned_host_bytes, pageable_host_bytes, device_arena_bytes;
   int64_t units_updated;    /* units whose Adam update completed this step */
+  /* host-side waits (ms): compute enqueue blocked on a free gradient ring
+   * buffer; offload thread blocked on a free slab and on backward ops;
+   * optimizer thread idle waiting for a landed gradient */
+  double host_ring_wait_ms, host_slab_wait_ms, host_op_wait_ms, host_adam_idle_ms;
 } mt_step_stats;
 
 typedef struct mt_model mt_model;
@@ -208,7 +212,7 @@ mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq,
                        uint16_t* bf16_shadow, size_t n, int64_t step,
                        const mt_run_cfg* hp);
 
-/* Defaults for every knob (ckpt 4, depth 2, pool of 4, lr 1e-4, betas
+/* Defaults for every knob (ckpt 4, depth 2, pool of 8, lr 1e-4, betas
  * 0.9/0.999, eps 1e-8, bf16, 16 host threads, pinned host memory). */
 void mt_run_cfg_default(mt_run_cfg* out);
 

@@ -81,6 +81,13 @@ mt_status mt_op_ce_rows(const float* logits, const int32_t* target, void* dlogit
                         float* loss_part, int32_t rows, int32_t vocab, float inv_n,
                         void* stream);
 
+/* Device -> host copy into pinned host memory (hipHostMalloc) by a kernel
+ * of `blocks` workgroups of 256 threads, so the gradient offload (MegaTrain
+ * listing page, Fig. 3, stream G) occupies a bounded part of the GPU.
+ * bytes and both addresses must be multiples of 16. */
+mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t blocks,
+                         void* stream);
+
 /* The stream schedule of mt_stream_step for n_layers, checkpoint interval
  * and prefetch depth, as plain integers so its hazards can be checked
  * without a GPU.  out receives, per compute op, (kind, layer, load) with

@@ -28,7 +28,7 @@ HIP_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 CXX_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-march=x86-64-v3", "-pthread", "-ffp-contract=off",
+    "-O3", "-std=c++17", "-fPIC", "-march=x86-64-v3", "-pthread", "-ffp-contract=off", "-fno-math-errno",
     "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
 ]
@@ -53,7 +53,8 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp] + objs + [
+        "-L" + os.path.join(ROCM, "lib"), "-lhsa-runtime64", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -94,7 +94,7 @@ Plan build_plan(int L, int K, int depth, int n_slots) {
 
 namespace {
 
-constexpr int NG = 3;  // device gradient ring depth
+constexpr int NG = 4;  // device gradient ring depth
 
 struct Arena {
   std::vector<uint16_t*> slot;
@@ -169,7 +169,7 @@ struct Events {
   hipEvent_t get() {
     if (next == pool->size()) {
       hipEvent_t e;
-      if (hipEventCreate(&e) != hipSuccess) {
+      if (hipEventCreateWithFlags(&e, hipEventBlockingSync) != hipSuccess) {
         err = MT_E_HIP;
         return nullptr;
       }
@@ -323,6 +323,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   Plan plan = build_plan(L, K, M->run.prefetch_depth, plan_slots(K, M->run.prefetch_depth));
   MT_CHECK(!plan.error, MT_E_INVALID, "mt_stream_step: %s", plan.error);
 
+  if (!M->sdma) {
+    std::unique_ptr<SdmaCopier> c(new SdmaCopier());
+    const char* why = "";
+    if (!c->init(&why)) return set_error(MT_E_HIP, "mt_stream_step: SDMA setup failed: %s", why);
+    M->sdma = std::move(c);
+  }
   // pinned per-step staging
   if (M->staging_tokens < (size_t)d.D) {
     const size_t nt = (size_t)d.D;
@@ -358,13 +364,15 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   Queue<Landed> landq;
   std::mutex ring_mu;
   std::condition_variable ring_cv;
-  long ring_enqueued = 0;  // offloads from the gradient ring already enqueued
   std::atomic<bool> abort_all{false};
   std::atomic<int> g_fail{0}, a_fail{0};
   std::atomic<int64_t> units_updated{0};
   double adam_ms = 0.0;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> d2h_ev;
-  double d2h_bytes = 0;
+  double d2h_ms = 0, d2h_bytes = 0;
+  double ring_wait_ms = 0, slab_wait_ms = 0, op_wait_ms = 0, adam_idle_ms = 0;
+  auto ms_since = [](clock::time_point t) {
+    return std::chrono::duration<double, std::milli>(clock::now() - t).count();
+  };
   hipEvent_t loss_ev = nullptr;
   std::mutex ev_mu;  // guards the event pool across threads
   auto get_ev = [&]() {
@@ -385,9 +393,11 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   std::condition_variable loss_cv;
   bool loss_ready = false;
 
-  hipEvent_t gfree[NG] = {};  // ring buffer i may be overwritten once this fires
-
   // --------------------------------------------------------- G thread
+  // Waits on the host for each backward op, copies its gradient to a pinned
+  // slab on an SDMA engine, then frees the ring slot and hands the slab to
+  // the optimizer thread.
+  long ring_done = 0;  // ring-buffer offloads whose copy has completed
   auto g_main = [&]() {
     for (;;) {
       Offload o = offq.pop();
@@ -395,51 +405,48 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         landq.push(Landed{0, nullptr, false, nullptr, true});
         return;
       }
-      if (abort_all.load()) {
-        if (o.ring >= 0) {
-          std::lock_guard<std::mutex> lk(ring_mu);
-          ++ring_enqueued;
-          ring_cv.notify_all();
-        }
-        continue;
-      }
       uint16_t* host = nullptr;
       bool own = false;
-      if (o.unit < 0) {
-        host = M->dx0_host;
-      } else if (M->run.use_slab_pool) {
-        host = M->slabs.acquire();
-      } else {
-        if (hipHostMalloc(reinterpret_cast<void**>(&host), M->slab_elems * 2, hipHostMallocDefault) !=
-            hipSuccess) {
-          g_fail = 1;
-          abort_all = true;
-          continue;
+      bool ok = !abort_all.load();
+      if (ok) {
+        if (o.unit < 0) {
+          host = M->dx0_host;
+        } else if (M->run.use_slab_pool) {
+          const auto tw = clock::now();
+          host = M->slabs.acquire();
+          slab_wait_ms += ms_since(tw);
+        } else {
+          ok = hipHostMalloc(reinterpret_cast<void**>(&host), M->slab_elems * 2,
+                             hipHostMallocDefault) == hipSuccess;
+          own = ok;
         }
-        own = true;
       }
-      hipEvent_t e0 = get_ev(), e1 = get_ev(), landed = get_ev();
-      bool ok = e0 && e1 && landed && hipStreamWaitEvent(sG, o.after, 0) == hipSuccess &&
-                hipEventRecord(e0, sG) == hipSuccess &&
-                hipMemcpyAsync(host, o.src, o.elems * 2, hipMemcpyDeviceToHost, sG) == hipSuccess &&
-                hipEventRecord(e1, sG) == hipSuccess;
-      if (ok && o.ring >= 0) ok = hipEventRecord(gfree[o.ring], sG) == hipSuccess;
+      if (ok) {
+        const auto tw = clock::now();
+        ok = hipEventSynchronize(o.after) == hipSuccess;
+        op_wait_ms += ms_since(tw);
+      }
+      if (ok) {
+        const auto t0 = clock::now();
+        ok = M->sdma->copy_d2h(host, o.src, o.elems * 2);
+        d2h_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+        d2h_bytes += (double)o.elems * 2;
+      }
       if (o.ring >= 0) {
         std::lock_guard<std::mutex> lk(ring_mu);
-        ++ring_enqueued;
+        ++ring_done;
         ring_cv.notify_all();
       }
-      ok = ok && hipEventRecord(landed, sG) == hipSuccess;
       if (!ok) {
-        g_fail = 1;
+        if (!abort_all.load()) g_fail = 1;
         abort_all = true;
-        if (!own && o.unit >= 0) M->slabs.release(host);
-        if (own) hipHostFree(host);
+        if (host && o.unit >= 0) {
+          if (own) hipHostFree(host);
+          else M->slabs.release(host);
+        }
         continue;
       }
-      d2h_ev.push_back({e0, e1});
-      d2h_bytes += (double)o.elems * 2;
-      landq.push(Landed{o.unit, host, own, landed, false});
+      landq.push(Landed{o.unit, host, own, nullptr, false});
     }
   };
 
@@ -452,12 +459,10 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     bool checked = false;
     bool skip = false;
     for (;;) {
+      const auto tw = clock::now();
       Landed x = landq.pop();
+      adam_idle_ms += ms_since(tw);
       if (x.end) return;
-      if (hipEventSynchronize(x.ev) != hipSuccess) {
-        a_fail = 1;
-        abort_all = true;
-      }
       if (!checked) {
         std::unique_lock<std::mutex> lk(loss_mu);
         loss_cv.wait(lk, [&] { return loss_ready; });
@@ -507,7 +512,6 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   };
 
   // ---------------------------------------------------- enqueue (main)
-  for (int i = 0; i < NG; ++i) gfree[i] = get_ev();
   loss_ev = get_ev();
   ph_start = get_ev();
   ph_fwd = get_ev();
@@ -596,14 +600,15 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         const int l = op.layer, a = (l / K) * K;
         const uint16_t* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
         const int r = bwd_count % NG;
-        if (bwd_count >= NG) {
+        if (bwd_count >= NG) {  // the ring slot's previous gradient must have left
+          const auto tw = clock::now();
           std::unique_lock<std::mutex> lk(ring_mu);
-          ring_cv.wait(lk, [&] { return ring_enqueued >= bwd_count - NG + 1 || abort_all.load(); });
+          ring_cv.wait(lk, [&] { return ring_done >= bwd_count - NG + 1 || abort_all.load(); });
+          ring_wait_ms += ms_since(tw);
           if (abort_all.load()) {
-            fail = MT_E_HIP;
+            fail = set_error(MT_E_HIP, "mt_stream_step: gradient offload failed");
             goto drain;
           }
-          MT_STEP_HIP(hipStreamWaitEvent(sC, gfree[r], 0));
         }
         MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
                                    A.lws, A.lws_bytes, sC, nullptr));
@@ -656,7 +661,7 @@ drain:
     s.bwd_ms = elapsed(ph_head, ph_end);
     s.adam_ms = adam_ms;
     for (auto& p : h2d_ev) s.h2d_ms += elapsed(p.first, p.second);
-    for (auto& p : d2h_ev) s.d2h_ms += elapsed(p.first, p.second);
+    s.d2h_ms = d2h_ms;
     for (auto& p : wait_ev_f) s.exposed_wait_fwd_ms += elapsed(p.first, p.second);
     for (auto& p : wait_ev_b) s.exposed_wait_bwd_ms += elapsed(p.first, p.second);
     for (int i = 0; i + 1 < probe.used; i += 2) s.probe_kernel_ms += elapsed(probe.ev[i], probe.ev[i + 1]);
@@ -670,6 +675,10 @@ drain:
     s.units_updated = units_updated.load();
     s.step_ms = std::chrono::duration<double, std::milli>(clock::now() - t_begin).count();
     s.tail_ms = s.step_ms - (s.fwd_ms + s.head_ms + s.bwd_ms);
+    s.host_ring_wait_ms = ring_wait_ms;
+    s.host_slab_wait_ms = slab_wait_ms;
+    s.host_op_wait_ms = op_wait_ms;
+    s.host_adam_idle_ms = adam_idle_ms;
   }
   return MT_OK;
 }

@@ -85,13 +85,32 @@ AdamHp adam_hp(const mt_run_cfg& hp, int64_t step) {
   return h;
 }
 
-void adam_range(float* __restrict p, float* __restrict m, float* __restrict v,
-                const uint16_t* __restrict gb, const float* __restrict gf,
-                uint16_t* __restrict shadow, size_t lo, size_t hi, const AdamHp& h) {
+namespace {
+
+// Branch-free RNE float32 -> bfloat16 (quiet NaN with the sign kept), written
+// so the compiler can vectorize it.
+inline uint32_t f2bf_bits(uint32_t u) {
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t q = ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? q : r;
+}
+
+template <bool BF16_GRAD, bool SHADOW>
+void adam_loop(float* __restrict p, float* __restrict m, float* __restrict v,
+               const void* __restrict graw, uint16_t* __restrict shadow, size_t lo, size_t hi,
+               const AdamHp& h) {
   const float b1 = h.b1, omb1 = h.omb1, b2 = h.b2, omb2 = h.omb2;
   const float bc1 = h.bc1, bc2 = h.bc2, lr = h.lr, eps = h.eps;
+  const uint16_t* __restrict gb = static_cast<const uint16_t*>(graw);
+  const float* __restrict gf = static_cast<const float*>(graw);
   for (size_t i = lo; i < hi; ++i) {
-    const float g = gb ? host_bf2f(gb[i]) : gf[i];
+    float g;
+    if constexpr (BF16_GRAD) {
+      const uint32_t gu = (uint32_t)gb[i] << 16;
+      __builtin_memcpy(&g, &gu, 4);
+    } else {
+      g = gf[i];
+    }
     const float mi = b1 * m[i] + omb1 * g;
     const float vi = b2 * v[i] + omb2 * (g * g);
     const float mh = mi / bc1;
@@ -100,7 +119,24 @@ void adam_range(float* __restrict p, float* __restrict m, float* __restrict v,
     m[i] = mi;
     v[i] = vi;
     p[i] = pi;
-    if (shadow) shadow[i] = host_f2bf(pi);
+    if constexpr (SHADOW) {
+      uint32_t pu;
+      __builtin_memcpy(&pu, &pi, 4);
+      shadow[i] = (uint16_t)f2bf_bits(pu);
+    }
+  }
+}
+
+}  // namespace
+
+void adam_range(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
+                uint16_t* shadow, size_t lo, size_t hi, const AdamHp& h) {
+  if (gb) {
+    if (shadow) adam_loop<true, true>(p, m, v, gb, shadow, lo, hi, h);
+    else adam_loop<true, false>(p, m, v, gb, nullptr, lo, hi, h);
+  } else {
+    if (shadow) adam_loop<false, true>(p, m, v, gf, shadow, lo, hi, h);
+    else adam_loop<false, false>(p, m, v, gf, nullptr, lo, hi, h);
   }
 }
 
@@ -169,7 +205,7 @@ void mt_run_cfg_default(mt_run_cfg* r) {
   r->ckpt_interval = 4;
   r->prefetch_depth = 2;
   r->use_slab_pool = 1;
-  r->n_slabs = 4;
+  r->n_slabs = 8;
   r->mlp_chunk_tokens = 0;
   r->head_chunk_tokens = 16384;
   r->precision = MT_PREC_BF16;

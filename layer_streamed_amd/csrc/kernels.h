@@ -69,6 +69,10 @@ hipError_t rope_apply(uint16_t* qkv, long ldq, int batch, int seq, int n_heads,
                       int n_kv_heads, int head_dim, const float* cos_t, const float* sin_t,
                       int inverse, hipStream_t s);
 
+// Device -> pinned host copy by a kernel of `blocks` workgroups (bytes,
+// src and dst multiples of 16).
+hipError_t copy_d2h(const void* src, void* dst_host, size_t bytes, int blocks, hipStream_t s);
+
 hipError_t cast_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
 hipError_t fill_f32(float* p, float v, size_t n, hipStream_t s);
 hipError_t copy_rows_bf16(const uint16_t* src, long lds, uint16_t* dst, long ldd, int rows,

@@ -15,6 +15,7 @@
 #include "host.h"
 #include "layer.h"
 #include "mt.h"
+#include "sdma.h"
 
 namespace mt {
 
@@ -77,6 +78,7 @@ struct mt_model {
   float* loss_host = nullptr;
   size_t staging_tokens = 0;
   std::vector<hipEvent_t> events;  // grown on demand
+  std::unique_ptr<mt::SdmaCopier> sdma;  // gradient offload engine (created on first step)
   int64_t step = 0;
   bool broken = false;
   int64_t pinned_bytes = 0, pageable_bytes = 0;

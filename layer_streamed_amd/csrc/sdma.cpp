@@ -1,0 +1,127 @@
+#include "sdma.h"
+
+#include <hip/hip_runtime_api.h>
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
+
+namespace mt {
+
+namespace {
+struct Find {
+  uint32_t want_bdf;
+  hsa_agent_t gpu{}, cpu{};
+  bool have_gpu = false, have_cpu = false;
+};
+
+hsa_status_t visit(hsa_agent_t a, void* data) {
+  Find* f = static_cast<Find*>(data);
+  hsa_device_type_t t;
+  if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) != HSA_STATUS_SUCCESS) return HSA_STATUS_SUCCESS;
+  if (t == HSA_DEVICE_TYPE_CPU && !f->have_cpu) {
+    f->cpu = a;
+    f->have_cpu = true;
+  } else if (t == HSA_DEVICE_TYPE_GPU && !f->have_gpu) {
+    uint32_t bdf = 0;
+    hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_BDFID), &bdf);
+    if (bdf == f->want_bdf) {
+      f->gpu = a;
+      f->have_gpu = true;
+    }
+  }
+  return HSA_STATUS_SUCCESS;
+}
+}  // namespace
+
+bool SdmaCopier::init(const char** err) {
+  int dev = 0, bus = 0, device = 0, domain = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&device, hipDeviceAttributePciDeviceId, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&domain, hipDeviceAttributePciDomainID, dev) != hipSuccess) {
+    *err = "cannot query the HIP device's PCI location";
+    return false;
+  }
+  if (hsa_init() != HSA_STATUS_SUCCESS) {
+    *err = "hsa_init failed";
+    return false;
+  }
+  hsa_inited_ = true;
+  Find f;
+  // BDF id as ROCr reports it: bus << 8 | device << 3 | function (function 0)
+  f.want_bdf = ((uint32_t)bus << 8) | ((uint32_t)device << 3);
+  hsa_iterate_agents(visit, &f);
+  if (!f.have_gpu) {  // fall back to the only GPU agent when the BDF does not match
+    struct Any {
+      hsa_agent_t gpu{};
+      int n = 0;
+    } any;
+    hsa_iterate_agents(
+        [](hsa_agent_t a, void* d) {
+          hsa_device_type_t t;
+          if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) == HSA_STATUS_SUCCESS &&
+              t == HSA_DEVICE_TYPE_GPU) {
+            Any* x = static_cast<Any*>(d);
+            if (x->n++ == 0) x->gpu = a;
+          }
+          return HSA_STATUS_SUCCESS;
+        },
+        &any);
+    if (any.n == 1) {
+      f.gpu = any.gpu;
+      f.have_gpu = true;
+    }
+  }
+  if (!f.have_gpu || !f.have_cpu) {
+    *err = "no matching HSA GPU/CPU agent";
+    return false;
+  }
+  uint32_t mask = 0;
+  if (hsa_amd_memory_copy_engine_status(f.cpu, f.gpu, &mask) != HSA_STATUS_SUCCESS || mask == 0) {
+    *err = "no SDMA engine available for device-to-host copies";
+    return false;
+  }
+  // ROCr's recommendation for this direction: on MI355X two engines serve
+  // the host link while the others are tuned for xGMI and reach only
+  // 7-11 GB/s to host memory.  Host-to-device traffic prefers engine 0, so
+  // device-to-host takes the lowest recommended engine.
+  uint32_t pref = 0;
+  if (hsa_amd_memory_get_preferred_copy_engine(f.cpu, f.gpu, &pref) != HSA_STATUS_SUCCESS ||
+      (pref & mask) == 0)
+    pref = mask;
+  pref &= mask;
+  unsigned e = 1;
+  while (!(pref & e)) e <<= 1;
+  hsa_signal_t sig;
+  if (hsa_signal_create(1, 0, nullptr, &sig) != HSA_STATUS_SUCCESS) {
+    *err = "hsa_signal_create failed";
+    return false;
+  }
+  gpu_ = f.gpu.handle;
+  cpu_ = f.cpu.handle;
+  signal_ = sig.handle;
+  engine_ = e;
+  ok_ = true;
+  return true;
+}
+
+SdmaCopier::~SdmaCopier() {
+  if (signal_) hsa_signal_destroy(hsa_signal_t{signal_});
+  if (hsa_inited_) hsa_shut_down();
+}
+
+bool SdmaCopier::copy_d2h(void* dst_host, const void* src_dev, size_t bytes) {
+  if (!ok_) return false;
+  if (bytes == 0) return true;
+  hsa_signal_t sig{signal_};
+  hsa_signal_store_screlease(sig, 1);
+  hsa_status_t st = hsa_amd_memory_async_copy_on_engine(
+      dst_host, hsa_agent_t{cpu_}, src_dev, hsa_agent_t{gpu_}, bytes, 0, nullptr, sig,
+      static_cast<hsa_amd_sdma_engine_id_t>(engine_), true);
+  if (st != HSA_STATUS_SUCCESS) return false;
+  while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_LT, 1, UINT64_MAX,
+                                   HSA_WAIT_STATE_BLOCKED) >= 1) {
+  }
+  return true;
+}
+
+}  // namespace mt

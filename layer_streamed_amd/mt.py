@@ -66,7 +66,8 @@ class StepStats(C.Structure):
         "d2h_bytes", "h2d_ms", "d2h_ms", "exposed_wait_fwd_ms", "exposed_wait_bwd_ms",
         "probe_kernel_ms", "probe_kernel_flops")] + [(n, C.c_int64) for n in (
             "probe_kernel_launches", "pinned_host_bytes", "pageable_host_bytes",
-            "device_arena_bytes", "units_updated")]
+            "device_arena_bytes", "units_updated")] + [(n, C.c_double) for n in (
+                "host_ring_wait_ms", "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -112,6 +113,7 @@ _SIGS = {
     "mt_run_cfg_default": (None, _P),
     "mt_op_rmsnorm_bwd_workspace": (_SZ, _I32, _I32),
     "mt_debug_plan": (_I32, _I32, _I32, _I32, _P, _SZ, _P),
+    "mt_op_copy_d2h": (_I32, _P, _P, _SZ, _I32, _P),
 }
 FN = {}
 for _name, (_res, *_args) in _SIGS.items():
