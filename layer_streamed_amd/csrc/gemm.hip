@@ -26,25 +26,43 @@ constexpr int BK = 64;
 constexpr int LDK = BK + 8;
 
 // K-contiguous operand: ROWS x BK tile of X[row][k] (row stride ld).
+// Row pointers are formed once per tile (rows past the edge are clamped to
+// a valid row and their data zeroed), so the K loop only adds k0.  CHECK
+// selects the guarded form for edge tiles and the K tail; interior tiles
+// take plain loads with no per-lane branches.
 template <int ROWS, int NTHR>
 struct LoadKC {
   static constexpr int CPR = BK / 8;  // 16-byte chunks per row
   static constexpr int PER = ROWS * CPR / NTHR;
   static_assert(PER >= 1 && ROWS * CPR % NTHR == 0, "tile/thread mismatch");
   u32x4_t r[PER];
+  const uint16_t* ptr[PER];
+  bool rok[PER];
 
   template <class Map>
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ X, long ld, int r0, int nrows,
-                                       int k0, int K, int tid, Map map) {
+  __device__ __forceinline__ void init(const uint16_t* __restrict__ X, long ld, int r0, int nrows,
+                                       int tid, Map map) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int c = tid + p * NTHR;
       const int row = c / CPR, kc = c % CPR;
-      const int gr = r0 + row, gk = k0 + kc * 8;
-      if (gr < nrows && gk < K)
-        r[p] = *reinterpret_cast<const u32x4_t*>(X + (long)map(gr) * ld + gk);
-      else
-        r[p] = u32x4_t{0, 0, 0, 0};
+      const int gr = r0 + row;
+      rok[p] = gr < nrows;
+      ptr[p] = X + (long)map(rok[p] ? gr : nrows - 1) * ld + kc * 8;
+    }
+  }
+  template <bool CHECK>
+  __device__ __forceinline__ void load(int k0, int K, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      if constexpr (CHECK) {
+        const int gk = k0 + ((tid + p * NTHR) % CPR) * 8;
+        const bool ok = rok[p] && gk < K;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ptr[p] + (gk < K ? k0 : 0));
+        r[p] = ok ? v : u32x4_t{0, 0, 0, 0};
+      } else {
+        r[p] = *reinterpret_cast<const u32x4_t*>(ptr[p] + k0);
+      }
     }
   }
   __device__ __forceinline__ void store(uint16_t* s, int tid) const {
@@ -65,21 +83,37 @@ struct LoadT {
   static constexpr int PER = (BK / 8) * RB / NTHR;
   static_assert(PER >= 1 && (BK / 8) * RB % NTHR == 0, "tile/thread mismatch");
   u32x2_t r[PER][8];
+  const uint16_t* ptr[PER];
+  bool rok[PER];
+  long ld_;
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ X, long ld, int r0, int nrows,
-                                       int k0, int K, int tid) {
+  __device__ __forceinline__ void init(const uint16_t* __restrict__ X, long ld, int r0, int nrows,
+                                       int tid) {
+    ld_ = ld;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int b = tid + p * NTHR;
       const int kb = b / RB, rb = b % RB;
       const int gr = r0 + rb * 4;
+      rok[p] = gr < nrows;
+      ptr[p] = X + (long)(kb * 8) * ld + (rok[p] ? gr : 0);
+    }
+  }
+  template <bool CHECK>
+  __device__ __forceinline__ void load(int k0, int K, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int kb = (tid + p * NTHR) / RB;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const int gk = k0 + kb * 8 + kk;
-        if (gr < nrows && gk < K)
-          r[p][kk] = *reinterpret_cast<const u32x2_t*>(X + (long)gk * ld + gr);
-        else
-          r[p][kk] = u32x2_t{0, 0};
+        if constexpr (CHECK) {
+          const int gk = k0 + kb * 8 + kk;
+          const bool ok = rok[p] && gk < K;
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(ptr[p] + (gk < K ? (long)(k0 + kk) * ld_ : 0));
+          r[p][kk] = ok ? v : u32x2_t{0, 0};
+        } else {
+          r[p][kk] = *reinterpret_cast<const u32x2_t*>(ptr[p] + (long)(k0 + kk) * ld_);
+        }
       }
     }
   }
@@ -157,19 +191,27 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
   using LB = typename std::conditional<LAYOUT == GEMM_NT, LoadKC<BN, NTHR>, LoadT<BN, NTHR>>::type;
   LA la;
   LB lb;
-  const uint16_t* __restrict__ Ap = a.A;
-  const uint16_t* __restrict__ Bp = a.B;
-
-  auto issue = [&](int k0) {
-    if constexpr (LAYOUT == GEMM_TN) la.load(Ap, a.lda, m0, M, k0, K, tid);
-    else la.load(Ap, a.lda, m0, M, k0, K, tid, IdMap{});
-    if constexpr (LAYOUT == GEMM_NT) {
-      if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE)
-        lb.load(Bp, a.ldb, n0, N, k0, K, tid, SwiMap{a.F});
-      else
-        lb.load(Bp, a.ldb, n0, N, k0, K, tid, IdMap{});
+  if constexpr (LAYOUT == GEMM_TN) la.init(a.A, a.lda, m0, M, tid);
+  else la.init(a.A, a.lda, m0, M, tid, IdMap{});
+  if constexpr (LAYOUT == GEMM_NT) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE)
+      lb.init(a.B, a.ldb, n0, N, tid, SwiMap{a.F});
+    else
+      lb.init(a.B, a.ldb, n0, N, tid, IdMap{});
+  } else {
+    lb.init(a.B, a.ldb, n0, N, tid);
+  }
+  // interior tiles need no row guards; K tiles need guards only at the tail
+  const bool edge = (m0 + BM > M) || (n0 + BN > N);
+  const int nk = (K + BK - 1) / BK;
+  const int nk_full = edge ? 0 : K / BK;
+  auto issue = [&](int kt) {
+    if (kt < nk_full) {
+      la.template load<false>(kt * BK, K, tid);
+      lb.template load<false>(kt * BK, K, tid);
     } else {
-      lb.load(Bp, a.ldb, n0, N, k0, K, tid);
+      la.template load<true>(kt * BK, K, tid);
+      lb.template load<true>(kt * BK, K, tid);
     }
   };
   auto commit = [&](int buf) {
@@ -178,16 +220,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
     lb.store(s + BM * LDK, tid);
   };
 
-  const int nk = (K + BK - 1) / BK;
   issue(0);
   commit(0);
   __syncthreads();
   const int arow = wm * TM * 32 + (lane & 31);
   const int brow = wn * TN * 32 + (lane & 31);
   const int koff = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue((kt + 1) * BK);
+  auto compute = [&](int buf) {
     const uint16_t* sA = smem + buf * STAGE;
     const uint16_t* sB = sA + BM * LDK;
 #pragma unroll
@@ -204,9 +243,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) commit(buf ^ 1);
+  };
+  // steady state: next tile's loads in flight while this tile computes
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) {
+    issue(kt + 1);
+    compute(kt & 1);
+    commit((kt + 1) & 1);
     __syncthreads();
   }
+  if (nk > 0) compute(kt & 1);
 
   // ------------------------------------------------------------ epilogue
   const int rbase = m0 + wm * TM * 32 + 4 * (lane >> 5);
@@ -250,18 +296,49 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
             reinterpret_cast<float*>(a.C)[(long)row * a.ldc + col] = v;
           } else if constexpr (EPI == EPI_ACC_F32) {
             reinterpret_cast<float*>(a.C)[(long)row * a.ldc + col] += v;
-          } else if constexpr (EPI == EPI_RESID_BF16) {
-            const float r = bf2f(a.R[(long)row * a.ldr + col]);
-            reinterpret_cast<uint16_t*>(a.C)[(long)row * a.ldc + col] = f2bf(r + v);
-          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            const int F = a.F;
-            const float gt = bf2f(a.G[(long)row * a.ldg + col]);
-            const float u = bf2f(a.G[(long)row * a.ldg + F + col]);
-            const float sg = 1.f / (1.f + __expf(-gt));
-            a.C2[(long)row * a.ldc2 + col] = f2bf(v * u * sg * (1.f + gt * (1.f - sg)));
-            a.C2[(long)row * a.ldc2 + F + col] = f2bf(v * gt * sg);
           }
         }
+  }
+  if constexpr (EPI == EPI_RESID_BF16 || EPI == EPI_SWIGLU_BWD) {
+    // Per 32 x 32 block: issue every load of the block first, then compute
+    // and store, so the loads overlap instead of each waiting its latency.
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = cbase + j * 32;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // half a block at a time bounds the live registers
+          float x0[8], x1[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int e = 8 * h + q;
+            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+            const bool ok = row < M && col < N;
+            if constexpr (EPI == EPI_RESID_BF16) {
+              x0[q] = ok ? bf2f(a.R[(long)row * a.ldr + col]) : 0.f;
+            } else {
+              x0[q] = ok ? bf2f(a.G[(long)row * a.ldg + col]) : 0.f;
+              x1[q] = ok ? bf2f(a.G[(long)row * a.ldg + a.F + col]) : 0.f;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int e = 8 * h + q;
+            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+            if (row >= M || col >= N) continue;
+            const float v = acc[i][j][e];
+            if constexpr (EPI == EPI_RESID_BF16) {
+              reinterpret_cast<uint16_t*>(a.C)[(long)row * a.ldc + col] = f2bf(x0[q] + v);
+            } else {
+              const float gt = x0[q], u = x1[q];
+              const float sg = 1.f / (1.f + __expf(-gt));
+              a.C2[(long)row * a.ldc2 + col] = f2bf(v * u * sg * (1.f + gt * (1.f - sg)));
+              a.C2[(long)row * a.ldc2 + a.F + col] = f2bf(v * gt * sg);
+            }
+          }
+        }
+      }
   }
 }
 
@@ -282,8 +359,22 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tile choice: 256 x 256 (eight waves of 128 x 64, two per SIMD so one
+// wave's memory stalls hide behind the other's MFMAs) cuts LDS reads per
+// MFMA flop and L2 re-reads against 128 x 128; it is used when the grid
+// still fills the 256 CUs several times over.
+inline bool use_big_tile(const GemmArgs& a) {
+  const long t = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  return t >= 4 * 256;
+}
+
 template <int LAYOUT, int EPI>
 hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
+  // the SwiGLU-backward epilogue needs more registers than the big tile
+  // leaves (it would spill its accumulators), so it keeps the 128 x 128 tile
+  if constexpr (EPI != EPI_SWIGLU_BWD) {
+    if (use_big_tile(a)) return launch_cfg<2, 4, 4, 2, LAYOUT, EPI>(a, s);
+  }
   return launch_cfg<2, 2, 2, 2, LAYOUT, EPI>(a, s);
 }
 
@@ -330,8 +421,8 @@ const char* gemm_check(const GemmArgs& a) {
 
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (a.epi == EPI_SWIGLU) return launch_cfg<2, 2, 2, 2, GEMM_NT, EPI_SWIGLU>(a, s);
-  if (a.epi == EPI_SWIGLU_SAVE) return launch_cfg<2, 2, 2, 2, GEMM_NT, EPI_SWIGLU_SAVE>(a, s);
+  if (a.epi == EPI_SWIGLU) return launch_layout<GEMM_NT, EPI_SWIGLU>(a, s);
+  if (a.epi == EPI_SWIGLU_SAVE) return launch_layout<GEMM_NT, EPI_SWIGLU_SAVE>(a, s);
   switch (a.layout) {
     case GEMM_NT: return launch_epi<GEMM_NT>(a, s);
     case GEMM_NN: return launch_epi<GEMM_NN>(a, s);

@@ -296,3 +296,21 @@ def test_attention_forward_32k_sampled_heads():
         o_ref, lse_ref = D.causal_attention(q, k, v, row_block=2048)
         assert rel_fro(to_np(O)[rows, h * d:(h + 1) * d], o_ref[0, rows, 0]) < 1e-2
         np.testing.assert_allclose(LSE[0, h].cpu().numpy()[rows], lse_ref[0, 0, rows], atol=2e-3)
+
+
+@pytest.mark.parametrize("layout,M,N,K", [(1, 16384, 3584, 4608), (2, 37888, 3584, 2048),
+                                          (0, 16384, 4608, 3584), (2, 3584, 18944, 3000)])
+def test_gemm_large_tiles_sampled(layout, M, N, K):
+    """Shapes of the 7B layer that take the 256 x 256 tile path (ragged K on TN)."""
+    torch, mt = _torch(), _mt()
+    g = torch.Generator(device="cuda").manual_seed(M + N)
+    A = torch.randn((K, M) if layout == 2 else (M, K), device="cuda", generator=g).to(torch.bfloat16)
+    B = torch.randn((N, K) if layout == 0 else (K, N), device="cuda", generator=g).to(torch.bfloat16)
+    Cm = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
+    mt.gemm(layout, 0, M, N, K, A, M if layout == 2 else K, B, K if layout == 0 else N, Cm, N)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(1).choice(M, 16, replace=False)
+    a = (A[:, rows].t() if layout == 2 else A[rows]).float().cpu().numpy().astype(np.float64)
+    b = B.float().cpu().numpy().astype(np.float64)
+    ref = a @ (b.T if layout == 0 else b)
+    assert rel_fro(Cm[rows].float().cpu().numpy(), ref) < 5e-3
