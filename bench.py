@@ -29,6 +29,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if the kernel's sources changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_7b_hbm_traffic.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    src = os.path.join(ROOT, "layer_streamed_amd", "csrc")
+    h = hashlib.sha256(open(os.path.join(src, "gemm.hip"), "rb").read()
+                       + open(os.path.join(src, "common.h"), "rb").read()).hexdigest()
+    sha = re.search(r"source_sha256: ([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not sha or not val or sha.group(1) != h:
+        return None
+    return int(val.group(1))
+
+
 def init_weights(model, shape, seed):
     """N(0, 0.02^2) matrices drawn on the GPU (plumbing only), gains 1."""
     import numpy as np
@@ -109,9 +129,8 @@ def main():
     ap.add_argument("--prefetch-depth", type=int, default=2)
     ap.add_argument("--no-slab-pool", action="store_true")
     ap.add_argument("--ckpt-interval", type=int, default=0)
-    # Adam is host-memory-bandwidth bound from about 4 threads on; the rest
-    # of the cores stay free for the enqueue and offload threads
-    ap.add_argument("--host-threads", type=int, default=8)
+    # CPU threads for Adam and the embedding scatter (memory-bandwidth bound)
+    ap.add_argument("--host-threads", type=int, default=16)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the "
@@ -242,13 +261,13 @@ def main():
         "device_arena_bytes": stats[-1]["device_arena_bytes"],
         "loss": losses[-1],
         "roofline": {
-            "kernel": "gemm_kernel<2,2,2,2,NT,SWIGLU> (gate/up projection + SwiGLU)",
+            "kernel": "gemm_kernel<2,4,4,2,NT,SwiGLU> (gate/up projection, 256x256 tile)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if shape.name == "qwen2.5-7b-b16-t1024" else None,
             "avg_launch_ms": round(avg_launch_ms, 4),
             "flops_per_launch": flops_per_launch,
             "launches": probe_n,
