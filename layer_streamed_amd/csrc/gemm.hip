@@ -156,6 +156,99 @@ struct SwiMap {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z)); }
 
+// Epilogue shared by the GEMM kernels: acc holds the wave's TM x TN blocks of
+// 32 x 32 (lane l: column l % 32, rows 8j + 4(l/32) + i in element 4j + i).
+template <int WM, int WN, int TM, int TN, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, f32x16_t (&acc)[TM][TN], int m0, int n0,
+                                         int wm, int wn, int lane) {
+  const int M = a.M, N = a.N;
+  const int rbase = m0 + wm * TM * 32 + 4 * (lane >> 5);
+  const int cbase = n0 + wn * TN * 32 + (lane & 31);
+  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) {
+    static_assert(TN % 2 == 0, "SwiGLU pairs need an even TN");
+    uint16_t* Cm = reinterpret_cast<uint16_t*>(a.C);
+    const int fbase = (n0 + wn * TN * 32) / 2 + (lane & 31);
+    const int F = a.F;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < TN / 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+          const int f = fbase + 32 * q;
+          if (row < M && f < F) {
+            const float gv = acc[i][2 * q][e], uv = acc[i][2 * q + 1][e];
+            Cm[(long)row * a.ldc + f] = f2bf(silu_f(gv) * uv);
+            if constexpr (EPI == EPI_SWIGLU_SAVE) {
+              a.C2[(long)row * a.ldc2 + f] = f2bf(gv);
+              a.C2[(long)row * a.ldc2 + F + f] = f2bf(uv);
+            }
+          }
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+          const int col = cbase + j * 32;
+          if (row >= M || col >= N) continue;
+          const float v = acc[i][j][e];
+          if constexpr (EPI == EPI_BF16) {
+            reinterpret_cast<uint16_t*>(a.C)[(long)row * a.ldc + col] = f2bf(v);
+          } else if constexpr (EPI == EPI_F32) {
+            reinterpret_cast<float*>(a.C)[(long)row * a.ldc + col] = v;
+          } else if constexpr (EPI == EPI_ACC_F32) {
+            reinterpret_cast<float*>(a.C)[(long)row * a.ldc + col] += v;
+          }
+        }
+  }
+  if constexpr (EPI == EPI_RESID_BF16 || EPI == EPI_SWIGLU_BWD) {
+    // Per 32 x 32 block: issue every load of the block first, then compute
+    // and store, so the loads overlap instead of each waiting its latency.
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = cbase + j * 32;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // half a block at a time bounds the live registers
+          float x0[8], x1[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int e = 8 * h + q;
+            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+            const bool ok = row < M && col < N;
+            if constexpr (EPI == EPI_RESID_BF16) {
+              x0[q] = ok ? bf2f(a.R[(long)row * a.ldr + col]) : 0.f;
+            } else {
+              x0[q] = ok ? bf2f(a.G[(long)row * a.ldg + col]) : 0.f;
+              x1[q] = ok ? bf2f(a.G[(long)row * a.ldg + a.F + col]) : 0.f;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int e = 8 * h + q;
+            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+            if (row >= M || col >= N) continue;
+            const float v = acc[i][j][e];
+            if constexpr (EPI == EPI_RESID_BF16) {
+              reinterpret_cast<uint16_t*>(a.C)[(long)row * a.ldc + col] = f2bf(x0[q] + v);
+            } else {
+              const float gt = x0[q], u = x1[q];
+              const float sg = 1.f / (1.f + __expf(-gt));
+              a.C2[(long)row * a.ldc2 + col] = f2bf(v * u * sg * (1.f + gt * (1.f - sg)));
+              a.C2[(long)row * a.ldc2 + a.F + col] = f2bf(v * gt * sg);
+            }
+          }
+        }
+      }
+  }
+}
+
 template <int WM, int WN, int TM, int TN, int LAYOUT, int EPI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NTHR = WM * WN * 64;
@@ -254,92 +347,160 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
   }
   if (nk > 0) compute(kt & 1);
 
-  // ------------------------------------------------------------ epilogue
-  const int rbase = m0 + wm * TM * 32 + 4 * (lane >> 5);
-  const int cbase = n0 + wn * TN * 32 + (lane & 31);
-  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) {
-    static_assert(TN % 2 == 0, "SwiGLU pairs need an even TN");
-    uint16_t* Cm = reinterpret_cast<uint16_t*>(a.C);
-    const int fbase = (n0 + wn * TN * 32) / 2 + (lane & 31);
-    const int F = a.F;
+  epilogue<WM, WN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
+// NT product with direct global -> LDS loads (gfx950 global_load_lds_dwordx4).
+// Both operands are K-contiguous, so each lane's 16-byte chunk can land in
+// LDS without passing through registers: lane t of a wave instruction writes
+// LDS base + 16 t.  A ring of DL_STAGES stages of DL_BK columns keeps three
+// stages of loads in flight while one is computed, so the load latency is
+// covered by LDS capacity instead of registers.  Within a row the 4 chunks
+// are stored in the order c ^ ((row >> 2) & 3), which makes the fragment
+// reads (32 lanes, 32 consecutive rows, one chunk) bank-conflict free.
+// Requires K % DL_BK == 0; rows past M or N are clamped to a valid row (they
+// only feed output elements the epilogue drops).
+constexpr int DL_BK = 32;
+constexpr int DL_STAGES = 4;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int WM, int WN, int TM, int TN, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_nt_dl_kernel(const GemmArgs a) {
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NW = WM * WN;
+  constexpr int CH = DL_BK / 8;  // 16-byte chunks per row
+  constexpr int A_CH = BM * CH, B_CH = BN * CH;
+  constexpr int A_PER = A_CH / 64 / NW, B_PER = B_CH / 64 / NW;  // instructions per wave
+  static_assert(A_PER * 64 * NW == A_CH && B_PER * 64 * NW == B_CH, "tile/wave mismatch");
+  constexpr int LPW = A_PER + B_PER;
+  constexpr int STAGE = (A_CH + B_CH) * 16;  // bytes
+  extern __shared__ __attribute__((aligned(16))) char dl_smem[];
+
+  const int M = a.M, N = a.N, K = a.K;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int pid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int g = pid / per_group;
+  const int first_m = g * GROUP;
+  const int gm = min(tiles_m - first_m, GROUP);
+  const int tile_m = first_m + (pid % per_group) % gm;
+  const int tile_n = (pid % per_group) / gm;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const uint16_t* ga[A_PER];
+  const uint16_t* gb[B_PER];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < TN / 2; ++q)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-          const int f = fbase + 32 * q;
-          if (row < M && f < F) {
-            const float gv = acc[i][2 * q][e], uv = acc[i][2 * q + 1][e];
-            Cm[(long)row * a.ldc + f] = f2bf(silu_f(gv) * uv);
-            if constexpr (EPI == EPI_SWIGLU_SAVE) {
-              a.C2[(long)row * a.ldc2 + f] = f2bf(gv);
-              a.C2[(long)row * a.ldc2 + F + f] = f2bf(uv);
-            }
-          }
-        }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-          const int col = cbase + j * 32;
-          if (row >= M || col >= N) continue;
-          const float v = acc[i][j][e];
-          if constexpr (EPI == EPI_BF16) {
-            reinterpret_cast<uint16_t*>(a.C)[(long)row * a.ldc + col] = f2bf(v);
-          } else if constexpr (EPI == EPI_F32) {
-            reinterpret_cast<float*>(a.C)[(long)row * a.ldc + col] = v;
-          } else if constexpr (EPI == EPI_ACC_F32) {
-            reinterpret_cast<float*>(a.C)[(long)row * a.ldc + col] += v;
-          }
-        }
+  for (int p = 0; p < A_PER; ++p) {
+    const int pos = (wave * A_PER + p) * 64 + lane;
+    const int row = pos / CH, slot = pos % CH;
+    const int c = slot ^ ((row >> 2) & (CH - 1));
+    const int gr = min(m0 + row, M - 1);
+    ga[p] = a.A + (long)gr * a.lda + c * 8;
   }
-  if constexpr (EPI == EPI_RESID_BF16 || EPI == EPI_SWIGLU_BWD) {
-    // Per 32 x 32 block: issue every load of the block first, then compute
-    // and store, so the loads overlap instead of each waiting its latency.
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int p = 0; p < B_PER; ++p) {
+    const int pos = (wave * B_PER + p) * 64 + lane;
+    const int row = pos / CH, slot = pos % CH;
+    const int c = slot ^ ((row >> 2) & (CH - 1));
+    int gr = min(n0 + row, N - 1);
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) gr = SwiMap{a.F}(gr);
+    gb[p] = a.B + (long)gr * a.ldb + c * 8;
+  }
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = K / DL_BK;
+  auto issue = [&](int kt) {
+    if (kt >= nk) return;
+    const int k0 = kt * DL_BK;
+    char* base = dl_smem + (kt % DL_STAGES) * STAGE;
+#pragma unroll
+    for (int p = 0; p < A_PER; ++p)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(ga[p] + k0),
+          (__attribute__((address_space(3))) void*)(base + (wave * A_PER + p) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int p = 0; p < B_PER; ++p)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(gb[p] + k0),
+          (__attribute__((address_space(3))) void*)(base + A_CH * 16 + (wave * B_PER + p) * 1024), 16,
+          0, 0);
+  };
+
+  const int arow = wm * TM * 32 + (lane & 31);
+  const int brow = wn * TN * 32 + (lane & 31);
+  const int hh = lane >> 5;
+  auto compute = [&](int kt) {
+    const u32x4_t* sA = reinterpret_cast<const u32x4_t*>(dl_smem + (kt % DL_STAGES) * STAGE);
+    const u32x4_t* sB = sA + A_CH;
+#pragma unroll
+    for (int ks = 0; ks < DL_BK / 16; ++ks) {
+      const int c = ks * 2 + hh;
+      u32x4_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = arow + i * 32;
+        af[i] = sA[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = cbase + j * 32;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {  // half a block at a time bounds the live registers
-          float x0[8], x1[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int e = 8 * h + q;
-            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-            const bool ok = row < M && col < N;
-            if constexpr (EPI == EPI_RESID_BF16) {
-              x0[q] = ok ? bf2f(a.R[(long)row * a.ldr + col]) : 0.f;
-            } else {
-              x0[q] = ok ? bf2f(a.G[(long)row * a.ldg + col]) : 0.f;
-              x1[q] = ok ? bf2f(a.G[(long)row * a.ldg + a.F + col]) : 0.f;
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int e = 8 * h + q;
-            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-            if (row >= M || col >= N) continue;
-            const float v = acc[i][j][e];
-            if constexpr (EPI == EPI_RESID_BF16) {
-              reinterpret_cast<uint16_t*>(a.C)[(long)row * a.ldc + col] = f2bf(x0[q] + v);
-            } else {
-              const float gt = x0[q], u = x1[q];
-              const float sg = 1.f / (1.f + __expf(-gt));
-              a.C2[(long)row * a.ldc2 + col] = f2bf(v * u * sg * (1.f + gt * (1.f - sg)));
-              a.C2[(long)row * a.ldc2 + a.F + col] = f2bf(v * gt * sg);
-            }
-          }
-        }
+        const int r = brow + j * 32;
+        bfr[j] = sB[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
       }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < DL_STAGES - 1; ++st) issue(st);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads for stage kt are done once at most `ahead` later
+    // stages are still in flight; the barrier then covers every wave's loads
+    // and every wave's reads of the stage about to be refilled
+    const int ahead = min(DL_STAGES - 2, nk - 1 - kt);
+    if (ahead >= 2) wait_vmcnt<2 * LPW>();
+    else if (ahead == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + DL_STAGES - 1);
+    compute(kt);
   }
+  epilogue<WM, WN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
+}
+
+template <int WM, int WN, int TM, int TN, int EPI>
+hipError_t launch_dl(const GemmArgs& a, hipStream_t s) {
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  const size_t lds = (size_t)DL_STAGES * (BM + BN) * (DL_BK / 8) * 16;
+  auto kern = gemm_nt_dl_kernel<WM, WN, TM, TN, EPI>;
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int WM, int WN, int TM, int TN, int LAYOUT, int EPI>
@@ -370,6 +531,9 @@ inline bool use_big_tile(const GemmArgs& a) {
 
 template <int LAYOUT, int EPI>
 hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
+  if constexpr (LAYOUT == GEMM_NT && EPI != EPI_SWIGLU_BWD) {
+    if (use_big_tile(a) && a.K % DL_BK == 0) return launch_dl<2, 4, 4, 2, EPI>(a, s);
+  }
   // the SwiGLU-backward epilogue needs more registers than the big tile
   // leaves (it would spill its accumulators), so it keeps the 128 x 128 tile
   if constexpr (EPI != EPI_SWIGLU_BWD) {

@@ -299,7 +299,8 @@ def test_attention_forward_32k_sampled_heads():
 
 
 @pytest.mark.parametrize("layout,M,N,K", [(1, 16384, 3584, 4608), (2, 37888, 3584, 2048),
-                                          (0, 16384, 4608, 3584), (2, 3584, 18944, 3000)])
+                                          (0, 16384, 4608, 3584), (2, 3584, 18944, 3000),
+                                          (0, 16344, 4616, 3584), (0, 9000, 30000, 2048)])
 def test_gemm_large_tiles_sampled(layout, M, N, K):
     """Shapes of the 7B layer that take the 256 x 256 tile path (ragged K on TN)."""
     torch, mt = _torch(), _mt()
@@ -309,7 +310,7 @@ def test_gemm_large_tiles_sampled(layout, M, N, K):
     Cm = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
     mt.gemm(layout, 0, M, N, K, A, M if layout == 2 else K, B, K if layout == 0 else N, Cm, N)
     torch.cuda.synchronize()
-    rows = np.random.default_rng(1).choice(M, 16, replace=False)
+    rows = np.concatenate([np.random.default_rng(1).choice(M, 14, replace=False), [0, M - 1]])
     a = (A[:, rows].t() if layout == 2 else A[rows]).float().cpu().numpy().astype(np.float64)
     b = B.float().cpu().numpy().astype(np.float64)
     ref = a @ (b.T if layout == 0 else b)

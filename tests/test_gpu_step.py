@@ -138,3 +138,17 @@ def test_bad_tokens_rejected_without_update(tiny):
         m.step(ids, small, streams)
     assert e.value.status == mt.MT_E_OOM_DEVICE
     m.close()
+
+
+def test_chunked_mlp_and_head_long_sequence_matches_oracle():
+    """Long sequence with both chunked paths on: MLP over 512-token chunks,
+    LM head over 768-token chunks (ragged last chunk of each), K = 2."""
+    s = synth.CONFIGS["tiny-2l-h256"].with_(n_layers=3, ckpt_interval=2, batch=1, seq=2000,
+                                             mlp_chunk_tokens=512)
+    w = synth.make_weights(s, seed=8, bf16_exact=True)
+    ids = synth.make_tokens(s, seed=9)
+    g = _run(s, w, ids, head_chunk_tokens=768)
+    loss, grads, newp, _ = D.train_step(w, ids, s)
+    assert abs(g["loss"][0] - loss) < LOSS_TOL, (g["loss"][0], loss)
+    for n in synth.param_names(s):
+        assert rel(g["grad"][n], grads[n]) < REL_TOL, (n, rel(g["grad"][n], grads[n]))
