@@ -41,6 +41,15 @@ mt_status mt_op_gemm(int32_t layout, int32_t epilogue, int32_t M, int32_t N, int
                      int64_t ldc, const void* R, int64_t ldr, void* C2, int64_t ldc2,
                      const void* G, int64_t ldg, int32_t F, void* stream);
 
+/* The same product in the fp32 debug precision (MT_PREC_FP32_DEBUG of
+ * mt.h): every operand, R, G and C2 is fp32, and so is C for MT_EPI_BF16
+ * and MT_EPI_RESID_BF16 ("storage" outputs); plain fp32 FMA with fp32
+ * accumulation.  No alignment or multiple-of-8 constraints. */
+mt_status mt_op_gemm_f32(int32_t layout, int32_t epilogue, int32_t M, int32_t N, int32_t K,
+                         const float* A, int64_t lda, const float* B, int64_t ldb, void* C,
+                         int64_t ldc, const float* R, int64_t ldr, float* C2, int64_t ldc2,
+                         const float* G, int64_t ldg, int32_t F, void* stream);
+
 /* RMSNorm over rows: y = x / sqrt(mean(x^2)+eps) * g; rstd [rows] fp32
  * (nullable).  x, y bf16 [rows, cols]; g bf16 [cols]; cols % 8 == 0. */
 mt_status mt_op_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int32_t rows,
@@ -74,6 +83,16 @@ mt_status mt_op_attn_fwd(const void* qkv, void* o, float* lse, int32_t batch, in
 mt_status mt_op_attn_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
                          float* delta, void* dqkv, int32_t batch, int32_t seq, int32_t n_heads,
                          int32_t n_kv_heads, int32_t head_dim, void* stream);
+
+/* Attention forward and backward in the fp32 debug precision: the same
+ * contract with fp32 qkv, o, dout and dqkv (exact softmax per row, fp32
+ * FMA; written for exactness, not speed). */
+mt_status mt_op_attn_fwd_f32(const float* qkv, float* o, float* lse, int32_t batch, int32_t seq,
+                             int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream);
+mt_status mt_op_attn_bwd_f32(const float* qkv, const float* o, const float* lse,
+                             const float* dout, float* delta, float* dqkv, int32_t batch,
+                             int32_t seq, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                             void* stream);
 
 /* Cross-entropy rows on fp32 logits [rows, vocab]: target[r] < 0 = no
  * target.  dlogits bf16 = (softmax - onehot) * inv_n; loss_part fp32 [rows]. */

@@ -45,6 +45,24 @@ mt_status mt_op_gemm(int32_t layout, int32_t epilogue, int32_t M, int32_t N, int
   return MT_OK;
 }
 
+mt_status mt_op_gemm_f32(int32_t layout, int32_t epilogue, int32_t M, int32_t N, int32_t K,
+                         const float* A, int64_t lda, const float* B, int64_t ldb, void* C,
+                         int64_t ldc, const float* R, int64_t ldr, float* C2, int64_t ldc2,
+                         const float* G, int64_t ldg, int32_t F, void* stream) {
+  GemmArgsF32 a;
+  a.layout = layout; a.epi = epilogue; a.M = M; a.N = N; a.K = K;
+  a.A = A; a.lda = lda;
+  a.B = B; a.ldb = ldb;
+  a.C = C; a.ldc = ldc;
+  a.R = R; a.ldr = ldr;
+  a.C2 = C2; a.ldc2 = ldc2;
+  a.G = G; a.ldg = ldg;
+  a.F = F;
+  if (const char* msg = gemm_check(a)) return set_error(MT_E_SHAPE, "mt_op_gemm_f32: %s", msg);
+  MT_HIP(gemm_launch(a, static_cast<hipStream_t>(stream)));
+  return MT_OK;
+}
+
 mt_status mt_op_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int32_t rows,
                             int32_t cols, float eps, void* stream) {
   MT_CHECK(x && g && y, MT_E_INVALID, "mt_op_rmsnorm_fwd: null pointer");
@@ -75,7 +93,7 @@ mt_status mt_op_rmsnorm_bwd(const void* dy, const void* x, const void* g, const 
   MT_HIP(rmsnorm_bwd(static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(g), rstd, static_cast<const uint16_t*>(resid),
                      static_cast<uint16_t*>(dx), part, rows, cols, s));
-  MT_HIP(reduce_rows_to_bf16(part, rmsnorm_bwd_blocks(rows), cols, static_cast<uint16_t*>(dg), s));
+  MT_HIP(reduce_rows(part, rmsnorm_bwd_blocks(rows), cols, static_cast<uint16_t*>(dg), s));
   return MT_OK;
 }
 
@@ -127,6 +145,29 @@ mt_status mt_op_attn_bwd(const void* qkv, const void* o, const float* lse, const
   MT_HIP(attn_bwd(static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(o), lse,
                   static_cast<const uint16_t*>(dout), delta, static_cast<uint16_t*>(dqkv), batch,
                   seq, n_heads, n_kv_heads, head_dim, static_cast<hipStream_t>(stream)));
+  return MT_OK;
+}
+
+mt_status mt_op_attn_fwd_f32(const float* qkv, float* o, float* lse, int32_t batch, int32_t seq,
+                             int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream) {
+  MT_CHECK(qkv && o && lse, MT_E_INVALID, "mt_op_attn_fwd_f32: null pointer");
+  if (const char* m = attn_shape_check(batch, seq, n_heads, n_kv_heads, head_dim))
+    return set_error(MT_E_SHAPE, "mt_op_attn_fwd_f32: %s", m);
+  MT_HIP(attn_fwd(qkv, o, lse, batch, seq, n_heads, n_kv_heads, head_dim,
+                  static_cast<hipStream_t>(stream)));
+  return MT_OK;
+}
+
+mt_status mt_op_attn_bwd_f32(const float* qkv, const float* o, const float* lse,
+                             const float* dout, float* delta, float* dqkv, int32_t batch,
+                             int32_t seq, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                             void* stream) {
+  MT_CHECK(qkv && o && lse && dout && delta && dqkv, MT_E_INVALID,
+           "mt_op_attn_bwd_f32: null pointer");
+  if (const char* m = attn_shape_check(batch, seq, n_heads, n_kv_heads, head_dim))
+    return set_error(MT_E_SHAPE, "mt_op_attn_bwd_f32: %s", m);
+  MT_HIP(attn_bwd(qkv, o, lse, dout, delta, dqkv, batch, seq, n_heads, n_kv_heads, head_dim,
+                  static_cast<hipStream_t>(stream)));
   return MT_OK;
 }
 

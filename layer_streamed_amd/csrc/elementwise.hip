@@ -23,33 +23,65 @@ __device__ __forceinline__ u32x4_t pack8(const float* f) {
   return v;
 }
 
+// Storage of activations, weights and gradients: bf16 bit patterns (the
+// training path) or fp32 (the debug precision).  Math is fp32 either way.
+template <class E>
+struct St;
+template <>
+struct St<uint16_t> {
+  static __device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+    unpack8(*reinterpret_cast<const u32x4_t*>(p), f);
+  }
+  static __device__ __forceinline__ void store8(uint16_t* p, const float* f) {
+    *reinterpret_cast<u32x4_t*>(p) = pack8(f);
+  }
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f2bf(v); }
+};
+template <>
+struct St<float> {
+  static __device__ __forceinline__ void load8(const float* p, float* f) {
+    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+    const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  static __device__ __forceinline__ void store8(float* p, const float* f) {
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{f[0], f[1], f[2], f[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{f[4], f[5], f[6], f[7]};
+  }
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+
 // y = x * rsqrt(mean(x^2) + eps) * g.  One wave per row; cols % 8 == 0.
+template <class E>
 __global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_fwd_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, uint16_t* __restrict__ y,
+    const E* __restrict__ x, const E* __restrict__ g, E* __restrict__ y,
     float* __restrict__ rstd_out, int rows, int cols, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * RN_WAVES + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const uint16_t* xr = x + (long)row * cols;
+  const E* xr = x + (long)row * cols;
   const int nch = cols / 8;
   float ss = 0.f;
   for (int c = lane; c < nch; c += 64) {
     float f[8];
-    unpack8(*reinterpret_cast<const u32x4_t*>(xr + c * 8), f);
+    St<E>::load8(xr + c * 8, f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
   }
   ss = wave_sum(ss);
   const float r = 1.f / sqrtf(ss / (float)cols + eps);
   if (lane == 0 && rstd_out) rstd_out[row] = r;
-  uint16_t* yr = y + (long)row * cols;
+  E* yr = y + (long)row * cols;
   for (int c = lane; c < nch; c += 64) {
     float f[8], gg[8];
-    unpack8(*reinterpret_cast<const u32x4_t*>(xr + c * 8), f);
-    unpack8(*reinterpret_cast<const u32x4_t*>(g + c * 8), gg);
+    St<E>::load8(xr + c * 8, f);
+    St<E>::load8(g + c * 8, gg);
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = f[i] * r * gg[i];
-    *reinterpret_cast<u32x4_t*>(yr + c * 8) = pack8(f);
+    St<E>::store8(yr + c * 8, f);
   }
 }
 
@@ -59,11 +91,11 @@ __global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_fwd_kernel(
 // one partial row of dg_part.  MAXC = max chunk iterations per lane.
 constexpr int RB_ROWS = 64;
 
-template <int MAXC>
+template <class E, int MAXC>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
-    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ g, const float* __restrict__ rstd,
-    const uint16_t* __restrict__ resid, uint16_t* __restrict__ dx, float* __restrict__ dg_part,
+    const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ g,
+    const float* __restrict__ rstd, const E* __restrict__ resid, E* __restrict__ dx,
+    float* __restrict__ dg_part,
     int rows, int cols) {
   extern __shared__ float red[];  // [4][cols]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -86,9 +118,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
       const int c = lane + 64 * k;
       if (c < nch) {
         float fd[8], fx[8], fg[8];
-        unpack8(*reinterpret_cast<const u32x4_t*>(dy + off + c * 8), fd);
-        unpack8(*reinterpret_cast<const u32x4_t*>(x + off + c * 8), fx);
-        unpack8(*reinterpret_cast<const u32x4_t*>(g + c * 8), fg);
+        St<E>::load8(dy + off + c * 8, fd);
+        St<E>::load8(x + off + c * 8, fx);
+        St<E>::load8(g + c * 8, fg);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float xh = fx[i] * r;
@@ -103,10 +135,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
       const int c = lane + 64 * k;
       if (c < nch) {
         float fd[8], fx[8], fg[8], fr[8];
-        unpack8(*reinterpret_cast<const u32x4_t*>(dy + off + c * 8), fd);
-        unpack8(*reinterpret_cast<const u32x4_t*>(x + off + c * 8), fx);
-        unpack8(*reinterpret_cast<const u32x4_t*>(g + c * 8), fg);
-        if (resid) unpack8(*reinterpret_cast<const u32x4_t*>(resid + off + c * 8), fr);
+        St<E>::load8(dy + off + c * 8, fd);
+        St<E>::load8(x + off + c * 8, fx);
+        St<E>::load8(g + c * 8, fg);
+        if (resid) St<E>::load8(resid + off + c * 8, fr);
         else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) fr[i] = 0.f;
@@ -117,7 +149,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
           const float xh = fx[i] * r;
           o[i] = fr[i] + r * (fd[i] * fg[i] - xh * dot);
         }
-        *reinterpret_cast<u32x4_t*>(dx + off + c * 8) = pack8(o);
+        St<E>::store8(dx + off + c * 8, o);
       }
     }
   }
@@ -136,13 +168,14 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
   }
 }
 
+template <class E>
 __global__ void reduce_rows_kernel(const float* __restrict__ part, int nblk, int cols,
-                                   uint16_t* __restrict__ out) {
+                                   E* __restrict__ out) {
   const int col = blockIdx.x * blockDim.x + threadIdx.x;
   if (col >= cols) return;
   float s = 0.f;
   for (int b = 0; b < nblk; ++b) s += part[(long)b * cols + col];
-  out[col] = f2bf(s);
+  St<E>::store(out + col, s);
 }
 
 __global__ void rope_table_kernel(float* cos_t, float* sin_t, int seq, int half, int head_dim,
@@ -157,7 +190,8 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, int seq, int half,
 }
 
 // One thread per (token, head, pair j): rotates (x_j, x_{j+d/2}).
-__global__ void rope_kernel(uint16_t* __restrict__ qkv, long ldq, int tokens, int seq, int nh,
+template <class E>
+__global__ void rope_kernel(E* __restrict__ qkv, long ldq, int tokens, int seq, int nh,
                             int half, const float* __restrict__ cos_t,
                             const float* __restrict__ sin_t, float sgn) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -168,29 +202,31 @@ __global__ void rope_kernel(uint16_t* __restrict__ qkv, long ldq, int tokens, in
   const int h = (int)(th % nh);
   const int tok = (int)(th / nh);
   const int t = tok % seq;
-  uint16_t* p = qkv + (long)tok * ldq + (long)h * 2 * half;
+  E* p = qkv + (long)tok * ldq + (long)h * 2 * half;
   const float c = cos_t[t * half + j], sn = sgn * sin_t[t * half + j];
-  const float x1 = bf2f(p[j]), x2 = bf2f(p[j + half]);
-  p[j] = f2bf(x1 * c - x2 * sn);
-  p[j + half] = f2bf(x2 * c + x1 * sn);
+  const float x1 = St<E>::load(p + j), x2 = St<E>::load(p + j + half);
+  St<E>::store(p + j, x1 * c - x2 * sn);
+  St<E>::store(p + j + half, x2 * c + x1 * sn);
 }
 
 // Cross-entropy over one row of fp32 logits per workgroup (256 threads):
-// pass 1 online max/sum, pass 2 writes (softmax - onehot) * inv_n as bf16.
+// pass 1 online max/sum, pass 2 writes (softmax - onehot) * inv_n.
+template <class E>
 __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ logits,
                                                       const int32_t* __restrict__ target,
-                                                      uint16_t* __restrict__ dlogits,
+                                                      E* __restrict__ dlogits,
                                                       float* __restrict__ loss_part, int vocab,
                                                       float inv_n) {
   __shared__ float sm[2][4];
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* lr = logits + (long)row * vocab;
-  uint16_t* dr = dlogits + (long)row * vocab;
+  E* dr = dlogits + (long)row * vocab;
   const int tgt = target[row];
   if (tgt < 0 || tgt >= vocab) {
     for (int c = tid * 4; c < vocab; c += 1024)
-      *reinterpret_cast<u32x2_t*>(dr + c) = u32x2_t{0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) St<E>::store(dr + c + i, 0.f);
     if (tid == 0) loss_part[row] = 0.f;
     return;
   }
@@ -225,10 +261,8 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (c + i == tgt) p[i] -= 1.f;
-    u32x2_t o;
-    o.x = pack_bf(p[0] * inv_n, p[1] * inv_n);
-    o.y = pack_bf(p[2] * inv_n, p[3] * inv_n);
-    *reinterpret_cast<u32x2_t*>(dr + c) = o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) St<E>::store(dr + c + i, p[i] * inv_n);
   }
   if (tid == 0) loss_part[row] = (M + logf(S)) - lr[tgt];
 }
@@ -249,9 +283,10 @@ __global__ __launch_bounds__(256) void sum_kernel(const float* __restrict__ part
   if (threadIdx.x == 0) out[0] = sh[0] * scale;
 }
 
-__global__ void cast_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, size_t n) {
+template <class E>
+__global__ void cast_kernel(const float* __restrict__ in, E* __restrict__ out, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = f2bf(in[i]);
+  if (i < n) St<E>::store(out + i, in[i]);
 }
 
 __global__ void fill_kernel(float* __restrict__ p, float v, size_t n) {
@@ -295,19 +330,19 @@ hipError_t copy_d2h(const void* src, void* dst_host, size_t bytes, int blocks, h
   return hipGetLastError();
 }
 
-hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int rows,
-                       int cols, float eps, hipStream_t s) {
+namespace {
+template <class E>
+hipError_t rmsnorm_fwd_t(const E* x, const E* g, E* y, float* rstd, int rows, int cols, float eps,
+                         hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((rows + RN_WAVES - 1) / RN_WAVES),
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel<E>, dim3((rows + RN_WAVES - 1) / RN_WAVES),
                      dim3(RN_WAVES * 64), 0, s, x, g, y, rstd, rows, cols, eps);
   return hipGetLastError();
 }
 
-int rmsnorm_bwd_blocks(int rows) { return (rows + RB_ROWS - 1) / RB_ROWS; }
-
-hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
-                       const float* rstd, const uint16_t* resid, uint16_t* dx, float* dg_part,
-                       int rows, int cols, hipStream_t s) {
+template <class E>
+hipError_t rmsnorm_bwd_t(const E* dy, const E* x, const E* g, const float* rstd, const E* resid,
+                         E* dx, float* dg_part, int rows, int cols, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int nch = cols / 8;
   const int iters = (nch + 63) / 64;
@@ -317,13 +352,13 @@ hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
   if (iters <= C) {                                                                        \
     static bool attr = false;                                                              \
     if (!attr) {                                                                           \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rmsnorm_bwd_kernel<C>), \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rmsnorm_bwd_kernel<E, C>), \
                                          hipFuncAttributeMaxDynamicSharedMemorySize,       \
                                          4 * 8192 * (int)sizeof(float));                   \
       if (e != hipSuccess) return e;                                                       \
       attr = true;                                                                         \
     }                                                                                      \
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<C>, grid, block, lds, s, dy, x, g, rstd, resid, dx, \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, C>), grid, block, lds, s, dy, x, g, rstd, resid, dx, \
                        dg_part, rows, cols);                                               \
     return hipGetLastError();                                                              \
   }
@@ -332,11 +367,93 @@ hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
   return hipErrorInvalidValue;
 }
 
-hipError_t reduce_rows_to_bf16(const float* part, int nblk, int cols, uint16_t* out,
-                               hipStream_t s) {
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, part, nblk,
+template <class E>
+hipError_t reduce_rows_t(const float* part, int nblk, int cols, E* out, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_rows_kernel<E>, dim3((cols + 255) / 256), dim3(256), 0, s, part, nblk,
                      cols, out);
   return hipGetLastError();
+}
+
+template <class E>
+hipError_t rope_apply_t(E* qkv, long ldq, int batch, int seq, int n_heads, int n_kv_heads,
+                        int head_dim, const float* cos_t, const float* sin_t, int inverse,
+                        hipStream_t s) {
+  const int tokens = batch * seq, nh = n_heads + n_kv_heads, half = head_dim / 2;
+  const long total = (long)tokens * nh * half;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_kernel<E>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, qkv,
+                     ldq, tokens, seq, nh, half, cos_t, sin_t, inverse ? -1.f : 1.f);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t ce_rows_t(const float* logits, const int32_t* target, E* dlogits, float* loss_part,
+                     int rows, int vocab, float inv_n, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_rows_kernel<E>, dim3(rows), dim3(256), 0, s, logits, target, dlogits,
+                     loss_part, vocab, inv_n);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t cast_t(const float* in, E* out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_kernel<E>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+}  // namespace
+
+int rmsnorm_bwd_blocks(int rows) { return (rows + RB_ROWS - 1) / RB_ROWS; }
+
+hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int rows,
+                       int cols, float eps, hipStream_t s) {
+  return rmsnorm_fwd_t(x, g, y, rstd, rows, cols, eps, s);
+}
+hipError_t rmsnorm_fwd(const float* x, const float* g, float* y, float* rstd, int rows, int cols,
+                       float eps, hipStream_t s) {
+  return rmsnorm_fwd_t(x, g, y, rstd, rows, cols, eps, s);
+}
+hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
+                       const float* rstd, const uint16_t* resid, uint16_t* dx, float* dg_part,
+                       int rows, int cols, hipStream_t s) {
+  return rmsnorm_bwd_t(dy, x, g, rstd, resid, dx, dg_part, rows, cols, s);
+}
+hipError_t rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd,
+                       const float* resid, float* dx, float* dg_part, int rows, int cols,
+                       hipStream_t s) {
+  return rmsnorm_bwd_t(dy, x, g, rstd, resid, dx, dg_part, rows, cols, s);
+}
+hipError_t reduce_rows(const float* part, int nblk, int cols, uint16_t* out, hipStream_t s) {
+  return reduce_rows_t(part, nblk, cols, out, s);
+}
+hipError_t reduce_rows(const float* part, int nblk, int cols, float* out, hipStream_t s) {
+  return reduce_rows_t(part, nblk, cols, out, s);
+}
+hipError_t rope_apply(uint16_t* qkv, long ldq, int batch, int seq, int n_heads, int n_kv_heads,
+                      int head_dim, const float* cos_t, const float* sin_t, int inverse,
+                      hipStream_t s) {
+  return rope_apply_t(qkv, ldq, batch, seq, n_heads, n_kv_heads, head_dim, cos_t, sin_t, inverse,
+                      s);
+}
+hipError_t rope_apply(float* qkv, long ldq, int batch, int seq, int n_heads, int n_kv_heads,
+                      int head_dim, const float* cos_t, const float* sin_t, int inverse,
+                      hipStream_t s) {
+  return rope_apply_t(qkv, ldq, batch, seq, n_heads, n_kv_heads, head_dim, cos_t, sin_t, inverse,
+                      s);
+}
+hipError_t ce_rows(const float* logits, const int32_t* target, uint16_t* dlogits,
+                   float* loss_part, int rows, int vocab, float inv_n, hipStream_t s) {
+  return ce_rows_t(logits, target, dlogits, loss_part, rows, vocab, inv_n, s);
+}
+hipError_t ce_rows(const float* logits, const int32_t* target, float* dlogits, float* loss_part,
+                   int rows, int vocab, float inv_n, hipStream_t s) {
+  return ce_rows_t(logits, target, dlogits, loss_part, rows, vocab, inv_n, s);
+}
+hipError_t cast_f32(const float* in, uint16_t* out, size_t n, hipStream_t s) {
+  return cast_t(in, out, n, s);
+}
+hipError_t cast_f32(const float* in, float* out, size_t n, hipStream_t s) {
+  return cast_t(in, out, n, s);
 }
 
 hipError_t rope_table(float* cos_t, float* sin_t, int seq, int head_dim, double theta,
@@ -348,35 +465,13 @@ hipError_t rope_table(float* cos_t, float* sin_t, int seq, int head_dim, double 
   return hipGetLastError();
 }
 
-hipError_t rope_apply(uint16_t* qkv, long ldq, int batch, int seq, int n_heads, int n_kv_heads,
-                      int head_dim, const float* cos_t, const float* sin_t, int inverse,
-                      hipStream_t s) {
-  const int tokens = batch * seq, nh = n_heads + n_kv_heads, half = head_dim / 2;
-  const long total = (long)tokens * nh * half;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, qkv,
-                     ldq, tokens, seq, nh, half, cos_t, sin_t, inverse ? -1.f : 1.f);
-  return hipGetLastError();
-}
 
-hipError_t ce_rows(const float* logits, const int32_t* target, uint16_t* dlogits,
-                   float* loss_part, int rows, int vocab, float inv_n, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_rows_kernel, dim3(rows), dim3(256), 0, s, logits, target, dlogits,
-                     loss_part, vocab, inv_n);
-  return hipGetLastError();
-}
 
 hipError_t sum_loss(const float* part, int n, float inv_n, float* out, hipStream_t s) {
   hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(256), 0, s, part, n, inv_n, out);
   return hipGetLastError();
 }
 
-hipError_t cast_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(cast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in, out, n);
-  return hipGetLastError();
-}
 
 hipError_t fill_f32(float* p, float v, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;

@@ -96,14 +96,16 @@ namespace {
 
 constexpr int NG = 4;  // device gradient ring depth
 
+// Device buffers of one step.  Weight slots, gradient buffers and
+// activations hold the model's streamed element type (es bytes each).
 struct Arena {
-  std::vector<uint16_t*> slot;
-  uint16_t* head_slot = nullptr;
-  uint16_t* gring[NG] = {};
-  uint16_t* head_grad = nullptr;
-  uint16_t* act[2] = {};
-  std::vector<uint16_t*> ckpt, seg;
-  uint16_t* dy = nullptr;
+  std::vector<char*> slot;
+  char* head_slot = nullptr;
+  char* gring[NG] = {};
+  char* head_grad = nullptr;
+  char* act[2] = {};
+  std::vector<char*> ckpt, seg;
+  char* dy = nullptr;
   int32_t* tgt = nullptr;
   float* loss = nullptr;
   void* lws = nullptr;
@@ -116,17 +118,18 @@ Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
   Carve c{base};
   Arena a;
   const int L = M->cfg.n_layers, K = M->run.ckpt_interval;
-  const size_t lay = M->ll.total, head = M->hl.total, act = (size_t)d.D * d.H;
+  const size_t es = M->es;
+  const size_t lay = M->ll.total * es, head = M->hl.total * es, act = (size_t)d.D * d.H * es;
   const int ns = plan_slots(K, M->run.prefetch_depth);
-  for (int i = 0; i < ns; ++i) a.slot.push_back(c.take<uint16_t>(lay));
-  a.head_slot = c.take<uint16_t>(head);
-  for (int i = 0; i < NG; ++i) a.gring[i] = c.take<uint16_t>(lay);
-  a.head_grad = c.take<uint16_t>(head);
-  a.act[0] = c.take<uint16_t>(act);
-  a.act[1] = c.take<uint16_t>(act);
-  for (int i = 0; i <= L / K; ++i) a.ckpt.push_back(c.take<uint16_t>(act));
-  for (int i = 0; i < K - 1; ++i) a.seg.push_back(c.take<uint16_t>(act));
-  a.dy = c.take<uint16_t>(act);
+  for (int i = 0; i < ns; ++i) a.slot.push_back(c.take<char>(lay));
+  a.head_slot = c.take<char>(head);
+  for (int i = 0; i < NG; ++i) a.gring[i] = c.take<char>(lay);
+  a.head_grad = c.take<char>(head);
+  a.act[0] = c.take<char>(act);
+  a.act[1] = c.take<char>(act);
+  for (int i = 0; i <= L / K; ++i) a.ckpt.push_back(c.take<char>(act));
+  for (int i = 0; i < K - 1; ++i) a.seg.push_back(c.take<char>(act));
+  a.dy = c.take<char>(act);
   a.tgt = c.take<int32_t>(d.D);
   a.loss = c.take<float>(64);
   a.lws_bytes = layer_ws_bytes(d, 1);
@@ -137,27 +140,29 @@ Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
   return a;
 }
 
-mt_layer_view layer_view(const mt_model* M, const uint16_t* slab) {
+mt_layer_view layer_view(const mt_model* M, const char* slab) {
   const LayerLayout& l = M->ll;
+  const size_t es = M->es;
   mt_layer_view v;
-  v.attn_norm = slab + l.attn_norm;
-  v.w_qkv = slab + l.w_qkv;
-  v.w_o = slab + l.w_o;
-  v.mlp_norm = slab + l.mlp_norm;
-  v.w_gate_up = slab + l.w_gate_up;
-  v.w_down = slab + l.w_down;
+  v.attn_norm = slab + l.attn_norm * es;
+  v.w_qkv = slab + l.w_qkv * es;
+  v.w_o = slab + l.w_o * es;
+  v.mlp_norm = slab + l.mlp_norm * es;
+  v.w_gate_up = slab + l.w_gate_up * es;
+  v.w_down = slab + l.w_down * es;
   return v;
 }
 
-mt_layer_grad_view grad_view(const mt_model* M, uint16_t* slab) {
+mt_layer_grad_view grad_view(const mt_model* M, char* slab) {
   const LayerLayout& l = M->ll;
+  const size_t es = M->es;
   mt_layer_grad_view v;
-  v.attn_norm = slab + l.attn_norm;
-  v.w_qkv = slab + l.w_qkv;
-  v.w_o = slab + l.w_o;
-  v.mlp_norm = slab + l.mlp_norm;
-  v.w_gate_up = slab + l.w_gate_up;
-  v.w_down = slab + l.w_down;
+  v.attn_norm = slab + l.attn_norm * es;
+  v.w_qkv = slab + l.w_qkv * es;
+  v.w_o = slab + l.w_o * es;
+  v.mlp_norm = slab + l.mlp_norm * es;
+  v.w_gate_up = slab + l.w_gate_up * es;
+  v.w_down = slab + l.w_down * es;
   return v;
 }
 
@@ -187,7 +192,7 @@ float elapsed(hipEvent_t a, hipEvent_t b) {
 
 struct Offload {
   int unit;          // -1 = dx0
-  const uint16_t* src;
+  const char* src;
   size_t elems;
   hipEvent_t after;  // compute event the copy waits for
   int ring;          // gradient ring index or -1
@@ -196,7 +201,7 @@ struct Offload {
 
 struct Landed {
   int unit;
-  uint16_t* host;  // slab (or dx0 staging)
+  void* host;      // slab (or dx0 staging)
   bool own_alloc;  // allocated for this transfer (no pool)
   hipEvent_t ev;
   bool end = false;
@@ -332,8 +337,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   // pinned per-step staging
   if (M->staging_tokens < (size_t)d.D) {
     const size_t nt = (size_t)d.D;
-    M->x0_host = static_cast<uint16_t*>(M->host_alloc(nt * d.H * 2, true));
-    M->dx0_host = static_cast<uint16_t*>(M->host_alloc(nt * d.H * 2, true));
+    M->x0_host = M->host_alloc(nt * d.H * M->es, true);
+    M->dx0_host = M->host_alloc(nt * d.H * M->es, true);
     M->tgt_host = static_cast<int32_t*>(M->host_alloc(nt * 4, true));
     M->loss_host = static_cast<float*>(M->host_alloc(64, true));
     MT_CHECK(M->x0_host && M->dx0_host && M->tgt_host && M->loss_host, MT_E_OOM_HOST,
@@ -350,13 +355,15 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   Events ev{&M->events};
   mt_status fail = MT_OK;
   const size_t act = (size_t)d.D * d.H;
+  const size_t es = M->es;
+  const bool f32 = es == 4;
 
-  // host: targets and the embedding gather (from the bf16 copy)
+  // host: targets and the embedding gather (from the streamed copy)
   const Unit& emb = M->units[L + 1];
   for (int b = 0; b < d.B; ++b)
     for (int t = 0; t < d.T; ++t)
       M->tgt_host[(size_t)b * d.T + t] = t + 1 < d.T ? tokens[(size_t)b * d.T + t + 1] : -1;
-  embed_gather(emb.shadow, tokens, (size_t)d.D, (size_t)d.H, M->x0_host, M->pool.get());
+  embed_gather(emb.shadow, tokens, (size_t)d.D, (size_t)d.H * es, M->x0_host, M->pool.get());
   const float inv_n = 1.f / (float)((size_t)d.B * (d.T - 1));
 
   // thread state
@@ -405,7 +412,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         landq.push(Landed{0, nullptr, false, nullptr, true});
         return;
       }
-      uint16_t* host = nullptr;
+      void* host = nullptr;
       bool own = false;
       bool ok = !abort_all.load();
       if (ok) {
@@ -416,8 +423,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           host = M->slabs.acquire();
           slab_wait_ms += ms_since(tw);
         } else {
-          ok = hipHostMalloc(reinterpret_cast<void**>(&host), M->slab_elems * 2,
-                             hipHostMallocDefault) == hipSuccess;
+          ok = hipHostMalloc(&host, M->slab_elems * es, hipHostMallocDefault) == hipSuccess;
           own = ok;
         }
       }
@@ -428,9 +434,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       }
       if (ok) {
         const auto t0 = clock::now();
-        ok = M->sdma->copy_d2h(host, o.src, o.elems * 2);
+        ok = M->sdma->copy_d2h(host, o.src, o.elems * es);
         d2h_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-        d2h_bytes += (double)o.elems * 2;
+        d2h_bytes += (double)o.elems * es;
       }
       if (o.ring >= 0) {
         std::lock_guard<std::mutex> lk(ring_mu);
@@ -480,24 +486,35 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       if (!skip) {
         if (x.unit >= 0) {
           Unit& u = M->units[x.unit];
-          if (M->run.check_finite && !grad_finite(x.host, nullptr, u.n, M->pool.get())) {
+          const uint16_t* gb = f32 ? nullptr : static_cast<const uint16_t*>(x.host);
+          const float* gf = f32 ? static_cast<const float*>(x.host) : nullptr;
+          if (M->run.check_finite && !grad_finite(gb, gf, u.n, M->pool.get())) {
             a_fail = 2;
             abort_all = true;
             skip = true;
           } else {
-            adam_parallel(u.master, u.m, u.v, x.host, nullptr, u.shadow, u.n, hp, M->pool.get());
-            if (u.kept) memcpy(u.kept, x.host, u.n * 2);
+            adam_parallel(u.master, u.m, u.v, gb, gf,
+                          f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
+                          f32 ? static_cast<float*>(u.shadow) : nullptr, u.n, hp, M->pool.get());
+            if (u.kept) memcpy(u.kept, x.host, u.n * es);
             ++units_updated;
           }
         } else {
           Unit& u = M->units[L + 1];
-          embed_scatter_add(x.host, tokens, (size_t)d.D, (size_t)d.H, dE, M->pool.get());
+          if (f32)
+            embed_scatter_add(static_cast<const float*>(x.host), tokens, (size_t)d.D,
+                              (size_t)d.H, dE, M->pool.get());
+          else
+            embed_scatter_add(static_cast<const uint16_t*>(x.host), tokens, (size_t)d.D,
+                              (size_t)d.H, dE, M->pool.get());
           if (M->run.check_finite && !grad_finite(nullptr, dE, (size_t)d.V * d.H, M->pool.get())) {
             a_fail = 2;
             abort_all = true;
             skip = true;
           } else {
-            adam_parallel(u.master, u.m, u.v, nullptr, dE, u.shadow, (size_t)d.V * d.H, hp,
+            adam_parallel(u.master, u.m, u.v, nullptr, dE,
+                          f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
+                          f32 ? static_cast<float*>(u.shadow) : nullptr, (size_t)d.V * d.H, hp,
                           M->pool.get());
             ++units_updated;
           }
@@ -531,17 +548,17 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
 
   {
     // gradient buffers: pads must read as zero
-    MT_STEP_HIP(hipMemsetAsync(A.head_grad, 0, M->hl.total * 2, sC));
-    for (int i = 0; i < NG; ++i) MT_STEP_HIP(hipMemsetAsync(A.gring[i], 0, M->ll.total * 2, sC));
+    MT_STEP_HIP(hipMemsetAsync(A.head_grad, 0, M->hl.total * es, sC));
+    for (int i = 0; i < NG; ++i) MT_STEP_HIP(hipMemsetAsync(A.gring[i], 0, M->ll.total * es, sC));
     MT_STEP_HIP(hipEventRecord(ph_start, sC));
     // inputs of the step
-    MT_STEP_HIP(hipMemcpyAsync(A.ckpt[0], M->x0_host, act * 2, hipMemcpyHostToDevice, sW));
+    MT_STEP_HIP(hipMemcpyAsync(A.ckpt[0], M->x0_host, act * es, hipMemcpyHostToDevice, sW));
     MT_STEP_HIP(hipMemcpyAsync(A.tgt, M->tgt_host, (size_t)d.D * 4, hipMemcpyHostToDevice, sW));
     MT_STEP_HIP(hipEventRecord(x0_ready, sW));
-    h2d_bytes += (double)act * 2 + (double)d.D * 4;
+    h2d_bytes += (double)act * es + (double)d.D * 4;
     MT_STEP_HIP(hipStreamWaitEvent(sC, x0_ready, 0));
 
-    auto xloc = [&](int i) -> uint16_t* { return (i % K == 0) ? A.ckpt[i / K] : A.act[i % 2]; };
+    auto xloc = [&](int i) -> char* { return (i % K == 0) ? A.ckpt[i / K] : A.act[i % 2]; };
 
     for (size_t i = 0; i < plan.ops.size(); ++i) {
       // weight loads whose slot and look-ahead dependencies are enqueued
@@ -552,19 +569,19 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         if (ld.gate_use >= 0 && ld.gate_use != ld.wait_use)
           MT_STEP_HIP(hipStreamWaitEvent(sW, op_done[ld.gate_use], 0));
         const Unit& u = M->units[ld.unit];
-        uint16_t* dst = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+        char* dst = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
         hipEvent_t c0 = get_ev(), c1 = get_ev();
         MT_STEP_HIP(hipEventRecord(c0, sW));
-        MT_STEP_HIP(hipMemcpyAsync(dst, u.shadow, u.n * 2, hipMemcpyHostToDevice, sW));
+        MT_STEP_HIP(hipMemcpyAsync(dst, u.shadow, u.n * es, hipMemcpyHostToDevice, sW));
         MT_STEP_HIP(hipEventRecord(c1, sW));
         MT_STEP_HIP(hipEventRecord(load_done[next_load], sW));
         h2d_ev.push_back({c0, c1});
-        h2d_bytes += (double)u.n * 2;
+        h2d_bytes += (double)u.n * es;
         ++next_load;
       }
       const PlanOp& op = plan.ops[i];
       const PlanLoad& ld = plan.loads[op.load];
-      const uint16_t* w = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+      const char* w = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
       // wait for this op's weights; the gap is the exposed transfer time
       hipEvent_t w0 = get_ev(), w1 = get_ev();
       MT_STEP_HIP(hipEventRecord(w0, sC));
@@ -577,9 +594,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
                                    sC, M->run.time_kernels ? &probe : nullptr));
         if (l == L - 1) MT_STEP_HIP(hipEventRecord(ph_fwd, sC));
       } else if (op.kind == OP_HEAD) {
-        MT_STEP_RUN(head_impl(d, w + M->hl.final_norm, w + M->hl.lm_head, xloc(L), A.tgt, inv_n,
-                              A.dy, A.head_grad + M->hl.final_norm, A.head_grad + M->hl.lm_head,
-                              A.loss, A.hws, A.hws_bytes, sC));
+        MT_STEP_RUN(head_impl(d, w + M->hl.final_norm * es, w + M->hl.lm_head * es, xloc(L), A.tgt,
+                              inv_n, A.dy, A.head_grad + M->hl.final_norm * es,
+                              A.head_grad + M->hl.lm_head * es, A.loss, A.hws, A.hws_bytes, sC));
         MT_STEP_HIP(hipMemcpyAsync(M->loss_host, A.loss, 4, hipMemcpyDeviceToHost, sC));
         MT_STEP_HIP(hipEventRecord(loss_ev, sC));
         {
@@ -593,12 +610,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         continue;
       } else if (op.kind == OP_REFWD) {
         const int l = op.layer, a = (l / K) * K;
-        const uint16_t* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
+        const char* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
         MT_STEP_RUN(layer_fwd_impl(d, layer_view(M, w), in, A.seg[l - a], A.lws, A.lws_bytes, sC,
                                    M->run.time_kernels ? &probe : nullptr));
       } else {  // OP_BWD
         const int l = op.layer, a = (l / K) * K;
-        const uint16_t* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
+        const char* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
         const int r = bwd_count % NG;
         if (bwd_count >= NG) {  // the ring slot's previous gradient must have left
           const auto tw = clock::now();
@@ -611,7 +628,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           }
         }
         MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
-                                   A.lws, A.lws_bytes, sC, nullptr));
+                                   A.lws, A.lws_bytes, sC));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
         Offload o{l, A.gring[r], M->ll.total, op_done[i], r};
         offq.push(o);

@@ -95,9 +95,10 @@ inline uint32_t f2bf_bits(uint32_t u) {
   return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? q : r;
 }
 
-template <bool BF16_GRAD, bool SHADOW>
+// SHADOW: 0 none, 1 bf16 streamed copy, 2 fp32 streamed copy.
+template <bool BF16_GRAD, int SHADOW>
 void adam_loop(float* __restrict p, float* __restrict m, float* __restrict v,
-               const void* __restrict graw, uint16_t* __restrict shadow, size_t lo, size_t hi,
+               const void* __restrict graw, void* __restrict shadow, size_t lo, size_t hi,
                const AdamHp& h) {
   const float b1 = h.b1, omb1 = h.omb1, b2 = h.b2, omb2 = h.omb2;
   const float bc1 = h.bc1, bc2 = h.bc2, lr = h.lr, eps = h.eps;
@@ -119,10 +120,12 @@ void adam_loop(float* __restrict p, float* __restrict m, float* __restrict v,
     m[i] = mi;
     v[i] = vi;
     p[i] = pi;
-    if constexpr (SHADOW) {
+    if constexpr (SHADOW == 1) {
       uint32_t pu;
       __builtin_memcpy(&pu, &pi, 4);
-      shadow[i] = (uint16_t)f2bf_bits(pu);
+      static_cast<uint16_t*>(shadow)[i] = (uint16_t)f2bf_bits(pu);
+    } else if constexpr (SHADOW == 2) {
+      static_cast<float*>(shadow)[i] = pi;
     }
   }
 }
@@ -130,13 +133,15 @@ void adam_loop(float* __restrict p, float* __restrict m, float* __restrict v,
 }  // namespace
 
 void adam_range(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                uint16_t* shadow, size_t lo, size_t hi, const AdamHp& h) {
+                uint16_t* sb, float* sf, size_t lo, size_t hi, const AdamHp& h) {
   if (gb) {
-    if (shadow) adam_loop<true, true>(p, m, v, gb, shadow, lo, hi, h);
-    else adam_loop<true, false>(p, m, v, gb, nullptr, lo, hi, h);
+    if (sb) adam_loop<true, 1>(p, m, v, gb, sb, lo, hi, h);
+    else if (sf) adam_loop<true, 2>(p, m, v, gb, sf, lo, hi, h);
+    else adam_loop<true, 0>(p, m, v, gb, nullptr, lo, hi, h);
   } else {
-    if (shadow) adam_loop<false, true>(p, m, v, gf, shadow, lo, hi, h);
-    else adam_loop<false, false>(p, m, v, gf, nullptr, lo, hi, h);
+    if (sb) adam_loop<false, 1>(p, m, v, gf, sb, lo, hi, h);
+    else if (sf) adam_loop<false, 2>(p, m, v, gf, sf, lo, hi, h);
+    else adam_loop<false, 0>(p, m, v, gf, nullptr, lo, hi, h);
   }
 }
 
@@ -162,35 +167,51 @@ bool grad_finite(const uint16_t* gb, const float* gf, size_t n, ThreadPool* pool
 }
 
 void adam_parallel(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                   uint16_t* shadow, size_t n, const AdamHp& h, ThreadPool* pool) {
-  auto body = [&](size_t lo, size_t hi) { adam_range(p, m, v, gb, gf, shadow, lo, hi, h); };
+                   uint16_t* sb, float* sf, size_t n, const AdamHp& h, ThreadPool* pool) {
+  auto body = [&](size_t lo, size_t hi) { adam_range(p, m, v, gb, gf, sb, sf, lo, hi, h); };
   if (pool) pool->parallel_for(n, body);
   else body(0, n);
 }
 
-void embed_gather(const uint16_t* table, const int32_t* ids, size_t n_tok, size_t H,
-                  uint16_t* out, ThreadPool* pool) {
+void embed_gather(const void* table, const int32_t* ids, size_t n_tok, size_t row_bytes,
+                  void* out, ThreadPool* pool) {
+  const char* tb = static_cast<const char*>(table);
+  char* ob = static_cast<char*>(out);
   auto body = [&](size_t lo, size_t hi) {
-    for (size_t t = lo; t < hi; ++t)
-      memcpy(out + t * H, table + (size_t)ids[t] * H, H * sizeof(uint16_t));
+    for (size_t t = lo; t < hi; ++t) memcpy(ob + t * row_bytes, tb + (size_t)ids[t] * row_bytes, row_bytes);
   };
   if (pool) pool->parallel_for(n_tok, body, 64);
   else body(0, n_tok);
 }
 
-void embed_scatter_add(const uint16_t* dx0, const int32_t* ids, size_t n_tok, size_t H,
-                       float* dE, ThreadPool* pool) {
+namespace {
+inline float to_f32(uint16_t b) { return host_bf2f(b); }
+inline float to_f32(float f) { return f; }
+
+template <class G>
+void scatter_add_t(const G* dx0, const int32_t* ids, size_t n_tok, size_t H, float* dE,
+                   ThreadPool* pool) {
   // each worker owns a column slice and walks every token in order, so the
   // summation order per element is the token order regardless of threads
   auto body = [&](size_t c0, size_t c1) {
     for (size_t t = 0; t < n_tok; ++t) {
       float* row = dE + (size_t)ids[t] * H;
-      const uint16_t* src = dx0 + t * H;
-      for (size_t c = c0; c < c1; ++c) row[c] += host_bf2f(src[c]);
+      const G* src = dx0 + t * H;
+      for (size_t c = c0; c < c1; ++c) row[c] += to_f32(src[c]);
     }
   };
   if (pool) pool->parallel_for(H, body, 64);
   else body(0, H);
+}
+}  // namespace
+
+void embed_scatter_add(const uint16_t* dx0, const int32_t* ids, size_t n_tok, size_t H,
+                       float* dE, ThreadPool* pool) {
+  scatter_add_t(dx0, ids, n_tok, H, dE, pool);
+}
+void embed_scatter_add(const float* dx0, const int32_t* ids, size_t n_tok, size_t H, float* dE,
+                       ThreadPool* pool) {
+  scatter_add_t(dx0, ids, n_tok, H, dE, pool);
 }
 
 }  // namespace mt
@@ -248,7 +269,8 @@ mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq, const vo
   }
   if (hp->check_finite && !grad_finite(gb, gf, n, pool))
     return set_error(MT_E_NONFINITE, "mt_host_adam: gradient has NaN or Inf; nothing updated");
-  adam_parallel(param, exp_avg, exp_avg_sq, gb, gf, bf16_shadow, n, adam_hp(*hp, step), pool);
+  adam_parallel(param, exp_avg, exp_avg_sq, gb, gf, bf16_shadow, nullptr, n, adam_hp(*hp, step),
+                pool);
   return MT_OK;
 }
 

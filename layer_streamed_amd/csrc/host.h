@@ -42,13 +42,15 @@ struct AdamHp {
 };
 AdamHp adam_hp(const mt_run_cfg& hp, int64_t step);
 
-// One Adam update over [lo, hi): grad is bf16 (gb) or fp32 (gf).
+// One Adam update over [lo, hi): grad is bf16 (gb) or fp32 (gf).  The
+// updated master is also written to the streamed copy when one is given:
+// bf16 (sb, round to nearest even) or fp32 (sf, the debug precision).
 void adam_range(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                uint16_t* shadow, size_t lo, size_t hi, const AdamHp& h);
+                uint16_t* sb, float* sf, size_t lo, size_t hi, const AdamHp& h);
 // True if every gradient value in [0, n) is finite.
 bool grad_finite(const uint16_t* gb, const float* gf, size_t n, ThreadPool* pool);
 void adam_parallel(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                   uint16_t* shadow, size_t n, const AdamHp& h, ThreadPool* pool);
+                   uint16_t* sb, float* sf, size_t n, const AdamHp& h, ThreadPool* pool);
 
 inline uint16_t host_f2bf(float f) {
   uint32_t u;
@@ -63,11 +65,14 @@ inline float host_bf2f(uint16_t b) {
   return f;
 }
 
-// x0[t] = table[ids[t]] (bf16 rows of width H).
-void embed_gather(const uint16_t* table, const int32_t* ids, size_t n_tok, size_t H,
-                  uint16_t* out, ThreadPool* pool);
-// dE[ids[t]] += dx0[t] in token order (fp32 accumulate; dE pre-zeroed).
+// x0[t] = table[ids[t]] (rows of row_bytes bytes: H bf16 or H fp32 values).
+void embed_gather(const void* table, const int32_t* ids, size_t n_tok, size_t row_bytes,
+                  void* out, ThreadPool* pool);
+// dE[ids[t]] += dx0[t] in token order (fp32 accumulate; dE pre-zeroed);
+// dx0 rows are H bf16 or H fp32 values.
 void embed_scatter_add(const uint16_t* dx0, const int32_t* ids, size_t n_tok, size_t H,
                        float* dE, ThreadPool* pool);
+void embed_scatter_add(const float* dx0, const int32_t* ids, size_t n_tok, size_t H, float* dE,
+                       ThreadPool* pool);
 
 }  // namespace mt

@@ -9,56 +9,71 @@
 namespace mt {
 
 // ---------------------------------------------------------------- GEMM
-// C[M, N] = op(A) * op(B) with fp32 accumulation on bf16 MFMA.
+// C[M, N] = op(A) * op(B) with fp32 accumulation.  Operands are stored as
+// E: bf16 bit patterns (uint16_t; bf16 MFMA kernels) or fp32 (float; the
+// fp32 debug precision, plain fp32 FMA).  "Storage" below means E.
 //  NT: A [M, K] (row stride lda), B [N, K] (ldb)      C = A B^T
 //  NN: A [M, K],                  B [K, N]            C = A B
 //  TN: A [K, M],                  B [K, N]            C = A^T B
 enum GemmLayout { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
 
 enum GemmEpi {
-  EPI_BF16 = 0,        // C (bf16) = acc
+  EPI_BF16 = 0,        // C (storage) = acc
   EPI_F32 = 1,         // C (fp32) = acc
   EPI_ACC_F32 = 2,     // C (fp32) += acc
-  EPI_RESID_BF16 = 3,  // C (bf16) = R (bf16) + acc
+  EPI_RESID_BF16 = 3,  // C (storage) = R (storage) + acc
   EPI_SWIGLU = 4,      // NT only; B = [W_gate; W_up] (2F rows); N = 2F:
-                       //   C (bf16) [M, F] = silu(gate) * up
-  EPI_SWIGLU_SAVE = 5, // as EPI_SWIGLU, and C2 (bf16) [M, 2F] = [gate | up]
-  EPI_SWIGLU_BWD = 6   // acc = dm [M, F]; G = [gate | up] (bf16, ldg);
-                       //   C2 (bf16) [M, 2F] = [dgate | dup]
+                       //   C (storage) [M, F] = silu(gate) * up
+  EPI_SWIGLU_SAVE = 5, // as EPI_SWIGLU, and C2 (storage) [M, 2F] = [gate | up]
+  EPI_SWIGLU_BWD = 6   // acc = dm [M, F]; G = [gate | up] (storage, ldg);
+                       //   C2 (storage) [M, 2F] = [dgate | dup]
 };
 
-struct GemmArgs {
+template <class E>
+struct GemmArgsT {
   int layout = GEMM_NT, epi = EPI_BF16;
   int M = 0, N = 0, K = 0;
-  const uint16_t* A = nullptr; long lda = 0;
-  const uint16_t* B = nullptr; long ldb = 0;
+  const E* A = nullptr; long lda = 0;
+  const E* B = nullptr; long ldb = 0;
   void* C = nullptr; long ldc = 0;
-  const uint16_t* R = nullptr; long ldr = 0;
-  uint16_t* C2 = nullptr; long ldc2 = 0;
-  const uint16_t* G = nullptr; long ldg = 0;
+  const E* R = nullptr; long ldr = 0;
+  E* C2 = nullptr; long ldc2 = 0;
+  const E* G = nullptr; long ldg = 0;
   int F = 0;  // FFN width for the SwiGLU epilogues
 };
+using GemmArgs = GemmArgsT<uint16_t>;
+using GemmArgsF32 = GemmArgsT<float>;
 
 // Returns a message for unsupported arguments, or nullptr if OK.
 const char* gemm_check(const GemmArgs& a);
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t s);
 const char* gemm_kernel_name(const GemmArgs& a);
+const char* gemm_check(const GemmArgsF32& a);
+hipError_t gemm_launch(const GemmArgsF32& a, hipStream_t s);
 
 // ------------------------------------------------------------ elementwise
-// RMSNorm over rows of x [rows, cols] (bf16): y = x * rstd * g (bf16),
-// rstd [rows] fp32 (may be null).
+// Each storage-typed launcher below has a bf16 (uint16_t) and an fp32
+// (float) overload running the same kernel template; math is fp32.
+//
+// RMSNorm over rows of x [rows, cols]: y = x * rstd * g, rstd [rows] fp32
+// (may be null).
 hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd,
                        int rows, int cols, float eps, hipStream_t s);
-// dx = resid + rstd*(e - xh*mean(e*xh)), e = dy*g, xh = x*rstd  (bf16 out;
-// resid may be null).  Writes per-block partial gain gradients
-// dg_part [nblk, cols] fp32; nblk = rmsnorm_bwd_blocks(rows).
+hipError_t rmsnorm_fwd(const float* x, const float* g, float* y, float* rstd, int rows,
+                       int cols, float eps, hipStream_t s);
+// dx = resid + rstd*(e - xh*mean(e*xh)), e = dy*g, xh = x*rstd (resid may
+// be null).  Writes per-block partial gain gradients dg_part [nblk, cols]
+// fp32; nblk = rmsnorm_bwd_blocks(rows).
 int rmsnorm_bwd_blocks(int rows);
 hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
                        const float* rstd, const uint16_t* resid, uint16_t* dx,
                        float* dg_part, int rows, int cols, hipStream_t s);
-// out[c] = bf16(sum_b part[b, c]) in fixed block order.
-hipError_t reduce_rows_to_bf16(const float* part, int nblk, int cols, uint16_t* out,
-                               hipStream_t s);
+hipError_t rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd,
+                       const float* resid, float* dx, float* dg_part, int rows, int cols,
+                       hipStream_t s);
+// out[c] = sum_b part[b, c] in fixed block order, stored as the out type.
+hipError_t reduce_rows(const float* part, int nblk, int cols, uint16_t* out, hipStream_t s);
+hipError_t reduce_rows(const float* part, int nblk, int cols, float* out, hipStream_t s);
 
 // cos/sin tables [seq, head_dim/2] fp32, angle = t * theta^(-2j/d) in fp64.
 hipError_t rope_table(float* cos_t, float* sin_t, int seq, int head_dim, double theta,
@@ -68,12 +83,17 @@ hipError_t rope_table(float* cos_t, float* sin_t, int seq, int head_dim, double 
 hipError_t rope_apply(uint16_t* qkv, long ldq, int batch, int seq, int n_heads,
                       int n_kv_heads, int head_dim, const float* cos_t, const float* sin_t,
                       int inverse, hipStream_t s);
+hipError_t rope_apply(float* qkv, long ldq, int batch, int seq, int n_heads, int n_kv_heads,
+                      int head_dim, const float* cos_t, const float* sin_t, int inverse,
+                      hipStream_t s);
 
 // Device -> pinned host copy by a kernel of `blocks` workgroups (bytes,
 // src and dst multiples of 16).
 hipError_t copy_d2h(const void* src, void* dst_host, size_t bytes, int blocks, hipStream_t s);
 
-hipError_t cast_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
+// out[i] = in[i] stored as the out type (bf16: RNE).
+hipError_t cast_f32(const float* in, uint16_t* out, size_t n, hipStream_t s);
+hipError_t cast_f32(const float* in, float* out, size_t n, hipStream_t s);
 hipError_t fill_f32(float* p, float v, size_t n, hipStream_t s);
 hipError_t copy_rows_bf16(const uint16_t* src, long lds, uint16_t* dst, long ldd, int rows,
                           int cols, hipStream_t s);
@@ -87,13 +107,22 @@ hipError_t attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int
 hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
                     const uint16_t* dout, float* delta, uint16_t* dqkv, int batch, int seq,
                     int n_heads, int n_kv_heads, int head_dim, hipStream_t s);
+// fp32 storage (debug precision): same contract, one wave per query row
+// (forward, dq) or key row (dk, dv) with fp32 FMA and exact exp/log.
+hipError_t attn_fwd(const float* qkv, float* o, float* lse, int batch, int seq, int n_heads,
+                    int n_kv_heads, int head_dim, hipStream_t s);
+hipError_t attn_bwd(const float* qkv, const float* o, const float* lse, const float* dout,
+                    float* delta, float* dqkv, int batch, int seq, int n_heads, int n_kv_heads,
+                    int head_dim, hipStream_t s);
 
 // ------------------------------------------------------------------ head
 // Row-wise softmax cross-entropy on fp32 logits [rows, V] for next-token
 // targets: target[r] < 0 means no target (zero gradient, no loss).
-// dlogits (bf16) = (softmax - onehot) * inv_n; loss_part[r] = lse - picked.
+// dlogits (storage) = (softmax - onehot) * inv_n; loss_part[r] = lse - picked.
 hipError_t ce_rows(const float* logits, const int32_t* target, uint16_t* dlogits,
                    float* loss_part, int rows, int vocab, float inv_n, hipStream_t s);
+hipError_t ce_rows(const float* logits, const int32_t* target, float* dlogits, float* loss_part,
+                   int rows, int vocab, float inv_n, hipStream_t s);
 // loss = sum(loss_part[0..n)) * inv_n in fixed order -> out[0] (fp32).
 hipError_t sum_loss(const float* part, int n, float inv_n, float* out, hipStream_t s);
 

@@ -42,7 +42,8 @@ const char* make_dims(const mt_model_cfg* cfg, const mt_run_cfg* run, int batch,
   if (!(c.rms_eps > 0) || !(c.rope_theta > 0)) return "rms_eps and rope_theta must be positive";
   if (batch < 1 || seq < 1) return "batch and seq must be >= 1";
   if ((long)batch * seq > (1L << 30)) return "too many tokens";
-  if (run->precision != MT_PREC_BF16) return "only the bf16 precision mode is built";
+  if (run->precision != MT_PREC_BF16 && run->precision != MT_PREC_FP32_DEBUG)
+    return "precision must be MT_PREC_BF16 or MT_PREC_FP32_DEBUG";
   if (run->mlp_chunk_tokens < 0 || run->head_chunk_tokens < 0) return "chunk sizes must be >= 0";
   Dims d;
   d.B = batch;
@@ -59,6 +60,7 @@ const char* make_dims(const mt_model_cfg* cfg, const mt_run_cfg* run, int batch,
   d.V = c.vocab;
   d.eps = c.rms_eps;
   d.theta = c.rope_theta;
+  d.prec = run->precision;
   d.mlp_chunk = run->mlp_chunk_tokens > 0 ? std::min(run->mlp_chunk_tokens, d.D) : d.D;
   d.head_chunk = run->head_chunk_tokens > 0 ? std::min(run->head_chunk_tokens, d.D) : std::min(d.D, 16384);
   *out = d;
@@ -90,37 +92,41 @@ HeadLayout head_layout(const Dims& d) {
 
 namespace {
 
+// Workspace of one layer call.  E is the storage type of activations
+// (uint16_t: bf16 bit patterns; float: the fp32 debug precision).
+template <class E>
 struct LayerWs {
   float *cos_t, *sin_t, *rstd1, *rstd2, *lse;
-  uint16_t *a, *qkv, *o, *x_mid, *b, *gu, *m;
+  E *a, *qkv, *o, *x_mid, *b, *gu, *m;
   // backward only
-  uint16_t *dgu, *db, *dx_mid, *dout, *dqkv, *da;
+  E *dgu, *db, *dx_mid, *dout, *dqkv, *da;
   float *delta, *dg_part, *acc_d, *acc_gu;
 };
 
-LayerWs carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
+template <class E>
+LayerWs<E> carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
   Carve c{base};
-  LayerWs w{};
+  LayerWs<E> w{};
   const size_t D = d.D, H = d.H, C = d.mlp_chunk;
   w.cos_t = c.take<float>((size_t)d.T * d.d / 2);
   w.sin_t = c.take<float>((size_t)d.T * d.d / 2);
   w.rstd1 = c.take<float>(D);
   w.rstd2 = c.take<float>(D);
   w.lse = c.take<float>((size_t)d.B * d.Hq * d.T);
-  w.a = c.take<uint16_t>(D * H);
-  w.qkv = c.take<uint16_t>(D * d.NQKV);
-  w.o = c.take<uint16_t>(D * d.Qd);
-  w.x_mid = c.take<uint16_t>(D * H);
-  w.b = c.take<uint16_t>(D * H);
-  w.m = c.take<uint16_t>(C * d.F);
+  w.a = c.take<E>(D * H);
+  w.qkv = c.take<E>(D * d.NQKV);
+  w.o = c.take<E>(D * d.Qd);
+  w.x_mid = c.take<E>(D * H);
+  w.b = c.take<E>(D * H);
+  w.m = c.take<E>(C * d.F);
   if (which == 1) {
-    w.gu = c.take<uint16_t>(C * 2 * d.F);
-    w.dgu = c.take<uint16_t>(C * 2 * d.F);
-    w.db = c.take<uint16_t>(D * H);
-    w.dx_mid = c.take<uint16_t>(D * H);
-    w.dout = c.take<uint16_t>(D * d.Qd);
-    w.dqkv = c.take<uint16_t>(D * d.NQKV);
-    w.da = c.take<uint16_t>(D * H);
+    w.gu = c.take<E>(C * 2 * d.F);
+    w.dgu = c.take<E>(C * 2 * d.F);
+    w.db = c.take<E>(D * H);
+    w.dx_mid = c.take<E>(D * H);
+    w.dout = c.take<E>(D * d.Qd);
+    w.dqkv = c.take<E>(D * d.NQKV);
+    w.da = c.take<E>(D * H);
     w.delta = c.take<float>((size_t)d.B * d.Hq * d.T);
     w.dg_part = c.take<float>((size_t)rmsnorm_bwd_blocks((int)D) * H);
     if (C < D) {
@@ -132,9 +138,10 @@ LayerWs carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
   return w;
 }
 
-GemmArgs gemm(int layout, int epi, int M, int N, int K, const uint16_t* A, long lda,
-              const uint16_t* B, long ldb, void* C, long ldc) {
-  GemmArgs g;
+template <class E>
+GemmArgsT<E> gemm(int layout, int epi, int M, int N, int K, const E* A, long lda, const E* B,
+                  long ldb, void* C, long ldc) {
+  GemmArgsT<E> g;
   g.layout = layout;
   g.epi = epi;
   g.M = M;
@@ -149,7 +156,8 @@ GemmArgs gemm(int layout, int epi, int M, int N, int K, const uint16_t* A, long 
   return g;
 }
 
-mt_status run_gemm(const GemmArgs& g, hipStream_t s, Probe* probe = nullptr) {
+template <class E>
+mt_status run_gemm(const GemmArgsT<E>& g, hipStream_t s, Probe* probe = nullptr) {
   if (const char* m = gemm_check(g)) return set_error(MT_E_SHAPE, "layer GEMM: %s", m);
   const bool timed = probe && probe->used + 2 <= (int)probe->ev.size();
   if (timed) MT_HIP(hipEventRecord(probe->ev[probe->used], s));
@@ -168,51 +176,53 @@ mt_status run_gemm(const GemmArgs& g, hipStream_t s, Probe* probe = nullptr) {
     if (st_ != MT_OK) return st_;     \
   } while (0)
 
+// Typed weight pointers of a layer view.
+template <class E>
+struct LayerW {
+  const E *g1, *wqkv, *wo, *g2, *wgu, *wd;
+  explicit LayerW(const mt_layer_view& w)
+      : g1(static_cast<const E*>(w.attn_norm)), wqkv(static_cast<const E*>(w.w_qkv)),
+        wo(static_cast<const E*>(w.w_o)), g2(static_cast<const E*>(w.mlp_norm)),
+        wgu(static_cast<const E*>(w.w_gate_up)), wd(static_cast<const E*>(w.w_down)) {}
+};
+
 // Attention half of the block, shared by forward and recompute.
-mt_status attn_half(const Dims& d, const mt_layer_view& w, const uint16_t* x, const LayerWs& ws,
+template <class E>
+mt_status attn_half(const Dims& d, const LayerW<E>& w, const E* x, const LayerWs<E>& ws,
                     hipStream_t s) {
-  const uint16_t* g1 = static_cast<const uint16_t*>(w.attn_norm);
   MT_HIP(rope_table(ws.cos_t, ws.sin_t, d.T, d.d, d.theta, s));
-  MT_HIP(rmsnorm_fwd(x, g1, ws.a, ws.rstd1, d.D, d.H, d.eps, s));
-  MT_RUN(run_gemm(gemm(GEMM_NT, EPI_BF16, d.D, d.NQKV, d.H, ws.a, d.H,
-                       static_cast<const uint16_t*>(w.w_qkv), d.H, ws.qkv, d.NQKV), s));
+  MT_HIP(rmsnorm_fwd(x, w.g1, ws.a, ws.rstd1, d.D, d.H, d.eps, s));
+  MT_RUN(run_gemm(gemm<E>(GEMM_NT, EPI_BF16, d.D, d.NQKV, d.H, ws.a, d.H, w.wqkv, d.H, ws.qkv,
+                          d.NQKV),
+                  s));
   MT_HIP(rope_apply(ws.qkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 0, s));
   MT_HIP(attn_fwd(ws.qkv, ws.o, ws.lse, d.B, d.T, d.Hq, d.Hkv, d.d, s));
-  GemmArgs go = gemm(GEMM_NT, EPI_RESID_BF16, d.D, d.H, d.Qd, ws.o, d.Qd,
-                     static_cast<const uint16_t*>(w.w_o), d.Qd, ws.x_mid, d.H);
+  GemmArgsT<E> go = gemm<E>(GEMM_NT, EPI_RESID_BF16, d.D, d.H, d.Qd, ws.o, d.Qd, w.wo, d.Qd,
+                            ws.x_mid, d.H);
   go.R = x;
   go.ldr = d.H;
   MT_RUN(run_gemm(go, s));
-  MT_HIP(rmsnorm_fwd(ws.x_mid, static_cast<const uint16_t*>(w.mlp_norm), ws.b, ws.rstd2, d.D, d.H,
-                     d.eps, s));
+  MT_HIP(rmsnorm_fwd(ws.x_mid, w.g2, ws.b, ws.rstd2, d.D, d.H, d.eps, s));
   return MT_OK;
 }
 
-}  // namespace
-
-size_t layer_ws_bytes(const Dims& d, int which) {
-  size_t bytes = 0;
-  carve_layer(d, nullptr, which, &bytes);
-  return bytes;
-}
-
-mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* x_in,
-                         uint16_t* x_out, void* wsp, size_t ws_bytes, hipStream_t s, Probe* probe) {
+template <class E>
+mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* x_out, void* wsp,
+                      size_t ws_bytes, hipStream_t s, Probe* probe) {
   size_t need = 0;
-  LayerWs ws = carve_layer(d, static_cast<char*>(wsp), 0, &need);
+  LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), 0, &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE, "layer forward: workspace %zu < %zu bytes",
            ws_bytes, need);
+  const LayerW<E> w(wv);
   MT_RUN(attn_half(d, w, x_in, ws, s));
-  const uint16_t* wgu = static_cast<const uint16_t*>(w.w_gate_up);
-  const uint16_t* wd = static_cast<const uint16_t*>(w.w_down);
   for (int r0 = 0; r0 < d.D; r0 += d.mlp_chunk) {
     const int rows = std::min(d.mlp_chunk, d.D - r0);
-    GemmArgs gu = gemm(GEMM_NT, EPI_SWIGLU, rows, 2 * d.F, d.H, ws.b + (size_t)r0 * d.H, d.H, wgu,
-                       d.H, ws.m, d.F);
+    GemmArgsT<E> gu = gemm<E>(GEMM_NT, EPI_SWIGLU, rows, 2 * d.F, d.H, ws.b + (size_t)r0 * d.H,
+                              d.H, w.wgu, d.H, ws.m, d.F);
     gu.F = d.F;
     MT_RUN(run_gemm(gu, s, probe));
-    GemmArgs dn = gemm(GEMM_NT, EPI_RESID_BF16, rows, d.H, d.F, ws.m, d.F, wd, d.F,
-                       x_out + (size_t)r0 * d.H, d.H);
+    GemmArgsT<E> dn = gemm<E>(GEMM_NT, EPI_RESID_BF16, rows, d.H, d.F, ws.m, d.F, w.wd, d.F,
+                              x_out + (size_t)r0 * d.H, d.H);
     dn.R = ws.x_mid + (size_t)r0 * d.H;
     dn.ldr = d.H;
     MT_RUN(run_gemm(dn, s));
@@ -220,21 +230,19 @@ mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* 
   return MT_OK;
 }
 
-mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* x_in,
-                         const uint16_t* dy, uint16_t* dx, const mt_layer_grad_view& g, void* wsp,
-                         size_t ws_bytes, hipStream_t s, Probe* probe) {
-  (void)probe;
+template <class E>
+mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, const E* dy, E* dx,
+                      const mt_layer_grad_view& g, void* wsp, size_t ws_bytes, hipStream_t s) {
   size_t need = 0;
-  LayerWs ws = carve_layer(d, static_cast<char*>(wsp), 1, &need);
+  LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), 1, &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE,
            "layer recompute/backward: workspace %zu < %zu bytes", ws_bytes, need);
+  const LayerW<E> w(wv);
   // ---- recompute the attention half (rebuilds a, qkv (rotated), o, lse, x_mid, b)
   MT_RUN(attn_half(d, w, x_in, ws, s));
-  const uint16_t* wgu = static_cast<const uint16_t*>(w.w_gate_up);
-  const uint16_t* wd = static_cast<const uint16_t*>(w.w_down);
   const bool chunked = d.mlp_chunk < d.D;
-  uint16_t* gd = static_cast<uint16_t*>(g.w_down);
-  uint16_t* ggu = static_cast<uint16_t*>(g.w_gate_up);
+  E* gd = static_cast<E*>(g.w_down);
+  E* ggu = static_cast<E*>(g.w_gate_up);
   if (chunked) {
     MT_HIP(fill_f32(ws.acc_d, 0.f, (size_t)d.H * d.F, s));
     MT_HIP(fill_f32(ws.acc_gu, 0.f, 2 * (size_t)d.F * d.H, s));
@@ -242,15 +250,17 @@ mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* 
   // ---- MLP: recompute gate/up per chunk, then its backward
   for (int r0 = 0; r0 < d.D; r0 += d.mlp_chunk) {
     const int rows = std::min(d.mlp_chunk, d.D - r0);
-    const uint16_t* b_c = ws.b + (size_t)r0 * d.H;
-    const uint16_t* dy_c = dy + (size_t)r0 * d.H;
-    GemmArgs gu = gemm(GEMM_NT, EPI_SWIGLU_SAVE, rows, 2 * d.F, d.H, b_c, d.H, wgu, d.H, ws.m, d.F);
+    const E* b_c = ws.b + (size_t)r0 * d.H;
+    const E* dy_c = dy + (size_t)r0 * d.H;
+    GemmArgsT<E> gu = gemm<E>(GEMM_NT, EPI_SWIGLU_SAVE, rows, 2 * d.F, d.H, b_c, d.H, w.wgu, d.H,
+                              ws.m, d.F);
     gu.F = d.F;
     gu.C2 = ws.gu;
     gu.ldc2 = 2 * d.F;
     MT_RUN(run_gemm(gu, s));
     // dgate, dup from dm = dy W_down (NN) fused with the SwiGLU derivative
-    GemmArgs dm = gemm(GEMM_NN, EPI_SWIGLU_BWD, rows, d.F, d.H, dy_c, d.H, wd, d.F, ws.dgu, 2 * d.F);
+    GemmArgsT<E> dm = gemm<E>(GEMM_NN, EPI_SWIGLU_BWD, rows, d.F, d.H, dy_c, d.H, w.wd, d.F,
+                              ws.dgu, 2 * d.F);
     dm.F = d.F;
     dm.G = ws.gu;
     dm.ldg = 2 * d.F;
@@ -258,86 +268,111 @@ mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* 
     dm.ldc2 = 2 * d.F;
     MT_RUN(run_gemm(dm, s));
     // dW_down = dy^T m  (TN: A = dy as [K=rows, M=H], B = m [rows, F])
-    MT_RUN(run_gemm(gemm(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.H, d.F, rows, dy_c, d.H, ws.m,
-                         d.F, chunked ? static_cast<void*>(ws.acc_d) : static_cast<void*>(gd), d.F),
+    MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.H, d.F, rows, dy_c, d.H,
+                            ws.m, d.F,
+                            chunked ? static_cast<void*>(ws.acc_d) : static_cast<void*>(gd), d.F),
                     s));
     // dW_gu = dgu^T b  (TN: A = dgu [rows, 2F], B = b [rows, H])
-    MT_RUN(run_gemm(gemm(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, 2 * d.F, d.H, rows, ws.dgu,
-                         2 * d.F, b_c, d.H,
-                         chunked ? static_cast<void*>(ws.acc_gu) : static_cast<void*>(ggu), d.H),
+    MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, 2 * d.F, d.H, rows, ws.dgu,
+                            2 * d.F, b_c, d.H,
+                            chunked ? static_cast<void*>(ws.acc_gu) : static_cast<void*>(ggu),
+                            d.H),
                     s));
     // db = dgu W_gu  (NN: B = W_gu [2F, H])
-    MT_RUN(run_gemm(gemm(GEMM_NN, EPI_BF16, rows, d.H, 2 * d.F, ws.dgu, 2 * d.F, wgu, d.H,
-                         ws.db + (size_t)r0 * d.H, d.H),
+    MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, rows, d.H, 2 * d.F, ws.dgu, 2 * d.F, w.wgu, d.H,
+                            ws.db + (size_t)r0 * d.H, d.H),
                     s));
   }
   if (chunked) {
-    MT_HIP(cast_f32_to_bf16(ws.acc_d, gd, (size_t)d.H * d.F, s));
-    MT_HIP(cast_f32_to_bf16(ws.acc_gu, ggu, 2 * (size_t)d.F * d.H, s));
+    MT_HIP(cast_f32(ws.acc_d, gd, (size_t)d.H * d.F, s));
+    MT_HIP(cast_f32(ws.acc_gu, ggu, 2 * (size_t)d.F * d.H, s));
   }
   // ---- second norm (residual dy)
   const int nblk = rmsnorm_bwd_blocks(d.D);
-  MT_HIP(rmsnorm_bwd(ws.db, ws.x_mid, static_cast<const uint16_t*>(w.mlp_norm), ws.rstd2, dy,
-                     ws.dx_mid, ws.dg_part, d.D, d.H, s));
-  MT_HIP(reduce_rows_to_bf16(ws.dg_part, nblk, d.H, static_cast<uint16_t*>(g.mlp_norm), s));
+  MT_HIP(rmsnorm_bwd(ws.db, ws.x_mid, w.g2, ws.rstd2, dy, ws.dx_mid, ws.dg_part, d.D, d.H, s));
+  MT_HIP(reduce_rows(ws.dg_part, nblk, d.H, static_cast<E*>(g.mlp_norm), s));
   // ---- output projection
-  MT_RUN(run_gemm(gemm(GEMM_NN, EPI_BF16, d.D, d.Qd, d.H, ws.dx_mid, d.H,
-                       static_cast<const uint16_t*>(w.w_o), d.Qd, ws.dout, d.Qd),
+  MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, d.D, d.Qd, d.H, ws.dx_mid, d.H, w.wo, d.Qd, ws.dout,
+                          d.Qd),
                   s));
-  MT_RUN(run_gemm(gemm(GEMM_TN, EPI_BF16, d.H, d.Qd, d.D, ws.dx_mid, d.H, ws.o, d.Qd, g.w_o, d.Qd),
+  MT_RUN(run_gemm(gemm<E>(GEMM_TN, EPI_BF16, d.H, d.Qd, d.D, ws.dx_mid, d.H, ws.o, d.Qd, g.w_o,
+                          d.Qd),
                   s));
   // ---- attention and RoPE
   MT_HIP(attn_bwd(ws.qkv, ws.o, ws.lse, ws.dout, ws.delta, ws.dqkv, d.B, d.T, d.Hq, d.Hkv, d.d, s));
   MT_HIP(rope_apply(ws.dqkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 1, s));
   // ---- QKV projection
-  MT_RUN(run_gemm(gemm(GEMM_TN, EPI_BF16, d.NQKV, d.H, d.D, ws.dqkv, d.NQKV, ws.a, d.H, g.w_qkv, d.H),
+  MT_RUN(run_gemm(gemm<E>(GEMM_TN, EPI_BF16, d.NQKV, d.H, d.D, ws.dqkv, d.NQKV, ws.a, d.H,
+                          g.w_qkv, d.H),
                   s));
-  MT_RUN(run_gemm(gemm(GEMM_NN, EPI_BF16, d.D, d.H, d.NQKV, ws.dqkv, d.NQKV,
-                       static_cast<const uint16_t*>(w.w_qkv), d.H, ws.da, d.H),
+  MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, d.D, d.H, d.NQKV, ws.dqkv, d.NQKV, w.wqkv, d.H, ws.da,
+                          d.H),
                   s));
   // ---- first norm (residual dx_mid)
-  MT_HIP(rmsnorm_bwd(ws.da, x_in, static_cast<const uint16_t*>(w.attn_norm), ws.rstd1, ws.dx_mid,
-                     dx, ws.dg_part, d.D, d.H, s));
-  MT_HIP(reduce_rows_to_bf16(ws.dg_part, nblk, d.H, static_cast<uint16_t*>(g.attn_norm), s));
+  MT_HIP(rmsnorm_bwd(ws.da, x_in, w.g1, ws.rstd1, ws.dx_mid, dx, ws.dg_part, d.D, d.H, s));
+  MT_HIP(reduce_rows(ws.dg_part, nblk, d.H, static_cast<E*>(g.attn_norm), s));
   return MT_OK;
+}
+
+}  // namespace
+
+size_t layer_ws_bytes(const Dims& d, int which) {
+  size_t bytes = 0;
+  if (d.prec == MT_PREC_FP32_DEBUG) carve_layer<float>(d, nullptr, which, &bytes);
+  else carve_layer<uint16_t>(d, nullptr, which, &bytes);
+  return bytes;
+}
+
+mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in, void* x_out,
+                         void* ws, size_t ws_bytes, hipStream_t s, Probe* probe) {
+  if (d.prec == MT_PREC_FP32_DEBUG)
+    return layer_fwd_t(d, w, static_cast<const float*>(x_in), static_cast<float*>(x_out), ws,
+                       ws_bytes, s, probe);
+  return layer_fwd_t(d, w, static_cast<const uint16_t*>(x_in), static_cast<uint16_t*>(x_out), ws,
+                     ws_bytes, s, probe);
+}
+
+mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in, const void* dy,
+                         void* dx, const mt_layer_grad_view& g, void* ws, size_t ws_bytes,
+                         hipStream_t s) {
+  if (d.prec == MT_PREC_FP32_DEBUG)
+    return layer_bwd_t(d, w, static_cast<const float*>(x_in), static_cast<const float*>(dy),
+                       static_cast<float*>(dx), g, ws, ws_bytes, s);
+  return layer_bwd_t(d, w, static_cast<const uint16_t*>(x_in), static_cast<const uint16_t*>(dy),
+                     static_cast<uint16_t*>(dx), g, ws, ws_bytes, s);
 }
 
 // ------------------------------------------------------------------- head
 
 namespace {
+template <class E>
 struct HeadWs {
-  uint16_t *h, *dlogits, *dh;
+  E *h, *dlogits, *dh;
   float *rstd, *logits, *loss_part, *dg_part, *acc_out;
 };
-HeadWs carve_head(const Dims& d, char* base, size_t* bytes) {
+template <class E>
+HeadWs<E> carve_head(const Dims& d, char* base, size_t* bytes) {
   Carve c{base};
-  HeadWs w{};
+  HeadWs<E> w{};
   const size_t D = d.D, H = d.H, Ch = d.head_chunk;
-  w.h = c.take<uint16_t>(D * H);
-  w.dh = c.take<uint16_t>(D * H);
+  w.h = c.take<E>(D * H);
+  w.dh = c.take<E>(D * H);
   w.rstd = c.take<float>(D);
   w.loss_part = c.take<float>(D);
   w.logits = c.take<float>(Ch * d.V);
-  w.dlogits = c.take<uint16_t>(Ch * d.V);
+  w.dlogits = c.take<E>(Ch * d.V);
   w.dg_part = c.take<float>((size_t)rmsnorm_bwd_blocks((int)D) * H);
   if ((int)Ch < d.D) w.acc_out = c.take<float>((size_t)d.V * H);
   *bytes = c.off + 256;
   return w;
 }
-}  // namespace
 
-size_t head_ws_bytes(const Dims& d) {
-  size_t b = 0;
-  carve_head(d, nullptr, &b);
-  return b;
-}
-
-mt_status head_impl(const Dims& d, const uint16_t* g_f, const uint16_t* w_out,
-                    const uint16_t* x_L, const int32_t* targets, float inv_n, uint16_t* dx_L,
-                    uint16_t* dg_f, uint16_t* dw_out, float* loss_dev, void* wsp, size_t ws_bytes,
-                    hipStream_t s) {
+template <class E>
+mt_status head_t(const Dims& d, const E* g_f, const E* w_out, const E* x_L,
+                 const int32_t* targets, float inv_n, E* dx_L, E* dg_f, E* dw_out, float* loss_dev,
+                 void* wsp, size_t ws_bytes, hipStream_t s) {
   size_t need = 0;
-  HeadWs ws = carve_head(d, static_cast<char*>(wsp), &need);
+  HeadWs<E> ws = carve_head<E>(d, static_cast<char*>(wsp), &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE, "head: workspace %zu < %zu bytes", ws_bytes,
            need);
   const bool chunked = d.head_chunk < d.D;
@@ -345,22 +380,47 @@ mt_status head_impl(const Dims& d, const uint16_t* g_f, const uint16_t* w_out,
   if (chunked) MT_HIP(fill_f32(ws.acc_out, 0.f, (size_t)d.V * d.H, s));
   for (int r0 = 0; r0 < d.D; r0 += d.head_chunk) {
     const int rows = std::min(d.head_chunk, d.D - r0);
-    const uint16_t* h_c = ws.h + (size_t)r0 * d.H;
-    MT_RUN(run_gemm(gemm(GEMM_NT, EPI_F32, rows, d.V, d.H, h_c, d.H, w_out, d.H, ws.logits, d.V), s));
-    MT_HIP(ce_rows(ws.logits, targets + r0, ws.dlogits, ws.loss_part + r0, rows, d.V, inv_n, s));
-    MT_RUN(run_gemm(gemm(GEMM_NN, EPI_BF16, rows, d.H, d.V, ws.dlogits, d.V, w_out, d.H,
-                         ws.dh + (size_t)r0 * d.H, d.H),
+    const E* h_c = ws.h + (size_t)r0 * d.H;
+    MT_RUN(run_gemm(gemm<E>(GEMM_NT, EPI_F32, rows, d.V, d.H, h_c, d.H, w_out, d.H, ws.logits,
+                            d.V),
                     s));
-    MT_RUN(run_gemm(gemm(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.V, d.H, rows, ws.dlogits, d.V,
-                         h_c, d.H, chunked ? static_cast<void*>(ws.acc_out) : static_cast<void*>(dw_out),
-                         d.H),
+    MT_HIP(ce_rows(ws.logits, targets + r0, ws.dlogits, ws.loss_part + r0, rows, d.V, inv_n, s));
+    MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, rows, d.H, d.V, ws.dlogits, d.V, w_out, d.H,
+                            ws.dh + (size_t)r0 * d.H, d.H),
+                    s));
+    MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.V, d.H, rows, ws.dlogits,
+                            d.V, h_c, d.H,
+                            chunked ? static_cast<void*>(ws.acc_out) : static_cast<void*>(dw_out),
+                            d.H),
                     s));
   }
-  if (chunked) MT_HIP(cast_f32_to_bf16(ws.acc_out, dw_out, (size_t)d.V * d.H, s));
+  if (chunked) MT_HIP(cast_f32(ws.acc_out, dw_out, (size_t)d.V * d.H, s));
   MT_HIP(sum_loss(ws.loss_part, d.D, inv_n, loss_dev, s));
-  MT_HIP(rmsnorm_bwd(ws.dh, x_L, g_f, ws.rstd, nullptr, dx_L, ws.dg_part, d.D, d.H, s));
-  MT_HIP(reduce_rows_to_bf16(ws.dg_part, rmsnorm_bwd_blocks(d.D), d.H, dg_f, s));
+  MT_HIP(rmsnorm_bwd(ws.dh, x_L, g_f, ws.rstd, static_cast<const E*>(nullptr), dx_L, ws.dg_part,
+                     d.D, d.H, s));
+  MT_HIP(reduce_rows(ws.dg_part, rmsnorm_bwd_blocks(d.D), d.H, dg_f, s));
   return MT_OK;
+}
+}  // namespace
+
+size_t head_ws_bytes(const Dims& d) {
+  size_t b = 0;
+  if (d.prec == MT_PREC_FP32_DEBUG) carve_head<float>(d, nullptr, &b);
+  else carve_head<uint16_t>(d, nullptr, &b);
+  return b;
+}
+
+mt_status head_impl(const Dims& d, const void* g_f, const void* w_out, const void* x_L,
+                    const int32_t* targets, float inv_n, void* dx_L, void* dg_f, void* dw_out,
+                    float* loss_dev, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (d.prec == MT_PREC_FP32_DEBUG)
+    return head_t(d, static_cast<const float*>(g_f), static_cast<const float*>(w_out),
+                  static_cast<const float*>(x_L), targets, inv_n, static_cast<float*>(dx_L),
+                  static_cast<float*>(dg_f), static_cast<float*>(dw_out), loss_dev, ws, ws_bytes, s);
+  return head_t(d, static_cast<const uint16_t*>(g_f), static_cast<const uint16_t*>(w_out),
+                static_cast<const uint16_t*>(x_L), targets, inv_n, static_cast<uint16_t*>(dx_L),
+                static_cast<uint16_t*>(dg_f), static_cast<uint16_t*>(dw_out), loss_dev, ws,
+                ws_bytes, s);
 }
 
 }  // namespace mt
@@ -391,8 +451,8 @@ mt_status mt_layer_fwd(const mt_model_cfg* cfg, const mt_run_cfg* run, const mt_
   MT_RUN(check_view(w));
   MT_CHECK(x_in && x_out, MT_E_INVALID, "mt_layer_fwd: null activation pointer");
   MT_CHECK(x_in != x_out, MT_E_INVALID, "mt_layer_fwd: x_out may not alias x_in");
-  return layer_fwd_impl(d, *w, static_cast<const uint16_t*>(x_in), static_cast<uint16_t*>(x_out),
-                        workspace, workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
+  return layer_fwd_impl(d, *w, x_in, x_out, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(stream), nullptr);
 }
 
 mt_status mt_layer_recompute_bwd(const mt_model_cfg* cfg, const mt_run_cfg* run,
@@ -408,9 +468,8 @@ mt_status mt_layer_recompute_bwd(const mt_model_cfg* cfg, const mt_run_cfg* run,
   MT_CHECK(dw && dw->attn_norm && dw->w_qkv && dw->w_o && dw->mlp_norm && dw->w_gate_up &&
                dw->w_down,
            MT_E_INVALID, "mt_layer_recompute_bwd: null gradient pointer");
-  return layer_bwd_impl(d, *w, static_cast<const uint16_t*>(x_in), static_cast<const uint16_t*>(dy),
-                        static_cast<uint16_t*>(dx), *dw, workspace, workspace_bytes,
-                        static_cast<hipStream_t>(stream), nullptr);
+  return layer_bwd_impl(d, *w, x_in, dy, dx, *dw, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

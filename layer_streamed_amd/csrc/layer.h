@@ -17,6 +17,9 @@ struct Dims {
   double theta;
   int mlp_chunk;   // tokens per MLP chunk (== D when not chunked)
   int head_chunk;  // tokens per LM-head chunk
+  int prec;        // MT_PREC_BF16 or MT_PREC_FP32_DEBUG
+  // bytes per stored element of weights, activations and gradients
+  size_t es() const { return prec == MT_PREC_FP32_DEBUG ? 4 : 2; }
 };
 
 // Validates the model shape and run knobs; fills dims.  Returns nullptr or
@@ -46,24 +49,26 @@ struct Carve {
   }
 };
 
+// Activations, weights and gradients are stored as bf16 bit patterns or,
+// with d.prec == MT_PREC_FP32_DEBUG, as fp32 (d.es() bytes per element).
 size_t layer_ws_bytes(const Dims& d, int which);
-mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* x_in,
-                         uint16_t* x_out, void* ws, size_t ws_bytes, hipStream_t s, Probe* probe);
-mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const uint16_t* x_in,
-                         const uint16_t* dy, uint16_t* dx, const mt_layer_grad_view& g, void* ws,
-                         size_t ws_bytes, hipStream_t s, Probe* probe);
+mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in, void* x_out,
+                         void* ws, size_t ws_bytes, hipStream_t s, Probe* probe);
+mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in, const void* dy,
+                         void* dx, const mt_layer_grad_view& g, void* ws, size_t ws_bytes,
+                         hipStream_t s);
 
 // LM head: h = rms(x_L) g_f; logits = h W_out^T per token chunk; next-token
 // cross-entropy; dh, dW_out, dg_f; dx_L = rmsnorm backward.  targets: device
 // int32 [D] (-1 = none).  loss_dev: device fp32 scalar (mean over targets).
 size_t head_ws_bytes(const Dims& d);
-mt_status head_impl(const Dims& d, const uint16_t* g_f, const uint16_t* w_out,
-                    const uint16_t* x_L, const int32_t* targets, float inv_n, uint16_t* dx_L,
-                    uint16_t* dg_f, uint16_t* dw_out, float* loss_dev, void* ws, size_t ws_bytes,
-                    hipStream_t s);
+mt_status head_impl(const Dims& d, const void* g_f, const void* w_out, const void* x_L,
+                    const int32_t* targets, float inv_n, void* dx_L, void* dg_f, void* dw_out,
+                    float* loss_dev, void* ws, size_t ws_bytes, hipStream_t s);
 
-// Element offsets of the tensors inside one layer's flat unit (bf16 slab
-// and fp32 store share them), each aligned to 128 elements.
+// Element offsets of the tensors inside one layer's flat unit (streamed
+// copy, gradient slab and fp32 store share them), each aligned to 128
+// elements.
 struct LayerLayout {
   size_t attn_norm, w_qkv, w_q, w_k, w_v, w_o, mlp_norm, w_gate_up, w_gate, w_up, w_down, total;
 };

@@ -7,7 +7,8 @@
 // three flat arrays with one shared layout; only the bf16 copy of the
 // master (what the GPU receives) and the gradient slabs (what it sends back)
 // are pinned, since only they are DMA endpoints: 2 B/param pinned plus the
-// slab pool, instead of 14 B/param.
+// slab pool, instead of 14 B/param.  In the fp32 debug precision the
+// streamed copy, slabs and kept gradients hold fp32 instead.
 #include <stdlib.h>
 #include <string.h>
 
@@ -19,15 +20,15 @@
 
 namespace mt {
 
-uint16_t* SlabPool::acquire() {
+void* SlabPool::acquire() {
   std::unique_lock<std::mutex> lk(mu_);
   cv_.wait(lk, [&] { return !free_.empty(); });
-  uint16_t* p = free_.back();
+  void* p = free_.back();
   free_.pop_back();
   return p;
 }
 
-void SlabPool::release(uint16_t* p) {
+void SlabPool::release(void* p) {
   {
     std::lock_guard<std::mutex> lk(mu_);
     free_.push_back(p);
@@ -119,6 +120,7 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
   m->cfg = *cfg;
   m->run = *run;
   m->shape = d;
+  m->es = d.es();
   m->ll = layer_layout(d);
   m->hl = head_layout(d);
   const int L = cfg->n_layers;
@@ -128,16 +130,17 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
   m->units[L + 1].n = align128((size_t)d.V * d.H);
   const bool pinned = run->host_alloc == MT_HOST_PINNED;
 
-  // bf16 copy of every unit in one pinned region
+  // streamed copy of every unit in one pinned region
+  const size_t es = m->es;
   size_t shadow_elems = 0;
   for (auto& u : m->units) shadow_elems += u.n;
-  uint16_t* sh = static_cast<uint16_t*>(m->host_alloc(shadow_elems * 2, pinned));
+  char* sh = static_cast<char*>(m->host_alloc(shadow_elems * es, pinned));
   if (!sh) return set_error(MT_E_OOM_HOST, "mt_model_create: %s allocation of %zu bytes failed",
-                            pinned ? "pinned" : "host", shadow_elems * 2);
+                            pinned ? "pinned" : "host", shadow_elems * es);
   m->pool.reset(new ThreadPool(run->host_threads));
   size_t off = 0;
   for (auto& u : m->units) {
-    u.shadow = sh + off;
+    u.shadow = sh + off * es;
     off += u.n;
     u.master = static_cast<float*>(m->host_alloc(u.n * 4, false));
     u.m = static_cast<float*>(m->host_alloc(u.n * 4, false));
@@ -145,17 +148,17 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
     if (!u.master || !u.m || !u.v)
       return set_error(MT_E_OOM_HOST, "mt_model_create: host allocation of %zu bytes failed", u.n * 4);
     if (run->keep_grads) {
-      u.kept = static_cast<uint16_t*>(m->host_alloc(u.n * 2, false));
+      u.kept = m->host_alloc(u.n * es, false);
       if (!u.kept) return set_error(MT_E_OOM_HOST, "mt_model_create: keep_grads allocation failed");
     }
     // first touch in parallel (places pages, zeroes pads and moments)
     float* ps[3] = {u.master, u.m, u.v};
-    uint16_t* shp = u.shadow;
-    uint16_t* kp = u.kept;
+    char* shp = static_cast<char*>(u.shadow);
+    char* kp = static_cast<char*>(u.kept);
     m->pool->parallel_for(u.n, [&](size_t lo, size_t hi) {
       for (float* p : ps) memset(p + lo, 0, (hi - lo) * 4);
-      memset(shp + lo, 0, (hi - lo) * 2);
-      if (kp) memset(kp + lo, 0, (hi - lo) * 2);
+      memset(shp + lo * es, 0, (hi - lo) * es);
+      if (kp) memset(kp + lo * es, 0, (hi - lo) * es);
     });
   }
   m->dE = static_cast<float*>(m->host_alloc((size_t)d.V * d.H * 4, false));
@@ -165,7 +168,7 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
   m->slab_elems = std::max(m->ll.total, m->hl.total);
   const int n_slabs = run->use_slab_pool ? run->n_slabs : 0;
   for (int i = 0; i < n_slabs; ++i) {
-    uint16_t* s = static_cast<uint16_t*>(m->host_alloc(m->slab_elems * 2, pinned));
+    void* s = m->host_alloc(m->slab_elems * es, pinned);
     if (!s) return set_error(MT_E_OOM_HOST, "mt_model_create: slab allocation failed");
     m->slab_list.push_back(s);
   }
@@ -186,11 +189,17 @@ mt_status mt_model_set_param(mt_model* m, const char* name, const float* src, si
            name ? name : "(null)");
   MT_CHECK(n == r.n, MT_E_SHAPE, "mt_model_set_param: '%s' has %zu elements, got %zu", name, r.n, n);
   Unit& u = m->units[r.unit];
+  const bool f32 = m->es == 4;
   m->pool->parallel_for(n, [&](size_t lo, size_t hi) {
     memcpy(u.master + r.off + lo, src + lo, (hi - lo) * 4);
     memset(u.m + r.off + lo, 0, (hi - lo) * 4);
     memset(u.v + r.off + lo, 0, (hi - lo) * 4);
-    for (size_t i = lo; i < hi; ++i) u.shadow[r.off + i] = host_f2bf(src[i]);
+    if (f32) {
+      memcpy(static_cast<float*>(u.shadow) + r.off + lo, src + lo, (hi - lo) * 4);
+    } else {
+      uint16_t* sh = static_cast<uint16_t*>(u.shadow) + r.off;
+      for (size_t i = lo; i < hi; ++i) sh[i] = host_f2bf(src[i]);
+    }
   });
   return MT_OK;
 }
@@ -204,18 +213,23 @@ mt_status mt_model_get_param(const mt_model* m, const char* name, int32_t which,
   MT_CHECK(n == r.n, MT_E_SHAPE, "mt_model_get_param: '%s' has %zu elements, got %zu", name, r.n, n);
   const Unit& u = m->units[r.unit];
   const bool embed = r.unit == m->cfg.n_layers + 1;
+  // element i of a streamed-precision array (bf16 or fp32) as fp32
+  auto elem = [&](const void* base, size_t i) {
+    return m->es == 4 ? static_cast<const float*>(base)[i]
+                      : host_bf2f(static_cast<const uint16_t*>(base)[i]);
+  };
   switch (which) {
     case MT_GET_MASTER: memcpy(dst, u.master + r.off, n * 4); break;
     case MT_GET_M: memcpy(dst, u.m + r.off, n * 4); break;
     case MT_GET_V: memcpy(dst, u.v + r.off, n * 4); break;
     case MT_GET_SHADOW:
-      for (size_t i = 0; i < n; ++i) dst[i] = host_bf2f(u.shadow[r.off + i]);
+      for (size_t i = 0; i < n; ++i) dst[i] = elem(u.shadow, r.off + i);
       break;
     case MT_GET_GRAD:
       MT_CHECK(m->run.keep_grads, MT_E_STATE, "mt_model_get_param: gradients need keep_grads = 1");
       if (embed) memcpy(dst, m->dE + r.off, n * 4);
       else
-        for (size_t i = 0; i < n; ++i) dst[i] = host_bf2f(u.kept[r.off + i]);
+        for (size_t i = 0; i < n; ++i) dst[i] = elem(u.kept, r.off + i);
       break;
     default: return set_error(MT_E_INVALID, "mt_model_get_param: bad 'which' %d", which);
   }

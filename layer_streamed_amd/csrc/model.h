@@ -1,6 +1,7 @@
 // The host-resident model: the authoritative flat store of fp32 master
-// weights and Adam moments, the pinned bf16 copy that streams to the GPU,
-// the pinned gradient slab pool, and the per-step scratch the engine uses.
+// weights and Adam moments, the pinned copy that streams to the GPU (bf16,
+// or fp32 in the debug precision), the pinned gradient slab pool, and the
+// per-step scratch the engine uses.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -20,13 +21,15 @@
 namespace mt {
 
 // Units: 0..L-1 layers, L = head (final norm + LM head), L+1 = embedding.
+// Element types of the streamed copy, slabs and kept gradients follow the
+// model's precision: bf16 bit patterns (uint16_t) or fp32.
 struct Unit {
   size_t n = 0;               // elements (with alignment padding)
   float* master = nullptr;    // fp32, pageable
   float* m = nullptr;
   float* v = nullptr;
-  uint16_t* shadow = nullptr; // bf16 copy, inside the pinned shadow region
-  uint16_t* kept = nullptr;   // last step's bf16 gradient (keep_grads)
+  void* shadow = nullptr;     // streamed copy, inside the pinned shadow region
+  void* kept = nullptr;       // last step's gradient (keep_grads)
 };
 
 struct TensorRef {
@@ -37,16 +40,16 @@ struct TensorRef {
 // Pool of pinned gradient slabs shared by the offload and optimizer threads.
 class SlabPool {
  public:
-  void init(std::vector<uint16_t*> slabs) { free_ = std::move(slabs); }
-  uint16_t* acquire();
-  void release(uint16_t* p);
+  void init(std::vector<void*> slabs) { free_ = std::move(slabs); }
+  void* acquire();
+  void release(void* p);
   size_t capacity() const { return total_; }
   void set_total(size_t t) { total_ = t; }
 
  private:
   std::mutex mu_;
   std::condition_variable cv_;
-  std::vector<uint16_t*> free_;
+  std::vector<void*> free_;
   size_t total_ = 0;
 };
 
@@ -66,14 +69,15 @@ struct mt_model {
   mt::HeadLayout hl{};
   std::vector<mt::Unit> units;
   std::vector<mt::HostBlock> blocks;
+  size_t es = 2;  // bytes per streamed element (2: bf16, 4: fp32 debug)
   size_t slab_elems = 0;
   mt::SlabPool slabs;
-  std::vector<uint16_t*> slab_list;
+  std::vector<void*> slab_list;
   std::unique_ptr<mt::ThreadPool> pool;
   float* dE = nullptr;          // fp32 embedding gradient [V, H]
   // pinned per-step staging, grown on demand
-  uint16_t* x0_host = nullptr;
-  uint16_t* dx0_host = nullptr;
+  void* x0_host = nullptr;
+  void* dx0_host = nullptr;
   int32_t* tgt_host = nullptr;
   float* loss_host = nullptr;
   size_t staging_tokens = 0;

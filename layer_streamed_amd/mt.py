@@ -92,6 +92,10 @@ _lib.mt_last_error.argtypes = []
 _SIGS = {
     "mt_op_gemm": (_I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                    _P, _I64, _P, _I64, _I32, _P),
+    "mt_op_gemm_f32": (_I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                       _P, _I64, _P, _I64, _I32, _P),
+    "mt_op_attn_fwd_f32": (_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
+    "mt_op_attn_bwd_f32": (_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
     "mt_op_rmsnorm_fwd": (_I32, _P, _P, _P, _P, _I32, _I32, _F, _P),
     "mt_op_rmsnorm_bwd": (_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
     "mt_op_rope_table": (_I32, _P, _P, _I32, _I32, _D, _P),
@@ -176,6 +180,14 @@ def gemm(layout, epi, M, N, K, A, lda, B, ldb, Cm, ldc, R=None, ldr=0, C2=None, 
                ptr(R), ldr, ptr(C2), ldc2, ptr(G), ldg, F, stream_handle(stream)), "mt_op_gemm")
 
 
+def gemm_f32(layout, epi, M, N, K, A, lda, B, ldb, Cm, ldc, R=None, ldr=0, C2=None, ldc2=0,
+             G=None, ldg=0, F=0, stream=None):
+    """The fp32 debug-precision product: every operand fp32."""
+    check(call("mt_op_gemm_f32", layout, epi, M, N, K, ptr(A), lda, ptr(B), ldb, ptr(Cm), ldc,
+               ptr(R), ldr, ptr(C2), ldc2, ptr(G), ldg, F, stream_handle(stream)),
+          "mt_op_gemm_f32")
+
+
 def rmsnorm_fwd(x, g, y, rstd, rows, cols, eps, stream=None):
     check(call("mt_op_rmsnorm_fwd", ptr(x), ptr(g), ptr(y), ptr(rstd), rows, cols, eps,
                stream_handle(stream)), "mt_op_rmsnorm_fwd")
@@ -210,6 +222,18 @@ def attn_bwd(qkv, o, lse, dout, delta, dqkv, batch, seq, n_heads, n_kv_heads, he
              stream=None):
     check(call("mt_op_attn_bwd", ptr(qkv), ptr(o), ptr(lse), ptr(dout), ptr(delta), ptr(dqkv),
                batch, seq, n_heads, n_kv_heads, head_dim, stream_handle(stream)), "mt_op_attn_bwd")
+
+
+def attn_fwd_f32(qkv, o, lse, batch, seq, n_heads, n_kv_heads, head_dim, stream=None):
+    check(call("mt_op_attn_fwd_f32", ptr(qkv), ptr(o), ptr(lse), batch, seq, n_heads, n_kv_heads,
+               head_dim, stream_handle(stream)), "mt_op_attn_fwd_f32")
+
+
+def attn_bwd_f32(qkv, o, lse, dout, delta, dqkv, batch, seq, n_heads, n_kv_heads, head_dim,
+                 stream=None):
+    check(call("mt_op_attn_bwd_f32", ptr(qkv), ptr(o), ptr(lse), ptr(dout), ptr(delta),
+               ptr(dqkv), batch, seq, n_heads, n_kv_heads, head_dim, stream_handle(stream)),
+          "mt_op_attn_bwd_f32")
 
 
 def ce_rows(logits, target, dlogits, loss_part, rows, vocab, inv_n, stream=None):

@@ -24,8 +24,11 @@ def rel(a, b):
     return float(np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-30))
 
 
-def _layer_case(shape, B, T, seed, mlp_chunk=0, x_scale=1.0):
+def _layer_case(shape, B, T, seed, mlp_chunk=0, x_scale=1.0, fp32=False):
+    """fp32=True runs the fp32 debug precision: the GPU holds the fp32
+    values unrounded and the oracle runs in float64."""
     torch, mt = _env()
+    rnd = (lambda a: a.astype(np.float64)) if fp32 else oracle.bf16_round
     names = synth.layer_param_names(0)
     w = synth.make_weights(shape, seed=seed, names=names)
     w = {n.split(".")[-1]: v for n, v in w.items()}
@@ -33,12 +36,13 @@ def _layer_case(shape, B, T, seed, mlp_chunk=0, x_scale=1.0):
     # gains away from 1 so their gradients are exercised
     w["attn_norm"] = (1 + 0.1 * rng.standard_normal(shape.hidden)).astype(np.float32)
     w["mlp_norm"] = (1 + 0.1 * rng.standard_normal(shape.hidden)).astype(np.float32)
-    wb = {k: oracle.bf16_round(v) for k, v in w.items()}  # the values the GPU holds
-    x = oracle.bf16_round((rng.standard_normal((B, T, shape.hidden)) * x_scale).astype(np.float32))
-    dy = oracle.bf16_round((rng.standard_normal((B, T, shape.hidden)) * 1e-2).astype(np.float32))
+    wb = {k: rnd(v) for k, v in w.items()}  # the values the GPU holds
+    x = rnd((rng.standard_normal((B, T, shape.hidden)) * x_scale).astype(np.float32))
+    dy = rnd((rng.standard_normal((B, T, shape.hidden)) * 1e-2).astype(np.float32))
 
     def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+        return t if fp32 else t.to(torch.bfloat16)
 
     W = {
         "attn_norm": dev(wb["attn_norm"]),
@@ -52,7 +56,8 @@ def _layer_case(shape, B, T, seed, mlp_chunk=0, x_scale=1.0):
     G = {k: torch.full_like(v, float("nan")) for k, v in W.items()}
     gview = mt.GradView(*[G[k].data_ptr() for k, _ in mt.GradView._fields_])
     mcfg = mt.model_cfg(shape)
-    rcfg = mt.run_cfg(mlp_chunk_tokens=mlp_chunk)
+    rcfg = mt.run_cfg(mlp_chunk_tokens=mlp_chunk,
+                      precision=mt.PREC_FP32_DEBUG if fp32 else mt.PREC_BF16)
     X = dev(x.reshape(B * T, -1))
     Y = torch.empty_like(X)
     ws = torch.empty(mt.layer_workspace_bytes(mcfg, rcfg, B, T, 1), dtype=torch.uint8, device="cuda")
@@ -102,3 +107,24 @@ def test_layer_7b_shape_one_sequence():
     out = _layer_case(shape, 1, 256, seed=3)
     for k, (gpu, ref) in out.items():
         assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))
+
+
+# fp32 debug precision: every buffer fp32, fp32 FMA kernels; the oracle in
+# float64.  The bar is 1e-4 relative (the fp32 error of the longest
+# reductions here is ~1e-6).
+F32_TOL = 1e-4
+
+F32_CASES = [
+    ("tiny", synth.CONFIGS["tiny-2l-h256"], 2, 128, 0),
+    ("tiny-ragged-chunked", synth.CONFIGS["tiny-2l-h256"], 3, 45, 64),
+    ("gqa5-d128", synth.ModelShape(name="gqa5", n_layers=1, hidden=640, n_heads=10,
+                                   n_kv_heads=2, head_dim=128, ffn=1536, vocab=1024), 1, 96, 0),
+]
+
+
+@pytest.mark.parametrize("name,shape,B,T,chunk", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_layer_fp32_debug_precision(name, shape, B, T, chunk):
+    out = _layer_case(shape, B, T, seed=12, mlp_chunk=chunk, fp32=True)
+    for k, (gpu, ref) in out.items():
+        assert np.isfinite(gpu).all(), k
+        assert rel(gpu, ref) < F32_TOL, (k, rel(gpu, ref))

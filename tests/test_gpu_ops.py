@@ -315,3 +315,113 @@ def test_gemm_large_tiles_sampled(layout, M, N, K):
     b = B.float().cpu().numpy().astype(np.float64)
     ref = a @ (b.T if layout == 0 else b)
     assert rel_fro(Cm[rows].float().cpu().numpy(), ref) < 5e-3
+
+
+# ------------------------------------------------- fp32 debug precision
+# The fp32 kernels are plain fp32 FMA with exact exp/log: against a float64
+# evaluation of the same inputs the relative error is a few fp32 ulps times
+# the square root of the reduction length, far below 1e-5.
+F32_TOL = 1e-5
+
+F32_GEMM_CASES = [(0, 130, 70, 100), (1, 130, 70, 100), (2, 130, 70, 100),
+                  (0, 64, 128, 16), (1, 1, 3, 1), (2, 3, 1, 5)]
+
+
+def f32_dev(a):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+
+@pytest.mark.parametrize("layout,M,N,K", F32_GEMM_CASES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+def test_gemm_f32_layouts_and_epilogues(layout, M, N, K, epi):
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(300 + layout * 7 + epi)
+    a = _rand(rng, (K, M) if layout == 2 else (M, K))
+    b = _rand(rng, (N, K) if layout == 0 else (K, N))
+    af, bf = a.astype(np.float64), b.astype(np.float64)
+    ref = (af.T if layout == 2 else af) @ (bf.T if layout == 0 else bf)
+    r = None
+    Cm = torch.zeros((M, N), device="cuda", dtype=torch.float32)
+    if epi == 3:
+        r = _rand(rng, (M, N))
+        ref = ref + r
+    if epi == 2:
+        init = _rand(rng, (M, N))
+        Cm.copy_(torch.from_numpy(init))
+        ref = ref + init
+    lda = M if layout == 2 else K
+    ldb = K if layout == 0 else N
+    mt.gemm_f32(layout, epi, M, N, K, f32_dev(a), lda, f32_dev(b), ldb, Cm, N,
+                R=None if r is None else f32_dev(r), ldr=N)
+    torch.cuda.synchronize()
+    assert rel_fro(Cm.cpu().numpy(), ref) < F32_TOL
+
+
+@pytest.mark.parametrize("M,F,K", [(130, 96, 72), (64, 64, 64)])
+def test_gemm_f32_swiglu_epilogues(M, F, K):
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(8)
+    b = _rand(rng, (M, K))
+    wg, wu = _rand(rng, (F, K), 0.2), _rand(rng, (F, K), 0.2)
+    m = torch.zeros((M, F), device="cuda", dtype=torch.float32)
+    gu = torch.zeros((M, 2 * F), device="cuda", dtype=torch.float32)
+    mt.gemm_f32(0, 5, M, 2 * F, K, f32_dev(b), K, f32_dev(np.concatenate([wg, wu])), K, m, F,
+                C2=gu, ldc2=2 * F, F=F)
+    m4 = torch.zeros_like(m)
+    mt.gemm_f32(0, 4, M, 2 * F, K, f32_dev(b), K, f32_dev(np.concatenate([wg, wu])), K, m4, F,
+                F=F)
+    torch.cuda.synchronize()
+    gt = b.astype(np.float64) @ wg.T.astype(np.float64)
+    ut = b.astype(np.float64) @ wu.T.astype(np.float64)
+    assert rel_fro(gu.cpu().numpy()[:, :F], gt) < F32_TOL
+    assert rel_fro(gu.cpu().numpy()[:, F:], ut) < F32_TOL
+    assert rel_fro(m.cpu().numpy(), D.silu(gt) * ut) < F32_TOL
+    np.testing.assert_array_equal(m4.cpu().numpy(), m.cpu().numpy())
+    H = K
+    dy = _rand(rng, (M, H))
+    wd = _rand(rng, (H, F), 0.2)
+    dgu = torch.zeros((M, 2 * F), device="cuda", dtype=torch.float32)
+    mt.gemm_f32(1, 6, M, F, H, f32_dev(dy), H, f32_dev(wd), F, dgu, 2 * F, C2=dgu, ldc2=2 * F,
+                G=gu, ldg=2 * F, F=F)
+    torch.cuda.synchronize()
+    g64 = gu.cpu().numpy()[:, :F].astype(np.float64)
+    u64 = gu.cpu().numpy()[:, F:].astype(np.float64)
+    dm = dy.astype(np.float64) @ wd.astype(np.float64)
+    sg = 1 / (1 + np.exp(-g64))
+    assert rel_fro(dgu.cpu().numpy()[:, :F], dm * u64 * sg * (1 + g64 * (1 - sg))) < F32_TOL
+    assert rel_fro(dgu.cpu().numpy()[:, F:], dm * D.silu(g64)) < F32_TOL
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,d", [(2, 128, 4, 2, 64), (1, 70, 6, 2, 128),
+                                          (2, 33, 10, 2, 64), (3, 1, 4, 4, 128)])
+def test_attention_f32_forward_backward(B, T, Hq, Hkv, d):
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(T + 17 * Hq)
+    qkv = _rand(rng, (B * T, (Hq + 2 * Hkv) * d))
+    q = qkv[:, : Hq * d].reshape(B, T, Hq, d).astype(np.float64)
+    k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(B, T, Hkv, d).astype(np.float64)
+    v = qkv[:, (Hq + Hkv) * d:].reshape(B, T, Hkv, d).astype(np.float64)
+    QKV = f32_dev(qkv)
+    O = torch.empty((B * T, Hq * d), device="cuda", dtype=torch.float32)
+    LSE = torch.empty((B, Hq, T), device="cuda", dtype=torch.float32)
+    mt.attn_fwd_f32(QKV, O, LSE, B, T, Hq, Hkv, d)
+    do = _rand(rng, (B * T, Hq * d))
+    delta = torch.empty((B, Hq, T), device="cuda", dtype=torch.float32)
+    DQKV = torch.full((B * T, (Hq + 2 * Hkv) * d), float("nan"), device="cuda")
+    mt.attn_bwd_f32(QKV, O, LSE, f32_dev(do), delta, DQKV, B, T, Hq, Hkv, d)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = D.causal_attention(q, k, v)
+    assert rel_fro(O.cpu().numpy(), o_ref.reshape(B * T, -1)) < F32_TOL
+    np.testing.assert_allclose(LSE.cpu().numpy(), lse_ref, rtol=0, atol=1e-5)
+    dq, dk, dv = D.causal_attention_backward(q, k, v, o_ref, lse_ref,
+                                             do.reshape(B, T, Hq, d).astype(np.float64))
+    out = DQKV.cpu().numpy()
+    floor = 1e-4 * np.linalg.norm(do)  # dq, dk vanish at T = 1
+
+    def err(a, b):
+        return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), floor))
+
+    assert err(out[:, : Hq * d], dq.reshape(B * T, -1)) < F32_TOL
+    assert err(out[:, Hq * d:(Hq + Hkv) * d], dk.reshape(B * T, -1)) < F32_TOL
+    assert err(out[:, (Hq + Hkv) * d:], dv.reshape(B * T, -1)) < F32_TOL

@@ -152,3 +152,42 @@ def test_chunked_mlp_and_head_long_sequence_matches_oracle():
     assert abs(g["loss"][0] - loss) < LOSS_TOL, (g["loss"][0], loss)
     for n in synth.param_names(s):
         assert rel(g["grad"][n], grads[n]) < REL_TOL, (n, rel(g["grad"][n], grads[n]))
+
+
+# fp32 debug precision: streamed copy, activations, gradients and slabs all
+# fp32; the oracle in float64.  Bar: 1e-4 relative (loss: absolute).
+F32_TOL = 1e-4
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(mlp_chunk_tokens=64, head_chunk_tokens=100)],
+                         ids=["whole", "chunked"])
+def test_step_fp32_debug_precision_matches_oracle(tiny, kw):
+    torch, mt = _env()
+    s, w, ids = tiny
+    g = _run(s, w, ids, precision=mt.PREC_FP32_DEBUG, **kw)
+    w64 = {k: v.astype(np.float64) for k, v in w.items()}
+    loss, grads, newp, state = D.train_step(w64, ids, s)
+    assert abs(g["loss"][0] - loss) < F32_TOL, (g["loss"][0], loss)
+    for n in synth.param_names(s):
+        assert rel(g["grad"][n], grads[n]) < F32_TOL, (n, rel(g["grad"][n], grads[n]))
+        assert rel(g["m"][n], state[n][0]) < F32_TOL, n
+        assert rel(g["master"][n], newp[n]) < F32_TOL, n
+        # the streamed copy is the updated master itself
+        np.testing.assert_array_equal(g["shadow"][n], g["master"][n])
+    # the update itself: away from gradients within fp32 noise of zero,
+    # Adam's first step moves each weight by lr * sign(g)
+    for n in synth.param_names(s):
+        dp, dref = g["master"][n] - w[n], newp[n] - w64[n]
+        sure = np.abs(grads[n]) > 1e-3 * np.abs(grads[n]).max()
+        assert rel(dp[sure], dref[sure]) < 1e-3, (n, rel(dp[sure], dref[sure]))
+
+
+def test_step_fp32_schedule_invariance_bitwise(tiny):
+    torch, mt = _env()
+    s, w, ids = tiny
+    base = _run(s, w, ids, precision=mt.PREC_FP32_DEBUG)
+    other = _run(s, w, ids, precision=mt.PREC_FP32_DEBUG, serialize=1, ckpt_interval=2)
+    assert base["loss"] == other["loss"]
+    for n in synth.param_names(s):
+        np.testing.assert_array_equal(base["grad"][n], other["grad"][n], err_msg=n)
+        np.testing.assert_array_equal(base["master"][n], other["master"][n], err_msg=n)

@@ -102,3 +102,32 @@ def test_run_cfg_defaults():
     r = _mt().run_cfg()
     assert r.ckpt_interval == 4 and r.prefetch_depth == 2 and r.use_slab_pool == 1
     assert r.lr == 1e-4 and r.beta1 == 0.9 and r.beta2 == 0.999 and r.eps == 1e-8
+
+
+@pytest.mark.parametrize("prec", [0, 1], ids=["bf16", "fp32_debug"])
+def test_host_store_roundtrip_and_streamed_copy(prec):
+    """A model in pageable host memory (no GPU): parameters round-trip, and
+    the streamed copy is the bf16 rounding of the master (bf16 precision)
+    or the master itself (fp32 debug precision)."""
+    import synth
+    mt = _mt()
+    s = synth.CONFIGS["tiny-2l-h256"]
+    m = mt.Model(s, host_alloc=mt.HOST_PAGEABLE, precision=prec)
+    w = synth.make_weights(s, seed=9)
+    m.set_params(w)
+    for n in ("embed", "layers.1.w_k", "lm_head", "final_norm"):
+        np.testing.assert_array_equal(m.get(n), w[n])
+        sh = m.get(n, mt.GET_SHADOW)
+        np.testing.assert_array_equal(sh, D.bf16_round(w[n]) if prec == 0 else w[n])
+    m.close()
+
+
+def test_workspace_grows_with_fp32_and_rejects_unknown_precision():
+    import synth
+    mt = _mt()
+    s = synth.CONFIGS["tiny-2l-h256"]
+    mc = mt.model_cfg(s)
+    b = mt.layer_workspace_bytes(mc, mt.run_cfg(precision=0), 2, 128, 1)
+    f = mt.layer_workspace_bytes(mc, mt.run_cfg(precision=1), 2, 128, 1)
+    assert 0 < b < f
+    assert mt.layer_workspace_bytes(mc, mt.run_cfg(precision=2), 2, 128, 1) == 0
