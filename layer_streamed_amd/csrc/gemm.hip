@@ -351,31 +351,262 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// NT product with direct global -> LDS loads (gfx950 global_load_lds_dwordx4).
-// Both operands are K-contiguous, so each lane's 16-byte chunk can land in
-// LDS without passing through registers: lane t of a wave instruction writes
-// LDS base + 16 t.  A ring of DL_STAGES stages of DL_BK columns keeps three
-// stages of loads in flight while one is computed, so the load latency is
-// covered by LDS capacity instead of registers.  Within a row the 4 chunks
-// are stored in the order c ^ ((row >> 2) & 3), which makes the fragment
-// reads (32 lanes, 32 consecutive rows, one chunk) bank-conflict free.
-// Requires K % DL_BK == 0; rows past M or N are clamped to a valid row (they
-// only feed output elements the epilogue drops).
+// Products with direct global -> LDS loads (gfx950 global_load_lds_dwordx4):
+// lane t of a wave instruction writes its 16-byte chunk to LDS base + 16 t,
+// so no operand passes through registers on its way in.  A ring of
+// DL_STAGES stages of DL_BK k-values keeps three stages of loads in flight
+// while one is computed: the load latency is covered by LDS capacity instead
+// of registers.
+//
+// Each operand keeps its global layout in LDS:
+//  - K-contiguous (NT's A and B, NN's A): a stage is BM rows of DL_BK k, 4
+//    chunks of 8 per row stored in the order c ^ ((row >> 2) & 3); a
+//    fragment (8 consecutive k of one row per lane) is one ds_read_b128, and
+//    32 lanes reading 32 consecutive rows hit distinct banks.
+//  - K-major (NN's B, TN's A and B): a stage is DL_BK rows of k, each BM
+//    values of m wide (BM / 8 chunks) stored in the order c ^ km_swz(k).
+//    A fragment is read with two ds_read_b64_tr_b16 (gfx950 LDS transpose
+//    read): within each group of 16 lanes, lane i receives element i & 3 of
+//    the 8-byte pieces addressed by lanes 4 j + (i >> 2), j = 0..3; when
+//    those lanes address rows k..k+3 at columns m0, m0+4, m0+8, m0+12, lane
+//    i holds column m0 + i at rows k..k+3, i.e. four consecutive k of one
+//    MFMA row (issued as inline asm; see dl_frag).  Each 16-lane group reads
+//    4 rows x 2 chunks and each half-wave
+//    4 rows x 4 chunks; the XOR patterns {0, 6, 10, 12} of km_swz differ in
+//    bits 1-2 and in bits 2-3, so both sets land on distinct banks.
+// Both give each lane k-slots 8 (l / 32) .. + 7 in natural order, so the
+// operand kinds mix freely.  Requires K % DL_BK == 0 and, for K-major
+// operands, M or N % 8 == 0; rows or columns past M or N are clamped to a
+// valid one (they only feed output elements the epilogue drops).
 constexpr int DL_BK = 32;
 constexpr int DL_STAGES = 4;
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int km_swz(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Global source of one LDS slot of an operand stage (k0 = 0) and the
+// per-stage advance, for a tile whose first row (K-contiguous) or column
+// (K-major) is r0 of an extent of `ext`.
+template <bool KM, int BR>
+__device__ __forceinline__ const uint16_t* dl_src(const uint16_t* base, long ld, int pos, int r0,
+                                                   int ext, int swi_f) {
+  if constexpr (!KM) {
+    constexpr int CH = DL_BK / 8;
+    const int row = pos / CH, slot = pos % CH;
+    const int c = slot ^ ((row >> 2) & (CH - 1));
+    int gr = min(r0 + row, ext - 1);
+    if (swi_f) gr = SwiMap{swi_f}(gr);
+    return base + (long)gr * ld + c * 8;
+  } else {
+    constexpr int RC = BR / 8;  // chunks per k-row
+    const int k = pos / RC, slot = pos % RC;
+    const int c = slot ^ km_swz(k);
+    const int col = min(r0 + 8 * c, ext - 8);
+    return base + (long)k * ld + col;
+  }
+}
+
+// Fragment of rows (K-contiguous) or columns (K-major) rb .. rb + 31 for
+// k-substep ks of a stage starting at `st`.
+template <bool KM, int BR>
+__device__ __forceinline__ u32x4_t dl_frag(const char* st, int rb, int ks, int lane) {
+  if constexpr (!KM) {
+    constexpr int CH = DL_BK / 8;
+    const int r = rb + (lane & 31);
+    const int c = ks * 2 + (lane >> 5);
+    return reinterpret_cast<const u32x4_t*>(st)[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
+  } else {
+    constexpr int RC = BR / 8;
+    const int grp = lane >> 4, i = lane & 15;
+    const int m = rb + 16 * (grp & 1) + 4 * (i & 3);
+    const int c = m >> 3, half = (m >> 2) & 1;
+    u32x2_t v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = ks * 16 + 8 * (grp >> 1) + 4 * h + (i >> 2);
+      const char* p = st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8);
+      // Issued as asm: the compiler's wait insertion cannot tell this LDS
+      // read from the in-flight global->LDS stores of later stages and would
+      // drain every outstanding load before it (vmcnt(0)), serializing the
+      // ring.  The kernel orders the stores itself (vmcnt + barrier), and
+      // the caller waits lgkmcnt(0) before the first use of the result.
+      const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[h]) : "v"(la) : "memory");
+    }
+    return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
+  }
+}
+
+// Epilogue of the direct-to-LDS kernels, staged through LDS (free once the
+// main loop is done): each wave writes one 32 x 32 accumulator block (two
+// for a SwiGLU gate/up pair) to a private slot, reads it back so that every
+// lane owns 16 consecutive columns of one row, and moves them with 16-byte
+// global accesses instead of 2- or 4-byte scattered ones.  Blocks that
+// cross the matrix edge, or launches whose strides or pointers are not
+// 16-byte multiples (a.vec == 0), take a per-element path.
+constexpr int EPI_LD = 36;  // slot row stride in floats (16-byte aligned rows)
+constexpr int EPI_SLOT = 32 * EPI_LD * 4;  // bytes per staged block
+
+__device__ __forceinline__ void unpack8f(u32x4_t v, float* f) {
+  f[0] = lo_bf(v.x); f[1] = hi_bf(v.x); f[2] = lo_bf(v.y); f[3] = hi_bf(v.y);
+  f[4] = lo_bf(v.z); f[5] = hi_bf(v.z); f[6] = lo_bf(v.w); f[7] = hi_bf(v.w);
+}
+__device__ __forceinline__ u32x4_t pack8f(const float* f) {
+  return u32x4_t{pack_bf(f[0], f[1]), pack_bf(f[2], f[3]), pack_bf(f[4], f[5]), pack_bf(f[6], f[7])};
+}
+__device__ __forceinline__ void ld16_bf(const uint16_t* p, float* f) {
+  unpack8f(reinterpret_cast<const u32x4_t*>(p)[0], f);
+  unpack8f(reinterpret_cast<const u32x4_t*>(p)[1], f + 8);
+}
+__device__ __forceinline__ void st16_bf(uint16_t* p, const float* f) {
+  reinterpret_cast<u32x4_t*>(p)[0] = pack8f(f);
+  reinterpret_cast<u32x4_t*>(p)[1] = pack8f(f + 8);
+}
+
+// acc block -> slot (row-major 32 x 32 fp32), then this lane's 16 values
+__device__ __forceinline__ void stage_block(float* slot, const f32x16_t& blk, int lane, float* v) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    slot[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EPI_LD + (lane & 31)] = blk[e];
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(slot + (lane >> 1) * EPI_LD + 16 * (lane & 1));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4_t t = src[q];
+    v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+  }
+}
+
 template <int WM, int WN, int TM, int TN, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_nt_dl_kernel(const GemmArgs a) {
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& a, f32x16_t (&acc)[TM][TN], int m0,
+                                             int n0, int wm, int wn, int lane, char* wslot) {
+  constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
+  float* s0 = reinterpret_cast<float*>(wslot);
+  float* s1 = reinterpret_cast<float*>(wslot + EPI_SLOT);
+  const int M = a.M;
+  const int rl = lane >> 1, c0 = 16 * (lane & 1);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm * TM * 32 + i * 32 + rl;
+    if constexpr (SWI) {
+      static_assert(TN % 2 == 0, "SwiGLU pairs need an even TN");
+      const int F = a.F;
+#pragma unroll
+      for (int q = 0; q < TN / 2; ++q) {
+        float g[16], u[16];
+        stage_block(s0, acc[i][2 * q], lane, g);
+        stage_block(s1, acc[i][2 * q + 1], lane, u);
+        const int f = (n0 + wn * TN * 32) / 2 + 32 * q + c0;
+        float m[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m[e] = silu_f(g[e]) * u[e];
+        uint16_t* Cm = reinterpret_cast<uint16_t*>(a.C);
+        if (a.vec && row < M && f + 16 <= F) {
+          st16_bf(Cm + (long)row * a.ldc + f, m);
+          if constexpr (EPI == EPI_SWIGLU_SAVE) {
+            st16_bf(a.C2 + (long)row * a.ldc2 + f, g);
+            st16_bf(a.C2 + (long)row * a.ldc2 + F + f, u);
+          }
+        } else if (row < M) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (f + e >= F) break;
+            Cm[(long)row * a.ldc + f + e] = f2bf(m[e]);
+            if constexpr (EPI == EPI_SWIGLU_SAVE) {
+              a.C2[(long)row * a.ldc2 + f + e] = f2bf(g[e]);
+              a.C2[(long)row * a.ldc2 + F + f + e] = f2bf(u[e]);
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float v[16];
+        stage_block(s0, acc[i][j], lane, v);
+        const int col = n0 + wn * TN * 32 + j * 32 + c0;
+        const int N = a.N;
+        if (row >= M) continue;
+        const bool full = a.vec && col + 16 <= N;
+        if constexpr (EPI == EPI_BF16) {
+          uint16_t* p = reinterpret_cast<uint16_t*>(a.C) + (long)row * a.ldc + col;
+          if (full) st16_bf(p, v);
+          else
+            for (int e = 0; e < 16 && col + e < N; ++e) p[e] = f2bf(v[e]);
+        } else if constexpr (EPI == EPI_F32 || EPI == EPI_ACC_F32) {
+          float* p = reinterpret_cast<float*>(a.C) + (long)row * a.ldc + col;
+          if (full) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              f32x4_t t = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+              if constexpr (EPI == EPI_ACC_F32) {
+                const f32x4_t o = reinterpret_cast<const f32x4_t*>(p)[q];
+                t = f32x4_t{o.x + t.x, o.y + t.y, o.z + t.z, o.w + t.w};
+              }
+              reinterpret_cast<f32x4_t*>(p)[q] = t;
+            }
+          } else {
+            for (int e = 0; e < 16 && col + e < N; ++e) {
+              if constexpr (EPI == EPI_ACC_F32) p[e] += v[e];
+              else p[e] = v[e];
+            }
+          }
+        } else if constexpr (EPI == EPI_RESID_BF16) {
+          uint16_t* p = reinterpret_cast<uint16_t*>(a.C) + (long)row * a.ldc + col;
+          const uint16_t* r = a.R + (long)row * a.ldr + col;
+          if (full) {
+            float x[16];
+            ld16_bf(r, x);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] += v[e];
+            st16_bf(p, x);
+          } else {
+            for (int e = 0; e < 16 && col + e < N; ++e) p[e] = f2bf(bf2f(r[e]) + v[e]);
+          }
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+          const uint16_t* gp = a.G + (long)row * a.ldg + col;
+          uint16_t* dp = a.C2 + (long)row * a.ldc2 + col;
+          const int F = a.F;
+          if (full) {
+            float gt[16], u[16], dg[16], du[16];
+            ld16_bf(gp, gt);
+            ld16_bf(gp + F, u);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float sg = 1.f / (1.f + __expf(-gt[e]));
+              dg[e] = v[e] * u[e] * sg * (1.f + gt[e] * (1.f - sg));
+              du[e] = v[e] * gt[e] * sg;
+            }
+            st16_bf(dp, dg);
+            st16_bf(dp + F, du);
+          } else {
+            for (int e = 0; e < 16 && col + e < N; ++e) {
+              const float gt = bf2f(gp[e]), u = bf2f(gp[F + e]);
+              const float sg = 1.f / (1.f + __expf(-gt));
+              dp[e] = f2bf(v[e] * u * sg * (1.f + gt * (1.f - sg)));
+              dp[F + e] = f2bf(v[e] * gt * sg);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) {
+  constexpr bool A_KM = LAYOUT == GEMM_TN, B_KM = LAYOUT != GEMM_NT;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NW = WM * WN;
-  constexpr int CH = DL_BK / 8;  // 16-byte chunks per row
-  constexpr int A_CH = BM * CH, B_CH = BN * CH;
+  constexpr int A_CH = BM * DL_BK / 8, B_CH = BN * DL_BK / 8;  // 16-byte chunks per stage
   constexpr int A_PER = A_CH / 64 / NW, B_PER = B_CH / 64 / NW;  // instructions per wave
   static_assert(A_PER * 64 * NW == A_CH && B_PER * 64 * NW == B_CH, "tile/wave mismatch");
+  static_assert(!A_KM || BM >= 128, "K-major swizzle needs 16 chunks per row");
+  static_assert(!B_KM || BN >= 128, "K-major swizzle needs 16 chunks per row");
   constexpr int LPW = A_PER + B_PER;
   constexpr int STAGE = (A_CH + B_CH) * 16;  // bytes
   extern __shared__ __attribute__((aligned(16))) char dl_smem[];
@@ -396,25 +627,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_dl_kernel(const GemmArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
+  constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
   const uint16_t* ga[A_PER];
   const uint16_t* gb[B_PER];
 #pragma unroll
-  for (int p = 0; p < A_PER; ++p) {
-    const int pos = (wave * A_PER + p) * 64 + lane;
-    const int row = pos / CH, slot = pos % CH;
-    const int c = slot ^ ((row >> 2) & (CH - 1));
-    const int gr = min(m0 + row, M - 1);
-    ga[p] = a.A + (long)gr * a.lda + c * 8;
-  }
+  for (int p = 0; p < A_PER; ++p)
+    ga[p] = dl_src<A_KM, BM>(a.A, a.lda, (wave * A_PER + p) * 64 + lane, m0, M, 0);
 #pragma unroll
-  for (int p = 0; p < B_PER; ++p) {
-    const int pos = (wave * B_PER + p) * 64 + lane;
-    const int row = pos / CH, slot = pos % CH;
-    const int c = slot ^ ((row >> 2) & (CH - 1));
-    int gr = min(n0 + row, N - 1);
-    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) gr = SwiMap{a.F}(gr);
-    gb[p] = a.B + (long)gr * a.ldb + c * 8;
-  }
+  for (int p = 0; p < B_PER; ++p)
+    gb[p] = dl_src<B_KM, BN>(a.B, a.ldb, (wave * B_PER + p) * 64 + lane, n0, N, SWI ? a.F : 0);
+  // per-stage advance along K
+  const long a_step = A_KM ? (long)DL_BK * a.lda : DL_BK;
+  const long b_step = B_KM ? (long)DL_BK * a.ldb : DL_BK;
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -427,40 +651,39 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_dl_kernel(const GemmArgs 
   const int nk = K / DL_BK;
   auto issue = [&](int kt) {
     if (kt >= nk) return;
-    const int k0 = kt * DL_BK;
     char* base = dl_smem + (kt % DL_STAGES) * STAGE;
 #pragma unroll
     for (int p = 0; p < A_PER; ++p)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(ga[p] + k0),
+          (const void*)(ga[p] + kt * a_step),
           (__attribute__((address_space(3))) void*)(base + (wave * A_PER + p) * 1024), 16, 0, 0);
 #pragma unroll
     for (int p = 0; p < B_PER; ++p)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(gb[p] + k0),
+          (const void*)(gb[p] + kt * b_step),
           (__attribute__((address_space(3))) void*)(base + A_CH * 16 + (wave * B_PER + p) * 1024), 16,
           0, 0);
   };
 
-  const int arow = wm * TM * 32 + (lane & 31);
-  const int brow = wn * TN * 32 + (lane & 31);
-  const int hh = lane >> 5;
   auto compute = [&](int kt) {
-    const u32x4_t* sA = reinterpret_cast<const u32x4_t*>(dl_smem + (kt % DL_STAGES) * STAGE);
-    const u32x4_t* sB = sA + A_CH;
+    const char* sA = dl_smem + (kt % DL_STAGES) * STAGE;
+    const char* sB = sA + A_CH * 16;
 #pragma unroll
     for (int ks = 0; ks < DL_BK / 16; ++ks) {
-      const int c = ks * 2 + hh;
       u32x4_t af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = arow + i * 32;
-        af[i] = sA[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
-      }
+      for (int i = 0; i < TM; ++i) af[i] = dl_frag<A_KM, BM>(sA, wm * TM * 32 + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = brow + j * 32;
-        bfr[j] = sB[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
+      for (int j = 0; j < TN; ++j) bfr[j] = dl_frag<B_KM, BN>(sB, wn * TN * 32 + j * 32, ks, lane);
+      if constexpr (A_KM || B_KM) {
+        // the transpose reads were issued as asm, outside the compiler's
+        // wait tracking: wait for them, and tie every fragment to the wait
+        // so no use can be scheduled above it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < TM; ++i) asm volatile("" : "+v"(af[i]));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(bfr[j]));
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -483,14 +706,33 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_dl_kernel(const GemmArgs 
     issue(kt + DL_STAGES - 1);
     compute(kt);
   }
-  epilogue<WM, WN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
+  // the ring is free once every wave has finished reading its last stage
+  __syncthreads();
+  epilogue_lds<WM, WN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane,
+                                    dl_smem + wave * (SWI ? 2 : 1) * EPI_SLOT);
 }
 
-template <int WM, int WN, int TM, int TN, int EPI>
+// Whether the epilogue's 16-byte accesses are aligned for every row.
+inline bool epi_vec_ok(const GemmArgs& a) {
+  auto al = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  const bool f32 = a.epi == EPI_F32 || a.epi == EPI_ACC_F32;
+  bool ok = al(a.C) && a.ldc % (f32 ? 4 : 8) == 0;
+  if (a.epi == EPI_RESID_BF16) ok = ok && al(a.R) && a.ldr % 8 == 0;
+  if (a.epi == EPI_SWIGLU_SAVE || a.epi == EPI_SWIGLU_BWD)
+    ok = ok && al(a.C2) && a.ldc2 % 8 == 0 && a.F % 8 == 0;
+  if (a.epi == EPI_SWIGLU_BWD) ok = ok && al(a.G) && a.ldg % 8 == 0;
+  return ok;
+}
+
+template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI>
 hipError_t launch_dl(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  const size_t lds = (size_t)DL_STAGES * (BM + BN) * (DL_BK / 8) * 16;
-  auto kern = gemm_nt_dl_kernel<WM, WN, TM, TN, EPI>;
+  constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
+  constexpr size_t ring = (size_t)DL_STAGES * (BM + BN) * (DL_BK / 8) * 16;
+  constexpr size_t stage_out = (size_t)WM * WN * (SWI ? 2 : 1) * EPI_SLOT;
+  static_assert(stage_out <= ring, "epilogue slots must fit in the ring");
+  const size_t lds = ring;
+  auto kern = gemm_dl_kernel<LAYOUT, WM, WN, TM, TN, EPI>;
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -499,7 +741,9 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t s) {
     attr_done = true;
   }
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, a);
+  GemmArgs b = a;
+  b.vec = epi_vec_ok(a) ? 1 : 0;
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, b);
   return hipGetLastError();
 }
 
@@ -520,24 +764,26 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice: 256 x 256 (eight waves of 128 x 64, two per SIMD so one
-// wave's memory stalls hide behind the other's MFMAs) cuts LDS reads per
-// MFMA flop and L2 re-reads against 128 x 128; it is used when the grid
-// still fills the 256 CUs several times over.
-inline bool use_big_tile(const GemmArgs& a) {
-  const long t = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  return t >= 4 * 256;
+// Tile choice.  With K % 32 == 0 every layout takes the direct-to-LDS
+// kernel: 256 x 256 (eight waves of 128 x 64, two per SIMD, so one wave's
+// memory stalls hide behind the other's MFMAs) when the grid fills the 256
+// CUs at least four times over, else 256 x 128 (eight waves of 64 x 64) when
+// that does, else 128 x 128 (four waves of 64 x 64).  The SwiGLU-backward
+// epilogue keeps 128 x 128 (its extra live values would spill the larger
+// tiles' accumulators).  A ragged K takes the register-staged kernel.
+inline long tiles_of(const GemmArgs& a, int bm, int bn) {
+  return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
 template <int LAYOUT, int EPI>
 hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
-  if constexpr (LAYOUT == GEMM_NT && EPI != EPI_SWIGLU_BWD) {
-    if (use_big_tile(a) && a.K % DL_BK == 0) return launch_dl<2, 4, 4, 2, EPI>(a, s);
+  if (a.K % DL_BK == 0) {
+    if (tiles_of(a, 256, 256) >= 3 * 256) return launch_dl<LAYOUT, 2, 4, 4, 2, EPI>(a, s);
+    if (tiles_of(a, 256, 128) >= 4 * 256) return launch_dl<LAYOUT, 4, 2, 2, 2, EPI>(a, s);
+    return launch_dl<LAYOUT, 2, 2, 2, 2, EPI>(a, s);
   }
-  // the SwiGLU-backward epilogue needs more registers than the big tile
-  // leaves (it would spill its accumulators), so it keeps the 128 x 128 tile
   if constexpr (EPI != EPI_SWIGLU_BWD) {
-    if (use_big_tile(a)) return launch_cfg<2, 4, 4, 2, LAYOUT, EPI>(a, s);
+    if (tiles_of(a, 256, 256) >= 4 * 256) return launch_cfg<2, 4, 4, 2, LAYOUT, EPI>(a, s);
   }
   return launch_cfg<2, 2, 2, 2, LAYOUT, EPI>(a, s);
 }

@@ -40,6 +40,7 @@ struct GemmArgsT {
   E* C2 = nullptr; long ldc2 = 0;
   const E* G = nullptr; long ldg = 0;
   int F = 0;  // FFN width for the SwiGLU epilogues
+  int vec = 0;  // set by the launcher: strides and alignment allow 16-byte epilogue accesses
 };
 using GemmArgs = GemmArgsT<uint16_t>;
 using GemmArgsF32 = GemmArgsT<float>;

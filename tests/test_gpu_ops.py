@@ -46,6 +46,10 @@ GEMM_CASES = [
     (0, 300, 200, 264), (1, 300, 200, 264), (2, 296, 200, 264),
     (0, 256, 512, 256), (1, 256, 256, 1024), (2, 1024, 256, 256),
     (0, 128, 128, 64), (1, 8, 8, 8), (2, 8, 8, 8),
+    # direct-to-LDS tiles with ragged M and N (a partial last 16-column
+    # group takes the per-element epilogue) and, for NT, an odd ldc (no
+    # 16-byte epilogue at all)
+    (0, 300, 200, 256), (1, 300, 200, 256), (2, 296, 200, 256), (0, 300, 203, 256),
 ]
 
 
@@ -83,7 +87,7 @@ def test_gemm_layouts_and_epilogues(layout, M, N, K, epi):
         np.testing.assert_allclose(out, ref, rtol=1e-2, atol=1e-2 * np.abs(ref).max())
 
 
-@pytest.mark.parametrize("M,F,K", [(256, 1024, 256), (200, 96, 136)])
+@pytest.mark.parametrize("M,F,K", [(256, 1024, 256), (200, 96, 136), (200, 96, 128)])
 def test_gemm_swiglu_forward_and_backward_epilogues(M, F, K):
     torch, mt = _torch(), _mt()
     rng = np.random.default_rng(7)
@@ -298,23 +302,37 @@ def test_attention_forward_32k_sampled_heads():
         np.testing.assert_allclose(LSE[0, h].cpu().numpy()[rows], lse_ref[0, 0, rows], atol=2e-3)
 
 
-@pytest.mark.parametrize("layout,M,N,K", [(1, 16384, 3584, 4608), (2, 37888, 3584, 2048),
-                                          (0, 16384, 4608, 3584), (2, 3584, 18944, 3000),
-                                          (0, 16344, 4616, 3584), (0, 9000, 30000, 2048)])
-def test_gemm_large_tiles_sampled(layout, M, N, K):
-    """Shapes of the 7B layer that take the 256 x 256 tile path (ragged K on TN)."""
+@pytest.mark.parametrize("layout,M,N,K,epi", [
+    (1, 16384, 3584, 4608, 0), (2, 37888, 3584, 2048, 0), (0, 16384, 4608, 3584, 0),
+    (2, 3584, 18944, 3000, 0), (0, 16344, 4616, 3584, 0), (0, 9000, 30000, 2048, 0),
+    # direct-to-LDS path with K-major operands: NN's B, TN's A and B, ragged
+    # contiguous extents (clamped columns) and the fp32 accumulate epilogue
+    (1, 16380, 18936, 3584, 0), (2, 37880, 3592, 2048, 0), (2, 18944, 3584, 1024, 2)])
+def test_gemm_large_tiles_sampled(layout, M, N, K, epi):
+    """Shapes of the 7B layer that take the 256 x 256 tile paths (ragged K on
+    TN), plus ragged extents of the direct-to-LDS kernels."""
     torch, mt = _torch(), _mt()
     g = torch.Generator(device="cuda").manual_seed(M + N)
     A = torch.randn((K, M) if layout == 2 else (M, K), device="cuda", generator=g).to(torch.bfloat16)
     B = torch.randn((N, K) if layout == 0 else (K, N), device="cuda", generator=g).to(torch.bfloat16)
-    Cm = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
-    mt.gemm(layout, 0, M, N, K, A, M if layout == 2 else K, B, K if layout == 0 else N, Cm, N)
+    if epi == 2:
+        Cm = torch.randn((M, N), device="cuda", generator=g)
+        C0 = Cm.clone()
+    else:
+        Cm = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
+    mt.gemm(layout, epi, M, N, K, A, M if layout == 2 else K, B, K if layout == 0 else N, Cm, N)
     torch.cuda.synchronize()
     rows = np.concatenate([np.random.default_rng(1).choice(M, 14, replace=False), [0, M - 1]])
     a = (A[:, rows].t() if layout == 2 else A[rows]).float().cpu().numpy().astype(np.float64)
     b = B.float().cpu().numpy().astype(np.float64)
     ref = a @ (b.T if layout == 0 else b)
-    assert rel_fro(Cm[rows].float().cpu().numpy(), ref) < 5e-3
+    if epi == 2:
+        ref = ref + C0[rows].cpu().numpy()
+        assert rel_fro(Cm[rows].cpu().numpy(), ref) < 1e-5
+    else:
+        assert rel_fro(Cm[rows].float().cpu().numpy(), ref) < 5e-3
+    # the last column too (clamped chunks of a ragged contiguous extent)
+    assert np.isfinite(Cm[rows].float().cpu().numpy()).all()
 
 
 # ------------------------------------------------- fp32 debug precision
