@@ -106,8 +106,9 @@ typedef struct {
   double h2d_bytes, d2h_bytes;
   double h2d_ms, d2h_ms;    /* summed copy durations on the W and G streams */
   double exposed_wait_fwd_ms, exposed_wait_bwd_ms; /* compute idle while waiting on weights */
-  double probe_kernel_ms;   /* summed duration of the timed GEMM launches */
-  double probe_kernel_flops;/* algorithmic FLOPs of those launches */
+  double probe_kernel_ms;   /* summed duration of the launches of the GEMM kernel
+                               instantiation with the largest total time (time_kernels) */
+  double probe_kernel_flops;/* algorithmic FLOPs (2 M N K) of those launches */
   int64_t probe_kernel_launches;
   int64_t pinned_host_bytes, pageable_host_bytes, device_arena_bytes;
   int64_t units_updated;    /* units whose Adam update completed this step */
@@ -115,6 +116,8 @@ typedef struct {
    * buffer; offload thread blocked on a free slab and on backward ops;
    * optimizer thread idle waiting for a landed gradient */
   double host_ring_wait_ms, host_slab_wait_ms, host_op_wait_ms, host_adam_idle_ms;
+  double probe_all_gemm_ms; /* summed duration of every timed GEMM launch of the step */
+  char probe_kernel[96];    /* that instantiation's name, e.g. "gemm_dl_kernel<2, 2, 4, 4, 2, 0>" */
 } mt_step_stats;
 
 typedef struct mt_model mt_model;

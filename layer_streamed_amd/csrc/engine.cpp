@@ -16,6 +16,7 @@
 // op that reads it has finished, and a load may run at most `depth` compute
 // ops ahead of its first use (depth 2 = double buffering).
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
@@ -23,7 +24,9 @@
 #include <chrono>
 #include <condition_variable>
 #include <deque>
+#include <map>
 #include <mutex>
+#include <string>
 #include <thread>
 #include <vector>
 
@@ -538,7 +541,13 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   for (auto& e : op_done) e = get_ev();
   for (auto& e : load_done) e = get_ev();
   if (M->run.time_kernels) {
-    probe.ev.resize(4 * (size_t)L + 8);
+    // every GEMM launch of the step: per layer forward (2 + 2 per MLP
+    // chunk, run up to twice: forward and segment re-forward) and
+    // recompute+backward (6 + 5 per MLP chunk), and 3 per head chunk
+    const size_t nmc = (d.D + d.mlp_chunk - 1) / d.mlp_chunk;
+    const size_t nhc = (d.D + d.head_chunk - 1) / d.head_chunk;
+    const size_t launches = (size_t)L * (2 * (2 + 2 * nmc) + 6 + 5 * nmc) + 3 * nhc + 8;
+    probe.ev.resize(2 * launches);
     for (auto& e : probe.ev) e = get_ev();
   }
   if (ev.err != MT_OK) return set_error(MT_E_HIP, "mt_stream_step: event creation failed");
@@ -596,7 +605,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       } else if (op.kind == OP_HEAD) {
         MT_STEP_RUN(head_impl(d, w + M->hl.final_norm * es, w + M->hl.lm_head * es, xloc(L), A.tgt,
                               inv_n, A.dy, A.head_grad + M->hl.final_norm * es,
-                              A.head_grad + M->hl.lm_head * es, A.loss, A.hws, A.hws_bytes, sC));
+                              A.head_grad + M->hl.lm_head * es, A.loss, A.hws, A.hws_bytes, sC,
+                              M->run.time_kernels ? &probe : nullptr));
         MT_STEP_HIP(hipMemcpyAsync(M->loss_host, A.loss, 4, hipMemcpyDeviceToHost, sC));
         MT_STEP_HIP(hipEventRecord(loss_ev, sC));
         {
@@ -628,7 +638,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           }
         }
         MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
-                                   A.lws, A.lws_bytes, sC));
+                                   A.lws, A.lws_bytes, sC, M->run.time_kernels ? &probe : nullptr));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
         Offload o{l, A.gring[r], M->ll.total, op_done[i], r};
         offq.push(o);
@@ -681,9 +691,29 @@ drain:
     s.d2h_ms = d2h_ms;
     for (auto& p : wait_ev_f) s.exposed_wait_fwd_ms += elapsed(p.first, p.second);
     for (auto& p : wait_ev_b) s.exposed_wait_bwd_ms += elapsed(p.first, p.second);
-    for (int i = 0; i + 1 < probe.used; i += 2) s.probe_kernel_ms += elapsed(probe.ev[i], probe.ev[i + 1]);
-    s.probe_kernel_launches = probe.used / 2;
-    s.probe_kernel_flops = probe.flops;
+    {
+      // group the timed GEMM launches by kernel instantiation; report the
+      // one with the largest total time
+      struct Agg { double ms = 0, flops = 0; int64_t n = 0; };
+      std::map<std::string, Agg> by;
+      for (int i = 0; i + 1 < probe.used; i += 2) {
+        const double ms = elapsed(probe.ev[i], probe.ev[i + 1]);
+        Agg& g = by[probe.name[i / 2]];
+        g.ms += ms;
+        g.flops += probe.flops[i / 2];
+        ++g.n;
+        s.probe_all_gemm_ms += ms;
+      }
+      const std::pair<const std::string, Agg>* top = nullptr;
+      for (auto& kv : by)
+        if (!top || kv.second.ms > top->second.ms) top = &kv;
+      if (top) {
+        s.probe_kernel_ms = top->second.ms;
+        s.probe_kernel_flops = top->second.flops;
+        s.probe_kernel_launches = top->second.n;
+        snprintf(s.probe_kernel, sizeof s.probe_kernel, "%s", top->first.c_str());
+      }
+    }
     s.h2d_bytes = h2d_bytes;
     s.d2h_bytes = d2h_bytes;
     s.pinned_host_bytes = M->pinned_bytes;

@@ -15,6 +15,10 @@
 // of the 8 XCDs (which the dispatcher feeds round-robin) owns a contiguous
 // range of tiles, then walked in groups of 8 tile-rows so that neighbouring
 // workgroups on one XCD share A rows and B columns in that XCD's L2.
+#include <stdio.h>
+
+#include <string>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -775,17 +779,33 @@ inline long tiles_of(const GemmArgs& a, int bm, int bn) {
   return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
+// The tile configurations, chosen from the arguments alone (launch and the
+// kernel-name query below share this choice).
+enum TileCfg { DL_256x256, DL_256x128, DL_128x128, RS_256x256, RS_128x128 };
+
+TileCfg choose_cfg(const GemmArgs& a) {
+  if (a.K % DL_BK == 0) {
+    if (tiles_of(a, 256, 256) >= 3 * 256) return DL_256x256;
+    if (tiles_of(a, 256, 128) >= 4 * 256) return DL_256x128;
+    return DL_128x128;
+  }
+  if (a.epi != EPI_SWIGLU_BWD && tiles_of(a, 256, 256) >= 4 * 256) return RS_256x256;
+  return RS_128x128;
+}
+
 template <int LAYOUT, int EPI>
 hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
-  if (a.K % DL_BK == 0) {
-    if (tiles_of(a, 256, 256) >= 3 * 256) return launch_dl<LAYOUT, 2, 4, 4, 2, EPI>(a, s);
-    if (tiles_of(a, 256, 128) >= 4 * 256) return launch_dl<LAYOUT, 4, 2, 2, 2, EPI>(a, s);
-    return launch_dl<LAYOUT, 2, 2, 2, 2, EPI>(a, s);
+  switch (choose_cfg(a)) {
+    case DL_256x256: return launch_dl<LAYOUT, 2, 4, 4, 2, EPI>(a, s);
+    case DL_256x128: return launch_dl<LAYOUT, 4, 2, 2, 2, EPI>(a, s);
+    case DL_128x128: return launch_dl<LAYOUT, 2, 2, 2, 2, EPI>(a, s);
+    case RS_256x256:
+      // the SwiGLU-backward epilogue would spill this tile's accumulators
+      if constexpr (EPI != EPI_SWIGLU_BWD) return launch_cfg<2, 4, 4, 2, LAYOUT, EPI>(a, s);
+      [[fallthrough]];
+    case RS_128x128: return launch_cfg<2, 2, 2, 2, LAYOUT, EPI>(a, s);
   }
-  if constexpr (EPI != EPI_SWIGLU_BWD) {
-    if (tiles_of(a, 256, 256) >= 4 * 256) return launch_cfg<2, 4, 4, 2, LAYOUT, EPI>(a, s);
-  }
-  return launch_cfg<2, 2, 2, 2, LAYOUT, EPI>(a, s);
+  return hipErrorInvalidValue;
 }
 
 template <int LAYOUT>
@@ -841,9 +861,23 @@ hipError_t gemm_launch(const GemmArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-const char* gemm_kernel_name(const GemmArgs& a) {
-  (void)a;
-  return "gemm_kernel";
+std::string gemm_kernel_name(const GemmArgs& a) {
+  // the demangled template name profilers report for the launch
+  const int lay = (a.epi == EPI_SWIGLU || a.epi == EPI_SWIGLU_SAVE) ? GEMM_NT : a.layout;
+  char buf[64];
+  switch (choose_cfg(a)) {
+    case DL_256x256: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 4, 4, 2, %d>", lay, a.epi); break;
+    case DL_256x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 4, 2, 2, 2, %d>", lay, a.epi); break;
+    case DL_128x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 2, 2, 2, %d>", lay, a.epi); break;
+    case RS_256x256:
+      if (a.epi != EPI_SWIGLU_BWD) {
+        snprintf(buf, sizeof buf, "gemm_kernel<2, 4, 4, 2, %d, %d>", lay, a.epi);
+        break;
+      }
+      [[fallthrough]];
+    case RS_128x128: snprintf(buf, sizeof buf, "gemm_kernel<2, 2, 2, 2, %d, %d>", lay, a.epi); break;
+  }
+  return buf;
 }
 
 }  // namespace mt

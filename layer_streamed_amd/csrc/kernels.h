@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace mt {
 
 // ---------------------------------------------------------------- GEMM
@@ -48,7 +50,9 @@ using GemmArgsF32 = GemmArgsT<float>;
 // Returns a message for unsupported arguments, or nullptr if OK.
 const char* gemm_check(const GemmArgs& a);
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t s);
-const char* gemm_kernel_name(const GemmArgs& a);
+// Name of the kernel instantiation a launch with these arguments runs (as
+// profilers report it, without namespace and parameter list).
+std::string gemm_kernel_name(const GemmArgs& a);
 const char* gemm_check(const GemmArgsF32& a);
 hipError_t gemm_launch(const GemmArgsF32& a, hipStream_t s);
 

@@ -22,6 +22,7 @@
 #include "layer.h"
 
 #include <algorithm>
+#include <string>
 
 #include "kernels.h"
 #include "status.h"
@@ -156,8 +157,14 @@ GemmArgsT<E> gemm(int layout, int epi, int M, int N, int K, const E* A, long lda
   return g;
 }
 
+inline std::string kernel_name(const GemmArgsT<uint16_t>& g) { return gemm_kernel_name(g); }
+inline std::string kernel_name(const GemmArgsT<float>& g) {
+  const int lay = (g.epi == EPI_SWIGLU || g.epi == EPI_SWIGLU_SAVE) ? GEMM_NT : g.layout;
+  return "gemm_f32_kernel<" + std::to_string(lay) + ", " + std::to_string(g.epi) + ">";
+}
+
 template <class E>
-mt_status run_gemm(const GemmArgsT<E>& g, hipStream_t s, Probe* probe = nullptr) {
+mt_status run_gemm(const GemmArgsT<E>& g, hipStream_t s, Probe* probe) {
   if (const char* m = gemm_check(g)) return set_error(MT_E_SHAPE, "layer GEMM: %s", m);
   const bool timed = probe && probe->used + 2 <= (int)probe->ev.size();
   if (timed) MT_HIP(hipEventRecord(probe->ev[probe->used], s));
@@ -165,7 +172,8 @@ mt_status run_gemm(const GemmArgsT<E>& g, hipStream_t s, Probe* probe = nullptr)
   if (timed) {
     MT_HIP(hipEventRecord(probe->ev[probe->used + 1], s));
     probe->used += 2;
-    probe->flops += 2.0 * g.M * (double)g.N * g.K;
+    probe->name.push_back(kernel_name(g));
+    probe->flops.push_back(2.0 * g.M * (double)g.N * g.K);
   }
   return MT_OK;
 }
@@ -189,19 +197,19 @@ struct LayerW {
 // Attention half of the block, shared by forward and recompute.
 template <class E>
 mt_status attn_half(const Dims& d, const LayerW<E>& w, const E* x, const LayerWs<E>& ws,
-                    hipStream_t s) {
+                    hipStream_t s, Probe* probe) {
   MT_HIP(rope_table(ws.cos_t, ws.sin_t, d.T, d.d, d.theta, s));
   MT_HIP(rmsnorm_fwd(x, w.g1, ws.a, ws.rstd1, d.D, d.H, d.eps, s));
   MT_RUN(run_gemm(gemm<E>(GEMM_NT, EPI_BF16, d.D, d.NQKV, d.H, ws.a, d.H, w.wqkv, d.H, ws.qkv,
                           d.NQKV),
-                  s));
+                  s, probe));
   MT_HIP(rope_apply(ws.qkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 0, s));
   MT_HIP(attn_fwd(ws.qkv, ws.o, ws.lse, d.B, d.T, d.Hq, d.Hkv, d.d, s));
   GemmArgsT<E> go = gemm<E>(GEMM_NT, EPI_RESID_BF16, d.D, d.H, d.Qd, ws.o, d.Qd, w.wo, d.Qd,
                             ws.x_mid, d.H);
   go.R = x;
   go.ldr = d.H;
-  MT_RUN(run_gemm(go, s));
+  MT_RUN(run_gemm(go, s, probe));
   MT_HIP(rmsnorm_fwd(ws.x_mid, w.g2, ws.b, ws.rstd2, d.D, d.H, d.eps, s));
   return MT_OK;
 }
@@ -214,7 +222,7 @@ mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* 
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE, "layer forward: workspace %zu < %zu bytes",
            ws_bytes, need);
   const LayerW<E> w(wv);
-  MT_RUN(attn_half(d, w, x_in, ws, s));
+  MT_RUN(attn_half(d, w, x_in, ws, s, probe));
   for (int r0 = 0; r0 < d.D; r0 += d.mlp_chunk) {
     const int rows = std::min(d.mlp_chunk, d.D - r0);
     GemmArgsT<E> gu = gemm<E>(GEMM_NT, EPI_SWIGLU, rows, 2 * d.F, d.H, ws.b + (size_t)r0 * d.H,
@@ -225,21 +233,22 @@ mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* 
                               x_out + (size_t)r0 * d.H, d.H);
     dn.R = ws.x_mid + (size_t)r0 * d.H;
     dn.ldr = d.H;
-    MT_RUN(run_gemm(dn, s));
+    MT_RUN(run_gemm(dn, s, probe));
   }
   return MT_OK;
 }
 
 template <class E>
 mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, const E* dy, E* dx,
-                      const mt_layer_grad_view& g, void* wsp, size_t ws_bytes, hipStream_t s) {
+                      const mt_layer_grad_view& g, void* wsp, size_t ws_bytes, hipStream_t s,
+                      Probe* probe) {
   size_t need = 0;
   LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), 1, &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE,
            "layer recompute/backward: workspace %zu < %zu bytes", ws_bytes, need);
   const LayerW<E> w(wv);
   // ---- recompute the attention half (rebuilds a, qkv (rotated), o, lse, x_mid, b)
-  MT_RUN(attn_half(d, w, x_in, ws, s));
+  MT_RUN(attn_half(d, w, x_in, ws, s, probe));
   const bool chunked = d.mlp_chunk < d.D;
   E* gd = static_cast<E*>(g.w_down);
   E* ggu = static_cast<E*>(g.w_gate_up);
@@ -257,7 +266,7 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
     gu.F = d.F;
     gu.C2 = ws.gu;
     gu.ldc2 = 2 * d.F;
-    MT_RUN(run_gemm(gu, s));
+    MT_RUN(run_gemm(gu, s, probe));
     // dgate, dup from dm = dy W_down (NN) fused with the SwiGLU derivative
     GemmArgsT<E> dm = gemm<E>(GEMM_NN, EPI_SWIGLU_BWD, rows, d.F, d.H, dy_c, d.H, w.wd, d.F,
                               ws.dgu, 2 * d.F);
@@ -266,22 +275,22 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
     dm.ldg = 2 * d.F;
     dm.C2 = ws.dgu;
     dm.ldc2 = 2 * d.F;
-    MT_RUN(run_gemm(dm, s));
+    MT_RUN(run_gemm(dm, s, probe));
     // dW_down = dy^T m  (TN: A = dy as [K=rows, M=H], B = m [rows, F])
     MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.H, d.F, rows, dy_c, d.H,
                             ws.m, d.F,
                             chunked ? static_cast<void*>(ws.acc_d) : static_cast<void*>(gd), d.F),
-                    s));
+                    s, probe));
     // dW_gu = dgu^T b  (TN: A = dgu [rows, 2F], B = b [rows, H])
     MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, 2 * d.F, d.H, rows, ws.dgu,
                             2 * d.F, b_c, d.H,
                             chunked ? static_cast<void*>(ws.acc_gu) : static_cast<void*>(ggu),
                             d.H),
-                    s));
+                    s, probe));
     // db = dgu W_gu  (NN: B = W_gu [2F, H])
     MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, rows, d.H, 2 * d.F, ws.dgu, 2 * d.F, w.wgu, d.H,
                             ws.db + (size_t)r0 * d.H, d.H),
-                    s));
+                    s, probe));
   }
   if (chunked) {
     MT_HIP(cast_f32(ws.acc_d, gd, (size_t)d.H * d.F, s));
@@ -294,20 +303,20 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
   // ---- output projection
   MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, d.D, d.Qd, d.H, ws.dx_mid, d.H, w.wo, d.Qd, ws.dout,
                           d.Qd),
-                  s));
+                  s, probe));
   MT_RUN(run_gemm(gemm<E>(GEMM_TN, EPI_BF16, d.H, d.Qd, d.D, ws.dx_mid, d.H, ws.o, d.Qd, g.w_o,
                           d.Qd),
-                  s));
+                  s, probe));
   // ---- attention and RoPE
   MT_HIP(attn_bwd(ws.qkv, ws.o, ws.lse, ws.dout, ws.delta, ws.dqkv, d.B, d.T, d.Hq, d.Hkv, d.d, s));
   MT_HIP(rope_apply(ws.dqkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 1, s));
   // ---- QKV projection
   MT_RUN(run_gemm(gemm<E>(GEMM_TN, EPI_BF16, d.NQKV, d.H, d.D, ws.dqkv, d.NQKV, ws.a, d.H,
                           g.w_qkv, d.H),
-                  s));
+                  s, probe));
   MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, d.D, d.H, d.NQKV, ws.dqkv, d.NQKV, w.wqkv, d.H, ws.da,
                           d.H),
-                  s));
+                  s, probe));
   // ---- first norm (residual dx_mid)
   MT_HIP(rmsnorm_bwd(ws.da, x_in, w.g1, ws.rstd1, ws.dx_mid, dx, ws.dg_part, d.D, d.H, s));
   MT_HIP(reduce_rows(ws.dg_part, nblk, d.H, static_cast<E*>(g.attn_norm), s));
@@ -334,12 +343,12 @@ mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in
 
 mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in, const void* dy,
                          void* dx, const mt_layer_grad_view& g, void* ws, size_t ws_bytes,
-                         hipStream_t s) {
+                         hipStream_t s, Probe* probe) {
   if (d.prec == MT_PREC_FP32_DEBUG)
     return layer_bwd_t(d, w, static_cast<const float*>(x_in), static_cast<const float*>(dy),
-                       static_cast<float*>(dx), g, ws, ws_bytes, s);
+                       static_cast<float*>(dx), g, ws, ws_bytes, s, probe);
   return layer_bwd_t(d, w, static_cast<const uint16_t*>(x_in), static_cast<const uint16_t*>(dy),
-                     static_cast<uint16_t*>(dx), g, ws, ws_bytes, s);
+                     static_cast<uint16_t*>(dx), g, ws, ws_bytes, s, probe);
 }
 
 // ------------------------------------------------------------------- head
@@ -370,7 +379,7 @@ HeadWs<E> carve_head(const Dims& d, char* base, size_t* bytes) {
 template <class E>
 mt_status head_t(const Dims& d, const E* g_f, const E* w_out, const E* x_L,
                  const int32_t* targets, float inv_n, E* dx_L, E* dg_f, E* dw_out, float* loss_dev,
-                 void* wsp, size_t ws_bytes, hipStream_t s) {
+                 void* wsp, size_t ws_bytes, hipStream_t s, Probe* probe) {
   size_t need = 0;
   HeadWs<E> ws = carve_head<E>(d, static_cast<char*>(wsp), &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE, "head: workspace %zu < %zu bytes", ws_bytes,
@@ -383,16 +392,16 @@ mt_status head_t(const Dims& d, const E* g_f, const E* w_out, const E* x_L,
     const E* h_c = ws.h + (size_t)r0 * d.H;
     MT_RUN(run_gemm(gemm<E>(GEMM_NT, EPI_F32, rows, d.V, d.H, h_c, d.H, w_out, d.H, ws.logits,
                             d.V),
-                    s));
+                    s, probe));
     MT_HIP(ce_rows(ws.logits, targets + r0, ws.dlogits, ws.loss_part + r0, rows, d.V, inv_n, s));
     MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, rows, d.H, d.V, ws.dlogits, d.V, w_out, d.H,
                             ws.dh + (size_t)r0 * d.H, d.H),
-                    s));
+                    s, probe));
     MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.V, d.H, rows, ws.dlogits,
                             d.V, h_c, d.H,
                             chunked ? static_cast<void*>(ws.acc_out) : static_cast<void*>(dw_out),
                             d.H),
-                    s));
+                    s, probe));
   }
   if (chunked) MT_HIP(cast_f32(ws.acc_out, dw_out, (size_t)d.V * d.H, s));
   MT_HIP(sum_loss(ws.loss_part, d.D, inv_n, loss_dev, s));
@@ -412,15 +421,16 @@ size_t head_ws_bytes(const Dims& d) {
 
 mt_status head_impl(const Dims& d, const void* g_f, const void* w_out, const void* x_L,
                     const int32_t* targets, float inv_n, void* dx_L, void* dg_f, void* dw_out,
-                    float* loss_dev, void* ws, size_t ws_bytes, hipStream_t s) {
+                    float* loss_dev, void* ws, size_t ws_bytes, hipStream_t s, Probe* probe) {
   if (d.prec == MT_PREC_FP32_DEBUG)
     return head_t(d, static_cast<const float*>(g_f), static_cast<const float*>(w_out),
                   static_cast<const float*>(x_L), targets, inv_n, static_cast<float*>(dx_L),
-                  static_cast<float*>(dg_f), static_cast<float*>(dw_out), loss_dev, ws, ws_bytes, s);
+                  static_cast<float*>(dg_f), static_cast<float*>(dw_out), loss_dev, ws, ws_bytes, s,
+                  probe);
   return head_t(d, static_cast<const uint16_t*>(g_f), static_cast<const uint16_t*>(w_out),
                 static_cast<const uint16_t*>(x_L), targets, inv_n, static_cast<uint16_t*>(dx_L),
                 static_cast<uint16_t*>(dg_f), static_cast<uint16_t*>(dw_out), loss_dev, ws,
-                ws_bytes, s);
+                ws_bytes, s, probe);
 }
 
 }  // namespace mt
@@ -469,7 +479,7 @@ mt_status mt_layer_recompute_bwd(const mt_model_cfg* cfg, const mt_run_cfg* run,
                dw->w_down,
            MT_E_INVALID, "mt_layer_recompute_bwd: null gradient pointer");
   return layer_bwd_impl(d, *w, x_in, dy, dx, *dw, workspace, workspace_bytes,
-                        static_cast<hipStream_t>(stream));
+                        static_cast<hipStream_t>(stream), nullptr);
 }
 
 }  // extern "C"

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
 #include <vector>
 
 #include "mt.h"
@@ -27,12 +28,13 @@ struct Dims {
 const char* make_dims(const mt_model_cfg* cfg, const mt_run_cfg* run, int batch, int seq,
                       Dims* out);
 
-// Optional timing of one GEMM class (the gate/up projection with its SwiGLU
-// epilogue, the largest product of the layer) with event pairs.
+// Optional timing of GEMM launches with event pairs, each tagged with the
+// kernel instantiation it ran and its algorithmic FLOPs.
 struct Probe {
   std::vector<hipEvent_t> ev;  // pairs
-  int used = 0;
-  double flops = 0;
+  std::vector<std::string> name;
+  std::vector<double> flops;
+  int used = 0;  // events used (2 per launch)
 };
 
 // Bump allocator over a caller-provided device workspace; with base ==
@@ -56,7 +58,7 @@ mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in
                          void* ws, size_t ws_bytes, hipStream_t s, Probe* probe);
 mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in, const void* dy,
                          void* dx, const mt_layer_grad_view& g, void* ws, size_t ws_bytes,
-                         hipStream_t s);
+                         hipStream_t s, Probe* probe);
 
 // LM head: h = rms(x_L) g_f; logits = h W_out^T per token chunk; next-token
 // cross-entropy; dh, dW_out, dg_f; dx_L = rmsnorm backward.  targets: device
@@ -64,7 +66,7 @@ mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in
 size_t head_ws_bytes(const Dims& d);
 mt_status head_impl(const Dims& d, const void* g_f, const void* w_out, const void* x_L,
                     const int32_t* targets, float inv_n, void* dx_L, void* dg_f, void* dw_out,
-                    float* loss_dev, void* ws, size_t ws_bytes, hipStream_t s);
+                    float* loss_dev, void* ws, size_t ws_bytes, hipStream_t s, Probe* probe);
 
 // Element offsets of the tensors inside one layer's flat unit (streamed
 // copy, gradient slab and fp32 store share them), each aligned to 128

@@ -67,10 +67,13 @@ class StepStats(C.Structure):
         "probe_kernel_ms", "probe_kernel_flops")] + [(n, C.c_int64) for n in (
             "probe_kernel_launches", "pinned_host_bytes", "pageable_host_bytes",
             "device_arena_bytes", "units_updated")] + [(n, C.c_double) for n in (
-                "host_ring_wait_ms", "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms")]
+                "host_ring_wait_ms", "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms",
+                "probe_all_gemm_ms")] + [("probe_kernel", C.c_char * 96)]
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_}
+        d = {n: getattr(self, n) for n, _ in self._fields_}
+        d["probe_kernel"] = self.probe_kernel.decode()
+        return d
 
 
 # ---------------------------------------------------------------- signatures

@@ -1,0 +1,137 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+  stats    kernel statistics of a --kernel-trace --stats run (top kernels by
+           total time)
+  traffic  HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE,
+           then WRITE_SIZE), each calibrated by what the same counter reads
+           for the plain 1 GiB device copy that `bench.py --pmc-copy` runs
+           (the copy reads 1 GiB and writes 1 GiB per launch)
+
+Usage:
+  python -m layer_streamed_amd.prof_summary stats STATS_CSV OUT_MD --title T --command C
+  python -m layer_streamed_amd.prof_summary traffic FETCH_CSV WRITE_CSV OUT_MD \\
+      --kernel NAME --flops-per-launch F --command-fetch C1 --command-write C2
+"""
+import argparse
+import csv
+import hashlib
+import os
+import re
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_BYTES = 1 << 30
+
+
+def short(name):
+    name = re.sub(r"^void ", "", name)
+    name = name.replace("mt::(anonymous namespace)::", "")
+    return re.sub(r"\(.*$", "", name)
+
+
+def gemm_sources_sha256():
+    src = os.path.join(ROOT, "layer_streamed_amd", "csrc")
+    return hashlib.sha256(open(os.path.join(src, "gemm.hip"), "rb").read()
+                          + open(os.path.join(src, "common.h"), "rb").read()).hexdigest()
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = [f"# {args.title}", "", "Command (from the repository root):", "",
+           f"    {args.command}", "", f"Top kernels by total time ({total / 1e6:.1f} ms of "
+           "kernel time in the run):", "",
+           "| kernel | calls | avg (us) | total (ms) | % |", "|---|---|---|---|---|"]
+    for r in rows[: args.top]:
+        out.append(f"| {short(r['Name'])[:72]} | {r['Calls']} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.1f} | "
+                   f"{100 * float(r['TotalDurationNs']) / total:.2f} |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
+def _per_dispatch(path, counter):
+    """(short kernel name, dispatch id) -> counter value summed over dimensions."""
+    agg = defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        agg[(short(r["Kernel_Name"]), int(r["Dispatch_Id"]))] += float(r["Counter_Value"])
+    return agg
+
+
+def traffic(args):
+    fetch = _per_dispatch(args.fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(args.write_csv, "WRITE_SIZE")
+
+    def pick(agg, pred):
+        return [v for (n, _), v in sorted(agg.items(), key=lambda kv: kv[0][1]) if pred(n)]
+
+    is_copy = lambda n: "copyBuffer" in n  # noqa: E731
+    is_k = lambda n: n == args.kernel  # noqa: E731
+    kf, kw = pick(fetch, is_k), pick(write, is_k)
+    # the calibration copies are the 1 GiB ones: far larger than any other
+    # device copy of the run (weight initialisation makes many small ones)
+    cf, cw = pick(fetch, is_copy), pick(write, is_copy)
+    cf = [v for v in cf if v > 0.5 * max(cf)]
+    cw = [v for v in cw if v > 0.5 * max(cw)]
+    assert kf and kw, f"no dispatch of {args.kernel} in the counter files"
+    assert cf and cw, "no calibration copy (bench.py --pmc-copy) in the counter files"
+    # counters are in KiB; the copy moves COPY_BYTES each way
+    f_scale = COPY_BYTES / (sum(cf) / len(cf) * 1024)
+    w_scale = COPY_BYTES / (sum(cw) / len(cw) * 1024)
+    fb = sum(kf) / len(kf) * 1024 * f_scale
+    wb = sum(kw) / len(kw) * 1024 * w_scale
+    out = [f"# HBM traffic of {args.kernel} ({args.workload})", "",
+           f"kernel: {args.kernel}", "",
+           "Commands (two passes, one counter each, from the repository root):", "",
+           f"    {args.command_fetch}", f"    {args.command_write}", "",
+           f"Dispatches of the kernel: {len(kf)} (FETCH_SIZE pass), {len(kw)} (WRITE_SIZE pass); "
+           f"calibration copies: {len(cf)} / {len(cw)}.", "",
+           "| | FETCH_SIZE (KiB, mean) | WRITE_SIZE (KiB, mean) |", "|---|---|---|",
+           f"| kernel | {sum(kf) / len(kf):.1f} | {sum(kw) / len(kw):.1f} |",
+           f"| copy 1 GiB | {sum(cf) / len(cf):.1f} | {sum(cw) / len(cw):.1f} |", "",
+           f"Calibration (the copy reads and writes 1 GiB per launch): FETCH_SIZE scale "
+           f"{f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f} (bytes = KiB x 1024 x scale).", "",
+           "Per launch (mean over the kernel's dispatches):",
+           f"- fetched from HBM: {fb / 1e9:.3f} GB",
+           f"- written to HBM: {wb / 1e9:.3f} GB",
+           f"- traffic_bytes_per_launch: {int(fb + wb)}"]
+    if args.flops_per_launch:
+        out.append(f"- algorithmic FLOPs per launch: {args.flops_per_launch:.4g} "
+                   f"(arithmetic intensity {args.flops_per_launch / (fb + wb):.0f} FLOP/byte "
+                   f"of measured traffic)")
+    if args.note:
+        out += ["", args.note]
+    out += ["", f"source_sha256: {gemm_sources_sha256()}",
+            "(sha256 of gemm.hip followed by common.h when the counters were taken; the "
+            "benchmark reports this traffic only while the sources still hash to it and the "
+            "kernel is still the dominant one.)"]
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("out")
+    a.add_argument("--title", required=True)
+    a.add_argument("--command", required=True)
+    a.add_argument("--top", type=int, default=24)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("out")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--workload", default="Qwen2.5-7B shape, B 16 x T 1024")
+    b.add_argument("--flops-per-launch", type=float, default=0.0)
+    b.add_argument("--command-fetch", required=True)
+    b.add_argument("--command-write", required=True)
+    b.add_argument("--note", default="")
+    args = ap.parse_args()
+    stats(args) if args.cmd == "stats" else traffic(args)
+
+
+if __name__ == "__main__":
+    main()
