@@ -79,9 +79,10 @@ def init_weights(model, shape, seed):
 
 def cpu_baseline(shape):
     """The oracle on a bounded sample of the same workload: one decoder layer
-    at the real width on one sequence (forward, the re-forward share,
-    recompute and backward), the head on the same sequence, and Adam over
-    one layer's parameters; extrapolated to the full step."""
+    at the real width on a few sequences (forward, the re-forward share,
+    recompute and backward), the head on the same sequences, and Adam over
+    one layer's parameters (about 10-15 s of CPU work); extrapolated to the
+    full step."""
     import numpy as np
 
     import synth
@@ -92,12 +93,13 @@ def cpu_baseline(shape):
     except Exception:
         cores = os.cpu_count()
     T = min(shape.seq, 1024)
-    s1 = shape.with_(batch=1, seq=T)
+    nb = max(1, min(4, shape.batch * shape.seq // T))  # sequences in the sample
+    s1 = shape.with_(batch=nb, seq=T)
     w = synth.make_weights(s1, seed=0, names=synth.layer_param_names(0))
     w = {k.split(".")[-1]: v for k, v in w.items()}
     rng = np.random.default_rng(0)
-    x = rng.standard_normal((1, T, shape.hidden)).astype(np.float32)
-    dy = (rng.standard_normal((1, T, shape.hidden)) * 1e-3).astype(np.float32)
+    x = rng.standard_normal((nb, T, shape.hidden)).astype(np.float32)
+    dy = (rng.standard_normal((nb, T, shape.hidden)) * 1e-3).astype(np.float32)
     cos, sin = D.rope_cos_sin(T, shape.head_dim, shape.rope_theta, np.float32)
     K, L = shape.ckpt_interval, shape.n_layers
     t0 = time.perf_counter()
@@ -111,7 +113,7 @@ def cpu_baseline(shape):
     # head on the same sequence: final norm, logits, CE fwd/bwd
     Vh = shape.vocab
     wout = (rng.standard_normal((Vh, shape.hidden)) * 0.02).astype(np.float32)
-    ids = rng.integers(0, Vh, (1, T)).astype(np.int32)
+    ids = rng.integers(0, Vh, (nb, T)).astype(np.int32)
     t0 = time.perf_counter()
     D.head_forward_backward(y, np.ones(shape.hidden, np.float32), wout, ids, shape.rms_eps)
     t_head = time.perf_counter() - t0
@@ -123,10 +125,10 @@ def cpu_baseline(shape):
     D.adam_update(p, z, z.copy(), p * 1e-3, 1, shape.lr, shape.beta1, shape.beta2, shape.adam_eps)
     t_adam_layer = time.perf_counter() - t0
     n_total = sum(int(np.prod(v)) for v in synth.param_shapes(shape).values())
-    seqs = shape.batch * (shape.seq // T)
-    step_s = seqs * (L * per_layer + t_head) + t_adam_layer * n_total / n
+    reps = shape.batch * (shape.seq // T) / nb  # samples of nb sequences per step
+    step_s = reps * (L * per_layer + t_head) + t_adam_layer * n_total / n
     sample_s = t_fwd + t_rb + t_head + t_adam_layer
-    return step_s, cores, sample_s, T
+    return step_s, cores, sample_s, T, nb
 
 
 def main():
@@ -233,7 +235,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        cpu_step_s, cores, sample_s, T_s = cpu_baseline(shape)
+        cpu_step_s, cores, sample_s, T_s, nb_s = cpu_baseline(shape)
         log(f"cpu baseline: {cpu_step_s:.0f} s/step extrapolated from a {sample_s:.1f} s sample "
             f"({time.perf_counter() - t0:.1f} s with weight draws)")
         cpu = {
@@ -242,10 +244,11 @@ def main():
             "tokens_per_s": round(D / cpu_step_s, 3),
             "cores": int(cores),
             "kind": "oracle",
-            "sample": (f"one decoder layer at the full width on 1 x {T_s} tokens (forward, "
-                       f"re-forward share, recompute, backward) + head on the same tokens + "
-                       f"Adam over one layer; extrapolated x{shape.n_layers} layers x "
-                       f"{shape.batch * (shape.seq // T_s)} sequences"),
+            "sample": (f"one decoder layer at the full width on {nb_s} x {T_s} tokens "
+                       f"(forward, re-forward share, recompute, backward) + head on the same "
+                       f"tokens + Adam over one layer ({sample_s:.1f} s of CPU work); "
+                       f"extrapolated x{shape.n_layers} layers x "
+                       f"{shape.batch * (shape.seq // T_s) / nb_s:g} samples"),
         }
 
     line = {
