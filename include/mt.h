@@ -81,7 +81,14 @@ typedef struct {
   int32_t serialize;         /* 1: run W, C and G work on one stream (for invariance tests) */
   int32_t host_alloc;        /* MT_HOST_PINNED (default) | MT_HOST_PAGEABLE (no GPU needed) */
   int32_t keep_grads;        /* 1: keep each step's gradients on the host for mt_model_get_param */
-  int32_t time_kernels;      /* 1: bracket the dominant GEMM with HIP events (stats) */
+  int32_t time_kernels;      /* 1: time every GEMM launch with HIP events (stats) */
+  int32_t keep_internals;    /* 1 (default): each backward segment's re-forward runs every
+                                layer of the segment with mt_layer_fwd_keep and the
+                                backward uses mt_layer_bwd_saved (K layers of internals
+                                on the device, no second forward per layer); 0: the
+                                re-forward covers the first K-1 layers and every layer's
+                                backward recomputes (mt_layer_recompute_bwd).  Needs
+                                mlp_chunk_tokens = 0, else treated as 0. */
   double lr, beta1, beta2, eps, weight_decay; /* Adam (weight_decay must be 0) */
 } mt_run_cfg;
 
@@ -132,7 +139,8 @@ const char* mt_last_error(void);
  * at least mt_layer_workspace_bytes(...) bytes (256-B aligned).
  * ------------------------------------------------------------------- */
 
-/* which: 0 = forward, 1 = recompute + backward. */
+/* which: 0 = forward, 1 = recompute + backward, 2 = backward from kept
+ * internals (mt_layer_bwd_saved).  Returns 0 for an invalid shape. */
 size_t mt_layer_workspace_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run,
                                 int32_t batch, int32_t seq, int32_t which);
 
@@ -153,6 +161,35 @@ mt_status mt_layer_recompute_bwd(const mt_model_cfg* cfg, const mt_run_cfg* run,
                                  const mt_layer_grad_view* dw, int32_t batch,
                                  int32_t seq, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* The recompute of the backward split off (blog summary, section 3: layer
+ * inputs are rebuilt from checkpoints; here a layer forward run while
+ * rebuilding them keeps everything its backward needs, so the backward
+ * computes no forward of its own).  mt_layer_fwd_keep is mt_layer_fwd that
+ * also leaves the layer's internals (normed inputs, rotated q/k and v,
+ * attention output and log-sum-exp, mid residual, gate/up pre-activations,
+ * SwiGLU output, RMS factors) in `internals`, a caller-owned device buffer
+ * of mt_layer_internals_bytes(...) bytes (256-B aligned) that must stay
+ * untouched until mt_layer_bwd_saved has consumed it.  mt_layer_bwd_saved
+ * is mt_layer_recompute_bwd without the recompute: same inputs, outputs
+ * and aliasing rules, plus the internals of a mt_layer_fwd_keep of the same
+ * weights and x_in; its workspace is mt_layer_workspace_bytes(..., 2).
+ * The results are bitwise equal to mt_layer_recompute_bwd's (same kernels
+ * on the same inputs).  Both need mlp_chunk_tokens = 0 (the chunked MLP
+ * exists to avoid holding the full gate/up activations): MT_E_SHAPE
+ * otherwise, and mt_layer_internals_bytes returns 0. */
+size_t mt_layer_internals_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                                int32_t batch, int32_t seq);
+mt_status mt_layer_fwd_keep(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                            const mt_layer_view* w, const void* x_in, void* x_out,
+                            int32_t batch, int32_t seq, void* internals,
+                            size_t internals_bytes, void* stream);
+mt_status mt_layer_bwd_saved(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                             const mt_layer_view* w, const void* x_in,
+                             const void* dy, void* dx, const mt_layer_grad_view* dw,
+                             int32_t batch, int32_t seq, void* internals,
+                             size_t internals_bytes, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
  * Host-resident model: the authoritative flat store (blog summary,

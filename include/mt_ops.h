@@ -107,8 +107,8 @@ mt_status mt_op_ce_rows(const float* logits, const int32_t* target, void* dlogit
 mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t blocks,
                          void* stream);
 
-/* The stream schedule of mt_stream_step for n_layers, checkpoint interval
- * and prefetch depth, as plain integers so its hazards can be checked
+/* The stream schedule of mt_stream_step for n_layers, checkpoint interval,
+ * prefetch depth and kept internals (mt_run_cfg.keep_internals), as plain integers so its hazards can be checked
  * without a GPU.  out receives, per compute op, (kind, layer, load) with
  * kind 0 forward, 1 head, 2 segment re-forward, 3 recompute+backward; then,
  * per weight load, (unit, slot, first_use, last_use, wait_use, gate_use):
@@ -117,7 +117,7 @@ mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t 
  * n_slots}.  MT_E_SHAPE if the schedule would deadlock, MT_E_OOM_HOST if
  * cap (entries) is too small. */
 mt_status mt_debug_plan(int32_t n_layers, int32_t ckpt_interval, int32_t prefetch_depth,
-                        int32_t* out, size_t cap, int32_t* counts);
+                        int32_t keep_internals, int32_t* out, size_t cap, int32_t* counts);
 
 #ifdef __cplusplus
 }

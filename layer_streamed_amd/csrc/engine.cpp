@@ -10,9 +10,11 @@
 //
 // Compute order: forward of every layer (keeping the input of layers
 // l = 0 mod K), the head (final norm, LM head, loss, its backward), then
-// the segments from the last: re-forward the segment's first K-1 layers
-// from its checkpoint to rebuild their inputs, then recompute+backward each
-// layer in reverse.  A weight slot is reused only after the last compute
+// the segments from the last: re-forward the segment's layers from its
+// checkpoint to rebuild their inputs, then backward each layer in reverse.
+// With kept internals the re-forward runs all K layers of the segment and
+// keeps what their backward needs (no second forward per layer); without,
+// it runs the first K-1 and each backward recomputes its layer's forward.  A weight slot is reused only after the last compute
 // op that reads it has finished, and a load may run at most `depth` compute
 // ops ahead of its first use (depth 2 = double buffering).
 #include <math.h>
@@ -53,7 +55,7 @@ struct Plan {
 
 static int plan_slots(int K, int depth) { return std::max(2, K + depth); }
 
-Plan build_plan(int L, int K, int depth, int n_slots) {
+Plan build_plan(int L, int K, int depth, int n_slots, bool keep) {
   Plan p;
   p.n_slots = n_slots;
   auto add_load = [&](int unit) {
@@ -73,7 +75,7 @@ Plan build_plan(int L, int K, int depth, int n_slots) {
     const int e = std::min(a + K, L);
     std::vector<int> ld(e - a);
     for (int l = a; l < e; ++l) ld[l - a] = add_load(l);
-    for (int l = a; l < e - 1; ++l) add_op(OP_REFWD, l, ld[l - a]);
+    for (int l = a; l < (keep ? e : e - 1); ++l) add_op(OP_REFWD, l, ld[l - a]);
     for (int l = e - 1; l >= a; --l) add_op(OP_BWD, l, ld[l - a]);
   }
   std::vector<int> free_after(n_slots, -1);
@@ -108,6 +110,8 @@ struct Arena {
   char* head_grad = nullptr;
   char* act[2] = {};
   std::vector<char*> ckpt, seg;
+  std::vector<char*> keep;  // kept internals, one per layer of a segment
+  size_t keep_bytes = 0;
   char* dy = nullptr;
   int32_t* tgt = nullptr;
   float* loss = nullptr;
@@ -116,6 +120,11 @@ struct Arena {
   void* hws = nullptr;
   size_t hws_bytes = 0;
 };
+
+// Whether the step keeps the re-forward's internals for the backward.
+bool keep_mode(const mt_model* M, const Dims& d) {
+  return M->run.keep_internals != 0 && d.mlp_chunk == d.D;
+}
 
 Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
   Carve c{base};
@@ -131,7 +140,12 @@ Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
   a.act[0] = c.take<char>(act);
   a.act[1] = c.take<char>(act);
   for (int i = 0; i <= L / K; ++i) a.ckpt.push_back(c.take<char>(act));
-  for (int i = 0; i < K - 1; ++i) a.seg.push_back(c.take<char>(act));
+  const bool keep = keep_mode(M, d);
+  for (int i = 0; i < (keep ? K : K - 1); ++i) a.seg.push_back(c.take<char>(act));
+  if (keep) {
+    a.keep_bytes = layer_ws_bytes(d, 2);
+    for (int i = 0; i < K; ++i) a.keep.push_back(c.take<char>(a.keep_bytes));
+  }
   a.dy = c.take<char>(act);
   a.tgt = c.take<int32_t>(d.D);
   a.loss = c.take<float>(64);
@@ -276,11 +290,11 @@ size_t mt_stream_arena_bytes(const mt_model* model, int32_t batch, int32_t seq) 
 // counts[0..2] = n_ops, n_loads, n_slots.  Returns MT_E_SHAPE if the plan is
 // invalid, MT_E_OOM_HOST if out is too small.
 mt_status mt_debug_plan(int32_t n_layers, int32_t ckpt_interval, int32_t prefetch_depth,
-                        int32_t* out, size_t cap, int32_t* counts) {
+                        int32_t keep_internals, int32_t* out, size_t cap, int32_t* counts) {
   MT_CHECK(n_layers >= 1 && ckpt_interval >= 1 && prefetch_depth >= 1 && out && counts,
            MT_E_INVALID, "mt_debug_plan: bad arguments");
   Plan p = build_plan(n_layers, ckpt_interval, prefetch_depth,
-                      plan_slots(ckpt_interval, prefetch_depth));
+                      plan_slots(ckpt_interval, prefetch_depth), keep_internals != 0);
   counts[0] = (int32_t)p.ops.size();
   counts[1] = (int32_t)p.loads.size();
   counts[2] = p.n_slots;
@@ -328,7 +342,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   MT_CHECK(arena_bytes >= need, MT_E_OOM_DEVICE, "mt_stream_step: arena %zu < %zu bytes",
            arena_bytes, need);
   MT_CHECK(((uintptr_t)arena & 255) == 0, MT_E_INVALID, "mt_stream_step: arena must be 256-byte aligned");
-  Plan plan = build_plan(L, K, M->run.prefetch_depth, plan_slots(K, M->run.prefetch_depth));
+  const bool keep = keep_mode(M, d);
+  Plan plan = build_plan(L, K, M->run.prefetch_depth, plan_slots(K, M->run.prefetch_depth), keep);
   MT_CHECK(!plan.error, MT_E_INVALID, "mt_stream_step: %s", plan.error);
 
   if (!M->sdma) {
@@ -621,8 +636,13 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       } else if (op.kind == OP_REFWD) {
         const int l = op.layer, a = (l / K) * K;
         const char* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
-        MT_STEP_RUN(layer_fwd_impl(d, layer_view(M, w), in, A.seg[l - a], A.lws, A.lws_bytes, sC,
-                                   M->run.time_kernels ? &probe : nullptr));
+        if (keep)
+          MT_STEP_RUN(layer_fwd_keep_impl(d, layer_view(M, w), in, A.seg[l - a], A.keep[l - a],
+                                          A.keep_bytes, sC,
+                                          M->run.time_kernels ? &probe : nullptr));
+        else
+          MT_STEP_RUN(layer_fwd_impl(d, layer_view(M, w), in, A.seg[l - a], A.lws, A.lws_bytes, sC,
+                                     M->run.time_kernels ? &probe : nullptr));
       } else {  // OP_BWD
         const int l = op.layer, a = (l / K) * K;
         const char* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
@@ -637,8 +657,15 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
             goto drain;
           }
         }
-        MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
-                                   A.lws, A.lws_bytes, sC, M->run.time_kernels ? &probe : nullptr));
+        if (keep)
+          MT_STEP_RUN(layer_bwd_saved_impl(d, layer_view(M, w), in, A.dy, A.dy,
+                                           grad_view(M, A.gring[r]), A.keep[l - a], A.keep_bytes,
+                                           A.lws, A.lws_bytes, sC,
+                                           M->run.time_kernels ? &probe : nullptr));
+        else
+          MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
+                                     A.lws, A.lws_bytes, sC,
+                                     M->run.time_kernels ? &probe : nullptr));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
         Offload o{l, A.gring[r], M->ll.total, op_done[i], r};
         offq.push(o);

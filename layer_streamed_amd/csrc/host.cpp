@@ -236,6 +236,7 @@ void mt_run_cfg_default(mt_run_cfg* r) {
   r->host_alloc = MT_HOST_PINNED;
   r->keep_grads = 0;
   r->time_kernels = 1;
+  r->keep_internals = 1;
   r->lr = 1e-4;
   r->beta1 = 0.9;
   r->beta2 = 0.999;

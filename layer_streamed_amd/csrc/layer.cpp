@@ -105,10 +105,35 @@ struct LayerWs {
 };
 
 template <class E>
+void carve_bwd_scratch(const Dims& d, Carve& c, LayerWs<E>* w) {
+  const size_t D = d.D, H = d.H, C = d.mlp_chunk;
+  w->dgu = c.take<E>(C * 2 * d.F);
+  w->db = c.take<E>(D * H);
+  w->dx_mid = c.take<E>(D * H);
+  w->dout = c.take<E>(D * d.Qd);
+  w->dqkv = c.take<E>(D * d.NQKV);
+  w->da = c.take<E>(D * H);
+  w->delta = c.take<float>((size_t)d.B * d.Hq * d.T);
+  w->dg_part = c.take<float>((size_t)rmsnorm_bwd_blocks((int)D) * H);
+  if (C < D) {
+    w->acc_d = c.take<float>(H * d.F);
+    w->acc_gu = c.take<float>(2 * (size_t)d.F * H);
+  }
+}
+
+template <class E>
+// which: 0 forward (internals, gate/up not kept), 1 recompute + backward
+// (internals with gate/up, then backward scratch), 2 kept internals of one
+// layer (gate/up included; needs an unchunked MLP), 3 backward scratch only.
 LayerWs<E> carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
   Carve c{base};
   LayerWs<E> w{};
   const size_t D = d.D, H = d.H, C = d.mlp_chunk;
+  if (which == 3) {
+    carve_bwd_scratch(d, c, &w);
+    *bytes = c.off + 256;
+    return w;
+  }
   w.cos_t = c.take<float>((size_t)d.T * d.d / 2);
   w.sin_t = c.take<float>((size_t)d.T * d.d / 2);
   w.rstd1 = c.take<float>(D);
@@ -120,21 +145,8 @@ LayerWs<E> carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
   w.x_mid = c.take<E>(D * H);
   w.b = c.take<E>(D * H);
   w.m = c.take<E>(C * d.F);
-  if (which == 1) {
-    w.gu = c.take<E>(C * 2 * d.F);
-    w.dgu = c.take<E>(C * 2 * d.F);
-    w.db = c.take<E>(D * H);
-    w.dx_mid = c.take<E>(D * H);
-    w.dout = c.take<E>(D * d.Qd);
-    w.dqkv = c.take<E>(D * d.NQKV);
-    w.da = c.take<E>(D * H);
-    w.delta = c.take<float>((size_t)d.B * d.Hq * d.T);
-    w.dg_part = c.take<float>((size_t)rmsnorm_bwd_blocks((int)D) * H);
-    if (C < D) {
-      w.acc_d = c.take<float>(H * d.F);
-      w.acc_gu = c.take<float>(2 * (size_t)d.F * H);
-    }
-  }
+  if (which == 1 || which == 2) w.gu = c.take<E>(C * 2 * d.F);
+  if (which == 1) carve_bwd_scratch(d, c, &w);
   *bytes = c.off + 256;
   return w;
 }
@@ -214,20 +226,28 @@ mt_status attn_half(const Dims& d, const LayerW<E>& w, const E* x, const LayerWs
   return MT_OK;
 }
 
+// keep = true: the internals (a, qkv, o, lse, x_mid, b, gate/up, m, rstd)
+// stay in the buffer for a later backward without recompute (unchunked MLP).
 template <class E>
 mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* x_out, void* wsp,
-                      size_t ws_bytes, hipStream_t s, Probe* probe) {
+                      size_t ws_bytes, hipStream_t s, Probe* probe, bool keep = false) {
   size_t need = 0;
-  LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), 0, &need);
+  LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), keep ? 2 : 0, &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE, "layer forward: workspace %zu < %zu bytes",
            ws_bytes, need);
+  MT_CHECK(!keep || d.mlp_chunk == d.D, MT_E_SHAPE,
+           "layer forward: kept internals need an unchunked MLP");
   const LayerW<E> w(wv);
   MT_RUN(attn_half(d, w, x_in, ws, s, probe));
   for (int r0 = 0; r0 < d.D; r0 += d.mlp_chunk) {
     const int rows = std::min(d.mlp_chunk, d.D - r0);
-    GemmArgsT<E> gu = gemm<E>(GEMM_NT, EPI_SWIGLU, rows, 2 * d.F, d.H, ws.b + (size_t)r0 * d.H,
-                              d.H, w.wgu, d.H, ws.m, d.F);
+    GemmArgsT<E> gu = gemm<E>(GEMM_NT, keep ? EPI_SWIGLU_SAVE : EPI_SWIGLU, rows, 2 * d.F, d.H,
+                              ws.b + (size_t)r0 * d.H, d.H, w.wgu, d.H, ws.m, d.F);
     gu.F = d.F;
+    if (keep) {
+      gu.C2 = ws.gu;
+      gu.ldc2 = 2 * d.F;
+    }
     MT_RUN(run_gemm(gu, s, probe));
     GemmArgsT<E> dn = gemm<E>(GEMM_NT, EPI_RESID_BF16, rows, d.H, d.F, ws.m, d.F, w.wd, d.F,
                               x_out + (size_t)r0 * d.H, d.H);
@@ -238,17 +258,29 @@ mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* 
   return MT_OK;
 }
 
+// saved != nullptr: the internals come from layer_fwd_t(keep = true) and
+// nothing is recomputed; wsp then holds only the backward scratch.
 template <class E>
 mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, const E* dy, E* dx,
                       const mt_layer_grad_view& g, void* wsp, size_t ws_bytes, hipStream_t s,
-                      Probe* probe) {
+                      Probe* probe, void* saved = nullptr, size_t saved_bytes = 0) {
   size_t need = 0;
-  LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), 1, &need);
+  LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), saved ? 3 : 1, &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE,
            "layer recompute/backward: workspace %zu < %zu bytes", ws_bytes, need);
+  if (saved) {
+    size_t need_s = 0;
+    const LayerWs<E> in = carve_layer<E>(d, static_cast<char*>(saved), 2, &need_s);
+    MT_CHECK(saved_bytes >= need_s, MT_E_OOM_DEVICE, "layer backward: internals %zu < %zu bytes",
+             saved_bytes, need_s);
+    MT_CHECK(d.mlp_chunk == d.D, MT_E_SHAPE, "layer backward: kept internals need an unchunked MLP");
+    ws.cos_t = in.cos_t; ws.sin_t = in.sin_t; ws.rstd1 = in.rstd1; ws.rstd2 = in.rstd2;
+    ws.lse = in.lse; ws.a = in.a; ws.qkv = in.qkv; ws.o = in.o; ws.x_mid = in.x_mid;
+    ws.b = in.b; ws.m = in.m; ws.gu = in.gu;
+  }
   const LayerW<E> w(wv);
   // ---- recompute the attention half (rebuilds a, qkv (rotated), o, lse, x_mid, b)
-  MT_RUN(attn_half(d, w, x_in, ws, s, probe));
+  if (!saved) MT_RUN(attn_half(d, w, x_in, ws, s, probe));
   const bool chunked = d.mlp_chunk < d.D;
   E* gd = static_cast<E*>(g.w_down);
   E* ggu = static_cast<E*>(g.w_gate_up);
@@ -266,7 +298,7 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
     gu.F = d.F;
     gu.C2 = ws.gu;
     gu.ldc2 = 2 * d.F;
-    MT_RUN(run_gemm(gu, s, probe));
+    if (!saved) MT_RUN(run_gemm(gu, s, probe));
     // dgate, dup from dm = dy W_down (NN) fused with the SwiGLU derivative
     GemmArgsT<E> dm = gemm<E>(GEMM_NN, EPI_SWIGLU_BWD, rows, d.F, d.H, dy_c, d.H, w.wd, d.F,
                               ws.dgu, 2 * d.F);
@@ -324,6 +356,29 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
 }
 
 }  // namespace
+
+mt_status layer_fwd_keep_impl(const Dims& d, const mt_layer_view& w, const void* x_in, void* x_out,
+                              void* internals, size_t internals_bytes, hipStream_t s,
+                              Probe* probe) {
+  if (d.prec == MT_PREC_FP32_DEBUG)
+    return layer_fwd_t(d, w, static_cast<const float*>(x_in), static_cast<float*>(x_out),
+                       internals, internals_bytes, s, probe, true);
+  return layer_fwd_t(d, w, static_cast<const uint16_t*>(x_in), static_cast<uint16_t*>(x_out),
+                     internals, internals_bytes, s, probe, true);
+}
+
+mt_status layer_bwd_saved_impl(const Dims& d, const mt_layer_view& w, const void* x_in,
+                               const void* dy, void* dx, const mt_layer_grad_view& g,
+                               void* internals, size_t internals_bytes, void* ws,
+                               size_t ws_bytes, hipStream_t s, Probe* probe) {
+  if (d.prec == MT_PREC_FP32_DEBUG)
+    return layer_bwd_t(d, w, static_cast<const float*>(x_in), static_cast<const float*>(dy),
+                       static_cast<float*>(dx), g, ws, ws_bytes, s, probe, internals,
+                       internals_bytes);
+  return layer_bwd_t(d, w, static_cast<const uint16_t*>(x_in), static_cast<const uint16_t*>(dy),
+                     static_cast<uint16_t*>(dx), g, ws, ws_bytes, s, probe, internals,
+                     internals_bytes);
+}
 
 size_t layer_ws_bytes(const Dims& d, int which) {
   size_t bytes = 0;
@@ -442,8 +497,15 @@ extern "C" {
 size_t mt_layer_workspace_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run, int32_t batch,
                                 int32_t seq, int32_t which) {
   Dims d;
-  if (make_dims(cfg, run, batch, seq, &d) || (which != 0 && which != 1)) return 0;
-  return layer_ws_bytes(d, which);
+  if (make_dims(cfg, run, batch, seq, &d) || which < 0 || which > 2) return 0;
+  return layer_ws_bytes(d, which == 2 ? 3 : which);
+}
+
+size_t mt_layer_internals_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run, int32_t batch,
+                                int32_t seq) {
+  Dims d;
+  if (make_dims(cfg, run, batch, seq, &d) || d.mlp_chunk < d.D) return 0;
+  return layer_ws_bytes(d, 2);
 }
 
 static mt_status check_view(const mt_layer_view* w) {
@@ -463,6 +525,38 @@ mt_status mt_layer_fwd(const mt_model_cfg* cfg, const mt_run_cfg* run, const mt_
   MT_CHECK(x_in != x_out, MT_E_INVALID, "mt_layer_fwd: x_out may not alias x_in");
   return layer_fwd_impl(d, *w, x_in, x_out, workspace, workspace_bytes,
                         static_cast<hipStream_t>(stream), nullptr);
+}
+
+mt_status mt_layer_fwd_keep(const mt_model_cfg* cfg, const mt_run_cfg* run, const mt_layer_view* w,
+                            const void* x_in, void* x_out, int32_t batch, int32_t seq,
+                            void* internals, size_t internals_bytes, void* stream) {
+  Dims d;
+  if (const char* m = make_dims(cfg, run, batch, seq, &d))
+    return set_error(MT_E_SHAPE, "mt_layer_fwd_keep: %s", m);
+  MT_RUN(check_view(w));
+  MT_CHECK(x_in && x_out, MT_E_INVALID, "mt_layer_fwd_keep: null activation pointer");
+  MT_CHECK(x_in != x_out, MT_E_INVALID, "mt_layer_fwd_keep: x_out may not alias x_in");
+  MT_CHECK(d.mlp_chunk == d.D, MT_E_SHAPE, "mt_layer_fwd_keep: needs mlp_chunk_tokens = 0");
+  return layer_fwd_keep_impl(d, *w, x_in, x_out, internals, internals_bytes,
+                             static_cast<hipStream_t>(stream), nullptr);
+}
+
+mt_status mt_layer_bwd_saved(const mt_model_cfg* cfg, const mt_run_cfg* run,
+                             const mt_layer_view* w, const void* x_in, const void* dy, void* dx,
+                             const mt_layer_grad_view* dw, int32_t batch, int32_t seq,
+                             void* internals, size_t internals_bytes, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Dims d;
+  if (const char* m = make_dims(cfg, run, batch, seq, &d))
+    return set_error(MT_E_SHAPE, "mt_layer_bwd_saved: %s", m);
+  MT_RUN(check_view(w));
+  MT_CHECK(x_in && dy && dx && internals, MT_E_INVALID, "mt_layer_bwd_saved: null pointer");
+  MT_CHECK(dw && dw->attn_norm && dw->w_qkv && dw->w_o && dw->mlp_norm && dw->w_gate_up &&
+               dw->w_down,
+           MT_E_INVALID, "mt_layer_bwd_saved: null gradient pointer");
+  MT_CHECK(d.mlp_chunk == d.D, MT_E_SHAPE, "mt_layer_bwd_saved: needs mlp_chunk_tokens = 0");
+  return layer_bwd_saved_impl(d, *w, x_in, dy, dx, *dw, internals, internals_bytes, workspace,
+                              workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
 }
 
 mt_status mt_layer_recompute_bwd(const mt_model_cfg* cfg, const mt_run_cfg* run,

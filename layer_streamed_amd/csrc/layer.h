@@ -59,6 +59,16 @@ mt_status layer_fwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in
 mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in, const void* dy,
                          void* dx, const mt_layer_grad_view& g, void* ws, size_t ws_bytes,
                          hipStream_t s, Probe* probe);
+// Forward that keeps its internals in `internals` (layer_ws_bytes(d, 2)
+// bytes; unchunked MLP only), and the backward that uses them instead of
+// recomputing (ws: layer_ws_bytes(d, 3) bytes of backward scratch).
+mt_status layer_fwd_keep_impl(const Dims& d, const mt_layer_view& w, const void* x_in, void* x_out,
+                              void* internals, size_t internals_bytes, hipStream_t s,
+                              Probe* probe);
+mt_status layer_bwd_saved_impl(const Dims& d, const mt_layer_view& w, const void* x_in,
+                               const void* dy, void* dx, const mt_layer_grad_view& g,
+                               void* internals, size_t internals_bytes, void* ws,
+                               size_t ws_bytes, hipStream_t s, Probe* probe);
 
 // LM head: h = rms(x_L) g_f; logits = h W_out^T per token chunk; next-token
 // cross-entropy; dh, dW_out, dg_f; dx_L = rmsnorm backward.  targets: device

@@ -128,3 +128,58 @@ def test_layer_fp32_debug_precision(name, shape, B, T, chunk):
     for k, (gpu, ref) in out.items():
         assert np.isfinite(gpu).all(), k
         assert rel(gpu, ref) < F32_TOL, (k, rel(gpu, ref))
+
+
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_kept_internals_backward_is_bitwise_the_recompute(fp32):
+    """mt_layer_fwd_keep + mt_layer_bwd_saved (no recompute) against
+    mt_layer_fwd + mt_layer_recompute_bwd on the same weights and input:
+    same kernels on the same inputs, so every output is bitwise equal."""
+    torch, mt = _env()
+    shape = synth.ModelShape(name="gqa5", n_layers=1, hidden=640, n_heads=10, n_kv_heads=2,
+                             head_dim=128, ffn=1536, vocab=1024)
+    B, T = 2, 96
+    names = synth.layer_param_names(0)
+    w = {n.split(".")[-1]: v for n, v in synth.make_weights(shape, seed=21, names=names).items()}
+    rng = np.random.default_rng(22)
+    dt = torch.float32 if fp32 else torch.bfloat16
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(dt)
+
+    W = {"attn_norm": dev(1 + 0.1 * rng.standard_normal(shape.hidden)),
+         "w_qkv": dev(np.concatenate([w["w_q"], w["w_k"], w["w_v"]])), "w_o": dev(w["w_o"]),
+         "mlp_norm": dev(1 + 0.1 * rng.standard_normal(shape.hidden)),
+         "w_gate_up": dev(np.concatenate([w["w_gate"], w["w_up"]])), "w_down": dev(w["w_down"])}
+    view = mt.LayerView(*[W[k].data_ptr() for k, _ in mt.LayerView._fields_])
+    mcfg = mt.model_cfg(shape)
+    rcfg = mt.run_cfg(precision=mt.PREC_FP32_DEBUG if fp32 else mt.PREC_BF16)
+    X = dev(rng.standard_normal((B * T, shape.hidden)))
+    DY = dev(rng.standard_normal((B * T, shape.hidden)) * 1e-2)
+    outs = []
+    for keep in (False, True):
+        G = {k: torch.full_like(v, float("nan")) for k, v in W.items()}
+        gview = mt.GradView(*[G[k].data_ptr() for k, _ in mt.GradView._fields_])
+        Y = torch.empty_like(X)
+        DX = DY.clone()
+        if keep:
+            nb = mt.layer_internals_bytes(mcfg, rcfg, B, T)
+            assert nb > 0
+            internals = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            ws = torch.empty(mt.layer_workspace_bytes(mcfg, rcfg, B, T, 2), dtype=torch.uint8,
+                             device="cuda")
+            assert ws.numel() < mt.layer_workspace_bytes(mcfg, rcfg, B, T, 1)
+            mt.layer_fwd_keep(mcfg, rcfg, view, X, Y, B, T, internals)
+            mt.layer_bwd_saved(mcfg, rcfg, view, X, DX, DX, gview, B, T, internals, ws)
+        else:
+            ws = torch.empty(mt.layer_workspace_bytes(mcfg, rcfg, B, T, 1), dtype=torch.uint8,
+                             device="cuda")
+            mt.layer_fwd(mcfg, rcfg, view, X, Y, B, T, ws)
+            mt.layer_recompute_bwd(mcfg, rcfg, view, X, DX, DX, gview, B, T, ws)
+        torch.cuda.synchronize()
+        outs.append({"y": Y.clone(), "dx": DX.clone(), **{k: v.clone() for k, v in G.items()}})
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
+        assert torch.isfinite(outs[1][k].float()).all(), k
+    # with a chunked MLP there is nothing to keep
+    assert mt.layer_internals_bytes(mcfg, mt.run_cfg(mlp_chunk_tokens=64), B, T) == 0

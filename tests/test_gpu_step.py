@@ -89,9 +89,10 @@ def test_two_steps_match_oracle(tiny):
 
 @pytest.mark.parametrize("kw", [dict(serialize=1), dict(ckpt_interval=2), dict(prefetch_depth=1),
                                 dict(prefetch_depth=3), dict(use_slab_pool=0),
-                                dict(n_slabs=1), dict(host_threads=3)],
+                                dict(n_slabs=1), dict(host_threads=3), dict(keep_internals=0),
+                                dict(keep_internals=0, ckpt_interval=1)],
                          ids=["serialized", "K2", "depth1", "depth3", "no-pool", "one-slab",
-                              "3-threads"])
+                              "3-threads", "recompute", "recompute-K1"])
 def test_schedule_invariance_bitwise(tiny, kw):
     s, w, ids = tiny
     base = _run(s, w, ids)

@@ -12,30 +12,32 @@ import pytest
 FWD, HEAD, REFWD, BWD = 0, 1, 2, 3
 
 
-def _plan(L, K, depth):
+def _plan(L, K, depth, keep=1):
     from layer_streamed_amd import mt
-    return mt.debug_plan(L, K, depth)
+    return mt.debug_plan(L, K, depth, keep)
 
 
 @pytest.mark.parametrize("L", [1, 2, 5, 28])
 @pytest.mark.parametrize("K", [1, 2, 3, 4, 7, 28])
 @pytest.mark.parametrize("depth", [1, 2, 3])
-def test_plan_is_hazard_free(L, K, depth):
+@pytest.mark.parametrize("keep", [0, 1])
+def test_plan_is_hazard_free(L, K, depth, keep):
     if K > L:
         K = L
-    st, ops, loads, n_slots = _plan(L, K, depth)
+    st, ops, loads, n_slots = _plan(L, K, depth, keep)
     assert st == 0
     kinds = ops[:, 0].tolist()
     # forward of every layer in order, then the head
     assert kinds[:L] == [FWD] * L and ops[:L, 1].tolist() == list(range(L))
     assert kinds[L] == HEAD
-    # backward: segments from the last, each re-forwarding all but its last
-    # layer from the checkpoint, then backward in reverse
+    # backward: segments from the last, each re-forwarding from the
+    # checkpoint (every layer when internals are kept, else all but the
+    # last), then backward in reverse
     rest = ops[L + 1:]
     expect = []
     for a in reversed(range(0, L, K)):
         e = min(a + K, L)
-        expect += [(REFWD, l) for l in range(a, e - 1)]
+        expect += [(REFWD, l) for l in range(a, e if keep else e - 1)]
         expect += [(BWD, l) for l in reversed(range(a, e))]
     assert [(int(k), int(l)) for k, l, _ in rest] == expect
     # every op reads a load of its own unit, inside that load's live range
@@ -63,11 +65,12 @@ def test_plan_is_hazard_free(L, K, depth):
         by_slot[slot] = j
 
 
-def test_plan_single_stream_replay_never_reads_stale_weights():
+@pytest.mark.parametrize("keep", [0, 1])
+def test_plan_single_stream_replay_never_reads_stale_weights(keep):
     """Replay the plan as the executor does on one in-order stream and track
     which unit each slot holds at every compute op."""
     L, K, depth = 28, 4, 2
-    st, ops, loads, n_slots = _plan(L, K, depth)
+    st, ops, loads, n_slots = _plan(L, K, depth, keep)
     assert st == 0
     holds = {}
     nxt = 0
@@ -82,9 +85,12 @@ def test_plan_single_stream_replay_never_reads_stale_weights():
 
 def test_plan_counts_match_the_method():
     """Per step: L forward loads + head + L backward loads; the forward uses
-    each layer once, recompute+backward once, re-forward (K-1)/K of them."""
+    each layer once, backward once; the re-forward covers (K-1)/K of the
+    layers (each backward then recomputes its layer) or, with kept
+    internals, every layer (and no backward recomputes)."""
     L, K = 28, 4
-    st, ops, loads, _ = _plan(L, K, 2)
-    assert len(loads) == 2 * L + 1
-    assert (ops[:, 0] == REFWD).sum() == L - L // K
-    assert (ops[:, 0] == BWD).sum() == L
+    for keep, refwd in ((0, L - L // K), (1, L)):
+        st, ops, loads, _ = _plan(L, K, 2, keep)
+        assert len(loads) == 2 * L + 1
+        assert (ops[:, 0] == REFWD).sum() == refwd
+        assert (ops[:, 0] == BWD).sum() == L
