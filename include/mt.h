@@ -89,6 +89,13 @@ typedef struct {
                                 re-forward covers the first K-1 layers and every layer's
                                 backward recomputes (mt_layer_recompute_bwd).  Needs
                                 mlp_chunk_tokens = 0, else treated as 0. */
+  int32_t defer_updates;     /* 1 (default): the host Adam of the LM head and of the
+                                embedding is left to the next step, which applies it
+                                while its forward streams the other units (the head is
+                                needed only after every layer's forward, the embedding
+                                only for the batch's rows at its start); reading or
+                                setting a parameter applies it first, so results are
+                                bitwise those of 0 (apply within the step). */
   double lr, beta1, beta2, eps, weight_decay; /* Adam (weight_decay must be 0) */
 } mt_run_cfg;
 
@@ -212,8 +219,9 @@ mt_status mt_model_set_param(mt_model* model, const char* name,
 
 enum { MT_GET_MASTER = 0, MT_GET_M = 1, MT_GET_V = 2, MT_GET_GRAD = 3,
        MT_GET_SHADOW = 4 };
-/* get: copies a tensor out as fp32.  MT_GET_GRAD needs keep_grads = 1 and
- * returns the last step's gradient as the optimizer saw it. */
+/* get: copies a tensor out as fp32 (after applying any update the last
+ * step deferred).  MT_GET_GRAD needs keep_grads = 1 and returns the last
+ * step's gradient as the optimizer saw it. */
 mt_status mt_model_get_param(const mt_model* model, const char* name,
                              int32_t which, float* dst, size_t n);
 
@@ -229,10 +237,14 @@ size_t mt_stream_arena_bytes(const mt_model* model, int32_t batch, int32_t seq);
  * offload each unit's bf16 gradient on streams[2] (G) into a pinned slab,
  * where a CPU Adam step updates that unit while the GPU continues.
  * tokens: host int32 [batch, seq], ids in [0, vocab).  arena: device, at
- * least mt_stream_arena_bytes bytes.  Blocks until every unit is updated;
- * writes the mean next-token loss to *loss_out and, if stats_out is not
- * null, timings and byte counts.  With check_finite, a non-finite loss
- * returns MT_E_NONFINITE before any update. */
+ * least mt_stream_arena_bytes bytes.  Blocks until every unit is updated
+ * (with defer_updates, every unit but the LM head and the embedding, whose
+ * updates the next step, mt_model_get_param or mt_model_set_param applies
+ * first; the values are the same either way); writes the mean next-token
+ * loss to *loss_out and, if stats_out is not null, timings and byte
+ * counts.  With check_finite, a non-finite loss returns MT_E_NONFINITE
+ * before any update.  A step that fails after validation drops the updates
+ * it deferred. */
 mt_status mt_stream_step(mt_model* model, const int32_t* tokens, int32_t batch,
                          int32_t seq, void* arena, size_t arena_bytes,
                          void* const streams[3], float* loss_out,

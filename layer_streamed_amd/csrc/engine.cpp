@@ -218,7 +218,7 @@ struct Offload {
 
 struct Landed {
   int unit;
-  void* host;      // slab (or dx0 staging)
+  void* host;      // slab, dx0 staging or the head's deferred-gradient buffer
   bool own_alloc;  // allocated for this transfer (no pool)
   hipEvent_t ev;
   bool end = false;
@@ -376,6 +376,15 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   const size_t es = M->es;
   const bool f32 = es == 4;
 
+  if (M->run.defer_updates && !M->pending.head_grad) {
+    M->pending.head_grad = M->host_alloc(M->hl.total * M->es, true);
+    MT_CHECK(M->pending.head_grad, MT_E_OOM_HOST,
+             "mt_stream_step: pinned allocation of the head's gradient buffer failed");
+  }
+  // the previous step's embedding update, for the rows this batch gathers
+  // (the other rows follow on the optimizer thread during the forward)
+  apply_pending_embed_rows(M, tokens, (size_t)d.D);
+  const bool defer = M->run.defer_updates != 0;
   // host: targets and the embedding gather (from the streamed copy)
   const Unit& emb = M->units[L + 1];
   for (int b = 0; b < d.B; ++b)
@@ -414,6 +423,11 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   size_t next_load = 0;
   int bwd_count = 0;
   std::thread gthr, athr;
+  // the previous step's head update must land before the head is streamed
+  std::mutex head_mu;
+  std::condition_variable head_cv;
+  bool head_done = !M->pending.head;
+  std::atomic<int64_t> units_deferred{0};
   std::mutex loss_mu;
   std::condition_variable loss_cv;
   bool loss_ready = false;
@@ -436,6 +450,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       if (ok) {
         if (o.unit < 0) {
           host = M->dx0_host;
+        } else if (o.unit == L && defer) {
+          host = M->pending.head_grad;  // free: the previous head update ran first
         } else if (M->run.use_slab_pool) {
           const auto tw = clock::now();
           host = M->slabs.acquire();
@@ -464,7 +480,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       if (!ok) {
         if (!abort_all.load()) g_fail = 1;
         abort_all = true;
-        if (host && o.unit >= 0) {
+        if (host && o.unit >= 0 && !(o.unit == L && defer)) {
           if (own) hipHostFree(host);
           else M->slabs.release(host);
         }
@@ -476,6 +492,18 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
 
   // ------------------------------------------------------ Adam thread
   auto a_main = [&]() {
+    // the previous step's deferred updates, while the GPU runs the forward
+    {
+      const auto t0 = clock::now();
+      apply_pending_head(M);
+      {
+        std::lock_guard<std::mutex> lk(head_mu);
+        head_done = true;
+      }
+      head_cv.notify_all();
+      apply_pending_embed_rest(M);
+      adam_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+    }
     // zero the embedding gradient while the GPU runs the forward
     float* dE = M->dE;
     M->pool->parallel_for((size_t)d.V * d.H,
@@ -510,6 +538,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
             a_fail = 2;
             abort_all = true;
             skip = true;
+          } else if (defer && x.unit == L) {
+            // the head's update waits for the next step (PendingAdam)
+            if (u.kept) memcpy(u.kept, x.host, u.n * es);
+            M->pending.head = true;  // its gradient stays in pending.head_grad
+            M->pending.hp_head = hp;
+            ++units_deferred;
           } else {
             adam_parallel(u.master, u.m, u.v, gb, gf,
                           f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
@@ -529,6 +563,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
             a_fail = 2;
             abort_all = true;
             skip = true;
+          } else if (defer) {
+            // the embedding's update waits for the next step (PendingAdam)
+            M->pending.embed = true;
+            M->pending.hp_embed = hp;
+            M->pending.row_done.assign((size_t)d.V, 0);
+            ++units_deferred;
           } else {
             adam_parallel(u.master, u.m, u.v, nullptr, dE,
                           f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
@@ -539,7 +579,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         }
       }
       adam_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-      if (x.unit >= 0) {
+      if (x.unit >= 0 && !(x.unit == L && defer)) {
         if (x.own_alloc) hipHostFree(x.host);
         else M->slabs.release(x.host);
       }
@@ -594,6 +634,10 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           MT_STEP_HIP(hipStreamWaitEvent(sW, op_done[ld.gate_use], 0));
         const Unit& u = M->units[ld.unit];
         char* dst = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+        if (ld.unit == L) {
+          std::unique_lock<std::mutex> lk(head_mu);
+          head_cv.wait(lk, [&] { return head_done; });
+        }
         hipEvent_t c0 = get_ev(), c1 = get_ev();
         MT_STEP_HIP(hipEventRecord(c0, sW));
         MT_STEP_HIP(hipMemcpyAsync(dst, u.shadow, u.n * es, hipMemcpyHostToDevice, sW));
@@ -703,6 +747,8 @@ drain:
                      (long long)units_updated.load());
   *loss_out = *M->loss_host;
   if (fail != MT_OK) {
+    // an update this step deferred belongs to a step that did not complete
+    if (units_deferred.load() > 0) drop_pending(M);
     if (units_updated.load() > 0) M->broken = true;
     return fail;
   }
@@ -746,7 +792,7 @@ drain:
     s.pinned_host_bytes = M->pinned_bytes;
     s.pageable_host_bytes = M->pageable_bytes;
     s.device_arena_bytes = (int64_t)need;
-    s.units_updated = units_updated.load();
+    s.units_updated = units_updated.load() + units_deferred.load();
     s.step_ms = std::chrono::duration<double, std::milli>(clock::now() - t_begin).count();
     s.tail_ms = s.step_ms - (s.fwd_ms + s.head_ms + s.bwd_ms);
     s.host_ring_wait_ms = ring_wait_ms;

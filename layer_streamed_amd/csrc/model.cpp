@@ -67,6 +67,74 @@ bool lookup_param(const mt_model* m, const char* name, TensorRef* out) {
   return true;
 }
 
+void apply_pending_head(mt_model* M) {
+  PendingAdam& pa = M->pending;
+  if (!pa.head) return;
+  Unit& u = M->units[M->cfg.n_layers];
+  const bool f32 = M->es == 4;
+  adam_parallel(u.master, u.m, u.v, f32 ? nullptr : static_cast<const uint16_t*>(pa.head_grad),
+                f32 ? static_cast<const float*>(pa.head_grad) : nullptr,
+                f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
+                f32 ? static_cast<float*>(u.shadow) : nullptr, u.n, pa.hp_head, M->pool.get());
+  pa.head = false;
+}
+
+namespace {
+// Adam over whole embedding rows [r0, r1) of the list (or of every row when
+// rows == nullptr), skipping and then marking rows already done.
+void embed_rows(mt_model* M, const std::vector<int32_t>* rows) {
+  PendingAdam& pa = M->pending;
+  Unit& u = M->units[M->cfg.n_layers + 1];
+  const size_t H = M->shape.H;
+  const bool f32 = M->es == 4;
+  const size_t n = rows ? rows->size() : (size_t)M->shape.V;
+  M->pool->parallel_for(n, [&](size_t lo, size_t hi) {
+    for (size_t i = lo; i < hi; ++i) {
+      const size_t r = rows ? (size_t)(*rows)[i] : i;
+      if (pa.row_done[r]) continue;
+      const size_t a = r * H;
+      if (f32)
+        adam_range(u.master + a, u.m + a, u.v + a, nullptr, M->dE + a, nullptr,
+                   static_cast<float*>(u.shadow) + a, 0, H, pa.hp_embed);
+      else
+        adam_range(u.master + a, u.m + a, u.v + a, nullptr, M->dE + a,
+                   static_cast<uint16_t*>(u.shadow) + a, nullptr, 0, H, pa.hp_embed);
+      pa.row_done[r] = 1;
+    }
+  }, 16);
+}
+}  // namespace
+
+void apply_pending_embed_rows(mt_model* M, const int32_t* ids, size_t n) {
+  PendingAdam& pa = M->pending;
+  if (!pa.embed) return;
+  std::vector<uint8_t> seen(M->shape.V, 0);
+  std::vector<int32_t> rows;
+  for (size_t t = 0; t < n; ++t)
+    if (!seen[ids[t]]) {
+      seen[ids[t]] = 1;
+      rows.push_back(ids[t]);
+    }
+  embed_rows(M, &rows);
+}
+
+void apply_pending_embed_rest(mt_model* M) {
+  PendingAdam& pa = M->pending;
+  if (!pa.embed) return;
+  embed_rows(M, nullptr);
+  pa.embed = false;
+}
+
+void flush_pending(mt_model* M) {
+  apply_pending_head(M);
+  apply_pending_embed_rest(M);
+}
+
+void drop_pending(mt_model* M) {
+  PendingAdam& pa = M->pending;
+  pa.head = pa.embed = false;
+}
+
 }  // namespace mt
 
 using namespace mt;
@@ -188,6 +256,7 @@ mt_status mt_model_set_param(mt_model* m, const char* name, const float* src, si
   MT_CHECK(lookup_param(m, name, &r), MT_E_INVALID, "mt_model_set_param: unknown parameter '%s'",
            name ? name : "(null)");
   MT_CHECK(n == r.n, MT_E_SHAPE, "mt_model_set_param: '%s' has %zu elements, got %zu", name, r.n, n);
+  flush_pending(m);  // a pending update must not land on the new value later
   Unit& u = m->units[r.unit];
   const bool f32 = m->es == 4;
   m->pool->parallel_for(n, [&](size_t lo, size_t hi) {
@@ -211,6 +280,8 @@ mt_status mt_model_get_param(const mt_model* m, const char* name, int32_t which,
   MT_CHECK(lookup_param(m, name, &r), MT_E_INVALID, "mt_model_get_param: unknown parameter '%s'",
            name ? name : "(null)");
   MT_CHECK(n == r.n, MT_E_SHAPE, "mt_model_get_param: '%s' has %zu elements, got %zu", name, r.n, n);
+  // the model is observed: apply any update the last step left pending
+  flush_pending(const_cast<mt_model*>(m));
   const Unit& u = m->units[r.unit];
   const bool embed = r.unit == m->cfg.n_layers + 1;
   // element i of a streamed-precision array (bf16 or fp32) as fp32

@@ -53,6 +53,21 @@ class SlabPool {
   size_t total_ = 0;
 };
 
+// Optimizer updates a step leaves for the next one to apply (the LM head
+// and the embedding: their weights are needed late in the next forward, or
+// for only a few rows at its start, so their host Adam runs while the next
+// forward streams the other units instead of after this step's backward).
+// Every reader of the model applies them first (flush_pending).
+struct PendingAdam {
+  bool head = false, embed = false;
+  AdamHp hp_head{}, hp_embed{};
+  // the head's gradient lands in a pinned buffer of its own (never a pool
+  // slab: holding a slab across units would stall the offload of the rest
+  // of the step when the pool is small)
+  void* head_grad = nullptr;
+  std::vector<uint8_t> row_done;  // embedding rows already updated
+};
+
 struct HostBlock {  // one host allocation
   void* p = nullptr;
   size_t bytes = 0;
@@ -83,6 +98,7 @@ struct mt_model {
   size_t staging_tokens = 0;
   std::vector<hipEvent_t> events;  // grown on demand
   std::unique_ptr<mt::SdmaCopier> sdma;  // gradient offload engine (created on first step)
+  mt::PendingAdam pending;
   int64_t step = 0;
   bool broken = false;
   int64_t pinned_bytes = 0, pageable_bytes = 0;
@@ -93,4 +109,13 @@ struct mt_model {
 
 namespace mt {
 bool lookup_param(const mt_model* m, const char* name, TensorRef* out);
+// Pending head / embedding updates (PendingAdam): apply the head's; apply the
+// embedding's for the rows of `ids` only (marking them done) or for every row
+// not yet done; apply everything and clear (flush_pending).  Each uses the
+// model's thread pool, so callers must not overlap them with other pool work.
+void apply_pending_head(mt_model* m);
+void apply_pending_embed_rows(mt_model* m, const int32_t* ids, size_t n);
+void apply_pending_embed_rest(mt_model* m);
+void flush_pending(mt_model* m);
+void drop_pending(mt_model* m);
 }

@@ -51,7 +51,7 @@ class RunCfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "ckpt_interval", "prefetch_depth", "use_slab_pool", "n_slabs", "mlp_chunk_tokens",
         "head_chunk_tokens", "precision", "host_threads", "check_finite", "serialize",
-        "host_alloc", "keep_grads", "time_kernels", "keep_internals")] + [
+        "host_alloc", "keep_grads", "time_kernels", "keep_internals", "defer_updates")] + [
         (n, C.c_double) for n in ("lr", "beta1", "beta2", "eps", "weight_decay")]
 
 

@@ -90,9 +90,9 @@ def test_two_steps_match_oracle(tiny):
 @pytest.mark.parametrize("kw", [dict(serialize=1), dict(ckpt_interval=2), dict(prefetch_depth=1),
                                 dict(prefetch_depth=3), dict(use_slab_pool=0),
                                 dict(n_slabs=1), dict(host_threads=3), dict(keep_internals=0),
-                                dict(keep_internals=0, ckpt_interval=1)],
+                                dict(keep_internals=0, ckpt_interval=1), dict(defer_updates=0)],
                          ids=["serialized", "K2", "depth1", "depth3", "no-pool", "one-slab",
-                              "3-threads", "recompute", "recompute-K1"])
+                              "3-threads", "recompute", "recompute-K1", "no-defer"])
 def test_schedule_invariance_bitwise(tiny, kw):
     s, w, ids = tiny
     base = _run(s, w, ids)
@@ -192,3 +192,29 @@ def test_step_fp32_schedule_invariance_bitwise(tiny):
     for n in synth.param_names(s):
         np.testing.assert_array_equal(base["grad"][n], other["grad"][n], err_msg=n)
         np.testing.assert_array_equal(base["master"][n], other["master"][n], err_msg=n)
+
+
+def test_deferred_updates_apply_before_reads_and_never_after_a_set(tiny):
+    """With deferred head / embedding updates: two steps equal two steps
+    without deferral bitwise (the second step applies the first's pending
+    updates while it streams), and a parameter set after a step keeps the
+    set value (the pending update lands before the set, not after)."""
+    torch, mt = _env()
+    s, w, ids = tiny
+    a = _run(s, w, ids, steps=2)
+    b = _run(s, w, ids, steps=2, defer_updates=0)
+    assert a["loss"] == b["loss"]
+    for n in synth.param_names(s):
+        np.testing.assert_array_equal(a["master"][n], b["master"][n], err_msg=n)
+        np.testing.assert_array_equal(a["shadow"][n], b["shadow"][n], err_msg=n)
+    m = mt.Model(s)
+    m.set_params(w)
+    arena = torch.empty(m.arena_bytes(*ids.shape), dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    m.step(ids, arena, streams)
+    new = np.full(w["lm_head"].shape, 0.125, np.float32)
+    m.set_param("lm_head", new)
+    np.testing.assert_array_equal(m.get("lm_head"), new)
+    m.step(ids, arena, streams)  # uses the set head (no stale pending update)
+    assert m.step_count == 2
+    m.close()

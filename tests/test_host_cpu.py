@@ -36,10 +36,12 @@ def test_library_exports_every_declared_symbol():
     assert _declared() <= set(mt.EXPORTED)
 
 
-def _adam(p, m, v, g, step, dtype, shadow=True, **hp):
+def _adam(p, m, v, g, step, dtype, shadow=True, shadow_offset=0, **hp):
     mt = _mt()
     cfg = mt.run_cfg(**hp)
-    sh = np.zeros(p.size, np.uint16) if shadow else None
+    # shadow_offset shifts the bf16 copy off 16-byte alignment (the
+    # vectorized path streams 16-byte stores after a scalar prologue)
+    sh = np.zeros(p.size + shadow_offset, np.uint16)[shadow_offset:] if shadow else None
     gbuf = D.bf16_bits(g) if dtype == mt.DT_BF16 else np.ascontiguousarray(g, np.float32)
     st = mt.call("mt_host_adam", mt.ptr(p), mt.ptr(m), mt.ptr(v), mt.ptr(gbuf), dtype,
                  mt.ptr(sh), p.size, step, C.byref(cfg))
@@ -48,7 +50,8 @@ def _adam(p, m, v, g, step, dtype, shadow=True, **hp):
 
 @pytest.mark.parametrize("dtype", [0, 1], ids=["bf16_grad", "f32_grad"])
 @pytest.mark.parametrize("threads", [1, 7])
-def test_host_adam_bitwise_equals_oracle(dtype, threads):
+@pytest.mark.parametrize("offset", [0, 3])
+def test_host_adam_bitwise_equals_oracle(dtype, threads, offset):
     rng = np.random.default_rng(1 + dtype)
     n = 100_003
     p = (rng.standard_normal(n) * 0.02).astype(np.float32)
@@ -61,7 +64,7 @@ def test_host_adam_bitwise_equals_oracle(dtype, threads):
     for step in (1, 3):
         rp, rm, rv = D.adam_update(p.copy(), m.copy(), v.copy(), g, step, 1e-4, 0.9, 0.999, 1e-8)
         pp, mm, vv = p.copy(), m.copy(), v.copy()
-        st, sh = _adam(pp, mm, vv, g, step, dtype, host_threads=threads)
+        st, sh = _adam(pp, mm, vv, g, step, dtype, shadow_offset=offset, host_threads=threads)
         assert st == 0
         np.testing.assert_array_equal(mm, rm)
         np.testing.assert_array_equal(vv, rv)
