@@ -182,6 +182,15 @@ mt_status mt_op_ce_rows(const float* logits, const int32_t* target, void* dlogit
   return MT_OK;
 }
 
+mt_status mt_op_nonfinite_flags(const void* g, size_t bytes, int32_t f32, int32_t* flags,
+                                void* stream) {
+  MT_CHECK(g && flags, MT_E_INVALID, "mt_op_nonfinite_flags: null pointer");
+  MT_CHECK(bytes % 16 == 0 && (f32 == 0 || f32 == 1), MT_E_INVALID,
+           "mt_op_nonfinite_flags: bytes must be a multiple of 16, f32 0 or 1");
+  MT_HIP(nonfinite_flags(g, bytes, f32, flags, static_cast<hipStream_t>(stream)));
+  return MT_OK;
+}
+
 mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t blocks,
                          void* stream) {
   MT_CHECK(src && dst_host, MT_E_INVALID, "mt_op_copy_d2h: null pointer");

@@ -303,6 +303,31 @@ __global__ void copy_rows_kernel(const uint16_t* __restrict__ src, long lds,
       *reinterpret_cast<const u32x4_t*>(src + r * lds + c * 8);
 }
 
+// One flag per workgroup: any Inf/NaN in its strided share of the buffer
+// (bf16: exponent bits all ones; fp32 likewise), OR-reduced over the
+// workgroup through LDS.
+__global__ __launch_bounds__(256) void nonfinite_kernel(const u32x4_t* __restrict__ g, size_t n16,
+                                                        int f32, int32_t* __restrict__ flags) {
+  __shared__ int any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  uint32_t bad = 0;
+  const uint32_t em = f32 ? 0x7F800000u : 0x7F807F80u;  // exponent masks per dword
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const u32x4_t v = g[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = v[k] & em;
+      if (f32) bad |= (x == 0x7F800000u);
+      else bad |= ((x & 0xFFFFu) == 0x7F80u) | ((x >> 16) == 0x7F80u);
+    }
+  }
+  if (bad) any = 1;  // benign race: every writer stores 1
+  __syncthreads();
+  if (threadIdx.x == 0) flags[blockIdx.x] = any;
+}
+
 // Device -> pinned host copy with a bounded footprint: `blocks` workgroups
 // stride over 16-byte chunks, so the copy occupies a few CUs instead of the
 // whole chip.  The host buffer must be device-accessible pinned memory.
@@ -404,6 +429,13 @@ hipError_t cast_t(const float* in, E* out, size_t n, hipStream_t s) {
 }  // namespace
 
 int rmsnorm_bwd_blocks(int rows) { return (rows + RB_ROWS - 1) / RB_ROWS; }
+
+hipError_t nonfinite_flags(const void* g, size_t bytes, int f32, int32_t* flags, hipStream_t s) {
+  if (bytes & 15) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(nonfinite_kernel, dim3(NONFINITE_BLOCKS), dim3(256), 0, s,
+                     static_cast<const u32x4_t*>(g), bytes / 16, f32, flags);
+  return hipGetLastError();
+}
 
 hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int rows,
                        int cols, float eps, hipStream_t s) {

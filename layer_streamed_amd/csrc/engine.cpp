@@ -99,7 +99,7 @@ Plan build_plan(int L, int K, int depth, int n_slots, bool keep) {
 
 namespace {
 
-constexpr int NG = 4;  // device gradient ring depth
+constexpr int NG = 6;  // device gradient ring depth
 
 // Device buffers of one step.  Weight slots, gradient buffers and
 // activations hold the model's streamed element type (es bytes each).
@@ -113,6 +113,7 @@ struct Arena {
   std::vector<char*> keep;  // kept internals, one per layer of a segment
   size_t keep_bytes = 0;
   char* dy = nullptr;
+  int32_t* flags = nullptr;  // [NG + 1][NONFINITE_BLOCKS]: ring slots, then the head
   int32_t* tgt = nullptr;
   float* loss = nullptr;
   void* lws = nullptr;
@@ -147,6 +148,7 @@ Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
     for (int i = 0; i < K; ++i) a.keep.push_back(c.take<char>(a.keep_bytes));
   }
   a.dy = c.take<char>(act);
+  a.flags = c.take<int32_t>((size_t)(NG + 1) * NONFINITE_BLOCKS);
   a.tgt = c.take<int32_t>(d.D);
   a.loss = c.take<float>(64);
   a.lws_bytes = layer_ws_bytes(d, 1);
@@ -211,6 +213,7 @@ struct Offload {
   int unit;          // -1 = dx0
   const char* src;
   size_t elems;
+  const int32_t* dflags;  // device finiteness flags of the gradient (or null)
   hipEvent_t after;  // compute event the copy waits for
   int ring;          // gradient ring index or -1
   bool end = false;
@@ -359,6 +362,10 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     M->dx0_host = M->host_alloc(nt * d.H * M->es, true);
     M->tgt_host = static_cast<int32_t*>(M->host_alloc(nt * 4, true));
     M->loss_host = static_cast<float*>(M->host_alloc(64, true));
+    if (!M->flags_host)
+      M->flags_host = static_cast<int32_t*>(
+          M->host_alloc((size_t)(L + 1) * NONFINITE_BLOCKS * 4, true));
+    MT_CHECK(M->flags_host, MT_E_OOM_HOST, "mt_stream_step: pinned flag allocation failed");
     MT_CHECK(M->x0_host && M->dx0_host && M->tgt_host && M->loss_host, MT_E_OOM_HOST,
              "mt_stream_step: pinned staging allocation failed");
     M->staging_tokens = nt;
@@ -384,6 +391,14 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   // the previous step's embedding update, for the rows this batch gathers
   // (the other rows follow on the optimizer thread during the forward)
   apply_pending_embed_rows(M, tokens, (size_t)d.D);
+  // the embedding rows this batch touches: its gradient is zero elsewhere
+  std::vector<int32_t> rows_now;
+  std::vector<uint8_t> touched((size_t)d.V, 0);
+  for (int i = 0; i < d.D; ++i)
+    if (!touched[tokens[i]]) {
+      touched[tokens[i]] = 1;
+      rows_now.push_back(tokens[i]);
+    }
   const bool defer = M->run.defer_updates != 0;
   // host: targets and the embedding gather (from the streamed copy)
   const Unit& emb = M->units[L + 1];
@@ -469,6 +484,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       if (ok) {
         const auto t0 = clock::now();
         ok = M->sdma->copy_d2h(host, o.src, o.elems * es);
+        if (ok && o.dflags)
+          ok = M->sdma->copy_d2h(M->flags_host + (size_t)o.unit * NONFINITE_BLOCKS, o.dflags,
+                                 NONFINITE_BLOCKS * 4);
         d2h_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
         d2h_bytes += (double)o.elems * es;
       }
@@ -504,10 +522,16 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       apply_pending_embed_rest(M);
       adam_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
     }
-    // zero the embedding gradient while the GPU runs the forward
+    // clear the rows the previous step scattered into (dE is zero elsewhere)
     float* dE = M->dE;
-    M->pool->parallel_for((size_t)d.V * d.H,
-                          [&](size_t lo, size_t hi) { memset(dE + lo, 0, (hi - lo) * 4); });
+    {
+      const std::vector<int32_t>& prev = M->dE_rows;
+      const size_t H = (size_t)d.H;
+      M->pool->parallel_for(prev.size(), [&](size_t lo, size_t hi) {
+        for (size_t i = lo; i < hi; ++i) memset(dE + (size_t)prev[i] * H, 0, H * 4);
+      }, 64);
+      M->dE_rows = rows_now;
+    }
     bool checked = false;
     bool skip = false;
     for (;;) {
@@ -534,7 +558,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           Unit& u = M->units[x.unit];
           const uint16_t* gb = f32 ? nullptr : static_cast<const uint16_t*>(x.host);
           const float* gf = f32 ? static_cast<const float*>(x.host) : nullptr;
-          if (M->run.check_finite && !grad_finite(gb, gf, u.n, M->pool.get())) {
+          const int32_t* fl = M->flags_host + (size_t)x.unit * NONFINITE_BLOCKS;
+          bool bad = false;
+          for (int k = 0; k < NONFINITE_BLOCKS && M->run.check_finite; ++k) bad |= fl[k] != 0;
+          (void)gb;
+          (void)gf;
+          if (bad) {
             a_fail = 2;
             abort_all = true;
             skip = true;
@@ -559,22 +588,34 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           else
             embed_scatter_add(static_cast<const uint16_t*>(x.host), tokens, (size_t)d.D,
                               (size_t)d.H, dE, M->pool.get());
-          if (M->run.check_finite && !grad_finite(nullptr, dE, (size_t)d.V * d.H, M->pool.get())) {
+          // only the batch's rows of dE can be nonzero, hence non-finite
+          bool bad = false;
+          if (M->run.check_finite) {
+            std::atomic<bool> any{false};
+            const size_t H = (size_t)d.H;
+            M->pool->parallel_for(rows_now.size(), [&](size_t lo, size_t hi) {
+              for (size_t i = lo; i < hi && !any.load(std::memory_order_relaxed); ++i)
+                if (!grad_finite(nullptr, dE + (size_t)rows_now[i] * H, H, nullptr)) any = true;
+            }, 64);
+            bad = any.load();
+          }
+          (void)u;
+          if (bad) {
             a_fail = 2;
             abort_all = true;
             skip = true;
-          } else if (defer) {
-            // the embedding's update waits for the next step (PendingAdam)
+          } else {
+            // the update of every row (untouched rows with a zero gradient)
             M->pending.embed = true;
             M->pending.hp_embed = hp;
             M->pending.row_done.assign((size_t)d.V, 0);
-            ++units_deferred;
-          } else {
-            adam_parallel(u.master, u.m, u.v, nullptr, dE,
-                          f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
-                          f32 ? static_cast<float*>(u.shadow) : nullptr, (size_t)d.V * d.H, hp,
-                          M->pool.get());
-            ++units_updated;
+            M->pending.touched = touched;
+            if (defer) {
+              ++units_deferred;  // applied by the next step (PendingAdam)
+            } else {
+              apply_pending_embed_rest(M);
+              ++units_updated;
+            }
           }
         }
       }
@@ -674,8 +715,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         }
         loss_cv.notify_all();
         MT_STEP_HIP(hipEventRecord(ph_head, sC));
+        int32_t* hf = A.flags + (size_t)NG * NONFINITE_BLOCKS;
+        if (M->run.check_finite)
+          MT_STEP_HIP(nonfinite_flags(A.head_grad, M->hl.total * es, f32, hf, sC));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
-        offq.push(Offload{L, A.head_grad, M->hl.total, op_done[i], -1});
+        offq.push(Offload{L, A.head_grad, M->hl.total, M->run.check_finite ? hf : nullptr,
+                          op_done[i], -1});
         continue;
       } else if (op.kind == OP_REFWD) {
         const int l = op.layer, a = (l / K) * K;
@@ -710,8 +755,11 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
                                      A.lws, A.lws_bytes, sC,
                                      M->run.time_kernels ? &probe : nullptr));
+        int32_t* lf = A.flags + (size_t)r * NONFINITE_BLOCKS;
+        if (M->run.check_finite)
+          MT_STEP_HIP(nonfinite_flags(A.gring[r], M->ll.total * es, f32, lf, sC));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
-        Offload o{l, A.gring[r], M->ll.total, op_done[i], r};
+        Offload o{l, A.gring[r], M->ll.total, M->run.check_finite ? lf : nullptr, op_done[i], r};
         offq.push(o);
         ++bwd_count;
         if (l == 0) MT_STEP_HIP(hipEventRecord(ph_end, sC));
@@ -720,7 +768,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       MT_STEP_HIP(hipEventRecord(op_done[i], sC));
     }
     // dx0 = gradient of the embedding output
-    offq.push(Offload{-1, A.dy, act, ph_end, -1});
+    offq.push(Offload{-1, A.dy, act, nullptr, ph_end, -1});
   }
 drain:
   if (fail != MT_OK) {
@@ -729,7 +777,7 @@ drain:
     loss_ready = true;
     loss_cv.notify_all();
   }
-  offq.push(Offload{0, nullptr, 0, nullptr, -1, true});
+  offq.push(Offload{0, nullptr, 0, nullptr, nullptr, -1, true});
   if (gthr.joinable()) gthr.join();
   if (athr.joinable()) athr.join();
   const hipError_t e1 = hipStreamSynchronize(sW), e2 = hipStreamSynchronize(sC),

@@ -93,11 +93,14 @@ void embed_rows(mt_model* M, const std::vector<int32_t>* rows) {
       const size_t r = rows ? (size_t)(*rows)[i] : i;
       if (pa.row_done[r]) continue;
       const size_t a = r * H;
+      // an untouched row's gradient is zero: read a cached zero row instead
+      // of the row of dE (the same values, so the same result)
+      const float* g = pa.touched[r] ? M->dE + a : M->zero_row;
       if (f32)
-        adam_range(u.master + a, u.m + a, u.v + a, nullptr, M->dE + a, nullptr,
+        adam_range(u.master + a, u.m + a, u.v + a, nullptr, g, nullptr,
                    static_cast<float*>(u.shadow) + a, 0, H, pa.hp_embed);
       else
-        adam_range(u.master + a, u.m + a, u.v + a, nullptr, M->dE + a,
+        adam_range(u.master + a, u.m + a, u.v + a, nullptr, g,
                    static_cast<uint16_t*>(u.shadow) + a, nullptr, 0, H, pa.hp_embed);
       pa.row_done[r] = 1;
     }
@@ -230,7 +233,15 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
     });
   }
   m->dE = static_cast<float*>(m->host_alloc((size_t)d.V * d.H * 4, false));
-  if (!m->dE) return set_error(MT_E_OOM_HOST, "mt_model_create: embedding gradient allocation failed");
+  m->zero_row = static_cast<float*>(m->host_alloc((size_t)d.H * 4, false));
+  if (!m->dE || !m->zero_row)
+    return set_error(MT_E_OOM_HOST, "mt_model_create: embedding gradient allocation failed");
+  {
+    float* dE = m->dE;
+    m->pool->parallel_for((size_t)d.V * d.H,
+                          [&](size_t lo, size_t hi) { memset(dE + lo, 0, (hi - lo) * 4); });
+    memset(m->zero_row, 0, (size_t)d.H * 4);
+  }
 
   // gradient slab pool: each slab fits the largest streamed unit
   m->slab_elems = std::max(m->ll.total, m->hl.total);

@@ -66,6 +66,7 @@ struct PendingAdam {
   // of the step when the pool is small)
   void* head_grad = nullptr;
   std::vector<uint8_t> row_done;  // embedding rows already updated
+  std::vector<uint8_t> touched;   // embedding rows with a nonzero gradient row in dE
 };
 
 struct HostBlock {  // one host allocation
@@ -89,7 +90,10 @@ struct mt_model {
   mt::SlabPool slabs;
   std::vector<void*> slab_list;
   std::unique_ptr<mt::ThreadPool> pool;
-  float* dE = nullptr;          // fp32 embedding gradient [V, H]
+  float* dE = nullptr;          // fp32 embedding gradient [V, H]; zero outside dE_rows
+  std::vector<int32_t> dE_rows; // rows the last step scattered into dE
+  float* zero_row = nullptr;    // H zeros: the gradient row of an untouched embedding row
+  int32_t* flags_host = nullptr;  // pinned, (n_layers + 1) x NONFINITE_BLOCKS per-unit flags
   // pinned per-step staging, grown on demand
   void* x0_host = nullptr;
   void* dx0_host = nullptr;

@@ -124,6 +124,7 @@ _SIGS = {
     "mt_layer_fwd_keep": (_I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
     "mt_layer_bwd_saved": (_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P, _SZ, _P),
     "mt_op_copy_d2h": (_I32, _P, _P, _SZ, _I32, _P),
+    "mt_op_nonfinite_flags": (_I32, _P, _SZ, _I32, _P, _P),
 }
 FN = {}
 for _name, (_res, *_args) in _SIGS.items():

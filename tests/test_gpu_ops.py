@@ -443,3 +443,25 @@ def test_attention_f32_forward_backward(B, T, Hq, Hkv, d):
     assert err(out[:, : Hq * d], dq.reshape(B * T, -1)) < F32_TOL
     assert err(out[:, Hq * d:(Hq + Hkv) * d], dk.reshape(B * T, -1)) < F32_TOL
     assert err(out[:, (Hq + Hkv) * d:], dv.reshape(B * T, -1)) < F32_TOL
+
+
+@pytest.mark.parametrize("f32", [0, 1])
+def test_nonfinite_flags(f32):
+    """The engine's GPU finiteness check: clean buffers give all-zero flags;
+    an Inf or a NaN anywhere (first, last, middle element) sets a flag."""
+    torch, mt = _torch(), _mt()
+    dt = torch.float32 if f32 else torch.bfloat16
+    n = 1_000_008  # elements; bytes a multiple of 16
+    flags = torch.empty(256, dtype=torch.int32, device="cuda")
+    g = (torch.randn(n, device="cuda") * 1e3).to(dt)
+    nbytes = n * g.element_size()
+    assert mt.call("mt_op_nonfinite_flags", g.data_ptr(), nbytes, f32, flags.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert int(flags.sum()) == 0
+    for pos, val in ((0, float("inf")), (n - 1, float("nan")), (n // 2 + 3, float("-inf"))):
+        h = g.clone()
+        h[pos] = val
+        assert mt.call("mt_op_nonfinite_flags", h.data_ptr(), nbytes, f32, flags.data_ptr(),
+                       None) == 0
+        torch.cuda.synchronize()
+        assert int(flags.sum()) == 1, (pos, val)
