@@ -118,7 +118,8 @@ mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t 
 /* The stream schedule of mt_stream_step for n_layers, checkpoint interval,
  * prefetch depth and kept internals (mt_run_cfg.keep_internals), as plain integers so its hazards can be checked
  * without a GPU.  out receives, per compute op, (kind, layer, load) with
- * kind 0 forward, 1 head, 2 segment re-forward, 3 recompute+backward; then,
+ * kind 0 forward, 1 head, 2 segment re-forward, 3 (recompute+)backward, 4
+ * forward keeping internals (the last segment, with keep_internals); then,
  * per weight load, (unit, slot, first_use, last_use, wait_use, gate_use):
  * the load may start once compute ops wait_use and gate_use have finished
  * (-1: no wait); slot -2 is the head's own slot.  counts = {n_ops, n_loads,

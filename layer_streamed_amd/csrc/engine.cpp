@@ -13,8 +13,10 @@
 // the segments from the last: re-forward the segment's layers from its
 // checkpoint to rebuild their inputs, then backward each layer in reverse.
 // With kept internals the re-forward runs all K layers of the segment and
-// keeps what their backward needs (no second forward per layer); without,
-// it runs the first K-1 and each backward recomputes its layer's forward.  A weight slot is reused only after the last compute
+// keeps what their backward needs (no second forward per layer), and the
+// last segment keeps them in the forward itself (no re-forward at all);
+// without, the re-forward runs the first K-1 and each backward recomputes
+// its layer's forward.  A weight slot is reused only after the last compute
 // op that reads it has finished, and a load may run at most `depth` compute
 // ops ahead of its first use (depth 2 = double buffering).
 #include <math.h>
@@ -39,7 +41,9 @@
 
 namespace mt {
 
-enum OpKind { OP_FWD = 0, OP_HEAD = 1, OP_REFWD = 2, OP_BWD = 3 };
+// OP_FWDK: forward of a layer of the last segment that keeps its internals
+// (that segment's re-forward coincides with the forward itself).
+enum OpKind { OP_FWD = 0, OP_HEAD = 1, OP_REFWD = 2, OP_BWD = 3, OP_FWDK = 4 };
 struct PlanOp {
   int kind, layer, load;
 };
@@ -69,10 +73,21 @@ Plan build_plan(int L, int K, int depth, int n_slots, bool keep) {
     if (ld.first_use < 0) ld.first_use = i;
     ld.last_use = i;
   };
-  for (int l = 0; l < L; ++l) add_op(OP_FWD, l, add_load(l));
+  // with kept internals, the last segment's layers keep them already in the
+  // forward, and their backward reuses the forward's weight loads
+  const int a_last = ((L - 1) / K) * K;
+  std::vector<int> fwd_load(L);
+  for (int l = 0; l < L; ++l) {
+    fwd_load[l] = add_load(l);
+    add_op(keep && l >= a_last ? OP_FWDK : OP_FWD, l, fwd_load[l]);
+  }
   add_op(OP_HEAD, -1, add_load(L));
-  for (int a = ((L - 1) / K) * K; a >= 0; a -= K) {
+  for (int a = a_last; a >= 0; a -= K) {
     const int e = std::min(a + K, L);
+    if (keep && a == a_last) {
+      for (int l = e - 1; l >= a; --l) add_op(OP_BWD, l, fwd_load[l]);
+      continue;
+    }
     std::vector<int> ld(e - a);
     for (int l = a; l < e; ++l) ld[l - a] = add_load(l);
     for (int l = a; l < (keep ? e : e - 1); ++l) add_op(OP_REFWD, l, ld[l - a]);
@@ -697,7 +712,16 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       MT_STEP_HIP(hipStreamWaitEvent(sC, load_done[op.load], 0));
       MT_STEP_HIP(hipEventRecord(w1, sC));
       (op.kind == OP_BWD ? wait_ev_b : wait_ev_f).push_back({w0, w1});
-      if (op.kind == OP_FWD) {
+      if (op.kind == OP_FWDK) {
+        // the last segment: inputs land in the segment buffers the backward
+        // reads, the last layer's output where the head reads it
+        const int l = op.layer, a = (l / K) * K;
+        const char* in = l == a ? A.ckpt[a / K] : A.seg[l - a - 1];
+        char* out = l == L - 1 ? xloc(L) : A.seg[l - a];
+        MT_STEP_RUN(layer_fwd_keep_impl(d, layer_view(M, w), in, out, A.keep[l - a],
+                                        A.keep_bytes, sC, M->run.time_kernels ? &probe : nullptr));
+        if (l == L - 1) MT_STEP_HIP(hipEventRecord(ph_fwd, sC));
+      } else if (op.kind == OP_FWD) {
         const int l = op.layer;
         MT_STEP_RUN(layer_fwd_impl(d, layer_view(M, w), xloc(l), xloc(l + 1), A.lws, A.lws_bytes,
                                    sC, M->run.time_kernels ? &probe : nullptr));

@@ -9,7 +9,7 @@ deadlock), and no load runs more than `depth` ops ahead.
 """
 import pytest
 
-FWD, HEAD, REFWD, BWD = 0, 1, 2, 3
+FWD, HEAD, REFWD, BWD, FWDK = 0, 1, 2, 3, 4
 
 
 def _plan(L, K, depth, keep=1):
@@ -27,19 +27,28 @@ def test_plan_is_hazard_free(L, K, depth, keep):
     st, ops, loads, n_slots = _plan(L, K, depth, keep)
     assert st == 0
     kinds = ops[:, 0].tolist()
-    # forward of every layer in order, then the head
-    assert kinds[:L] == [FWD] * L and ops[:L, 1].tolist() == list(range(L))
+    a_last = ((L - 1) // K) * K
+    # forward of every layer in order (the last segment keeping its
+    # internals when internals are kept), then the head
+    assert kinds[:L] == [FWDK if keep and l >= a_last else FWD for l in range(L)]
+    assert ops[:L, 1].tolist() == list(range(L))
     assert kinds[L] == HEAD
     # backward: segments from the last, each re-forwarding from the
     # checkpoint (every layer when internals are kept, else all but the
-    # last), then backward in reverse
+    # last; nothing for the last segment when it kept them in the forward),
+    # then backward in reverse
     rest = ops[L + 1:]
     expect = []
     for a in reversed(range(0, L, K)):
         e = min(a + K, L)
-        expect += [(REFWD, l) for l in range(a, e if keep else e - 1)]
+        if not (keep and a == a_last):
+            expect += [(REFWD, l) for l in range(a, e if keep else e - 1)]
         expect += [(BWD, l) for l in reversed(range(a, e))]
     assert [(int(k), int(l)) for k, l, _ in rest] == expect
+    if keep:  # the last segment's backward reads the forward's loads
+        for k, l, ld in ops[L + 1:]:
+            if k == BWD and l >= a_last:
+                assert ld == ops[l][2]
     # every op reads a load of its own unit, inside that load's live range
     for i, (kind, layer, load) in enumerate(ops):
         unit, slot, first, last, wait, gate = loads[load]
@@ -84,13 +93,16 @@ def test_plan_single_stream_replay_never_reads_stale_weights(keep):
 
 
 def test_plan_counts_match_the_method():
-    """Per step: L forward loads + head + L backward loads; the forward uses
-    each layer once, backward once; the re-forward covers (K-1)/K of the
-    layers (each backward then recomputes its layer) or, with kept
-    internals, every layer (and no backward recomputes)."""
+    """Per step: L forward loads + head + backward loads; the forward uses
+    each layer once, backward once.  Without kept internals the re-forward
+    covers (K-1)/K of the layers (each backward then recomputes its layer)
+    and every backward loads its weights again; with them, the re-forward
+    covers every layer but the last segment's, which kept its internals in
+    the forward and whose backward reuses the forward's weight loads."""
     L, K = 28, 4
-    for keep, refwd in ((0, L - L // K), (1, L)):
+    for keep, refwd, n_loads in ((0, L - L // K, 2 * L + 1), (1, L - K, 2 * L + 1 - K)):
         st, ops, loads, _ = _plan(L, K, 2, keep)
-        assert len(loads) == 2 * L + 1
+        assert len(loads) == n_loads
         assert (ops[:, 0] == REFWD).sum() == refwd
         assert (ops[:, 0] == BWD).sum() == L
+        assert (ops[:, 0] == FWDK).sum() == (K if keep else 0)
