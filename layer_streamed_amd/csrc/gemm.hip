@@ -357,17 +357,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Products with direct global -> LDS loads (gfx950 global_load_lds_dwordx4):
 // lane t of a wave instruction writes its 16-byte chunk to LDS base + 16 t,
-// so no operand passes through registers on its way in.  A ring of
-// DL_STAGES stages of DL_BK k-values keeps three stages of loads in flight
-// while one is computed: the load latency is covered by LDS capacity instead
-// of registers.
+// so no operand passes through registers on its way in.  A ring of NS
+// stages of BK k-values keeps NS - 1 stages of loads in flight while one is
+// computed: the load latency is covered by LDS capacity instead of
+// registers.  Two shapes of the 128 KiB ring are used: 4 stages of 32 k and
+// 2 stages of 64 k (half the stage barriers; the better one per layout was
+// measured on the 7B layer shapes, see launch_layout).
 //
 // Each operand keeps its global layout in LDS:
-//  - K-contiguous (NT's A and B, NN's A): a stage is BM rows of DL_BK k, 4
-//    chunks of 8 per row stored in the order c ^ ((row >> 2) & 3); a
-//    fragment (8 consecutive k of one row per lane) is one ds_read_b128, and
-//    32 lanes reading 32 consecutive rows hit distinct banks.
-//  - K-major (NN's B, TN's A and B): a stage is DL_BK rows of k, each BM
+//  - K-contiguous (NT's A and B, NN's A): a stage is BM rows of BK k, BK / 8
+//    chunks of 8 per row stored in the order c ^ ((row >> 2) & (BK / 8 - 1));
+//    a fragment (8 consecutive k of one row per lane) is one ds_read_b128,
+//    and 32 lanes reading 32 consecutive rows hit distinct banks.
+//  - K-major (NN's B, TN's A and B): a stage is BK rows of k, each BM
 //    values of m wide (BM / 8 chunks) stored in the order c ^ km_swz(k).
 //    A fragment is read with two ds_read_b64_tr_b16 (gfx950 LDS transpose
 //    read): within each group of 16 lanes, lane i receives element i & 3 of
@@ -379,11 +381,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
 //    4 rows x 4 chunks; the XOR patterns {0, 6, 10, 12} of km_swz differ in
 //    bits 1-2 and in bits 2-3, so both sets land on distinct banks.
 // Both give each lane k-slots 8 (l / 32) .. + 7 in natural order, so the
-// operand kinds mix freely.  Requires K % DL_BK == 0 and, for K-major
+// operand kinds mix freely.  Requires K % BK == 0 and, for K-major
 // operands, M or N % 8 == 0; rows or columns past M or N are clamped to a
 // valid one (they only feed output elements the epilogue drops).
-constexpr int DL_BK = 32;
-constexpr int DL_STAGES = 4;
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -397,11 +397,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Global source of one LDS slot of an operand stage (k0 = 0) and the
 // per-stage advance, for a tile whose first row (K-contiguous) or column
 // (K-major) is r0 of an extent of `ext`.
-template <bool KM, int BR>
+template <bool KM, int BR, int BK>
 __device__ __forceinline__ const uint16_t* dl_src(const uint16_t* base, long ld, int pos, int r0,
                                                    int ext, int swi_f) {
   if constexpr (!KM) {
-    constexpr int CH = DL_BK / 8;
+    constexpr int CH = BK / 8;
     const int row = pos / CH, slot = pos % CH;
     const int c = slot ^ ((row >> 2) & (CH - 1));
     int gr = min(r0 + row, ext - 1);
@@ -418,10 +418,10 @@ __device__ __forceinline__ const uint16_t* dl_src(const uint16_t* base, long ld,
 
 // Fragment of rows (K-contiguous) or columns (K-major) rb .. rb + 31 for
 // k-substep ks of a stage starting at `st`.
-template <bool KM, int BR>
+template <bool KM, int BR, int BK>
 __device__ __forceinline__ u32x4_t dl_frag(const char* st, int rb, int ks, int lane) {
   if constexpr (!KM) {
-    constexpr int CH = DL_BK / 8;
+    constexpr int CH = BK / 8;
     const int r = rb + (lane & 31);
     const int c = ks * 2 + (lane >> 5);
     return reinterpret_cast<const u32x4_t*>(st)[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
@@ -602,11 +602,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, f32x16_t (&acc)[
   }
 }
 
-template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI>
+template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI, int BK, int NS>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) {
+  static_assert(BK % 16 == 0 && BK <= 64 && NS >= 2 && NS <= 4, "stage shape");
   constexpr bool A_KM = LAYOUT == GEMM_TN, B_KM = LAYOUT != GEMM_NT;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NW = WM * WN;
-  constexpr int A_CH = BM * DL_BK / 8, B_CH = BN * DL_BK / 8;  // 16-byte chunks per stage
+  constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;  // 16-byte chunks per stage
   constexpr int A_PER = A_CH / 64 / NW, B_PER = B_CH / 64 / NW;  // instructions per wave
   static_assert(A_PER * 64 * NW == A_CH && B_PER * 64 * NW == B_CH, "tile/wave mismatch");
   static_assert(!A_KM || BM >= 128, "K-major swizzle needs 16 chunks per row");
@@ -636,13 +637,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
   const uint16_t* gb[B_PER];
 #pragma unroll
   for (int p = 0; p < A_PER; ++p)
-    ga[p] = dl_src<A_KM, BM>(a.A, a.lda, (wave * A_PER + p) * 64 + lane, m0, M, 0);
+    ga[p] = dl_src<A_KM, BM, BK>(a.A, a.lda, (wave * A_PER + p) * 64 + lane, m0, M, 0);
 #pragma unroll
   for (int p = 0; p < B_PER; ++p)
-    gb[p] = dl_src<B_KM, BN>(a.B, a.ldb, (wave * B_PER + p) * 64 + lane, n0, N, SWI ? a.F : 0);
+    gb[p] = dl_src<B_KM, BN, BK>(a.B, a.ldb, (wave * B_PER + p) * 64 + lane, n0, N, SWI ? a.F : 0);
   // per-stage advance along K
-  const long a_step = A_KM ? (long)DL_BK * a.lda : DL_BK;
-  const long b_step = B_KM ? (long)DL_BK * a.ldb : DL_BK;
+  const long a_step = A_KM ? (long)BK * a.lda : BK;
+  const long b_step = B_KM ? (long)BK * a.ldb : BK;
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -652,10 +653,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = K / DL_BK;
+  const int nk = K / BK;
   auto issue = [&](int kt) {
     if (kt >= nk) return;
-    char* base = dl_smem + (kt % DL_STAGES) * STAGE;
+    char* base = dl_smem + (kt % NS) * STAGE;
 #pragma unroll
     for (int p = 0; p < A_PER; ++p)
       __builtin_amdgcn_global_load_lds(
@@ -670,15 +671,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
   };
 
   auto compute = [&](int kt) {
-    const char* sA = dl_smem + (kt % DL_STAGES) * STAGE;
+    const char* sA = dl_smem + (kt % NS) * STAGE;
     const char* sB = sA + A_CH * 16;
 #pragma unroll
-    for (int ks = 0; ks < DL_BK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
       u32x4_t af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = dl_frag<A_KM, BM>(sA, wm * TM * 32 + i * 32, ks, lane);
+      for (int i = 0; i < TM; ++i) af[i] = dl_frag<A_KM, BM, BK>(sA, wm * TM * 32 + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = dl_frag<B_KM, BN>(sB, wn * TN * 32 + j * 32, ks, lane);
+      for (int j = 0; j < TN; ++j) bfr[j] = dl_frag<B_KM, BN, BK>(sB, wn * TN * 32 + j * 32, ks, lane);
       if constexpr (A_KM || B_KM) {
         // the transpose reads were issued as asm, outside the compiler's
         // wait tracking: wait for them, and tie every fragment to the wait
@@ -697,17 +698,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
   };
 
 #pragma unroll
-  for (int st = 0; st < DL_STAGES - 1; ++st) issue(st);
+  for (int st = 0; st < NS - 1; ++st) issue(st);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads for stage kt are done once at most `ahead` later
     // stages are still in flight; the barrier then covers every wave's loads
     // and every wave's reads of the stage about to be refilled
-    const int ahead = min(DL_STAGES - 2, nk - 1 - kt);
+    const int ahead = min(NS - 2, nk - 1 - kt);
     if (ahead >= 2) wait_vmcnt<2 * LPW>();
     else if (ahead == 1) wait_vmcnt<LPW>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    issue(kt + DL_STAGES - 1);
+    issue(kt + NS - 1);
     compute(kt);
   }
   // the ring is free once every wave has finished reading its last stage
@@ -728,15 +729,15 @@ inline bool epi_vec_ok(const GemmArgs& a) {
   return ok;
 }
 
-template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI>
+template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI, int BK, int NS>
 hipError_t launch_dl(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
-  constexpr size_t ring = (size_t)DL_STAGES * (BM + BN) * (DL_BK / 8) * 16;
+  constexpr size_t ring = (size_t)NS * (BM + BN) * (BK / 8) * 16;
   constexpr size_t stage_out = (size_t)WM * WN * (SWI ? 2 : 1) * EPI_SLOT;
   static_assert(stage_out <= ring, "epilogue slots must fit in the ring");
   const size_t lds = ring;
-  auto kern = gemm_dl_kernel<LAYOUT, WM, WN, TM, TN, EPI>;
+  auto kern = gemm_dl_kernel<LAYOUT, WM, WN, TM, TN, EPI, BK, NS>;
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -771,10 +772,12 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 // Tile choice.  With K % 32 == 0 every layout takes the direct-to-LDS
 // kernel: 256 x 256 (eight waves of 128 x 64, two per SIMD, so one wave's
 // memory stalls hide behind the other's MFMAs) when the grid fills the 256
-// CUs at least four times over, else 256 x 128 (eight waves of 64 x 64) when
-// that does, else 128 x 128 (four waves of 64 x 64).  The SwiGLU-backward
-// epilogue keeps 128 x 128 (its extra live values would spill the larger
-// tiles' accumulators).  A ragged K takes the register-staged kernel.
+// CUs at least three times over (a partly filled last round still beats the
+// smaller tiles' lower rate per tile on every 7B layer shape measured), else
+// 256 x 128 (eight waves of 64 x 64) when it fills them four times over,
+// else 128 x 128 (four waves of 64 x 64).  A ragged K takes the
+// register-staged kernel, whose SwiGLU-backward epilogue keeps 128 x 128
+// (its extra live values would spill the larger tile's accumulators).
 inline long tiles_of(const GemmArgs& a, int bm, int bn) {
   return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
@@ -784,7 +787,7 @@ inline long tiles_of(const GemmArgs& a, int bm, int bn) {
 enum TileCfg { DL_256x256, DL_256x128, DL_128x128, RS_256x256, RS_128x128 };
 
 TileCfg choose_cfg(const GemmArgs& a) {
-  if (a.K % DL_BK == 0) {
+  if (a.K % 32 == 0) {
     if (tiles_of(a, 256, 256) >= 3 * 256) return DL_256x256;
     if (tiles_of(a, 256, 128) >= 4 * 256) return DL_256x128;
     return DL_128x128;
@@ -793,12 +796,26 @@ TileCfg choose_cfg(const GemmArgs& a) {
   return RS_128x128;
 }
 
+// Stage shape of the direct-to-LDS kernels: 2 stages of 64 k for NT (every
+// tile) and for TN's 256 x 256 tile when K allows, else 4 stages of 32 k
+// (NN, where the deeper ring measured faster, and the smaller TN tiles).
+inline bool deep_stages(const GemmArgs& a, int layout, TileCfg c) {
+  return a.K % 64 == 0 && (layout == GEMM_NT || (layout == GEMM_TN && c == DL_256x256));
+}
+
+template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI>
+hipError_t launch_dl_stages(const GemmArgs& a, TileCfg c, hipStream_t s) {
+  if (deep_stages(a, LAYOUT, c)) return launch_dl<LAYOUT, WM, WN, TM, TN, EPI, 64, 2>(a, s);
+  return launch_dl<LAYOUT, WM, WN, TM, TN, EPI, 32, 4>(a, s);
+}
+
 template <int LAYOUT, int EPI>
 hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
-  switch (choose_cfg(a)) {
-    case DL_256x256: return launch_dl<LAYOUT, 2, 4, 4, 2, EPI>(a, s);
-    case DL_256x128: return launch_dl<LAYOUT, 4, 2, 2, 2, EPI>(a, s);
-    case DL_128x128: return launch_dl<LAYOUT, 2, 2, 2, 2, EPI>(a, s);
+  const TileCfg c = choose_cfg(a);
+  switch (c) {
+    case DL_256x256: return launch_dl_stages<LAYOUT, 2, 4, 4, 2, EPI>(a, c, s);
+    case DL_256x128: return launch_dl_stages<LAYOUT, 4, 2, 2, 2, EPI>(a, c, s);
+    case DL_128x128: return launch_dl_stages<LAYOUT, 2, 2, 2, 2, EPI>(a, c, s);
     case RS_256x256:
       // the SwiGLU-backward epilogue would spill this tile's accumulators
       if constexpr (EPI != EPI_SWIGLU_BWD) return launch_cfg<2, 4, 4, 2, LAYOUT, EPI>(a, s);
@@ -865,10 +882,12 @@ std::string gemm_kernel_name(const GemmArgs& a) {
   // the demangled template name profilers report for the launch
   const int lay = (a.epi == EPI_SWIGLU || a.epi == EPI_SWIGLU_SAVE) ? GEMM_NT : a.layout;
   char buf[64];
-  switch (choose_cfg(a)) {
-    case DL_256x256: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 4, 4, 2, %d>", lay, a.epi); break;
-    case DL_256x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 4, 2, 2, 2, %d>", lay, a.epi); break;
-    case DL_128x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 2, 2, 2, %d>", lay, a.epi); break;
+  const TileCfg c = choose_cfg(a);
+  const char* st = deep_stages(a, lay, c) ? "64, 2" : "32, 4";
+  switch (c) {
+    case DL_256x256: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 4, 4, 2, %d, %s>", lay, a.epi, st); break;
+    case DL_256x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 4, 2, 2, 2, %d, %s>", lay, a.epi, st); break;
+    case DL_128x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 2, 2, 2, %d, %s>", lay, a.epi, st); break;
     case RS_256x256:
       if (a.epi != EPI_SWIGLU_BWD) {
         snprintf(buf, sizeof buf, "gemm_kernel<2, 4, 4, 2, %d, %d>", lay, a.epi);

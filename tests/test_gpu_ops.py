@@ -307,7 +307,11 @@ def test_attention_forward_32k_sampled_heads():
     (2, 3584, 18944, 3000, 0), (0, 16344, 4616, 3584, 0), (0, 9000, 30000, 2048, 0),
     # direct-to-LDS path with K-major operands: NN's B, TN's A and B, ragged
     # contiguous extents (clamped columns) and the fp32 accumulate epilogue
-    (1, 16380, 18936, 3584, 0), (2, 37880, 3592, 2048, 0), (2, 18944, 3584, 1024, 2)])
+    (1, 16380, 18936, 3584, 0), (2, 37880, 3592, 2048, 0), (2, 18944, 3584, 1024, 2),
+    # two stages of 64 k (NT, TN's 256 x 256 tile): the residual epilogue of
+    # the down projection with a ragged M, and TN with K % 64 == 32 (the
+    # 4-stage ring instead)
+    (0, 16380, 3584, 18944, 3), (2, 18944, 3584, 1056, 0)])
 def test_gemm_large_tiles_sampled(layout, M, N, K, epi):
     """Shapes of the 7B layer that take the 256 x 256 tile paths (ragged K on
     TN), plus ragged extents of the direct-to-LDS kernels."""
@@ -315,12 +319,16 @@ def test_gemm_large_tiles_sampled(layout, M, N, K, epi):
     g = torch.Generator(device="cuda").manual_seed(M + N)
     A = torch.randn((K, M) if layout == 2 else (M, K), device="cuda", generator=g).to(torch.bfloat16)
     B = torch.randn((N, K) if layout == 0 else (K, N), device="cuda", generator=g).to(torch.bfloat16)
+    R = None
     if epi == 2:
         Cm = torch.randn((M, N), device="cuda", generator=g)
         C0 = Cm.clone()
     else:
         Cm = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
-    mt.gemm(layout, epi, M, N, K, A, M if layout == 2 else K, B, K if layout == 0 else N, Cm, N)
+        if epi == 3:
+            R = torch.randn((M, N), device="cuda", generator=g).to(torch.bfloat16)
+    mt.gemm(layout, epi, M, N, K, A, M if layout == 2 else K, B, K if layout == 0 else N, Cm, N,
+            R=R, ldr=N)
     torch.cuda.synchronize()
     rows = np.concatenate([np.random.default_rng(1).choice(M, 14, replace=False), [0, M - 1]])
     a = (A[:, rows].t() if layout == 2 else A[rows]).float().cpu().numpy().astype(np.float64)
@@ -330,6 +338,8 @@ def test_gemm_large_tiles_sampled(layout, M, N, K, epi):
         ref = ref + C0[rows].cpu().numpy()
         assert rel_fro(Cm[rows].cpu().numpy(), ref) < 1e-5
     else:
+        if epi == 3:
+            ref = ref + R[rows].float().cpu().numpy()
         assert rel_fro(Cm[rows].float().cpu().numpy(), ref) < 5e-3
     # the last column too (clamped chunks of a ragged contiguous extent)
     assert np.isfinite(Cm[rows].float().cpu().numpy()).all()
