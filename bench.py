@@ -193,7 +193,9 @@ def main():
             f"tail {st['tail_ms']:.0f} adam {st['adam_ms']:.0f} exposed "
             f"{st['exposed_wait_fwd_ms']:.0f}/{st['exposed_wait_bwd_ms']:.0f} ms; host waits "
             f"ring {st['host_ring_wait_ms']:.0f} slab {st['host_slab_wait_ms']:.0f} "
-            f"op {st['host_op_wait_ms']:.0f} adam-idle {st['host_adam_idle_ms']:.0f} ms")
+            f"op {st['host_op_wait_ms']:.0f} adam-idle {st['host_adam_idle_ms']:.0f} ms; "
+            f"at {st['host_start_ms']:.0f} start, {st['gpu_done_ms']:.0f} gpu done, "
+            f"{st['grads_landed_ms']:.0f} grads landed, {st['updates_done_ms']:.0f} updates done")
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = 1e3 * elapsed / args.steps
@@ -280,7 +282,8 @@ def main():
         "phases_ms": {k: round(float(np.mean([s[k] for s in stats])), 2) for k in
                       ("fwd_ms", "head_ms", "bwd_ms", "tail_ms", "adam_ms",
                        "exposed_wait_fwd_ms", "exposed_wait_bwd_ms", "host_ring_wait_ms",
-                       "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms")},
+                       "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms",
+                       "host_start_ms", "gpu_done_ms", "grads_landed_ms", "updates_done_ms")},
         "link": {"h2d_bytes": h2d, "d2h_bytes": d2h,
                  "h2d_GBps_while_copying": round(h2d / max(h2d_ms, 1e-9) / 1e6, 2),
                  "d2h_GBps_while_copying": round(d2h / max(d2h_ms, 1e-9) / 1e6, 2),

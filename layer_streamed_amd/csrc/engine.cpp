@@ -434,6 +434,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   double adam_ms = 0.0;
   double d2h_ms = 0, d2h_bytes = 0;
   double ring_wait_ms = 0, slab_wait_ms = 0, op_wait_ms = 0, adam_idle_ms = 0;
+  double host_start_ms = 0, gpu_done_ms = 0, grads_landed_ms = 0, updates_done_ms = 0;
   auto ms_since = [](clock::time_point t) {
     return std::chrono::duration<double, std::milli>(clock::now() - t).count();
   };
@@ -450,9 +451,15 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   Probe probe;
   hipEvent_t ph_start = nullptr, ph_fwd = nullptr, ph_head = nullptr, ph_end = nullptr;
   std::vector<hipEvent_t> op_done(plan.ops.size(), nullptr), load_done(plan.loads.size(), nullptr);
-  size_t next_load = 0;
+  // loader thread <-> enqueue (main): ops whose completion events are
+  // recorded, loads whose copies are enqueued
+  std::mutex load_mu;
+  std::condition_variable load_cv;
+  size_t ops_enqueued = 0, loads_issued = 0;
+  std::atomic<int> w_fail{0};
+  double h2d_load_bytes = 0;
   int bwd_count = 0;
-  std::thread gthr, athr;
+  std::thread gthr, athr, wthr;
   // the previous step's head update must land before the head is streamed
   std::mutex head_mu;
   std::condition_variable head_cv;
@@ -495,6 +502,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         const auto tw = clock::now();
         ok = hipEventSynchronize(o.after) == hipSuccess;
         op_wait_ms += ms_since(tw);
+        if (o.unit == 0 && o.ring >= 0) gpu_done_ms = ms_since(t_begin);
       }
       if (ok) {
         const auto t0 = clock::now();
@@ -504,6 +512,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
                                  NONFINITE_BLOCKS * 4);
         d2h_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
         d2h_bytes += (double)o.elems * es;
+        grads_landed_ms = ms_since(t_begin);
       }
       if (o.ring >= 0) {
         std::lock_guard<std::mutex> lk(ring_mu);
@@ -520,6 +529,69 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         continue;
       }
       landq.push(Landed{o.unit, host, own, nullptr, false});
+    }
+  };
+
+  // ------------------------------------------------------- W thread
+  // Issues the weight loads in plan order.  Each load's dependencies (the
+  // op that frees its slot, the look-ahead gate, the previous step's head
+  // update) are waited for on the host, so no copy is ever submitted with
+  // an unresolved wait: a copy waiting inside a copy engine's queue would
+  // hold up every later copy the process submits to that engine, the
+  // gradient offload's included.
+  auto w_main = [&]() {
+    auto publish = [&](size_t k) {
+      {
+        std::lock_guard<std::mutex> lk(load_mu);
+        loads_issued = k;
+      }
+      load_cv.notify_all();
+    };
+    // wakes the enqueue on every way out (it may wait for a load that an
+    // abort leaves unissued)
+    struct Wake {
+      std::mutex& mu;
+      std::condition_variable& cv;
+      ~Wake() {
+        { std::lock_guard<std::mutex> lk(mu); }
+        cv.notify_all();
+      }
+    } wake{load_mu, load_cv};
+    for (size_t k = 0; k < plan.loads.size(); ++k) {
+      const PlanLoad& ld = plan.loads[k];
+      const int need = std::max(ld.wait_use, ld.gate_use);
+      {
+        std::unique_lock<std::mutex> lk(load_mu);
+        load_cv.wait(lk, [&] { return (int)ops_enqueued > need || abort_all.load(); });
+      }
+      if (abort_all.load()) return;
+      bool ok = true;
+      if (ld.wait_use >= 0) ok = hipEventSynchronize(op_done[ld.wait_use]) == hipSuccess;
+      if (ok && ld.gate_use >= 0 && ld.gate_use != ld.wait_use)
+        ok = hipEventSynchronize(op_done[ld.gate_use]) == hipSuccess;
+      if (ok && ld.unit == L) {
+        std::unique_lock<std::mutex> lk(head_mu);
+        head_cv.wait(lk, [&] { return head_done; });
+      }
+      if (ok) {
+        const Unit& u = M->units[ld.unit];
+        char* dst = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+        hipEvent_t c0 = get_ev(), c1 = get_ev();
+        ok = c0 && c1 && hipEventRecord(c0, sW) == hipSuccess &&
+             hipMemcpyAsync(dst, u.shadow, u.n * es, hipMemcpyHostToDevice, sW) == hipSuccess &&
+             hipEventRecord(c1, sW) == hipSuccess &&
+             hipEventRecord(load_done[k], sW) == hipSuccess;
+        if (ok) {
+          h2d_ev.push_back({c0, c1});
+          h2d_load_bytes += (double)u.n * es;
+        }
+      }
+      if (!ok) {
+        w_fail = 1;
+        abort_all = true;
+        return;
+      }
+      publish(k + 1);
     }
   };
 
@@ -553,7 +625,10 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       const auto tw = clock::now();
       Landed x = landq.pop();
       adam_idle_ms += ms_since(tw);
-      if (x.end) return;
+      if (x.end) {
+        updates_done_ms = ms_since(t_begin);
+        return;
+      }
       if (!checked) {
         std::unique_lock<std::mutex> lk(loss_mu);
         loss_cv.wait(lk, [&] { return loss_ready; });
@@ -670,6 +745,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     // gradient buffers: pads must read as zero
     MT_STEP_HIP(hipMemsetAsync(A.head_grad, 0, M->hl.total * es, sC));
     for (int i = 0; i < NG; ++i) MT_STEP_HIP(hipMemsetAsync(A.gring[i], 0, M->ll.total * es, sC));
+    host_start_ms = ms_since(t_begin);
     MT_STEP_HIP(hipEventRecord(ph_start, sC));
     // inputs of the step
     MT_STEP_HIP(hipMemcpyAsync(A.ckpt[0], M->x0_host, act * es, hipMemcpyHostToDevice, sW));
@@ -680,30 +756,21 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
 
     auto xloc = [&](int i) -> char* { return (i % K == 0) ? A.ckpt[i / K] : A.act[i % 2]; };
 
+    if (!wthr.joinable()) wthr = std::thread(w_main);
     for (size_t i = 0; i < plan.ops.size(); ++i) {
-      // weight loads whose slot and look-ahead dependencies are enqueued
-      while (next_load < plan.loads.size()) {
-        const PlanLoad& ld = plan.loads[next_load];
-        if (std::max(ld.wait_use, ld.gate_use) >= (int)i) break;
-        if (ld.wait_use >= 0) MT_STEP_HIP(hipStreamWaitEvent(sW, op_done[ld.wait_use], 0));
-        if (ld.gate_use >= 0 && ld.gate_use != ld.wait_use)
-          MT_STEP_HIP(hipStreamWaitEvent(sW, op_done[ld.gate_use], 0));
-        const Unit& u = M->units[ld.unit];
-        char* dst = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
-        if (ld.unit == L) {
-          std::unique_lock<std::mutex> lk(head_mu);
-          head_cv.wait(lk, [&] { return head_done; });
-        }
-        hipEvent_t c0 = get_ev(), c1 = get_ev();
-        MT_STEP_HIP(hipEventRecord(c0, sW));
-        MT_STEP_HIP(hipMemcpyAsync(dst, u.shadow, u.n * es, hipMemcpyHostToDevice, sW));
-        MT_STEP_HIP(hipEventRecord(c1, sW));
-        MT_STEP_HIP(hipEventRecord(load_done[next_load], sW));
-        h2d_ev.push_back({c0, c1});
-        h2d_bytes += (double)u.n * es;
-        ++next_load;
-      }
       const PlanOp& op = plan.ops[i];
+      {
+        // every op before this one has its completion event recorded; wait
+        // until the loader has enqueued this op's weights
+        std::unique_lock<std::mutex> lk(load_mu);
+        ops_enqueued = i;
+        load_cv.notify_all();
+        load_cv.wait(lk, [&] { return loads_issued > (size_t)op.load || abort_all.load(); });
+      }
+      if (abort_all.load()) {
+        if (w_fail.load()) fail = set_error(MT_E_HIP, "mt_stream_step: weight load failed");
+        goto drain;  // otherwise the failing thread's status is reported below
+      }
       const PlanLoad& ld = plan.loads[op.load];
       const char* w = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
       // wait for this op's weights; the gap is the exposed transfer time
@@ -765,10 +832,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           std::unique_lock<std::mutex> lk(ring_mu);
           ring_cv.wait(lk, [&] { return ring_done >= bwd_count - NG + 1 || abort_all.load(); });
           ring_wait_ms += ms_since(tw);
-          if (abort_all.load()) {
-            fail = set_error(MT_E_HIP, "mt_stream_step: gradient offload failed");
-            goto drain;
-          }
+          if (abort_all.load()) goto drain;  // the failing thread's status is reported below
         }
         if (keep)
           MT_STEP_RUN(layer_bwd_saved_impl(d, layer_view(M, w), in, A.dy, A.dy,
@@ -791,16 +855,28 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       }
       MT_STEP_HIP(hipEventRecord(op_done[i], sC));
     }
+    {
+      std::lock_guard<std::mutex> lk(load_mu);
+      ops_enqueued = plan.ops.size();
+    }
+    load_cv.notify_all();
     // dx0 = gradient of the embedding output
     offq.push(Offload{-1, A.dy, act, nullptr, ph_end, -1});
   }
 drain:
-  if (fail != MT_OK) {
+  if (fail != MT_OK || abort_all.load()) {
     abort_all = true;
-    std::lock_guard<std::mutex> lk(loss_mu);
-    loss_ready = true;
+    {
+      std::lock_guard<std::mutex> lk(loss_mu);
+      loss_ready = true;
+    }
     loss_cv.notify_all();
   }
+  {
+    std::lock_guard<std::mutex> lk(load_mu);  // the loader sees abort_all or every op
+  }
+  load_cv.notify_all();
+  if (wthr.joinable()) wthr.join();
   offq.push(Offload{0, nullptr, 0, nullptr, nullptr, -1, true});
   if (gthr.joinable()) gthr.join();
   if (athr.joinable()) athr.join();
@@ -810,6 +886,8 @@ drain:
     fail = set_error(MT_E_HIP, "mt_stream_step: asynchronous HIP error: %s",
                      hipGetErrorString(e1 != hipSuccess ? e1 : e2 != hipSuccess ? e2 : e3));
   }
+  if (fail == MT_OK && w_fail.load())
+    fail = set_error(MT_E_HIP, "mt_stream_step: weight load failed");
   if (fail == MT_OK && (g_fail.load() || a_fail.load() == 1))
     fail = set_error(MT_E_HIP, "mt_stream_step: gradient offload or optimizer thread failed");
   if (fail == MT_OK && nonfinite_loss)
@@ -859,7 +937,7 @@ drain:
         snprintf(s.probe_kernel, sizeof s.probe_kernel, "%s", top->first.c_str());
       }
     }
-    s.h2d_bytes = h2d_bytes;
+    s.h2d_bytes = h2d_bytes + h2d_load_bytes;
     s.d2h_bytes = d2h_bytes;
     s.pinned_host_bytes = M->pinned_bytes;
     s.pageable_host_bytes = M->pageable_bytes;
@@ -868,6 +946,10 @@ drain:
     s.step_ms = std::chrono::duration<double, std::milli>(clock::now() - t_begin).count();
     s.tail_ms = s.step_ms - (s.fwd_ms + s.head_ms + s.bwd_ms);
     s.host_ring_wait_ms = ring_wait_ms;
+    s.host_start_ms = host_start_ms;
+    s.gpu_done_ms = gpu_done_ms;
+    s.grads_landed_ms = grads_landed_ms;
+    s.updates_done_ms = updates_done_ms;
     s.host_slab_wait_ms = slab_wait_ms;
     s.host_op_wait_ms = op_wait_ms;
     s.host_adam_idle_ms = adam_idle_ms;

@@ -243,17 +243,30 @@ inline float to_f32(float f) { return f; }
 template <class G>
 void scatter_add_t(const G* dx0, const int32_t* ids, size_t n_tok, size_t H, float* dE,
                    ThreadPool* pool) {
-  // each worker owns a column slice and walks every token in order, so the
-  // summation order per element is the token order regardless of threads
-  auto body = [&](size_t c0, size_t c1) {
-    for (size_t t = 0; t < n_tok; ++t) {
-      float* row = dE + (size_t)ids[t] * H;
-      const G* src = dx0 + t * H;
-      for (size_t c = c0; c < c1; ++c) row[c] += to_f32(src[c]);
+  // tokens grouped by destination row (stable: token order within a row);
+  // each worker owns whole rows and adds their tokens in token order, so
+  // the summation order per element is the token order regardless of
+  // threads, and every access is a full contiguous row
+  std::vector<int32_t> order(n_tok);
+  for (size_t t = 0; t < n_tok; ++t) order[t] = (int32_t)t;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return ids[a] < ids[b]; });
+  std::vector<size_t> seg;
+  for (size_t i = 0; i < n_tok; ++i)
+    if (i == 0 || ids[order[i]] != ids[order[i - 1]]) seg.push_back(i);
+  seg.push_back(n_tok);
+  auto body = [&](size_t s0, size_t s1) {
+    for (size_t s = s0; s < s1; ++s) {
+      float* row = dE + (size_t)ids[order[seg[s]]] * H;
+      for (size_t i = seg[s]; i < seg[s + 1]; ++i) {
+        const G* src = dx0 + (size_t)order[i] * H;
+        for (size_t c = 0; c < H; ++c) row[c] += to_f32(src[c]);
+      }
     }
   };
-  if (pool) pool->parallel_for(H, body, 64);
-  else body(0, H);
+  const size_t n_seg = seg.size() - 1;
+  if (pool) pool->parallel_for(n_seg, body, 16);
+  else body(0, n_seg);
 }
 }  // namespace
 

@@ -80,15 +80,17 @@ bool SdmaCopier::init(const char** err) {
     *err = "no SDMA engine available for device-to-host copies";
     return false;
   }
-  // ROCr's recommendation for this direction: on MI355X two engines serve
-  // the host link while the others are tuned for xGMI and reach only
-  // 7-11 GB/s to host memory.  Host-to-device traffic prefers engine 0, so
-  // device-to-host takes the lowest recommended engine.
+  // ROCr's recommendation for this direction (on MI355X it names every
+  // engine).  Engine 0 carries the runtime's own host-to-device copies (the
+  // weight loads); sharing it serializes the two directions, so the
+  // offload takes the lowest recommended engine after it (engine 1 moves
+  // 57 GB/s to pinned host memory while engine 0 loads weights).
   uint32_t pref = 0;
   if (hsa_amd_memory_get_preferred_copy_engine(f.cpu, f.gpu, &pref) != HSA_STATUS_SUCCESS ||
       (pref & mask) == 0)
     pref = mask;
   pref &= mask;
+  if (pref & ~1u) pref &= ~1u;
   unsigned e = 1;
   while (!(pref & e)) e <<= 1;
   hsa_signal_t sig;

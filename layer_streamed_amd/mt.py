@@ -68,7 +68,9 @@ class StepStats(C.Structure):
             "probe_kernel_launches", "pinned_host_bytes", "pageable_host_bytes",
             "device_arena_bytes", "units_updated")] + [(n, C.c_double) for n in (
                 "host_ring_wait_ms", "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms",
-                "probe_all_gemm_ms")] + [("probe_kernel", C.c_char * 96)]
+                "probe_all_gemm_ms")] + [("probe_kernel", C.c_char * 96)] + [
+            (n, C.c_double) for n in ("host_start_ms", "gpu_done_ms", "grads_landed_ms",
+                                      "updates_done_ms")]
 
     def as_dict(self):
         d = {n: getattr(self, n) for n, _ in self._fields_}
