@@ -18,6 +18,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -447,6 +448,47 @@ __device__ __forceinline__ u32x4_t dl_frag(const char* st, int rb, int ks, int l
   }
 }
 
+// Fragment of rows (K-contiguous) or columns (K-major) rb .. rb + 15 for the
+// 32-deep k-substep ks of a stage, as v_mfma_f32_16x16x32_bf16 takes it:
+// lane l holds row (column) rb + (l & 15) at k-slots 8 (l >> 4) .. + 7.  The
+// K-major form issues two transpose reads per lane (k .. k+3 and k+4 ..
+// k+7 of one column, the same 16-lane pattern as dl_frag).
+template <bool KM, int BR, int BK>
+__device__ __forceinline__ u32x4_t dl_frag16(const char* st, int rb, int ks, int lane) {
+  if constexpr (!KM) {
+    constexpr int CH = BK / 8;
+    const int r = rb + (lane & 15);
+    const int c = ks * 4 + (lane >> 4);
+    return reinterpret_cast<const u32x4_t*>(st)[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
+  } else {
+    constexpr int RC = BR / 8;
+    const int grp = lane >> 4, i = lane & 15;
+    const int m = rb + 4 * (i & 3);
+    const int c = m >> 3, half = (m >> 2) & 1;
+    u32x2_t v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = ks * 32 + 8 * grp + 4 * h + (i >> 2);
+      const char* p = st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8);
+      // asm for the reason given in dl_frag
+      const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[h]) : "v"(la) : "memory");
+    }
+    return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
+  }
+}
+
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// A 32 x 32 accumulator block held as four 16 x 16 blocks (q = 2 a + b
+// covers rows 16 a .., columns 16 b ..; lane l holds column l & 15, rows
+// 4 (l >> 4) .. + 3 of each).
+struct Sub4 {
+  f32x4_t s[4];
+};
+
 // Epilogue of the direct-to-LDS kernels, staged through LDS (free once the
 // main loop is done): each wave writes one 32 x 32 accumulator block (two
 // for a SwiGLU gate/up pair) to a private slot, reads it back so that every
@@ -486,8 +528,23 @@ __device__ __forceinline__ void stage_block(float* slot, const f32x16_t& blk, in
   }
 }
 
-template <int WM, int WN, int TM, int TN, int EPI>
-__device__ __forceinline__ void epilogue_lds(const GemmArgs& a, f32x16_t (&acc)[TM][TN], int m0,
+// the same for a block held as four 16 x 16 blocks
+__device__ __forceinline__ void stage_block(float* slot, const Sub4& blk, int lane, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      slot[(16 * (q >> 1) + 4 * (lane >> 4) + r) * EPI_LD + 16 * (q & 1) + (lane & 15)] = blk.s[q][r];
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(slot + (lane >> 1) * EPI_LD + 16 * (lane & 1));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4_t t = src[q];
+    v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+  }
+}
+
+template <int WM, int WN, int TM, int TN, int EPI, class Acc>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& a, Acc (&acc)[TM][TN], int m0,
                                              int n0, int wm, int wn, int lane, char* wslot) {
   constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
   float* s0 = reinterpret_cast<float*>(wslot);
@@ -602,9 +659,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, f32x16_t (&acc)[
   }
 }
 
-template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI, int BK, int NS>
+// MI selects the MFMA: 32 (v_mfma_f32_32x32x16_bf16, 16-deep substeps) or
+// 16 (v_mfma_f32_16x16x32_bf16, 32-deep substeps, each 32 x 32 block of
+// the wave tile as four 16 x 16 blocks).  The two give bitwise equal
+// products; which is faster depends on the layout (see launch_layout).
+template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI, int BK, int NS, int MI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) {
-  static_assert(BK % 16 == 0 && BK <= 64 && NS >= 2 && NS <= 4, "stage shape");
+  static_assert(BK % 32 == 0 && BK <= 64 && NS >= 2 && NS <= 4, "stage shape");
+  static_assert(MI == 16 || MI == 32, "MFMA shape");
   constexpr bool A_KM = LAYOUT == GEMM_TN, B_KM = LAYOUT != GEMM_NT;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NW = WM * WN;
   constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;  // 16-byte chunks per stage
@@ -645,13 +707,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
   const long a_step = A_KM ? (long)BK * a.lda : BK;
   const long b_step = B_KM ? (long)BK * a.ldb : BK;
 
-  f32x16_t acc[TM][TN];
+  using Acc = std::conditional_t<MI == 16, Sub4, f32x16_t>;
+  Acc acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (MI == 16) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        for (int q = 0; q < 4; ++q) acc[i][j].s[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      }
+    }
 
   const int nk = K / BK;
   auto issue = [&](int kt) {
@@ -668,6 +737,48 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
           (const void*)(gb[p] + kt * b_step),
           (__attribute__((address_space(3))) void*)(base + A_CH * 16 + (wave * B_PER + p) * 1024), 16,
           0, 0);
+  };
+
+  auto compute16 = [&](int kt) {
+    const char* sA = dl_smem + (kt % NS) * STAGE;
+    const char* sB = sA + A_CH * 16;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      u32x4_t af[TM][2], bfr[TN][2];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          af[i][h] = dl_frag16<A_KM, BM, BK>(sA, wm * TM * 32 + i * 32 + 16 * h, ks, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          bfr[j][h] = dl_frag16<B_KM, BN, BK>(sB, wn * TN * 32 + j * 32 + 16 * h, ks, lane);
+      if constexpr (A_KM || B_KM) {
+        // as in compute below
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          asm volatile("" : "+v"(af[i][0]));
+          asm volatile("" : "+v"(af[i][1]));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          asm volatile("" : "+v"(bfr[j][0]));
+          asm volatile("" : "+v"(bfr[j][1]));
+        }
+      }
+      if constexpr (MI == 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[i][j].s[q] = mfma16(af[i][q >> 1], bfr[j][q & 1], acc[i][j].s[q]);
+      }
+    }
   };
 
   auto compute = [&](int kt) {
@@ -690,10 +801,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
 #pragma unroll
         for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(bfr[j]));
       }
+      if constexpr (MI == 32) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+      }
     }
   };
 
@@ -709,7 +822,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     issue(kt + NS - 1);
-    compute(kt);
+    if constexpr (MI == 16) compute16(kt);
+    else compute(kt);
   }
   // the ring is free once every wave has finished reading its last stage
   __syncthreads();
@@ -729,7 +843,7 @@ inline bool epi_vec_ok(const GemmArgs& a) {
   return ok;
 }
 
-template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI, int BK, int NS>
+template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI, int BK, int NS, int MI>
 hipError_t launch_dl(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
@@ -737,7 +851,7 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t s) {
   constexpr size_t stage_out = (size_t)WM * WN * (SWI ? 2 : 1) * EPI_SLOT;
   static_assert(stage_out <= ring, "epilogue slots must fit in the ring");
   const size_t lds = ring;
-  auto kern = gemm_dl_kernel<LAYOUT, WM, WN, TM, TN, EPI, BK, NS>;
+  auto kern = gemm_dl_kernel<LAYOUT, WM, WN, TM, TN, EPI, BK, NS, MI>;
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -803,10 +917,15 @@ inline bool deep_stages(const GemmArgs& a, int layout, TileCfg c) {
   return a.K % 64 == 0 && (layout == GEMM_NT || (layout == GEMM_TN && c == DL_256x256));
 }
 
+// MFMA shape per layout: TN (both operands K-major) runs faster on the
+// 16 x 16 x 32 MFMA, NT and NN on 32 x 32 x 16 (measured on the 7B shapes).
+constexpr int dl_mfma(int layout) { return layout == GEMM_TN ? 16 : 32; }
+
 template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI>
 hipError_t launch_dl_stages(const GemmArgs& a, TileCfg c, hipStream_t s) {
-  if (deep_stages(a, LAYOUT, c)) return launch_dl<LAYOUT, WM, WN, TM, TN, EPI, 64, 2>(a, s);
-  return launch_dl<LAYOUT, WM, WN, TM, TN, EPI, 32, 4>(a, s);
+  constexpr int MI = dl_mfma(LAYOUT);
+  if (deep_stages(a, LAYOUT, c)) return launch_dl<LAYOUT, WM, WN, TM, TN, EPI, 64, 2, MI>(a, s);
+  return launch_dl<LAYOUT, WM, WN, TM, TN, EPI, 32, 4, MI>(a, s);
 }
 
 template <int LAYOUT, int EPI>
@@ -881,9 +1000,10 @@ hipError_t gemm_launch(const GemmArgs& a, hipStream_t s) {
 std::string gemm_kernel_name(const GemmArgs& a) {
   // the demangled template name profilers report for the launch
   const int lay = (a.epi == EPI_SWIGLU || a.epi == EPI_SWIGLU_SAVE) ? GEMM_NT : a.layout;
-  char buf[64];
+  char buf[80];
   const TileCfg c = choose_cfg(a);
-  const char* st = deep_stages(a, lay, c) ? "64, 2" : "32, 4";
+  char st[16];
+  snprintf(st, sizeof st, "%s, %d", deep_stages(a, lay, c) ? "64, 2" : "32, 4", dl_mfma(lay));
   switch (c) {
     case DL_256x256: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 4, 4, 2, %d, %s>", lay, a.epi, st); break;
     case DL_256x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 4, 2, 2, 2, %d, %s>", lay, a.epi, st); break;
