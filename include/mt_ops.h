@@ -102,7 +102,7 @@ mt_status mt_op_ce_rows(const float* logits, const int32_t* target, void* dlogit
 
 /* Finiteness of a gradient buffer (the engine's per-unit check, run on the
  * GPU so the host never re-reads the gradient): flags[NONFINITE_BLOCKS =
- * 256] int32 receive 1 where that workgroup's strided share of the buffer
+ * 2048] int32 receive 1 where that workgroup's strided share of the buffer
  * holds an Inf or NaN, else 0.  g: device, bytes % 16 == 0, bf16 (f32 = 0)
  * or fp32 (f32 = 1) values. */
 mt_status mt_op_nonfinite_flags(const void* g, size_t bytes, int32_t f32, int32_t* flags,

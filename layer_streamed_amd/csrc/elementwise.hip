@@ -313,16 +313,25 @@ __global__ __launch_bounds__(256) void nonfinite_kernel(const u32x4_t* __restric
   __syncthreads();
   uint32_t bad = 0;
   const uint32_t em = f32 ? 0x7F800000u : 0x7F807F80u;  // exponent masks per dword
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const u32x4_t v = g[i];
+  auto check = [&](const u32x4_t v) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t x = v[k] & em;
       if (f32) bad |= (x == 0x7F800000u);
       else bad |= ((x & 0xFFFFu) == 0x7F80u) | ((x >> 16) == 0x7F80u);
     }
+  };
+  // four independent 16-byte loads in flight per lane per trip
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = g[i], b = g[i + stride], c = g[i + 2 * stride], d = g[i + 3 * stride];
+    check(a);
+    check(b);
+    check(c);
+    check(d);
   }
+  for (; i < n16; i += stride) check(g[i]);
   if (bad) any = 1;  // benign race: every writer stores 1
   __syncthreads();
   if (threadIdx.x == 0) flags[blockIdx.x] = any;

@@ -100,7 +100,7 @@ hipError_t copy_d2h(const void* src, void* dst_host, size_t bytes, int blocks, h
 // Finiteness of a gradient buffer: NONFINITE_BLOCKS workgroups each scan a
 // strided share of `bytes` bytes of bf16 (f32 = 0) or fp32 values and write
 // flags[block] = 1 if any is Inf or NaN, else 0 (bytes % 16 == 0).
-constexpr int NONFINITE_BLOCKS = 256;
+constexpr int NONFINITE_BLOCKS = 2048;
 hipError_t nonfinite_flags(const void* g, size_t bytes, int f32, int32_t* flags, hipStream_t s);
 hipError_t cast_f32(const float* in, uint16_t* out, size_t n, hipStream_t s);
 hipError_t cast_f32(const float* in, float* out, size_t n, hipStream_t s);

@@ -462,7 +462,7 @@ def test_nonfinite_flags(f32):
     torch, mt = _torch(), _mt()
     dt = torch.float32 if f32 else torch.bfloat16
     n = 1_000_008  # elements; bytes a multiple of 16
-    flags = torch.empty(256, dtype=torch.int32, device="cuda")
+    flags = torch.empty(2048, dtype=torch.int32, device="cuda")  # NONFINITE_BLOCKS
     g = (torch.randn(n, device="cuda") * 1e3).to(dt)
     nbytes = n * g.element_size()
     assert mt.call("mt_op_nonfinite_flags", g.data_ptr(), nbytes, f32, flags.data_ptr(), None) == 0
