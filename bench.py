@@ -182,10 +182,12 @@ def main():
     torch.cuda.synchronize()
     stats = []
     losses = []
+    step_wall = []
     t_start = time.perf_counter()
     for i in range(args.steps):
         ts = time.perf_counter()
         loss, st = model.step(ids, arena, streams)
+        step_wall.append(1e3 * (time.perf_counter() - ts))
         stats.append(st)
         losses.append(loss)
         log(f"step {i}: loss {loss:.4f} {1e3 * (time.perf_counter() - ts):.0f} ms "
@@ -276,6 +278,9 @@ def main():
             "slab_pool": not args.no_slab_pool, "parallelism": "single-gpu layer streaming",
             "params": n_params,
         },
+        "step_ms": {"median": round(float(np.median(step_wall)), 2),
+                    "min": round(float(np.min(step_wall)), 2),
+                    "max": round(float(np.max(step_wall)), 2)},
         "tflops_xbatch_formula": round(f_xb / step_s / 1e12, 3),
         "tflops_executed": round(f_exec / step_s / 1e12, 3),
         "mfma_frac_executed": round(f_exec / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),

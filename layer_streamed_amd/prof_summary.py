@@ -6,11 +6,16 @@
            then WRITE_SIZE), each calibrated by what the same counter reads
            for the plain 1 GiB device copy that `bench.py --pmc-copy` runs
            (the copy reads 1 GiB and writes 1 GiB per launch)
+  mfma     MFMA-busy fraction per kernel from one --pmc run of
+           SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and
+           SQ_INSTS_VALU_MFMA_MOPS_BF16: busy SIMD cycles over active GPU
+           cycles x SIMD_NUM, and the MFMA FLOPs those instructions did
 
 Usage:
   python -m layer_streamed_amd.prof_summary stats STATS_CSV OUT_MD --title T --command C
   python -m layer_streamed_amd.prof_summary traffic FETCH_CSV WRITE_CSV OUT_MD \\
       --kernel NAME --flops-per-launch F --command-fetch C1 --command-write C2
+  python -m layer_streamed_amd.prof_summary mfma PMC_CSV OUT_MD --title T --command C
 """
 import argparse
 import csv
@@ -110,6 +115,63 @@ def traffic(args):
     open(args.out, "w").write("\n".join(out) + "\n")
 
 
+def _gpu_agent(csv_path):
+    """(XCD count, SIMD count) of the GPU agent from the run's agent-info file."""
+    info = os.path.join(os.path.dirname(csv_path),
+                        os.path.basename(csv_path).replace("counter_collection", "agent_info"))
+    for r in csv.DictReader(open(info)):
+        if r["Agent_Type"] == "GPU":
+            return int(r["Num_Xcc"]), int(r["Simd_Count"])
+    raise SystemExit(f"no GPU agent in {info}")
+
+
+def mfma(args):
+    busy, active, mops, dur = (defaultdict(float) for _ in range(4))
+    names = {}
+    for r in csv.DictReader(open(args.csv)):
+        key = int(r["Dispatch_Id"])
+        names[key] = short(r["Kernel_Name"])
+        dur[key] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])  # ns
+        v = float(r["Counter_Value"])
+        c = r["Counter_Name"]
+        if c == "SQ_VALU_MFMA_BUSY_CYCLES":
+            busy[key] += v
+        elif c == "GRBM_GUI_ACTIVE":
+            active[key] += v
+        elif c == "SQ_INSTS_VALU_MFMA_MOPS_BF16":
+            mops[key] += v
+    xcc, simds = _gpu_agent(args.csv)
+    # the file holds one value per dispatch, GRBM_GUI_ACTIVE summed over the
+    # XCDs: per XCD (the clock that every SIMD shares) it is that / xcc
+    by = defaultdict(lambda: [0, 0.0, 0.0, 0.0, 0.0])
+    for key, n in names.items():
+        g = by[n]
+        g[0] += 1
+        g[1] += busy[key]
+        g[2] += active[key] / xcc
+        g[3] += mops[key] * 512
+        g[4] += dur[key]
+    tot_busy = sum(g[1] for g in by.values())
+    tot_active = sum(g[2] for g in by.values())
+    rows = sorted(by.items(), key=lambda kv: -kv[1][2])
+    out = [f"# {args.title}", "", "Command (from the repository root):", "", f"    {args.command}", "",
+           "MFMA-busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (active cycles "
+           f"x {simds} SIMDs), per kernel over its dispatches, where active cycles = "
+           f"GRBM_GUI_ACTIVE / {xcc} (the file sums it over the {xcc} XCDs); clock = active "
+           "cycles / kernel duration; MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. Kernels "
+           "on other streams may overlap a dispatch.", "",
+           f"All kernels of the run: MFMA busy {100 * tot_busy / max(tot_active * simds, 1):.1f}% "
+           f"of {tot_active:.4g} active cycles.", "",
+           "| kernel | dispatches | active cycles | clock (GHz) | MFMA busy | MFMA TFLOP (counted) | "
+           "TFLOP/s (counted / time) |",
+           "|---|---|---|---|---|---|---|"]
+    for n, (k, b, a, f, t) in rows[: args.top]:
+        out.append(f"| {n[:72]} | {k} | {a:.4g} | {a / max(t, 1):.2f} | "
+                   f"{100 * b / max(a * simds, 1):.1f}% | {f / 1e12:.2f} | "
+                   f"{f / max(t, 1) / 1e3:.0f} |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -129,8 +191,14 @@ def main():
     b.add_argument("--command-fetch", required=True)
     b.add_argument("--command-write", required=True)
     b.add_argument("--note", default="")
+    c = sub.add_parser("mfma")
+    c.add_argument("csv")
+    c.add_argument("out")
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--top", type=int, default=20)
     args = ap.parse_args()
-    stats(args) if args.cmd == "stats" else traffic(args)
+    {"stats": stats, "traffic": traffic, "mfma": mfma}[args.cmd](args)
 
 
 if __name__ == "__main__":
