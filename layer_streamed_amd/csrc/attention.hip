@@ -326,7 +326,10 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(const AttnArgs a) {
   const int T = a.T;
   const int nkb = (T + BK - 1) / BK;
   const int per = a.Hkv * a.B;
-  const int kb = nkb - 1 - (int)blockIdx.x / per;
+  // key block 0 sees every query tile, the last one only its own: launch
+  // the longest first so the short ones fill the tail (the blocks are
+  // independent, so the order changes no result)
+  const int kb = (int)blockIdx.x / per;
   const int rest = blockIdx.x % per;
   const int g = rest % a.Hkv, b = rest / a.Hkv;
   const int rep = a.Hq / a.Hkv;
