@@ -20,7 +20,10 @@
 // Backward (deterministic, no atomics): delta = rowsum(dO * O); a dK/dV
 // kernel owns 128 keys per workgroup and loops over every query head of the
 // GQA group and every query tile at or after its keys; a dQ kernel owns 128
-// queries and loops over key tiles up to the diagonal.
+// queries and loops over key tiles up to the diagonal.  For head_dim 128 the
+// dK/dV kernel takes its query tiles straight into LDS and reads the
+// transposed operands with LDS transpose reads (attn_dkdv_dl_kernel); the
+// register-staged form (attn_dkdv_kernel) serves head_dim 64.
 #include "common.h"
 #include "kernels.h"
 
@@ -454,6 +457,215 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(const AttnArgs a) {
   }
 }
 
+// dK/dV for head_dim 128 with the Q and dO tiles loaded straight into LDS
+// (gfx950 global_load_lds_dwordx4, double-buffered, one barrier per tile)
+// in their natural [query][d] layout, 16 chunks of 8 per row stored in the
+// order c ^ dkdv_swz(row).  The MFMA operands are those of attn_dkdv_kernel
+// (same values, same order, so the same bits): Q and dO rows for S and dP
+// are one ds_read_b128 per lane; the transposed, permuted dO^T and Q^T for
+// dV and dK are two ds_read_b64_tr_b16 per lane (the 16-lane pattern of the
+// GEMM's K-major fragments: lane 4j + s addresses query row base + j,
+// columns 4s .. 4s+3, and lane i receives column i at rows base .. base+3).
+// The swizzle keeps both kinds of read on distinct banks: 8 consecutive
+// rows take 8 different chunks, and the 4 rows of a transpose read take
+// disjoint chunk pairs (quads for a half-wave).  LDS reads of the tiles are
+// inline asm, waited for explicitly: the compiler would otherwise drain the
+// next tile's in-flight loads before each read.
+__device__ __forceinline__ int dkdv_swz(int row) {
+  return ((0xCA60 >> (4 * (row & 3))) & 15) ^ ((row >> 2) & 1);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+__device__ __forceinline__ u32x4_t lds_row16(const char* tile, int row, int chunk) {
+  u32x4_t v;
+  const uint32_t la = lds_addr(tile + row * 256 + ((chunk ^ dkdv_swz(row)) << 4));
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(la) : "memory");
+  return v;
+}
+
+// Rows base .. base+3 (pass h = 0) and base+8 .. base+11 (h = 1) of columns
+// m0 + (lane & 15) as one MFMA A fragment (slots 0-3, then 4-7).
+__device__ __forceinline__ u32x4_t lds_tr_frag(const char* tile, int base, int m0, int lane) {
+  const int i = lane & 15;
+  const int d = m0 + 4 * (i & 3);
+  const int c = d >> 3, half = (d >> 2) & 1;
+  u32x2_t v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = base + 8 * h + (i >> 2);
+    const uint32_t la = lds_addr(tile + row * 256 + ((c ^ dkdv_swz(row)) << 4) + half * 8);
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[h]) : "v"(la) : "memory");
+  }
+  return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
+  static_assert(D == 128, "rows of 16 chunks");
+  constexpr int BQ = 64, CH = D / 8, TILE = BQ * D * 2, STAGE = 2 * TILE;
+  constexpr int PER = BQ * CH / 256;  // 16-byte load instructions per wave per operand
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  float* sLb = reinterpret_cast<float*>(dsm + 2 * STAGE);  // [2][BQ]
+  float* sDb = sLb + 2 * BQ;                               // [2][BQ]
+
+  const int T = a.T;
+  const int per = a.Hkv * a.B;
+  const int kb = (int)blockIdx.x / per;  // most query tiles first
+  const int rest = blockIdx.x % per;
+  const int g = rest % a.Hkv, b = rest / a.Hkv;
+  const int rep = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int k0 = kb * 128;
+  const int key = k0 + 32 * w + n;
+  const long ldq = a.ldq;
+  const uint16_t* base = a.qkv + (long)b * T * ldq;
+  const uint16_t* dbase = a.dout + (long)b * T * a.ldo;
+
+  u32x4_t kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bool ok = key < T;
+    kf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + g) * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+    vf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + a.Hkv + g) * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+  }
+  f32x16_t dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    zero16(dk[dt]);
+    zero16(dv[dt]);
+  }
+
+  const int ntq = (T - k0 + BQ - 1) / BQ;  // query tiles from k0 to T
+  const int nit = rep * ntq;
+  float lse_r = 0.f, del_r = 0.f;
+  // tile `it` -> stage `buf`: Q and dO rows clamped to T - 1 past the end
+  // (their P is 0 through lse = +1e30, so they add exact zeros)
+  auto issue = [&](int it, int buf) {
+    const int hq = g * rep + it / ntq;
+    const int qt0 = k0 + (it % ntq) * BQ;
+    char* sq = dsm + buf * STAGE;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int slot = (w * PER + p) * 64 + lane;
+      const int row = slot / CH, pos = slot % CH;
+      const int c = pos ^ dkdv_swz(row);
+      const long gq = min(qt0 + row, T - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(base + gq * ldq + hq * D + c * 8),
+          (__attribute__((address_space(3))) void*)(sq + (w * PER + p) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(dbase + gq * a.ldo + hq * D + c * 8),
+          (__attribute__((address_space(3))) void*)(sq + TILE + (w * PER + p) * 1024), 16, 0, 0);
+    }
+    if (tid < BQ) {
+      const int q = qt0 + tid;
+      const long li = ((long)b * a.Hq + hq) * T + q;
+      lse_r = q < T ? a.lse[li] * LOG2E : -NEG;  // +1e30 makes P = 0 for padding rows
+      del_r = q < T ? a.delta[li] : 0.f;
+    }
+  };
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (tid < BQ) {
+    sLb[tid] = lse_r;
+    sDb[tid] = del_r;
+  }
+  __syncthreads();
+  for (int it = 0; it < nit; ++it) {
+    const int buf = it & 1;
+    const int qt0 = k0 + (it % ntq) * BQ;
+    const char* sq = dsm + buf * STAGE;
+    const char* sdo = sq + TILE;
+    const float* sL = sLb + buf * BQ;
+    const float* sDl = sDb + buf * BQ;
+    const bool active = qt0 + BQ - 1 >= k0 + 32 * w;  // some query of the tile sees this wave's keys
+    f32x16_t sacc[2], dpacc[2];
+    if (active) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        zero16(sacc[qt]);
+        zero16(dpacc[qt]);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          u32x4_t Aq = lds_row16(sq, 32 * qt + n, 2 * ks + hh);
+          u32x4_t Ad = lds_row16(sdo, 32 * qt + n, 2 * ks + hh);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          asm volatile("" : "+v"(Aq));
+          asm volatile("" : "+v"(Ad));
+          sacc[qt] = mfma32(Aq, kf[ks], sacc[qt]);
+          dpacc[qt] = mfma32(Ad, vf[ks], dpacc[qt]);
+        }
+      }
+      // P and dS, rows = queries (qt0 + 32qt + 8j + 4hh + i), column = key
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int qi = 32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const int q = qt0 + qi;
+          float p = exp2f(sacc[qt][e] * a.scale_log2 - sL[qi]);
+          if (key > q) p = 0.f;
+          sacc[qt][e] = p;
+          dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
+        }
+    }
+    // the next tile streams in while this one's dV and dK are formed
+    if (it + 1 < nit) issue(it + 1, buf ^ 1);
+    if (active) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4_t Pb = pack_p(sacc[qt], jj);
+          const u32x4_t Sb = pack_p(dpacc[qt], jj);
+          const int rb = 32 * qt + 16 * jj + 4 * hh;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const int m0 = 32 * dt + 16 * ((lane >> 4) & 1);
+            u32x4_t At = lds_tr_frag(sdo, rb, m0, lane);
+            u32x4_t Aq = lds_tr_frag(sq, rb, m0, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("" : "+v"(At));
+            asm volatile("" : "+v"(Aq));
+            dv[dt] = mfma32(At, Pb, dv[dt]);
+            dk[dt] = mfma32(Aq, Sb, dk[dt]);
+          }
+        }
+    }
+    if (it + 1 < nit) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (tid < BQ) {
+        sLb[(buf ^ 1) * BQ + tid] = lse_r;
+        sDb[(buf ^ 1) * BQ + tid] = del_r;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (key < T) {
+    uint16_t* drow = a.dqkv + ((long)b * T + key) * ldq;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * hh;
+        u32x2_t vk, vv;
+        vk.x = pack_bf(dk[dt][4 * j] * a.scale, dk[dt][4 * j + 1] * a.scale);
+        vk.y = pack_bf(dk[dt][4 * j + 2] * a.scale, dk[dt][4 * j + 3] * a.scale);
+        vv.x = pack_bf(dv[dt][4 * j], dv[dt][4 * j + 1]);
+        vv.y = pack_bf(dv[dt][4 * j + 2], dv[dt][4 * j + 3]);
+        *reinterpret_cast<u32x2_t*>(drow + (a.Hq + g) * D + d) = vk;
+        *reinterpret_cast<u32x2_t*>(drow + (a.Hq + a.Hkv + g) * D + d) = vv;
+      }
+  }
+}
+
 // --------------------------------------------------------------------- dQ
 // Two waves per SIMD as in the forward (a few registers spill, still 4-12%
 // faster than one wave); the dK/dV kernel stays at one (its accumulators
@@ -597,12 +809,17 @@ template <int D>
 hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   constexpr size_t lds_kv = (2 * 64 * (D + 8) + 2 * D * (64 + 8)) * sizeof(uint16_t) + 2 * 64 * sizeof(float);
   constexpr size_t lds_q = (2 * 64 * (D + 8) + D * (64 + 8)) * sizeof(uint16_t);
+  constexpr size_t lds_dl = 2 * 2 * 64 * D * sizeof(uint16_t) + 4 * 64 * sizeof(float);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(attn_dkdv_kernel<D>, lds_kv);
     if (e != hipSuccess) return e;
     e = set_lds(attn_dq_kernel<D>, lds_q);
     if (e != hipSuccess) return e;
+    if constexpr (D == 128) {
+      e = set_lds(attn_dkdv_dl_kernel<D>, lds_dl);
+      if (e != hipSuccess) return e;
+    }
     attr = true;
   }
   const long rows = (long)a.B * a.T * a.Hq;
@@ -610,7 +827,10 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (a.T + 127) / 128;
-  hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_kv, s, a);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL(attn_dkdv_dl_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_dl, s, a);
+  else
+    hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_kv, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.T + 127) / 128;

@@ -1,13 +1,14 @@
-"""Static check of the compiled GEMM kernels (no GPU needed).
+"""Static check of the compiled direct-to-LDS kernels (no GPU needed).
 
-The direct-to-LDS GEMM issues its LDS transpose reads (ds_read_b64_tr_b16)
-as inline asm, outside the compiler's wait tracking, and waits for them
-itself with s_waitcnt lgkmcnt(0).  This test compiles gemm.hip to gfx950
-assembly with the library's own flags and walks every such kernel: between
-a transpose read and the next lgkmcnt(0) wait, no instruction may read or
-overwrite the read's destination registers, and no branch or label may
-intervene (the result lands asynchronously, so an early use would see stale
-data)."""
+The direct-to-LDS GEMM and the head_dim-128 attention dK/dV kernel issue LDS
+reads as inline asm (the GEMM's transpose reads, every tile read of the
+attention kernel), outside the compiler's wait tracking, and wait for them
+themselves with s_waitcnt lgkmcnt(0).  This test compiles the sources to
+gfx950 assembly with the library's own flags and walks every such kernel:
+between an untracked LDS read and the next lgkmcnt(0) wait, no instruction
+may read or overwrite the read's destination registers, and no branch or
+label may intervene (the result lands asynchronously, so an early use would
+see stale data)."""
 import os
 import re
 import subprocess
@@ -17,7 +18,7 @@ import pytest
 
 from layer_streamed_amd import build
 
-SRC = os.path.join(os.path.dirname(build.__file__), "csrc", "gemm.hip")
+CSRC = os.path.join(os.path.dirname(build.__file__), "csrc")
 
 _REG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
 
@@ -32,23 +33,24 @@ def _regs(text):
     return out
 
 
-def _device_asm():
+def _device_asm(src):
     if not os.path.exists(build.HIPCC):
         pytest.skip("hipcc not available")
     with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "gemm.s")
+        out = os.path.join(d, "k.s")
         flags = [f for f in build.HIP_FLAGS if f != "-fPIC"]
-        subprocess.run([build.HIPCC] + flags + ["--cuda-device-only", "-S", SRC, "-o", out],
+        subprocess.run([build.HIPCC] + flags + ["--cuda-device-only", "-S",
+                                                os.path.join(CSRC, src), "-o", out],
                        check=True, capture_output=True)
         return open(out).read()
 
 
-def _kernels(asm):
-    """(name, body lines) of every direct-to-LDS GEMM kernel."""
+def _kernels(asm, pattern):
+    """(name, body lines) of every kernel whose symbol contains `pattern`."""
     ks = []
     cur, body = None, []
     for line in asm.splitlines():
-        m = re.match(r"^(_Z\S*gemm_dl_kernel\S*):", line)
+        m = re.match(r"^(_Z\S*" + pattern + r"\S*):", line)
         if m:
             cur, body = m.group(1), []
             continue
@@ -63,7 +65,14 @@ def _kernels(asm):
 
 def _check(body):
     pending = set()
+    in_asm = False
     for line in body:
+        if ";;#ASMSTART" in line:
+            in_asm = True
+            continue
+        if ";;#ASMEND" in line:
+            in_asm = False
+            continue
         code = line.split(";")[0].strip()
         if not code or code.startswith("."):
             if code.startswith(".LBB") and pending:
@@ -77,7 +86,7 @@ def _check(body):
             if pending:
                 return f"branch with transpose reads in flight: {code}"
             continue
-        if op == "ds_read_b64_tr_b16":
+        if op == "ds_read_b64_tr_b16" or (in_asm and op.startswith("ds_read")):
             dst, addr = code[len(op):].split(",", 1)
             if _regs(addr) & pending or _regs(dst) & pending:
                 return f"transpose read uses an in-flight register: {code}"
@@ -88,10 +97,12 @@ def _check(body):
     return None if not pending else "kernel ends with transpose reads in flight"
 
 
-def test_transpose_reads_are_waited_for_before_use():
-    kernels = _kernels(_device_asm())
+@pytest.mark.parametrize("src,pattern", [("gemm.hip", "gemm_dl_kernel"),
+                                         ("attention.hip", "attn_dkdv_dl_kernel")])
+def test_untracked_lds_reads_are_waited_for_before_use(src, pattern):
+    kernels = _kernels(_device_asm(src), pattern)
     with_tr = [(n, b) for n, b in kernels if any("ds_read_b64_tr_b16" in l for l in b)]
-    assert with_tr, "no direct-to-LDS kernel with transpose reads found"
+    assert with_tr, f"no {pattern} kernel with transpose reads found"
     bad = {n: e for n, b in with_tr if (e := _check(b))}
     assert not bad, bad
 
@@ -109,3 +120,10 @@ def test_checker_catches_planted_early_use():
     assert "touched" in _check(partial)
     branch = ["ds_read_b64_tr_b16 v[10:11], v5", "s_cbranch_scc1 .LBB0_3"]
     assert "branch" in _check(branch)
+    # an asm-issued row read is untracked too; a compiler-issued one is not
+    asm_row = [";;#ASMSTART", "ds_read_b128 v[10:13], v5", ";;#ASMEND",
+               "v_mfma_f32_32x32x16_bf16 v[0:15], v[10:13], v[20:23], v[0:15]"]
+    assert "touched" in _check(asm_row)
+    compiler_row = ["ds_read_b128 v[10:13], v5",
+                    "v_mfma_f32_32x32x16_bf16 v[0:15], v[10:13], v[20:23], v[0:15]"]
+    assert _check(compiler_row) is None
