@@ -35,11 +35,19 @@ enum {
  *   NT: C[M,N] = A[M,K] B[N,K]^T;  NN: C = A[M,K] B[K,N];  TN: C = A[K,M]^T B[K,N].
  * Row strides lda/ldb/ldc/ldr/ldc2/ldg are in elements.  K and the
  * contiguous dimension of every operand must be multiples of 8; M and N
- * (the strided ones) may be anything.  A and B must be 16-byte aligned. */
+ * (the strided ones) may be anything.  A and B must be 16-byte aligned.
+ * workspace (device, 16-byte aligned; may be null): when the 256 x 256
+ * tiles leave a last round at most half full, its tiles are split along K
+ * and their fp32 partial sums go here (up to MT_GEMM_SPLIT_BYTES); with a
+ * smaller or no workspace the product runs unsplit.  Both are
+ * deterministic; they differ only in fp32 summation order.  Calls sharing a
+ * workspace must not overlap. */
+#define MT_GEMM_SPLIT_BYTES ((size_t)64 << 20)
 mt_status mt_op_gemm(int32_t layout, int32_t epilogue, int32_t M, int32_t N, int32_t K,
                      const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                      int64_t ldc, const void* R, int64_t ldr, void* C2, int64_t ldc2,
-                     const void* G, int64_t ldg, int32_t F, void* stream);
+                     const void* G, int64_t ldg, int32_t F, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* The same product in the fp32 debug precision (MT_PREC_FP32_DEBUG of
  * mt.h): every operand, R, G and C2 is fp32, and so is C for MT_EPI_BF16

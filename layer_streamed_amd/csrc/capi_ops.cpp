@@ -30,7 +30,10 @@ const char* mt_last_error(void) { return g_last_error; }
 mt_status mt_op_gemm(int32_t layout, int32_t epilogue, int32_t M, int32_t N, int32_t K,
                      const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                      int64_t ldc, const void* R, int64_t ldr, void* C2, int64_t ldc2,
-                     const void* G, int64_t ldg, int32_t F, void* stream) {
+                     const void* G, int64_t ldg, int32_t F, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  MT_CHECK(!workspace || ((uintptr_t)workspace & 15u) == 0, MT_E_INVALID,
+           "mt_op_gemm: workspace must be 16-byte aligned");
   GemmArgs a;
   a.layout = layout; a.epi = epilogue; a.M = M; a.N = N; a.K = K;
   a.A = static_cast<const uint16_t*>(A); a.lda = lda;
@@ -40,6 +43,8 @@ mt_status mt_op_gemm(int32_t layout, int32_t epilogue, int32_t M, int32_t N, int
   a.C2 = static_cast<uint16_t*>(C2); a.ldc2 = ldc2;
   a.G = static_cast<const uint16_t*>(G); a.ldg = ldg;
   a.F = F;
+  a.ws = static_cast<float*>(workspace);
+  a.ws_elems = workspace ? (long)(workspace_bytes / sizeof(float)) : 0;
   if (const char* msg = gemm_check(a)) return set_error(MT_E_SHAPE, "mt_op_gemm: %s", msg);
   MT_HIP(gemm_launch(a, static_cast<hipStream_t>(stream)));
   return MT_OK;

@@ -17,6 +17,7 @@
 // workgroups on one XCD share A rows and B columns in that XCD's L2.
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 #include <type_traits>
 
@@ -659,6 +660,20 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, Acc (&acc)[TM][T
   }
 }
 
+// Tile of launch position pid: positions walk groups of 8 tile rows, each
+// group column by column, so tiles running at the same time share operand
+// panels in L2.
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tile_m,
+                                            int& tile_n) {
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int g = pid / per_group;
+  const int first_m = g * GROUP;
+  const int gm = min(tiles_m - first_m, GROUP);
+  tile_m = first_m + (pid % per_group) % gm;
+  tile_n = (pid % per_group) / gm;
+}
+
 // MI selects the MFMA: 32 (v_mfma_f32_32x32x16_bf16, 16-deep substeps) or
 // 16 (v_mfma_f32_16x16x32_bf16, 32-deep substeps, each 32 x 32 block of
 // the wave tile as four 16 x 16 blocks).  The two give bitwise equal
@@ -680,16 +695,23 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
 
   const int M = a.M, N = a.N, K = a.K;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int pid = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  constexpr int GROUP = 8;
-  const int per_group = GROUP * tiles_n;
-  const int g = pid / per_group;
-  const int first_m = g * GROUP;
-  const int gm = min(tiles_m - first_m, GROUP);
-  const int tile_m = first_m + (pid % per_group) % gm;
-  const int tile_n = (pid % per_group) / gm;
+  const int nk = K / BK;
+  // Workgroups past split_full each take 1/split_s of the k-steps of one of
+  // the last tiles (a partly filled last round spread over the chip) and
+  // leave fp32 partial sums for gemm_split_fixup_kernel.
+  int pid = blockIdx.x, piece = -1, kbeg = 0, kend = nk;
+  if (a.split_s > 1 && pid >= a.split_full) {
+    const int x = pid - a.split_full;
+    piece = x % a.split_s;
+    pid = a.split_full + x / a.split_s;
+    kbeg = (int)((long)nk * piece / a.split_s);
+    kend = (int)((long)nk * (piece + 1) / a.split_s);
+  } else {
+    const int nwg = a.split_s > 1 ? a.split_full : (int)gridDim.x;
+    if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  }
+  int tile_m, tile_n;
+  tile_coords(pid, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -722,9 +744,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
       }
     }
 
-  const int nk = K / BK;
   auto issue = [&](int kt) {
-    if (kt >= nk) return;
+    if (kt >= kend) return;
     char* base = dl_smem + (kt % NS) * STAGE;
 #pragma unroll
     for (int p = 0; p < A_PER; ++p)
@@ -811,12 +832,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
   };
 
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st) issue(st);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int st = 0; st < NS - 1; ++st) issue(kbeg + st);
+  for (int kt = kbeg; kt < kend; ++kt) {
     // this wave's loads for stage kt are done once at most `ahead` later
     // stages are still in flight; the barrier then covers every wave's loads
     // and every wave's reads of the stage about to be refilled
-    const int ahead = min(NS - 2, nk - 1 - kt);
+    const int ahead = min(NS - 2, kend - 1 - kt);
     if (ahead >= 2) wait_vmcnt<2 * LPW>();
     else if (ahead == 1) wait_vmcnt<LPW>();
     else wait_vmcnt<0>();
@@ -825,10 +846,88 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
     if constexpr (MI == 16) compute16(kt);
     else compute(kt);
   }
+  if (piece >= 0) {
+    // partial sums of this tile's k-range, tile-local row-major [BM][BN]
+    float* part = a.ws + ((long)(pid - a.split_full) * a.split_s + piece) * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r0 = wm * TM * 32 + i * 32, c0 = wn * TN * 32 + j * 32;
+        if constexpr (MI == 16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              part[(r0 + 16 * (q >> 1) + 4 * (lane >> 4) + r) * BN + c0 + 16 * (q & 1) + (lane & 15)] =
+                  acc[i][j].s[q][r];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            part[(r0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * BN + c0 + (lane & 31)] = acc[i][j][e];
+        }
+      }
+    return;
+  }
   // the ring is free once every wave has finished reading its last stage
   __syncthreads();
   epilogue_lds<WM, WN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane,
                                     dl_smem + wave * (SWI ? 2 : 1) * EPI_SLOT);
+}
+
+// The split tail tiles: sums each output element's split_s partials in
+// piece order (a fixed order: the result does not depend on timing), then
+// applies the epilogue (bf16, fp32, fp32 accumulate, residual add).  One
+// thread per 4 consecutive columns of a tile row.
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void gemm_split_fixup_kernel(const GemmArgs a) {
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  constexpr int PER_TILE = BM * BN / 4;
+  const int t = (int)(idx / PER_TILE), w = (int)(idx % PER_TILE);
+  const int r = w / (BN / 4), c = 4 * (w % (BN / 4));
+  int tile_m, tile_n;
+  tile_coords(a.split_full + t, tiles_m, tiles_n, tile_m, tile_n);
+  const int row = tile_m * BM + r, col0 = tile_n * BN + c;
+  if (row >= a.M) return;
+  const float* part = a.ws + (long)t * a.split_s * (BM * BN) + r * BN + c;
+  f32x4_t v = *reinterpret_cast<const f32x4_t*>(part);
+  for (int p = 1; p < a.split_s; ++p) {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(part + (long)p * (BM * BN));
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int col = col0 + e;
+    if (col >= a.N) break;
+    const long o = (long)row * a.ldc + col;
+    if constexpr (EPI == EPI_BF16) {
+      reinterpret_cast<uint16_t*>(a.C)[o] = f2bf(v[e]);
+    } else if constexpr (EPI == EPI_F32) {
+      reinterpret_cast<float*>(a.C)[o] = v[e];
+    } else if constexpr (EPI == EPI_ACC_F32) {
+      reinterpret_cast<float*>(a.C)[o] += v[e];
+    } else if constexpr (EPI == EPI_RESID_BF16) {
+      reinterpret_cast<uint16_t*>(a.C)[o] = f2bf(bf2f(a.R[(long)row * a.ldr + col]) + v[e]);
+    }
+  }
+}
+
+// Compute units of the current device (one 256 x 256 workgroup fits per CU).
+inline int cu_count() {
+  static int n[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!n[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
 }
 
 // Whether the epilogue's 16-byte accesses are aligned for every row.
@@ -862,7 +961,40 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   GemmArgs b = a;
   b.vec = epi_vec_ok(a) ? 1 : 0;
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, b);
+  b.split_full = 0;
+  b.split_s = 1;
+  int grid = tiles, rem = 0;
+  // The 256 x 256 tile runs one workgroup per CU, so the tiles past the
+  // last full round leave most CUs idle for a whole tile time.  When that
+  // round is at most half full (and a workspace is given), each of its
+  // tiles is split along K into up to 8 pieces that fill the chip, and a
+  // fix-up pass sums the pieces in order and applies the epilogue.
+  constexpr bool SPLITTABLE = BM == 256 && BN == 256 &&
+                              (EPI == EPI_BF16 || EPI == EPI_F32 || EPI == EPI_ACC_F32 ||
+                               EPI == EPI_RESID_BF16);
+  if constexpr (SPLITTABLE) {
+    if (a.ws) {
+      const int P = cu_count();
+      rem = tiles % P;
+      const int full = tiles - rem;
+      if (full > 0 && rem > 0 && 2 * rem <= P) {
+        const int sp = std::min({P / rem, a.K / BK / 4, 8});
+        if (sp >= 2 && (long)rem * sp * BM * BN <= a.ws_elems) {
+          b.split_full = full;
+          b.split_s = sp;
+          grid = full + rem * sp;
+        }
+      }
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WM * WN * 64), lds, s, b);
+  if constexpr (SPLITTABLE) {
+    if (b.split_s > 1) {
+      const long threads = (long)rem * BM * BN / 4;
+      hipLaunchKernelGGL((gemm_split_fixup_kernel<BM, BN, EPI>), dim3((unsigned)((threads + 255) / 256)),
+                         dim3(256), 0, s, b);
+    }
+  }
   return hipGetLastError();
 }
 

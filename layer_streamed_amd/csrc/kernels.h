@@ -43,6 +43,11 @@ struct GemmArgsT {
   const E* G = nullptr; long ldg = 0;
   int F = 0;  // FFN width for the SwiGLU epilogues
   int vec = 0;  // set by the launcher: strides and alignment allow 16-byte epilogue accesses
+  // fp32 workspace for splitting the tiles of a partly filled last round
+  // along K (null: no split; the 256 x 256 tile needs up to 64 MiB)
+  float* ws = nullptr;
+  long ws_elems = 0;
+  int split_full = 0, split_s = 1;  // set by the launcher
 };
 using GemmArgs = GemmArgsT<uint16_t>;
 using GemmArgsF32 = GemmArgsT<float>;

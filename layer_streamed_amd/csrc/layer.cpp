@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <string>
+#include <type_traits>
 
 #include "kernels.h"
 #include "status.h"
@@ -95,8 +96,23 @@ namespace {
 
 // Workspace of one layer call.  E is the storage type of activations
 // (uint16_t: bf16 bit patterns; float: the fp32 debug precision).
+// fp32 partial sums of the GEMMs' split tail tiles (up to 256 tiles of
+// 256 x 256).  Only bf16 products tiled 256 x 256 split, and that tile needs
+// at least 768 tiles, so smaller models carve nothing.
+constexpr size_t SPLIT_ELEMS = (size_t)256 * 256 * 256;
+
+template <class E>
+size_t split_elems(const Dims& d, bool head) {
+  if (!std::is_same_v<E, uint16_t>) return 0;
+  const double D = d.D, H = d.H, F = d.F, V = d.V, C = d.mlp_chunk, Ch = d.head_chunk;
+  const double largest = head ? std::max(Ch * V, V * H)
+                              : std::max({C * 2 * F, 2 * F * H, D * (double)d.NQKV, D * H});
+  return largest >= 768.0 * 256 * 256 ? SPLIT_ELEMS : 0;
+}
+
 template <class E>
 struct LayerWs {
+  float* split;  // GEMM split-tail workspace (null for fp32 storage)
   float *cos_t, *sin_t, *rstd1, *rstd2, *lse;
   E *a, *qkv, *o, *x_mid, *b, *gu, *m;
   // backward only
@@ -129,6 +145,7 @@ LayerWs<E> carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
   Carve c{base};
   LayerWs<E> w{};
   const size_t D = d.D, H = d.H, C = d.mlp_chunk;
+  if (const size_t n = split_elems<E>(d, false)) w.split = c.take<float>(n);
   if (which == 3) {
     carve_bwd_scratch(d, c, &w);
     *bytes = c.off + 256;
@@ -175,9 +192,12 @@ inline std::string kernel_name(const GemmArgsT<float>& g) {
   return "gemm_f32_kernel<" + std::to_string(lay) + ", " + std::to_string(g.epi) + ">";
 }
 
+// `split`: the workspace's split-tail area (SPLIT_ELEMS floats), or null.
 template <class E>
-mt_status run_gemm(const GemmArgsT<E>& g, hipStream_t s, Probe* probe) {
+mt_status run_gemm(GemmArgsT<E> g, hipStream_t s, Probe* probe, float* split) {
   if (const char* m = gemm_check(g)) return set_error(MT_E_SHAPE, "layer GEMM: %s", m);
+  g.ws = split;
+  g.ws_elems = split ? (long)SPLIT_ELEMS : 0;
   const bool timed = probe && probe->used + 2 <= (int)probe->ev.size();
   if (timed) MT_HIP(hipEventRecord(probe->ev[probe->used], s));
   MT_HIP(gemm_launch(g, s));
@@ -214,14 +234,14 @@ mt_status attn_half(const Dims& d, const LayerW<E>& w, const E* x, const LayerWs
   MT_HIP(rmsnorm_fwd(x, w.g1, ws.a, ws.rstd1, d.D, d.H, d.eps, s));
   MT_RUN(run_gemm(gemm<E>(GEMM_NT, EPI_BF16, d.D, d.NQKV, d.H, ws.a, d.H, w.wqkv, d.H, ws.qkv,
                           d.NQKV),
-                  s, probe));
+                  s, probe, ws.split));
   MT_HIP(rope_apply(ws.qkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 0, s));
   MT_HIP(attn_fwd(ws.qkv, ws.o, ws.lse, d.B, d.T, d.Hq, d.Hkv, d.d, s));
   GemmArgsT<E> go = gemm<E>(GEMM_NT, EPI_RESID_BF16, d.D, d.H, d.Qd, ws.o, d.Qd, w.wo, d.Qd,
                             ws.x_mid, d.H);
   go.R = x;
   go.ldr = d.H;
-  MT_RUN(run_gemm(go, s, probe));
+  MT_RUN(run_gemm(go, s, probe, ws.split));
   MT_HIP(rmsnorm_fwd(ws.x_mid, w.g2, ws.b, ws.rstd2, d.D, d.H, d.eps, s));
   return MT_OK;
 }
@@ -248,12 +268,12 @@ mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* 
       gu.C2 = ws.gu;
       gu.ldc2 = 2 * d.F;
     }
-    MT_RUN(run_gemm(gu, s, probe));
+    MT_RUN(run_gemm(gu, s, probe, ws.split));
     GemmArgsT<E> dn = gemm<E>(GEMM_NT, EPI_RESID_BF16, rows, d.H, d.F, ws.m, d.F, w.wd, d.F,
                               x_out + (size_t)r0 * d.H, d.H);
     dn.R = ws.x_mid + (size_t)r0 * d.H;
     dn.ldr = d.H;
-    MT_RUN(run_gemm(dn, s, probe));
+    MT_RUN(run_gemm(dn, s, probe, ws.split));
   }
   return MT_OK;
 }
@@ -298,7 +318,7 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
     gu.F = d.F;
     gu.C2 = ws.gu;
     gu.ldc2 = 2 * d.F;
-    if (!saved) MT_RUN(run_gemm(gu, s, probe));
+    if (!saved) MT_RUN(run_gemm(gu, s, probe, ws.split));
     // dgate, dup from dm = dy W_down (NN) fused with the SwiGLU derivative
     GemmArgsT<E> dm = gemm<E>(GEMM_NN, EPI_SWIGLU_BWD, rows, d.F, d.H, dy_c, d.H, w.wd, d.F,
                               ws.dgu, 2 * d.F);
@@ -307,22 +327,22 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
     dm.ldg = 2 * d.F;
     dm.C2 = ws.dgu;
     dm.ldc2 = 2 * d.F;
-    MT_RUN(run_gemm(dm, s, probe));
+    MT_RUN(run_gemm(dm, s, probe, ws.split));
     // dW_down = dy^T m  (TN: A = dy as [K=rows, M=H], B = m [rows, F])
     MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.H, d.F, rows, dy_c, d.H,
                             ws.m, d.F,
                             chunked ? static_cast<void*>(ws.acc_d) : static_cast<void*>(gd), d.F),
-                    s, probe));
+                    s, probe, ws.split));
     // dW_gu = dgu^T b  (TN: A = dgu [rows, 2F], B = b [rows, H])
     MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, 2 * d.F, d.H, rows, ws.dgu,
                             2 * d.F, b_c, d.H,
                             chunked ? static_cast<void*>(ws.acc_gu) : static_cast<void*>(ggu),
                             d.H),
-                    s, probe));
+                    s, probe, ws.split));
     // db = dgu W_gu  (NN: B = W_gu [2F, H])
     MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, rows, d.H, 2 * d.F, ws.dgu, 2 * d.F, w.wgu, d.H,
                             ws.db + (size_t)r0 * d.H, d.H),
-                    s, probe));
+                    s, probe, ws.split));
   }
   if (chunked) {
     MT_HIP(cast_f32(ws.acc_d, gd, (size_t)d.H * d.F, s));
@@ -335,20 +355,20 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
   // ---- output projection
   MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, d.D, d.Qd, d.H, ws.dx_mid, d.H, w.wo, d.Qd, ws.dout,
                           d.Qd),
-                  s, probe));
+                  s, probe, ws.split));
   MT_RUN(run_gemm(gemm<E>(GEMM_TN, EPI_BF16, d.H, d.Qd, d.D, ws.dx_mid, d.H, ws.o, d.Qd, g.w_o,
                           d.Qd),
-                  s, probe));
+                  s, probe, ws.split));
   // ---- attention and RoPE
   MT_HIP(attn_bwd(ws.qkv, ws.o, ws.lse, ws.dout, ws.delta, ws.dqkv, d.B, d.T, d.Hq, d.Hkv, d.d, s));
   MT_HIP(rope_apply(ws.dqkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 1, s));
   // ---- QKV projection
   MT_RUN(run_gemm(gemm<E>(GEMM_TN, EPI_BF16, d.NQKV, d.H, d.D, ws.dqkv, d.NQKV, ws.a, d.H,
                           g.w_qkv, d.H),
-                  s, probe));
+                  s, probe, ws.split));
   MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, d.D, d.H, d.NQKV, ws.dqkv, d.NQKV, w.wqkv, d.H, ws.da,
                           d.H),
-                  s, probe));
+                  s, probe, ws.split));
   // ---- first norm (residual dx_mid)
   MT_HIP(rmsnorm_bwd(ws.da, x_in, w.g1, ws.rstd1, ws.dx_mid, dx, ws.dg_part, d.D, d.H, s));
   MT_HIP(reduce_rows(ws.dg_part, nblk, d.H, static_cast<E*>(g.attn_norm), s));
@@ -411,6 +431,7 @@ mt_status layer_bwd_impl(const Dims& d, const mt_layer_view& w, const void* x_in
 namespace {
 template <class E>
 struct HeadWs {
+  float* split;  // GEMM split-tail workspace (null for fp32 storage)
   E *h, *dlogits, *dh;
   float *rstd, *logits, *loss_part, *dg_part, *acc_out;
 };
@@ -419,6 +440,7 @@ HeadWs<E> carve_head(const Dims& d, char* base, size_t* bytes) {
   Carve c{base};
   HeadWs<E> w{};
   const size_t D = d.D, H = d.H, Ch = d.head_chunk;
+  if (const size_t n = split_elems<E>(d, true)) w.split = c.take<float>(n);
   w.h = c.take<E>(D * H);
   w.dh = c.take<E>(D * H);
   w.rstd = c.take<float>(D);
@@ -447,16 +469,16 @@ mt_status head_t(const Dims& d, const E* g_f, const E* w_out, const E* x_L,
     const E* h_c = ws.h + (size_t)r0 * d.H;
     MT_RUN(run_gemm(gemm<E>(GEMM_NT, EPI_F32, rows, d.V, d.H, h_c, d.H, w_out, d.H, ws.logits,
                             d.V),
-                    s, probe));
+                    s, probe, ws.split));
     MT_HIP(ce_rows(ws.logits, targets + r0, ws.dlogits, ws.loss_part + r0, rows, d.V, inv_n, s));
     MT_RUN(run_gemm(gemm<E>(GEMM_NN, EPI_BF16, rows, d.H, d.V, ws.dlogits, d.V, w_out, d.H,
                             ws.dh + (size_t)r0 * d.H, d.H),
-                    s, probe));
+                    s, probe, ws.split));
     MT_RUN(run_gemm(gemm<E>(GEMM_TN, chunked ? EPI_ACC_F32 : EPI_BF16, d.V, d.H, rows, ws.dlogits,
                             d.V, h_c, d.H,
                             chunked ? static_cast<void*>(ws.acc_out) : static_cast<void*>(dw_out),
                             d.H),
-                    s, probe));
+                    s, probe, ws.split));
   }
   if (chunked) MT_HIP(cast_f32(ws.acc_out, dw_out, (size_t)d.V * d.H, s));
   MT_HIP(sum_loss(ws.loss_part, d.D, inv_n, loss_dev, s));

@@ -96,7 +96,7 @@ _lib.mt_last_error.argtypes = []
 
 _SIGS = {
     "mt_op_gemm": (_I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
-                   _P, _I64, _P, _I64, _I32, _P),
+                   _P, _I64, _P, _I64, _I32, _P, _SZ, _P),
     "mt_op_gemm_f32": (_I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                        _P, _I64, _P, _I64, _I32, _P),
     "mt_op_attn_fwd_f32": (_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
@@ -183,10 +183,17 @@ def model_cfg(shape) -> ModelCfg:
 
 
 # ----------------------------------------------------------------- op calls
+GEMM_SPLIT_BYTES = 64 << 20  # MT_GEMM_SPLIT_BYTES
+
+
 def gemm(layout, epi, M, N, K, A, lda, B, ldb, Cm, ldc, R=None, ldr=0, C2=None, ldc2=0,
-         G=None, ldg=0, F=0, stream=None):
+         G=None, ldg=0, F=0, workspace=None, stream=None):
+    """`workspace`: optional device tensor for the split tail tiles (see
+    mt_op_gemm); None runs every tile whole."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(call("mt_op_gemm", layout, epi, M, N, K, ptr(A), lda, ptr(B), ldb, ptr(Cm), ldc,
-               ptr(R), ldr, ptr(C2), ldc2, ptr(G), ldg, F, stream_handle(stream)), "mt_op_gemm")
+               ptr(R), ldr, ptr(C2), ldc2, ptr(G), ldg, F, ptr(workspace), ws_bytes,
+               stream_handle(stream)), "mt_op_gemm")
 
 
 def gemm_f32(layout, epi, M, N, K, A, lda, B, ldb, Cm, ldc, R=None, ldr=0, C2=None, ldc2=0,

@@ -475,3 +475,54 @@ def test_nonfinite_flags(f32):
                        None) == 0
         torch.cuda.synchronize()
         assert int(flags.sum()) == 1, (pos, val)
+
+
+@pytest.mark.parametrize("layout,M,N,K,epi", [
+    # 896 tiles of 256 x 256 on 256 CUs: a half-full last round, split in 2
+    (1, 16384, 3584, 4608, 0), (0, 16384, 3584, 3584, 3), (0, 16384, 3584, 2048, 1),
+    (1, 16380, 3576, 4608, 0),
+    # 1036 tiles: 12 in the last round, split in 8 (in 4 where K is short)
+    (2, 3584, 18944, 16384, 0), (2, 18944, 3584, 1024, 2)])
+def test_gemm_split_tail_tiles(layout, M, N, K, epi):
+    """A workspace lets the tiles of a partly filled last round be split
+    along K: the result matches the unsplit product to bf16 rounding (fp32
+    outputs to 1e-6), matches a float64 evaluation on rows of the split
+    tiles, and is the same bits on every run."""
+    torch, mt = _torch(), _mt()
+    g = torch.Generator(device="cuda").manual_seed(M * 7 + N + K)
+    A = torch.randn((K, M) if layout == 2 else (M, K), device="cuda", generator=g).to(torch.bfloat16)
+    B = torch.randn((N, K) if layout == 0 else (K, N), device="cuda", generator=g).to(torch.bfloat16)
+    lda, ldb = (M if layout == 2 else K), (K if layout == 0 else N)
+    R = torch.randn((M, N), device="cuda", generator=g).to(torch.bfloat16) if epi == 3 else None
+    f32 = epi in (1, 2)
+    init = torch.randn((M, N), device="cuda", generator=g) if epi == 2 else None
+
+    def run(ws):
+        C = (init.clone() if init is not None else
+             torch.zeros((M, N), device="cuda", dtype=torch.float32 if f32 else torch.bfloat16))
+        mt.gemm(layout, epi, M, N, K, A, lda, B, ldb, C, N, R=R, ldr=N, workspace=ws)
+        return C
+
+    ws = torch.empty(mt.GEMM_SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+    c_whole, c_split, c_again = run(None), run(ws), run(ws)
+    torch.cuda.synchronize()
+    assert torch.equal(c_split, c_again)
+    a, b = c_split.float(), c_whole.float()
+    if f32:
+        assert float((a - b).abs().max() / b.abs().max()) < 1e-6
+    else:
+        # one rounding of a slightly different fp32 sum: at most one bf16 step,
+        # plus the fp32 summation-order difference where the sum cancels
+        slack = 1e-4 * float(b.pow(2).mean().sqrt())
+        excess = float(((a - b).abs() - (b.abs() * 2.0 ** -7 + slack)).max())
+        assert excess <= 0, excess
+    # the split tiles are the last ones launched: rows of the last tile rows
+    rows = np.concatenate([np.arange(M - 3, M), M - 1 - np.random.default_rng(2).choice(M // 4, 9, replace=False)])
+    at = (A[:, rows].t() if layout == 2 else A[rows]).float().cpu().numpy().astype(np.float64)
+    bt = B.float().cpu().numpy().astype(np.float64)
+    ref = at @ (bt.T if layout == 0 else bt)
+    if epi == 2:
+        ref = ref + init[rows].cpu().numpy()
+    if epi == 3:
+        ref = ref + R[rows].float().cpu().numpy()
+    assert rel_fro(c_split[rows].float().cpu().numpy(), ref) < (1e-5 if f32 else 5e-3)
