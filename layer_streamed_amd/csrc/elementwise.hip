@@ -88,8 +88,10 @@ __global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_fwd_kernel(
 // Backward.  Each workgroup (4 waves) owns RB_ROWS consecutive rows; every
 // wave walks its rows and keeps per-column dg sums for its chunk columns in
 // registers; the 4 waves are combined in LDS in fixed order and written as
-// one partial row of dg_part.  MAXC = max chunk iterations per lane.
-constexpr int RB_ROWS = 64;
+// one partial row of dg_part.  MAXC = max chunk iterations per lane.  16
+// rows per workgroup give the memory-bound kernel several waves per SIMD
+// (1024 workgroups for 16384 rows).
+constexpr int RB_ROWS = 16;
 
 template <class E, int MAXC>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
@@ -168,14 +170,31 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
   }
 }
 
+// out[col] = sum over the nblk partial rows.  A workgroup covers 64
+// columns with 4 row groups (rows b = 4 i + q); each thread keeps 8 running
+// sums (over i mod 8) so its loads stay independent; the sums are combined
+// in a fixed order (the result does not depend on timing).
 template <class E>
-__global__ void reduce_rows_kernel(const float* __restrict__ part, int nblk, int cols,
-                                   E* __restrict__ out) {
-  const int col = blockIdx.x * blockDim.x + threadIdx.x;
-  if (col >= cols) return;
-  float s = 0.f;
-  for (int b = 0; b < nblk; ++b) s += part[(long)b * cols + col];
-  St<E>::store(out + col, s);
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, int nblk,
+                                                          int cols, E* __restrict__ out) {
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + c;
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  if (col < cols) {
+    int i = 0;
+    for (; 4 * (i + 7) + q < nblk; i += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += part[(long)(4 * (i + u) + q) * cols + col];
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      if (4 * (i + u) + q < nblk) acc[u] += part[(long)(4 * (i + u) + q) * cols + col];
+  }
+  red[q][c] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  if (q == 0 && col < cols) St<E>::store(out + col, ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
 }
 
 __global__ void rope_table_kernel(float* cos_t, float* sin_t, int seq, int half, int head_dim,
@@ -189,24 +208,36 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, int seq, int half,
   sin_t[idx] = (float)sin(ang);
 }
 
-// One thread per (token, head, pair j): rotates (x_j, x_{j+d/2}).
+// One thread per (token, head, 8 consecutive pairs j): rotates
+// (x_j, x_{j+d/2}) with 16-byte accesses (half % 8 == 0).
 template <class E>
 __global__ void rope_kernel(E* __restrict__ qkv, long ldq, int tokens, int seq, int nh,
                             int half, const float* __restrict__ cos_t,
                             const float* __restrict__ sin_t, float sgn) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)tokens * nh * half;
+  const int h8 = half / 8;
+  const long total = (long)tokens * nh * h8;
   if (idx >= total) return;
-  const int j = (int)(idx % half);
-  const long th = idx / half;
+  const int j = 8 * (int)(idx % h8);
+  const long th = idx / h8;
   const int h = (int)(th % nh);
   const int tok = (int)(th / nh);
   const int t = tok % seq;
   E* p = qkv + (long)tok * ldq + (long)h * 2 * half;
-  const float c = cos_t[t * half + j], sn = sgn * sin_t[t * half + j];
-  const float x1 = St<E>::load(p + j), x2 = St<E>::load(p + j + half);
-  St<E>::store(p + j, x1 * c - x2 * sn);
-  St<E>::store(p + j + half, x2 * c + x1 * sn);
+  float x1[8], x2[8], c[8], sn[8];
+  St<E>::load8(p + j, x1);
+  St<E>::load8(p + j + half, x2);
+  St<float>::load8(cos_t + t * half + j, c);
+  St<float>::load8(sin_t + t * half + j, sn);
+  float o1[8], o2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float si = sgn * sn[i];
+    o1[i] = x1[i] * c[i] - x2[i] * si;
+    o2[i] = x2[i] * c[i] + x1[i] * si;
+  }
+  St<E>::store8(p + j, o1);
+  St<E>::store8(p + j + half, o2);
 }
 
 // Cross-entropy over one row of fp32 logits per workgroup (256 threads):
@@ -403,7 +434,7 @@ hipError_t rmsnorm_bwd_t(const E* dy, const E* x, const E* g, const float* rstd,
 
 template <class E>
 hipError_t reduce_rows_t(const float* part, int nblk, int cols, E* out, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_rows_kernel<E>, dim3((cols + 255) / 256), dim3(256), 0, s, part, nblk,
+  hipLaunchKernelGGL(reduce_rows_kernel<E>, dim3((cols + 63) / 64), dim3(256), 0, s, part, nblk,
                      cols, out);
   return hipGetLastError();
 }
@@ -413,7 +444,8 @@ hipError_t rope_apply_t(E* qkv, long ldq, int batch, int seq, int n_heads, int n
                         int head_dim, const float* cos_t, const float* sin_t, int inverse,
                         hipStream_t s) {
   const int tokens = batch * seq, nh = n_heads + n_kv_heads, half = head_dim / 2;
-  const long total = (long)tokens * nh * half;
+  if (half % 8) return hipErrorInvalidValue;
+  const long total = (long)tokens * nh * (half / 8);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(rope_kernel<E>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, qkv,
                      ldq, tokens, seq, nh, half, cos_t, sin_t, inverse ? -1.f : 1.f);
