@@ -96,6 +96,23 @@ typedef struct {
                                 only for the batch's rows at its start); reading or
                                 setting a parameter applies it first, so results are
                                 bitwise those of 0 (apply within the step). */
+  int32_t resident_layers;   /* C >= 0 (default 0): the weights of C layers (1 .. C, or
+                                all when C = n_layers) stay on the device from one step
+                                to the next.  Right after such a layer's host Adam
+                                update (in the backward, while the host link has time
+                                to spare) its new streamed copy is uploaded into one of
+                                C slots at the start of the arena, and the next step's
+                                forward, re-forward and backward read it there instead
+                                of loading it.  The forward, which is link-bound,
+                                streams C layers fewer, and its loads run ahead (up to
+                                the weight slots) while the resident layers compute.
+                                Layer 0 stays streamed: its update ends the step, and
+                                its upload would lengthen the step.  Device memory
+                                grows by C layers, independent of the depth.  The slots are trusted while steps get the same
+                                arena pointer and nothing writes its first
+                                C x layer bytes; setting a parameter, a failed step or
+                                another arena makes the next step load them again.
+                                Results are bitwise those of 0. */
   double lr, beta1, beta2, eps, weight_decay; /* Adam (weight_decay must be 0) */
 } mt_run_cfg;
 

@@ -124,17 +124,22 @@ mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t 
                          void* stream);
 
 /* The stream schedule of mt_stream_step for n_layers, checkpoint interval,
- * prefetch depth and kept internals (mt_run_cfg.keep_internals), as plain integers so its hazards can be checked
- * without a GPU.  out receives, per compute op, (kind, layer, load) with
- * kind 0 forward, 1 head, 2 segment re-forward, 3 (recompute+)backward, 4
- * forward keeping internals (the last segment, with keep_internals); then,
- * per weight load, (unit, slot, first_use, last_use, wait_use, gate_use):
- * the load may start once compute ops wait_use and gate_use have finished
- * (-1: no wait); slot -2 is the head's own slot.  counts = {n_ops, n_loads,
- * n_slots}.  MT_E_SHAPE if the schedule would deadlock, MT_E_OOM_HOST if
- * cap (entries) is too small. */
+ * prefetch depth, kept internals (mt_run_cfg.keep_internals) and resident
+ * layers (mt_run_cfg.resident_layers), as plain integers so its hazards can
+ * be checked without a GPU.  out receives, per compute op, (kind, layer,
+ * load) with kind 0 forward, 1 head, 2 segment re-forward, 3
+ * (recompute+)backward, 4 forward keeping internals (the last segment, with
+ * keep_internals); then, per weight load, (unit, slot, first_use, last_use,
+ * wait_use, gate_use): the load may start once compute ops wait_use and
+ * gate_use have finished (-1: no wait); slot -2 is the head's own slot,
+ * slot -3 - c resident slot c (layer 1 + c, or c when every layer is
+ * resident; one load serving every op of that layer, skipped when the
+ * previous step left the layer there).  counts = {n_ops, n_loads, n_slots}.
+ * MT_E_SHAPE if the schedule would deadlock, MT_E_OOM_HOST if cap
+ * (entries) is too small. */
 mt_status mt_debug_plan(int32_t n_layers, int32_t ckpt_interval, int32_t prefetch_depth,
-                        int32_t keep_internals, int32_t* out, size_t cap, int32_t* counts);
+                        int32_t keep_internals, int32_t resident_layers, int32_t* out, size_t cap,
+                        int32_t* counts);
 
 #ifdef __cplusplus
 }

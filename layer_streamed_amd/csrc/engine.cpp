@@ -18,7 +18,15 @@
 // without, the re-forward runs the first K-1 and each backward recomputes
 // its layer's forward.  A weight slot is reused only after the last compute
 // op that reads it has finished, and a load may run at most `depth` compute
-// ops ahead of its first use (depth 2 = double buffering).
+// ops ahead of its first use (depth 2 = double buffering).  R layers
+// (resident_layers: layers 1 .. R, or all of them) each have a slot of their
+// own that one load fills for every op of the layer; after the layer's host
+// update its new copy is uploaded there, so the next step skips that load.
+// They come first in the forward so that their compute, which needs no
+// transfer, covers the streamed layers' loads: with resident layers the
+// forward loads may run as far ahead as the slots allow.  Layer 0 stays
+// streamed because its update ends the step: its upload would add to the
+// step's tail.
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -59,8 +67,12 @@ struct Plan {
 
 static int plan_slots(int K, int depth) { return std::max(2, K + depth); }
 
-Plan build_plan(int L, int K, int depth, int n_slots, bool keep) {
+int resident_first(int L, int R) { return R < L ? 1 : 0; }
+
+Plan build_plan(int L, int K, int depth, int n_slots, bool keep, int R) {
   Plan p;
+  const int rs = resident_first(L, R);  // resident layers rs .. rs + R - 1
+  auto resident = [&](int l) { return l >= rs && l < rs + R; };
   p.n_slots = n_slots;
   auto add_load = [&](int unit) {
     p.loads.push_back({unit, -1, -1, -1, -1, -1});
@@ -89,15 +101,26 @@ Plan build_plan(int L, int K, int depth, int n_slots, bool keep) {
       continue;
     }
     std::vector<int> ld(e - a);
-    for (int l = a; l < e; ++l) ld[l - a] = add_load(l);
+    for (int l = a; l < e; ++l) ld[l - a] = resident(l) ? fwd_load[l] : add_load(l);
     for (int l = a; l < (keep ? e : e - 1); ++l) add_op(OP_REFWD, l, ld[l - a]);
     for (int l = e - 1; l >= a; --l) add_op(OP_BWD, l, ld[l - a]);
   }
   std::vector<int> free_after(n_slots, -1);
-  for (auto& ld : p.loads) {
-    ld.gate_use = ld.first_use - depth >= 0 ? ld.first_use - depth : -1;
+  for (size_t j = 0; j < p.loads.size(); ++j) {
+    PlanLoad& ld = p.loads[j];
+    // forward loads run up to n_slots ops ahead when resident layers give
+    // the link time to get ahead (slot reuse still waits for the readers)
+    const int ahead = (R > 0 && ld.first_use < L) ? std::max(depth, n_slots) : depth;
+    ld.gate_use = ld.first_use - ahead >= 0 ? ld.first_use - ahead : -1;
     if (ld.unit == L) {  // the head has a slot of its own
       ld.slot = -2;
+      ld.wait_use = -1;
+      // with resident layers, right behind the last layer's forward load
+      if (R > 0 && j > 0) ld.gate_use = std::min(ld.gate_use, p.loads[j - 1].gate_use);
+      continue;
+    }
+    if (resident(ld.unit)) {  // a resident layer's own slot
+      ld.slot = -3 - (ld.unit - rs);
       ld.wait_use = -1;
       continue;
     }
@@ -119,6 +142,7 @@ constexpr int NG = 6;  // device gradient ring depth
 // Device buffers of one step.  Weight slots, gradient buffers and
 // activations hold the model's streamed element type (es bytes each).
 struct Arena {
+  std::vector<char*> res;  // resident layers' slots (first in the arena)
   std::vector<char*> slot;
   char* head_slot = nullptr;
   char* gring[NG] = {};
@@ -148,6 +172,8 @@ Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
   const int L = M->cfg.n_layers, K = M->run.ckpt_interval;
   const size_t es = M->es;
   const size_t lay = M->ll.total * es, head = M->hl.total * es, act = (size_t)d.D * d.H * es;
+  // resident slots first: their place must not depend on the step's shape
+  for (int i = 0; i < M->run.resident_layers; ++i) a.res.push_back(c.take<char>(lay));
   const int ns = plan_slots(K, M->run.prefetch_depth);
   for (int i = 0; i < ns; ++i) a.slot.push_back(c.take<char>(lay));
   a.head_slot = c.take<char>(head);
@@ -302,17 +328,20 @@ size_t mt_stream_arena_bytes(const mt_model* model, int32_t batch, int32_t seq) 
   return stream_arena_bytes(model, d);
 }
 
-// Diagnostic: the plan for L layers, checkpoint interval K and prefetch
-// depth.  out receives, for each compute op, (kind, layer, load) and then,
+// Diagnostic: the plan for L layers, checkpoint interval K, prefetch depth
+// and resident layers.  out receives, for each compute op, (kind, layer, load) and then,
 // for each load, (unit, slot, first_use, last_use, wait_use, gate_use);
 // counts[0..2] = n_ops, n_loads, n_slots.  Returns MT_E_SHAPE if the plan is
 // invalid, MT_E_OOM_HOST if out is too small.
 mt_status mt_debug_plan(int32_t n_layers, int32_t ckpt_interval, int32_t prefetch_depth,
-                        int32_t keep_internals, int32_t* out, size_t cap, int32_t* counts) {
-  MT_CHECK(n_layers >= 1 && ckpt_interval >= 1 && prefetch_depth >= 1 && out && counts,
+                        int32_t keep_internals, int32_t resident_layers, int32_t* out, size_t cap,
+                        int32_t* counts) {
+  MT_CHECK(n_layers >= 1 && ckpt_interval >= 1 && prefetch_depth >= 1 && resident_layers >= 0 &&
+               resident_layers <= n_layers && out && counts,
            MT_E_INVALID, "mt_debug_plan: bad arguments");
   Plan p = build_plan(n_layers, ckpt_interval, prefetch_depth,
-                      plan_slots(ckpt_interval, prefetch_depth), keep_internals != 0);
+                      plan_slots(ckpt_interval, prefetch_depth), keep_internals != 0,
+                      resident_layers);
   counts[0] = (int32_t)p.ops.size();
   counts[1] = (int32_t)p.loads.size();
   counts[2] = p.n_slots;
@@ -361,7 +390,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
            arena_bytes, need);
   MT_CHECK(((uintptr_t)arena & 255) == 0, MT_E_INVALID, "mt_stream_step: arena must be 256-byte aligned");
   const bool keep = keep_mode(M, d);
-  Plan plan = build_plan(L, K, M->run.prefetch_depth, plan_slots(K, M->run.prefetch_depth), keep);
+  const int R = M->run.resident_layers, rs = resident_first(L, R);
+  Plan plan = build_plan(L, K, M->run.prefetch_depth, plan_slots(K, M->run.prefetch_depth), keep, R);
   MT_CHECK(!plan.error, MT_E_INVALID, "mt_stream_step: %s", plan.error);
 
   if (!M->sdma) {
@@ -468,6 +498,11 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   std::mutex loss_mu;
   std::condition_variable loss_cv;
   bool loss_ready = false;
+  // resident layers: which slots the previous step left current (read by
+  // the loader), which this step refilled after the layer's update (written
+  // by the optimizer thread)
+  std::vector<uint8_t> res_valid, res_uploaded((size_t)R, 0);
+  double res_bytes = 0;
 
   // --------------------------------------------------------- G thread
   // Waits on the host for each backward op, copies its gradient to a pinned
@@ -559,6 +594,16 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     } wake{load_mu, load_cv};
     for (size_t k = 0; k < plan.loads.size(); ++k) {
       const PlanLoad& ld = plan.loads[k];
+      if (ld.slot <= -3 && res_valid[-3 - ld.slot]) {
+        // left on the device by the previous step: nothing to copy
+        if (hipEventRecord(load_done[k], sW) != hipSuccess) {
+          w_fail = 1;
+          abort_all = true;
+          return;
+        }
+        publish(k + 1);
+        continue;
+      }
       const int need = std::max(ld.wait_use, ld.gate_use);
       {
         std::unique_lock<std::mutex> lk(load_mu);
@@ -575,7 +620,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       }
       if (ok) {
         const Unit& u = M->units[ld.unit];
-        char* dst = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+        char* dst = ld.slot >= 0 ? A.slot[ld.slot] : ld.slot == -2 ? A.head_slot : A.res[-3 - ld.slot];
         hipEvent_t c0 = get_ev(), c1 = get_ev();
         ok = c0 && c1 && hipEventRecord(c0, sW) == hipSuccess &&
              hipMemcpyAsync(dst, u.shadow, u.n * es, hipMemcpyHostToDevice, sW) == hipSuccess &&
@@ -669,6 +714,21 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
                           f32 ? static_cast<float*>(u.shadow) : nullptr, u.n, hp, M->pool.get());
             if (u.kept) memcpy(u.kept, x.host, u.n * es);
             ++units_updated;
+            if (x.unit >= rs && x.unit < rs + R) {
+              // a resident layer: its updated copy goes to its slot now, for
+              // the next step (every op of this step that reads the slot has
+              // finished: its gradient has landed)
+              const int c = x.unit - rs;
+              if (hipMemcpyAsync(A.res[c], u.shadow, u.n * es, hipMemcpyHostToDevice, sW) ==
+                  hipSuccess) {
+                res_uploaded[c] = 1;
+                res_bytes += (double)u.n * es;
+              } else {
+                a_fail = 1;
+                abort_all = true;
+                skip = true;
+              }
+            }
           }
         } else {
           Unit& u = M->units[L + 1];
@@ -738,6 +798,14 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   }
   if (ev.err != MT_OK) return set_error(MT_E_HIP, "mt_stream_step: event creation failed");
 
+  // the resident slots hold current copies only if the previous step left
+  // them in this same arena; until this step's uploads land, none does
+  if (M->resident_arena != arena || (int)M->resident_valid.size() != R)
+    M->resident_valid.assign((size_t)R, 0);
+  res_valid = M->resident_valid;
+  M->resident_valid.assign((size_t)R, 0);
+  M->resident_arena = arena;
+
   gthr = std::thread(g_main);
   athr = std::thread(a_main);
 
@@ -772,7 +840,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         goto drain;  // otherwise the failing thread's status is reported below
       }
       const PlanLoad& ld = plan.loads[op.load];
-      const char* w = ld.slot >= 0 ? A.slot[ld.slot] : A.head_slot;
+      const char* w =
+          ld.slot >= 0 ? A.slot[ld.slot] : ld.slot == -2 ? A.head_slot : A.res[-3 - ld.slot];
       // wait for this op's weights; the gap is the exposed transfer time
       hipEvent_t w0 = get_ev(), w1 = get_ev();
       MT_STEP_HIP(hipEventRecord(w0, sC));
@@ -903,6 +972,7 @@ drain:
     return fail;
   }
   M->step = t_step;
+  M->resident_valid = res_uploaded;  // the uploads completed with the W stream
   if (stats_out) {
     mt_step_stats& s = *stats_out;
     memset(&s, 0, sizeof(s));
@@ -937,7 +1007,7 @@ drain:
         snprintf(s.probe_kernel, sizeof s.probe_kernel, "%s", top->first.c_str());
       }
     }
-    s.h2d_bytes = h2d_bytes + h2d_load_bytes;
+    s.h2d_bytes = h2d_bytes + h2d_load_bytes + res_bytes;
     s.d2h_bytes = d2h_bytes;
     s.pinned_host_bytes = M->pinned_bytes;
     s.pageable_host_bytes = M->pageable_bytes;

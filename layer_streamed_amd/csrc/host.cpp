@@ -303,6 +303,7 @@ void mt_run_cfg_default(mt_run_cfg* r) {
   r->time_kernels = 1;
   r->keep_internals = 1;
   r->defer_updates = 1;
+  r->resident_layers = 0;
   r->lr = 1e-4;
   r->beta1 = 0.9;
   r->beta2 = 0.999;

@@ -183,6 +183,8 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
   MT_CHECK(run->host_alloc == MT_HOST_PINNED || run->host_alloc == MT_HOST_PAGEABLE, MT_E_INVALID,
            "bad host_alloc");
   MT_CHECK(run->weight_decay == 0.0, MT_E_INVALID, "weight decay is not supported");
+  MT_CHECK(run->resident_layers >= 0 && run->resident_layers <= cfg->n_layers, MT_E_INVALID,
+           "resident_layers must be in [0, n_layers]");
   MT_CHECK(run->lr > 0 && run->beta1 >= 0 && run->beta1 < 1 && run->beta2 >= 0 &&
                run->beta2 < 1 && run->eps >= 0,
            MT_E_INVALID, "bad Adam hyperparameters");
@@ -268,6 +270,7 @@ mt_status mt_model_set_param(mt_model* m, const char* name, const float* src, si
            name ? name : "(null)");
   MT_CHECK(n == r.n, MT_E_SHAPE, "mt_model_set_param: '%s' has %zu elements, got %zu", name, r.n, n);
   flush_pending(m);  // a pending update must not land on the new value later
+  m->resident_valid.assign(m->resident_valid.size(), 0);  // the device copies are stale now
   Unit& u = m->units[r.unit];
   const bool f32 = m->es == 4;
   m->pool->parallel_for(n, [&](size_t lo, size_t hi) {

@@ -103,6 +103,11 @@ struct mt_model {
   std::vector<hipEvent_t> events;  // grown on demand
   std::unique_ptr<mt::SdmaCopier> sdma;  // gradient offload engine (created on first step)
   mt::PendingAdam pending;
+  // resident layers (mt_run_cfg.resident_layers): which of the resident
+  // slots at the start of resident_arena hold their layer's current
+  // streamed copy, left there by the previous step
+  std::vector<uint8_t> resident_valid;
+  const void* resident_arena = nullptr;
   int64_t step = 0;
   bool broken = false;
   int64_t pinned_bytes = 0, pageable_bytes = 0;

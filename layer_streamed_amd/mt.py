@@ -51,7 +51,8 @@ class RunCfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "ckpt_interval", "prefetch_depth", "use_slab_pool", "n_slabs", "mlp_chunk_tokens",
         "head_chunk_tokens", "precision", "host_threads", "check_finite", "serialize",
-        "host_alloc", "keep_grads", "time_kernels", "keep_internals", "defer_updates")] + [
+        "host_alloc", "keep_grads", "time_kernels", "keep_internals", "defer_updates",
+        "resident_layers")] + [
         (n, C.c_double) for n in ("lr", "beta1", "beta2", "eps", "weight_decay")]
 
 
@@ -121,7 +122,7 @@ _SIGS = {
     "mt_host_adam": (_I32, _P, _P, _P, _P, _I32, _P, _SZ, _I64, _P),
     "mt_run_cfg_default": (None, _P),
     "mt_op_rmsnorm_bwd_workspace": (_SZ, _I32, _I32),
-    "mt_debug_plan": (_I32, _I32, _I32, _I32, _I32, _P, _SZ, _P),
+    "mt_debug_plan": (_I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P),
     "mt_layer_internals_bytes": (_SZ, _P, _P, _I32, _I32),
     "mt_layer_fwd_keep": (_I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
     "mt_layer_bwd_saved": (_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P, _SZ, _P),
@@ -296,14 +297,14 @@ def layer_bwd_saved(mcfg, rcfg, view, x_in, dy, dx, gview, batch, seq, internals
                ws.numel() * ws.element_size(), stream_handle(stream)), "mt_layer_bwd_saved")
 
 
-def debug_plan(n_layers, ckpt_interval, prefetch_depth, keep_internals=1):
+def debug_plan(n_layers, ckpt_interval, prefetch_depth, keep_internals=1, resident_layers=0):
     """The engine's schedule as (status, ops [n,3], loads [n,6], n_slots)."""
     import numpy as np
     cap = 64 * (n_layers + 2) * 4 + 64
     out = np.zeros(cap, np.int32)
     counts = np.zeros(3, np.int32)
-    st = call("mt_debug_plan", n_layers, ckpt_interval, prefetch_depth, keep_internals, ptr(out),
-              cap, ptr(counts))
+    st = call("mt_debug_plan", n_layers, ckpt_interval, prefetch_depth, keep_internals,
+              resident_layers, ptr(out), cap, ptr(counts))
     n_ops, n_loads, n_slots = (int(c) for c in counts)
     ops = out[: 3 * n_ops].reshape(n_ops, 3).copy()
     loads = out[3 * n_ops: 3 * n_ops + 6 * n_loads].reshape(n_loads, 6).copy()

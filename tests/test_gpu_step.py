@@ -90,9 +90,11 @@ def test_two_steps_match_oracle(tiny):
 @pytest.mark.parametrize("kw", [dict(serialize=1), dict(ckpt_interval=2), dict(prefetch_depth=1),
                                 dict(prefetch_depth=3), dict(use_slab_pool=0),
                                 dict(n_slabs=1), dict(host_threads=3), dict(keep_internals=0),
-                                dict(keep_internals=0, ckpt_interval=1), dict(defer_updates=0)],
+                                dict(keep_internals=0, ckpt_interval=1), dict(defer_updates=0),
+                                dict(resident_layers=1), dict(resident_layers=2)],
                          ids=["serialized", "K2", "depth1", "depth3", "no-pool", "one-slab",
-                              "3-threads", "recompute", "recompute-K1", "no-defer"])
+                              "3-threads", "recompute", "recompute-K1", "no-defer", "resident1",
+                              "resident2"])
 def test_schedule_invariance_bitwise(tiny, kw):
     s, w, ids = tiny
     base = _run(s, w, ids)
@@ -218,3 +220,63 @@ def test_deferred_updates_apply_before_reads_and_never_after_a_set(tiny):
     m.step(ids, arena, streams)  # uses the set head (no stale pending update)
     assert m.step_count == 2
     m.close()
+
+
+def _steps(shape, weights, ids, n, arenas=None, set_between=None, **run_kw):
+    """n steps; arenas[i] picks the arena of step i (0 or 1, two arenas of
+    the same size); set_between = (step, name, value) sets a parameter
+    before that step."""
+    torch, mt = _env()
+    m = mt.Model(shape, **run_kw)
+    m.set_params(weights)
+    B, T = ids.shape
+    ar = [torch.empty(m.arena_bytes(B, T), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    losses, h2d = [], []
+    for i in range(n):
+        if set_between and set_between[0] == i:
+            m.set_param(set_between[1], set_between[2])
+        loss, st = m.step(ids, ar[arenas[i] if arenas else 0], streams)
+        losses.append(loss)
+        h2d.append(st["h2d_bytes"])
+    names = synth.param_names(shape)
+    out = {"loss": losses, "h2d": h2d,
+           "master": {n_: m.get(n_, mt.GET_MASTER) for n_ in names},
+           "shadow": {n_: m.get(n_, mt.GET_SHADOW) for n_ in names}}
+    m.close()
+    return out
+
+
+def _same(a, b, names):
+    assert a["loss"] == b["loss"]
+    for n in names:
+        np.testing.assert_array_equal(a["master"][n], b["master"][n], err_msg=n)
+        np.testing.assert_array_equal(a["shadow"][n], b["shadow"][n], err_msg=n)
+
+
+@pytest.mark.parametrize("R", [1, 3, 5])
+def test_resident_layers_bitwise_over_steps(R):
+    """Resident layers (kept on the device between steps, refilled after
+    each update): three steps equal three steps without them bitwise, and
+    from the second step on the forward streams R layers fewer; a set
+    parameter or a different arena makes the next step load them again,
+    still with the same results."""
+    s = synth.CONFIGS["tiny-2l-h256"].with_(n_layers=5, ckpt_interval=2, seq=60, batch=3)
+    w = synth.make_weights(s, seed=4)
+    ids = synth.make_tokens(s, seed=5)
+    names = synth.param_names(s)
+    base = _steps(s, w, ids, 3)
+    res = _steps(s, w, ids, 3, resident_layers=R)
+    _same(base, res, names)
+    # step 1 loads the resident layers (and uploads their update); steps 2
+    # and 3 skip those loads but still upload the updates: the same bytes
+    # per step as step 1 minus R layer loads
+    assert res["h2d"][1] == res["h2d"][2] < res["h2d"][0]
+    # another arena in step 2, a set parameter before step 3
+    new = (w["layers.4.w_down"] * 0.5).astype(np.float32)
+    base2 = _steps(s, w, ids, 3, set_between=(2, "layers.4.w_down", new))
+    res2 = _steps(s, w, ids, 3, arenas=[0, 1, 1], set_between=(2, "layers.4.w_down", new),
+                  resident_layers=R)
+    _same(base2, res2, names)
+    assert res2["h2d"][1] == res2["h2d"][0]  # new arena: loaded again
+    assert res2["h2d"][2] == res2["h2d"][0]  # after a set: loaded again

@@ -12,19 +12,21 @@ import pytest
 FWD, HEAD, REFWD, BWD, FWDK = 0, 1, 2, 3, 4
 
 
-def _plan(L, K, depth, keep=1):
+def _plan(L, K, depth, keep=1, resident=0):
     from layer_streamed_amd import mt
-    return mt.debug_plan(L, K, depth, keep)
+    return mt.debug_plan(L, K, depth, keep, resident)
 
 
 @pytest.mark.parametrize("L", [1, 2, 5, 28])
 @pytest.mark.parametrize("K", [1, 2, 3, 4, 7, 28])
 @pytest.mark.parametrize("depth", [1, 2, 3])
 @pytest.mark.parametrize("keep", [0, 1])
-def test_plan_is_hazard_free(L, K, depth, keep):
+@pytest.mark.parametrize("resident", [0, 1, 5, 12, 28])
+def test_plan_is_hazard_free(L, K, depth, keep, resident):
     if K > L:
         K = L
-    st, ops, loads, n_slots = _plan(L, K, depth, keep)
+    R = min(resident, L)
+    st, ops, loads, n_slots = _plan(L, K, depth, keep, R)
     assert st == 0
     kinds = ops[:, 0].tolist()
     a_last = ((L - 1) // K) * K
@@ -54,17 +56,36 @@ def test_plan_is_hazard_free(L, K, depth, keep):
         unit, slot, first, last, wait, gate = loads[load]
         assert unit == (L if kind == HEAD else layer)
         assert first <= i <= last
+    # a resident layer (1 .. R, or all) has one load, in slot -3 - c,
+    # serving every op of it
+    rs = 1 if R < L else 0
+    for l in range(L):
+        used = {int(ld) for k, lay, ld in ops if k != HEAD and lay == l}
+        if rs <= l < rs + R:
+            assert len(used) == 1
+            assert loads[used.pop()][1] == -3 - (l - rs)
+    assert sum(1 for ld in loads if ld[1] <= -3) == R
     # loads are issued in order of first use; dependencies precede the use
     firsts = loads[:, 2].tolist()
     assert firsts == sorted(firsts)
-    for unit, slot, first, last, wait, gate in loads:
+    for j, (unit, slot, first, last, wait, gate) in enumerate(loads):
         assert wait < first and gate < first
-        assert gate == (first - depth if first - depth >= 0 else -1)
+        # forward loads look further ahead when resident layers leave the
+        # link idle; the head then follows the last layer's forward load
+        ahead = max(depth, n_slots) if (R > 0 and first < L) else depth
+        base = first - ahead if first - ahead >= 0 else -1
+        if unit == L and R > 0 and j > 0:
+            assert gate == min(base, loads[j - 1][5])
+        else:
+            assert gate == base
     # slot reuse: the next occupant waits for the last reader of the previous
     by_slot = {}
     for j, (unit, slot, first, last, wait, gate) in enumerate(loads):
         if slot == -2:
             assert unit == L
+            continue
+        if slot <= -3:
+            assert unit == rs + (-3 - slot) and wait == -1
             continue
         assert 0 <= slot < n_slots
         if slot in by_slot:
@@ -75,11 +96,12 @@ def test_plan_is_hazard_free(L, K, depth, keep):
 
 
 @pytest.mark.parametrize("keep", [0, 1])
-def test_plan_single_stream_replay_never_reads_stale_weights(keep):
+@pytest.mark.parametrize("resident", [0, 6])
+def test_plan_single_stream_replay_never_reads_stale_weights(keep, resident):
     """Replay the plan as the executor does on one in-order stream and track
     which unit each slot holds at every compute op."""
     L, K, depth = 28, 4, 2
-    st, ops, loads, n_slots = _plan(L, K, depth, keep)
+    st, ops, loads, n_slots = _plan(L, K, depth, keep, resident)
     assert st == 0
     holds = {}
     nxt = 0
@@ -90,6 +112,22 @@ def test_plan_single_stream_replay_never_reads_stale_weights(keep):
             nxt += 1
         unit, slot = loads[load][0], loads[load][1]
         assert holds[slot] == (unit, load), (i, kind, layer)
+
+
+def test_plan_resident_layers_skip_their_loads():
+    """With the last R layers resident, those layers have one load each (in
+    the first step the only copy of them; later steps skip it), and the
+    backward reloads only the streamed layers' segments."""
+    L, K = 28, 4
+    for R in (0, 4, 8, 12, 27, 28):
+        st, ops, loads, _ = _plan(L, K, 2, 1, R)
+        assert st == 0
+        rs = 1 if R < L else 0
+        # forward: one load per layer + head; backward: re-forward loads of
+        # the streamed layers outside the last segment
+        refwd_loaded = sum(1 for l in range(L - K) if not rs <= l < rs + R)
+        assert len(loads) == L + 1 + refwd_loaded
+        assert (ops[:, 0] == BWD).sum() == L
 
 
 def test_plan_counts_match_the_method():
