@@ -3,11 +3,11 @@
 Workload (default): Qwen2.5-7B-shaped decoder, random N(0, 0.02^2) init,
 batch 16 x seq 1024 uniform random token ids, checkpoint interval 4; bf16
 weights stream from pinned host memory, fp32 master + Adam states on the
-host, CPU Adam.  Layers 1-8 stay on the device between steps: each one's
-updated copy streams in during the backward right after its host update
-(--resident-layers).  A step is one full mt_stream_step (forward, head,
-segment re-forward, recompute + backward, gradient offload, CPU Adam of
-every unit).
+host, CPU Adam.  Layers 1-8 (at most a third of the layers) stay on the
+device between steps: each one's updated copy streams in during the
+backward right after its host update (--resident-layers).  A step is one
+full mt_stream_step (forward, head, segment re-forward, recompute +
+backward, gradient offload, CPU Adam of every unit).
 
 Prints one JSON line: sustained TFLOPS by the 6ND + 12LHT^2 formula
 (MegaTrain listing page, Table 7 caption; T^2 term not scaled by the batch)
@@ -146,10 +146,11 @@ def main():
     ap.add_argument("--ckpt-interval", type=int, default=0)
     # layers whose weights stay on the device between steps (refilled after
     # each update, during the backward): the forward streams that many fewer.
-    # 8 at the 7B workload: 20 streamed layers (8.7 ms each on the host link)
-    # plus the LM head then fit within the forward's compute (about 7 ms per
-    # layer); measured 0 / 8 / 12 / 16: 1060 / 1030 / 1034 / 1029 ms per step
-    ap.add_argument("--resident-layers", type=int, default=8)
+    # Default (-1): 8, at most a third of the layers.  At the 7B workload 20
+    # streamed layers (8.7 ms each on the host link) plus the LM head then
+    # fit within the forward's compute (about 7 ms per layer); measured
+    # 0 / 8 / 12 / 16: 1060 / 1030 / 1034 / 1029 ms per step
+    ap.add_argument("--resident-layers", type=int, default=-1)
     # CPU threads for Adam and the embedding scatter (memory-bandwidth bound)
     ap.add_argument("--host-threads", type=int, default=16)
     # after the timed steps, three plain 1 GiB device copies: the known-size
@@ -171,12 +172,14 @@ def main():
     shape = synth.CONFIGS[args.config]
     if args.ckpt_interval:
         shape = shape.with_(ckpt_interval=args.ckpt_interval)
+    resident = (min(8, shape.n_layers // 3) if args.resident_layers < 0
+                else min(args.resident_layers, shape.n_layers))
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     model = mt.Model(shape, prefetch_depth=args.prefetch_depth,
                      use_slab_pool=0 if args.no_slab_pool else 1, check_finite=1,
                      time_kernels=1, host_threads=args.host_threads,
-                     resident_layers=min(args.resident_layers, shape.n_layers))
+                     resident_layers=resident)
     log(f"model created in {time.perf_counter() - t0:.1f}s")
     t0 = time.perf_counter()
     init_weights(model, shape, seed=0)
@@ -286,7 +289,7 @@ def main():
             "global_batch": shape.batch, "seq_len": shape.seq,
             "ckpt_interval": shape.ckpt_interval, "prefetch_depth": args.prefetch_depth,
             "slab_pool": not args.no_slab_pool,
-            "resident_layers": min(args.resident_layers, shape.n_layers),
+            "resident_layers": resident,
             "parallelism": "single-gpu layer streaming",
             "params": n_params,
         },

@@ -149,8 +149,9 @@ typedef struct {
   double host_ring_wait_ms, host_slab_wait_ms, host_op_wait_ms, host_adam_idle_ms;
   double probe_all_gemm_ms; /* summed duration of every timed GEMM launch of the step */
   char probe_kernel[96];    /* that instantiation's name, e.g. "gemm_dl_kernel<2, 2, 4, 4, 2, 0, 64, 2>" */
-  /* host-clock times (ms) from the start of mt_stream_step: first GPU work
-   * enqueued; the host seeing the last backward op complete; the last
+  /* host-clock times (ms) from the start of mt_stream_step: the step's
+   * input (the embedding gather) enqueued, the first weight loads already
+   * under way; the host seeing the last backward op complete; the last
    * gradient landed in host memory; the optimizer thread done (the step's
    * tail is what follows gpu_done_ms) */
   double host_start_ms, gpu_done_ms, grads_landed_ms, updates_done_ms;

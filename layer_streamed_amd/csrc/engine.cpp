@@ -433,24 +433,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     MT_CHECK(M->pending.head_grad, MT_E_OOM_HOST,
              "mt_stream_step: pinned allocation of the head's gradient buffer failed");
   }
-  // the previous step's embedding update, for the rows this batch gathers
-  // (the other rows follow on the optimizer thread during the forward)
-  apply_pending_embed_rows(M, tokens, (size_t)d.D);
-  // the embedding rows this batch touches: its gradient is zero elsewhere
+  // the embedding rows this batch touches (its gradient is zero elsewhere),
+  // filled once the weight loads are under way
   std::vector<int32_t> rows_now;
   std::vector<uint8_t> touched((size_t)d.V, 0);
-  for (int i = 0; i < d.D; ++i)
-    if (!touched[tokens[i]]) {
-      touched[tokens[i]] = 1;
-      rows_now.push_back(tokens[i]);
-    }
   const bool defer = M->run.defer_updates != 0;
-  // host: targets and the embedding gather (from the streamed copy)
   const Unit& emb = M->units[L + 1];
-  for (int b = 0; b < d.B; ++b)
-    for (int t = 0; t < d.T; ++t)
-      M->tgt_host[(size_t)b * d.T + t] = t + 1 < d.T ? tokens[(size_t)b * d.T + t + 1] : -1;
-  embed_gather(emb.shadow, tokens, (size_t)d.D, (size_t)d.H * es, M->x0_host, M->pool.get());
   const float inv_n = 1.f / (float)((size_t)d.B * (d.T - 1));
 
   // thread state
@@ -806,25 +794,40 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   M->resident_valid.assign((size_t)R, 0);
   M->resident_arena = arena;
 
-  gthr = std::thread(g_main);
-  athr = std::thread(a_main);
-
   {
     // gradient buffers: pads must read as zero
     MT_STEP_HIP(hipMemsetAsync(A.head_grad, 0, M->hl.total * es, sC));
     for (int i = 0; i < NG; ++i) MT_STEP_HIP(hipMemsetAsync(A.gring[i], 0, M->ll.total * es, sC));
+    // the first weight loads go out now, while the host prepares the input
+    wthr = std::thread(w_main);
+    // the previous step's embedding update, for the rows this batch gathers
+    // (the other rows follow on the optimizer thread during the forward;
+    // this must precede that thread)
+    apply_pending_embed_rows(M, tokens, (size_t)d.D);
+    for (int i = 0; i < d.D; ++i)
+      if (!touched[tokens[i]]) {
+        touched[tokens[i]] = 1;
+        rows_now.push_back(tokens[i]);
+      }
+    // targets and the embedding gather (from the streamed copy)
+    for (int b = 0; b < d.B; ++b)
+      for (int t = 0; t < d.T; ++t)
+        M->tgt_host[(size_t)b * d.T + t] = t + 1 < d.T ? tokens[(size_t)b * d.T + t + 1] : -1;
+    embed_gather(emb.shadow, tokens, (size_t)d.D, (size_t)d.H * es, M->x0_host, M->pool.get());
+    gthr = std::thread(g_main);
+    athr = std::thread(a_main);
     host_start_ms = ms_since(t_begin);
     MT_STEP_HIP(hipEventRecord(ph_start, sC));
-    // inputs of the step
-    MT_STEP_HIP(hipMemcpyAsync(A.ckpt[0], M->x0_host, act * es, hipMemcpyHostToDevice, sW));
-    MT_STEP_HIP(hipMemcpyAsync(A.tgt, M->tgt_host, (size_t)d.D * 4, hipMemcpyHostToDevice, sW));
-    MT_STEP_HIP(hipEventRecord(x0_ready, sW));
+    // inputs of the step, on the G stream: idle until the backward, while
+    // the W stream is already busy with weights
+    MT_STEP_HIP(hipMemcpyAsync(A.ckpt[0], M->x0_host, act * es, hipMemcpyHostToDevice, sG));
+    MT_STEP_HIP(hipMemcpyAsync(A.tgt, M->tgt_host, (size_t)d.D * 4, hipMemcpyHostToDevice, sG));
+    MT_STEP_HIP(hipEventRecord(x0_ready, sG));
     h2d_bytes += (double)act * es + (double)d.D * 4;
     MT_STEP_HIP(hipStreamWaitEvent(sC, x0_ready, 0));
 
     auto xloc = [&](int i) -> char* { return (i % K == 0) ? A.ckpt[i / K] : A.act[i % 2]; };
 
-    if (!wthr.joinable()) wthr = std::thread(w_main);
     for (size_t i = 0; i < plan.ops.size(); ++i) {
       const PlanOp& op = plan.ops[i];
       {
