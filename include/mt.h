@@ -135,7 +135,9 @@ typedef struct {
   double adam_ms;           /* summed host Adam time */
   double tail_ms;           /* from the end of GPU work to return */
   double h2d_bytes, d2h_bytes;
-  double h2d_ms, d2h_ms;    /* summed copy durations on the W and G streams */
+  double h2d_ms, d2h_ms;    /* summed durations of the host-to-device copies (weight
+                               loads, resident-layer uploads, the step's input) and of
+                               the gradient offload copies */
   double exposed_wait_fwd_ms, exposed_wait_bwd_ms; /* compute idle while waiting on weights */
   double probe_kernel_ms;   /* summed duration of the launches of the GEMM kernel
                                instantiation with the largest total time (time_kernels) */

@@ -491,6 +491,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   // by the optimizer thread)
   std::vector<uint8_t> res_valid, res_uploaded((size_t)R, 0);
   double res_bytes = 0;
+  // host-to-device copies outside the loader, timed like its loads: the
+  // step's input (main thread) and the resident uploads (optimizer thread)
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> x0_ev, res_ev;
 
   // --------------------------------------------------------- G thread
   // Waits on the host for each backward op, copies its gradient to a pinned
@@ -707,10 +710,14 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
               // the next step (every op of this step that reads the slot has
               // finished: its gradient has landed)
               const int c = x.unit - rs;
-              if (hipMemcpyAsync(A.res[c], u.shadow, u.n * es, hipMemcpyHostToDevice, sW) ==
-                  hipSuccess) {
+              hipEvent_t c0 = get_ev(), c1 = get_ev();
+              if (c0 && c1 && hipEventRecord(c0, sW) == hipSuccess &&
+                  hipMemcpyAsync(A.res[c], u.shadow, u.n * es, hipMemcpyHostToDevice, sW) ==
+                      hipSuccess &&
+                  hipEventRecord(c1, sW) == hipSuccess) {
                 res_uploaded[c] = 1;
                 res_bytes += (double)u.n * es;
+                res_ev.push_back({c0, c1});
               } else {
                 a_fail = 1;
                 abort_all = true;
@@ -820,6 +827,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     MT_STEP_HIP(hipEventRecord(ph_start, sC));
     // inputs of the step, on the G stream: idle until the backward, while
     // the W stream is already busy with weights
+    x0_ev.push_back({get_ev(), x0_ready});
+    MT_STEP_HIP(hipEventRecord(x0_ev[0].first, sG));
     MT_STEP_HIP(hipMemcpyAsync(A.ckpt[0], M->x0_host, act * es, hipMemcpyHostToDevice, sG));
     MT_STEP_HIP(hipMemcpyAsync(A.tgt, M->tgt_host, (size_t)d.D * 4, hipMemcpyHostToDevice, sG));
     MT_STEP_HIP(hipEventRecord(x0_ready, sG));
@@ -984,6 +993,8 @@ drain:
     s.bwd_ms = elapsed(ph_head, ph_end);
     s.adam_ms = adam_ms;
     for (auto& p : h2d_ev) s.h2d_ms += elapsed(p.first, p.second);
+    for (auto& p : x0_ev) s.h2d_ms += elapsed(p.first, p.second);
+    for (auto& p : res_ev) s.h2d_ms += elapsed(p.first, p.second);
     s.d2h_ms = d2h_ms;
     for (auto& p : wait_ev_f) s.exposed_wait_fwd_ms += elapsed(p.first, p.second);
     for (auto& p : wait_ev_b) s.exposed_wait_bwd_ms += elapsed(p.first, p.second);
