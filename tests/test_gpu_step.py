@@ -280,3 +280,23 @@ def test_resident_layers_bitwise_over_steps(R):
     _same(base2, res2, names)
     assert res2["h2d"][1] == res2["h2d"][0]  # new arena: loaded again
     assert res2["h2d"][2] == res2["h2d"][0]  # after a set: loaded again
+
+
+@pytest.mark.parametrize("kw", [dict(precision=1), dict(mlp_chunk_tokens=64, head_chunk_tokens=100),
+                                dict(serialize=1), dict(keep_internals=0, ckpt_interval=1)],
+                         ids=["fp32", "chunked", "serialized", "recompute-K1"])
+def test_resident_layers_bitwise_in_every_mode(kw):
+    """Resident layers in the fp32 debug precision, with the chunked MLP and
+    head (recompute schedule), on one stream and with K = 1: two steps equal
+    two steps without resident layers, bitwise."""
+    s = synth.CONFIGS["tiny-2l-h256"].with_(n_layers=4, ckpt_interval=2, seq=96, batch=2)
+    if "ckpt_interval" in kw:
+        s = s.with_(ckpt_interval=kw["ckpt_interval"])
+    w = synth.make_weights(s, seed=6)
+    ids = synth.make_tokens(s, seed=7)
+    names = synth.param_names(s)
+    run_kw = {k: v for k, v in kw.items() if k != "ckpt_interval"}
+    base = _steps(s, w, ids, 2, **run_kw)
+    res = _steps(s, w, ids, 2, resident_layers=2, **run_kw)
+    _same(base, res, names)
+    assert res["h2d"][1] < res["h2d"][0]
