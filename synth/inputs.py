@@ -67,7 +67,7 @@ class ModelShape:
         return replace(self, **kw)
 
 
-# The five workloads.  Names say what each one is.
+# The workloads.  Names say what each one is.
 CONFIGS: dict[str, ModelShape] = {
     # Small parity model: 2 layers, hidden 256, GQA 4/2, head_dim 64.
     "tiny-2l-h256": ModelShape(
@@ -93,6 +93,11 @@ CONFIGS: dict[str, ModelShape] = {
         name="qwen2.5-7b-b1-t32768", n_layers=28, hidden=3584, n_heads=28,
         n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064, batch=1,
         seq=32768, ckpt_interval=4, mlp_chunk_tokens=4096),
+    # 128K context, the pages' ultra-long-context range (Table 7)
+    "qwen2.5-7b-b1-t131072": ModelShape(
+        name="qwen2.5-7b-b1-t131072", n_layers=28, hidden=3584, n_heads=28,
+        n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064, batch=1,
+        seq=131072, ckpt_interval=4, mlp_chunk_tokens=4096),
 }
 
 # Per-layer tensors in draw order; gains ("*_norm") are not drawn.
