@@ -85,10 +85,11 @@ typedef struct {
   int32_t keep_internals;    /* 1 (default): each backward segment's re-forward runs every
                                 layer of the segment with mt_layer_fwd_keep and the
                                 backward uses mt_layer_bwd_saved (K layers of internals
-                                on the device, no second forward per layer); 0: the
-                                re-forward covers the first K-1 layers and every layer's
-                                backward recomputes (mt_layer_recompute_bwd).  Needs
-                                mlp_chunk_tokens = 0, else treated as 0. */
+                                on the device, no second forward per layer; with a
+                                chunked MLP the attention half's internals are kept and
+                                each chunk's gate/up is recomputed in the backward); 0:
+                                the re-forward covers the first K-1 layers and every
+                                layer's backward recomputes (mt_layer_recompute_bwd). */
   int32_t defer_updates;     /* 1 (default): the host Adam of the LM head and of the
                                 embedding is left to the next step, which applies it
                                 while its forward streams the other units (the head is
@@ -207,9 +208,10 @@ mt_status mt_layer_recompute_bwd(const mt_model_cfg* cfg, const mt_run_cfg* run,
  * and aliasing rules, plus the internals of a mt_layer_fwd_keep of the same
  * weights and x_in; its workspace is mt_layer_workspace_bytes(..., 2).
  * The results are bitwise equal to mt_layer_recompute_bwd's (same kernels
- * on the same inputs).  Both need mlp_chunk_tokens = 0 (the chunked MLP
- * exists to avoid holding the full gate/up activations): MT_E_SHAPE
- * otherwise, and mt_layer_internals_bytes returns 0. */
+ * on the same inputs).  With mlp_chunk_tokens > 0 (the chunked MLP exists
+ * to avoid holding the full gate/up activations) only the attention half's
+ * internals and the normed MLP input are kept, and mt_layer_bwd_saved
+ * recomputes each chunk's gate/up from them. */
 size_t mt_layer_internals_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run,
                                 int32_t batch, int32_t seq);
 mt_status mt_layer_fwd_keep(const mt_model_cfg* cfg, const mt_run_cfg* run,

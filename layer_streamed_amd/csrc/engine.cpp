@@ -161,10 +161,9 @@ struct Arena {
   size_t hws_bytes = 0;
 };
 
-// Whether the step keeps the re-forward's internals for the backward.
-bool keep_mode(const mt_model* M, const Dims& d) {
-  return M->run.keep_internals != 0 && d.mlp_chunk == d.D;
-}
+// Whether the step keeps the re-forward's internals for the backward (with
+// a chunked MLP, those of the attention half).
+bool keep_mode(const mt_model* M, const Dims&) { return M->run.keep_internals != 0; }
 
 Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
   Carve c{base};

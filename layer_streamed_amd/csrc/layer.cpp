@@ -140,14 +140,22 @@ void carve_bwd_scratch(const Dims& d, Carve& c, LayerWs<E>* w) {
 template <class E>
 // which: 0 forward (internals, gate/up not kept), 1 recompute + backward
 // (internals with gate/up, then backward scratch), 2 kept internals of one
-// layer (gate/up included; needs an unchunked MLP), 3 backward scratch only.
+// layer (with a whole-token MLP gate/up and the SwiGLU output too; with a
+// chunked MLP only the attention half's, and the backward recomputes each
+// chunk's gate/up from the kept b), 3 backward scratch only (plus a chunk's
+// gate/up and SwiGLU output for that recompute when the MLP is chunked).
 LayerWs<E> carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
   Carve c{base};
   LayerWs<E> w{};
   const size_t D = d.D, H = d.H, C = d.mlp_chunk;
+  const bool chunked = C < D;
   if (const size_t n = split_elems<E>(d, false)) w.split = c.take<float>(n);
   if (which == 3) {
     carve_bwd_scratch(d, c, &w);
+    if (chunked) {
+      w.m = c.take<E>(C * d.F);
+      w.gu = c.take<E>(C * 2 * d.F);
+    }
     *bytes = c.off + 256;
     return w;
   }
@@ -162,7 +170,7 @@ LayerWs<E> carve_layer(const Dims& d, char* base, int which, size_t* bytes) {
   w.x_mid = c.take<E>(D * H);
   w.b = c.take<E>(D * H);
   w.m = c.take<E>(C * d.F);
-  if (which == 1 || which == 2) w.gu = c.take<E>(C * 2 * d.F);
+  if (which == 1 || (which == 2 && !chunked)) w.gu = c.take<E>(C * 2 * d.F);
   if (which == 1) carve_bwd_scratch(d, c, &w);
   *bytes = c.off + 256;
   return w;
@@ -246,8 +254,9 @@ mt_status attn_half(const Dims& d, const LayerW<E>& w, const E* x, const LayerWs
   return MT_OK;
 }
 
-// keep = true: the internals (a, qkv, o, lse, x_mid, b, gate/up, m, rstd)
-// stay in the buffer for a later backward without recompute (unchunked MLP).
+// keep = true: the internals (a, qkv, o, lse, x_mid, b, rstd, and with a
+// whole-token MLP gate/up and m) stay in the buffer for a later backward
+// without recompute of the attention half (nor of the MLP when whole).
 template <class E>
 mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* x_out, void* wsp,
                       size_t ws_bytes, hipStream_t s, Probe* probe, bool keep = false) {
@@ -255,16 +264,15 @@ mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* 
   LayerWs<E> ws = carve_layer<E>(d, static_cast<char*>(wsp), keep ? 2 : 0, &need);
   MT_CHECK(wsp && ws_bytes >= need, MT_E_OOM_DEVICE, "layer forward: workspace %zu < %zu bytes",
            ws_bytes, need);
-  MT_CHECK(!keep || d.mlp_chunk == d.D, MT_E_SHAPE,
-           "layer forward: kept internals need an unchunked MLP");
   const LayerW<E> w(wv);
   MT_RUN(attn_half(d, w, x_in, ws, s, probe));
+  const bool keep_gu = keep && d.mlp_chunk == d.D;  // a chunked MLP keeps no gate/up
   for (int r0 = 0; r0 < d.D; r0 += d.mlp_chunk) {
     const int rows = std::min(d.mlp_chunk, d.D - r0);
-    GemmArgsT<E> gu = gemm<E>(GEMM_NT, keep ? EPI_SWIGLU_SAVE : EPI_SWIGLU, rows, 2 * d.F, d.H,
+    GemmArgsT<E> gu = gemm<E>(GEMM_NT, keep_gu ? EPI_SWIGLU_SAVE : EPI_SWIGLU, rows, 2 * d.F, d.H,
                               ws.b + (size_t)r0 * d.H, d.H, w.wgu, d.H, ws.m, d.F);
     gu.F = d.F;
-    if (keep) {
+    if (keep_gu) {
       gu.C2 = ws.gu;
       gu.ldc2 = 2 * d.F;
     }
@@ -279,7 +287,9 @@ mt_status layer_fwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, E* 
 }
 
 // saved != nullptr: the internals come from layer_fwd_t(keep = true) and
-// nothing is recomputed; wsp then holds only the backward scratch.
+// the attention half is not recomputed (nor the MLP when whole; a chunked
+// MLP recomputes each chunk's gate/up from the kept b); wsp then holds the
+// backward scratch.
 template <class E>
 mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, const E* dy, E* dx,
                       const mt_layer_grad_view& g, void* wsp, size_t ws_bytes, hipStream_t s,
@@ -293,10 +303,13 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
     const LayerWs<E> in = carve_layer<E>(d, static_cast<char*>(saved), 2, &need_s);
     MT_CHECK(saved_bytes >= need_s, MT_E_OOM_DEVICE, "layer backward: internals %zu < %zu bytes",
              saved_bytes, need_s);
-    MT_CHECK(d.mlp_chunk == d.D, MT_E_SHAPE, "layer backward: kept internals need an unchunked MLP");
     ws.cos_t = in.cos_t; ws.sin_t = in.sin_t; ws.rstd1 = in.rstd1; ws.rstd2 = in.rstd2;
     ws.lse = in.lse; ws.a = in.a; ws.qkv = in.qkv; ws.o = in.o; ws.x_mid = in.x_mid;
-    ws.b = in.b; ws.m = in.m; ws.gu = in.gu;
+    ws.b = in.b;
+    if (d.mlp_chunk == d.D) {
+      ws.m = in.m;
+      ws.gu = in.gu;
+    }
   }
   const LayerW<E> w(wv);
   // ---- recompute the attention half (rebuilds a, qkv (rotated), o, lse, x_mid, b)
@@ -318,7 +331,7 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
     gu.F = d.F;
     gu.C2 = ws.gu;
     gu.ldc2 = 2 * d.F;
-    if (!saved) MT_RUN(run_gemm(gu, s, probe, ws.split));
+    if (!saved || chunked) MT_RUN(run_gemm(gu, s, probe, ws.split));
     // dgate, dup from dm = dy W_down (NN) fused with the SwiGLU derivative
     GemmArgsT<E> dm = gemm<E>(GEMM_NN, EPI_SWIGLU_BWD, rows, d.F, d.H, dy_c, d.H, w.wd, d.F,
                               ws.dgu, 2 * d.F);
@@ -526,7 +539,7 @@ size_t mt_layer_workspace_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run, 
 size_t mt_layer_internals_bytes(const mt_model_cfg* cfg, const mt_run_cfg* run, int32_t batch,
                                 int32_t seq) {
   Dims d;
-  if (make_dims(cfg, run, batch, seq, &d) || d.mlp_chunk < d.D) return 0;
+  if (make_dims(cfg, run, batch, seq, &d)) return 0;
   return layer_ws_bytes(d, 2);
 }
 
@@ -558,7 +571,6 @@ mt_status mt_layer_fwd_keep(const mt_model_cfg* cfg, const mt_run_cfg* run, cons
   MT_RUN(check_view(w));
   MT_CHECK(x_in && x_out, MT_E_INVALID, "mt_layer_fwd_keep: null activation pointer");
   MT_CHECK(x_in != x_out, MT_E_INVALID, "mt_layer_fwd_keep: x_out may not alias x_in");
-  MT_CHECK(d.mlp_chunk == d.D, MT_E_SHAPE, "mt_layer_fwd_keep: needs mlp_chunk_tokens = 0");
   return layer_fwd_keep_impl(d, *w, x_in, x_out, internals, internals_bytes,
                              static_cast<hipStream_t>(stream), nullptr);
 }
@@ -576,7 +588,6 @@ mt_status mt_layer_bwd_saved(const mt_model_cfg* cfg, const mt_run_cfg* run,
   MT_CHECK(dw && dw->attn_norm && dw->w_qkv && dw->w_o && dw->mlp_norm && dw->w_gate_up &&
                dw->w_down,
            MT_E_INVALID, "mt_layer_bwd_saved: null gradient pointer");
-  MT_CHECK(d.mlp_chunk == d.D, MT_E_SHAPE, "mt_layer_bwd_saved: needs mlp_chunk_tokens = 0");
   return layer_bwd_saved_impl(d, *w, x_in, dy, dx, *dw, internals, internals_bytes, workspace,
                               workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
 }

@@ -130,11 +130,14 @@ def test_layer_fp32_debug_precision(name, shape, B, T, chunk):
         assert rel(gpu, ref) < F32_TOL, (k, rel(gpu, ref))
 
 
+@pytest.mark.parametrize("chunk", [0, 64], ids=["whole-mlp", "chunked-mlp"])
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
-def test_kept_internals_backward_is_bitwise_the_recompute(fp32):
-    """mt_layer_fwd_keep + mt_layer_bwd_saved (no recompute) against
-    mt_layer_fwd + mt_layer_recompute_bwd on the same weights and input:
-    same kernels on the same inputs, so every output is bitwise equal."""
+def test_kept_internals_backward_is_bitwise_the_recompute(fp32, chunk):
+    """mt_layer_fwd_keep + mt_layer_bwd_saved (no recompute of the attention
+    half; with a chunked MLP each chunk's gate/up is recomputed from the kept
+    normed input) against mt_layer_fwd + mt_layer_recompute_bwd on the same
+    weights and input: same kernels on the same inputs, so every output is
+    bitwise equal."""
     torch, mt = _env()
     shape = synth.ModelShape(name="gqa5", n_layers=1, hidden=640, n_heads=10, n_kv_heads=2,
                              head_dim=128, ffn=1536, vocab=1024)
@@ -153,7 +156,8 @@ def test_kept_internals_backward_is_bitwise_the_recompute(fp32):
          "w_gate_up": dev(np.concatenate([w["w_gate"], w["w_up"]])), "w_down": dev(w["w_down"])}
     view = mt.LayerView(*[W[k].data_ptr() for k, _ in mt.LayerView._fields_])
     mcfg = mt.model_cfg(shape)
-    rcfg = mt.run_cfg(precision=mt.PREC_FP32_DEBUG if fp32 else mt.PREC_BF16)
+    rcfg = mt.run_cfg(precision=mt.PREC_FP32_DEBUG if fp32 else mt.PREC_BF16,
+                      mlp_chunk_tokens=chunk)
     X = dev(rng.standard_normal((B * T, shape.hidden)))
     DY = dev(rng.standard_normal((B * T, shape.hidden)) * 1e-2)
     outs = []
@@ -181,5 +185,6 @@ def test_kept_internals_backward_is_bitwise_the_recompute(fp32):
     for k in outs[0]:
         assert torch.equal(outs[0][k], outs[1][k]), k
         assert torch.isfinite(outs[1][k].float()).all(), k
-    # with a chunked MLP there is nothing to keep
-    assert mt.layer_internals_bytes(mcfg, mt.run_cfg(mlp_chunk_tokens=64), B, T) == 0
+    # a chunked MLP keeps no gate/up: less to keep than a whole one
+    whole = mt.layer_internals_bytes(mcfg, mt.run_cfg(), B, T)
+    assert 0 < mt.layer_internals_bytes(mcfg, mt.run_cfg(mlp_chunk_tokens=64), B, T) < whole

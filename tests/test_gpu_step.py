@@ -300,3 +300,16 @@ def test_resident_layers_bitwise_in_every_mode(kw):
     res = _steps(s, w, ids, 2, resident_layers=2, **run_kw)
     _same(base, res, names)
     assert res["h2d"][1] < res["h2d"][0]
+
+
+def test_chunked_mlp_kept_attention_internals_bitwise():
+    """With a chunked MLP, keeping the attention half's internals (and
+    recomputing each chunk's gate/up in the backward) equals the full
+    recompute schedule bitwise over two steps."""
+    s = synth.CONFIGS["tiny-2l-h256"].with_(n_layers=4, ckpt_interval=2, seq=96, batch=2)
+    w = synth.make_weights(s, seed=8)
+    ids = synth.make_tokens(s, seed=9)
+    kw = dict(mlp_chunk_tokens=64, head_chunk_tokens=100)
+    base = _steps(s, w, ids, 2, keep_internals=0, **kw)
+    kept = _steps(s, w, ids, 2, keep_internals=1, **kw)
+    _same(base, kept, synth.param_names(s))
