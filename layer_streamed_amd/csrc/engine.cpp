@@ -28,6 +28,7 @@
 // streamed because its update ends the step: its upload would add to the
 // step's tail.
 #include <math.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -416,6 +417,12 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   }
 
   const bool ser = M->run.serialize != 0;
+  // MT_PROGRESS=1: a line on stderr as each unit's backward completes (long
+  // steps, e.g. 256K-token contexts, otherwise print nothing for minutes)
+  static const bool progress = [] {
+    const char* e = getenv("MT_PROGRESS");
+    return e && e[0] == '1';
+  }();
   hipStream_t sC = static_cast<hipStream_t>(streams[1]);
   hipStream_t sW = ser ? sC : static_cast<hipStream_t>(streams[0]);
   hipStream_t sG = ser ? sC : static_cast<hipStream_t>(streams[2]);
@@ -528,6 +535,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         ok = hipEventSynchronize(o.after) == hipSuccess;
         op_wait_ms += ms_since(tw);
         if (o.unit == 0 && o.ring >= 0) gpu_done_ms = ms_since(t_begin);
+        if (ok && progress && o.unit >= 0)
+          fprintf(stderr, "mt_stream_step: %s %d backward done at %.0f ms\n",
+                  o.unit == L ? "head" : "layer", o.unit == L ? 0 : o.unit, ms_since(t_begin));
       }
       if (ok) {
         const auto t0 = clock::now();
