@@ -937,10 +937,16 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         if (M->run.check_finite)
           MT_STEP_HIP(nonfinite_flags(A.gring[r], M->ll.total * es, f32, lf, sC));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
+        if (l == 0) {
+          MT_STEP_HIP(hipEventRecord(ph_end, sC));
+          // dx0, the gradient of the embedding output, leaves before layer
+          // 0's gradient: its scatter-add then runs while that larger copy
+          // is still on the link instead of after the last Adam update
+          offq.push(Offload{-1, A.dy, act, nullptr, ph_end, -1});
+        }
         Offload o{l, A.gring[r], M->ll.total, M->run.check_finite ? lf : nullptr, op_done[i], r};
         offq.push(o);
         ++bwd_count;
-        if (l == 0) MT_STEP_HIP(hipEventRecord(ph_end, sC));
         continue;
       }
       MT_STEP_HIP(hipEventRecord(op_done[i], sC));
@@ -950,8 +956,6 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       ops_enqueued = plan.ops.size();
     }
     load_cv.notify_all();
-    // dx0 = gradient of the embedding output
-    offq.push(Offload{-1, A.dy, act, nullptr, ph_end, -1});
   }
 drain:
   if (fail != MT_OK || abort_all.load()) {
