@@ -225,6 +225,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # the host link's copy rate in this run, after the timed steps: three
+    # 1 GiB pinned <-> device copies each way (not under --pmc-copy, whose
+    # counter passes calibrate on the device copy alone)
+    link_peak = {}
+    if not args.pmc_copy:
+        hbuf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        dbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for name, dst, src in (("h2d", dbuf, hbuf), ("d2h", hbuf, dbuf)):
+            dst.copy_(src, non_blocking=True)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                dst.copy_(src, non_blocking=True)
+            e1.record()
+            torch.cuda.synchronize()
+            link_peak[name] = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
+        del hbuf, dbuf
 
     n_params = metrics.shape_param_count(shape)
     D = shape.tokens
@@ -311,7 +329,16 @@ def main():
                  "h2d_GBps_while_copying": round(h2d / max(h2d_ms, 1e-9) / 1e6, 2),
                  "d2h_GBps_while_copying": round(d2h / max(d2h_ms, 1e-9) / 1e6, 2),
                  "h2d_GBps_per_step": round(h2d / step_s / 1e9, 2),
-                 "d2h_GBps_per_step": round(d2h / step_s / 1e9, 2)},
+                 "d2h_GBps_per_step": round(d2h / step_s / 1e9, 2),
+                 # the same run's 1 GiB pinned copies, and PCIe Gen5 x16 per
+                 # direction (32 GT/s x 16 lanes x 128/130 / 8)
+                 "h2d_peak_GBps": round(link_peak["h2d"], 2) if link_peak else None,
+                 "d2h_peak_GBps": round(link_peak["d2h"], 2) if link_peak else None,
+                 "h2d_busy_frac_of_peak": (round(h2d / step_s / 1e9 / link_peak["h2d"], 3)
+                                           if link_peak else None),
+                 "d2h_busy_frac_of_peak": (round(d2h / step_s / 1e9 / link_peak["d2h"], 3)
+                                           if link_peak else None),
+                 "nominal_GBps": 63.0},
         "host_bytes": {"pinned": stats[-1]["pinned_host_bytes"],
                        "pageable": stats[-1]["pageable_host_bytes"]},
         "device_arena_bytes": stats[-1]["device_arena_bytes"],
