@@ -109,6 +109,74 @@ def test_layer_7b_shape_one_sequence():
         assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))
 
 
+def test_layer_7b_full_batch_one_sequence_checked():
+    """One Qwen2.5-7B-shaped layer at the benchmark's launch configuration
+    (B 16 x T 1024: the 256 x 256 GEMM tiles with split tail tiles, the
+    full attention grids) through the calls the engine makes for it
+    (mt_layer_fwd_keep, then mt_layer_bwd_saved).  The upstream gradient is
+    zero outside one sequence, so that sequence's output and input
+    gradient and every weight gradient (a sum over all tokens) are what the
+    oracle computes for that sequence alone, and the other sequences' input
+    gradients are exactly zero."""
+    torch, mt = _env()
+    shape = synth.CONFIGS["qwen2.5-7b-b16-t1024"]
+    B, T, H, bc = 16, 1024, shape.hidden, 5
+    names = synth.layer_param_names(0)
+    w = {n.split(".")[-1]: v for n, v in synth.make_weights(shape, seed=31, names=names).items()}
+    rng = np.random.default_rng(32)
+    w["attn_norm"] = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    w["mlp_norm"] = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    wb = {k: oracle.bf16_round(v) for k, v in w.items()}
+    x = oracle.bf16_round(rng.standard_normal((B, T, H)).astype(np.float32))
+    dy = np.zeros((B, T, H), np.float32)
+    dy[bc] = oracle.bf16_round((rng.standard_normal((T, H)) * 1e-2).astype(np.float32))
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+
+    W = {"attn_norm": dev(wb["attn_norm"]),
+         "w_qkv": dev(np.concatenate([wb["w_q"], wb["w_k"], wb["w_v"]])), "w_o": dev(wb["w_o"]),
+         "mlp_norm": dev(wb["mlp_norm"]),
+         "w_gate_up": dev(np.concatenate([wb["w_gate"], wb["w_up"]])), "w_down": dev(wb["w_down"])}
+    view = mt.LayerView(*[W[k].data_ptr() for k, _ in mt.LayerView._fields_])
+    G = {k: torch.full_like(v, float("nan")) for k, v in W.items()}
+    gview = mt.GradView(*[G[k].data_ptr() for k, _ in mt.GradView._fields_])
+    mcfg, rcfg = mt.model_cfg(shape), mt.run_cfg()
+    X = dev(x.reshape(B * T, H))
+    Y = torch.empty_like(X)
+    DX = dev(dy.reshape(B * T, H))
+    internals = torch.empty(mt.layer_internals_bytes(mcfg, rcfg, B, T), dtype=torch.uint8,
+                            device="cuda")
+    ws = torch.empty(mt.layer_workspace_bytes(mcfg, rcfg, B, T, 2), dtype=torch.uint8,
+                     device="cuda")
+    mt.layer_fwd_keep(mcfg, rcfg, view, X, Y, B, T, internals)
+    mt.layer_bwd_saved(mcfg, rcfg, view, X, DX, DX, gview, B, T, internals, ws)
+    torch.cuda.synchronize()
+    cos, sin = D.rope_cos_sin(T, shape.head_dim, shape.rope_theta, np.float32)
+    y_ref, saved = D.layer_forward(wb, x[bc:bc + 1], shape, cos, sin)
+    dx_ref, g_ref = D.layer_backward(wb, saved, dy[bc:bc + 1], shape, cos, sin)
+    rows = slice(bc * T, (bc + 1) * T)
+    dxg = DX.float().cpu().numpy()
+    checks = {
+        "y": (Y[rows].float().cpu().numpy(), y_ref.reshape(T, H)),
+        "dx": (dxg[rows], dx_ref.reshape(T, H)),
+        "attn_norm": (G["attn_norm"].float().cpu().numpy(), g_ref["attn_norm"]),
+        "w_qkv": (G["w_qkv"].float().cpu().numpy(),
+                  np.concatenate([g_ref["w_q"], g_ref["w_k"], g_ref["w_v"]])),
+        "w_o": (G["w_o"].float().cpu().numpy(), g_ref["w_o"]),
+        "mlp_norm": (G["mlp_norm"].float().cpu().numpy(), g_ref["mlp_norm"]),
+        "w_gate_up": (G["w_gate_up"].float().cpu().numpy(),
+                      np.concatenate([g_ref["w_gate"], g_ref["w_up"]])),
+        "w_down": (G["w_down"].float().cpu().numpy(), g_ref["w_down"]),
+    }
+    for k, (gpu, ref) in checks.items():
+        assert np.isfinite(gpu).all(), k
+        assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))
+    other = np.delete(dxg.reshape(B, T, H), bc, axis=0)
+    assert not other.any(), "input gradient of a sequence with zero upstream gradient"
+    assert np.isfinite(Y.float().cpu().numpy()).all()
+
+
 # fp32 debug precision: every buffer fp32, fp32 FMA kernels; the oracle in
 # float64.  The bar is 1e-4 relative (the fp32 error of the longest
 # reductions here is ~1e-6).
