@@ -587,19 +587,31 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
     const bool active = qt0 + BQ - 1 >= k0 + 32 * w;  // some query of the tile sees this wave's keys
     f32x16_t sacc[2], dpacc[2];
     if (active) {
+      // S and dP: the row reads of step ks+1 are issued before the MFMAs of
+      // step ks (lgkmcnt(2) then leaves only those two in flight; LDS reads
+      // return in order), so a lone wave does not wait a full LDS round
+      // trip per MFMA pair; the last step drains every read
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         zero16(sacc[qt]);
         zero16(dpacc[qt]);
+        u32x4_t Aq[2], Ad[2];
+        Aq[0] = lds_row16(sq, 32 * qt + n, hh);
+        Ad[0] = lds_row16(sdo, 32 * qt + n, hh);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          u32x4_t Aq = lds_row16(sq, 32 * qt + n, 2 * ks + hh);
-          u32x4_t Ad = lds_row16(sdo, 32 * qt + n, 2 * ks + hh);
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          asm volatile("" : "+v"(Aq));
-          asm volatile("" : "+v"(Ad));
-          sacc[qt] = mfma32(Aq, kf[ks], sacc[qt]);
-          dpacc[qt] = mfma32(Ad, vf[ks], dpacc[qt]);
+          const int c = ks & 1;
+          if (ks + 1 < D / 16) {
+            Aq[c ^ 1] = lds_row16(sq, 32 * qt + n, 2 * (ks + 1) + hh);
+            Ad[c ^ 1] = lds_row16(sdo, 32 * qt + n, 2 * (ks + 1) + hh);
+            asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
+          } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          }
+          asm volatile("" : "+v"(Aq[c]));
+          asm volatile("" : "+v"(Ad[c]));
+          sacc[qt] = mfma32(Aq[c], kf[ks], sacc[qt]);
+          dpacc[qt] = mfma32(Ad[c], vf[ks], dpacc[qt]);
         }
       }
       // P and dS, rows = queries (qt0 + 32qt + 8j + 4hh + i), column = key
@@ -618,25 +630,39 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
     // the next tile streams in while this one's dV and dK are formed
     if (it + 1 < nit) issue(it + 1, buf ^ 1);
     if (active) {
+      // dV and dK over steps i = (qt, jj, dt) in the same order as a plain
+      // nested loop: the four transpose reads of step i+1 go out before the
+      // MFMAs of step i (lgkmcnt(4) leaves only those in flight)
+      constexpr int NI = 2 * 2 * (D / 32);
+      u32x4_t At[2], Aq[2];
+      u32x4_t Pb = {0, 0, 0, 0}, Sb = {0, 0, 0, 0};
+      auto reads = [&](int i, int slot) {
+        const int qt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
+        const int rb = 32 * qt + 16 * jj + 4 * hh;
+        const int m0 = 32 * dt + 16 * ((lane >> 4) & 1);
+        At[slot] = lds_tr_frag(sdo, rb, m0, lane);
+        Aq[slot] = lds_tr_frag(sq, rb, m0, lane);
+      };
+      reads(0, 0);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const u32x4_t Pb = pack_p(sacc[qt], jj);
-          const u32x4_t Sb = pack_p(dpacc[qt], jj);
-          const int rb = 32 * qt + 16 * jj + 4 * hh;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const int m0 = 32 * dt + 16 * ((lane >> 4) & 1);
-            u32x4_t At = lds_tr_frag(sdo, rb, m0, lane);
-            u32x4_t Aq = lds_tr_frag(sq, rb, m0, lane);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            asm volatile("" : "+v"(At));
-            asm volatile("" : "+v"(Aq));
-            dv[dt] = mfma32(At, Pb, dv[dt]);
-            dk[dt] = mfma32(Aq, Sb, dk[dt]);
-          }
+      for (int i = 0; i < NI; ++i) {
+        const int qt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
+        const int c = i & 1;
+        if (dt == 0) {
+          Pb = pack_p(sacc[qt], jj);
+          Sb = pack_p(dpacc[qt], jj);
         }
+        if (i + 1 < NI) {
+          reads(i + 1, c ^ 1);
+          asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        asm volatile("" : "+v"(At[c]));
+        asm volatile("" : "+v"(Aq[c]));
+        dv[dt] = mfma32(At[c], Pb, dv[dt]);
+        dk[dt] = mfma32(Aq[c], Sb, dk[dt]);
+      }
     }
     if (it + 1 < nit) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
