@@ -579,6 +579,10 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
   __syncthreads();
   for (int it = 0; it < nit; ++it) {
     const int buf = it & 1;
+    // the other stage was last read in the previous iteration (the barrier
+    // at its end retired those reads): the next tile streams into it under
+    // this whole iteration
+    if (it + 1 < nit) issue(it + 1, buf ^ 1);
     const int qt0 = k0 + (it % ntq) * BQ;
     const char* sq = dsm + buf * STAGE;
     const char* sdo = sq + TILE;
@@ -627,8 +631,6 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
           dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
         }
     }
-    // the next tile streams in while this one's dV and dK are formed
-    if (it + 1 < nit) issue(it + 1, buf ^ 1);
     if (active) {
       // dV and dK over steps i = (qt, jj, dt) in the same order as a plain
       // nested loop: the four transpose reads of step i+1 go out before the
