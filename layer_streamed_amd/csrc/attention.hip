@@ -71,6 +71,12 @@ __device__ __forceinline__ u32x4_t col_of(const u32x2_t* r, int di) {
   return o;
 }
 
+// 2^x as the bare v_exp_f32: results below 2^-126 (probabilities of keys
+// more than 87 nats below the row maximum) come out as 0 instead of fp32
+// denormals, which drops the library exp2f's range-scaling around it (a
+// compare, an add, a select and a ldexp per element).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ u32x4_t pack_p(const f32x16_t& acc, int jj) {
   u32x4_t v;
   v.x = pack_bf(acc[8 * jj + 0], acc[8 * jj + 1]);
@@ -234,13 +240,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mnew = fmaxf(m, mx);
-      const float alpha = exp2f(m - mnew);
+      const float alpha = exp2_hw(m - mnew);
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(sacc[kt][e] - mnew);
+          const float p = exp2_hw(sacc[kt][e] - mnew);
           sacc[kt][e] = p;
           rs += p;
         }
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(const AttnArgs a) {
         for (int e = 0; e < 16; ++e) {
           const int qi = 32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3);
           const int q = qt0 + qi;
-          float p = exp2f(sacc[qt][e] * a.scale_log2 - sL[qi]);
+          float p = exp2_hw(sacc[qt][e] * a.scale_log2 - sL[qi]);
           if (key > q) p = 0.f;
           sacc[qt][e] = p;
           dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
@@ -625,7 +631,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
         for (int e = 0; e < 16; ++e) {
           const int qi = 32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3);
           const int q = qt0 + qi;
-          float p = exp2f(sacc[qt][e] * a.scale_log2 - sL[qi]);
+          float p = exp2_hw(sacc[qt][e] * a.scale_log2 - sL[qi]);
           if (key > q) p = 0.f;
           sacc[qt][e] = p;
           dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
@@ -777,7 +783,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int kk = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
-          float p = exp2f(sacc[kt][e] * a.scale_log2 - lse2);
+          float p = exp2_hw(sacc[kt][e] * a.scale_log2 - lse2);
           if (kk > qrow || kk >= T) p = 0.f;
           dpacc[kt][e] = p * (dpacc[kt][e] - del);
         }
