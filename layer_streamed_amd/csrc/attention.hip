@@ -24,6 +24,8 @@
 // dK/dV kernel takes its query tiles straight into LDS and reads the
 // transposed operands with LDS transpose reads (attn_dkdv_dl_kernel); the
 // register-staged form (attn_dkdv_kernel) serves head_dim 64.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -492,20 +494,14 @@ __device__ __forceinline__ u32x4_t lds_row16(const char* tile, int row, int chun
   return v;
 }
 
-// Rows base .. base+3 (pass h = 0) and base+8 .. base+11 (h = 1) of columns
-// m0 + (lane & 15) as one MFMA A fragment (slots 0-3, then 4-7).
-__device__ __forceinline__ u32x4_t lds_tr_frag(const char* tile, int base, int m0, int lane) {
-  const int i = lane & 15;
-  const int d = m0 + 4 * (i & 3);
-  const int c = d >> 3, half = (d >> 2) & 1;
-  u32x2_t v[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = base + 8 * h + (i >> 2);
-    const uint32_t la = lds_addr(tile + row * 256 + ((c ^ dkdv_swz(row)) << 4) + half * 8);
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[h]) : "v"(la) : "memory");
-  }
-  return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
+// Two transpose reads at addr + o0 and addr + o1 (immediate offsets, which
+// must fold to constants) as one MFMA A fragment: rows r .. r+3 (o0) and
+// r+8 .. r+11 (o1) of the lane's column, in slots 0-3 and 4-7.
+__device__ __forceinline__ u32x4_t lds_tr_pair(uint32_t addr, const int o0, const int o1) {
+  u32x2_t v0, v1;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v0) : "v"(addr), "i"(o0) : "memory");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v1) : "v"(addr), "i"(o1) : "memory");
+  return u32x4_t{v0.x, v0.y, v1.x, v1.y};
 }
 
 template <int D>
@@ -576,6 +572,20 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
     }
   };
 
+  // Transpose-read addresses: row & 7, and with it the swizzle, is the same
+  // for every (qt, jj, h) of a lane, so per lane only the column block dt
+  // varies the address beyond a constant; (32 qt + 16 jj + 8 h) rows of 256
+  // bytes and the dO tile's place go in the reads' immediate offsets.
+  uint32_t trb[D / 32];
+  {
+    const int i = lane & 15;
+    const int sw = dkdv_swz(4 * hh + (i >> 2));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      trb[dt] = (4 * hh + (i >> 2)) * 256 +
+                (((4 * dt + 2 * ((lane >> 4) & 1) + ((i >> 1) & 1)) ^ sw) << 4) + (i & 1) * 8;
+  }
+
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tid < BQ) {
@@ -624,18 +634,25 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
           dpacc[qt] = mfma32(Ad[c], vf[ks], dpacc[qt]);
         }
       }
-      // P and dS, rows = queries (qt0 + 32qt + 8j + 4hh + i), column = key
+      // P and dS, rows = queries (qt0 + 32qt + 8j + 4hh + i), column = key;
+      // the causal mask only where some query of the tile precedes one of
+      // this wave's keys (a wave-uniform test)
+      auto p_ds = [&](auto masked) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qi = 32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const int q = qt0 + qi;
-          float p = exp2_hw(sacc[qt][e] * a.scale_log2 - sL[qi]);
-          if (key > q) p = 0.f;
-          sacc[qt][e] = p;
-          dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int qi = 32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3);
+            float p = exp2_hw(sacc[qt][e] * a.scale_log2 - sL[qi]);
+            if (decltype(masked)::value && key > qt0 + qi) p = 0.f;
+            sacc[qt][e] = p;
+            dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
+          }
+      };
+      if (qt0 < k0 + 32 * w + 31)
+        p_ds(std::true_type{});
+      else
+        p_ds(std::false_type{});
     }
     if (active) {
       // dV and dK over steps i = (qt, jj, dt) in the same order as a plain
@@ -644,12 +661,13 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
       constexpr int NI = 2 * 2 * (D / 32);
       u32x4_t At[2], Aq[2];
       u32x4_t Pb = {0, 0, 0, 0}, Sb = {0, 0, 0, 0};
+      const uint32_t sqa = lds_addr(sq);
       auto reads = [&](int i, int slot) {
         const int qt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
-        const int rb = 32 * qt + 16 * jj + 4 * hh;
-        const int m0 = 32 * dt + 16 * ((lane >> 4) & 1);
-        At[slot] = lds_tr_frag(sdo, rb, m0, lane);
-        Aq[slot] = lds_tr_frag(sq, rb, m0, lane);
+        const int ro = (32 * qt + 16 * jj) * 256;
+        const uint32_t ad = sqa + trb[dt];
+        At[slot] = lds_tr_pair(ad, TILE + ro, TILE + ro + 8 * 256);
+        Aq[slot] = lds_tr_pair(ad, ro, ro + 8 * 256);
       };
       reads(0, 0);
 #pragma unroll
