@@ -230,16 +230,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
           sacc[kt] = mfma32(A, qf[ks], sacc[kt]);
         }
       float mx = NEG;
+      auto scores = [&](auto masked) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
-          float s = sacc[kt][e] * a.scale_log2;
-          if (key > qrow || key >= T) s = NEG;
-          sacc[kt][e] = s;
-          mx = fmaxf(mx, s);
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int key = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+            float s = sacc[kt][e] * a.scale_log2;
+            if (decltype(masked)::value && (key > qrow || key >= T)) s = NEG;
+            sacc[kt][e] = s;
+            mx = fmaxf(mx, s);
+          }
+      };
+      // a tile whose keys all precede the wave's first query and lie in the
+      // sequence masks nothing (a wave-uniform test)
+      if (kv0 + BKV - 1 <= q0 + 32 * w && kv0 + BKV <= T)
+        scores(std::false_type{});
+      else
+        scores(std::true_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mnew = fmaxf(m, mx);
       const float alpha = exp2_hw(m - mnew);
