@@ -93,7 +93,7 @@ CONFIGS: dict[str, ModelShape] = {
         name="qwen2.5-7b-b1-t32768", n_layers=28, hidden=3584, n_heads=28,
         n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064, batch=1,
         seq=32768, ckpt_interval=4, mlp_chunk_tokens=4096),
-    # 128K and 256K context, the pages' ultra-long-context range (Table 7)
+    # 128K, 256K and 512K context, the pages' ultra-long-context range (Table 7)
     "qwen2.5-7b-b1-t131072": ModelShape(
         name="qwen2.5-7b-b1-t131072", n_layers=28, hidden=3584, n_heads=28,
         n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064, batch=1,
@@ -102,6 +102,10 @@ CONFIGS: dict[str, ModelShape] = {
         name="qwen2.5-7b-b1-t262144", n_layers=28, hidden=3584, n_heads=28,
         n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064, batch=1,
         seq=262144, ckpt_interval=4, mlp_chunk_tokens=4096),
+    "qwen2.5-7b-b1-t524288": ModelShape(
+        name="qwen2.5-7b-b1-t524288", n_layers=28, hidden=3584, n_heads=28,
+        n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064, batch=1,
+        seq=524288, ckpt_interval=4, mlp_chunk_tokens=4096),
 }
 
 # Per-layer tensors in draw order; gains ("*_norm") are not drawn.
