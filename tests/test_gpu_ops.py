@@ -87,6 +87,34 @@ def test_gemm_layouts_and_epilogues(layout, M, N, K, epi):
         np.testing.assert_allclose(out, ref, rtol=1e-2, atol=1e-2 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("layout,M,N,K", [(0, 300, 200, 264), (1, 300, 200, 256), (2, 296, 200, 256),
+                                           (0, 256, 512, 256), (0, 300, 203, 256)])
+def test_gemm_bf16_store_is_rne_of_the_fp32_result(layout, M, N, K):
+    """The bf16 epilogues round in the device (gfx950's packed conversion):
+    the same product stored as fp32 (same accumulation, same order) and then
+    rounded to nearest even by the oracle must give the bf16 store bit for
+    bit, plain and with the residual added in fp32 first."""
+    torch, mt = _torch(), _mt()
+    rng = np.random.default_rng(700 + layout)
+    a = oracle.bf16_round(_rand(rng, (K, M) if layout == 2 else (M, K)))
+    b = oracle.bf16_round(_rand(rng, (N, K) if layout == 0 else (K, N)))
+    r = oracle.bf16_round(_rand(rng, (M, N)))
+    A, B, R = bf16_dev(a), bf16_dev(b), bf16_dev(r)
+    lda = M if layout == 2 else K
+    ldb = K if layout == 0 else N
+    f32 = torch.zeros((M, N), device="cuda", dtype=torch.float32)
+    c16 = torch.zeros((M, N), device="cuda", dtype=torch.bfloat16)
+    res16 = torch.zeros((M, N), device="cuda", dtype=torch.bfloat16)
+    mt.gemm(layout, 1, M, N, K, A, lda, B, ldb, f32, N)
+    mt.gemm(layout, 0, M, N, K, A, lda, B, ldb, c16, N)
+    mt.gemm(layout, 3, M, N, K, A, lda, B, ldb, res16, N, R=R, ldr=N)
+    torch.cuda.synchronize()
+    acc = to_np(f32)
+    assert np.array_equal(to_np(c16).view(np.uint32), oracle.bf16_round(acc).view(np.uint32))
+    with_r = (r + acc).astype(np.float32)
+    assert np.array_equal(to_np(res16).view(np.uint32), oracle.bf16_round(with_r).view(np.uint32))
+
+
 @pytest.mark.parametrize("M,F,K", [(256, 1024, 256), (200, 96, 136), (200, 96, 128)])
 def test_gemm_swiglu_forward_and_backward_epilogues(M, F, K):
     torch, mt = _torch(), _mt()
