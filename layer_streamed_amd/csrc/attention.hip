@@ -726,6 +726,174 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
   }
 }
 
+// dQ for head_dim 128 in the dK/dV kernel's form: the K and V tiles of 64
+// keys go straight into LDS (global_load_lds, double-buffered, one barrier
+// per tile) in their natural [key][d] layout with the same chunk swizzle; K
+// and V rows for S^T and dP^T are one ds_read_b128 per lane, and the
+// transposed K^T fragments for dQ two ds_read_b64_tr_b16 at immediate
+// offsets.  Products, operand k-slot order and summation order per query are
+// those of attn_dq_kernel, without its register-staged tile copies.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
+  static_assert(D == 128, "rows of 16 chunks");
+  constexpr int BQ = 128, BKV = 64, CH = D / 8, TILE = BKV * D * 2, STAGE = 2 * TILE;
+  constexpr int PER = BKV * CH / 256;  // 16-byte load instructions per lane per operand
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+
+  const int T = a.T;
+  const int nqb = (T + BQ - 1) / BQ;
+  const int per = a.Hq * a.B;
+  const int qb = nqb - 1 - (int)blockIdx.x / per;
+  const int rest = blockIdx.x % per;
+  const int h = rest % a.Hq, b = rest / a.Hq;
+  const int g = (h * a.Hkv) / a.Hq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int q0 = qb * BQ;
+  const int qrow = q0 + 32 * w + n;
+  const long ldq = a.ldq;
+  const uint16_t* base = a.qkv + (long)b * T * ldq;
+  const uint16_t* kbase = base + (long)(a.Hq + g) * D;
+  const uint16_t* vbase = base + (long)(a.Hq + a.Hkv + g) * D;
+
+  u32x4_t qf[D / 16], df[D / 16];
+  const bool ok = qrow < T;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)qrow * ldq + h * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+    df[ks] = ok ? *reinterpret_cast<const u32x4_t*>(a.dout + ((long)b * T + qrow) * a.ldo + h * D + ks * 16 + hh * 8)
+                : u32x4_t{0, 0, 0, 0};
+  }
+  const long li = ((long)b * a.Hq + h) * T + qrow;
+  const float lse2 = ok ? a.lse[li] * LOG2E : -NEG;
+  const float del = ok ? a.delta[li] : 0.f;
+
+  f32x16_t dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) zero16(dq[dt]);
+
+  const int kv_end = min(q0 + BQ, T);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int wave_qmax = q0 + 32 * w + 31;
+  // tile t -> stage buf: K and V rows clamped to T - 1 past the end (those
+  // keys are masked)
+  auto issue = [&](int t, int buf) {
+    const int kv0 = t * BKV;
+    char* sk = dsm + buf * STAGE;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int slot = (w * PER + p) * 64 + lane;
+      const int row = slot / CH, pos = slot % CH;
+      const int c = pos ^ dkdv_swz(row);
+      const long gk = min(kv0 + row, T - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(kbase + gk * ldq + c * 8),
+          (__attribute__((address_space(3))) void*)(sk + (w * PER + p) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(vbase + gk * ldq + c * 8),
+          (__attribute__((address_space(3))) void*)(sk + TILE + (w * PER + p) * 1024), 16, 0, 0);
+    }
+  };
+  // K^T read addresses, as the dK/dV kernel's Q^T reads
+  uint32_t trb[D / 32];
+  {
+    const int i = lane & 15;
+    const int sw = dkdv_swz(4 * hh + (i >> 2));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      trb[dt] = (4 * hh + (i >> 2)) * 256 +
+                (((4 * dt + 2 * ((lane >> 4) & 1) + ((i >> 1) & 1)) ^ sw) << 4) + (i & 1) * 8;
+  }
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+    const int kv0 = t * BKV;
+    const char* sk = dsm + buf * STAGE;
+    const char* sv = sk + TILE;
+    if (kv0 <= wave_qmax) {
+      f32x16_t sacc[2], dpacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        zero16(sacc[kt]);
+        zero16(dpacc[kt]);
+        u32x4_t Ak[2], Av[2];
+        Ak[0] = lds_row16(sk, 32 * kt + n, hh);
+        Av[0] = lds_row16(sv, 32 * kt + n, hh);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int c = ks & 1;
+          if (ks + 1 < D / 16) {
+            Ak[c ^ 1] = lds_row16(sk, 32 * kt + n, 2 * (ks + 1) + hh);
+            Av[c ^ 1] = lds_row16(sv, 32 * kt + n, 2 * (ks + 1) + hh);
+            asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
+          } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          }
+          asm volatile("" : "+v"(Ak[c]));
+          asm volatile("" : "+v"(Av[c]));
+          sacc[kt] = mfma32(Ak[c], qf[ks], sacc[kt]);
+          dpacc[kt] = mfma32(Av[c], df[ks], dpacc[kt]);
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          float p = exp2_hw(sacc[kt][e] * a.scale_log2 - lse2);
+          if (kk > qrow || kk >= T) p = 0.f;
+          dpacc[kt][e] = p * (dpacc[kt][e] - del);
+        }
+      // dQ over steps i = (kt, jj, dt); the two transpose reads of step
+      // i+1 go out before the MFMA of step i
+      constexpr int NI = 2 * 2 * (D / 32);
+      const uint32_t ska = lds_addr(sk);
+      u32x4_t Kt[2];
+      u32x4_t Sb = {0, 0, 0, 0};
+      auto reads = [&](int i, int slot) {
+        const int kt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
+        const int ro = (32 * kt + 16 * jj) * 256;
+        Kt[slot] = lds_tr_pair(ska + trb[dt], ro, ro + 8 * 256);
+      };
+      reads(0, 0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int kt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
+        const int c = i & 1;
+        if (dt == 0) Sb = pack_p(dpacc[kt], jj);
+        if (i + 1 < NI) {
+          reads(i + 1, c ^ 1);
+          asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        asm volatile("" : "+v"(Kt[c]));
+        dq[dt] = mfma32(Kt[c], Sb, dq[dt]);
+      }
+    }
+    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (ok) {
+    uint16_t* drow = a.dqkv + ((long)b * T + qrow) * ldq + h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * hh;
+        u32x2_t v;
+        v.x = pack_bf(dq[dt][4 * j] * a.scale, dq[dt][4 * j + 1] * a.scale);
+        v.y = pack_bf(dq[dt][4 * j + 2] * a.scale, dq[dt][4 * j + 3] * a.scale);
+        *reinterpret_cast<u32x2_t*>(drow + d) = v;
+      }
+  }
+}
+
 // --------------------------------------------------------------------- dQ
 // Two waves per SIMD as in the forward (a few registers spill, still 4-12%
 // faster than one wave); the dK/dV kernel stays at one (its accumulators
@@ -870,6 +1038,7 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   constexpr size_t lds_kv = (2 * 64 * (D + 8) + 2 * D * (64 + 8)) * sizeof(uint16_t) + 2 * 64 * sizeof(float);
   constexpr size_t lds_q = (2 * 64 * (D + 8) + D * (64 + 8)) * sizeof(uint16_t);
   constexpr size_t lds_dl = 2 * 2 * 64 * D * sizeof(uint16_t) + 4 * 64 * sizeof(float);
+  constexpr size_t lds_dq_dl = 2 * 2 * 64 * D * sizeof(uint16_t);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(attn_dkdv_kernel<D>, lds_kv);
@@ -878,6 +1047,8 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     if constexpr (D == 128) {
       e = set_lds(attn_dkdv_dl_kernel<D>, lds_dl);
+      if (e != hipSuccess) return e;
+      e = set_lds(attn_dq_dl_kernel<D>, lds_dq_dl);
       if (e != hipSuccess) return e;
     }
     attr = true;
@@ -894,7 +1065,10 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.T + 127) / 128;
-  hipLaunchKernelGGL(attn_dq_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_q, s, a);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL(attn_dq_dl_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_dq_dl, s, a);
+  else
+    hipLaunchKernelGGL(attn_dq_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_q, s, a);
   return hipGetLastError();
 }
 
