@@ -20,10 +20,11 @@
 // Backward (deterministic, no atomics): delta = rowsum(dO * O); a dK/dV
 // kernel owns 128 keys per workgroup and loops over every query head of the
 // GQA group and every query tile at or after its keys; a dQ kernel owns 128
-// queries and loops over key tiles up to the diagonal.  For head_dim 128 the
-// dK/dV kernel takes its query tiles straight into LDS and reads the
-// transposed operands with LDS transpose reads (attn_dkdv_dl_kernel); the
-// register-staged form (attn_dkdv_kernel) serves head_dim 64.
+// queries and loops over key tiles up to the diagonal.  For head_dim 128
+// both take their streamed tiles (queries for dK/dV, keys for dQ) straight
+// into LDS and read the transposed operands with LDS transpose reads
+// (attn_dkdv_dl_kernel, attn_dq_dl_kernel); the register-staged forms
+// (attn_dkdv_kernel, attn_dq_kernel) serve head_dim 64.
 #include <type_traits>
 
 #include "common.h"
