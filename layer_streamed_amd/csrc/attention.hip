@@ -513,6 +513,196 @@ __device__ __forceinline__ u32x4_t lds_tr_pair(uint32_t addr, const int o0, cons
   return u32x4_t{v0.x, v0.y, v1.x, v1.y};
 }
 
+// The forward for head_dim 128 in the dK/dV kernel's form: K and V tiles of
+// 64 keys go straight into LDS (global_load_lds, double-buffered, one
+// barrier per tile) in natural [key][d] layout; K rows for S^T are one
+// ds_read_b128 per lane, and the V^T fragments for O^T = V^T P^T two
+// ds_read_b64_tr_b16 at immediate offsets.  Products, k-slot order and
+// summation order are those of attn_fwd_kernel.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
+  static_assert(D == 128, "rows of 16 chunks");
+  constexpr int BQ = 128, BKV = 64, CH = D / 8, TILE = BKV * D * 2, STAGE = 2 * TILE;
+  constexpr int PER = BKV * CH / 256;  // 16-byte load instructions per lane per operand
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+
+  const int T = a.T;
+  const int nqb = (T + BQ - 1) / BQ;
+  const int per = a.Hq * a.B;
+  const int id = blockIdx.x;
+  const int qb = nqb - 1 - id / per;  // longest causal rows first
+  const int rest = id % per;
+  const int h = rest % a.Hq, b = rest / a.Hq;
+  const int g = (h * a.Hkv) / a.Hq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int q0 = qb * BQ;
+  const int qrow = q0 + 32 * w + n;
+  const long ldq = a.ldq;
+  const uint16_t* base = a.qkv + (long)b * T * ldq;
+  const uint16_t* kbase = base + (long)(a.Hq + g) * D;
+  const uint16_t* vbase = base + (long)(a.Hq + a.Hkv + g) * D;
+
+  u32x4_t qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = qrow < T ? *reinterpret_cast<const u32x4_t*>(base + (long)qrow * ldq + h * D + ks * 16 + hh * 8)
+                      : u32x4_t{0, 0, 0, 0};
+
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) zero16(oacc[dt]);
+  float m = NEG, l = 0.f;
+
+  const int kv_end = min(q0 + BQ, T);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int wave_qmax = q0 + 32 * w + 31;
+  // tile t -> stage buf: K and V rows clamped to T - 1 past the end (those
+  // keys are masked)
+  auto issue = [&](int t, int buf) {
+    const int kv0 = t * BKV;
+    char* sk = dsm + buf * STAGE;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int slot = (w * PER + p) * 64 + lane;
+      const int row = slot / CH, pos = slot % CH;
+      const int c = pos ^ dkdv_swz(row);
+      const long gk = min(kv0 + row, T - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(kbase + gk * ldq + c * 8),
+          (__attribute__((address_space(3))) void*)(sk + (w * PER + p) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(vbase + gk * ldq + c * 8),
+          (__attribute__((address_space(3))) void*)(sk + TILE + (w * PER + p) * 1024), 16, 0, 0);
+    }
+  };
+  // V^T read addresses, as the dK/dV kernel's Q^T reads
+  uint32_t trb[D / 32];
+  {
+    const int i = lane & 15;
+    const int sw = dkdv_swz(4 * hh + (i >> 2));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      trb[dt] = (4 * hh + (i >> 2)) * 256 +
+                (((4 * dt + 2 * ((lane >> 4) & 1) + ((i >> 1) & 1)) ^ sw) << 4) + (i & 1) * 8;
+  }
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+    const int kv0 = t * BKV;
+    const char* sk = dsm + buf * STAGE;
+    if (kv0 <= wave_qmax) {
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        zero16(sacc[kt]);
+        u32x4_t Ak[2];
+        Ak[0] = lds_row16(sk, 32 * kt + n, hh);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int c = ks & 1;
+          if (ks + 1 < D / 16) {
+            Ak[c ^ 1] = lds_row16(sk, 32 * kt + n, 2 * (ks + 1) + hh);
+            asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory");
+          } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          }
+          asm volatile("" : "+v"(Ak[c]));
+          sacc[kt] = mfma32(Ak[c], qf[ks], sacc[kt]);
+        }
+      }
+      float mx = NEG;
+      auto scores = [&](auto masked) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+            float s = sacc[kt][e] * a.scale_log2;
+            if (decltype(masked)::value && (key > qrow || key >= T)) s = NEG;
+            sacc[kt][e] = s;
+            mx = fmaxf(mx, s);
+          }
+      };
+      // a tile whose keys all precede the wave's first query and lie in the
+      // sequence masks nothing (a wave-uniform test)
+      if (kv0 + BKV - 1 <= q0 + 32 * w && kv0 + BKV <= T)
+        scores(std::false_type{});
+      else
+        scores(std::true_type{});
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2_hw(m - mnew);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2_hw(sacc[kt][e] - mnew);
+          sacc[kt][e] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l = l * alpha + rs;
+      m = mnew;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      u32x4_t pf[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) pf[kt][jj] = pack_p(sacc[kt], jj);
+      // O^T over steps i = (dt, kt, jj); the two transpose reads of step
+      // i+1 go out before the MFMA of step i
+      constexpr int NI = (D / 32) * 2 * 2;
+      const uint32_t sva = lds_addr(sk + TILE);
+      u32x4_t Vt[2];
+      auto reads = [&](int i, int slot) {
+        const int dt = i / 4, kt = (i >> 1) & 1, jj = i & 1;
+        const int ro = (32 * kt + 16 * jj) * 256;
+        Vt[slot] = lds_tr_pair(sva + trb[dt], ro, ro + 8 * 256);
+      };
+      reads(0, 0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int dt = i / 4, kt = (i >> 1) & 1, jj = i & 1;
+        const int c = i & 1;
+        if (i + 1 < NI) {
+          reads(i + 1, c ^ 1);
+          asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        asm volatile("" : "+v"(Vt[c]));
+        oacc[dt] = mfma32(Vt[c], pf[kt][jj], oacc[dt]);
+      }
+    }
+    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (qrow < T) {
+    const float linv = 1.f / l;
+    uint16_t* orow = a.o + ((long)b * T + qrow) * a.ldo + h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * hh;
+        u32x2_t v;
+        v.x = pack_bf(oacc[dt][4 * j] * linv, oacc[dt][4 * j + 1] * linv);
+        v.y = pack_bf(oacc[dt][4 * j + 2] * linv, oacc[dt][4 * j + 3] * linv);
+        *reinterpret_cast<u32x2_t*>(orow + d) = v;
+      }
+    if (hh == 0) a.lse[((long)b * a.Hq + h) * T + qrow] = (m + log2f(l)) * LN2;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
   static_assert(D == 128, "rows of 16 chunks");
@@ -1023,14 +1213,22 @@ hipError_t set_lds(K kern, size_t bytes) {
 template <int D>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
   constexpr size_t lds = 2 * (64 * (D + 8) + D * (64 + 8)) * sizeof(uint16_t);
+  constexpr size_t lds_dl = 2 * 2 * 64 * D * sizeof(uint16_t);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(attn_fwd_kernel<D>, lds);
     if (e != hipSuccess) return e;
+    if constexpr (D == 128) {
+      e = set_lds(attn_fwd_dl_kernel<D>, lds_dl);
+      if (e != hipSuccess) return e;
+    }
     attr = true;
   }
   const int nqb = (a.T + 127) / 128;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds, s, a);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL(attn_fwd_dl_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_dl, s, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

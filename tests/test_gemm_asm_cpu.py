@@ -124,7 +124,8 @@ def _check(body):
 
 @pytest.mark.parametrize("src,pattern", [("gemm.hip", "gemm_dl_kernel"),
                                          ("attention.hip", "attn_dkdv_dl_kernel"),
-                                         ("attention.hip", "attn_dq_dl_kernel")])
+                                         ("attention.hip", "attn_dq_dl_kernel"),
+                                         ("attention.hip", "attn_fwd_dl_kernel")])
 def test_untracked_lds_reads_are_waited_for_before_use(src, pattern):
     kernels = _kernels(_device_asm(src), pattern)
     with_tr = [(n, b) for n, b in kernels if any("ds_read_b64_tr_b16" in l for l in b)]
