@@ -21,10 +21,11 @@
 // kernel owns 128 keys per workgroup and loops over every query head of the
 // GQA group and every query tile at or after its keys; a dQ kernel owns 128
 // queries and loops over key tiles up to the diagonal.  For head_dim 128
-// both take their streamed tiles (queries for dK/dV, keys for dQ) straight
-// into LDS and read the transposed operands with LDS transpose reads
-// (attn_dkdv_dl_kernel, attn_dq_dl_kernel); the register-staged forms
-// (attn_dkdv_kernel, attn_dq_kernel) serve head_dim 64.
+// the forward and both backward kernels take their streamed tiles (keys and
+// values, or queries and dO for dK/dV) straight into LDS and read the
+// transposed operands with LDS transpose reads (attn_fwd_dl_kernel,
+// attn_dkdv_dl_kernel, attn_dq_dl_kernel); the register-staged forms serve
+// head_dim 64.
 #include <type_traits>
 
 #include "common.h"
