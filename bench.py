@@ -1,21 +1,24 @@
 """Benchmark of the layer-streamed training step on one MI355X.
 
 Workload (default): Qwen2.5-7B-shaped decoder, random N(0, 0.02^2) init,
-batch 16 x seq 1024 uniform random token ids, checkpoint interval 4; bf16
-weights stream from pinned host memory, fp32 master + Adam states on the
-host, CPU Adam, weight loads up to 3 layers ahead of compute.  Layers 1-8
-(at most a third of the layers) stay on the device between steps: each
-one's updated copy streams in during the backward right after its host
-update (--resident-layers).  A step is one full mt_stream_step (forward,
-head, segment re-forward, recompute + backward, gradient offload, CPU Adam
-of every unit).
+batch 16 x seq 1024 uniform random token ids (a fresh seeded batch every
+step), checkpoint interval 4; bf16 weights stream from pinned host memory,
+fp32 master + Adam states on the host, CPU Adam, weight loads up to 3 layers
+ahead of compute.  Layers 1-8 (at most a third of the layers) stay on the
+device between steps: each one's updated copy streams in during the
+backward right after its host update (--resident-layers).  A step is one
+full mt_stream_step (forward, head, segment re-forward, backward, gradient
+offload, CPU Adam of every unit).
 
 Prints one JSON line: sustained TFLOPS by the 6ND + 12LHT^2 formula
 (MegaTrain listing page, Table 7 caption; T^2 term not scaled by the batch)
-plus tokens/s, the roofline of the dominant kernel (the GEMM kernel
-instantiation with the largest total time in the step, every launch timed
-with HIP events on the compute stream inside the timed steps), and the CPU
-oracle timed on a bounded sample.
+plus tokens/s, the roofline of the dominant kernel (the GEMM instantiation
+or attention kernel with the largest total time in the step, every launch
+timed with HIP events on the compute stream inside the timed steps), the
+same steps under the pages' own schedule (every layer streamed every step,
+double buffering, per-layer recompute in the backward), and the CPU oracle
+timed on a bounded sample.  --ablation adds the listing page's Table 4
+ablation (prefetch depth, slab pool, checkpoint interval) on the same model.
 """
 import argparse
 import json
@@ -135,6 +138,79 @@ def cpu_baseline(shape):
     return step_s, cores, sample_s, T, nb
 
 
+def step_log(tag, loss, ms, st):
+    log(f"{tag}: loss {loss:.4f} {ms:.0f} ms "
+        f"fwd {st['fwd_ms']:.0f} head {st['head_ms']:.0f} bwd {st['bwd_ms']:.0f} "
+        f"tail {st['tail_ms']:.0f} adam {st['adam_ms']:.0f} exposed "
+        f"{st['exposed_wait_fwd_ms']:.0f}/{st['exposed_wait_bwd_ms']:.0f} ms; host waits "
+        f"ring {st['host_ring_wait_ms']:.0f} slab {st['host_slab_wait_ms']:.0f} "
+        f"op {st['host_op_wait_ms']:.0f} adam-idle {st['host_adam_idle_ms']:.0f} ms; "
+        f"at {st['host_start_ms']:.0f} start, {st['gpu_done_ms']:.0f} gpu done, "
+        f"{st['grads_landed_ms']:.0f} grads landed, {st['updates_done_ms']:.0f} updates done")
+
+
+def gemm_layout(name):
+    """NT / NN / TN from a GEMM kernel name (the layout template argument:
+    first of gemm_dl_kernel, fifth of gemm_kernel)."""
+    import re
+    m = re.match(r"(gemm_dl_kernel|gemm_kernel)<([^>]*)>", name)
+    if not m:
+        return None
+    args = [a.strip() for a in m.group(2).split(",")]
+    lay = int(args[0] if m.group(1) == "gemm_dl_kernel" else args[4])
+    return ("NT", "NN", "TN")[lay]
+
+
+def kernel_table(per_step):
+    """Sum each kernel's launches, time and FLOPs over the timed steps."""
+    agg = {}
+    for kts in per_step:
+        for k in kts:
+            a = agg.setdefault(k["name"], {"launches": 0, "ms": 0.0, "flops": 0.0})
+            a["launches"] += k["launches"]
+            a["ms"] += k["ms"]
+            a["flops"] += k["flops"]
+    return agg
+
+
+def rate(a):
+    """Achieved TFLOP/s of an aggregate: FLOPs per launch / mean launch time."""
+    return a["flops"] / (a["ms"] / 1e3) / 1e12 if a["ms"] > 0 else 0.0
+
+
+def run_schedule(model, shape, batches, warmup, tag, **knobs):
+    """Switch the model to another schedule, then time len(batches) - warmup
+    steps on a fresh arena; returns a small record."""
+    import numpy as np
+    import torch
+    model.set_schedule(**knobs)
+    torch.cuda.synchronize()
+    arena = torch.empty(model.arena_bytes(shape.batch, shape.seq), dtype=torch.uint8,
+                        device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    walls, stats = [], []
+    for i, ids in enumerate(batches):
+        ts = time.perf_counter()
+        loss, st = model.step(ids, arena, streams)
+        ms = 1e3 * (time.perf_counter() - ts)
+        step_log(f"{tag} {'warmup' if i < warmup else 'step'} {i}", loss, ms, st)
+        if i >= warmup:
+            walls.append(ms)
+            stats.append(st)
+    torch.cuda.synchronize()
+    rec = {"knobs": knobs, "steps": len(walls),
+           "ms_per_step": round(float(np.mean(walls)), 2),
+           "arena_bytes": int(arena.numel()),
+           "exposed_wait_fwd_ms": round(float(np.mean([s["exposed_wait_fwd_ms"] for s in stats])), 2),
+           "exposed_wait_bwd_ms": round(float(np.mean([s["exposed_wait_bwd_ms"] for s in stats])), 2),
+           "fwd_ms": round(float(np.mean([s["fwd_ms"] for s in stats])), 2),
+           "bwd_ms": round(float(np.mean([s["bwd_ms"] for s in stats])), 2),
+           "h2d_bytes": float(np.mean([s["h2d_bytes"] for s in stats]))}
+    del arena
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,8 +230,13 @@ def main():
     # fit within the forward's compute (about 7 ms per layer); measured
     # 0 / 8 / 12 / 16: 1060 / 1030 / 1034 / 1029 ms per step
     ap.add_argument("--resident-layers", type=int, default=-1)
+    ap.add_argument("--keep-internals", type=int, default=1)
     # CPU threads for Adam and the embedding scatter (memory-bandwidth bound)
     ap.add_argument("--host-threads", type=int, default=16)
+    # the same model under the pages' schedule after the timed steps (0: skip)
+    ap.add_argument("--pages-steps", type=int, default=3)
+    # the listing page's Table 4 ablation on the same model
+    ap.add_argument("--ablation", action="store_true")
     # after the timed steps, three plain 1 GiB device copies: the known-size
     # kernel that hardware byte counters (rocprofv3 --pmc) are calibrated by
     ap.add_argument("--pmc-copy", action="store_true")
@@ -177,47 +258,146 @@ def main():
         shape = shape.with_(ckpt_interval=args.ckpt_interval)
     resident = (min(8, shape.n_layers // 3) if args.resident_layers < 0
                 else min(args.resident_layers, shape.n_layers))
+    keep = args.keep_internals
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     model = mt.Model(shape, prefetch_depth=args.prefetch_depth,
                      use_slab_pool=0 if args.no_slab_pool else 1, check_finite=1,
                      time_kernels=1, host_threads=args.host_threads,
-                     resident_layers=resident)
+                     resident_layers=resident, keep_internals=keep)
     log(f"model created in {time.perf_counter() - t0:.1f}s")
     t0 = time.perf_counter()
     init_weights(model, shape, seed=0)
     log(f"weights initialised in {time.perf_counter() - t0:.1f}s")
-    ids = synth.make_tokens(shape)
+    # a fresh seeded batch for every step, drawn before any step runs
+    n_batches = args.warmup + args.steps
+    batches = [synth.make_tokens(shape, seed=1000 + i) for i in range(n_batches)]
     arena_bytes = model.arena_bytes(shape.batch, shape.seq)
     arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
     streams = [torch.cuda.Stream() for _ in range(3)]
     for i in range(args.warmup):
         t0 = time.perf_counter()
-        loss, st = model.step(ids, arena, streams)
-        log(f"warmup {i}: loss {loss:.4f} {1e3 * (time.perf_counter() - t0):.0f} ms")
+        loss, st = model.step(batches[i], arena, streams)
+        step_log(f"warmup {i}", loss, 1e3 * (time.perf_counter() - t0), st)
     torch.cuda.synchronize()
-    stats = []
-    losses = []
-    step_wall = []
+    stats, losses, step_wall, ktimes = [], [], [], []
     t_start = time.perf_counter()
     for i in range(args.steps):
         ts = time.perf_counter()
-        loss, st = model.step(ids, arena, streams)
+        loss, st = model.step(batches[args.warmup + i], arena, streams)
         step_wall.append(1e3 * (time.perf_counter() - ts))
         stats.append(st)
         losses.append(loss)
-        log(f"step {i}: loss {loss:.4f} {1e3 * (time.perf_counter() - ts):.0f} ms "
-            f"fwd {st['fwd_ms']:.0f} head {st['head_ms']:.0f} bwd {st['bwd_ms']:.0f} "
-            f"tail {st['tail_ms']:.0f} adam {st['adam_ms']:.0f} exposed "
-            f"{st['exposed_wait_fwd_ms']:.0f}/{st['exposed_wait_bwd_ms']:.0f} ms; host waits "
-            f"ring {st['host_ring_wait_ms']:.0f} slab {st['host_slab_wait_ms']:.0f} "
-            f"op {st['host_op_wait_ms']:.0f} adam-idle {st['host_adam_idle_ms']:.0f} ms; "
-            f"at {st['host_start_ms']:.0f} start, {st['gpu_done_ms']:.0f} gpu done, "
-            f"{st['grads_landed_ms']:.0f} grads landed, {st['updates_done_ms']:.0f} updates done")
+        ktimes.append(model.kernel_times())
+        step_log(f"step {i}", loss, step_wall[-1], st)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = 1e3 * elapsed / args.steps
-    log(f"dominant GEMM kernel per step: {[s['probe_kernel'] for s in stats]}")
+    log(f"dominant kernel per step: {[s['probe_kernel'] for s in stats]}")
+    del arena
+    torch.cuda.empty_cache()
+
+    n_params = metrics.shape_param_count(shape)
+    D = shape.tokens
+    f_formula = metrics.formula_flops(n_params, shape.n_layers, shape.hidden, shape.batch, shape.seq)
+    f_xb = metrics.formula_flops_xbatch(n_params, shape.n_layers, shape.hidden, shape.batch, shape.seq)
+    _, plan_ops, _, _ = mt.debug_plan(shape.n_layers, shape.ckpt_interval, args.prefetch_depth,
+                                      keep, resident)
+    f_exec = metrics.executed_flops(shape, plan_ops, keep)
+    f_timed = float(np.mean([s["probe_all_flops"] for s in stats]))
+    step_s = ms_per_step / 1e3
+    tflops = f_formula / step_s / 1e12
+    tok_s = D / step_s
+
+    # per-kernel aggregates over the timed steps; the dominant kernel is the
+    # one with the largest total time
+    agg = kernel_table(ktimes)
+    kernel = max(agg, key=lambda k: agg[k]["ms"]) if agg else ""
+    top = agg.get(kernel, {"launches": 0, "ms": 0.0, "flops": 0.0})
+    probe_n = top["launches"]
+    avg_launch_ms = top["ms"] / max(probe_n, 1)
+    flops_per_launch = top["flops"] / max(probe_n, 1)
+    achieved = rate(top)
+    gemm_ms = float(np.mean([s["probe_all_gemm_ms"] for s in stats]))
+    attn_ms = float(np.mean([s["probe_all_attn_ms"] for s in stats]))
+    families = {}
+    for name, a in agg.items():
+        lay = gemm_layout(name)
+        if lay:
+            f = families.setdefault(lay, {"launches": 0, "ms": 0.0, "flops": 0.0})
+            for k in f:
+                f[k] += a[k]
+    gemm_families = {lay: {"ms_per_step": round(f["ms"] / args.steps, 2),
+                           "tflops": round(rate(f), 1),
+                           "frac": round(rate(f) / PEAK_BF16_TFLOPS, 4)}
+                     for lay, f in sorted(families.items())}
+    attn = {}
+    for name, a in agg.items():
+        if name.startswith("attn"):
+            attn[name] = {"ms_per_step": round(a["ms"] / args.steps, 3),
+                          "avg_launch_ms": round(a["ms"] / max(a["launches"], 1), 4),
+                          "tflops": round(rate(a), 1),
+                          "frac": round(rate(a) / PEAK_BF16_TFLOPS, 4)}
+    # the backward as a whole against its 5 algorithmic products (the two
+    # kernels together execute 7: S and dP are formed in both)
+    bwd = [a for n, a in agg.items() if n.startswith(("attn_delta", "attn_dkdv", "attn_dq"))]
+    if bwd:
+        b_ms = sum(a["ms"] for a in bwd)
+        b_alg = sum(a["flops"] for a in bwd) * 5 / 7
+        attn["backward_algorithmic"] = {
+            "ms_per_step": round(b_ms / args.steps, 3),
+            "tflops": round(b_alg / (b_ms / 1e3) / 1e12, 1),
+            "frac": round(b_alg / (b_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    h2d = np.mean([s["h2d_bytes"] for s in stats])
+    d2h = np.mean([s["d2h_bytes"] for s in stats])
+    h2d_ms = np.mean([s["h2d_ms"] for s in stats])
+    d2h_ms = np.mean([s["d2h_ms"] for s in stats])
+
+    # the pages' schedule on the same model: every layer streamed every
+    # step (no resident layers), double buffering, and the per-layer
+    # recompute inside the backward instead of kept internals
+    pages = None
+    base_knobs = dict(prefetch_depth=args.prefetch_depth, resident_layers=resident,
+                      keep_internals=keep, use_slab_pool=0 if args.no_slab_pool else 1,
+                      ckpt_interval=shape.ckpt_interval)
+    if args.pages_steps > 0:
+        pb = [synth.make_tokens(shape, seed=2000 + i) for i in range(1 + args.pages_steps)]
+        pages = run_schedule(model, shape, pb, 1, "pages",
+                             prefetch_depth=2, resident_layers=0, keep_internals=0)
+        pages["tflops"] = round(f_formula / (pages["ms_per_step"] / 1e3) / 1e12, 3)
+        pages["tokens_per_s"] = round(D / (pages["ms_per_step"] / 1e3), 1)
+    ablation = None
+    if args.ablation:
+        # listing page, Table 4: double buffering off (depth 1), slab pool
+        # off, checkpoint interval 1; each against the pages' schedule and
+        # the tuned one
+        pages_k = dict(prefetch_depth=2, resident_layers=0, keep_internals=0, use_slab_pool=1,
+                       ckpt_interval=shape.ckpt_interval)
+        variants = [
+            ("pages", pages_k),
+            ("pages, no double buffering", dict(pages_k, prefetch_depth=1)),
+            ("pages, no slab pool", dict(pages_k, use_slab_pool=0)),
+            ("pages, K=1", dict(pages_k, ckpt_interval=1)),
+            ("tuned", dict(base_knobs, use_slab_pool=1)),
+            ("tuned, recompute (keep_internals=0)", dict(base_knobs, use_slab_pool=1,
+                                                          keep_internals=0)),
+            ("tuned, no resident layers", dict(base_knobs, use_slab_pool=1, resident_layers=0)),
+            ("tuned, depth 2", dict(base_knobs, use_slab_pool=1, prefetch_depth=2)),
+            ("tuned, no slab pool", dict(base_knobs, use_slab_pool=0)),
+            ("tuned, K=1", dict(base_knobs, use_slab_pool=1, ckpt_interval=1)),
+        ]
+        ablation = []
+        for j, (label, kn) in enumerate(variants):
+            if args.no_slab_pool and kn.get("use_slab_pool"):
+                continue
+            ab = [synth.make_tokens(shape, seed=3000 + 10 * j + i) for i in range(3)]
+            r = run_schedule(model, shape, ab, 1, label, **kn)
+            r["label"] = label
+            r["tflops"] = round(f_formula / (r["ms_per_step"] / 1e3) / 1e12, 3)
+            ablation.append(r)
+            log(f"ablation {label}: {r['ms_per_step']:.0f} ms/step, {r['tflops']:.1f} TFLOPS, "
+                f"arena {r['arena_bytes'] / 2**30:.2f} GiB")
+
     if args.pmc_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -243,32 +423,6 @@ def main():
             torch.cuda.synchronize()
             link_peak[name] = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
         del hbuf, dbuf
-
-    n_params = metrics.shape_param_count(shape)
-    D = shape.tokens
-    f_formula = metrics.formula_flops(n_params, shape.n_layers, shape.hidden, shape.batch, shape.seq)
-    f_xb = metrics.formula_flops_xbatch(n_params, shape.n_layers, shape.hidden, shape.batch, shape.seq)
-    f_exec = metrics.executed_flops(shape)
-    step_s = ms_per_step / 1e3
-    tflops = f_formula / step_s / 1e12
-    tok_s = D / step_s
-
-    # the GEMM kernel instantiation with the largest total time (per step,
-    # from HIP events on the compute stream); the one most steps name
-    names = [s["probe_kernel"] for s in stats]
-    kernel = max(set(names), key=names.count) if names else ""
-    kstats = [s for s in stats if s["probe_kernel"] == kernel]
-    probe_ms = sum(s["probe_kernel_ms"] for s in kstats)
-    probe_n = sum(s["probe_kernel_launches"] for s in kstats)
-    probe_flops = sum(s["probe_kernel_flops"] for s in kstats)
-    gemm_ms = float(np.mean([s["probe_all_gemm_ms"] for s in stats]))
-    avg_launch_ms = probe_ms / max(probe_n, 1)
-    flops_per_launch = probe_flops / max(probe_n, 1)
-    achieved = flops_per_launch / (avg_launch_ms / 1e3) / 1e12 if probe_n else 0.0
-    h2d = np.mean([s["h2d_bytes"] for s in stats])
-    d2h = np.mean([s["d2h_bytes"] for s in stats])
-    h2d_ms = np.mean([s["h2d_ms"] for s in stats])
-    d2h_ms = np.mean([s["d2h_ms"] for s in stats])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -302,7 +456,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic (seeded uniform token ids, a fresh batch each step; random init)",
         "config": {
             "workload": shape.name,
             "layers": shape.n_layers, "hidden": shape.hidden, "heads": shape.n_heads,
@@ -311,6 +465,7 @@ def main():
             "ckpt_interval": shape.ckpt_interval, "prefetch_depth": args.prefetch_depth,
             "slab_pool": not args.no_slab_pool,
             "resident_layers": resident,
+            "keep_internals": keep,
             "parallelism": "single-gpu layer streaming",
             "params": n_params,
         },
@@ -318,6 +473,11 @@ def main():
                     "min": round(float(np.min(step_wall)), 2),
                     "max": round(float(np.max(step_wall)), 2)},
         "tflops_xbatch_formula": round(f_xb / step_s / 1e12, 3),
+        # FLOPs the step's plan executes (forward, re-forward, recompute if
+        # any, backward, head; attention by causal pairs), and the same
+        # summed over the timed launches themselves
+        "executed_tflop_per_step": round(f_exec / 1e12, 2),
+        "timed_launch_tflop_per_step": round(f_timed / 1e12, 2),
         "tflops_executed": round(f_exec / step_s / 1e12, 3),
         "mfma_frac_executed": round(f_exec / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "phases_ms": {k: round(float(np.mean([s[k] for s in stats])), 2) for k in
@@ -344,6 +504,9 @@ def main():
         "device_arena_bytes": stats[-1]["device_arena_bytes"],
         "loss": losses[-1],
         "gemm_ms_per_step": round(gemm_ms, 2),
+        "attn_ms_per_step": round(attn_ms, 2),
+        "gemm_families": gemm_families,
+        "attention": attn,
         "roofline": {
             "kernel": kernel,
             "bound": "mfma",
@@ -357,8 +520,11 @@ def main():
             "flops_per_launch": flops_per_launch,
             "launches": probe_n,
         },
+        "pages_schedule": pages,
         "cpu_baseline": cpu,
     }
+    if ablation is not None:
+        line["ablation"] = ablation
     model.close()
     print(json.dumps(line), flush=True)
 

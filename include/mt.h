@@ -81,7 +81,8 @@ typedef struct {
   int32_t serialize;         /* 1: run W, C and G work on one stream (for invariance tests) */
   int32_t host_alloc;        /* MT_HOST_PINNED (default) | MT_HOST_PAGEABLE (no GPU needed) */
   int32_t keep_grads;        /* 1: keep each step's gradients on the host for mt_model_get_param */
-  int32_t time_kernels;      /* 1: time every GEMM launch with HIP events (stats) */
+  int32_t time_kernels;      /* 1: time every GEMM and attention launch with HIP events
+                                (mt_step_stats, mt_model_kernel_times) */
   int32_t keep_internals;    /* 1 (default): each backward segment's re-forward runs every
                                 layer of the segment with mt_layer_fwd_keep and the
                                 backward uses mt_layer_bwd_saved (K layers of internals
@@ -140,9 +141,12 @@ typedef struct {
                                loads, resident-layer uploads, the step's input) and of
                                the gradient offload copies */
   double exposed_wait_fwd_ms, exposed_wait_bwd_ms; /* compute idle while waiting on weights */
-  double probe_kernel_ms;   /* summed duration of the launches of the GEMM kernel
-                               instantiation with the largest total time (time_kernels) */
-  double probe_kernel_flops;/* algorithmic FLOPs (2 M N K) of those launches */
+  double probe_kernel_ms;   /* summed duration of the launches of the kernel (GEMM
+                               instantiation or attention kernel) with the largest
+                               total time (time_kernels) */
+  double probe_kernel_flops;/* algorithmic FLOPs of those launches (GEMM: 2 M N K;
+                               attention: 2 head_dim FLOPs per causal score pair per
+                               product the kernel needs, see mt_kernel_time) */
   int64_t probe_kernel_launches;
   int64_t pinned_host_bytes, pageable_host_bytes, device_arena_bytes;
   int64_t units_updated;    /* units whose Adam update completed this step */
@@ -151,14 +155,31 @@ typedef struct {
    * optimizer thread idle waiting for a landed gradient */
   double host_ring_wait_ms, host_slab_wait_ms, host_op_wait_ms, host_adam_idle_ms;
   double probe_all_gemm_ms; /* summed duration of every timed GEMM launch of the step */
-  char probe_kernel[96];    /* that instantiation's name, e.g. "gemm_dl_kernel<2, 2, 4, 4, 2, 0, 64, 2>" */
+  char probe_kernel[96];    /* that kernel's name, e.g. "gemm_dl_kernel<2, 2, 4, 4, 2, 0, 64, 2>" */
   /* host-clock times (ms) from the start of mt_stream_step: the step's
    * input (the embedding gather) enqueued, the first weight loads already
    * under way; the host seeing the last backward op complete; the last
    * gradient landed in host memory; the optimizer thread done (the step's
    * tail is what follows gpu_done_ms) */
   double host_start_ms, gpu_done_ms, grads_landed_ms, updates_done_ms;
+  double probe_all_attn_ms; /* summed duration of every timed attention launch */
+  double probe_all_flops;   /* algorithmic FLOPs of every timed launch of the step */
 } mt_step_stats;
+
+/* One kernel's timed launches in the last step (time_kernels = 1): launches
+ * grouped by kernel name (a GEMM instantiation as profilers print it, or an
+ * attention kernel), with their summed duration from HIP events recorded on
+ * the compute stream around each launch and their summed algorithmic FLOPs.
+ * GEMM: 2 M N K.  Attention, with P the causal score pairs (T (T + 1) / 2
+ * per sequence and query head): forward 4 d P (S = Q K^T, O = P V); dK/dV
+ * 8 d P (S, dP = dO V^T, dV = P^T dO, dK = dS^T Q); dQ 6 d P (S, dP,
+ * dQ = dS K); delta 0. */
+typedef struct {
+  char name[96];
+  int64_t launches;
+  double ms;
+  double flops;
+} mt_kernel_time;
 
 typedef struct mt_model mt_model;
 
@@ -237,6 +258,18 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run,
                           mt_model** out);
 void mt_model_destroy(mt_model* model);
 
+/* Changes the schedule knobs of a model between steps (the ablation of the
+ * listing page's Table 4 runs one model under several schedules):
+ * checkpoint interval, prefetch depth, slab pool on -> off, MLP and head
+ * chunks, keep_internals, defer_updates, resident_layers, serialize,
+ * check_finite, time_kernels and the Adam hyperparameters.  precision,
+ * host_alloc, keep_grads, host_threads and the slab pool's size are fixed
+ * at creation (MT_E_INVALID if they differ).  Applies any pending update
+ * first; resident layers are loaded again by the next step.  The next
+ * step's arena size is mt_stream_arena_bytes under the new knobs.  Results
+ * do not depend on the schedule (bitwise). */
+mt_status mt_model_set_schedule(mt_model* model, const mt_run_cfg* run);
+
 /* Parameter names: "embed", "layers.<l>.{attn_norm,w_q,w_k,w_v,w_o,
  * mlp_norm,w_gate,w_up,w_down}", "final_norm", "lm_head"; shapes [out, in].
  * set: copies n fp32 values into the master, writes the bf16 copy (RNE) and
@@ -255,8 +288,21 @@ mt_status mt_model_get_param(const mt_model* model, const char* name,
 /* Adam step counter of the model (number of completed steps). */
 int64_t mt_model_step_count(const mt_model* model);
 
+/* The last step's per-kernel timings (empty unless the run config set
+ * time_kernels).  Writes min(n, cap) entries, sorted by total time, largest
+ * first, and the number available to *n_out. */
+mt_status mt_model_kernel_times(const mt_model* model, mt_kernel_time* out, int32_t cap,
+                                int32_t* n_out);
+
 /* Device arena the streamed step needs for batch x seq tokens. */
 size_t mt_stream_arena_bytes(const mt_model* model, int32_t batch, int32_t seq);
+
+/* The same for a model shape and run config without creating the model (no
+ * host store): the device bytes a step of that depth would take (listing
+ * page, Table 5's depth study: device memory does not grow with depth).
+ * Returns 0 for an invalid shape or knob. */
+size_t mt_stream_arena_bytes_cfg(const mt_model_cfg* cfg, const mt_run_cfg* run, int32_t batch,
+                                 int32_t seq);
 
 /* One training step (blog summary, sections 1-4; listing page, Fig. 3):
  * stream each layer's bf16 weights in on streams[0] (W), run forward,

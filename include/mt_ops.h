@@ -116,13 +116,6 @@ mt_status mt_op_ce_rows(const float* logits, const int32_t* target, void* dlogit
 mt_status mt_op_nonfinite_flags(const void* g, size_t bytes, int32_t f32, int32_t* flags,
                                 void* stream);
 
-/* Device -> host copy into pinned host memory (hipHostMalloc) by a kernel
- * of `blocks` workgroups of 256 threads, so the gradient offload (MegaTrain
- * listing page, Fig. 3, stream G) occupies a bounded part of the GPU.
- * bytes and both addresses must be multiples of 16. */
-mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t blocks,
-                         void* stream);
-
 /* The stream schedule of mt_stream_step for n_layers, checkpoint interval,
  * prefetch depth, kept internals (mt_run_cfg.keep_internals) and resident
  * layers (mt_run_cfg.resident_layers), as plain integers so its hazards can

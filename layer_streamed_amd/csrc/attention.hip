@@ -1234,7 +1234,7 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
 }
 
 template <int D>
-hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
+hipError_t bwd_d(const AttnArgs& a, int stages, hipStream_t s) {
   constexpr size_t lds_kv = (2 * 64 * (D + 8) + 2 * D * (64 + 8)) * sizeof(uint16_t) + 2 * 64 * sizeof(float);
   constexpr size_t lds_q = (2 * 64 * (D + 8) + D * (64 + 8)) * sizeof(uint16_t);
   constexpr size_t lds_dl = 2 * 2 * 64 * D * sizeof(uint16_t) + 4 * 64 * sizeof(float);
@@ -1253,23 +1253,32 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
     }
     attr = true;
   }
-  const long rows = (long)a.B * a.T * a.Hq;
-  hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nkb = (a.T + 127) / 128;
-  if constexpr (D == 128)
-    hipLaunchKernelGGL(attn_dkdv_dl_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_dl, s, a);
-  else
-    hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_kv, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nqb = (a.T + 127) / 128;
-  if constexpr (D == 128)
-    hipLaunchKernelGGL(attn_dq_dl_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_dq_dl, s, a);
-  else
-    hipLaunchKernelGGL(attn_dq_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_q, s, a);
-  return hipGetLastError();
+  if (stages & ATTN_BWD_DELTA) {
+    const long rows = (long)a.B * a.T * a.Hq;
+    hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                       a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & ATTN_BWD_DKDV) {
+    const int nkb = (a.T + 127) / 128;
+    if constexpr (D == 128)
+      hipLaunchKernelGGL(attn_dkdv_dl_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_dl, s, a);
+    else
+      hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_kv, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & ATTN_BWD_DQ) {
+    const int nqb = (a.T + 127) / 128;
+    if constexpr (D == 128)
+      hipLaunchKernelGGL(attn_dq_dl_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_dq_dl, s, a);
+    else
+      hipLaunchKernelGGL(attn_dq_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_q, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 AttnArgs make_args(const uint16_t* qkv, int batch, int seq, int n_heads, int n_kv_heads,
@@ -1302,7 +1311,7 @@ hipError_t attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int
 
 hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
                     const uint16_t* dout, float* delta, uint16_t* dqkv, int batch, int seq,
-                    int n_heads, int n_kv_heads, int head_dim, hipStream_t s) {
+                    int n_heads, int n_kv_heads, int head_dim, hipStream_t s, int stages) {
   if (batch == 0 || seq == 0) return hipSuccess;
   AttnArgs a = make_args(qkv, batch, seq, n_heads, n_kv_heads, head_dim);
   a.o = const_cast<uint16_t*>(o);
@@ -1310,9 +1319,18 @@ hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
   a.dout = dout;
   a.delta = delta;
   a.dqkv = dqkv;
-  if (head_dim == 128) return bwd_d<128>(a, s);
-  if (head_dim == 64) return bwd_d<64>(a, s);
+  if (head_dim == 128) return bwd_d<128>(a, stages, s);
+  if (head_dim == 64) return bwd_d<64>(a, stages, s);
   return hipErrorInvalidValue;
+}
+
+const char* attn_kernel_name(int head_dim, int which) {
+  static const char* n128[4] = {"attn_fwd_dl_kernel<128>", "attn_delta_kernel<128>",
+                                "attn_dkdv_dl_kernel<128>", "attn_dq_dl_kernel<128>"};
+  static const char* n64[4] = {"attn_fwd_kernel<64>", "attn_delta_kernel<64>",
+                               "attn_dkdv_kernel<64>", "attn_dq_kernel<64>"};
+  if (which < 0 || which > 3) return "";
+  return head_dim == 128 ? n128[which] : n64[which];
 }
 
 }  // namespace mt

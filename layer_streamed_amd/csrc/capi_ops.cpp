@@ -196,14 +196,4 @@ mt_status mt_op_nonfinite_flags(const void* g, size_t bytes, int32_t f32, int32_
   return MT_OK;
 }
 
-mt_status mt_op_copy_d2h(const void* src, void* dst_host, size_t bytes, int32_t blocks,
-                         void* stream) {
-  MT_CHECK(src && dst_host, MT_E_INVALID, "mt_op_copy_d2h: null pointer");
-  MT_CHECK(blocks >= 1 && blocks <= 65535, MT_E_INVALID, "mt_op_copy_d2h: blocks in [1, 65535]");
-  MT_CHECK(bytes % 16 == 0 && ((uintptr_t)src & 15) == 0 && ((uintptr_t)dst_host & 15) == 0,
-           MT_E_INVALID, "mt_op_copy_d2h: size and addresses must be multiples of 16");
-  MT_HIP(copy_d2h(src, dst_host, bytes, blocks, static_cast<hipStream_t>(stream)));
-  return MT_OK;
-}
-
 }  // extern "C"

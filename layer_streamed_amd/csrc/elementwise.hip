@@ -368,32 +368,7 @@ __global__ __launch_bounds__(256) void nonfinite_kernel(const u32x4_t* __restric
   if (threadIdx.x == 0) flags[blockIdx.x] = any;
 }
 
-// Device -> pinned host copy with a bounded footprint: `blocks` workgroups
-// stride over 16-byte chunks, so the copy occupies a few CUs instead of the
-// whole chip.  The host buffer must be device-accessible pinned memory.
-__global__ __launch_bounds__(256) void copy_d2h_kernel(const u32x4_t* __restrict__ src,
-                                                       u32x4_t* __restrict__ dst, size_t n16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4_t a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    __builtin_nontemporal_store(a, dst + i);
-    __builtin_nontemporal_store(b, dst + i + stride);
-    __builtin_nontemporal_store(c, dst + i + 2 * stride);
-    __builtin_nontemporal_store(d, dst + i + 3 * stride);
-  }
-  for (; i < n16; i += stride) __builtin_nontemporal_store(src[i], dst + i);
-}
-
 }  // namespace
-
-hipError_t copy_d2h(const void* src, void* dst_host, size_t bytes, int blocks, hipStream_t s) {
-  if (bytes == 0) return hipSuccess;
-  if ((bytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)dst_host & 15)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(copy_d2h_kernel, dim3(blocks), dim3(256), 0, s,
-                     static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst_host), bytes / 16);
-  return hipGetLastError();
-}
 
 namespace {
 template <class E>

@@ -328,6 +328,26 @@ size_t mt_stream_arena_bytes(const mt_model* model, int32_t batch, int32_t seq) 
   return stream_arena_bytes(model, d);
 }
 
+size_t mt_stream_arena_bytes_cfg(const mt_model_cfg* cfg, const mt_run_cfg* run, int32_t batch,
+                                 int32_t seq) {
+  Dims d0, d;
+  if (!cfg || !run || make_dims(cfg, run, 1, 1, &d0) || make_dims(cfg, run, batch, seq, &d))
+    return 0;
+  if (run->ckpt_interval < 1 || run->prefetch_depth < 1 || run->prefetch_depth > 3 ||
+      run->resident_layers < 0 || run->resident_layers > cfg->n_layers)
+    return 0;
+  // a model with its shape and knobs but no host store: the arena depends
+  // on nothing else
+  mt_model m;
+  m.cfg = *cfg;
+  m.run = *run;
+  m.shape = d0;
+  m.es = d0.es();
+  m.ll = layer_layout(d0);
+  m.hl = head_layout(d0);
+  return stream_arena_bytes(&m, d);
+}
+
 // Diagnostic: the plan for L layers, checkpoint interval K, prefetch depth
 // and resident layers.  out receives, for each compute op, (kind, layer, load) and then,
 // for each load, (unit, slot, first_use, last_use, wait_use, gate_use);
@@ -555,9 +575,11 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         ring_cv.notify_all();
       }
       if (!ok) {
-        if (!abort_all.load()) g_fail = 1;
+        if (!abort_all.load()) g_fail = M->sdma->ready() ? 1 : 2;
         abort_all = true;
-        if (host && o.unit >= 0 && !(o.unit == L && defer)) {
+        // after a copy that timed out the engine may still write the slab:
+        // it is not handed back (the model is unusable from here on)
+        if (host && o.unit >= 0 && !(o.unit == L && defer) && M->sdma->ready()) {
           if (own) hipHostFree(host);
           else M->slabs.release(host);
         }
@@ -791,12 +813,15 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   for (auto& e : op_done) e = get_ev();
   for (auto& e : load_done) e = get_ev();
   if (M->run.time_kernels) {
-    // every GEMM launch of the step: per layer forward (2 + 2 per MLP
-    // chunk, run up to twice: forward and segment re-forward) and
-    // recompute+backward (6 + 5 per MLP chunk), and 3 per head chunk
+    // every GEMM and attention launch of the step: per layer forward
+    // (2 GEMMs + 1 attention + 2 GEMMs per MLP chunk, run up to twice:
+    // forward and segment re-forward) and recompute+backward (a forward's
+    // 3 + 1 per chunk, 4 GEMMs + 3 attention + 5 GEMMs per MLP chunk), and
+    // 3 per head chunk
     const size_t nmc = (d.D + d.mlp_chunk - 1) / d.mlp_chunk;
     const size_t nhc = (d.D + d.head_chunk - 1) / d.head_chunk;
-    const size_t launches = (size_t)L * (2 * (2 + 2 * nmc) + 6 + 5 * nmc) + 3 * nhc + 8;
+    const size_t launches =
+        (size_t)L * (2 * (3 + 2 * nmc) + (3 + nmc) + 7 + 5 * nmc) + 3 * nhc + 8;
     probe.ev.resize(2 * launches);
     for (auto& e : probe.ev) e = get_ev();
   }
@@ -982,6 +1007,9 @@ drain:
   }
   if (fail == MT_OK && w_fail.load())
     fail = set_error(MT_E_HIP, "mt_stream_step: weight load failed");
+  if (fail == MT_OK && g_fail.load() == 2)
+    fail = set_error(MT_E_HIP, "mt_stream_step: a gradient copy to the host did not complete "
+                               "within %.0f s", SdmaCopier::COPY_TIMEOUT_S);
   if (fail == MT_OK && (g_fail.load() || a_fail.load() == 1))
     fail = set_error(MT_E_HIP, "mt_stream_step: gradient offload or optimizer thread failed");
   if (fail == MT_OK && nonfinite_loss)
@@ -1012,26 +1040,38 @@ drain:
     for (auto& p : wait_ev_f) s.exposed_wait_fwd_ms += elapsed(p.first, p.second);
     for (auto& p : wait_ev_b) s.exposed_wait_bwd_ms += elapsed(p.first, p.second);
     {
-      // group the timed GEMM launches by kernel instantiation; report the
-      // one with the largest total time
+      // group the timed launches by kernel (GEMM instantiation or attention
+      // kernel); report the one with the largest total time, keep all
       struct Agg { double ms = 0, flops = 0; int64_t n = 0; };
       std::map<std::string, Agg> by;
       for (int i = 0; i + 1 < probe.used; i += 2) {
         const double ms = elapsed(probe.ev[i], probe.ev[i + 1]);
-        Agg& g = by[probe.name[i / 2]];
+        const std::string& name = probe.name[i / 2];
+        Agg& g = by[name];
         g.ms += ms;
         g.flops += probe.flops[i / 2];
         ++g.n;
-        s.probe_all_gemm_ms += ms;
+        if (name.compare(0, 4, "attn") == 0) s.probe_all_attn_ms += ms;
+        else s.probe_all_gemm_ms += ms;
+        s.probe_all_flops += probe.flops[i / 2];
       }
-      const std::pair<const std::string, Agg>* top = nullptr;
-      for (auto& kv : by)
-        if (!top || kv.second.ms > top->second.ms) top = &kv;
-      if (top) {
-        s.probe_kernel_ms = top->second.ms;
-        s.probe_kernel_flops = top->second.flops;
-        s.probe_kernel_launches = top->second.n;
-        snprintf(s.probe_kernel, sizeof s.probe_kernel, "%s", top->first.c_str());
+      M->kernel_times.clear();
+      for (auto& kv : by) {
+        mt_kernel_time k{};
+        snprintf(k.name, sizeof k.name, "%s", kv.first.c_str());
+        k.launches = kv.second.n;
+        k.ms = kv.second.ms;
+        k.flops = kv.second.flops;
+        M->kernel_times.push_back(k);
+      }
+      std::sort(M->kernel_times.begin(), M->kernel_times.end(),
+                [](const mt_kernel_time& a, const mt_kernel_time& b) { return a.ms > b.ms; });
+      if (!M->kernel_times.empty()) {
+        const mt_kernel_time& top = M->kernel_times.front();
+        s.probe_kernel_ms = top.ms;
+        s.probe_kernel_flops = top.flops;
+        s.probe_kernel_launches = top.launches;
+        snprintf(s.probe_kernel, sizeof s.probe_kernel, "%s", top.name);
       }
     }
     s.h2d_bytes = h2d_bytes + h2d_load_bytes + res_bytes;

@@ -97,10 +97,6 @@ hipError_t rope_apply(float* qkv, long ldq, int batch, int seq, int n_heads, int
                       int head_dim, const float* cos_t, const float* sin_t, int inverse,
                       hipStream_t s);
 
-// Device -> pinned host copy by a kernel of `blocks` workgroups (bytes,
-// src and dst multiples of 16).
-hipError_t copy_d2h(const void* src, void* dst_host, size_t bytes, int blocks, hipStream_t s);
-
 // out[i] = in[i] stored as the out type (bf16: RNE).
 // Finiteness of a gradient buffer: NONFINITE_BLOCKS workgroups each scan a
 // strided share of `bytes` bytes of bf16 (f32 = 0) or fp32 values and write
@@ -119,9 +115,17 @@ hipError_t copy_rows_bf16(const uint16_t* src, long lds, uint16_t* dst, long ldd
 hipError_t attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int seq,
                     int n_heads, int n_kv_heads, int head_dim, hipStream_t s);
 // Backward: delta [B, Hq, T] fp32 workspace; dqkv [B*T, (Hq+2Hkv)*d] bf16 out.
+// Three kernels in order: delta = rowsum(dO * O), then dK/dV per key block,
+// then dQ per query block; `stages` (a mask of ATTN_BWD_*) launches a
+// subset, so a caller can time each kernel on its own (in that order).
+enum { ATTN_BWD_DELTA = 1, ATTN_BWD_DKDV = 2, ATTN_BWD_DQ = 4, ATTN_BWD_ALL = 7 };
 hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
                     const uint16_t* dout, float* delta, uint16_t* dqkv, int batch, int seq,
-                    int n_heads, int n_kv_heads, int head_dim, hipStream_t s);
+                    int n_heads, int n_kv_heads, int head_dim, hipStream_t s,
+                    int stages = ATTN_BWD_ALL);
+// Name of the kernel behind attn_fwd (which 0) and the three backward
+// stages (1 delta, 2 dK/dV, 3 dQ) for a head dimension, as profilers print it.
+const char* attn_kernel_name(int head_dim, int which);
 // fp32 storage (debug precision): same contract, one wave per query row
 // (forward, dq) or key row (dk, dv) with fp32 FMA and exact exp/log.
 hipError_t attn_fwd(const float* qkv, float* o, float* lse, int batch, int seq, int n_heads,

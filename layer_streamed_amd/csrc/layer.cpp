@@ -200,29 +200,85 @@ inline std::string kernel_name(const GemmArgsT<float>& g) {
   return "gemm_f32_kernel<" + std::to_string(lay) + ", " + std::to_string(g.epi) + ">";
 }
 
+#define MT_RUN(expr)                  \
+  do {                                \
+    mt_status st_ = (expr);           \
+    if (st_ != MT_OK) return st_;     \
+  } while (0)
+
+// Runs `launch` (one kernel launch on s) between two of the probe's events
+// when a probe with events to spare is given, recording the kernel's name
+// and its algorithmic FLOPs.
+template <class F>
+mt_status timed_launch(Probe* probe, hipStream_t s, const std::string& name, double flops,
+                       F&& launch) {
+  const bool timed = probe && probe->used + 2 <= (int)probe->ev.size();
+  if (timed) MT_HIP(hipEventRecord(probe->ev[probe->used], s));
+  MT_HIP(launch());
+  if (timed) {
+    MT_HIP(hipEventRecord(probe->ev[probe->used + 1], s));
+    probe->used += 2;
+    probe->name.push_back(name);
+    probe->flops.push_back(flops);
+  }
+  return MT_OK;
+}
+
 // `split`: the workspace's split-tail area (SPLIT_ELEMS floats), or null.
 template <class E>
 mt_status run_gemm(GemmArgsT<E> g, hipStream_t s, Probe* probe, float* split) {
   if (const char* m = gemm_check(g)) return set_error(MT_E_SHAPE, "layer GEMM: %s", m);
   g.ws = split;
   g.ws_elems = split ? (long)SPLIT_ELEMS : 0;
-  const bool timed = probe && probe->used + 2 <= (int)probe->ev.size();
-  if (timed) MT_HIP(hipEventRecord(probe->ev[probe->used], s));
-  MT_HIP(gemm_launch(g, s));
-  if (timed) {
-    MT_HIP(hipEventRecord(probe->ev[probe->used + 1], s));
-    probe->used += 2;
-    probe->name.push_back(kernel_name(g));
-    probe->flops.push_back(2.0 * g.M * (double)g.N * g.K);
-  }
-  return MT_OK;
+  return timed_launch(probe, s, probe ? kernel_name(g) : std::string(),
+                      2.0 * g.M * (double)g.N * g.K, [&] { return gemm_launch(g, s); });
 }
 
-#define MT_RUN(expr)                  \
-  do {                                \
-    mt_status st_ = (expr);           \
-    if (st_ != MT_OK) return st_;     \
-  } while (0)
+// Causal score pairs of the attention (query t sees keys 0..t), over the
+// batch and the query heads: the products of the forward and backward each
+// take 2 * head_dim FLOPs per pair.
+inline double attn_pairs(const Dims& d) {
+  return (double)d.B * d.Hq * ((double)d.T * (d.T + 1) / 2);
+}
+
+// Attention forward: S = Q K^T and O = P V, 2 products.
+template <class E>
+mt_status run_attn_fwd(const Dims& d, const E* qkv, E* o, float* lse, hipStream_t s,
+                       Probe* probe) {
+  if constexpr (std::is_same_v<E, uint16_t>) {
+    return timed_launch(probe, s, attn_kernel_name(d.d, 0), 2 * 2.0 * d.d * attn_pairs(d), [&] {
+      return attn_fwd(qkv, o, lse, d.B, d.T, d.Hq, d.Hkv, d.d, s);
+    });
+  } else {
+    MT_HIP(attn_fwd(qkv, o, lse, d.B, d.T, d.Hq, d.Hkv, d.d, s));
+    return MT_OK;
+  }
+}
+
+// Attention backward, each kernel timed on its own.  FLOPs per kernel are
+// the products it needs for its outputs: dK/dV recomputes S and forms dP,
+// dV = P^T dO and dK = dS^T Q (4 products); dQ recomputes S and dP and
+// forms dQ = dS K (3).  The backward as a whole needs 5 (S, dP, dV, dK,
+// dQ); splitting it so that no two workgroups add into one output (no
+// atomics, a fixed summation order) costs the 2 recomputed ones.
+template <class E>
+mt_status run_attn_bwd(const Dims& d, const E* qkv, const E* o, const float* lse, const E* dout,
+                       float* delta, E* dqkv, hipStream_t s, Probe* probe) {
+  if constexpr (std::is_same_v<E, uint16_t>) {
+    const double pf = 2.0 * d.d * attn_pairs(d);
+    auto stage = [&](int st) {
+      return [&, st] {
+        return attn_bwd(qkv, o, lse, dout, delta, dqkv, d.B, d.T, d.Hq, d.Hkv, d.d, s, st);
+      };
+    };
+    MT_RUN(timed_launch(probe, s, attn_kernel_name(d.d, 1), 0.0, stage(ATTN_BWD_DELTA)));
+    MT_RUN(timed_launch(probe, s, attn_kernel_name(d.d, 2), 4 * pf, stage(ATTN_BWD_DKDV)));
+    return timed_launch(probe, s, attn_kernel_name(d.d, 3), 3 * pf, stage(ATTN_BWD_DQ));
+  } else {
+    MT_HIP(attn_bwd(qkv, o, lse, dout, delta, dqkv, d.B, d.T, d.Hq, d.Hkv, d.d, s));
+    return MT_OK;
+  }
+}
 
 // Typed weight pointers of a layer view.
 template <class E>
@@ -244,7 +300,7 @@ mt_status attn_half(const Dims& d, const LayerW<E>& w, const E* x, const LayerWs
                           d.NQKV),
                   s, probe, ws.split));
   MT_HIP(rope_apply(ws.qkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 0, s));
-  MT_HIP(attn_fwd(ws.qkv, ws.o, ws.lse, d.B, d.T, d.Hq, d.Hkv, d.d, s));
+  MT_RUN(run_attn_fwd(d, ws.qkv, ws.o, ws.lse, s, probe));
   GemmArgsT<E> go = gemm<E>(GEMM_NT, EPI_RESID_BF16, d.D, d.H, d.Qd, ws.o, d.Qd, w.wo, d.Qd,
                             ws.x_mid, d.H);
   go.R = x;
@@ -373,7 +429,7 @@ mt_status layer_bwd_t(const Dims& d, const mt_layer_view& wv, const E* x_in, con
                           d.Qd),
                   s, probe, ws.split));
   // ---- attention and RoPE
-  MT_HIP(attn_bwd(ws.qkv, ws.o, ws.lse, ws.dout, ws.delta, ws.dqkv, d.B, d.T, d.Hq, d.Hkv, d.d, s));
+  MT_RUN(run_attn_bwd(d, ws.qkv, ws.o, ws.lse, ws.dout, ws.delta, ws.dqkv, s, probe));
   MT_HIP(rope_apply(ws.dqkv, d.NQKV, d.B, d.T, d.Hq, d.Hkv, d.d, ws.cos_t, ws.sin_t, 1, s));
   // ---- QKV projection
   MT_RUN(run_gemm(gemm<E>(GEMM_TN, EPI_BF16, d.NQKV, d.H, d.D, ws.dqkv, d.NQKV, ws.a, d.H,

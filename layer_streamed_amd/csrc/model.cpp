@@ -165,14 +165,7 @@ mt_model::~mt_model() {
   }
 }
 
-extern "C" {
-
-mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_model** out) {
-  MT_CHECK(cfg && run && out, MT_E_INVALID, "mt_model_create: null argument");
-  *out = nullptr;
-  Dims d;
-  if (const char* msg = make_dims(cfg, run, 1, 1, &d))
-    return set_error(MT_E_SHAPE, "mt_model_create: %s", msg);
+static mt_status check_run(const mt_model_cfg* cfg, const mt_run_cfg* run) {
   MT_CHECK(run->ckpt_interval >= 1, MT_E_INVALID, "ckpt_interval must be >= 1");
   MT_CHECK(run->prefetch_depth >= 1 && run->prefetch_depth <= 3, MT_E_INVALID,
            "prefetch_depth must be 1, 2 or 3");
@@ -188,6 +181,18 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
   MT_CHECK(run->lr > 0 && run->beta1 >= 0 && run->beta1 < 1 && run->beta2 >= 0 &&
                run->beta2 < 1 && run->eps >= 0,
            MT_E_INVALID, "bad Adam hyperparameters");
+  return MT_OK;
+}
+
+extern "C" {
+
+mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_model** out) {
+  MT_CHECK(cfg && run && out, MT_E_INVALID, "mt_model_create: null argument");
+  *out = nullptr;
+  Dims d;
+  if (const char* msg = make_dims(cfg, run, 1, 1, &d))
+    return set_error(MT_E_SHAPE, "mt_model_create: %s", msg);
+  if (mt_status st = check_run(cfg, run); st != MT_OK) return st;
 
   std::unique_ptr<mt_model> m(new mt_model());
   m->cfg = *cfg;
@@ -261,7 +266,38 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
 
 void mt_model_destroy(mt_model* model) { delete model; }
 
+mt_status mt_model_set_schedule(mt_model* m, const mt_run_cfg* run) {
+  MT_CHECK(m && run, MT_E_INVALID, "mt_model_set_schedule: null argument");
+  Dims d;
+  if (const char* msg = make_dims(&m->cfg, run, 1, 1, &d))
+    return set_error(MT_E_SHAPE, "mt_model_set_schedule: %s", msg);
+  if (mt_status st = check_run(&m->cfg, run); st != MT_OK) return st;
+  const mt_run_cfg& o = m->run;
+  MT_CHECK(run->precision == o.precision && run->host_alloc == o.host_alloc &&
+               run->keep_grads == o.keep_grads && run->host_threads == o.host_threads,
+           MT_E_INVALID,
+           "mt_model_set_schedule: precision, host_alloc, keep_grads and host_threads are fixed "
+           "when the model is created");
+  MT_CHECK(!run->use_slab_pool || (o.use_slab_pool && run->n_slabs == o.n_slabs), MT_E_INVALID,
+           "mt_model_set_schedule: the slab pool (and its size) is allocated when the model is "
+           "created; it can only be switched off");
+  flush_pending(m);  // the pending updates belong to the old schedule's step
+  m->resident_valid.clear();  // resident slots are refilled under the new schedule
+  m->run = *run;
+  return MT_OK;
+}
+
 int64_t mt_model_step_count(const mt_model* model) { return model ? model->step : -1; }
+
+mt_status mt_model_kernel_times(const mt_model* model, mt_kernel_time* out, int32_t cap,
+                                int32_t* n_out) {
+  MT_CHECK(model && n_out && cap >= 0 && (out || cap == 0), MT_E_INVALID,
+           "mt_model_kernel_times: null pointer or negative capacity");
+  const int32_t n = (int32_t)model->kernel_times.size();
+  for (int32_t i = 0; i < n && i < cap; ++i) out[i] = model->kernel_times[i];
+  *n_out = n;
+  return MT_OK;
+}
 
 mt_status mt_model_set_param(mt_model* m, const char* name, const float* src, size_t n) {
   MT_CHECK(m && src, MT_E_INVALID, "mt_model_set_param: null argument");

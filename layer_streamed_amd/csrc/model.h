@@ -108,6 +108,8 @@ struct mt_model {
   // streamed copy, left there by the previous step
   std::vector<uint8_t> resident_valid;
   const void* resident_arena = nullptr;
+  // the last step's timed kernel launches (time_kernels), grouped by kernel
+  std::vector<mt_kernel_time> kernel_times;
   int64_t step = 0;
   bool broken = false;
   int64_t pinned_bytes = 0, pageable_bytes = 0;

@@ -1,5 +1,7 @@
 #include "sdma.h"
 
+#include <chrono>
+
 #include <hip/hip_runtime_api.h>
 #include <hsa/hsa.h>
 #include <hsa/hsa_ext_amd.h>
@@ -112,7 +114,7 @@ SdmaCopier::~SdmaCopier() {
 }
 
 bool SdmaCopier::copy_d2h(void* dst_host, const void* src_dev, size_t bytes) {
-  if (!ok_) return false;
+  if (!ok_ || timed_out_) return false;
   if (bytes == 0) return true;
   hsa_signal_t sig{signal_};
   hsa_signal_store_screlease(sig, 1);
@@ -120,10 +122,27 @@ bool SdmaCopier::copy_d2h(void* dst_host, const void* src_dev, size_t bytes) {
       dst_host, hsa_agent_t{cpu_}, src_dev, hsa_agent_t{gpu_}, bytes, 0, nullptr, sig,
       static_cast<hsa_amd_sdma_engine_id_t>(engine_), true);
   if (st != HSA_STATUS_SUCCESS) return false;
-  while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_LT, 1, UINT64_MAX,
-                                   HSA_WAIT_STATE_BLOCKED) >= 1) {
+  // Bounded wait: the copy engine signals completion by decrementing the
+  // signal to 0 (an error sets it negative).  A copy that has not finished
+  // after COPY_TIMEOUT_S is reported as a failure, so the caller's abort
+  // path returns an error instead of blocking its thread for ever.
+  uint64_t freq = 0;
+  if (hsa_system_get_info(HSA_SYSTEM_INFO_TIMESTAMP_FREQUENCY, &freq) != HSA_STATUS_SUCCESS ||
+      freq == 0)
+    freq = 1000000000ull;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    const hsa_signal_value_t v = hsa_signal_wait_scacquire(
+        sig, HSA_SIGNAL_CONDITION_LT, 1, freq / 10, HSA_WAIT_STATE_BLOCKED);
+    if (v == 0) return true;
+    if (v < 0) return false;
+    const double waited =
+        std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    if (waited > COPY_TIMEOUT_S) {
+      timed_out_ = true;
+      return false;
+    }
   }
-  return true;
 }
 
 }  // namespace mt

@@ -71,12 +71,17 @@ class StepStats(C.Structure):
                 "host_ring_wait_ms", "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms",
                 "probe_all_gemm_ms")] + [("probe_kernel", C.c_char * 96)] + [
             (n, C.c_double) for n in ("host_start_ms", "gpu_done_ms", "grads_landed_ms",
-                                      "updates_done_ms")]
+                                      "updates_done_ms", "probe_all_attn_ms", "probe_all_flops")]
 
     def as_dict(self):
         d = {n: getattr(self, n) for n, _ in self._fields_}
         d["probe_kernel"] = self.probe_kernel.decode()
         return d
+
+
+class KernelTime(C.Structure):
+    _fields_ = [("name", C.c_char * 96), ("launches", C.c_int64), ("ms", C.c_double),
+                ("flops", C.c_double)]
 
 
 # ---------------------------------------------------------------- signatures
@@ -114,10 +119,13 @@ _SIGS = {
     "mt_layer_recompute_bwd": (_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
     "mt_model_create": (_I32, _P, _P, _P),
     "mt_model_destroy": (None, _P),
+    "mt_model_set_schedule": (_I32, _P, _P),
     "mt_model_set_param": (_I32, _P, C.c_char_p, _P, _SZ),
     "mt_model_get_param": (_I32, _P, C.c_char_p, _I32, _P, _SZ),
     "mt_model_step_count": (_I64, _P),
+    "mt_model_kernel_times": (_I32, _P, _P, _I32, _P),
     "mt_stream_arena_bytes": (_SZ, _P, _I32, _I32),
+    "mt_stream_arena_bytes_cfg": (_SZ, _P, _P, _I32, _I32),
     "mt_stream_step": (_I32, _P, _P, _I32, _I32, _P, _SZ, _P, _P, _P),
     "mt_host_adam": (_I32, _P, _P, _P, _P, _I32, _P, _SZ, _I64, _P),
     "mt_run_cfg_default": (None, _P),
@@ -126,7 +134,6 @@ _SIGS = {
     "mt_layer_internals_bytes": (_SZ, _P, _P, _I32, _I32),
     "mt_layer_fwd_keep": (_I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
     "mt_layer_bwd_saved": (_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P, _SZ, _P),
-    "mt_op_copy_d2h": (_I32, _P, _P, _SZ, _I32, _P),
     "mt_op_nonfinite_flags": (_I32, _P, _SZ, _I32, _P, _P),
 }
 FN = {}
@@ -297,6 +304,16 @@ def layer_bwd_saved(mcfg, rcfg, view, x_in, dy, dx, gview, batch, seq, internals
                ws.numel() * ws.element_size(), stream_handle(stream)), "mt_layer_bwd_saved")
 
 
+def arena_bytes_for(shape, batch=None, seq=None, **run_kw) -> int:
+    """mt_stream_arena_bytes_cfg: device arena of a step without a model."""
+    mcfg = model_cfg(shape)
+    kw = dict(ckpt_interval=shape.ckpt_interval, mlp_chunk_tokens=shape.mlp_chunk_tokens)
+    kw.update(run_kw)
+    r = run_cfg(**kw)
+    return call("mt_stream_arena_bytes_cfg", C.byref(mcfg), C.byref(r),
+                shape.batch if batch is None else batch, shape.seq if seq is None else seq)
+
+
 def debug_plan(n_layers, ckpt_interval, prefetch_depth, keep_internals=1, resident_layers=0):
     """The engine's schedule as (status, ops [n,3], loads [n,6], n_slots)."""
     import numpy as np
@@ -337,6 +354,18 @@ class Model:
         except Exception:
             pass
 
+    def set_schedule(self, **run_kw):
+        """Change schedule knobs between steps (mt_model_set_schedule); the
+        knobs not named keep their current values."""
+        r = RunCfg()
+        C.memmove(C.byref(r), C.byref(self.rcfg), C.sizeof(RunCfg))
+        for k, v in run_kw.items():
+            if not hasattr(r, k):
+                raise AttributeError(k)
+            setattr(r, k, v)
+        check(call("mt_model_set_schedule", self.h, C.byref(r)), "mt_model_set_schedule")
+        self.rcfg = r
+
     def set_param(self, name, arr):
         import numpy as np
         a = np.ascontiguousarray(arr, dtype=np.float32).reshape(-1)
@@ -355,6 +384,17 @@ class Model:
         check(call("mt_model_get_param", self.h, name.encode(), which, ptr(out), out.size),
               f"mt_model_get_param({name})")
         return out.reshape(shp)
+
+    def kernel_times(self):
+        """The last step's timed launches per kernel (time_kernels=1), largest
+        total time first: [{name, launches, ms, flops}]."""
+        n = C.c_int32()
+        check(call("mt_model_kernel_times", self.h, None, 0, C.byref(n)), "mt_model_kernel_times")
+        arr = (KernelTime * max(n.value, 1))()
+        check(call("mt_model_kernel_times", self.h, arr, n.value, C.byref(n)),
+              "mt_model_kernel_times")
+        return [{"name": k.name.decode(), "launches": int(k.launches), "ms": float(k.ms),
+                 "flops": float(k.flops)} for k in arr[: n.value]]
 
     @property
     def step_count(self):

@@ -161,6 +161,65 @@ def causal_attention_backward(q, k, v, o, lse, do, row_block=None):
     return dq, dk, dv
 
 
+def causal_attention_rows(q_rows, rows, k, v):
+    """causal_attention at the query positions ``rows`` only.
+
+    q_rows [B, n, Hq, d] are the queries at positions rows[0..n) (ints,
+    each in [0, T)); k, v [B, T, Hkv, d].  Query position t attends to keys
+    0..t with the exact softmax, as in causal_attention; the result is that
+    function's o and lse at those positions: o [B, n, Hq, d], lse [B, Hq, n].
+    """
+    B, n, Hq, d = q_rows.shape
+    Hkv = k.shape[2]
+    rows = np.asarray(rows)
+    scale = q_rows.dtype.type(1.0 / math.sqrt(d))
+    r1 = int(rows.max()) + 1
+    o = np.empty_like(q_rows)
+    lse = np.empty((B, Hq, n), dtype=q_rows.dtype)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            s = (q_rows[b, :, h, :] @ k[b, :r1, g, :].T) * scale
+            s = np.where(np.arange(r1)[None, :] <= rows[:, None], s, -np.inf)
+            mx = np.max(s, axis=-1, keepdims=True)
+            p = np.exp(s - mx)
+            den = np.sum(p, axis=-1, keepdims=True)
+            o[b, :, h, :] = (p / den) @ v[b, :r1, g, :]
+            lse[b, h, :] = (mx + np.log(den))[:, 0]
+    return o, lse
+
+
+def causal_attention_backward_rows(q_rows, rows, k, v, o_rows, lse_rows, do_rows):
+    """causal_attention_backward restricted to the query positions ``rows``
+    (layouts as in causal_attention_rows; o_rows, lse_rows, do_rows at those
+    positions).  Returns dq at those positions and the part of dk, dv
+    [B, T, Hkv, d] that those queries contribute.  Key s receives
+    contributions only from queries t >= s, so when ``rows`` holds every
+    position from some r on, dk and dv are complete for the keys s >= r."""
+    B, n, Hq, d = q_rows.shape
+    T, Hkv = k.shape[1], k.shape[2]
+    rows = np.asarray(rows)
+    scale = q_rows.dtype.type(1.0 / math.sqrt(d))
+    r1 = int(rows.max()) + 1
+    dq = np.zeros_like(q_rows)
+    dk = np.zeros((B, T, Hkv, d), dtype=k.dtype)
+    dv = np.zeros((B, T, Hkv, d), dtype=v.dtype)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            kk, vv = k[b, :r1, g, :], v[b, :r1, g, :]
+            qq, dd = q_rows[b, :, h, :], do_rows[b, :, h, :]
+            s = (qq @ kk.T) * scale
+            mask = np.arange(r1)[None, :] <= rows[:, None]
+            p = np.where(mask, np.exp(s - lse_rows[b, h, :][:, None]), 0).astype(q_rows.dtype)
+            delta = np.sum(dd * o_rows[b, :, h, :], axis=-1, keepdims=True)
+            dv[b, :r1, g, :] += p.T @ dd
+            ds = p * (dd @ vv.T - delta)
+            dq[b, :, h, :] = (ds @ kk) * scale
+            dk[b, :r1, g, :] += (ds.T @ qq) * scale
+    return dq, dk, dv
+
+
 # --------------------------------------------------------------------------
 # SwiGLU
 # --------------------------------------------------------------------------

@@ -109,6 +109,19 @@ def test_layer_7b_shape_one_sequence():
         assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))
 
 
+@pytest.mark.parametrize("cfg", ["qwen2.5-14b-b8-t2048", "width2x-8l-b8-t1024"],
+                         ids=["14b-h5120-gqa5", "width2x-h7168-gqa7"])
+def test_layer_wide_shapes_one_sequence(cfg):
+    """One layer at the other workloads' widths against the oracle: the
+    14B shape (H 5120, 40/8 heads, F 13824) and the 2.0x width point
+    (H 7168, 56/8 heads, F 37888), on one sequence of 384 tokens."""
+    shape = synth.CONFIGS[cfg]
+    out = _layer_case(shape, 1, 384, seed=5)
+    for k, (gpu, ref) in out.items():
+        assert np.isfinite(gpu).all(), k
+        assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))
+
+
 def test_layer_7b_full_batch_one_sequence_checked():
     """One Qwen2.5-7B-shaped layer at the benchmark's launch configuration
     (B 16 x T 1024: the 256 x 256 GEMM tiles with split tail tiles, the

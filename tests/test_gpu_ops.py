@@ -132,16 +132,18 @@ def test_gemm_swiglu_forward_and_backward_epilogues(M, F, K):
     assert rel_fro(to_np(gu)[:, :F], gt) < 5e-3
     assert rel_fro(to_np(gu)[:, F:], ut) < 5e-3
     assert rel_fro(to_np(m), D.silu(gt) * ut) < 1e-2
-    # backward epilogue: dm = dy @ W_down (NN), fused into dgate/dup
+    # backward epilogue: dm = dy @ W_down (NN), fused into dgate/dup, with
+    # gate/up pre-activations of its own (seeded, not the product above)
     H = K
     dy = oracle.bf16_round(_rand(rng, (M, H)))
     wd = oracle.bf16_round(_rand(rng, (H, F), 0.1))
+    gu_in = oracle.bf16_round(_rand(rng, (M, 2 * F), 2.0))
     dgu = torch.zeros((M, 2 * F), device="cuda", dtype=torch.bfloat16)
     mt.gemm(1, 6, M, F, H, bf16_dev(dy), H, bf16_dev(wd), F, dgu, 2 * F, C2=dgu, ldc2=2 * F,
-            G=gu, ldg=2 * F, F=F)
+            G=bf16_dev(gu_in), ldg=2 * F, F=F)
     torch.cuda.synchronize()
-    g_bf = to_np(gu)[:, :F].astype(np.float64)
-    u_bf = to_np(gu)[:, F:].astype(np.float64)
+    g_bf = gu_in[:, :F].astype(np.float64)
+    u_bf = gu_in[:, F:].astype(np.float64)
     dm = dy.astype(np.float64) @ wd.astype(np.float64)
     sg = 1 / (1 + np.exp(-g_bf))
     assert rel_fro(to_np(dgu)[:, :F], dm * u_bf * sg * (1 + g_bf * (1 - sg))) < 1e-2
@@ -289,9 +291,8 @@ def test_attention_forward_backward(B, T, Hq, Hkv, d):
     DQKV = torch.full((B * T, (Hq + 2 * Hkv) * d), float("nan"), device="cuda", dtype=torch.bfloat16)
     mt.attn_bwd(QKV, O, LSE, DO, delta, DQKV, B, T, Hq, Hkv, d)
     torch.cuda.synchronize()
-    o_gpu = to_np(O).reshape(B, T, Hq, d)
-    dq, dk, dv = D.causal_attention_backward(q, k, v, o_gpu, LSE.cpu().numpy(),
-                                             do.reshape(B, T, Hq, d))
+    # the oracle's backward from its own forward (never from GPU outputs)
+    dq, dk, dv = D.causal_attention_backward(q, k, v, o_ref, lse_ref, do.reshape(B, T, Hq, d))
     out = to_np(DQKV)
     assert np.isfinite(out).all()
     # exact dq and dk vanish at T = 1 (P = 1, dS = 0): floor the denominator
@@ -437,12 +438,13 @@ def test_gemm_f32_swiglu_epilogues(M, F, K):
     H = K
     dy = _rand(rng, (M, H))
     wd = _rand(rng, (H, F), 0.2)
+    gu_in = _rand(rng, (M, 2 * F), 2.0)  # seeded gate/up pre-activations
     dgu = torch.zeros((M, 2 * F), device="cuda", dtype=torch.float32)
     mt.gemm_f32(1, 6, M, F, H, f32_dev(dy), H, f32_dev(wd), F, dgu, 2 * F, C2=dgu, ldc2=2 * F,
-                G=gu, ldg=2 * F, F=F)
+                G=f32_dev(gu_in), ldg=2 * F, F=F)
     torch.cuda.synchronize()
-    g64 = gu.cpu().numpy()[:, :F].astype(np.float64)
-    u64 = gu.cpu().numpy()[:, F:].astype(np.float64)
+    g64 = gu_in[:, :F].astype(np.float64)
+    u64 = gu_in[:, F:].astype(np.float64)
     dm = dy.astype(np.float64) @ wd.astype(np.float64)
     sg = 1 / (1 + np.exp(-g64))
     assert rel_fro(dgu.cpu().numpy()[:, :F], dm * u64 * sg * (1 + g64 * (1 - sg))) < F32_TOL

@@ -134,3 +134,47 @@ def test_workspace_grows_with_fp32_and_rejects_unknown_precision():
     f = mt.layer_workspace_bytes(mc, mt.run_cfg(precision=1), 2, 128, 1)
     assert 0 < b < f
     assert mt.layer_workspace_bytes(mc, mt.run_cfg(precision=2), 2, 128, 1) == 0
+
+
+def test_arena_query_without_model_matches_model_and_depth_study():
+    """The model-free arena query equals the model's own (pageable host
+    store, no GPU), for several schedules; over the depth study's layer
+    counts (listing page, Table 5) the arena grows only by the checkpoint
+    slots (one activation per K layers), not by any per-layer weight or
+    gradient storage."""
+    import synth
+    mt = _mt()
+    s = synth.CONFIGS["tiny-2l-h256"].with_(n_layers=5, ckpt_interval=2)
+    for kw in (dict(), dict(keep_internals=0), dict(resident_layers=2), dict(prefetch_depth=3),
+               dict(precision=1), dict(mlp_chunk_tokens=64, head_chunk_tokens=100)):
+        m = mt.Model(s, host_alloc=mt.HOST_PAGEABLE, **kw)
+        assert m.arena_bytes(2, 128) == mt.arena_bytes_for(s, 2, 128, **kw) > 0, kw
+        m.close()
+    q7 = synth.CONFIGS["qwen2.5-7b-b16-t1024"]
+    act = q7.tokens * q7.hidden * 2
+    base = mt.arena_bytes_for(q7)
+    for L in (42, 56, 84, 132, 180):
+        got = mt.arena_bytes_for(q7.with_(n_layers=L))
+        slots = (L // q7.ckpt_interval) - (q7.n_layers // q7.ckpt_interval)
+        assert got - base == slots * act, (L, got - base, slots * act)
+    assert mt.arena_bytes_for(q7, prefetch_depth=4) == 0
+
+
+def test_set_schedule_validates_and_keeps_fixed_knobs():
+    import synth
+    mt = _mt()
+    s = synth.CONFIGS["tiny-2l-h256"].with_(n_layers=5, ckpt_interval=2)
+    m = mt.Model(s, host_alloc=mt.HOST_PAGEABLE)
+    a0 = m.arena_bytes(2, 128)
+    m.set_schedule(keep_internals=0, ckpt_interval=1, resident_layers=2, prefetch_depth=3)
+    assert m.arena_bytes(2, 128) == mt.arena_bytes_for(
+        s, 2, 128, keep_internals=0, ckpt_interval=1, resident_layers=2, prefetch_depth=3) != a0
+    for bad in (dict(precision=1), dict(host_threads=3), dict(prefetch_depth=0),
+                dict(resident_layers=6), dict(n_slabs=3)):
+        with pytest.raises(mt.MTError) as e:
+            m.set_schedule(**bad)
+        assert e.value.status == mt.MT_E_INVALID, bad
+    m.set_schedule(use_slab_pool=0)
+    with pytest.raises(mt.MTError):
+        m.set_schedule(use_slab_pool=1)
+    m.close()

@@ -192,6 +192,39 @@ def test_attention_matches_sdpa_and_autograd(Hq, Hkv):
         np.testing.assert_allclose(mine, ref.numpy(), rtol=1e-10, atol=1e-11)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (7, 1)])
+def test_attention_rows_match_sdpa_autograd_at_those_rows(Hq, Hkv):
+    """The row-restricted forms (used where the full attention is too large
+    for the CPU) against torch SDPA and its autograd: o, lse and dq at the
+    chosen query rows, and dk, dv of every key at or after the first of a
+    run of rows that reaches the last position (later keys see no other
+    queries)."""
+    import torch
+    B, T, d = 2, 23, 8
+    q, k, v = _rand_qkv(B, T, Hq, Hkv, d, 7)
+    rep = Hq // Hkv
+    tq, tk, tv = (torch.tensor(z, requires_grad=True) for z in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq.transpose(1, 2), tk.transpose(1, 2).repeat_interleave(rep, 1),
+        tv.transpose(1, 2).repeat_interleave(rep, 1), is_causal=True).transpose(1, 2)
+    do = np.random.default_rng(8).standard_normal(q.shape)
+    (to * torch.tensor(do)).sum().backward()
+    s = torch.einsum("bthd,bshd->bhts", tq, tk.repeat_interleave(rep, 2)) / math.sqrt(d)
+    mask = torch.ones(T, T, dtype=torch.bool).tril()
+    tl = torch.logsumexp(s.masked_fill(~mask, -float("inf")), dim=-1).detach().numpy()
+    # scattered rows (forward, dq) and a suffix of rows (dk, dv)
+    for rows in (np.array([0, 3, 11, 22]), np.arange(15, T)):
+        o, lse = D.causal_attention_rows(q[:, rows], rows, k, v)
+        np.testing.assert_allclose(o, to.detach().numpy()[:, rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, tl[:, :, rows], rtol=1e-12, atol=1e-12)
+        dq, dk, dv = D.causal_attention_backward_rows(q[:, rows], rows, k, v, o, lse, do[:, rows])
+        np.testing.assert_allclose(dq, tq.grad.numpy()[:, rows], rtol=1e-10, atol=1e-11)
+        if rows[-1] == T - 1 and np.all(np.diff(rows) == 1):
+            r = rows[0]
+            np.testing.assert_allclose(dk[:, r:], tk.grad.numpy()[:, r:], rtol=1e-10, atol=1e-11)
+            np.testing.assert_allclose(dv[:, r:], tv.grad.numpy()[:, r:], rtol=1e-10, atol=1e-11)
+
+
 # ----------------------------------------------------------------------- RoPE
 
 
