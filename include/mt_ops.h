@@ -92,6 +92,24 @@ mt_status mt_op_attn_bwd(const void* qkv, const void* o, const float* lse, const
                          float* delta, void* dqkv, int32_t batch, int32_t seq, int32_t n_heads,
                          int32_t n_kv_heads, int32_t head_dim, void* stream);
 
+/* mt_op_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results (the same kernels), with the delta rows
+ * in a static device array of the library instead of a caller workspace.
+ * It allocates nothing; the array (MT_ATTN_NOALLOC_MAX_ROWS floats, 64 MiB)
+ * exists once per GPU the library runs on and is held until the process
+ * ends; its address is looked up on the first call on each device.
+ * batch * n_heads * seq above MT_ATTN_NOALLOC_MAX_ROWS returns MT_E_SHAPE
+ * (7B heads: up to 524288 tokens).  Every call on one GPU uses that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be ordered by the caller.  Nothing needs clearing between calls
+ * (each call writes every delta row it reads). */
+#define MT_ATTN_NOALLOC_MAX_ROWS ((size_t)16 << 20)
+mt_status mt_op_attn_bwd_noalloc(const void* qkv, const void* o, const float* lse,
+                                 const void* dout, void* dqkv, int32_t batch, int32_t seq,
+                                 int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 void* stream);
+
 /* Attention forward and backward in the fp32 debug precision: the same
  * contract with fp32 qkv, o, dout and dqkv (exact softmax per row, fp32
  * FMA; written for exactness, not speed). */

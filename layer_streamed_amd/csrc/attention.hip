@@ -26,12 +26,20 @@
 // transposed operands with LDS transpose reads (attn_fwd_dl_kernel,
 // attn_dkdv_dl_kernel, attn_dq_dl_kernel); the register-staged forms serve
 // head_dim 64.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace mt {
+
+// Scratch of the allocation-free attention backward (attn_bwd_static): the
+// delta rows, B*Hq*T floats, in a static device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code never uses the array's name as an address: the
+// per-device address comes from hipGetSymbolAddress (static_scratch).
+static __device__ __align__(256) float scratch[ATTN_STATIC_SCRATCH_FLOATS];
 
 namespace {
 
@@ -1322,6 +1330,41 @@ hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
   if (head_dim == 128) return bwd_d<128>(a, stages, s);
   if (head_dim == 64) return bwd_d<64>(a, stages, s);
   return hipErrorInvalidValue;
+}
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+float* scratch_dev[MAX_DEVICES] = {};  // scratch's address on each device
+}  // namespace
+
+// The address of `scratch` on the current device, resolved once per device
+// with that device current.
+static hipError_t static_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t attn_bwd_static(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                           const uint16_t* dout, uint16_t* dqkv, int batch, int seq, int n_heads,
+                           int n_kv_heads, int head_dim, hipStream_t s) {
+  if ((size_t)batch * n_heads * seq > ATTN_STATIC_SCRATCH_FLOATS) return hipErrorInvalidValue;
+  float* delta = nullptr;
+  const hipError_t e = static_scratch(&delta);
+  if (e != hipSuccess) return e;
+  return attn_bwd(qkv, o, lse, dout, delta, dqkv, batch, seq, n_heads, n_kv_heads, head_dim, s);
 }
 
 const char* attn_kernel_name(int head_dim, int which) {

@@ -153,6 +153,27 @@ mt_status mt_op_attn_bwd(const void* qkv, const void* o, const float* lse, const
   return MT_OK;
 }
 
+static_assert(MT_ATTN_NOALLOC_MAX_ROWS == ATTN_STATIC_SCRATCH_FLOATS,
+              "the header's limit is the static array's size");
+
+mt_status mt_op_attn_bwd_noalloc(const void* qkv, const void* o, const float* lse,
+                                 const void* dout, void* dqkv, int32_t batch, int32_t seq,
+                                 int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 void* stream) {
+  MT_CHECK(qkv && o && lse && dout && dqkv, MT_E_INVALID, "mt_op_attn_bwd_noalloc: null pointer");
+  if (const char* m = attn_shape_check(batch, seq, n_heads, n_kv_heads, head_dim))
+    return set_error(MT_E_SHAPE, "mt_op_attn_bwd_noalloc: %s", m);
+  const size_t need = (size_t)batch * n_heads * seq;
+  MT_CHECK(need <= MT_ATTN_NOALLOC_MAX_ROWS, MT_E_SHAPE,
+           "mt_op_attn_bwd_noalloc: batch * n_heads * seq = %zu exceeds the static scratch of "
+           "%zu rows (use mt_op_attn_bwd with a workspace)",
+           need, (size_t)MT_ATTN_NOALLOC_MAX_ROWS);
+  MT_HIP(attn_bwd_static(static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(o), lse,
+                         static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dqkv), batch,
+                         seq, n_heads, n_kv_heads, head_dim, static_cast<hipStream_t>(stream)));
+  return MT_OK;
+}
+
 mt_status mt_op_attn_fwd_f32(const float* qkv, float* o, float* lse, int32_t batch, int32_t seq,
                              int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream) {
   MT_CHECK(qkv && o && lse, MT_E_INVALID, "mt_op_attn_fwd_f32: null pointer");

@@ -123,6 +123,14 @@ hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
                     const uint16_t* dout, float* delta, uint16_t* dqkv, int batch, int seq,
                     int n_heads, int n_kv_heads, int head_dim, hipStream_t s,
                     int stages = ATTN_BWD_ALL);
+// attn_bwd with its delta rows in a static device array of the library
+// (ATTN_STATIC_SCRATCH_FLOATS floats per GPU) instead of a caller
+// workspace; allocates nothing.  batch * n_heads * seq must not exceed
+// that size (hipErrorInvalidValue).  Calls on one GPU share the array.
+constexpr size_t ATTN_STATIC_SCRATCH_FLOATS = (size_t)16 << 20;
+hipError_t attn_bwd_static(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                           const uint16_t* dout, uint16_t* dqkv, int batch, int seq, int n_heads,
+                           int n_kv_heads, int head_dim, hipStream_t s);
 // Name of the kernel behind attn_fwd (which 0) and the three backward
 // stages (1 delta, 2 dK/dV, 3 dQ) for a head dimension, as profilers print it.
 const char* attn_kernel_name(int head_dim, int which);

@@ -113,6 +113,7 @@ _SIGS = {
     "mt_op_rope": (_I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _P),
     "mt_op_attn_fwd": (_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
     "mt_op_attn_bwd": (_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
+    "mt_op_attn_bwd_noalloc": (_I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P),
     "mt_op_ce_rows": (_I32, _P, _P, _P, _P, _I32, _I32, _F, _P),
     "mt_layer_workspace_bytes": (_SZ, _P, _P, _I32, _I32, _I32),
     "mt_layer_fwd": (_I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P),
@@ -246,6 +247,17 @@ def attn_bwd(qkv, o, lse, dout, delta, dqkv, batch, seq, n_heads, n_kv_heads, he
              stream=None):
     check(call("mt_op_attn_bwd", ptr(qkv), ptr(o), ptr(lse), ptr(dout), ptr(delta), ptr(dqkv),
                batch, seq, n_heads, n_kv_heads, head_dim, stream_handle(stream)), "mt_op_attn_bwd")
+
+
+ATTN_NOALLOC_MAX_ROWS = 16 << 20  # MT_ATTN_NOALLOC_MAX_ROWS
+
+
+def attn_bwd_noalloc(qkv, o, lse, dout, dqkv, batch, seq, n_heads, n_kv_heads, head_dim,
+                     stream=None):
+    """Attention backward with the library's static scratch (no workspace)."""
+    check(call("mt_op_attn_bwd_noalloc", ptr(qkv), ptr(o), ptr(lse), ptr(dout), ptr(dqkv),
+               batch, seq, n_heads, n_kv_heads, head_dim, stream_handle(stream)),
+          "mt_op_attn_bwd_noalloc")
 
 
 def attn_fwd_f32(qkv, o, lse, batch, seq, n_heads, n_kv_heads, head_dim, stream=None):
