@@ -223,6 +223,9 @@ def main():
     ap.add_argument("--prefetch-depth", type=int, default=3)
     ap.add_argument("--no-slab-pool", action="store_true")
     ap.add_argument("--ckpt-interval", type=int, default=0)
+    # depth study (listing page, Table 5): the workload's width at another
+    # number of layers
+    ap.add_argument("--layers", type=int, default=0)
     # layers whose weights stay on the device between steps (refilled after
     # each update, during the backward): the forward streams that many fewer.
     # Default (-1): 8, at most a third of the layers.  At the 7B workload 20
@@ -256,10 +259,13 @@ def main():
     shape = synth.CONFIGS[args.config]
     if args.ckpt_interval:
         shape = shape.with_(ckpt_interval=args.ckpt_interval)
+    if args.layers:
+        shape = shape.with_(n_layers=args.layers, name=f"{shape.name}-l{args.layers}")
     resident = (min(8, shape.n_layers // 3) if args.resident_layers < 0
                 else min(args.resident_layers, shape.n_layers))
     keep = args.keep_internals
     torch.cuda.set_device(0)
+    dev_free0, dev_total = torch.cuda.mem_get_info()
     t0 = time.perf_counter()
     model = mt.Model(shape, prefetch_depth=args.prefetch_depth,
                      use_slab_pool=0 if args.no_slab_pool else 1, check_finite=1,
@@ -293,6 +299,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = 1e3 * elapsed / args.steps
+    # device memory the process holds beyond what it held before the model
+    # existed: the arena plus the library's own (events, static scratch)
+    dev_used = dev_free0 - torch.cuda.mem_get_info()[0]
     log(f"dominant kernel per step: {[s['probe_kernel'] for s in stats]}")
     del arena
     torch.cuda.empty_cache()
@@ -409,8 +418,13 @@ def main():
     # 1 GiB pinned <-> device copies each way (not under --pmc-copy, whose
     # counter passes calibrate on the device copy alone)
     link_peak = {}
+    hbuf = None
     if not args.pmc_copy:
-        hbuf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        try:
+            hbuf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        except RuntimeError as e:  # the wide models pin most of what the host allows
+            log(f"link copy rate not measured: pinning 1 GiB failed ({e})")
+    if hbuf is not None:
         dbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         for name, dst, src in (("h2d", dbuf, hbuf), ("d2h", hbuf, dbuf)):
             dst.copy_(src, non_blocking=True)
@@ -502,6 +516,7 @@ def main():
         "host_bytes": {"pinned": stats[-1]["pinned_host_bytes"],
                        "pageable": stats[-1]["pageable_host_bytes"]},
         "device_arena_bytes": stats[-1]["device_arena_bytes"],
+        "device_used_bytes": int(dev_used),
         "loss": losses[-1],
         "gemm_ms_per_step": round(gemm_ms, 2),
         "attn_ms_per_step": round(attn_ms, 2),

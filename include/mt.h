@@ -260,7 +260,8 @@ void mt_model_destroy(mt_model* model);
 
 /* Changes the schedule knobs of a model between steps (the ablation of the
  * listing page's Table 4 runs one model under several schedules):
- * checkpoint interval, prefetch depth, slab pool on -> off, MLP and head
+ * checkpoint interval, prefetch depth, slab pool off (and on again, when
+ * the model was created with it), MLP and head
  * chunks, keep_internals, defer_updates, resident_layers, serialize,
  * check_finite, time_kernels and the Adam hyperparameters.  precision,
  * host_alloc, keep_grads, host_threads and the slab pool's size are fixed
@@ -336,6 +337,28 @@ mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq,
                        const void* grad, int32_t grad_dtype,
                        uint16_t* bf16_shadow, size_t n, int64_t step,
                        const mt_run_cfg* hp);
+
+/* Hybrid 8-bit Adam with gradient clipping (LazyTrain abstract, on the
+ * listing pages: 8-bit optimizer states coupled with fast gradient
+ * clipping in one operator).  The same update as mt_host_adam, with these
+ * readings (the page gives no format): each moment is kept in blocks of
+ * 128 consecutive elements (the last block may be shorter) as OCP FP8 E4M3
+ * codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest 448)
+ * with one fp32 scale per block: scale = absmax / 448, code = E4M3(x /
+ * scale) rounded to nearest even, value = E4M3value(code) * scale; the
+ * first moment is stored as m, the second as r = sqrt(v).  The update
+ * dequantizes m and v = r * r, multiplies the gradient by `clip` (the
+ * caller's global-norm clipping factor min(1, max_norm / (norm + 1e-6)),
+ * in (0, 1]; 1 = no clipping), applies Adam in fp32 exactly as
+ * mt_host_adam, writes param (and bf16_shadow, nullable), then quantizes
+ * the new m and r.  Arrays: param [n]; m_code, r_code [n] bytes; m_scale,
+ * r_scale [ceil(n / 128)] floats; all zero for a fresh state.  grad as in
+ * mt_host_adam.  With hp->check_finite a non-finite gradient returns
+ * MT_E_NONFINITE and leaves every array unchanged. */
+mt_status mt_host_adam8(float* param, uint8_t* m_code, float* m_scale, uint8_t* r_code,
+                        float* r_scale, const void* grad, int32_t grad_dtype,
+                        uint16_t* bf16_shadow, size_t n, int64_t step, float clip,
+                        const mt_run_cfg* hp);
 
 /* Defaults for every knob (ckpt 4, depth 2, pool of 8, lr 1e-4, betas
  * 0.9/0.999, eps 1e-8, bf16, 16 host threads, pinned host memory). */

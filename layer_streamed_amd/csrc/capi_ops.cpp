@@ -88,8 +88,9 @@ mt_status mt_op_rmsnorm_bwd(const void* dy, const void* x, const void* g, const 
                             const void* resid, void* dx, void* dg, int32_t rows, int32_t cols,
                             void* workspace, size_t workspace_bytes, void* stream) {
   MT_CHECK(dy && x && g && rstd && dx && dg, MT_E_INVALID, "mt_op_rmsnorm_bwd: null pointer");
-  MT_CHECK(rows >= 0 && cols > 0 && cols % 8 == 0 && cols <= 8192, MT_E_SHAPE,
-           "mt_op_rmsnorm_bwd: cols must be a positive multiple of 8, at most 8192");
+  MT_CHECK(rows >= 0 && cols > 0 && cols % 8 == 0 && cols <= RMSNORM_MAX_COLS, MT_E_SHAPE,
+           "mt_op_rmsnorm_bwd: cols must be a positive multiple of 8, at most %d",
+           RMSNORM_MAX_COLS);
   MT_CHECK(workspace_bytes >= mt_op_rmsnorm_bwd_workspace(rows, cols) && (rows == 0 || workspace),
            MT_E_OOM_DEVICE, "mt_op_rmsnorm_bwd: workspace too small");
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -170,6 +170,96 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
   }
 }
 
+// The same backward for rows wider than the register-held form allows (the
+// pages' widest layers, hidden up to 16384): first each wave walks its rows
+// computing the row's dot product and dx (two passes over the row), then
+// the workgroup walks the columns in slabs of WIDE_SLAB, summing dy * xh
+// over its rows per wave in row order (the rows are re-read, mostly from
+// L2) and combining the 4 waves in the same fixed order as above.
+constexpr int WIDE_SLAB = 4096;
+
+template <class E>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_wide_kernel(
+    const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ g,
+    const float* __restrict__ rstd, const E* __restrict__ resid, E* __restrict__ dx,
+    float* __restrict__ dg_part, int rows, int cols) {
+  extern __shared__ float red[];  // [4][WIDE_SLAB]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = cols / 8;
+  const int r0 = blockIdx.x * RB_ROWS;
+  const float inv_cols = 1.f / (float)cols;
+  for (int rr = wave; rr < RB_ROWS; rr += 4) {
+    const int row = r0 + rr;
+    if (row >= rows) break;
+    const long off = (long)row * cols;
+    const float r = rstd[row];
+    float dot = 0.f;
+    for (int c = lane; c < nch; c += 64) {
+      float fd[8], fx[8], fg[8];
+      St<E>::load8(dy + off + c * 8, fd);
+      St<E>::load8(x + off + c * 8, fx);
+      St<E>::load8(g + c * 8, fg);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot += fd[i] * fg[i] * (fx[i] * r);
+    }
+    dot = wave_sum(dot) * inv_cols;
+    for (int c = lane; c < nch; c += 64) {
+      float fd[8], fx[8], fg[8], fr[8];
+      St<E>::load8(dy + off + c * 8, fd);
+      St<E>::load8(x + off + c * 8, fx);
+      St<E>::load8(g + c * 8, fg);
+      if (resid) St<E>::load8(resid + off + c * 8, fr);
+      else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fr[i] = 0.f;
+      }
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = fr[i] + r * (fd[i] * fg[i] - (fx[i] * r) * dot);
+      St<E>::store8(dx + off + c * 8, o);
+    }
+  }
+  constexpr int SCH = WIDE_SLAB / 8, PER = SCH / 64;  // chunks per slab, per lane
+  for (int s0 = 0; s0 < nch; s0 += SCH) {
+    float acc[PER][8];
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[k][i] = 0.f;
+    for (int rr = wave; rr < RB_ROWS; rr += 4) {
+      const int row = r0 + rr;
+      if (row >= rows) break;
+      const long off = (long)row * cols;
+      const float r = rstd[row];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int c = s0 + lane + 64 * k;
+        if (c < nch) {
+          float fd[8], fx[8];
+          St<E>::load8(dy + off + c * 8, fd);
+          St<E>::load8(x + off + c * 8, fx);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[k][i] += fd[i] * (fx[i] * r);
+        }
+      }
+    }
+    __syncthreads();  // the previous slab's combine has read red
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int c = lane + 64 * k;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wave * WIDE_SLAB + c * 8 + i] = acc[k][i];
+    }
+    __syncthreads();
+    const int ncol = min(WIDE_SLAB, cols - s0 * 8);
+    for (int col = threadIdx.x; col < ncol; col += 256) {
+      const float s = ((red[col] + red[WIDE_SLAB + col]) + red[2 * WIDE_SLAB + col]) +
+                      red[3 * WIDE_SLAB + col];
+      dg_part[(long)blockIdx.x * cols + s0 * 8 + col] = s;
+    }
+  }
+}
+
 // out[col] = sum over the nblk partial rows.  A workgroup covers 64
 // columns with 4 row groups (rows b = 4 i + q); each thread keeps 8 running
 // sums (over i mod 8) so its loads stay independent; the sums are combined
@@ -404,7 +494,18 @@ hipError_t rmsnorm_bwd_t(const E* dy, const E* x, const E* g, const float* rstd,
   }
   MT_RB(1) MT_RB(2) MT_RB(4) MT_RB(8) MT_RB(16)
 #undef MT_RB
-  return hipErrorInvalidValue;
+  if (cols > RMSNORM_MAX_COLS) return hipErrorInvalidValue;
+  static bool attr = false;
+  constexpr int lds_w = 4 * WIDE_SLAB * (int)sizeof(float);
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rmsnorm_bwd_wide_kernel<E>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_w);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(rmsnorm_bwd_wide_kernel<E>, grid, block, lds_w, s, dy, x, g, rstd, resid, dx,
+                     dg_part, rows, cols);
+  return hipGetLastError();
 }
 
 template <class E>

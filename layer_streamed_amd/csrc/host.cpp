@@ -311,6 +311,52 @@ void mt_run_cfg_default(mt_run_cfg* r) {
   r->weight_decay = 0.0;
 }
 
+// The worker pool of the standalone optimizer calls (resized on demand).
+static ThreadPool* standalone_pool(int threads, std::unique_lock<std::mutex>* lk) {
+  static ThreadPool* pool = nullptr;
+  static int pool_threads = 0;
+  static std::mutex pool_mu;
+  *lk = std::unique_lock<std::mutex>(pool_mu);
+  const int want = threads > 0 ? threads : 1;
+  if (!pool || pool_threads != want) {
+    delete pool;
+    pool = new ThreadPool(want);
+    pool_threads = want;
+  }
+  return pool;
+}
+
+static mt_status check_hp(const mt_run_cfg* hp, int64_t step, const char* fn) {
+  MT_CHECK(hp, MT_E_INVALID, "%s: null hyperparameters", fn);
+  MT_CHECK(step >= 1, MT_E_INVALID, "%s: step must be >= 1", fn);
+  MT_CHECK(hp->weight_decay == 0.0, MT_E_INVALID, "%s: weight decay is not supported", fn);
+  MT_CHECK(hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && hp->eps >= 0,
+           MT_E_INVALID, "%s: betas must be in [0, 1), eps >= 0", fn);
+  return MT_OK;
+}
+
+mt_status mt_host_adam8(float* param, uint8_t* m_code, float* m_scale, uint8_t* r_code,
+                        float* r_scale, const void* grad, int32_t grad_dtype,
+                        uint16_t* bf16_shadow, size_t n, int64_t step, float clip,
+                        const mt_run_cfg* hp) {
+  if (mt_status st = check_hp(hp, step, "mt_host_adam8"); st != MT_OK) return st;
+  MT_CHECK(n == 0 || (param && m_code && m_scale && r_code && r_scale && grad), MT_E_INVALID,
+           "mt_host_adam8: null array");
+  MT_CHECK(grad_dtype == MT_DT_BF16 || grad_dtype == MT_DT_F32, MT_E_INVALID,
+           "mt_host_adam8: grad_dtype must be MT_DT_BF16 or MT_DT_F32");
+  MT_CHECK(clip > 0.f && clip <= 1.f, MT_E_INVALID, "mt_host_adam8: clip must be in (0, 1]");
+  const uint16_t* gb = grad_dtype == MT_DT_BF16 ? static_cast<const uint16_t*>(grad) : nullptr;
+  const float* gf = grad_dtype == MT_DT_F32 ? static_cast<const float*>(grad) : nullptr;
+  std::unique_lock<std::mutex> lk;
+  ThreadPool* pool = standalone_pool(hp->host_threads, &lk);
+  if (hp->check_finite && !grad_finite(gb, gf, n, pool))
+    return set_error(MT_E_NONFINITE, "mt_host_adam8: gradient has NaN or Inf; nothing updated");
+  const Adam8Arrays a{param, m_code, r_code, m_scale, r_scale, gb, gf, bf16_shadow, nullptr};
+  const Adam8Seg seg{0, n, 0};
+  adam8_parallel(a, &seg, 1, adam_hp(*hp, step), clip, pool);
+  return MT_OK;
+}
+
 mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq, const void* grad,
                        int32_t grad_dtype, uint16_t* bf16_shadow, size_t n, int64_t step,
                        const mt_run_cfg* hp) {
@@ -325,16 +371,8 @@ mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq, const vo
            MT_E_INVALID, "mt_host_adam: betas must be in [0, 1), eps >= 0");
   const uint16_t* gb = grad_dtype == MT_DT_BF16 ? static_cast<const uint16_t*>(grad) : nullptr;
   const float* gf = grad_dtype == MT_DT_F32 ? static_cast<const float*>(grad) : nullptr;
-  static ThreadPool* pool = nullptr;
-  static int pool_threads = 0;
-  static std::mutex pool_mu;
-  std::lock_guard<std::mutex> lk(pool_mu);
-  const int want = hp->host_threads > 0 ? hp->host_threads : 1;
-  if (!pool || pool_threads != want) {
-    delete pool;
-    pool = new ThreadPool(want);
-    pool_threads = want;
-  }
+  std::unique_lock<std::mutex> lk;
+  ThreadPool* pool = standalone_pool(hp->host_threads, &lk);
   if (hp->check_finite && !grad_finite(gb, gf, n, pool))
     return set_error(MT_E_NONFINITE, "mt_host_adam: gradient has NaN or Inf; nothing updated");
   adam_parallel(param, exp_avg, exp_avg_sq, gb, gf, bf16_shadow, nullptr, n, adam_hp(*hp, step),

@@ -65,6 +65,38 @@ inline float host_bf2f(uint16_t b) {
   return f;
 }
 
+// ---- hybrid 8-bit Adam (host_adam8.cpp)
+// Moments per tensor in blocks of ADAM8_BLOCK elements as OCP FP8 E4M3
+// codes with one fp32 scale per block; m as is, v as r = sqrt(v).
+constexpr int ADAM8_BLOCK = 128;
+inline size_t adam8_blocks(size_t n) { return (n + ADAM8_BLOCK - 1) / ADAM8_BLOCK; }
+// A tensor inside a unit's flat arrays: elements [off, off + n); its
+// blocks' scales start at index sblk of the scale arrays.
+struct Adam8Seg {
+  size_t off, n, sblk;
+};
+struct Adam8Arrays {
+  float* p;              // fp32 master
+  uint8_t *mq, *rq;      // codes of m and of r = sqrt(v)
+  float *ms, *rs;        // per-block scales
+  const uint16_t* gb;    // gradient: bf16 ...
+  const float* gf;       // ... or fp32 (one of the two)
+  uint16_t* sb;          // streamed copy written from the new master: bf16,
+  float* sf;             // fp32, or neither
+};
+uint8_t e4m3_encode(float y);  // round to nearest even, saturating at 448
+float e4m3_decode(uint8_t c);
+size_t adam8_segment_blocks(const Adam8Seg* segs, int nseg);
+// Update blocks [blo, bhi) of the segments (numbered across segments in
+// order); the gradient is multiplied by `clip` first.
+void adam8_range(const Adam8Arrays& a, const Adam8Seg* segs, int nseg, size_t blo, size_t bhi,
+                 const AdamHp& h, float clip);
+void adam8_parallel(const Adam8Arrays& a, const Adam8Seg* segs, int nseg, const AdamHp& h,
+                    float clip, ThreadPool* pool);
+// Values of one segment's moment (square = true: r -> v = r * r) into out[n].
+void adam8_dequant(const uint8_t* q, const float* scales, const Adam8Seg& seg, bool square,
+                   float* out);
+
 // x0[t] = table[ids[t]] (rows of row_bytes bytes: H bf16 or H fp32 values).
 void embed_gather(const void* table, const int32_t* ids, size_t n_tok, size_t row_bytes,
                   void* out, ThreadPool* pool);

@@ -75,6 +75,8 @@ hipError_t rmsnorm_fwd(const float* x, const float* g, float* y, float* rstd, in
 // be null).  Writes per-block partial gain gradients dg_part [nblk, cols]
 // fp32; nblk = rmsnorm_bwd_blocks(rows).
 int rmsnorm_bwd_blocks(int rows);
+// Widest row the RMSNorm backward takes (the hidden size limit).
+constexpr int RMSNORM_MAX_COLS = 16384;
 hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* g,
                        const float* rstd, const uint16_t* resid, uint16_t* dx,
                        float* dg_part, int rows, int cols, hipStream_t s);

@@ -38,7 +38,7 @@ const char* make_dims(const mt_model_cfg* cfg, const mt_run_cfg* run, int batch,
       c.vocab < 64)
     return "model sizes must be positive (hidden, ffn, vocab >= 64)";
   if (c.hidden % 64 || c.ffn % 64 || c.vocab % 64) return "hidden, ffn and vocab must be multiples of 64";
-  if (c.hidden > 8192) return "hidden above 8192 is not supported";
+  if (c.hidden > RMSNORM_MAX_COLS) return "hidden above 16384 is not supported";
   if (c.n_heads % c.n_kv_heads) return "n_heads must be a multiple of n_kv_heads";
   if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
   if (!(c.rms_eps > 0) || !(c.rope_theta > 0)) return "rms_eps and rope_theta must be positive";

@@ -278,9 +278,10 @@ mt_status mt_model_set_schedule(mt_model* m, const mt_run_cfg* run) {
            MT_E_INVALID,
            "mt_model_set_schedule: precision, host_alloc, keep_grads and host_threads are fixed "
            "when the model is created");
-  MT_CHECK(!run->use_slab_pool || (o.use_slab_pool && run->n_slabs == o.n_slabs), MT_E_INVALID,
+  MT_CHECK(!run->use_slab_pool || (m->slab_list.size() > 0 && (size_t)run->n_slabs == m->slab_list.size()),
+           MT_E_INVALID,
            "mt_model_set_schedule: the slab pool (and its size) is allocated when the model is "
-           "created; it can only be switched off");
+           "created; a model created without it can not switch it on");
   flush_pending(m);  // the pending updates belong to the old schedule's step
   m->resident_valid.clear();  // resident slots are refilled under the new schedule
   m->run = *run;

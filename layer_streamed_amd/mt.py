@@ -129,6 +129,7 @@ _SIGS = {
     "mt_stream_arena_bytes_cfg": (_SZ, _P, _P, _I32, _I32),
     "mt_stream_step": (_I32, _P, _P, _I32, _I32, _P, _SZ, _P, _P, _P),
     "mt_host_adam": (_I32, _P, _P, _P, _P, _I32, _P, _SZ, _I64, _P),
+    "mt_host_adam8": (_I32, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _I64, _F, _P),
     "mt_run_cfg_default": (None, _P),
     "mt_op_rmsnorm_bwd_workspace": (_SZ, _I32, _I32),
     "mt_debug_plan": (_I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P),

@@ -106,7 +106,30 @@ CONFIGS: dict[str, ModelShape] = {
         name="qwen2.5-7b-b1-t524288", n_layers=28, hidden=3584, n_heads=28,
         n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064, batch=1,
         seq=524288, ckpt_interval=4, mlp_chunk_tokens=4096),
+    # The pages' larger dense shapes (Table 2: Qwen2.5-32B, H 5120 / F 27648,
+    # 64 layers; Qwen2.5-72B, H 8192 / F 29568, 80 layers) at their full
+    # width but a few layers (a host store of the whole depth would take
+    # 0.45-1.0 TB); head_dim 128, 8 KV heads as in those models.
+    "qwen2.5-32b-l8-b8-t1024": ModelShape(
+        name="qwen2.5-32b-l8-b8-t1024", n_layers=8, hidden=5120, n_heads=40,
+        n_kv_heads=8, head_dim=128, ffn=27648, vocab=152064, batch=8,
+        seq=1024, ckpt_interval=4),
+    "qwen2.5-72b-l4-b8-t1024": ModelShape(
+        name="qwen2.5-72b-l4-b8-t1024", n_layers=4, hidden=8192, n_heads=64,
+        n_kv_heads=8, head_dim=128, ffn=29568, vocab=152064, batch=8,
+        seq=1024, ckpt_interval=4),
 }
+
+# The width study (Table 6): the 7B-shaped layer scaled to 1.5x .. 3.5x
+# hidden and FFN size at head_dim 128 with GQA groups of 7 as in the 7B
+# shape, B 8 x T 1024.  A few layers each (the host store of 28 such
+# layers would take up to 1.1 TB); the 2.0x point is width2x-8l-b8-t1024.
+for _scale, _h, _f, _L in (("1.5x", 5376, 28416, 4), ("2.5x", 8960, 47360, 4),
+                           ("3.0x", 10752, 56832, 2), ("3.5x", 12544, 66304, 2)):
+    _name = f"width{_scale}-{_L}l-b8-t1024"
+    CONFIGS[_name] = ModelShape(
+        name=_name, n_layers=_L, hidden=_h, n_heads=_h // 128, n_kv_heads=_h // 128 // 7,
+        head_dim=128, ffn=_f, vocab=152064, batch=8, seq=1024, ckpt_interval=4)
 
 # Per-layer tensors in draw order; gains ("*_norm") are not drawn.
 _LAYER_TENSORS = ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm",

@@ -109,12 +109,17 @@ def test_layer_7b_shape_one_sequence():
         assert rel(gpu, ref) < TOL, (k, rel(gpu, ref))
 
 
-@pytest.mark.parametrize("cfg", ["qwen2.5-14b-b8-t2048", "width2x-8l-b8-t1024"],
-                         ids=["14b-h5120-gqa5", "width2x-h7168-gqa7"])
+@pytest.mark.parametrize("cfg", ["qwen2.5-14b-b8-t2048", "width2x-8l-b8-t1024",
+                                 "qwen2.5-72b-l4-b8-t1024", "width3.5x-2l-b8-t1024"],
+                         ids=["14b-h5120-gqa5", "width2x-h7168-gqa7", "72b-h8192-gqa8",
+                              "width3.5x-h12544-gqa7"])
 def test_layer_wide_shapes_one_sequence(cfg):
     """One layer at the other workloads' widths against the oracle: the
-    14B shape (H 5120, 40/8 heads, F 13824) and the 2.0x width point
-    (H 7168, 56/8 heads, F 37888), on one sequence of 384 tokens."""
+    14B shape (H 5120, 40/8 heads, F 13824), the 2.0x width point (H 7168,
+    56/8 heads, F 37888), the 72B shape (H 8192, 64/8 heads, F 29568) and
+    the widest point of the width study (H 12544, 98/14 heads, F 66304,
+    whose RMSNorm backward takes the wide-row kernel), on one sequence of
+    384 tokens."""
     shape = synth.CONFIGS[cfg]
     out = _layer_case(shape, 1, 384, seed=5)
     for k, (gpu, ref) in out.items():

@@ -171,7 +171,9 @@ def test_gemm_7b_gate_up_shape_sampled_rows():
     assert rel_fro(m[rows].float().cpu().numpy(), mref) < 1e-2
 
 
-@pytest.mark.parametrize("rows,cols", [(256, 256), (77, 3584), (130, 7168), (5, 8)])
+# rows wider than 8192 take the wide backward kernel (column slabs of 4096)
+@pytest.mark.parametrize("rows,cols", [(256, 256), (77, 3584), (130, 7168), (5, 8),
+                                       (33, 12544), (20, 16384), (19, 8200)])
 def test_rmsnorm_forward_backward(rows, cols):
     torch, mt = _torch(), _mt()
     rng = np.random.default_rng(rows + cols)

@@ -175,6 +175,9 @@ def test_set_schedule_validates_and_keeps_fixed_knobs():
             m.set_schedule(**bad)
         assert e.value.status == mt.MT_E_INVALID, bad
     m.set_schedule(use_slab_pool=0)
+    m.set_schedule(use_slab_pool=1)  # the pool allocated at creation
+    m.close()
+    m = mt.Model(s, host_alloc=mt.HOST_PAGEABLE, use_slab_pool=0)
     with pytest.raises(mt.MTError):
         m.set_schedule(use_slab_pool=1)
     m.close()
