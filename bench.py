@@ -234,6 +234,10 @@ def main():
     # 0 / 8 / 12 / 16: 1060 / 1030 / 1034 / 1029 ms per step
     ap.add_argument("--resident-layers", type=int, default=-1)
     ap.add_argument("--keep-internals", type=int, default=1)
+    # the hybrid 8-bit optimizer states and global-norm clipping (clipping
+    # holds every gradient until the norm is known: a pool of L + 1 slabs)
+    ap.add_argument("--opt-8bit", action="store_true")
+    ap.add_argument("--clip-norm", type=float, default=0.0)
     # CPU threads for Adam and the embedding scatter (memory-bandwidth bound)
     ap.add_argument("--host-threads", type=int, default=16)
     # the same model under the pages' schedule after the timed steps (0: skip)
@@ -270,7 +274,9 @@ def main():
     model = mt.Model(shape, prefetch_depth=args.prefetch_depth,
                      use_slab_pool=0 if args.no_slab_pool else 1, check_finite=1,
                      time_kernels=1, host_threads=args.host_threads,
-                     resident_layers=resident, keep_internals=keep)
+                     resident_layers=resident, keep_internals=keep,
+                     opt_8bit=1 if args.opt_8bit else 0, clip_norm=args.clip_norm,
+                     n_slabs=max(8, shape.n_layers + 1) if args.clip_norm > 0 else 8)
     log(f"model created in {time.perf_counter() - t0:.1f}s")
     t0 = time.perf_counter()
     init_weights(model, shape, seed=0)
@@ -480,6 +486,8 @@ def main():
             "slab_pool": not args.no_slab_pool,
             "resident_layers": resident,
             "keep_internals": keep,
+            "opt_8bit": bool(args.opt_8bit),
+            "clip_norm": args.clip_norm,
             "parallelism": "single-gpu layer streaming",
             "params": n_params,
         },
@@ -518,6 +526,8 @@ def main():
         "device_arena_bytes": stats[-1]["device_arena_bytes"],
         "device_used_bytes": int(dev_used),
         "loss": losses[-1],
+        "grad_norm": stats[-1]["grad_norm"],
+        "clip_factor": stats[-1]["clip_factor"],
         "gemm_ms_per_step": round(gemm_ms, 2),
         "attn_ms_per_step": round(attn_ms, 2),
         "gemm_families": gemm_families,

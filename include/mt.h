@@ -115,7 +115,22 @@ typedef struct {
                                 C x layer bytes; setting a parameter, a failed step or
                                 another arena makes the next step load them again.
                                 Results are bitwise those of 0. */
+  int32_t opt_8bit;          /* 1: the host store keeps Adam's moments as the hybrid 8-bit
+                                states of mt_host_adam8 (E4M3 codes + one fp32 scale per
+                                128 elements of a tensor; 2.06 instead of 8 bytes per
+                                parameter) and every unit is updated by that operator;
+                                needs hidden % 128 == 0; fixed at creation */
   double lr, beta1, beta2, eps, weight_decay; /* Adam (weight_decay must be 0) */
+  double clip_norm;          /* > 0: global gradient-norm clipping (LazyTrain's fast
+                                clipping): every gradient is multiplied by
+                                min(1, clip_norm / (norm + 1e-6)), norm over the whole
+                                model.  Each unit's sum of squares is accumulated on the
+                                GPU beside its finiteness check (the host never re-reads
+                                a gradient) and the factor is applied inside the Adam
+                                pass; since it depends on every gradient, each unit's
+                                update waits until the last gradient has landed, so the
+                                slab pool must hold every layer's and the head's
+                                gradient (n_slabs >= n_layers + 1, or no pool).  0: off */
 } mt_run_cfg;
 
 /* Device pointers of one layer's weights: the stateless template's binding.
@@ -164,6 +179,8 @@ typedef struct {
   double host_start_ms, gpu_done_ms, grads_landed_ms, updates_done_ms;
   double probe_all_attn_ms; /* summed duration of every timed attention launch */
   double probe_all_flops;   /* algorithmic FLOPs of every timed launch of the step */
+  double grad_norm;         /* with clip_norm > 0: the step's global gradient norm */
+  double clip_factor;       /* ... and the factor every gradient was multiplied by (else 1) */
 } mt_step_stats;
 
 /* One kernel's timed launches in the last step (time_kernels = 1): launches

@@ -27,6 +27,21 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source additions.  The attention kernels hold their MFMA accumulators
+# and operands in VGPR form: with the default AGPR form the dK/dV kernel's
+# allocation copied values between the two register files around every
+# tile (several hundred v_accvgpr moves per loop trip); the instructions and
+# their order are otherwise the same, so the results are too.
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
+
+def hip_flags(src: str) -> list:
+    """hipcc flags of one HIP source."""
+    return HIP_FLAGS + FILE_FLAGS.get(os.path.basename(src), [])
+
+
 CXX_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-march=x86-64-v3", "-pthread", "-ffp-contract=off", "-fno-math-errno",
     "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
@@ -37,7 +52,7 @@ CXX_FLAGS = [
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC] + HIP_FLAGS + ["-c", src, "-o", obj]
+        cmd = [HIPCC] + hip_flags(src) + ["-c", src, "-o", obj]
     else:
         cmd = ["g++"] + CXX_FLAGS + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

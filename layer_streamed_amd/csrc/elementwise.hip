@@ -428,18 +428,29 @@ __global__ void copy_rows_kernel(const uint16_t* __restrict__ src, long lds,
 // (bf16: exponent bits all ones; fp32 likewise), OR-reduced over the
 // workgroup through LDS.
 __global__ __launch_bounds__(256) void nonfinite_kernel(const u32x4_t* __restrict__ g, size_t n16,
-                                                        int f32, int32_t* __restrict__ flags) {
+                                                        int f32, int32_t* __restrict__ flags,
+                                                        float* __restrict__ ssq) {
   __shared__ int any;
+  __shared__ float part[4];
   if (threadIdx.x == 0) any = 0;
   __syncthreads();
   uint32_t bad = 0;
+  float sq = 0.f;  // this lane's sum of squares (the gradient-norm share)
   const uint32_t em = f32 ? 0x7F800000u : 0x7F807F80u;  // exponent masks per dword
   auto check = [&](const u32x4_t v) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t x = v[k] & em;
-      if (f32) bad |= (x == 0x7F800000u);
-      else bad |= ((x & 0xFFFFu) == 0x7F80u) | ((x >> 16) == 0x7F80u);
+      if (f32) {
+        bad |= (x == 0x7F800000u);
+        const float f = __uint_as_float(v[k]);
+        sq += f * f;
+      } else {
+        bad |= ((x & 0xFFFFu) == 0x7F80u) | ((x >> 16) == 0x7F80u);
+        const float lo = __uint_as_float(v[k] << 16), hi = __uint_as_float(v[k] & 0xFFFF0000u);
+        sq += lo * lo;
+        sq += hi * hi;
+      }
     }
   };
   // four independent 16-byte loads in flight per lane per trip
@@ -454,8 +465,16 @@ __global__ __launch_bounds__(256) void nonfinite_kernel(const u32x4_t* __restric
   }
   for (; i < n16; i += stride) check(g[i]);
   if (bad) any = 1;  // benign race: every writer stores 1
+  if (ssq) {
+    // the workgroup's sum of squares in a fixed order: lanes, then waves
+    sq = wave_sum(sq);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sq;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) flags[blockIdx.x] = any;
+  if (threadIdx.x == 0) {
+    flags[blockIdx.x] = any;
+    if (ssq) ssq[blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
+  }
 }
 
 }  // namespace
@@ -547,10 +566,11 @@ hipError_t cast_t(const float* in, E* out, size_t n, hipStream_t s) {
 
 int rmsnorm_bwd_blocks(int rows) { return (rows + RB_ROWS - 1) / RB_ROWS; }
 
-hipError_t nonfinite_flags(const void* g, size_t bytes, int f32, int32_t* flags, hipStream_t s) {
+hipError_t nonfinite_flags(const void* g, size_t bytes, int f32, int32_t* flags, hipStream_t s,
+                           float* ssq) {
   if (bytes & 15) return hipErrorInvalidValue;
   hipLaunchKernelGGL(nonfinite_kernel, dim3(NONFINITE_BLOCKS), dim3(256), 0, s,
-                     static_cast<const u32x4_t*>(g), bytes / 16, f32, flags);
+                     static_cast<const u32x4_t*>(g), bytes / 16, f32, flags, ssq);
   return hipGetLastError();
 }
 

@@ -153,7 +153,9 @@ struct Arena {
   std::vector<char*> keep;  // kept internals, one per layer of a segment
   size_t keep_bytes = 0;
   char* dy = nullptr;
-  int32_t* flags = nullptr;  // [NG + 1][NONFINITE_BLOCKS]: ring slots, then the head
+  // [NG + 1][2 * NONFINITE_BLOCKS]: ring slots, then the head; each slot the
+  // finiteness flags, then the per-block sums of squares (fp32 bits)
+  int32_t* flags = nullptr;
   int32_t* tgt = nullptr;
   float* loss = nullptr;
   void* lws = nullptr;
@@ -189,7 +191,7 @@ Arena carve_arena(const mt_model* M, const Dims& d, char* base, size_t* bytes) {
     for (int i = 0; i < K; ++i) a.keep.push_back(c.take<char>(a.keep_bytes));
   }
   a.dy = c.take<char>(act);
-  a.flags = c.take<int32_t>((size_t)(NG + 1) * NONFINITE_BLOCKS);
+  a.flags = c.take<int32_t>((size_t)(NG + 1) * 2 * NONFINITE_BLOCKS);
   a.tgt = c.take<int32_t>(d.D);
   a.loss = c.take<float>(64);
   a.lws_bytes = layer_ws_bytes(d, 1);
@@ -429,7 +431,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     M->loss_host = static_cast<float*>(M->host_alloc(64, true));
     if (!M->flags_host)
       M->flags_host = static_cast<int32_t*>(
-          M->host_alloc((size_t)(L + 1) * NONFINITE_BLOCKS * 4, true));
+          M->host_alloc((size_t)(L + 1) * 2 * NONFINITE_BLOCKS * 4, true));
     MT_CHECK(M->flags_host, MT_E_OOM_HOST, "mt_stream_step: pinned flag allocation failed");
     MT_CHECK(M->x0_host && M->dx0_host && M->tgt_host && M->loss_host, MT_E_OOM_HOST,
              "mt_stream_step: pinned staging allocation failed");
@@ -453,6 +455,10 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   const size_t act = (size_t)d.D * d.H;
   const size_t es = M->es;
   const bool f32 = es == 4;
+  // global-norm clipping: each unit's sum of squares comes with its
+  // finiteness flags; the flags kernel runs for either
+  const bool clipping = M->run.clip_norm > 0;
+  const bool stats = M->run.check_finite || clipping;
 
   if (M->run.defer_updates && !M->pending.head_grad) {
     M->pending.head_grad = M->host_alloc(M->hl.total * M->es, true);
@@ -476,6 +482,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   std::atomic<int> g_fail{0}, a_fail{0};
   std::atomic<int64_t> units_updated{0};
   double adam_ms = 0.0;
+  // clipping: each unit's gradient sum of squares (layers, head, embedding)
+  std::vector<double> unit_ss((size_t)L + 2, 0.0);
+  double last_clip = 1.0, last_norm = 0.0;
   double d2h_ms = 0, d2h_bytes = 0;
   double ring_wait_ms = 0, slab_wait_ms = 0, op_wait_ms = 0, adam_idle_ms = 0;
   double host_start_ms = 0, gpu_done_ms = 0, grads_landed_ms = 0, updates_done_ms = 0;
@@ -563,8 +572,8 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         const auto t0 = clock::now();
         ok = M->sdma->copy_d2h(host, o.src, o.elems * es);
         if (ok && o.dflags)
-          ok = M->sdma->copy_d2h(M->flags_host + (size_t)o.unit * NONFINITE_BLOCKS, o.dflags,
-                                 NONFINITE_BLOCKS * 4);
+          ok = M->sdma->copy_d2h(M->flags_host + (size_t)o.unit * 2 * NONFINITE_BLOCKS, o.dflags,
+                                 2 * NONFINITE_BLOCKS * 4);
         d2h_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
         d2h_bytes += (double)o.elems * es;
         grads_landed_ms = ms_since(t_begin);
@@ -688,26 +697,102 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
     }
     bool checked = false;
     bool skip = false;
+    // the first landing waits for the loss: a non-finite loss updates nothing
+    auto check_loss = [&]() {
+      if (checked) return;
+      std::unique_lock<std::mutex> lk(loss_mu);
+      loss_cv.wait(lk, [&] { return loss_ready; });
+      checked = true;
+      if (!loss_ev || hipEventSynchronize(loss_ev) != hipSuccess) {
+        a_fail = 1;
+        abort_all = true;
+      } else if (M->run.check_finite && !std::isfinite(*M->loss_host)) {
+        nonfinite_loss = true;
+        abort_all = true;
+      }
+    };
+    auto unit_bad = [&](int unit) {
+      const int32_t* fl = M->flags_host + (size_t)unit * 2 * NONFINITE_BLOCKS;
+      bool bad = false;
+      for (int k = 0; k < NONFINITE_BLOCKS && M->run.check_finite; ++k) bad |= fl[k] != 0;
+      return bad;
+    };
+    // dE from dx0 (rows of this batch only); true if a row is not finite
+    auto embed_scatter = [&](const Landed& x) {
+      if (f32)
+        embed_scatter_add(static_cast<const float*>(x.host), tokens, (size_t)d.D, (size_t)d.H,
+                          dE, M->pool.get());
+      else
+        embed_scatter_add(static_cast<const uint16_t*>(x.host), tokens, (size_t)d.D,
+                          (size_t)d.H, dE, M->pool.get());
+      bool bad = false;
+      if (M->run.check_finite) {
+        std::atomic<bool> any{false};
+        const size_t H = (size_t)d.H;
+        M->pool->parallel_for(rows_now.size(), [&](size_t lo, size_t hi) {
+          for (size_t i = lo; i < hi && !any.load(std::memory_order_relaxed); ++i)
+            if (!grad_finite(nullptr, dE + (size_t)rows_now[i] * H, H, nullptr)) any = true;
+        }, 64);
+        bad = any.load();
+      }
+      return bad;
+    };
+    float clip = 1.f;
+    std::vector<Landed> held;  // with clipping: every landing, until the norm is known
+    if (clipping) {
+      double ss = 0.0;  // the whole gradient's sum of squares, in a fixed order
+      bool bad = false;
+      for (;;) {
+        const auto tw = clock::now();
+        Landed x = landq.pop();
+        adam_idle_ms += ms_since(tw);
+        if (x.end) break;
+        check_loss();
+        held.push_back(x);
+        if (abort_all.load()) continue;
+        const auto t0 = clock::now();
+        if (x.unit >= 0) {
+          bad |= unit_bad(x.unit);
+          const float* sq = reinterpret_cast<const float*>(
+              M->flags_host + (size_t)x.unit * 2 * NONFINITE_BLOCKS + NONFINITE_BLOCKS);
+          double s = 0.0;
+          for (int k = 0; k < NONFINITE_BLOCKS; ++k) s += (double)sq[k];
+          unit_ss[x.unit] = s;
+        } else {
+          bad |= embed_scatter(x);
+          double s = 0.0;
+          const size_t H = (size_t)d.H;
+          for (int32_t r : rows_now)
+            for (size_t c = 0; c < H; ++c) s += (double)dE[(size_t)r * H + c] * dE[(size_t)r * H + c];
+          unit_ss[L + 1] = s;
+        }
+        adam_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+      }
+      if (bad) {
+        a_fail = 2;
+        abort_all = true;
+      }
+      for (int u = 0; u <= L + 1; ++u) ss += unit_ss[u];
+      clip = (float)std::min(1.0, M->run.clip_norm / (std::sqrt(ss) + 1e-6));
+      last_clip = clip;
+      last_norm = std::sqrt(ss);
+      held.push_back(Landed{0, nullptr, false, nullptr, true});
+    }
+    size_t next_held = 0;
     for (;;) {
-      const auto tw = clock::now();
-      Landed x = landq.pop();
-      adam_idle_ms += ms_since(tw);
+      Landed x;
+      if (clipping) {
+        x = held[next_held++];
+      } else {
+        const auto tw = clock::now();
+        x = landq.pop();
+        adam_idle_ms += ms_since(tw);
+      }
       if (x.end) {
         updates_done_ms = ms_since(t_begin);
         return;
       }
-      if (!checked) {
-        std::unique_lock<std::mutex> lk(loss_mu);
-        loss_cv.wait(lk, [&] { return loss_ready; });
-        checked = true;
-        if (!loss_ev || hipEventSynchronize(loss_ev) != hipSuccess) {
-          a_fail = 1;
-          abort_all = true;
-        } else if (M->run.check_finite && !std::isfinite(*M->loss_host)) {
-          nonfinite_loss = true;
-          abort_all = true;
-        }
-      }
+      check_loss();
       skip = skip || abort_all.load();
       const auto t0 = clock::now();
       if (!skip) {
@@ -715,11 +800,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           Unit& u = M->units[x.unit];
           const uint16_t* gb = f32 ? nullptr : static_cast<const uint16_t*>(x.host);
           const float* gf = f32 ? static_cast<const float*>(x.host) : nullptr;
-          const int32_t* fl = M->flags_host + (size_t)x.unit * NONFINITE_BLOCKS;
-          bool bad = false;
-          for (int k = 0; k < NONFINITE_BLOCKS && M->run.check_finite; ++k) bad |= fl[k] != 0;
-          (void)gb;
-          (void)gf;
+          const bool bad = unit_bad(x.unit);
           if (bad) {
             a_fail = 2;
             abort_all = true;
@@ -729,11 +810,10 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
             if (u.kept) memcpy(u.kept, x.host, u.n * es);
             M->pending.head = true;  // its gradient stays in pending.head_grad
             M->pending.hp_head = hp;
+            M->pending.clip_head = clip;
             ++units_deferred;
           } else {
-            adam_parallel(u.master, u.m, u.v, gb, gf,
-                          f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
-                          f32 ? static_cast<float*>(u.shadow) : nullptr, u.n, hp, M->pool.get());
+            unit_adam(M, x.unit, gb, gf, hp, clip);
             if (u.kept) memcpy(u.kept, x.host, u.n * es);
             ++units_updated;
             if (x.unit >= rs && x.unit < rs + R) {
@@ -757,25 +837,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
             }
           }
         } else {
-          Unit& u = M->units[L + 1];
-          if (f32)
-            embed_scatter_add(static_cast<const float*>(x.host), tokens, (size_t)d.D,
-                              (size_t)d.H, dE, M->pool.get());
-          else
-            embed_scatter_add(static_cast<const uint16_t*>(x.host), tokens, (size_t)d.D,
-                              (size_t)d.H, dE, M->pool.get());
           // only the batch's rows of dE can be nonzero, hence non-finite
-          bool bad = false;
-          if (M->run.check_finite) {
-            std::atomic<bool> any{false};
-            const size_t H = (size_t)d.H;
-            M->pool->parallel_for(rows_now.size(), [&](size_t lo, size_t hi) {
-              for (size_t i = lo; i < hi && !any.load(std::memory_order_relaxed); ++i)
-                if (!grad_finite(nullptr, dE + (size_t)rows_now[i] * H, H, nullptr)) any = true;
-            }, 64);
-            bad = any.load();
-          }
-          (void)u;
+          // (with clipping dE was formed, and checked, while collecting)
+          const bool bad = clipping ? false : embed_scatter(x);
           if (bad) {
             a_fail = 2;
             abort_all = true;
@@ -784,6 +848,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
             // the update of every row (untouched rows with a zero gradient)
             M->pending.embed = true;
             M->pending.hp_embed = hp;
+            M->pending.clip_embed = clip;
             M->pending.row_done.assign((size_t)d.V, 0);
             M->pending.touched = touched;
             if (defer) {
@@ -921,12 +986,13 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         }
         loss_cv.notify_all();
         MT_STEP_HIP(hipEventRecord(ph_head, sC));
-        int32_t* hf = A.flags + (size_t)NG * NONFINITE_BLOCKS;
-        if (M->run.check_finite)
-          MT_STEP_HIP(nonfinite_flags(A.head_grad, M->hl.total * es, f32, hf, sC));
+        int32_t* hf = A.flags + (size_t)NG * 2 * NONFINITE_BLOCKS;
+        if (stats)
+          MT_STEP_HIP(nonfinite_flags(A.head_grad, M->hl.total * es, f32, hf, sC,
+                                      clipping ? reinterpret_cast<float*>(hf + NONFINITE_BLOCKS)
+                                               : nullptr));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
-        offq.push(Offload{L, A.head_grad, M->hl.total, M->run.check_finite ? hf : nullptr,
-                          op_done[i], -1});
+        offq.push(Offload{L, A.head_grad, M->hl.total, stats ? hf : nullptr, op_done[i], -1});
         continue;
       } else if (op.kind == OP_REFWD) {
         const int l = op.layer, a = (l / K) * K;
@@ -958,9 +1024,11 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           MT_STEP_RUN(layer_bwd_impl(d, layer_view(M, w), in, A.dy, A.dy, grad_view(M, A.gring[r]),
                                      A.lws, A.lws_bytes, sC,
                                      M->run.time_kernels ? &probe : nullptr));
-        int32_t* lf = A.flags + (size_t)r * NONFINITE_BLOCKS;
-        if (M->run.check_finite)
-          MT_STEP_HIP(nonfinite_flags(A.gring[r], M->ll.total * es, f32, lf, sC));
+        int32_t* lf = A.flags + (size_t)r * 2 * NONFINITE_BLOCKS;
+        if (stats)
+          MT_STEP_HIP(nonfinite_flags(A.gring[r], M->ll.total * es, f32, lf, sC,
+                                      clipping ? reinterpret_cast<float*>(lf + NONFINITE_BLOCKS)
+                                               : nullptr));
         MT_STEP_HIP(hipEventRecord(op_done[i], sC));
         if (l == 0) {
           MT_STEP_HIP(hipEventRecord(ph_end, sC));
@@ -969,7 +1037,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
           // is still on the link instead of after the last Adam update
           offq.push(Offload{-1, A.dy, act, nullptr, ph_end, -1});
         }
-        Offload o{l, A.gring[r], M->ll.total, M->run.check_finite ? lf : nullptr, op_done[i], r};
+        Offload o{l, A.gring[r], M->ll.total, stats ? lf : nullptr, op_done[i], r};
         offq.push(o);
         ++bwd_count;
         continue;
@@ -1074,6 +1142,8 @@ drain:
         snprintf(s.probe_kernel, sizeof s.probe_kernel, "%s", top.name);
       }
     }
+    s.grad_norm = last_norm;
+    s.clip_factor = last_clip;
     s.h2d_bytes = h2d_bytes + h2d_load_bytes + res_bytes;
     s.d2h_bytes = d2h_bytes;
     s.pinned_host_bytes = M->pinned_bytes;

@@ -104,7 +104,10 @@ hipError_t rope_apply(float* qkv, long ldq, int batch, int seq, int n_heads, int
 // strided share of `bytes` bytes of bf16 (f32 = 0) or fp32 values and write
 // flags[block] = 1 if any is Inf or NaN, else 0 (bytes % 16 == 0).
 constexpr int NONFINITE_BLOCKS = 2048;
-hipError_t nonfinite_flags(const void* g, size_t bytes, int f32, int32_t* flags, hipStream_t s);
+// With ssq, each workgroup also writes the sum of squares of its share
+// (fp32, a fixed order within the workgroup): the gradient norm's pieces.
+hipError_t nonfinite_flags(const void* g, size_t bytes, int f32, int32_t* flags, hipStream_t s,
+                           float* ssq = nullptr);
 hipError_t cast_f32(const float* in, uint16_t* out, size_t n, hipStream_t s);
 hipError_t cast_f32(const float* in, float* out, size_t n, hipStream_t s);
 hipError_t fill_f32(float* p, float v, size_t n, hipStream_t s);

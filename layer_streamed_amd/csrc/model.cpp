@@ -67,15 +67,26 @@ bool lookup_param(const mt_model* m, const char* name, TensorRef* out) {
   return true;
 }
 
+void unit_adam(mt_model* M, int unit, const uint16_t* gb, const float* gf, const AdamHp& hp,
+               float clip) {
+  Unit& u = M->units[unit];
+  const bool f32 = M->es == 4;
+  uint16_t* sb = f32 ? nullptr : static_cast<uint16_t*>(u.shadow);
+  float* sf = f32 ? static_cast<float*>(u.shadow) : nullptr;
+  if (M->run.opt_8bit) {
+    const Adam8Arrays a{u.master, u.mq, u.rq, u.ms, u.rs, gb, gf, sb, sf};
+    adam8_parallel(a, u.segs.data(), (int)u.segs.size(), hp, clip, M->pool.get());
+  } else {
+    adam_parallel(u.master, u.m, u.v, gb, gf, sb, sf, u.n, hp, M->pool.get());
+  }
+}
+
 void apply_pending_head(mt_model* M) {
   PendingAdam& pa = M->pending;
   if (!pa.head) return;
-  Unit& u = M->units[M->cfg.n_layers];
   const bool f32 = M->es == 4;
-  adam_parallel(u.master, u.m, u.v, f32 ? nullptr : static_cast<const uint16_t*>(pa.head_grad),
-                f32 ? static_cast<const float*>(pa.head_grad) : nullptr,
-                f32 ? nullptr : static_cast<uint16_t*>(u.shadow),
-                f32 ? static_cast<float*>(u.shadow) : nullptr, u.n, pa.hp_head, M->pool.get());
+  unit_adam(M, M->cfg.n_layers, f32 ? nullptr : static_cast<const uint16_t*>(pa.head_grad),
+            f32 ? static_cast<const float*>(pa.head_grad) : nullptr, pa.hp_head, pa.clip_head);
   pa.head = false;
 }
 
@@ -96,7 +107,15 @@ void embed_rows(mt_model* M, const std::vector<int32_t>* rows) {
       // an untouched row's gradient is zero: read a cached zero row instead
       // of the row of dE (the same values, so the same result)
       const float* g = pa.touched[r] ? M->dE + a : M->zero_row;
-      if (f32)
+      if (M->run.opt_8bit) {
+        // a row is whole 8-bit blocks (hidden % 128 == 0) of the one tensor
+        const size_t b = a / ADAM8_BLOCK;
+        const Adam8Arrays ar{u.master + a, u.mq + a, u.rq + a, u.ms + b, u.rs + b, nullptr, g,
+                             f32 ? nullptr : static_cast<uint16_t*>(u.shadow) + a,
+                             f32 ? static_cast<float*>(u.shadow) + a : nullptr};
+        const Adam8Seg seg{0, H, 0};
+        adam8_range(ar, &seg, 1, 0, adam8_blocks(H), pa.hp_embed, pa.clip_embed);
+      } else if (f32)
         adam_range(u.master + a, u.m + a, u.v + a, nullptr, g, nullptr,
                    static_cast<float*>(u.shadow) + a, 0, H, pa.hp_embed);
       else
@@ -181,7 +200,46 @@ static mt_status check_run(const mt_model_cfg* cfg, const mt_run_cfg* run) {
   MT_CHECK(run->lr > 0 && run->beta1 >= 0 && run->beta1 < 1 && run->beta2 >= 0 &&
                run->beta2 < 1 && run->eps >= 0,
            MT_E_INVALID, "bad Adam hyperparameters");
+  MT_CHECK(run->opt_8bit == 0 || run->opt_8bit == 1, MT_E_INVALID, "opt_8bit must be 0 or 1");
+  MT_CHECK(!run->opt_8bit || cfg->hidden % ADAM8_BLOCK == 0, MT_E_INVALID,
+           "opt_8bit needs hidden to be a multiple of %d (embedding rows are whole blocks)",
+           ADAM8_BLOCK);
+  MT_CHECK(run->clip_norm >= 0, MT_E_INVALID, "clip_norm must be >= 0");
+  MT_CHECK(!(run->clip_norm > 0) || !run->use_slab_pool || run->n_slabs >= cfg->n_layers + 1,
+           MT_E_INVALID,
+           "clip_norm needs every layer's and the head's gradient held at once: n_slabs >= "
+           "n_layers + 1 (%d), or no slab pool",
+           cfg->n_layers + 1);
   return MT_OK;
+}
+
+// The tensors of each unit, in layout order, with their 8-bit blocks'
+// first scale index.
+static void build_segments(mt_model* m) {
+  const Dims& d = m->shape;
+  const size_t H = d.H, Q = d.Qd, Kv = d.Kvd, F = d.F, V = d.V;
+  const LayerLayout& l = m->ll;
+  const int L = m->cfg.n_layers;
+  auto fill = [](Unit& u, std::initializer_list<std::pair<size_t, size_t>> t) {
+    u.segs.clear();
+    size_t b = 0;
+    for (const auto& [off, n] : t) {
+      u.segs.push_back({off, n, b});
+      b += adam8_blocks(n);
+    }
+  };
+  for (int i = 0; i < L; ++i)
+    fill(m->units[i], {{l.attn_norm, H}, {l.w_q, Q * H}, {l.w_k, Kv * H}, {l.w_v, Kv * H},
+                       {l.w_o, H * Q}, {l.mlp_norm, H}, {l.w_gate, F * H}, {l.w_up, F * H},
+                       {l.w_down, H * F}});
+  fill(m->units[L], {{m->hl.final_norm, H}, {m->hl.lm_head, V * H}});
+  fill(m->units[L + 1], {{0, V * H}});
+}
+
+static const Adam8Seg* find_segment(const Unit& u, size_t off) {
+  for (const Adam8Seg& s : u.segs)
+    if (s.off == off) return &s;
+  return nullptr;
 }
 
 extern "C" {
@@ -207,6 +265,7 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
   m->units[L].n = m->hl.total;
   m->units[L + 1].n = align128((size_t)d.V * d.H);
   const bool pinned = run->host_alloc == MT_HOST_PINNED;
+  build_segments(m.get());
 
   // streamed copy of every unit in one pinned region
   const size_t es = m->es;
@@ -221,23 +280,44 @@ mt_status mt_model_create(const mt_model_cfg* cfg, const mt_run_cfg* run, mt_mod
     u.shadow = sh + off * es;
     off += u.n;
     u.master = static_cast<float*>(m->host_alloc(u.n * 4, false));
-    u.m = static_cast<float*>(m->host_alloc(u.n * 4, false));
-    u.v = static_cast<float*>(m->host_alloc(u.n * 4, false));
-    if (!u.master || !u.m || !u.v)
+    if (!u.master)
       return set_error(MT_E_OOM_HOST, "mt_model_create: host allocation of %zu bytes failed", u.n * 4);
+    const size_t nb = adam8_segment_blocks(u.segs.data(), (int)u.segs.size());
+    if (run->opt_8bit) {
+      u.mq = static_cast<uint8_t*>(m->host_alloc(u.n, false));
+      u.rq = static_cast<uint8_t*>(m->host_alloc(u.n, false));
+      u.ms = static_cast<float*>(m->host_alloc(nb * 4, false));
+      u.rs = static_cast<float*>(m->host_alloc(nb * 4, false));
+      if (!u.mq || !u.rq || !u.ms || !u.rs)
+        return set_error(MT_E_OOM_HOST, "mt_model_create: 8-bit state allocation failed");
+    } else {
+      u.m = static_cast<float*>(m->host_alloc(u.n * 4, false));
+      u.v = static_cast<float*>(m->host_alloc(u.n * 4, false));
+      if (!u.m || !u.v)
+        return set_error(MT_E_OOM_HOST, "mt_model_create: host allocation of %zu bytes failed",
+                         u.n * 4);
+    }
     if (run->keep_grads) {
       u.kept = m->host_alloc(u.n * es, false);
       if (!u.kept) return set_error(MT_E_OOM_HOST, "mt_model_create: keep_grads allocation failed");
     }
     // first touch in parallel (places pages, zeroes pads and moments)
     float* ps[3] = {u.master, u.m, u.v};
+    uint8_t* qs[2] = {u.mq, u.rq};
     char* shp = static_cast<char*>(u.shadow);
     char* kp = static_cast<char*>(u.kept);
     m->pool->parallel_for(u.n, [&](size_t lo, size_t hi) {
-      for (float* p : ps) memset(p + lo, 0, (hi - lo) * 4);
+      for (float* p : ps)
+        if (p) memset(p + lo, 0, (hi - lo) * 4);
+      for (uint8_t* q : qs)
+        if (q) memset(q + lo, 0, hi - lo);
       memset(shp + lo * es, 0, (hi - lo) * es);
       if (kp) memset(kp + lo * es, 0, (hi - lo) * es);
     });
+    if (u.ms) {
+      memset(u.ms, 0, nb * 4);
+      memset(u.rs, 0, nb * 4);
+    }
   }
   m->dE = static_cast<float*>(m->host_alloc((size_t)d.V * d.H * 4, false));
   m->zero_row = static_cast<float*>(m->host_alloc((size_t)d.H * 4, false));
@@ -274,10 +354,11 @@ mt_status mt_model_set_schedule(mt_model* m, const mt_run_cfg* run) {
   if (mt_status st = check_run(&m->cfg, run); st != MT_OK) return st;
   const mt_run_cfg& o = m->run;
   MT_CHECK(run->precision == o.precision && run->host_alloc == o.host_alloc &&
-               run->keep_grads == o.keep_grads && run->host_threads == o.host_threads,
+               run->keep_grads == o.keep_grads && run->host_threads == o.host_threads &&
+               run->opt_8bit == o.opt_8bit,
            MT_E_INVALID,
-           "mt_model_set_schedule: precision, host_alloc, keep_grads and host_threads are fixed "
-           "when the model is created");
+           "mt_model_set_schedule: precision, host_alloc, keep_grads, host_threads and opt_8bit "
+           "are fixed when the model is created");
   MT_CHECK(!run->use_slab_pool || (m->slab_list.size() > 0 && (size_t)run->n_slabs == m->slab_list.size()),
            MT_E_INVALID,
            "mt_model_set_schedule: the slab pool (and its size) is allocated when the model is "
@@ -310,10 +391,18 @@ mt_status mt_model_set_param(mt_model* m, const char* name, const float* src, si
   m->resident_valid.assign(m->resident_valid.size(), 0);  // the device copies are stale now
   Unit& u = m->units[r.unit];
   const bool f32 = m->es == 4;
+  if (m->run.opt_8bit) {  // fresh moments: zero codes and scales
+    const Adam8Seg* s = find_segment(u, r.off);
+    MT_CHECK(s && s->n == n, MT_E_STATE, "mt_model_set_param: no 8-bit segment for '%s'", name);
+    memset(u.mq + r.off, 0, n);
+    memset(u.rq + r.off, 0, n);
+    memset(u.ms + s->sblk, 0, adam8_blocks(n) * 4);
+    memset(u.rs + s->sblk, 0, adam8_blocks(n) * 4);
+  }
   m->pool->parallel_for(n, [&](size_t lo, size_t hi) {
     memcpy(u.master + r.off + lo, src + lo, (hi - lo) * 4);
-    memset(u.m + r.off + lo, 0, (hi - lo) * 4);
-    memset(u.v + r.off + lo, 0, (hi - lo) * 4);
+    if (u.m) memset(u.m + r.off + lo, 0, (hi - lo) * 4);
+    if (u.v) memset(u.v + r.off + lo, 0, (hi - lo) * 4);
     if (f32) {
       memcpy(static_cast<float*>(u.shadow) + r.off + lo, src + lo, (hi - lo) * 4);
     } else {
@@ -342,8 +431,18 @@ mt_status mt_model_get_param(const mt_model* m, const char* name, int32_t which,
   };
   switch (which) {
     case MT_GET_MASTER: memcpy(dst, u.master + r.off, n * 4); break;
-    case MT_GET_M: memcpy(dst, u.m + r.off, n * 4); break;
-    case MT_GET_V: memcpy(dst, u.v + r.off, n * 4); break;
+    case MT_GET_M:
+    case MT_GET_V:
+      if (m->run.opt_8bit) {  // the values the 8-bit state holds
+        const Adam8Seg* s = find_segment(u, r.off);
+        MT_CHECK(s && s->n == n, MT_E_STATE, "mt_model_get_param: no 8-bit segment for '%s'",
+                 name);
+        if (which == MT_GET_M) adam8_dequant(u.mq, u.ms, *s, false, dst);
+        else adam8_dequant(u.rq, u.rs, *s, true, dst);
+      } else {
+        memcpy(dst, (which == MT_GET_M ? u.m : u.v) + r.off, n * 4);
+      }
+      break;
     case MT_GET_SHADOW:
       for (size_t i = 0; i < n; ++i) dst[i] = elem(u.shadow, r.off + i);
       break;

@@ -26,8 +26,13 @@ namespace mt {
 struct Unit {
   size_t n = 0;               // elements (with alignment padding)
   float* master = nullptr;    // fp32, pageable
-  float* m = nullptr;
+  float* m = nullptr;         // fp32 Adam moments (without opt_8bit)
   float* v = nullptr;
+  uint8_t* mq = nullptr;      // hybrid 8-bit moments (opt_8bit): codes of m and
+  uint8_t* rq = nullptr;      // of r = sqrt(v), and their per-block scales
+  float* ms = nullptr;
+  float* rs = nullptr;
+  std::vector<Adam8Seg> segs; // the unit's tensors (8-bit blocks never span two)
   void* shadow = nullptr;     // streamed copy, inside the pinned shadow region
   void* kept = nullptr;       // last step's gradient (keep_grads)
 };
@@ -61,6 +66,7 @@ class SlabPool {
 struct PendingAdam {
   bool head = false, embed = false;
   AdamHp hp_head{}, hp_embed{};
+  float clip_head = 1.f, clip_embed = 1.f;  // the step's clipping factor
   // the head's gradient lands in a pinned buffer of its own (never a pool
   // slab: holding a slab across units would stall the offload of the rest
   // of the step when the pool is small)
@@ -129,4 +135,8 @@ void apply_pending_embed_rows(mt_model* m, const int32_t* ids, size_t n);
 void apply_pending_embed_rest(mt_model* m);
 void flush_pending(mt_model* m);
 void drop_pending(mt_model* m);
+// Adam (fp32 or hybrid 8-bit moments, per the model) over a whole unit with
+// gradient gb (bf16) or gf (fp32), writing the streamed copy.
+void unit_adam(mt_model* m, int unit, const uint16_t* gb, const float* gf, const AdamHp& hp,
+               float clip);
 }

@@ -52,8 +52,8 @@ class RunCfg(C.Structure):
         "ckpt_interval", "prefetch_depth", "use_slab_pool", "n_slabs", "mlp_chunk_tokens",
         "head_chunk_tokens", "precision", "host_threads", "check_finite", "serialize",
         "host_alloc", "keep_grads", "time_kernels", "keep_internals", "defer_updates",
-        "resident_layers")] + [
-        (n, C.c_double) for n in ("lr", "beta1", "beta2", "eps", "weight_decay")]
+        "resident_layers", "opt_8bit")] + [
+        (n, C.c_double) for n in ("lr", "beta1", "beta2", "eps", "weight_decay", "clip_norm")]
 
 
 class LayerView(C.Structure):
@@ -71,7 +71,8 @@ class StepStats(C.Structure):
                 "host_ring_wait_ms", "host_slab_wait_ms", "host_op_wait_ms", "host_adam_idle_ms",
                 "probe_all_gemm_ms")] + [("probe_kernel", C.c_char * 96)] + [
             (n, C.c_double) for n in ("host_start_ms", "gpu_done_ms", "grads_landed_ms",
-                                      "updates_done_ms", "probe_all_attn_ms", "probe_all_flops")]
+                                      "updates_done_ms", "probe_all_attn_ms", "probe_all_flops",
+                                      "grad_norm", "clip_factor")]
 
     def as_dict(self):
         d = {n: getattr(self, n) for n, _ in self._fields_}

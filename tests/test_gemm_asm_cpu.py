@@ -38,7 +38,7 @@ def _device_asm(src):
         pytest.skip("hipcc not available")
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
-        flags = [f for f in build.HIP_FLAGS if f != "-fPIC"]
+        flags = [f for f in build.hip_flags(src) if f != "-fPIC"]
         subprocess.run([build.HIPCC] + flags + ["--cuda-device-only", "-S",
                                                 os.path.join(CSRC, src), "-o", out],
                        check=True, capture_output=True)

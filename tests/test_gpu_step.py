@@ -356,3 +356,78 @@ def test_chunked_mlp_kept_attention_internals_bitwise():
     base = _steps(s, w, ids, 2, keep_internals=0, **kw)
     kept = _steps(s, w, ids, 2, keep_internals=1, **kw)
     _same(base, kept, synth.param_names(s))
+
+
+# Hybrid 8-bit optimizer states and global-norm clipping (LazyTrain
+# abstract): the streamed step against the oracle's train_step_adam8.
+
+
+def _run8(shape, weights, batches, **run_kw):
+    torch, mt = _env()
+    m = mt.Model(shape, keep_grads=1, opt_8bit=1, **run_kw)
+    m.set_params(weights)
+    B, T = batches[0].shape
+    arena = torch.empty(m.arena_bytes(B, T), dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    losses, stats = [], []
+    for ids in batches:
+        loss, st = m.step(ids, arena, streams)
+        losses.append(loss)
+        stats.append(st)
+    names = synth.param_names(shape)
+    out = {"loss": losses, "stats": stats,
+           "grad": {n: m.get(n, mt.GET_GRAD) for n in names},
+           "master": {n: m.get(n, mt.GET_MASTER) for n in names},
+           "m": {n: m.get(n, mt.GET_M) for n in names},
+           "v": {n: m.get(n, mt.GET_V) for n in names}}
+    m.close()
+    return out
+
+
+@pytest.mark.parametrize("clip", [0.0, 0.05], ids=["no-clip", "clip"])
+def test_step_adam8_two_batches_match_oracle(tiny, clip):
+    """Two steps on different batches with the hybrid 8-bit states (and,
+    in the second case, a clipping norm below the gradient's norm, so every
+    gradient is scaled): loss, gradients, updated masters and the moments
+    the 8-bit states hold against the oracle; the clipping factor the step
+    reports against the oracle's."""
+    from oracle import adam8 as A8
+    s, w, ids1 = tiny
+    ids2 = synth.make_tokens(s, seed=77)
+    g = _run8(s, w, [ids1, ids2], clip_norm=clip)
+    l1, _, c1, p1, st1 = A8.train_step_adam8(w, ids1, s, max_norm=clip)
+    l2, g2, c2, p2, st2 = A8.train_step_adam8(p1, ids2, s, state=st1, step=2, max_norm=clip)
+    assert abs(g["loss"][0] - l1) < LOSS_TOL and abs(g["loss"][1] - l2) < LOSS_TOL
+    if clip:
+        assert c1 < 1 and c2 < 1  # clipping is active in both steps
+        for st, c in zip(g["stats"], (c1, c2)):
+            assert abs(st["clip_factor"] - c) / c < REL_TOL, (st["clip_factor"], c)
+    else:
+        assert all(st["clip_factor"] == 1.0 for st in g["stats"])
+    for n in synth.param_names(s):
+        assert rel(g["grad"][n], g2[n]) < REL_TOL, (n, rel(g["grad"][n], g2[n]))
+        assert rel(g["master"][n], p2[n]) < REL_TOL, n
+        m_ref = A8.dequantize(st2[n][0], st2[n][1]).reshape(w[n].shape)
+        r_ref = A8.dequantize(st2[n][2], st2[n][3]).reshape(w[n].shape)
+        assert rel(g["m"][n], m_ref) < 3 * REL_TOL, (n, rel(g["m"][n], m_ref))
+        assert rel(g["v"][n], r_ref * r_ref) < 3 * REL_TOL, (n, rel(g["v"][n], r_ref * r_ref))
+
+
+@pytest.mark.parametrize("kw", [dict(defer_updates=0), dict(serialize=1, ckpt_interval=2),
+                                dict(resident_layers=1), dict(use_slab_pool=0)],
+                         ids=["no-defer", "serialized-K2", "resident1", "no-pool"])
+def test_step_adam8_clip_schedule_invariance_bitwise(tiny, kw):
+    """The 8-bit states with clipping do not depend on the schedule: three
+    steps give bitwise the same losses, masters and moments."""
+    s, w, ids1 = tiny
+    batches = [ids1, synth.make_tokens(s, seed=78), synth.make_tokens(s, seed=79)]
+    run_kw = {k: v for k, v in kw.items() if k != "ckpt_interval"}
+    sh = s.with_(ckpt_interval=kw.get("ckpt_interval", s.ckpt_interval))
+    base = _run8(s, w, batches, clip_norm=0.05)
+    other = _run8(sh, w, batches, clip_norm=0.05, **run_kw)
+    assert base["loss"] == other["loss"]
+    assert [x["clip_factor"] for x in base["stats"]] == [x["clip_factor"] for x in other["stats"]]
+    for n in synth.param_names(s):
+        np.testing.assert_array_equal(base["master"][n], other["master"][n], err_msg=n)
+        np.testing.assert_array_equal(base["m"][n], other["m"][n], err_msg=n)
+        np.testing.assert_array_equal(base["v"][n], other["v"][n], err_msg=n)

@@ -181,3 +181,29 @@ def test_set_schedule_validates_and_keeps_fixed_knobs():
     with pytest.raises(mt.MTError):
         m.set_schedule(use_slab_pool=1)
     m.close()
+
+
+def test_opt_8bit_host_store_and_validation():
+    """A pageable model with 8-bit states: parameters round-trip, the moments
+    read back as zero after a set, the knob is fixed at creation, and
+    clipping refuses a slab pool too small to hold every gradient."""
+    import synth
+    mt = _mt()
+    s = synth.CONFIGS["tiny-2l-h256"]
+    m = mt.Model(s, host_alloc=mt.HOST_PAGEABLE, opt_8bit=1)
+    w = synth.make_weights(s, seed=9)
+    m.set_params(w)
+    for n in ("embed", "layers.1.w_k", "lm_head", "final_norm"):
+        np.testing.assert_array_equal(m.get(n), w[n])
+        assert not m.get(n, mt.GET_M).any() and not m.get(n, mt.GET_V).any()
+    with pytest.raises(mt.MTError):
+        m.set_schedule(opt_8bit=0)
+    m.set_schedule(clip_norm=1.0)  # 8 slabs >= 2 layers + head
+    m.close()
+    with pytest.raises(mt.MTError) as e:
+        mt.Model(s.with_(n_layers=9), host_alloc=mt.HOST_PAGEABLE, clip_norm=1.0)
+    assert e.value.status == mt.MT_E_INVALID
+    mt.Model(s.with_(n_layers=9), host_alloc=mt.HOST_PAGEABLE, clip_norm=1.0, n_slabs=10).close()
+    with pytest.raises(mt.MTError):  # hidden not a multiple of 128
+        mt.Model(s.with_(hidden=192, n_heads=3, n_kv_heads=1), host_alloc=mt.HOST_PAGEABLE,
+                 opt_8bit=1)
