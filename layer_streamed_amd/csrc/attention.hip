@@ -712,11 +712,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
   }
 }
 
+// dK and dV for head_dim 128 on v_mfma_f32_16x16x32_bf16: a workgroup of 8
+// waves owns 128 keys, 16 per wave, so a wave's live state (its keys' K and
+// V fragments, the dK/dV accumulators, one tile's scores) fits in half the
+// register file and two waves share each SIMD.  Per tile of 64 queries
+// (streamed into LDS as in the forward, double-buffered, one barrier per
+// tile) a wave forms S = Q K^T and dP = dO V^T as 16-query x 16-key blocks
+// (lane l: key l & 15, queries 4 (l >> 4) .. + 3 of the block), so each lane
+// holds 4 consecutive queries of every block.  For dV^T = dO^T P and
+// dK^T = Q^T dS, a 32-query k-step takes its B operand straight from those
+// registers: lane group g supplies queries 16 qb + 4g .. + 3 of the step's
+// two blocks qb as its 8 k-slots, and the A operand (dO^T, Q^T) is read in
+// the same permuted order with two LDS transpose reads (4 query rows each,
+// at the two blocks' rows 4g ..).  The summation order over queries is
+// therefore fixed: tiles in order, within a tile k-steps in order, slots in
+// that permutation.
 template <int D>
-__global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
   static_assert(D == 128, "rows of 16 chunks");
   constexpr int BQ = 64, CH = D / 8, TILE = BQ * D * 2, STAGE = 2 * TILE;
-  constexpr int PER = BQ * CH / 256;  // 16-byte load instructions per wave per operand
+  constexpr int NW = 8;                       // waves per workgroup
+  constexpr int PER = BQ * CH / (64 * NW);    // 16-byte loads per wave per operand
+  constexpr int NDB = D / 16;                 // 16-column blocks of d
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   float* sLb = reinterpret_cast<float*>(dsm + 2 * STAGE);  // [2][BQ]
   float* sDb = sLb + 2 * BQ;                               // [2][BQ]
@@ -727,27 +744,31 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
   const int rest = blockIdx.x % per;
   const int g = rest % a.Hkv, b = rest / a.Hkv;
   const int rep = a.Hq / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;  // lane in its 16-lane group, group
   const int k0 = kb * 128;
-  const int key = k0 + 32 * w + n;
+  const int kw = k0 + 16 * w;  // this wave's first key
+  const int key = kw + li;
   const long ldq = a.ldq;
   const uint16_t* base = a.qkv + (long)b * T * ldq;
   const uint16_t* dbase = a.dout + (long)b * T * a.ldo;
 
-  u32x4_t kf[D / 16], vf[D / 16];
+  // B operand of S and dP: key li, d-slots 32 ks + 8 lg .. + 7
+  u32x4_t kf[D / 32], vf[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
+  for (int ks = 0; ks < D / 32; ++ks) {
     const bool ok = key < T;
-    kf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + g) * D + ks * 16 + hh * 8)
+    kf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + g) * D + ks * 32 + lg * 8)
                 : u32x4_t{0, 0, 0, 0};
-    vf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + a.Hkv + g) * D + ks * 16 + hh * 8)
+    vf[ks] = ok ? *reinterpret_cast<const u32x4_t*>(base + (long)key * ldq + (a.Hq + a.Hkv + g) * D + ks * 32 + lg * 8)
                 : u32x4_t{0, 0, 0, 0};
   }
-  f32x16_t dk[D / 32], dv[D / 32];
+  // dK^T, dV^T blocks [16 d x 16 keys]: lane: key li, d = 16 db + 4 lg + i
+  f32x4_t dk[NDB], dv[NDB];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    zero16(dk[dt]);
-    zero16(dv[dt]);
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    dv[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   const int ntq = (T - k0 + BQ - 1) / BQ;  // query tiles from k0 to T
@@ -774,24 +795,23 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
     }
     if (tid < BQ) {
       const int q = qt0 + tid;
-      const long li = ((long)b * a.Hq + hq) * T + q;
-      lse_r = q < T ? a.lse[li] * LOG2E : -NEG;  // +1e30 makes P = 0 for padding rows
-      del_r = q < T ? a.delta[li] : 0.f;
+      const long lix = ((long)b * a.Hq + hq) * T + q;
+      lse_r = q < T ? a.lse[lix] * LOG2E : -NEG;  // +1e30 makes P = 0 for padding rows
+      del_r = q < T ? a.delta[lix] : 0.f;
     }
   };
 
-  // Transpose-read addresses: row & 7, and with it the swizzle, is the same
-  // for every (qt, jj, h) of a lane, so per lane only the column block dt
-  // varies the address beyond a constant; (32 qt + 16 jj + 8 h) rows of 256
-  // bytes and the dO tile's place go in the reads' immediate offsets.
-  uint32_t trb[D / 32];
+  // Transpose-read addresses of the A operand of dV^T / dK^T for column
+  // block db: the lane addresses query row 4 lg + (li >> 2) (plus the
+  // step's block offset, an immediate) and columns 16 db + 4 (li & 3);
+  // the row's low bits, hence its swizzle, are the same for every step.
+  uint32_t trb[NDB];
   {
-    const int i = lane & 15;
-    const int sw = dkdv_swz(4 * hh + (i >> 2));
+    const int row = 4 * lg + (li >> 2);
+    const int sw = dkdv_swz(row);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      trb[dt] = (4 * hh + (i >> 2)) * 256 +
-                (((4 * dt + 2 * ((lane >> 4) & 1) + ((i >> 1) & 1)) ^ sw) << 4) + (i & 1) * 8;
+    for (int db = 0; db < NDB; ++db)
+      trb[db] = row * 256 + (((2 * db + ((li >> 1) & 1)) ^ sw) << 4) + (li & 1) * 8;
   }
 
   issue(0, 0);
@@ -812,90 +832,97 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
     const char* sdo = sq + TILE;
     const float* sL = sLb + buf * BQ;
     const float* sDl = sDb + buf * BQ;
-    const bool active = qt0 + BQ - 1 >= k0 + 32 * w;  // some query of the tile sees this wave's keys
-    f32x16_t sacc[2], dpacc[2];
+    // some query of the tile sees this wave's first key
+    const bool active = qt0 + BQ - 1 >= kw;
     if (active) {
-      // S and dP: the row reads of step ks+1 are issued before the MFMAs of
-      // step ks (lgkmcnt(2) then leaves only those two in flight; LDS reads
-      // return in order), so a lone wave does not wait a full LDS round
-      // trip per MFMA pair; the last step drains every read
+      // S and dP, blocks qb of 16 queries: A = Q / dO rows 16 qb + li at
+      // d-slots 32 ks + 8 lg (one row read each), B = K / V fragments.  The
+      // row reads of step s+1 go out before the MFMAs of step s.
+      f32x4_t sacc[BQ / 16], dpacc[BQ / 16];
+      constexpr int NS1 = (BQ / 16) * (D / 32);
+      u32x4_t Aq[2], Ad[2];
+      Aq[0] = lds_row16(sq, li, lg);
+      Ad[0] = lds_row16(sdo, li, lg);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        zero16(sacc[qt]);
-        zero16(dpacc[qt]);
-        u32x4_t Aq[2], Ad[2];
-        Aq[0] = lds_row16(sq, 32 * qt + n, hh);
-        Ad[0] = lds_row16(sdo, 32 * qt + n, hh);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const int c = ks & 1;
-          if (ks + 1 < D / 16) {
-            Aq[c ^ 1] = lds_row16(sq, 32 * qt + n, 2 * (ks + 1) + hh);
-            Ad[c ^ 1] = lds_row16(sdo, 32 * qt + n, 2 * (ks + 1) + hh);
-            asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
-          } else {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          }
-          asm volatile("" : "+v"(Aq[c]));
-          asm volatile("" : "+v"(Ad[c]));
-          sacc[qt] = mfma32(Aq[c], kf[ks], sacc[qt]);
-          dpacc[qt] = mfma32(Ad[c], vf[ks], dpacc[qt]);
+      for (int s = 0; s < NS1; ++s) {
+        const int qb = s / (D / 32), ks = s % (D / 32), c = s & 1;
+        if (ks == 0) {
+          sacc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          dpacc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+        if (s + 1 < NS1) {
+          const int qn = (s + 1) / (D / 32), kn = (s + 1) % (D / 32);
+          Aq[c ^ 1] = lds_row16(sq, 16 * qn + li, 4 * kn + lg);
+          Ad[c ^ 1] = lds_row16(sdo, 16 * qn + li, 4 * kn + lg);
+          asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        asm volatile("" : "+v"(Aq[c]));
+        asm volatile("" : "+v"(Ad[c]));
+        sacc[qb] = mfma16x32(Aq[c], kf[ks], sacc[qb]);
+        dpacc[qb] = mfma16x32(Ad[c], vf[ks], dpacc[qb]);
       }
-      // P and dS, rows = queries (qt0 + 32qt + 8j + 4hh + i), column = key;
-      // the causal mask only where some query of the tile precedes one of
-      // this wave's keys (a wave-uniform test)
+      // P and dS: lane holds key li and queries 16 qb + 4 lg + i; the
+      // causal mask only where some query of the tile precedes one of this
+      // wave's keys (a wave-uniform test)
       auto p_ds = [&](auto masked) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qb = 0; qb < BQ / 16; ++qb) {
+          const f32x4_t L4 = *reinterpret_cast<const f32x4_t*>(sL + 16 * qb + 4 * lg);
+          const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(sDl + 16 * qb + 4 * lg);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int qi = 32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3);
-            float p = exp2_hw(sacc[qt][e] * a.scale_log2 - sL[qi]);
-            if (decltype(masked)::value && key > qt0 + qi) p = 0.f;
-            sacc[qt][e] = p;
-            dpacc[qt][e] = p * (dpacc[qt][e] - sDl[qi]);
+          for (int i = 0; i < 4; ++i) {
+            float p = exp2_hw(sacc[qb][i] * a.scale_log2 - L4[i]);
+            if (decltype(masked)::value && key > qt0 + 16 * qb + 4 * lg + i) p = 0.f;
+            sacc[qb][i] = p;
+            dpacc[qb][i] = p * (dpacc[qb][i] - D4[i]);
           }
+        }
       };
-      if (qt0 < k0 + 32 * w + 31)
+      if (qt0 < kw + 15)
         p_ds(std::true_type{});
       else
         p_ds(std::false_type{});
-    }
-    if (active) {
-      // dV and dK over steps i = (qt, jj, dt) in the same order as a plain
-      // nested loop: the four transpose reads of step i+1 go out before the
-      // MFMAs of step i (lgkmcnt(4) leaves only those in flight)
-      constexpr int NI = 2 * 2 * (D / 32);
-      u32x4_t At[2], Aq[2];
-      u32x4_t Pb = {0, 0, 0, 0}, Sb = {0, 0, 0, 0};
+      // dV^T and dK^T over steps (qc, db), qc the 32-query k-step: B is
+      // P / dS of blocks 2 qc and 2 qc + 1 packed in that slot order; A the
+      // dO^T / Q^T fragment of column block db at those rows (two transpose
+      // reads each).  The reads of step s+1 go out before the MFMAs of s.
+      constexpr int NS3 = (BQ / 32) * NDB;
       const uint32_t sqa = lds_addr(sq);
-      auto reads = [&](int i, int slot) {
-        const int qt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
-        const int ro = (32 * qt + 16 * jj) * 256;
-        const uint32_t ad = sqa + trb[dt];
-        At[slot] = lds_tr_pair(ad, TILE + ro, TILE + ro + 8 * 256);
-        Aq[slot] = lds_tr_pair(ad, ro, ro + 8 * 256);
+      u32x4_t At[2], Aq2[2];
+      auto reads = [&](int s, int slot) {
+        const int qc = s / NDB, db = s % NDB;
+        const int ro = 32 * qc * 256;
+        const uint32_t ad = sqa + trb[db];
+        At[slot] = lds_tr_pair(ad, TILE + ro, TILE + ro + 16 * 256);
+        Aq2[slot] = lds_tr_pair(ad, ro, ro + 16 * 256);
       };
+      u32x4_t Pb = {0, 0, 0, 0}, Sb = {0, 0, 0, 0};
       reads(0, 0);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int qt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
-        const int c = i & 1;
-        if (dt == 0) {
-          Pb = pack_p(sacc[qt], jj);
-          Sb = pack_p(dpacc[qt], jj);
+      for (int s = 0; s < NS3; ++s) {
+        const int qc = s / NDB, db = s % NDB, c = s & 1;
+        if (db == 0) {
+          Pb = u32x4_t{pack_bf(sacc[2 * qc][0], sacc[2 * qc][1]),
+                       pack_bf(sacc[2 * qc][2], sacc[2 * qc][3]),
+                       pack_bf(sacc[2 * qc + 1][0], sacc[2 * qc + 1][1]),
+                       pack_bf(sacc[2 * qc + 1][2], sacc[2 * qc + 1][3])};
+          Sb = u32x4_t{pack_bf(dpacc[2 * qc][0], dpacc[2 * qc][1]),
+                       pack_bf(dpacc[2 * qc][2], dpacc[2 * qc][3]),
+                       pack_bf(dpacc[2 * qc + 1][0], dpacc[2 * qc + 1][1]),
+                       pack_bf(dpacc[2 * qc + 1][2], dpacc[2 * qc + 1][3])};
         }
-        if (i + 1 < NI) {
-          reads(i + 1, c ^ 1);
+        if (s + 1 < NS3) {
+          reads(s + 1, c ^ 1);
           asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
         } else {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         asm volatile("" : "+v"(At[c]));
-        asm volatile("" : "+v"(Aq[c]));
-        dv[dt] = mfma32(At[c], Pb, dv[dt]);
-        dk[dt] = mfma32(Aq[c], Sb, dk[dt]);
+        asm volatile("" : "+v"(Aq2[c]));
+        dv[db] = mfma16x32(At[c], Pb, dv[db]);
+        dk[db] = mfma16x32(Aq2[c], Sb, dk[db]);
       }
     }
     if (it + 1 < nit) {
@@ -911,18 +938,16 @@ __global__ __launch_bounds__(256) void attn_dkdv_dl_kernel(const AttnArgs a) {
   if (key < T) {
     uint16_t* drow = a.dqkv + ((long)b * T + key) * ldq;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * dt + 8 * j + 4 * hh;
-        u32x2_t vk, vv;
-        vk.x = pack_bf(dk[dt][4 * j] * a.scale, dk[dt][4 * j + 1] * a.scale);
-        vk.y = pack_bf(dk[dt][4 * j + 2] * a.scale, dk[dt][4 * j + 3] * a.scale);
-        vv.x = pack_bf(dv[dt][4 * j], dv[dt][4 * j + 1]);
-        vv.y = pack_bf(dv[dt][4 * j + 2], dv[dt][4 * j + 3]);
-        *reinterpret_cast<u32x2_t*>(drow + (a.Hq + g) * D + d) = vk;
-        *reinterpret_cast<u32x2_t*>(drow + (a.Hq + a.Hkv + g) * D + d) = vv;
-      }
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 16 * db + 4 * lg;
+      u32x2_t vk, vv;
+      vk.x = pack_bf(dk[db][0] * a.scale, dk[db][1] * a.scale);
+      vk.y = pack_bf(dk[db][2] * a.scale, dk[db][3] * a.scale);
+      vv.x = pack_bf(dv[db][0], dv[db][1]);
+      vv.y = pack_bf(dv[db][2], dv[db][3]);
+      *reinterpret_cast<u32x2_t*>(drow + (a.Hq + g) * D + d) = vk;
+      *reinterpret_cast<u32x2_t*>(drow + (a.Hq + a.Hkv + g) * D + d) = vv;
+    }
   }
 }
 
@@ -1271,7 +1296,7 @@ hipError_t bwd_d(const AttnArgs& a, int stages, hipStream_t s) {
   if (stages & ATTN_BWD_DKDV) {
     const int nkb = (a.T + 127) / 128;
     if constexpr (D == 128)
-      hipLaunchKernelGGL(attn_dkdv_dl_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_dl, s, a);
+      hipLaunchKernelGGL(attn_dkdv_dl_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(512), lds_dl, s, a);
     else
       hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nkb * a.Hkv * a.B), dim3(256), lds_kv, s, a);
     const hipError_t e = hipGetLastError();

@@ -51,6 +51,13 @@ __device__ inline f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16: lane l supplies row (column) l % 16 of A (B)
+// at k-slots 8 (l / 16) .. + 7; the 16 x 16 fp32 result: lane l holds
+// column l % 16, rows 4 (l / 16) .. + 3.
+__device__ inline f32x4_t mfma16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 // Wave-level reductions over all 64 lanes (butterfly via ds_swizzle-free shuffles).
 __device__ inline float wave_sum(float v) {
 #pragma unroll
