@@ -12,10 +12,11 @@
 //    old moments and the gradient times the clipping factor, and the new
 //    moments are quantized afterwards; the fp32 master stays fp32.
 // Compiled with -ffp-contract=off: every fp32 operation is rounded as
-// written, so the scalar and AVX2 paths agree bit for bit with a plain fp32
-// evaluation of the same operations.
+// written, so the scalar, AVX2 and AVX-512 paths agree bit for bit with a
+// plain fp32 evaluation of the same operations.
 #include <immintrin.h>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -113,6 +114,23 @@ void adam8_block_scalar(const Adam8Arrays& A, size_t off, int n, size_t b, const
   A.rs[b] = quant_block(rb, n, A.rq + off);
 }
 
+// ---- vector forms of one full block: the same operations in the same order
+// as adam8_block_scalar, so every form gives the scalar one's bits.
+
+// fp32 -> bf16 bits, round to nearest even, NaN -> quiet NaN with the sign
+inline __m256i bf16_bits8(__m256 p) {
+  const __m256i u = _mm256_castps_si256(p);
+  const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(1));
+  const __m256i rn =
+      _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, _mm256_set1_epi32(0x7FFF)), lsb), 16);
+  const __m256i qn = _mm256_or_si256(
+      _mm256_and_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(0x8000)),
+      _mm256_set1_epi32(0x7FC0));
+  const __m256i isnan = _mm256_cmpgt_epi32(_mm256_and_si256(u, _mm256_set1_epi32(0x7FFFFFFF)),
+                                           _mm256_set1_epi32(0x7F800000));
+  return _mm256_blendv_epi8(rn, qn, isnan);
+}
+
 // E4M3 of 8 fp32 lanes (the same decision as e4m3_encode), as 8 x 32-bit.
 inline __m256i enc8(__m256 y) {
   const __m256i u = _mm256_castps_si256(y);
@@ -144,16 +162,22 @@ inline __m256 dec8(const uint8_t* c, __m256 scale) {
   return _mm256_mul_ps(_mm256_castsi256_ps(_mm256_or_si256(mag, sign)), scale);
 }
 
-// 8 x 32-bit codes (each < 256) -> 8 bytes
+// 8 x 32-bit values (each < 65536) -> 8 x 16-bit, and (each < 256) -> 8 bytes
+inline __m128i narrow16(__m256i c) {
+  return _mm_packus_epi32(_mm256_castsi256_si128(c), _mm256_extracti128_si256(c, 1));
+}
 inline void store8codes(uint8_t* dst, __m256i c) {
-  const __m128i lo = _mm256_castsi256_si128(c), hi = _mm256_extracti128_si256(c, 1);
-  const __m128i w = _mm_packus_epi32(lo, hi);      // 8 x 16
-  const __m128i b = _mm_packus_epi16(w, w);        // 16 x 8 (first 8 used)
-  _mm_storel_epi64(reinterpret_cast<__m128i*>(dst), b);
+  const __m128i w = narrow16(c);
+  _mm_storel_epi64(reinterpret_cast<__m128i*>(dst), _mm_packus_epi16(w, w));
 }
 
-// One full block, bf16 gradient and bf16 streamed copy: AVX2, the same
-// operations in the same order as adam8_block_scalar.
+// Scale of a block from its largest magnitude, and the factor that maps the
+// block onto [-448, 448] (0 for an all-zero block: every code is then 0).
+inline float block_scale(float amax) { return amax == 0.f ? 0.f : amax / 448.f; }
+inline float block_factor(float amax) { return amax == 0.f ? 0.f : 448.f / amax; }
+
+// One full block with 8-wide AVX2.
+template <bool BF16_GRAD, int SHADOW>
 void adam8_block_avx2(const Adam8Arrays& A, size_t off, size_t b, const AdamHp& h, float clip) {
   alignas(32) float mb[ADAM8_BLOCK], rb[ADAM8_BLOCK];
   const __m256 b1 = _mm256_set1_ps(h.b1), omb1 = _mm256_set1_ps(h.omb1);
@@ -162,13 +186,17 @@ void adam8_block_avx2(const Adam8Arrays& A, size_t off, size_t b, const AdamHp& 
   const __m256 lr = _mm256_set1_ps(h.lr), eps = _mm256_set1_ps(h.eps);
   const __m256 cl = _mm256_set1_ps(clip);
   const __m256 ms = _mm256_set1_ps(A.ms[b]), rs = _mm256_set1_ps(A.rs[b]);
-  const __m256i round = _mm256_set1_epi32(0x7FFF), one = _mm256_set1_epi32(1);
   const __m256 absf = _mm256_castsi256_ps(_mm256_set1_epi32(0x7FFFFFFF));
   __m256 am = _mm256_setzero_ps(), ar = _mm256_setzero_ps();
   for (int j = 0; j < ADAM8_BLOCK; j += 8) {
     const size_t k = off + j;
-    const __m128i g16 = _mm_loadu_si128(reinterpret_cast<const __m128i*>(A.gb + k));
-    __m256 g = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(g16), 16));
+    __m256 g;
+    if constexpr (BF16_GRAD) {
+      const __m128i g16 = _mm_loadu_si128(reinterpret_cast<const __m128i*>(A.gb + k));
+      g = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(g16), 16));
+    } else {
+      g = _mm256_loadu_ps(A.gf + k);
+    }
     g = _mm256_mul_ps(g, cl);
     const __m256 m_old = dec8(A.mq + k, ms);
     const __m256 r_old = dec8(A.rq + k, rs);
@@ -181,18 +209,10 @@ void adam8_block_avx2(const Adam8Arrays& A, size_t off, size_t b, const AdamHp& 
         _mm256_loadu_ps(A.p + k),
         _mm256_div_ps(_mm256_mul_ps(lr, mh), _mm256_add_ps(_mm256_sqrt_ps(vh), eps)));
     _mm256_storeu_ps(A.p + k, p);
-    // fp32 -> bf16 round to nearest even, NaN -> quiet NaN with the sign
-    const __m256i u = _mm256_castps_si256(p);
-    const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), one);
-    const __m256i rn = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, round), lsb), 16);
-    const __m256i qn = _mm256_or_si256(
-        _mm256_and_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(0x8000)),
-        _mm256_set1_epi32(0x7FC0));
-    const __m256i isnan = _mm256_cmpgt_epi32(_mm256_and_si256(u, _mm256_set1_epi32(0x7FFFFFFF)),
-                                             _mm256_set1_epi32(0x7F800000));
-    const __m256i bf = _mm256_blendv_epi8(rn, qn, isnan);
-    const __m256i packed = _mm256_permute4x64_epi64(_mm256_packus_epi32(bf, bf), 0x08);
-    _mm_storeu_si128(reinterpret_cast<__m128i*>(A.sb + k), _mm256_castsi256_si128(packed));
+    if constexpr (SHADOW == 1)
+      _mm_storeu_si128(reinterpret_cast<__m128i*>(A.sb + k), narrow16(bf16_bits8(p)));
+    else if constexpr (SHADOW == 2)
+      _mm256_storeu_ps(A.sf + k, p);
     const __m256 r = _mm256_sqrt_ps(v);
     _mm256_store_ps(mb + j, m);
     _mm256_store_ps(rb + j, r);
@@ -200,39 +220,163 @@ void adam8_block_avx2(const Adam8Arrays& A, size_t off, size_t b, const AdamHp& 
     ar = _mm256_max_ps(ar, r);
   }
   // horizontal maxima (max is exact: the order does not matter)
-  float t[8];
-  _mm256_storeu_ps(t, am);
+  alignas(32) float t[8];
+  _mm256_store_ps(t, am);
   float amax_m = 0.f;
   for (int i = 0; i < 8; ++i) amax_m = std::max(amax_m, t[i]);
-  _mm256_storeu_ps(t, ar);
+  _mm256_store_ps(t, ar);
   float amax_r = 0.f;
   for (int i = 0; i < 8; ++i) amax_r = std::max(amax_r, t[i]);
-  A.ms[b] = amax_m == 0.f ? 0.f : amax_m / 448.f;
-  A.rs[b] = amax_r == 0.f ? 0.f : amax_r / 448.f;
-  const __m256 im = _mm256_set1_ps(amax_m == 0.f ? 0.f : 448.f / amax_m);
-  const __m256 ir = _mm256_set1_ps(amax_r == 0.f ? 0.f : 448.f / amax_r);
+  A.ms[b] = block_scale(amax_m);
+  A.rs[b] = block_scale(amax_r);
+  const __m256 im = _mm256_set1_ps(block_factor(amax_m));
+  const __m256 ir = _mm256_set1_ps(block_factor(amax_r));
   for (int j = 0; j < ADAM8_BLOCK; j += 8) {
     const size_t k = off + j;
-    // an all-zero block: factor 0 gives code 0 for every (zero) value
     store8codes(A.mq + k, enc8(_mm256_mul_ps(_mm256_load_ps(mb + j), im)));
     store8codes(A.rq + k, enc8(_mm256_mul_ps(_mm256_load_ps(rb + j), ir)));
   }
 }
 
+// ---- 16-wide AVX-512 (chosen at run time where the CPU has it): the
+// block's new moments stay in registers between the update and the
+// quantization.
+#define MT_AVX512 __attribute__((target("avx512f,avx512bw,avx512vl,avx512dq")))
+
+MT_AVX512 inline __m512i bf16_bits16(__m512 p) {
+  const __m512i u = _mm512_castps_si512(p);
+  const __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(u, 16), _mm512_set1_epi32(1));
+  const __m512i rn =
+      _mm512_srli_epi32(_mm512_add_epi32(_mm512_add_epi32(u, _mm512_set1_epi32(0x7FFF)), lsb), 16);
+  const __m512i qn = _mm512_or_si512(
+      _mm512_and_si512(_mm512_srli_epi32(u, 16), _mm512_set1_epi32(0x8000)),
+      _mm512_set1_epi32(0x7FC0));
+  const __mmask16 isnan = _mm512_cmpgt_epi32_mask(
+      _mm512_and_si512(u, _mm512_set1_epi32(0x7FFFFFFF)), _mm512_set1_epi32(0x7F800000));
+  return _mm512_mask_blend_epi32(isnan, rn, qn);
+}
+
+MT_AVX512 inline __m512i enc16(__m512 y) {
+  const __m512i u = _mm512_castps_si512(y);
+  const __m512i a = _mm512_and_si512(u, _mm512_set1_epi32(0x7FFFFFFF));
+  const __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(a, 20), _mm512_set1_epi32(1));
+  __m512i tn = _mm512_sub_epi32(
+      _mm512_srli_epi32(_mm512_add_epi32(_mm512_add_epi32(a, _mm512_set1_epi32(0x7FFFF)), lsb), 20),
+      _mm512_set1_epi32(960));
+  tn = _mm512_min_epi32(tn, _mm512_set1_epi32(0x7E));
+  const __m512i ts = _mm512_cvtps_epi32(_mm512_mul_ps(_mm512_castsi512_ps(a), _mm512_set1_ps(512.f)));
+  const __mmask16 normal = _mm512_cmpgt_epi32_mask(a, _mm512_set1_epi32(0x3C7FFFFF));
+  const __m512i code = _mm512_mask_blend_epi32(normal, ts, tn);
+  return _mm512_or_si512(code, _mm512_and_si512(_mm512_srli_epi32(u, 24), _mm512_set1_epi32(0x80)));
+}
+
+MT_AVX512 inline __m512 dec16(const uint8_t* c, __m512 scale) {
+  const __m512i k = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(c)));
+  const __m512i sign = _mm512_slli_epi32(_mm512_and_si512(k, _mm512_set1_epi32(0x80)), 24);
+  const __m512i em = _mm512_and_si512(k, _mm512_set1_epi32(0x7F));
+  const __m512i nrm = _mm512_add_epi32(_mm512_slli_epi32(em, 20), _mm512_set1_epi32(120 << 23));
+  const __m512 sub = _mm512_mul_ps(_mm512_cvtepi32_ps(em), _mm512_set1_ps(1.f / 512.f));
+  const __mmask16 is_sub = _mm512_cmpgt_epi32_mask(_mm512_set1_epi32(8), em);
+  const __m512i mag = _mm512_mask_blend_epi32(is_sub, nrm, _mm512_castps_si512(sub));
+  return _mm512_mul_ps(_mm512_castsi512_ps(_mm512_or_si512(mag, sign)), scale);
+}
+
+template <bool BF16_GRAD, int SHADOW>
+MT_AVX512 void adam8_block_avx512(const Adam8Arrays& A, size_t off, size_t b, const AdamHp& h,
+                                  float clip) {
+  constexpr int NV = ADAM8_BLOCK / 16;
+  __m512 mv[NV], rv[NV];
+  const __m512 b1 = _mm512_set1_ps(h.b1), omb1 = _mm512_set1_ps(h.omb1);
+  const __m512 b2 = _mm512_set1_ps(h.b2), omb2 = _mm512_set1_ps(h.omb2);
+  const __m512 bc1 = _mm512_set1_ps(h.bc1), bc2 = _mm512_set1_ps(h.bc2);
+  const __m512 lr = _mm512_set1_ps(h.lr), eps = _mm512_set1_ps(h.eps);
+  const __m512 cl = _mm512_set1_ps(clip);
+  const __m512 ms = _mm512_set1_ps(A.ms[b]), rs = _mm512_set1_ps(A.rs[b]);
+  __m512 am = _mm512_setzero_ps(), ar = _mm512_setzero_ps();
+#pragma GCC unroll 8
+  for (int j = 0; j < NV; ++j) {
+    const size_t k = off + 16 * j;
+    __m512 g;
+    if constexpr (BF16_GRAD) {
+      const __m256i g16 = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(A.gb + k));
+      g = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(g16), 16));
+    } else {
+      g = _mm512_loadu_ps(A.gf + k);
+    }
+    g = _mm512_mul_ps(g, cl);
+    const __m512 m_old = dec16(A.mq + k, ms);
+    const __m512 r_old = dec16(A.rq + k, rs);
+    const __m512 v_old = _mm512_mul_ps(r_old, r_old);
+    const __m512 m = _mm512_add_ps(_mm512_mul_ps(b1, m_old), _mm512_mul_ps(omb1, g));
+    const __m512 v = _mm512_add_ps(_mm512_mul_ps(b2, v_old), _mm512_mul_ps(omb2, _mm512_mul_ps(g, g)));
+    const __m512 mh = _mm512_div_ps(m, bc1);
+    const __m512 vh = _mm512_div_ps(v, bc2);
+    const __m512 p = _mm512_sub_ps(
+        _mm512_loadu_ps(A.p + k),
+        _mm512_div_ps(_mm512_mul_ps(lr, mh), _mm512_add_ps(_mm512_sqrt_ps(vh), eps)));
+    _mm512_storeu_ps(A.p + k, p);
+    if constexpr (SHADOW == 1)
+      _mm256_storeu_si256(reinterpret_cast<__m256i*>(A.sb + k), _mm512_cvtepi32_epi16(bf16_bits16(p)));
+    else if constexpr (SHADOW == 2)
+      _mm512_storeu_ps(A.sf + k, p);
+    mv[j] = m;
+    rv[j] = _mm512_sqrt_ps(v);
+    am = _mm512_max_ps(am, _mm512_abs_ps(m));
+    ar = _mm512_max_ps(ar, rv[j]);
+  }
+  const float amax_m = _mm512_reduce_max_ps(am), amax_r = _mm512_reduce_max_ps(ar);
+  A.ms[b] = block_scale(amax_m);
+  A.rs[b] = block_scale(amax_r);
+  const __m512 im = _mm512_set1_ps(block_factor(amax_m));
+  const __m512 ir = _mm512_set1_ps(block_factor(amax_r));
+#pragma GCC unroll 8
+  for (int j = 0; j < NV; ++j) {
+    const size_t k = off + 16 * j;
+    _mm_storeu_si128(reinterpret_cast<__m128i*>(A.mq + k),
+                     _mm512_cvtepi32_epi8(enc16(_mm512_mul_ps(mv[j], im))));
+    _mm_storeu_si128(reinterpret_cast<__m128i*>(A.rq + k),
+                     _mm512_cvtepi32_epi8(enc16(_mm512_mul_ps(rv[j], ir))));
+  }
+}
+
+// ---- dispatch: the widest form this CPU runs (MT_HOST_SIMD=avx2 or
+// scalar forces a narrower one), chosen once.
+enum Simd { SIMD_SCALAR, SIMD_AVX2, SIMD_AVX512 };
+
+Simd detect_simd() {
+  Simd s = SIMD_SCALAR;
+  if (__builtin_cpu_supports("avx2")) s = SIMD_AVX2;
+  if (s == SIMD_AVX2 && __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+      __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("avx512dq"))
+    s = SIMD_AVX512;
+  if (const char* e = getenv("MT_HOST_SIMD")) {
+    if (!strcmp(e, "scalar")) s = SIMD_SCALAR;
+    else if (!strcmp(e, "avx2") && s > SIMD_AVX2) s = SIMD_AVX2;
+  }
+  return s;
+}
+const Simd kSimd = detect_simd();
+
+template <bool BF16_GRAD, int SHADOW>
+inline void adam8_block_t(const Adam8Arrays& A, size_t off, int n, size_t b, const AdamHp& h,
+                          float clip) {
+  if (n == ADAM8_BLOCK && kSimd == SIMD_AVX512)
+    adam8_block_avx512<BF16_GRAD, SHADOW>(A, off, b, h, clip);
+  else if (n == ADAM8_BLOCK && kSimd == SIMD_AVX2)
+    adam8_block_avx2<BF16_GRAD, SHADOW>(A, off, b, h, clip);
+  else
+    adam8_block_scalar<BF16_GRAD, SHADOW>(A, off, n, b, h, clip);
+}
+
 void adam8_block(const Adam8Arrays& A, size_t off, int n, size_t b, const AdamHp& h, float clip) {
   if (A.gb) {
-    if (A.sb) {
-      if (n == ADAM8_BLOCK) adam8_block_avx2(A, off, b, h, clip);
-      else adam8_block_scalar<true, 1>(A, off, n, b, h, clip);
-    } else if (A.sf) {
-      adam8_block_scalar<true, 2>(A, off, n, b, h, clip);
-    } else {
-      adam8_block_scalar<true, 0>(A, off, n, b, h, clip);
-    }
+    if (A.sb) adam8_block_t<true, 1>(A, off, n, b, h, clip);
+    else if (A.sf) adam8_block_t<true, 2>(A, off, n, b, h, clip);
+    else adam8_block_t<true, 0>(A, off, n, b, h, clip);
   } else {
-    if (A.sb) adam8_block_scalar<false, 1>(A, off, n, b, h, clip);
-    else if (A.sf) adam8_block_scalar<false, 2>(A, off, n, b, h, clip);
-    else adam8_block_scalar<false, 0>(A, off, n, b, h, clip);
+    if (A.sb) adam8_block_t<false, 1>(A, off, n, b, h, clip);
+    else if (A.sf) adam8_block_t<false, 2>(A, off, n, b, h, clip);
+    else adam8_block_t<false, 0>(A, off, n, b, h, clip);
   }
 }
 

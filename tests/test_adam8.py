@@ -176,3 +176,19 @@ def test_host_adam8_validates_and_refuses_nonfinite():
         assert status == mt.MT_E_INVALID
     status, *_ = _lib_step(p, st, np.ones(n, np.float32), 0, 1.0, mt.DT_F32, False, 2)
     assert status == mt.MT_E_INVALID
+
+
+@pytest.mark.parametrize("simd", ["avx2", "scalar"])
+def test_host_adam8_narrower_simd_paths_bitwise(simd):
+    """The library takes the widest vector form the CPU has; MT_HOST_SIMD
+    forces the narrower ones, which must give the same bits (the bitwise
+    test above, in a fresh process with the variable set)."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ, MT_HOST_SIMD=simd)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", "-k",
+                        "test_host_adam8_bitwise_equals_oracle", __file__],
+                       env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "8 passed" in r.stdout, r.stdout[-500:]
