@@ -362,15 +362,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
 // so no operand passes through registers on its way in.  A ring of NS
 // stages of BK k-values keeps NS - 1 stages of loads in flight while one is
 // computed: the load latency is covered by LDS capacity instead of
-// registers.  Two shapes of the 128 KiB ring are used: 4 stages of 32 k and
-// 2 stages of 64 k (half the stage barriers; the better one per layout was
-// measured on the 7B layer shapes, see launch_layout).
+// registers.  Two shapes of the 128 KiB ring exist: 2 stages of 64 k (half
+// the stage barriers; used whenever K % 64 == 0, see deep_stages) and 4
+// stages of 32 k (K % 64 == 32).
 //
 // Each operand keeps its global layout in LDS:
 //  - K-contiguous (NT's A and B, NN's A): a stage is BM rows of BK k, BK / 8
-//    chunks of 8 per row stored in the order c ^ ((row >> 2) & (BK / 8 - 1));
-//    a fragment (8 consecutive k of one row per lane) is one ds_read_b128,
-//    and 32 lanes reading 32 consecutive rows hit distinct banks.
+//    chunks of 8 per row stored in the order c ^ kc_swz(row); a fragment (8
+//    consecutive k of one row per lane) is one ds_read_b128.  The LDS serves
+//    such a read 16 lanes (256 bytes, all 64 banks) at a time, and those 16
+//    lanes read one chunk of 16 consecutive rows: kc_swz XORs the chunk with
+//    the row's index among the rows sharing a 256-byte line (row / 2 for
+//    128-byte rows, row / 4 for 64-byte rows), so the 16 chunks land on 16
+//    distinct 4-bank groups.  (An XOR with row / 4 for 128-byte rows would
+//    put rows r and r + 2 on the same banks and double each read's cycles.)
 //  - K-major (NN's B, TN's A and B): a stage is BK rows of k, each BM
 //    values of m wide (BM / 8 chunks) stored in the order c ^ km_swz(k).
 //    A fragment is read with two ds_read_b64_tr_b16 (gfx950 LDS transpose
@@ -391,6 +396,12 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int km_swz(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }
 
+template <int CH>
+__device__ __forceinline__ int kc_swz(int row) {
+  static_assert(CH == 4 || CH == 8, "K-contiguous rows of 32 or 64 k");
+  return (row / (16 / CH)) & (CH - 1);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -405,7 +416,7 @@ __device__ __forceinline__ const uint16_t* dl_src(const uint16_t* base, long ld,
   if constexpr (!KM) {
     constexpr int CH = BK / 8;
     const int row = pos / CH, slot = pos % CH;
-    const int c = slot ^ ((row >> 2) & (CH - 1));
+    const int c = slot ^ kc_swz<CH>(row);
     int gr = min(r0 + row, ext - 1);
     if (swi_f) gr = SwiMap{swi_f}(gr);
     return base + (long)gr * ld + c * 8;
@@ -426,7 +437,7 @@ __device__ __forceinline__ u32x4_t dl_frag(const char* st, int rb, int ks, int l
     constexpr int CH = BK / 8;
     const int r = rb + (lane & 31);
     const int c = ks * 2 + (lane >> 5);
-    return reinterpret_cast<const u32x4_t*>(st)[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
+    return reinterpret_cast<const u32x4_t*>(st)[r * CH + (c ^ kc_swz<CH>(r))];
   } else {
     constexpr int RC = BR / 8;
     const int grp = lane >> 4, i = lane & 15;
@@ -460,7 +471,7 @@ __device__ __forceinline__ u32x4_t dl_frag16(const char* st, int rb, int ks, int
     constexpr int CH = BK / 8;
     const int r = rb + (lane & 15);
     const int c = ks * 4 + (lane >> 4);
-    return reinterpret_cast<const u32x4_t*>(st)[r * CH + (c ^ ((r >> 2) & (CH - 1)))];
+    return reinterpret_cast<const u32x4_t*>(st)[r * CH + (c ^ kc_swz<CH>(r))];
   } else {
     constexpr int RC = BR / 8;
     const int grp = lane >> 4, i = lane & 15;
@@ -677,7 +688,7 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 // MI selects the MFMA: 32 (v_mfma_f32_32x32x16_bf16, 16-deep substeps) or
 // 16 (v_mfma_f32_16x16x32_bf16, 32-deep substeps, each 32 x 32 block of
 // the wave tile as four 16 x 16 blocks).  The two give bitwise equal
-// products; which is faster depends on the layout (see launch_layout).
+// products; dl_mfma picks the one the library runs.
 template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI, int BK, int NS, int MI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) {
   static_assert(BK % 32 == 0 && BK <= 64 && NS >= 2 && NS <= 4, "stage shape");
@@ -1042,16 +1053,17 @@ TileCfg choose_cfg(const GemmArgs& a) {
   return RS_128x128;
 }
 
-// Stage shape of the direct-to-LDS kernels: 2 stages of 64 k for NT (every
-// tile) and for TN's 256 x 256 tile when K allows, else 4 stages of 32 k
-// (NN, where the deeper ring measured faster, and the smaller TN tiles).
-inline bool deep_stages(const GemmArgs& a, int layout, TileCfg c) {
-  return a.K % 64 == 0 && (layout == GEMM_NT || (layout == GEMM_TN && c == DL_256x256));
-}
+// Stage shape of the direct-to-LDS kernels: 2 stages of 64 k whenever K
+// allows (half the stage barriers of 4 stages of 32 k), for every layout and
+// tile; measured on the 7B layer and head shapes at 8192 and 16384 tokens,
+// with each layout's real epilogues, 2-17% faster than 4 stages of 32 k
+// with either MFMA form.
+inline bool deep_stages(const GemmArgs& a, int /*layout*/, TileCfg /*c*/) { return a.K % 64 == 0; }
 
-// MFMA shape per layout: TN (both operands K-major) runs faster on the
-// 16 x 16 x 32 MFMA, NT and NN on 32 x 32 x 16 (measured on the 7B shapes).
-constexpr int dl_mfma(int layout) { return layout == GEMM_TN ? 16 : 32; }
+// MFMA shape: v_mfma_f32_16x16x32_bf16 for every layout (each 32 x 32 block
+// of a wave tile as four 16 x 16 blocks), faster than 32 x 32 x 16 on the
+// same shapes; the two give bitwise equal products.
+constexpr int dl_mfma(int /*layout*/) { return 16; }
 
 template <int LAYOUT, int WM, int WN, int TM, int TN, int EPI>
 hipError_t launch_dl_stages(const GemmArgs& a, TileCfg c, hipStream_t s) {
