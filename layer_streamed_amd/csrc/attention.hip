@@ -671,6 +671,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
           sacc[kt] = mfma32(Ak[c], qf[ks], sacc[kt]);
         }
       }
+      // scores stay unscaled: the scale (positive) commutes with the max
+      // (rounding is monotonic, so m is the max of the rounded scaled
+      // scores), and each exponent is one fused multiply-add
       float mx = NEG;
       auto scores = [&](auto masked) {
 #pragma unroll
@@ -678,10 +681,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
-            float s = sacc[kt][e] * a.scale_log2;
-            if (decltype(masked)::value && (key > qrow || key >= T)) s = NEG;
-            sacc[kt][e] = s;
-            mx = fmaxf(mx, s);
+            if (decltype(masked)::value && (key > qrow || key >= T)) sacc[kt][e] = NEG;
+            mx = fmaxf(mx, sacc[kt][e]);
           }
       };
       // a tile whose keys all precede the wave's first query and lie in the
@@ -691,24 +692,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
       else
         scores(std::true_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m, mx);
-      const float alpha = exp2_hw(m - mnew);
+      const float mnew = fmaxf(m, mx * a.scale_log2);
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2_hw(sacc[kt][e] - mnew);
+          const float p = exp2_hw(fmaf(sacc[kt][e], a.scale_log2, -mnew));
           sacc[kt][e] = p;
           rs += p;
         }
       rs += __shfl_xor(rs, 32, 64);
-      l = l * alpha + rs;
+      // where no query's running max moved, the rescale factor is exactly 1
+      // (2^0): the rescale of l and O is skipped for the whole wave (after
+      // the first few tiles, the usual case)
+      if (__ballot(mnew != m)) {
+        const float alpha = exp2_hw(m - mnew);
+        l = l * alpha + rs;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      } else {
+        l = l + rs;
+      }
       m = mnew;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
       u32x4_t pf[2][2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
