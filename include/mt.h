@@ -95,9 +95,13 @@ typedef struct {
                                 embedding is left to the next step, which applies it
                                 while its forward streams the other units (the head is
                                 needed only after every layer's forward, the embedding
-                                only for the batch's rows at its start); reading or
-                                setting a parameter applies it first, so results are
-                                bitwise those of 0 (apply within the step). */
+                                only for the batch's rows at its start); with clip_norm
+                                > 0 the layers' updates too (none can start before the
+                                last gradient has landed): the next step applies them
+                                in layer order, each before that layer's first weight
+                                load, holding their gradient slabs until then.  Reading
+                                or setting a parameter applies them first, so results
+                                are bitwise those of 0 (apply within the step). */
   int32_t resident_layers;   /* C >= 0 (default 0): the weights of C layers (1 .. C, or
                                 all when C = n_layers) stay on the device from one step
                                 to the next.  Right after such a layer's host Adam
@@ -128,9 +132,11 @@ typedef struct {
                                 GPU beside its finiteness check (the host never re-reads
                                 a gradient) and the factor is applied inside the Adam
                                 pass; since it depends on every gradient, each unit's
-                                update waits until the last gradient has landed, so the
-                                slab pool must hold every layer's and the head's
-                                gradient (n_slabs >= n_layers + 1, or no pool).  0: off */
+                                update waits until the last gradient has landed (with
+                                defer_updates, the layers' updates then run during the
+                                next step's forward), so the slab pool must hold every
+                                layer's and the head's gradient (n_slabs >= n_layers +
+                                1, or no pool).  0: off */
 } mt_run_cfg;
 
 /* Device pointers of one layer's weights: the stateless template's binding.
@@ -329,9 +335,10 @@ size_t mt_stream_arena_bytes_cfg(const mt_model_cfg* cfg, const mt_run_cfg* run,
  * where a CPU Adam step updates that unit while the GPU continues.
  * tokens: host int32 [batch, seq], ids in [0, vocab).  arena: device, at
  * least mt_stream_arena_bytes bytes.  Blocks until every unit is updated
- * (with defer_updates, every unit but the LM head and the embedding, whose
- * updates the next step, mt_model_get_param or mt_model_set_param applies
- * first; the values are the same either way); writes the mean next-token
+ * (with defer_updates, every unit but the LM head and the embedding, and
+ * with clip_norm > 0 but the layers too, whose updates the next step,
+ * mt_model_get_param or mt_model_set_param applies first; the values are
+ * the same either way); writes the mean next-token
  * loss to *loss_out and, if stats_out is not null, timings and byte
  * counts.  With check_finite, a non-finite loss returns MT_E_NONFINITE
  * before any update.  A step that fails after validation drops the updates

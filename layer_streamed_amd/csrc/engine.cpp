@@ -513,10 +513,13 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
   double h2d_load_bytes = 0;
   int bwd_count = 0;
   std::thread gthr, athr, wthr;
-  // the previous step's head update must land before the head is streamed
+  // the previous step's head update must land before the head is streamed,
+  // and a layer update it left (clipping) before the layer's first load
   std::mutex head_mu;
   std::condition_variable head_cv;
   bool head_done = !M->pending.head;
+  std::vector<uint8_t> layer_pending((size_t)L, 0);
+  for (const PendingAdam::Layer& x : M->pending.layers) layer_pending[x.unit] = 1;
   std::atomic<int64_t> units_deferred{0};
   std::mutex loss_mu;
   std::condition_variable loss_cv;
@@ -648,6 +651,9 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       if (ok && ld.unit == L) {
         std::unique_lock<std::mutex> lk(head_mu);
         head_cv.wait(lk, [&] { return head_done; });
+      } else if (ok && ld.unit >= 0 && ld.unit < L) {
+        std::unique_lock<std::mutex> lk(head_mu);
+        head_cv.wait(lk, [&] { return !layer_pending[ld.unit]; });
       }
       if (ok) {
         const Unit& u = M->units[ld.unit];
@@ -682,6 +688,14 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         head_done = true;
       }
       head_cv.notify_all();
+      // layer 0 first: the forward streams the layers in order
+      apply_pending_layers(M, [&](int unit) {
+        {
+          std::lock_guard<std::mutex> lk(head_mu);
+          layer_pending[unit] = 0;
+        }
+        head_cv.notify_all();
+      });
       apply_pending_embed_rest(M);
       adam_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
     }
@@ -795,6 +809,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
       check_loss();
       skip = skip || abort_all.load();
       const auto t0 = clock::now();
+      bool left_pending = false;  // the gradient stays with a pending update
       if (!skip) {
         if (x.unit >= 0) {
           Unit& u = M->units[x.unit];
@@ -811,6 +826,14 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
             M->pending.head = true;  // its gradient stays in pending.head_grad
             M->pending.hp_head = hp;
             M->pending.clip_head = clip;
+            ++units_deferred;
+          } else if (defer && clipping) {
+            // the update runs at the start of the next step (PendingAdam)
+            if (u.kept) memcpy(u.kept, x.host, u.n * es);
+            M->pending.layers.push_back({x.unit, x.host, x.own_alloc});
+            M->pending.hp_layers = hp;
+            M->pending.clip_layers = clip;
+            left_pending = true;
             ++units_deferred;
           } else {
             unit_adam(M, x.unit, gb, gf, hp, clip);
@@ -861,7 +884,7 @@ mt_status mt_stream_step(mt_model* M, const int32_t* tokens, int32_t batch, int3
         }
       }
       adam_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-      if (x.unit >= 0 && !(x.unit == L && defer)) {
+      if (x.unit >= 0 && !(x.unit == L && defer) && !left_pending) {
         if (x.own_alloc) hipHostFree(x.host);
         else M->slabs.release(x.host);
       }

@@ -100,7 +100,7 @@ inline uint32_t f2bf_bits(uint32_t u) {
 template <bool BF16_GRAD, int SHADOW>
 void adam_loop(float* __restrict p, float* __restrict m, float* __restrict v,
                const void* __restrict graw, void* __restrict shadow, size_t lo, size_t hi,
-               const AdamHp& h) {
+               const AdamHp& h, float clip) {
   const float b1 = h.b1, omb1 = h.omb1, b2 = h.b2, omb2 = h.omb2;
   const float bc1 = h.bc1, bc2 = h.bc2, lr = h.lr, eps = h.eps;
   const uint16_t* __restrict gb = static_cast<const uint16_t*>(graw);
@@ -113,6 +113,7 @@ void adam_loop(float* __restrict p, float* __restrict m, float* __restrict v,
     } else {
       g = gf[i];
     }
+    g = g * clip;
     const float mi = b1 * m[i] + omb1 * g;
     const float vi = b2 * v[i] + omb2 * (g * g);
     const float mh = mi / bc1;
@@ -139,23 +140,25 @@ void adam_loop(float* __restrict p, float* __restrict m, float* __restrict v,
 // (read-for-ownership), 2 of the ~30 bytes of host traffic per parameter.
 void adam_bf16_stream(float* __restrict p, float* __restrict m, float* __restrict v,
                       const uint16_t* __restrict gb, uint16_t* __restrict sh, size_t lo,
-                      size_t hi, const AdamHp& h) {
+                      size_t hi, const AdamHp& h, float clip) {
   // scalar until the copy is 16-byte aligned
   size_t i = lo;
   while (i < hi && ((uintptr_t)(sh + i) & 15)) {
-    adam_loop<true, 1>(p, m, v, gb, sh, i, i + 1, h);
+    adam_loop<true, 1>(p, m, v, gb, sh, i, i + 1, h, clip);
     ++i;
   }
   const __m256 b1 = _mm256_set1_ps(h.b1), omb1 = _mm256_set1_ps(h.omb1);
   const __m256 b2 = _mm256_set1_ps(h.b2), omb2 = _mm256_set1_ps(h.omb2);
   const __m256 bc1 = _mm256_set1_ps(h.bc1), bc2 = _mm256_set1_ps(h.bc2);
   const __m256 lr = _mm256_set1_ps(h.lr), eps = _mm256_set1_ps(h.eps);
+  const __m256 cl = _mm256_set1_ps(clip);
   const __m256i round = _mm256_set1_epi32(0x7FFF), one = _mm256_set1_epi32(1);
   const __m256i absmask = _mm256_set1_epi32(0x7FFFFFFF), inf = _mm256_set1_epi32(0x7F800000);
   const __m256i sign = _mm256_set1_epi32(0x8000), qnan = _mm256_set1_epi32(0x7FC0);
   for (; i + 8 <= hi; i += 8) {
     const __m128i g16 = _mm_loadu_si128(reinterpret_cast<const __m128i*>(gb + i));
-    const __m256 g = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(g16), 16));
+    const __m256 g = _mm256_mul_ps(
+        _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(g16), 16)), cl);
     const __m256 mi = _mm256_add_ps(_mm256_mul_ps(b1, _mm256_loadu_ps(m + i)), _mm256_mul_ps(omb1, g));
     const __m256 vi = _mm256_add_ps(_mm256_mul_ps(b2, _mm256_loadu_ps(v + i)),
                                     _mm256_mul_ps(omb2, _mm256_mul_ps(g, g)));
@@ -178,22 +181,22 @@ void adam_bf16_stream(float* __restrict p, float* __restrict m, float* __restric
     const __m256i packed = _mm256_permute4x64_epi64(_mm256_packus_epi32(b, b), 0x08);
     _mm_stream_si128(reinterpret_cast<__m128i*>(sh + i), _mm256_castsi256_si128(packed));
   }
-  if (i < hi) adam_loop<true, 1>(p, m, v, gb, sh, i, hi, h);
+  if (i < hi) adam_loop<true, 1>(p, m, v, gb, sh, i, hi, h, clip);
   _mm_sfence();  // streaming stores visible before the copy is read again
 }
 
 }  // namespace
 
 void adam_range(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                uint16_t* sb, float* sf, size_t lo, size_t hi, const AdamHp& h) {
+                uint16_t* sb, float* sf, size_t lo, size_t hi, const AdamHp& h, float clip) {
   if (gb) {
-    if (sb) adam_bf16_stream(p, m, v, gb, sb, lo, hi, h);
-    else if (sf) adam_loop<true, 2>(p, m, v, gb, sf, lo, hi, h);
-    else adam_loop<true, 0>(p, m, v, gb, nullptr, lo, hi, h);
+    if (sb) adam_bf16_stream(p, m, v, gb, sb, lo, hi, h, clip);
+    else if (sf) adam_loop<true, 2>(p, m, v, gb, sf, lo, hi, h, clip);
+    else adam_loop<true, 0>(p, m, v, gb, nullptr, lo, hi, h, clip);
   } else {
-    if (sb) adam_loop<false, 1>(p, m, v, gf, sb, lo, hi, h);
-    else if (sf) adam_loop<false, 2>(p, m, v, gf, sf, lo, hi, h);
-    else adam_loop<false, 0>(p, m, v, gf, nullptr, lo, hi, h);
+    if (sb) adam_loop<false, 1>(p, m, v, gf, sb, lo, hi, h, clip);
+    else if (sf) adam_loop<false, 2>(p, m, v, gf, sf, lo, hi, h, clip);
+    else adam_loop<false, 0>(p, m, v, gf, nullptr, lo, hi, h, clip);
   }
 }
 
@@ -219,8 +222,9 @@ bool grad_finite(const uint16_t* gb, const float* gf, size_t n, ThreadPool* pool
 }
 
 void adam_parallel(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                   uint16_t* sb, float* sf, size_t n, const AdamHp& h, ThreadPool* pool) {
-  auto body = [&](size_t lo, size_t hi) { adam_range(p, m, v, gb, gf, sb, sf, lo, hi, h); };
+                   uint16_t* sb, float* sf, size_t n, const AdamHp& h, float clip,
+                   ThreadPool* pool) {
+  auto body = [&](size_t lo, size_t hi) { adam_range(p, m, v, gb, gf, sb, sf, lo, hi, h, clip); };
   if (pool) pool->parallel_for(n, body);
   else body(0, n);
 }
@@ -376,7 +380,7 @@ mt_status mt_host_adam(float* param, float* exp_avg, float* exp_avg_sq, const vo
   if (hp->check_finite && !grad_finite(gb, gf, n, pool))
     return set_error(MT_E_NONFINITE, "mt_host_adam: gradient has NaN or Inf; nothing updated");
   adam_parallel(param, exp_avg, exp_avg_sq, gb, gf, bf16_shadow, nullptr, n, adam_hp(*hp, step),
-                pool);
+                1.f, pool);
   return MT_OK;
 }
 

@@ -42,15 +42,18 @@ struct AdamHp {
 };
 AdamHp adam_hp(const mt_run_cfg& hp, int64_t step);
 
-// One Adam update over [lo, hi): grad is bf16 (gb) or fp32 (gf).  The
-// updated master is also written to the streamed copy when one is given:
-// bf16 (sb, round to nearest even) or fp32 (sf, the debug precision).
+// One Adam update over [lo, hi): grad is bf16 (gb) or fp32 (gf), multiplied
+// by `clip` (the global-norm clipping factor, 1 without clipping: an exact
+// identity) before the update.  The updated master is also written to the
+// streamed copy when one is given: bf16 (sb, round to nearest even) or fp32
+// (sf, the debug precision).
 void adam_range(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                uint16_t* sb, float* sf, size_t lo, size_t hi, const AdamHp& h);
+                uint16_t* sb, float* sf, size_t lo, size_t hi, const AdamHp& h, float clip);
 // True if every gradient value in [0, n) is finite.
 bool grad_finite(const uint16_t* gb, const float* gf, size_t n, ThreadPool* pool);
 void adam_parallel(float* p, float* m, float* v, const uint16_t* gb, const float* gf,
-                   uint16_t* sb, float* sf, size_t n, const AdamHp& h, ThreadPool* pool);
+                   uint16_t* sb, float* sf, size_t n, const AdamHp& h, float clip,
+                   ThreadPool* pool);
 
 inline uint16_t host_f2bf(float f) {
   uint32_t u;

@@ -77,7 +77,7 @@ void unit_adam(mt_model* M, int unit, const uint16_t* gb, const float* gf, const
     const Adam8Arrays a{u.master, u.mq, u.rq, u.ms, u.rs, gb, gf, sb, sf};
     adam8_parallel(a, u.segs.data(), (int)u.segs.size(), hp, clip, M->pool.get());
   } else {
-    adam_parallel(u.master, u.m, u.v, gb, gf, sb, sf, u.n, hp, M->pool.get());
+    adam_parallel(u.master, u.m, u.v, gb, gf, sb, sf, u.n, hp, clip, M->pool.get());
   }
 }
 
@@ -117,10 +117,10 @@ void embed_rows(mt_model* M, const std::vector<int32_t>* rows) {
         adam8_range(ar, &seg, 1, 0, adam8_blocks(H), pa.hp_embed, pa.clip_embed);
       } else if (f32)
         adam_range(u.master + a, u.m + a, u.v + a, nullptr, g, nullptr,
-                   static_cast<float*>(u.shadow) + a, 0, H, pa.hp_embed);
+                   static_cast<float*>(u.shadow) + a, 0, H, pa.hp_embed, pa.clip_embed);
       else
         adam_range(u.master + a, u.m + a, u.v + a, nullptr, g,
-                   static_cast<uint16_t*>(u.shadow) + a, nullptr, 0, H, pa.hp_embed);
+                   static_cast<uint16_t*>(u.shadow) + a, nullptr, 0, H, pa.hp_embed, pa.clip_embed);
       pa.row_done[r] = 1;
     }
   }, 16);
@@ -147,14 +147,38 @@ void apply_pending_embed_rest(mt_model* M) {
   pa.embed = false;
 }
 
+namespace {
+void release_grad(mt_model* M, const PendingAdam::Layer& x) {
+  if (x.own_alloc) hipHostFree(x.grad);
+  else M->slabs.release(x.grad);
+}
+}  // namespace
+
+void apply_pending_layers(mt_model* M, const std::function<void(int)>& done) {
+  PendingAdam& pa = M->pending;
+  std::sort(pa.layers.begin(), pa.layers.end(),
+            [](const PendingAdam::Layer& a, const PendingAdam::Layer& b) { return a.unit < b.unit; });
+  const bool f32 = M->es == 4;
+  for (const PendingAdam::Layer& x : pa.layers) {
+    unit_adam(M, x.unit, f32 ? nullptr : static_cast<const uint16_t*>(x.grad),
+              f32 ? static_cast<const float*>(x.grad) : nullptr, pa.hp_layers, pa.clip_layers);
+    release_grad(M, x);
+    if (done) done(x.unit);
+  }
+  pa.layers.clear();
+}
+
 void flush_pending(mt_model* M) {
   apply_pending_head(M);
+  apply_pending_layers(M, nullptr);
   apply_pending_embed_rest(M);
 }
 
 void drop_pending(mt_model* M) {
   PendingAdam& pa = M->pending;
   pa.head = pa.embed = false;
+  for (const PendingAdam::Layer& x : pa.layers) release_grad(M, x);
+  pa.layers.clear();
 }
 
 }  // namespace mt
@@ -177,6 +201,8 @@ void* mt_model::host_alloc(size_t bytes, bool pinned) {
 }
 
 mt_model::~mt_model() {
+  for (auto& x : pending.layers)
+    if (x.own_alloc) hipHostFree(x.grad);  // pool slabs go with the blocks below
   for (auto& e : events) hipEventDestroy(e);
   for (auto& b : blocks) {
     if (b.pinned) hipHostFree(b.p);

@@ -8,6 +8,7 @@
 
 #include <condition_variable>
 #include <deque>
+#include <functional>
 #include <memory>
 #include <mutex>
 #include <string>
@@ -62,11 +63,22 @@ class SlabPool {
 // and the embedding: their weights are needed late in the next forward, or
 // for only a few rows at its start, so their host Adam runs while the next
 // forward streams the other units instead of after this step's backward).
-// Every reader of the model applies them first (flush_pending).
+// With global-norm clipping the layers' updates are left too: none can run
+// before the last gradient has landed, so they run while the next forward
+// streams, each before its layer's first weight load.  Every reader of the
+// model applies them first (flush_pending).
 struct PendingAdam {
   bool head = false, embed = false;
   AdamHp hp_head{}, hp_embed{};
   float clip_head = 1.f, clip_embed = 1.f;  // the step's clipping factor
+  struct Layer {
+    int unit;
+    void* grad;      // the landed gradient (a pool slab, or its own pinned buffer)
+    bool own_alloc;  // allocated for the transfer (no pool): freed after the update
+  };
+  std::vector<Layer> layers;
+  AdamHp hp_layers{};
+  float clip_layers = 1.f;
   // the head's gradient lands in a pinned buffer of its own (never a pool
   // slab: holding a slab across units would stall the offload of the rest
   // of the step when the pool is small)
@@ -133,6 +145,8 @@ bool lookup_param(const mt_model* m, const char* name, TensorRef* out);
 void apply_pending_head(mt_model* m);
 void apply_pending_embed_rows(mt_model* m, const int32_t* ids, size_t n);
 void apply_pending_embed_rest(mt_model* m);
+// The pending layer updates in layer order, calling done(unit) after each.
+void apply_pending_layers(mt_model* m, const std::function<void(int)>& done);
 void flush_pending(mt_model* m);
 void drop_pending(mt_model* m);
 // Adam (fp32 or hybrid 8-bit moments, per the model) over a whole unit with

@@ -431,3 +431,98 @@ def test_step_adam8_clip_schedule_invariance_bitwise(tiny, kw):
         np.testing.assert_array_equal(base["master"][n], other["master"][n], err_msg=n)
         np.testing.assert_array_equal(base["m"][n], other["m"][n], err_msg=n)
         np.testing.assert_array_equal(base["v"][n], other["v"][n], err_msg=n)
+
+
+# Global-norm clipping with fp32 moments, and the layers' clipped updates
+# the next step applies while it streams (defer_updates).
+
+
+def _run_clip(shape, weights, batches, get_between=False, **run_kw):
+    """Steps over `batches` with fp32 moments; get_between reads every
+    master after each step (which applies the pending updates early)."""
+    torch, mt = _env()
+    m = mt.Model(shape, keep_grads=1, **run_kw)
+    m.set_params(weights)
+    B, T = batches[0].shape
+    arena = torch.empty(m.arena_bytes(B, T), dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    names = synth.param_names(shape)
+    losses, stats, grads = [], [], []
+    for ids in batches:
+        loss, st = m.step(ids, arena, streams)
+        losses.append(loss)
+        stats.append(st)
+        grads.append({n: m.get(n, mt.GET_GRAD) for n in names})
+        if get_between:
+            for n in names:
+                m.get(n, mt.GET_MASTER)
+    out = {"loss": losses, "stats": stats, "grads": grads,
+           "master": {n: m.get(n, mt.GET_MASTER) for n in names},
+           "shadow": {n: m.get(n, mt.GET_SHADOW) for n in names},
+           "m": {n: m.get(n, mt.GET_M) for n in names},
+           "v": {n: m.get(n, mt.GET_V) for n in names}}
+    m.close()
+    return out
+
+
+def _oracle_clip_fp32(params, ids, shape, state, step, max_norm):
+    """Forward, backward, global-norm clipping (the oracle's coefficient)
+    and the fp32 Adam of the oracle on the clipped gradient."""
+    from oracle import adam8 as A8
+    loss, grads = D.loss_and_grads(params, ids, shape, "resident", None)
+    c = A8.clip_coefficient(grads, max_norm)
+    new_p, new_s = {}, {}
+    for n, p in params.items():
+        m, v = state[n] if state else (np.zeros_like(p), np.zeros_like(p))
+        g = (np.asarray(grads[n], np.float32) * np.float32(c)).astype(np.float32)
+        new_p[n], m2, v2 = D.adam_update(p, m, v, g, step, shape.lr, shape.beta1, shape.beta2,
+                                         shape.adam_eps)
+        new_s[n] = (m2, v2)
+    return loss, grads, c, new_p, new_s
+
+
+def test_step_clip_fp32_two_batches_match_oracle(tiny):
+    """Two steps on different batches with fp32 moments and a clipping norm
+    below the gradient's (every gradient scaled): loss, gradients, clip
+    factor, masters and moments against the oracle."""
+    s, w, ids1 = tiny
+    ids2 = synth.make_tokens(s, seed=81)
+    g = _run_clip(s, w, [ids1, ids2], clip_norm=0.05)
+    l1, g1, c1, p1, st1 = _oracle_clip_fp32(w, ids1, s, None, 1, 0.05)
+    l2, g2, c2, p2, st2 = _oracle_clip_fp32(p1, ids2, s, st1, 2, 0.05)
+    assert c1 < 1 and c2 < 1
+    assert abs(g["loss"][0] - l1) < LOSS_TOL and abs(g["loss"][1] - l2) < LOSS_TOL
+    for st, c in zip(g["stats"], (c1, c2)):
+        assert abs(st["clip_factor"] - c) / c < REL_TOL, (st["clip_factor"], c)
+    for n in synth.param_names(s):
+        assert rel(g["grads"][0][n], g1[n]) < REL_TOL, n
+        assert rel(g["grads"][1][n], g2[n]) < REL_TOL, n
+        assert rel(g["master"][n], p2[n]) < REL_TOL, n
+        assert rel(g["m"][n], st2[n][0]) < REL_TOL, n
+        assert rel(g["v"][n], st2[n][1]) < 2 * REL_TOL, n
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(resident_layers=1), dict(use_slab_pool=0),
+                                dict(get_between=True), dict(opt_8bit=1, get_between=True)],
+                         ids=["deferred", "resident1", "no-pool", "read-between",
+                              "8bit-read-between"])
+def test_step_clip_deferred_layer_updates_bitwise(tiny, kw):
+    """With clipping, the layers' updates run at the start of the next step
+    (before each layer's first load); three steps on different batches give
+    bitwise the losses, kept gradients, masters, streamed copies and moments
+    of the in-step updates, also when the model is read between steps (the
+    read applies the pending updates) and with a resident layer (its
+    device copy is refreshed from the updated streamed copy)."""
+    s, w, ids1 = tiny
+    batches = [ids1, synth.make_tokens(s, seed=82), synth.make_tokens(s, seed=83)]
+    kw = dict(kw)
+    base_kw = {"opt_8bit": kw.get("opt_8bit", 0)}
+    base = _run_clip(s, w, batches, clip_norm=0.05, defer_updates=0, **base_kw)
+    other = _run_clip(s, w, batches, clip_norm=0.05, **kw)
+    assert base["loss"] == other["loss"]
+    assert [x["clip_factor"] for x in base["stats"]] == [x["clip_factor"] for x in other["stats"]]
+    for n in synth.param_names(s):
+        for i in range(3):
+            np.testing.assert_array_equal(base["grads"][i][n], other["grads"][i][n], err_msg=n)
+        for k in ("master", "shadow", "m", "v"):
+            np.testing.assert_array_equal(base[k][n], other[k][n], err_msg=f"{k} {n}")
