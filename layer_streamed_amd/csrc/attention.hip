@@ -492,9 +492,9 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(const AttnArgs a) {
 // dV and dK are two ds_read_b64_tr_b16 per lane (the 16-lane pattern of the
 // GEMM's K-major fragments: lane 4j + s addresses query row base + j,
 // columns 4s .. 4s+3, and lane i receives column i at rows base .. base+3).
-// LDS reads of the tiles are inline asm, waited for explicitly: the
-// compiler would otherwise drain the next tile's in-flight loads before
-// each read.
+// The copies go out through lds_dma16 (untracked by the compiler, ordered
+// by the kernel's own vmcnt wait and barrier), so the compiler's waits for
+// the LDS reads never drain the next tile's copies.
 //
 // The chunk orders keep every tile read on distinct banks.  gfx950's LDS
 // has 64 banks (256 bytes per cycle).  A ds_read_b128 is served in four
@@ -533,35 +533,25 @@ constexpr bool tile_swz_ok() {
 }
 static_assert(tile_swz_ok(), "tile chunk order");
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
 template <bool QT = false>
 __device__ __forceinline__ u32x4_t lds_row16(const char* tile, int row, int chunk) {
-  u32x4_t v;
   const int sw = QT ? qtile_swz(row) : tile_swz(row);
-  const uint32_t la = lds_addr(tile + row * 256 + ((chunk ^ sw) << 4));
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(la) : "memory");
-  return v;
+  return *reinterpret_cast<const u32x4_t*>(tile + row * 256 + ((chunk ^ sw) << 4));
 }
 
-// Two transpose reads at addr + o0 and addr + o1 (immediate offsets, which
-// must fold to constants) as one MFMA A fragment: rows r .. r+3 (o0) and
-// r+8 .. r+11 (o1) of the lane's column, in slots 0-3 and 4-7.
-__device__ __forceinline__ u32x4_t lds_tr_pair(uint32_t addr, const int o0, const int o1) {
-  u32x2_t v0, v1;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v0) : "v"(addr), "i"(o0) : "memory");
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v1) : "v"(addr), "i"(o1) : "memory");
+// Two transpose reads at p + o0 and p + o1 (constant offsets, which fold
+// into the instructions' immediate field) as one MFMA A fragment: rows
+// r .. r+3 (o0) and r+8 .. r+11 (o1) of the lane's column, in slots 0-3
+// and 4-7.
+__device__ __forceinline__ u32x4_t lds_tr_pair(const char* p, const int o0, const int o1) {
+  const u32x2_t v0 = lds_tr16(p + o0), v1 = lds_tr16(p + o1);
   return u32x4_t{v0.x, v0.y, v1.x, v1.y};
 }
 
-// The same pair from two addresses at one immediate offset: rows r .. r+3
-// at addr and r+8 .. r+11 at addr8 (whose chunk order differs).
-__device__ __forceinline__ u32x4_t lds_tr_pair2(uint32_t addr, uint32_t addr8, const int o) {
-  u32x2_t v0, v1;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v0) : "v"(addr), "i"(o) : "memory");
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v1) : "v"(addr8), "i"(o) : "memory");
+// The same pair from two addresses at one offset: rows r .. r+3 at p and
+// r+8 .. r+11 at p8 (whose chunk order differs).
+__device__ __forceinline__ u32x4_t lds_tr_pair2(const char* p, const char* p8, const int o) {
+  const u32x2_t v0 = lds_tr16(p + o), v1 = lds_tr16(p8 + o);
   return u32x4_t{v0.x, v0.y, v1.x, v1.y};
 }
 
@@ -619,12 +609,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
       const int row = slot / CH, pos = slot % CH;
       const int c = pos ^ tile_swz(row);
       const long gk = min(kv0 + row, T - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(kbase + gk * ldq + c * 8),
-          (__attribute__((address_space(3))) void*)(sk + (w * PER + p) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(vbase + gk * ldq + c * 8),
-          (__attribute__((address_space(3))) void*)(sk + TILE + (w * PER + p) * 1024), 16, 0, 0);
+      lds_dma16(kbase + gk * ldq + c * 8, sk + (w * PER + p) * 1024);
+      lds_dma16(vbase + gk * ldq + c * 8, sk + TILE + (w * PER + p) * 1024);
     }
   };
   // V^T read addresses, as the dK/dV kernel's Q^T reads, and the offset
@@ -645,6 +631,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
 
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the Q fragments are complete here; tying them to this point keeps the
+  // compiler, which does not track the copies, from waiting for them (and
+  // so for every copy in flight) inside the loop
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
@@ -663,9 +654,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
           const int c = ks & 1;
           if (ks + 1 < D / 16) {
             Ak[c ^ 1] = lds_row16(sk, 32 * kt + n, 2 * (ks + 1) + hh);
-            asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory");
-          } else {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           }
           asm volatile("" : "+v"(Ak[c]));
           sacc[kt] = mfma32(Ak[c], qf[ks], sacc[kt]);
@@ -725,12 +713,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
       // O^T over steps i = (dt, kt, jj); the two transpose reads of step
       // i+1 go out before the MFMA of step i
       constexpr int NI = (D / 32) * 2 * 2;
-      const uint32_t sva = lds_addr(sk + TILE);
+      const char* sva = sk + TILE;
       u32x4_t Vt[2];
       auto reads = [&](int i, int slot) {
         const int dt = i / 4, kt = (i >> 1) & 1, jj = i & 1;
         const int ro = (32 * kt + 16 * jj) * 256;
-        const uint32_t ad = sva + trb[dt];
+        const char* ad = sva + trb[dt];
         Vt[slot] = lds_tr_pair2(ad, ad + d8, ro);
       };
       reads(0, 0);
@@ -740,9 +728,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
         const int c = i & 1;
         if (i + 1 < NI) {
           reads(i + 1, c ^ 1);
-          asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         asm volatile("" : "+v"(Vt[c]));
         oacc[dt] = mfma32(Vt[c], pf[kt][jj], oacc[dt]);
@@ -831,6 +816,7 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
   const int ntq = (T - k0 + BQ - 1) / BQ;  // query tiles from k0 to T
   const int nit = rep * ntq;
   float lse_r = 0.f, del_r = 0.f;
+  int lse_q = 0;
   // tile `it` -> stage `buf`: Q and dO rows clamped to T - 1 past the end
   // (their P is 0 through lse = +1e30, so they add exact zeros)
   auto issue = [&](int it, int buf) {
@@ -843,18 +829,26 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
       const int row = slot / CH, pos = slot % CH;
       const int c = pos ^ qtile_swz(row);
       const long gq = min(qt0 + row, T - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(base + gq * ldq + hq * D + c * 8),
-          (__attribute__((address_space(3))) void*)(sq + (w * PER + p) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(dbase + gq * a.ldo + hq * D + c * 8),
-          (__attribute__((address_space(3))) void*)(sq + TILE + (w * PER + p) * 1024), 16, 0, 0);
+      lds_dma16(base + gq * ldq + hq * D + c * 8, sq + (w * PER + p) * 1024);
+      lds_dma16(dbase + gq * a.ldo + hq * D + c * 8, sq + TILE + (w * PER + p) * 1024);
     }
+    // statistics of the tile's rows, raw: nothing reads them before the
+    // stage's copies are waited for (a use right after the load would wait
+    // for those copies too); rows past the end read row T - 1
     if (tid < BQ) {
-      const int q = qt0 + tid;
-      const long lix = ((long)b * a.Hq + hq) * T + q;
-      lse_r = q < T ? a.lse[lix] * LOG2E : -NEG;  // +1e30 makes P = 0 for padding rows
-      del_r = q < T ? a.delta[lix] : 0.f;
+      const long lix = ((long)b * a.Hq + hq) * T + min(qt0 + tid, T - 1);
+      lse_r = a.lse[lix];
+      del_r = a.delta[lix];
+      lse_q = qt0 + tid;
+    }
+  };
+  // the stage's statistics into LDS: lse in log2 units, +1e30 for padding
+  // rows (P = 0), delta 0 there
+  auto stats = [&](int buf) {
+    if (tid < BQ) {
+      const bool in = lse_q < T;
+      sLb[buf * BQ + tid] = in ? lse_r * LOG2E : -NEG;
+      sDb[buf * BQ + tid] = in ? del_r : 0.f;
     }
   };
 
@@ -873,10 +867,13 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
 
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (tid < BQ) {
-    sLb[tid] = lse_r;
-    sDb[tid] = del_r;
+  // the key's K and V fragments are complete here (as in the forward)
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    asm volatile("" : "+v"(kf[ks]));
+    asm volatile("" : "+v"(vf[ks]));
   }
+  stats(0);
   __syncthreads();
   for (int it = 0; it < nit; ++it) {
     const int buf = it & 1;
@@ -911,9 +908,6 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
           const int qn = (s + 1) / (D / 32), kn = (s + 1) % (D / 32);
           Aq[c ^ 1] = lds_row16<true>(sq, 16 * qn + li, 4 * kn + lg);
           Ad[c ^ 1] = lds_row16<true>(sdo, 16 * qn + li, 4 * kn + lg);
-          asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         asm volatile("" : "+v"(Aq[c]));
         asm volatile("" : "+v"(Ad[c]));
@@ -946,12 +940,12 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
       // dO^T / Q^T fragment of column block db at those rows (two transpose
       // reads each).  The reads of step s+1 go out before the MFMAs of s.
       constexpr int NS3 = (BQ / 32) * NDB;
-      const uint32_t sqa = lds_addr(sq);
+      const char* sqa = sq;
       u32x4_t At[2], Aq2[2];
       auto reads = [&](int s, int slot) {
         const int qc = s / NDB, db = s % NDB;
         const int ro = 32 * qc * 256;
-        const uint32_t ad = sqa + trb[db];
+        const char* ad = sqa + trb[db];
         At[slot] = lds_tr_pair(ad, TILE + ro, TILE + ro + 16 * 256);
         Aq2[slot] = lds_tr_pair(ad, ro, ro + 16 * 256);
       };
@@ -972,9 +966,6 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
         }
         if (s + 1 < NS3) {
           reads(s + 1, c ^ 1);
-          asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         asm volatile("" : "+v"(At[c]));
         asm volatile("" : "+v"(Aq2[c]));
@@ -984,10 +975,7 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
     }
     if (it + 1 < nit) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (tid < BQ) {
-        sLb[(buf ^ 1) * BQ + tid] = lse_r;
-        sDb[(buf ^ 1) * BQ + tid] = del_r;
-      }
+      stats(buf ^ 1);
     }
     __syncthreads();
   }
@@ -1047,8 +1035,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
                 : u32x4_t{0, 0, 0, 0};
   }
   const long li = ((long)b * a.Hq + h) * T + qrow;
-  const float lse2 = ok ? a.lse[li] * LOG2E : -NEG;
-  const float del = ok ? a.delta[li] : 0.f;
+  const float lse2_l = ok ? a.lse[li] * LOG2E : -NEG;
+  const float del_l = ok ? a.delta[li] : 0.f;
 
   f32x16_t dq[D / 32];
 #pragma unroll
@@ -1068,12 +1056,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
       const int row = slot / CH, pos = slot % CH;
       const int c = pos ^ tile_swz(row);
       const long gk = min(kv0 + row, T - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(kbase + gk * ldq + c * 8),
-          (__attribute__((address_space(3))) void*)(sk + (w * PER + p) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(vbase + gk * ldq + c * 8),
-          (__attribute__((address_space(3))) void*)(sk + TILE + (w * PER + p) * 1024), 16, 0, 0);
+      lds_dma16(kbase + gk * ldq + c * 8, sk + (w * PER + p) * 1024);
+      lds_dma16(vbase + gk * ldq + c * 8, sk + TILE + (w * PER + p) * 1024);
     }
   };
   // K^T read addresses and the row + 8 partner offset, as in the forward
@@ -1091,6 +1075,14 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
 
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // as in the forward: the row's fragments and statistics are complete here
+  float lse2 = lse2_l, del = del_l;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    asm volatile("" : "+v"(qf[ks]));
+    asm volatile("" : "+v"(df[ks]));
+  }
+  asm volatile("" : "+v"(lse2), "+v"(del));
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
@@ -1113,9 +1105,6 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
           if (ks + 1 < D / 16) {
             Ak[c ^ 1] = lds_row16(sk, 32 * kt + n, 2 * (ks + 1) + hh);
             Av[c ^ 1] = lds_row16(sv, 32 * kt + n, 2 * (ks + 1) + hh);
-            asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
-          } else {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           }
           asm volatile("" : "+v"(Ak[c]));
           asm volatile("" : "+v"(Av[c]));
@@ -1135,13 +1124,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
       // dQ over steps i = (kt, jj, dt); the two transpose reads of step
       // i+1 go out before the MFMA of step i
       constexpr int NI = 2 * 2 * (D / 32);
-      const uint32_t ska = lds_addr(sk);
+      const char* ska = sk;
       u32x4_t Kt[2];
       u32x4_t Sb = {0, 0, 0, 0};
       auto reads = [&](int i, int slot) {
         const int kt = i / (2 * (D / 32)), jj = (i / (D / 32)) & 1, dt = i % (D / 32);
         const int ro = (32 * kt + 16 * jj) * 256;
-        const uint32_t ad = ska + trb[dt];
+        const char* ad = ska + trb[dt];
         Kt[slot] = lds_tr_pair2(ad, ad + d8, ro);
       };
       reads(0, 0);
@@ -1152,9 +1141,6 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
         if (dt == 0) Sb = pack_p(dpacc[kt], jj);
         if (i + 1 < NI) {
           reads(i + 1, c ^ 1);
-          asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         asm volatile("" : "+v"(Kt[c]));
         dq[dt] = mfma32(Kt[c], Sb, dq[dt]);

@@ -58,6 +58,36 @@ __device__ inline f32x4_t mfma16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// LDS byte address of a pointer into shared memory.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One direct global -> LDS copy (gfx950 global_load_lds_dwordx4): lane l's
+// 16 bytes at g land at lds + 16 l (lds wave-uniform, through M0).  Issued
+// as asm so that the compiler's wait insertion does not track it: seeing an
+// LDS store in flight, it would drain every outstanding global load
+// (vmcnt(0)) before each LDS read that follows, including the reads of a
+// stage that an earlier wait and barrier already made complete, and so
+// serialize a load ring.  Kernels that use it order the copies themselves:
+// a vmcnt wait and a workgroup barrier before any wave reads the stage.
+// The instruction has no register result; the s_nop covers the one wait
+// state that a write of M0 needs before an LDS DMA.
+__device__ inline void lds_dma16(const void* g, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives 16-bit element i & 3 of the 8-byte pieces that
+// lanes 4 j + (i >> 2), j = 0..3, address.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ inline u32x2_t lds_tr16(const void* p) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (__attribute__((address_space(3))) i16x4_t*)(const __attribute__((address_space(3))) char*)p));
+}
+
 // Wave-level reductions over all 64 lanes (butterfly via ds_swizzle-free shuffles).
 __device__ inline float wave_sum(float v) {
 #pragma unroll

@@ -386,16 +386,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
 //    the 8-byte pieces addressed by lanes 4 j + (i >> 2), j = 0..3; when
 //    those lanes address rows k..k+3 at columns m0, m0+4, m0+8, m0+12, lane
 //    i holds column m0 + i at rows k..k+3, i.e. four consecutive k of one
-//    MFMA row (issued as inline asm; see dl_frag).  Each 16-lane group reads
-//    4 rows x 2 chunks and each half-wave
-//    4 rows x 4 chunks; the XOR patterns {0, 6, 10, 12} of km_swz differ in
+//    MFMA row.  Each 16-lane group reads 4 rows x 2 chunks and each
+//    half-wave 4 rows x 4 chunks; the XOR patterns {0, 6, 10, 12} of km_swz differ in
 //    bits 1-2 and in bits 2-3, so both sets land on distinct banks.
 // Both give each lane k-slots 8 (l / 32) .. + 7 in natural order, so the
 // operand kinds mix freely.  Requires K % BK == 0 and, for K-major
 // operands, M or N % 8 == 0; rows or columns past M or N are clamped to a
 // valid one (they only feed output elements the epilogue drops).
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int km_swz(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }
 
@@ -450,14 +447,7 @@ __device__ __forceinline__ u32x4_t dl_frag(const char* st, int rb, int ks, int l
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = ks * 16 + 8 * (grp >> 1) + 4 * h + (i >> 2);
-      const char* p = st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8);
-      // Issued as asm: the compiler's wait insertion cannot tell this LDS
-      // read from the in-flight global->LDS stores of later stages and would
-      // drain every outstanding load before it (vmcnt(0)), serializing the
-      // ring.  The kernel orders the stores itself (vmcnt + barrier), and
-      // the caller waits lgkmcnt(0) before the first use of the result.
-      const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[h]) : "v"(la) : "memory");
+      v[h] = lds_tr16(st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8));
     }
     return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
   }
@@ -484,10 +474,7 @@ __device__ __forceinline__ u32x4_t dl_frag16(const char* st, int rb, int ks, int
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = ks * 32 + 8 * grp + 4 * h + (i >> 2);
-      const char* p = st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8);
-      // asm for the reason given in dl_frag
-      const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[h]) : "v"(la) : "memory");
+      v[h] = lds_tr16(st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8));
     }
     return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
   }
@@ -762,16 +749,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
     if (kt >= kend) return;
     char* base = dl_smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int p = 0; p < A_PER; ++p)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(ga[p] + kt * a_step),
-          (__attribute__((address_space(3))) void*)(base + (wave * A_PER + p) * 1024), 16, 0, 0);
+    for (int p = 0; p < A_PER; ++p) lds_dma16(ga[p] + kt * a_step, base + (wave * A_PER + p) * 1024);
 #pragma unroll
     for (int p = 0; p < B_PER; ++p)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(gb[p] + kt * b_step),
-          (__attribute__((address_space(3))) void*)(base + A_CH * 16 + (wave * B_PER + p) * 1024), 16,
-          0, 0);
+      lds_dma16(gb[p] + kt * b_step, base + A_CH * 16 + (wave * B_PER + p) * 1024);
   };
 
   auto compute16 = [&](int kt) {
@@ -790,20 +771,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           bfr[j][h] = dl_frag16<B_KM, BN, BK>(sB, wn * TN * 32 + j * 32 + 16 * h, ks, lane);
-      if constexpr (A_KM || B_KM) {
-        // as in compute below
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          asm volatile("" : "+v"(af[i][0]));
-          asm volatile("" : "+v"(af[i][1]));
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          asm volatile("" : "+v"(bfr[j][0]));
-          asm volatile("" : "+v"(bfr[j][1]));
-        }
-      }
       if constexpr (MI == 16) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -826,16 +793,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
       for (int i = 0; i < TM; ++i) af[i] = dl_frag<A_KM, BM, BK>(sA, wm * TM * 32 + i * 32, ks, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[j] = dl_frag<B_KM, BN, BK>(sB, wn * TN * 32 + j * 32, ks, lane);
-      if constexpr (A_KM || B_KM) {
-        // the transpose reads were issued as asm, outside the compiler's
-        // wait tracking: wait for them, and tie every fragment to the wait
-        // so no use can be scheduled above it
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < TM; ++i) asm volatile("" : "+v"(af[i]));
-#pragma unroll
-        for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(bfr[j]));
-      }
       if constexpr (MI == 32) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -860,6 +817,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
     if constexpr (MI == 16) compute16(kt);
     else compute(kt);
   }
+  // the last trip waited for every copy; this (free) wait says so to the
+  // compiler, which does not track the copies, so that its own waits in the
+  // epilogue need not assume copies in flight
+  wait_vmcnt<0>();
   if (piece >= 0) {
     // partial sums of this tile's k-range, tile-local row-major [BM][BN]
     float* part = a.ws + ((long)(pid - a.split_full) * a.split_s + piece) * (BM * BN);
