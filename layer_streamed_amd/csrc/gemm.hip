@@ -758,19 +758,26 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
   auto compute16 = [&](int kt) {
     const char* sA = dl_smem + (kt % NS) * STAGE;
     const char* sB = sA + A_CH * 16;
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      u32x4_t af[TM][2], bfr[TN][2];
+    constexpr int KS = BK / 32;
+    constexpr int NMF = TM * TN * 4;  // MFMAs per substep
+    u32x4_t af[2][TM][2], bfr[2][TN][2];
+    auto reads = [&](int ks, int buf) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          af[i][h] = dl_frag16<A_KM, BM, BK>(sA, wm * TM * 32 + i * 32 + 16 * h, ks, lane);
+          af[buf][i][h] = dl_frag16<A_KM, BM, BK>(sA, wm * TM * 32 + i * 32 + 16 * h, ks, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          bfr[j][h] = dl_frag16<B_KM, BN, BK>(sB, wn * TN * 32 + j * 32 + 16 * h, ks, lane);
+          bfr[buf][j][h] = dl_frag16<B_KM, BN, BK>(sB, wn * TN * 32 + j * 32 + 16 * h, ks, lane);
+    };
+    reads(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int buf = ks & 1;
+      if (ks + 1 < KS) reads(ks + 1, buf ^ 1);
       if constexpr (MI == 16) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -778,8 +785,29 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
           for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              acc[i][j].s[q] = mfma16(af[i][q >> 1], bfr[j][q & 1], acc[i][j].s[q]);
+              acc[i][j].s[q] = mfma16(af[buf][i][q >> 1], bfr[buf][j][q & 1], acc[i][j].s[q]);
       }
+    }
+    // Order for the whole stage (the compiler's own order waited on each
+    // read right before its first use, so both waves of a SIMD, leaving the
+    // barrier together, stalled on LDS at every few MFMAs): substep 0's
+    // reads, then each substep's MFMAs with the next substep's reads
+    // spread among them, whose waits then find the data there.
+    // (sched_group_barrier classes: 0x008 MFMA, 0x100 LDS read.)
+    {
+      constexpr int NDS = TM * 2 * (A_KM ? 2 : 1) + TN * 2 * (B_KM ? 2 : 1);
+      constexpr int PER = NMF / NDS > 0 ? NMF / NDS : 1;
+      __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+#pragma unroll
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+#pragma unroll
+        for (int g = 0; g < NDS; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (NMF > NDS * PER) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NDS * PER, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     }
   };
 
