@@ -380,21 +380,47 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs a) {
 //    (An XOR with row / 4 for 128-byte rows would put rows r and r + 2 on
 //    the same banks and double each read's cycles.)
 //  - K-major (NN's B, TN's A and B): a stage is BK rows of k, each BM
-//    values of m wide (BM / 8 chunks) stored in the order c ^ km_swz(k).
+//    values of m wide (BM / 8 chunks) stored in the order c ^ km_swz<MI>(k).
 //    A fragment is read with two ds_read_b64_tr_b16 (gfx950 LDS transpose
 //    read): within each group of 16 lanes, lane i receives element i & 3 of
 //    the 8-byte pieces addressed by lanes 4 j + (i >> 2), j = 0..3; when
 //    those lanes address rows k..k+3 at columns m0, m0+4, m0+8, m0+12, lane
 //    i holds column m0 + i at rows k..k+3, i.e. four consecutive k of one
-//    MFMA row.  Each 16-lane group reads 4 rows x 2 chunks and each
-//    half-wave 4 rows x 4 chunks; the XOR patterns {0, 6, 10, 12} of km_swz differ in
-//    bits 1-2 and in bits 2-3, so both sets land on distinct banks.
+//    MFMA row.  The LDS serves a transpose read in two passes of 32
+//    consecutive lanes.  Every k-row starts on bank 0 (rows are 256 or
+//    512 bytes), so a row's chunk position mod 16 names its 4-bank group,
+//    and a fragment's two chunks (m0 even in chunks) form the pair
+//    {x, x ^ 1}.  With the 16 x 16 x 32 MFMA a pass reads 8 rows, k0 + r
+//    and k0 + 8 + r (r = 0..3), two chunks each: km_swz<16> XORs the chunk
+//    with 2 (r + 4 (bit 3 of k)), 8 distinct pairs, all 64 banks once.
+//    With the 32 x 32 x 16 MFMA a pass reads 4 rows k0 + r at 4 chunks,
+//    and km_swz<32> XORs with {0, 6, 10, 12}, whose pairs of adjacent
+//    chunks differ in bits 1-2 and 2-3.  (The 32 x 32 pattern under the
+//    16 x 16 reads put rows r and r + 8 on the same banks and doubled every
+//    transpose read's cycles.)
 // Both give each lane k-slots 8 (l / 32) .. + 7 in natural order, so the
 // operand kinds mix freely.  Requires K % BK == 0 and, for K-major
 // operands, M or N % 8 == 0; rows or columns past M or N are clamped to a
 // valid one (they only feed output elements the epilogue drops).
 
-__device__ __forceinline__ int km_swz(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }
+template <int MI>
+__host__ __device__ constexpr int km_swz(int k) {
+  if constexpr (MI == 16) return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+  else return (0xCA60 >> (4 * (k & 3))) & 15;
+}
+// every pass of a 16 x 16 x 32 transpose read (rows k0 + r, k0 + 8 + r at
+// an even chunk and its neighbour) covers the 8 chunk pairs once
+constexpr bool km_swz16_ok() {
+  for (int k0 = 0; k0 < 64; k0 += 16)
+    for (int h = 0; h < 2; ++h) {
+      int seen = 0;
+      for (int g = 0; g < 2; ++g)
+        for (int r = 0; r < 4; ++r) seen |= 1 << ((km_swz<16>(k0 + 8 * g + 4 * h + r) >> 1) & 7);
+      if (seen != 0xFF) return false;
+    }
+  return true;
+}
+static_assert(km_swz16_ok(), "K-major chunk order");
 
 template <int CH>
 __device__ __forceinline__ int kc_swz(int row) {
@@ -410,7 +436,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Global source of one LDS slot of an operand stage (k0 = 0) and the
 // per-stage advance, for a tile whose first row (K-contiguous) or column
 // (K-major) is r0 of an extent of `ext`.
-template <bool KM, int BR, int BK>
+template <bool KM, int BR, int BK, int MI>
 __device__ __forceinline__ const uint16_t* dl_src(const uint16_t* base, long ld, int pos, int r0,
                                                    int ext, int swi_f) {
   if constexpr (!KM) {
@@ -423,7 +449,7 @@ __device__ __forceinline__ const uint16_t* dl_src(const uint16_t* base, long ld,
   } else {
     constexpr int RC = BR / 8;  // chunks per k-row
     const int k = pos / RC, slot = pos % RC;
-    const int c = slot ^ km_swz(k);
+    const int c = slot ^ km_swz<MI>(k);
     const int col = min(r0 + 8 * c, ext - 8);
     return base + (long)k * ld + col;
   }
@@ -447,7 +473,7 @@ __device__ __forceinline__ u32x4_t dl_frag(const char* st, int rb, int ks, int l
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = ks * 16 + 8 * (grp >> 1) + 4 * h + (i >> 2);
-      v[h] = lds_tr16(st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8));
+      v[h] = lds_tr16(st + ((k * RC + (c ^ km_swz<32>(k))) * 16 + half * 8));
     }
     return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
   }
@@ -474,7 +500,7 @@ __device__ __forceinline__ u32x4_t dl_frag16(const char* st, int rb, int ks, int
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = ks * 32 + 8 * grp + 4 * h + (i >> 2);
-      v[h] = lds_tr16(st + ((k * RC + (c ^ km_swz(k))) * 16 + half * 8));
+      v[h] = lds_tr16(st + ((k * RC + (c ^ km_swz<16>(k))) * 16 + half * 8));
     }
     return u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
   }
@@ -722,10 +748,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dl_kernel(const GemmArgs a) 
   const uint16_t* gb[B_PER];
 #pragma unroll
   for (int p = 0; p < A_PER; ++p)
-    ga[p] = dl_src<A_KM, BM, BK>(a.A, a.lda, (wave * A_PER + p) * 64 + lane, m0, M, 0);
+    ga[p] = dl_src<A_KM, BM, BK, MI>(a.A, a.lda, (wave * A_PER + p) * 64 + lane, m0, M, 0);
 #pragma unroll
   for (int p = 0; p < B_PER; ++p)
-    gb[p] = dl_src<B_KM, BN, BK>(a.B, a.ldb, (wave * B_PER + p) * 64 + lane, n0, N, SWI ? a.F : 0);
+    gb[p] = dl_src<B_KM, BN, BK, MI>(a.B, a.ldb, (wave * B_PER + p) * 64 + lane, n0, N, SWI ? a.F : 0);
   // per-stage advance along K
   const long a_step = A_KM ? (long)BK * a.lda : BK;
   const long b_step = B_KM ? (long)BK * a.ldb : BK;
