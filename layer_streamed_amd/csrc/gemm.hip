@@ -1046,26 +1046,27 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 
 // Tile choice.  With K % 32 == 0 every layout takes the direct-to-LDS
 // kernel: 256 x 256 (eight waves of 128 x 64, two per SIMD, so one wave's
-// memory stalls hide behind the other's MFMAs) when the grid fills the 256
-// CUs at least three times over (a partly filled last round still beats the
-// smaller tiles' lower rate per tile on every 7B layer shape measured), else
-// 256 x 128 (eight waves of 64 x 64) when it fills them four times over,
-// else 128 x 128 (four waves of 64 x 64).  A ragged K takes the
-// register-staged kernel, whose SwiGLU-backward epilogue keeps 128 x 128
-// (its extra live values would spill the larger tile's accumulators).
+// memory stalls hide behind the other's MFMAs) whenever the grid has at
+// least 128 tiles, half the CUs, else 128 x 128 (four waves of 64 x 64).
+// Measured over the 7B, 14B and 2x-width attention/projection weight
+// gradients at 4K-32K tokens and the projections at 4K-16K tokens, the
+// larger tile was fastest or within 3% of the fastest on every shape, even
+// with one partly filled round (up to 36% faster than the smaller tiles
+// where those fill the chip several times over); 256 x 128 (eight waves of
+// 64 x 64) was never fastest.  A ragged K takes the register-staged kernel,
+// whose SwiGLU-backward epilogue keeps 128 x 128 (its extra live values
+// would spill the larger tile's accumulators).
 inline long tiles_of(const GemmArgs& a, int bm, int bn) {
   return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
 // The tile configurations, chosen from the arguments alone (launch and the
 // kernel-name query below share this choice).
-enum TileCfg { DL_256x256, DL_256x128, DL_128x128, RS_256x256, RS_128x128 };
+enum TileCfg { DL_256x256, DL_128x128, RS_256x256, RS_128x128 };
 
 TileCfg choose_cfg(const GemmArgs& a) {
   if (a.K % 32 == 0) {
-    if (tiles_of(a, 256, 256) >= 3 * 256) return DL_256x256;
-    if (tiles_of(a, 256, 128) >= 4 * 256) return DL_256x128;
-    return DL_128x128;
+    return tiles_of(a, 256, 256) >= 128 ? DL_256x256 : DL_128x128;
   }
   if (a.epi != EPI_SWIGLU_BWD && tiles_of(a, 256, 256) >= 4 * 256) return RS_256x256;
   return RS_128x128;
@@ -1095,7 +1096,6 @@ hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
   const TileCfg c = choose_cfg(a);
   switch (c) {
     case DL_256x256: return launch_dl_stages<LAYOUT, 2, 4, 4, 2, EPI>(a, c, s);
-    case DL_256x128: return launch_dl_stages<LAYOUT, 4, 2, 2, 2, EPI>(a, c, s);
     case DL_128x128: return launch_dl_stages<LAYOUT, 2, 2, 2, 2, EPI>(a, c, s);
     case RS_256x256:
       // the SwiGLU-backward epilogue would spill this tile's accumulators
@@ -1168,7 +1168,6 @@ std::string gemm_kernel_name(const GemmArgs& a) {
   snprintf(st, sizeof st, "%s, %d", deep_stages(a, lay, c) ? "64, 2" : "32, 4", dl_mfma(lay));
   switch (c) {
     case DL_256x256: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 4, 4, 2, %d, %s>", lay, a.epi, st); break;
-    case DL_256x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 4, 2, 2, 2, %d, %s>", lay, a.epi, st); break;
     case DL_128x128: snprintf(buf, sizeof buf, "gemm_dl_kernel<%d, 2, 2, 2, 2, %d, %s>", lay, a.epi, st); break;
     case RS_256x256:
       if (a.epi != EPI_SWIGLU_BWD) {
