@@ -598,21 +598,48 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
   const int kv_end = min(q0 + BQ, T);
   const int ntiles = (kv_end + BKV - 1) / BKV;
   const int wave_qmax = q0 + 32 * w + 31;
-  // tile t -> stage buf: K and V rows clamped to T - 1 past the end (those
+  // Loop-invariant address parts, so that the tile loop (unrolled by two,
+  // the stage a constant in each half) spends no vector instructions on
+  // addresses: the wave index as a scalar; per copy slot the source row
+  // and chunk (K and V tiles share the layout); per K fragment the LDS
+  // byte offset within a stage.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int crow[PER], ccol[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int slot = (wu * PER + p) * 64 + lane;
+    const int row = slot / CH, pos = slot % CH;
+    crow[p] = row;
+    ccol[p] = row * (int)ldq + ((pos ^ tile_swz(row)) << 3);
+  }
+  // tile t -> stage BUF: K and V rows clamped to T - 1 past the end (those
   // keys are masked)
-  auto issue = [&](int t, int buf) {
+  auto issue = [&](int t, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
     const int kv0 = t * BKV;
     char* sk = dsm + buf * STAGE;
+    if (kv0 + BKV <= T) {
+      const uint16_t* kt0 = kbase + (long)kv0 * ldq;
+      const uint16_t* vt0 = vbase + (long)kv0 * ldq;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int slot = (w * PER + p) * 64 + lane;
-      const int row = slot / CH, pos = slot % CH;
-      const int c = pos ^ tile_swz(row);
-      const long gk = min(kv0 + row, T - 1);
-      lds_dma16(kbase + gk * ldq + c * 8, sk + (w * PER + p) * 1024);
-      lds_dma16(vbase + gk * ldq + c * 8, sk + TILE + (w * PER + p) * 1024);
+      for (int p = 0; p < PER; ++p) {
+        lds_dma16(kt0 + ccol[p], sk + (wu * PER + p) * 1024);
+        lds_dma16(vt0 + ccol[p], sk + TILE + (wu * PER + p) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const long gk = min(kv0 + crow[p], T - 1);
+        const int c8 = ccol[p] - crow[p] * (int)ldq;
+        lds_dma16(kbase + gk * ldq + c8, sk + (wu * PER + p) * 1024);
+        lds_dma16(vbase + gk * ldq + c8, sk + TILE + (wu * PER + p) * 1024);
+      }
     }
   };
+  // K row fragments: key row n of each 32-key block at chunk 2 ks + hh
+  int kro[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kro[ks] = n * 256 + (((2 * ks + hh) ^ tile_swz(n)) << 4);
   // V^T read addresses, as the dK/dV kernel's Q^T reads, and the offset
   // from a read at row r to its partner at row r + 8: 8 rows, and the
   // chunk's position with bit 0 flipped (the same for every dt: bit 0 of
@@ -628,8 +655,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
     const int c0 = 2 * ((lane >> 4) & 1) + ((i >> 1) & 1);
     d8 = 8 * 256 + (((c0 ^ tile_swz(r + 8)) - (c0 ^ sw)) << 4);
   }
+  uint32_t trb8[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) trb8[dt] = trb[dt] + d8;
 
-  issue(0, 0);
+  issue(0, std::integral_constant<int, 0>{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // the Q fragments are complete here; tying them to this point keeps the
   // compiler, which does not track the copies, from waiting for them (and
@@ -637,9 +667,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+  auto tile = [&](int t, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
+    if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, buf ^ 1>{});
     const int kv0 = t * BKV;
     const char* sk = dsm + buf * STAGE;
     if (kv0 <= wave_qmax) {
@@ -648,12 +678,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
       for (int kt = 0; kt < 2; ++kt) {
         zero16(sacc[kt]);
         u32x4_t Ak[2];
-        Ak[0] = lds_row16(sk, 32 * kt + n, hh);
+        Ak[0] = *reinterpret_cast<const u32x4_t*>(sk + kt * 32 * 256 + kro[0]);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const int c = ks & 1;
           if (ks + 1 < D / 16) {
-            Ak[c ^ 1] = lds_row16(sk, 32 * kt + n, 2 * (ks + 1) + hh);
+            Ak[c ^ 1] = *reinterpret_cast<const u32x4_t*>(sk + kt * 32 * 256 + kro[ks + 1]);
           }
           asm volatile("" : "+v"(Ak[c]));
           sacc[kt] = mfma32(Ak[c], qf[ks], sacc[kt]);
@@ -718,8 +748,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
       auto reads = [&](int i, int slot) {
         const int dt = i / 4, kt = (i >> 1) & 1, jj = i & 1;
         const int ro = (32 * kt + 16 * jj) * 256;
-        const char* ad = sva + trb[dt];
-        Vt[slot] = lds_tr_pair2(ad, ad + d8, ro);
+        Vt[slot] = lds_tr_pair2(sva + trb[dt], sva + trb8[dt], ro);
       };
       reads(0, 0);
 #pragma unroll
@@ -735,6 +764,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
     }
     if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  {
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      tile(t, std::integral_constant<int, 0>{});
+      tile(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
   }
 
   if (qrow < T) {
