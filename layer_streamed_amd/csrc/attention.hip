@@ -854,20 +854,47 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
   const int nit = rep * ntq;
   float lse_r = 0.f, del_r = 0.f;
   int lse_q = 0;
-  // tile `it` -> stage `buf`: Q and dO rows clamped to T - 1 past the end
+  // Loop-invariant address parts, as in the forward: the wave index as a
+  // scalar, per copy slot the source row and chunk offsets, per Q / dO
+  // fragment the LDS byte offset within a stage (the tile loop is unrolled
+  // by two, the stage a constant in each half).
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int crow[PER], qoff[PER], doff[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int slot = (wu * PER + p) * 64 + lane;
+    const int row = slot / CH, pos = slot % CH;
+    const int c8 = (pos ^ qtile_swz(row)) << 3;
+    crow[p] = row;
+    qoff[p] = row * (int)ldq + c8;
+    doff[p] = row * (int)a.ldo + c8;
+  }
+  int qro[D / 32];
+#pragma unroll
+  for (int kn = 0; kn < D / 32; ++kn) qro[kn] = li * 256 + (((4 * kn + lg) ^ qtile_swz(li)) << 4);
+  // tile `it` -> stage BUF: Q and dO rows clamped to T - 1 past the end
   // (their P is 0 through lse = +1e30, so they add exact zeros)
-  auto issue = [&](int it, int buf) {
+  auto issue = [&](int it, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
     const int hq = g * rep + it / ntq;
     const int qt0 = k0 + (it % ntq) * BQ;
     char* sq = dsm + buf * STAGE;
+    if (qt0 + BQ <= T) {
+      const uint16_t* q0p = base + (long)qt0 * ldq + hq * D;
+      const uint16_t* d0p = dbase + (long)qt0 * a.ldo + hq * D;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int slot = (w * PER + p) * 64 + lane;
-      const int row = slot / CH, pos = slot % CH;
-      const int c = pos ^ qtile_swz(row);
-      const long gq = min(qt0 + row, T - 1);
-      lds_dma16(base + gq * ldq + hq * D + c * 8, sq + (w * PER + p) * 1024);
-      lds_dma16(dbase + gq * a.ldo + hq * D + c * 8, sq + TILE + (w * PER + p) * 1024);
+      for (int p = 0; p < PER; ++p) {
+        lds_dma16(q0p + qoff[p], sq + (wu * PER + p) * 1024);
+        lds_dma16(d0p + doff[p], sq + TILE + (wu * PER + p) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const long gq = min(qt0 + crow[p], T - 1);
+        const int c8 = qoff[p] - crow[p] * (int)ldq;
+        lds_dma16(base + gq * ldq + hq * D + c8, sq + (wu * PER + p) * 1024);
+        lds_dma16(dbase + gq * a.ldo + hq * D + c8, sq + TILE + (wu * PER + p) * 1024);
+      }
     }
     // statistics of the tile's rows, raw: nothing reads them before the
     // stage's copies are waited for (a use right after the load would wait
@@ -902,7 +929,7 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
       trb[db] = row * 256 + (((2 * db + ((li >> 1) & 1)) ^ sw) << 4) + (li & 1) * 8;
   }
 
-  issue(0, 0);
+  issue(0, std::integral_constant<int, 0>{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // the key's K and V fragments are complete here (as in the forward)
 #pragma unroll
@@ -912,12 +939,12 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
   }
   stats(0);
   __syncthreads();
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
+  auto tile = [&](int it, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
     // the other stage was last read in the previous iteration (the barrier
     // at its end retired those reads): the next tile streams into it under
     // this whole iteration
-    if (it + 1 < nit) issue(it + 1, buf ^ 1);
+    if (it + 1 < nit) issue(it + 1, std::integral_constant<int, buf ^ 1>{});
     const int qt0 = k0 + (it % ntq) * BQ;
     const char* sq = dsm + buf * STAGE;
     const char* sdo = sq + TILE;
@@ -932,8 +959,8 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
       f32x4_t sacc[BQ / 16], dpacc[BQ / 16];
       constexpr int NS1 = (BQ / 16) * (D / 32);
       u32x4_t Aq[2], Ad[2];
-      Aq[0] = lds_row16<true>(sq, li, lg);
-      Ad[0] = lds_row16<true>(sdo, li, lg);
+      Aq[0] = *reinterpret_cast<const u32x4_t*>(sq + qro[0]);
+      Ad[0] = *reinterpret_cast<const u32x4_t*>(sdo + qro[0]);
 #pragma unroll
       for (int s = 0; s < NS1; ++s) {
         const int qb = s / (D / 32), ks = s % (D / 32), c = s & 1;
@@ -943,8 +970,8 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
         }
         if (s + 1 < NS1) {
           const int qn = (s + 1) / (D / 32), kn = (s + 1) % (D / 32);
-          Aq[c ^ 1] = lds_row16<true>(sq, 16 * qn + li, 4 * kn + lg);
-          Ad[c ^ 1] = lds_row16<true>(sdo, 16 * qn + li, 4 * kn + lg);
+          Aq[c ^ 1] = *reinterpret_cast<const u32x4_t*>(sq + qn * 16 * 256 + qro[kn]);
+          Ad[c ^ 1] = *reinterpret_cast<const u32x4_t*>(sdo + qn * 16 * 256 + qro[kn]);
         }
         asm volatile("" : "+v"(Aq[c]));
         asm volatile("" : "+v"(Ad[c]));
@@ -1015,6 +1042,14 @@ __global__ __launch_bounds__(512) void attn_dkdv_dl_kernel(const AttnArgs a) {
       stats(buf ^ 1);
     }
     __syncthreads();
+  };
+  {
+    int it = 0;
+    for (; it + 1 < nit; it += 2) {
+      tile(it, std::integral_constant<int, 0>{});
+      tile(it + 1, std::integral_constant<int, 1>{});
+    }
+    if (it < nit) tile(it, std::integral_constant<int, 0>{});
   }
 
   if (key < T) {
