@@ -318,26 +318,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
 }
 
 // ------------------------------------------------------------ backward prep
+// delta[b, h, t] = sum_d O[b, t, h, d] dO[b, t, h, d].  A group of D / 8
+// lanes per row (16 bytes each: one contiguous row of O and of dO), the
+// groups on consecutive t of one (b, h), so the outputs are contiguous;
+// the group's partial sums are combined by lane exchange.
 template <int D>
-__global__ void attn_delta_kernel(const AttnArgs a) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)a.B * a.T * a.Hq;
-  if (idx >= total) return;
-  const int h = (int)(idx % a.Hq);
-  const long tok = idx / a.Hq;
-  const uint16_t* orow = a.o + tok * a.ldo + h * D;
-  const uint16_t* drow = a.dout + tok * a.ldo + h * D;
+__global__ __launch_bounds__(256) void attn_delta_kernel(const AttnArgs a) {
+  constexpr int LPR = D / 8;
+  static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "lanes per row");
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long o = gid / LPR;  // flat output index (b Hq + h) T + t
+  const int part = (int)(gid % LPR);
+  const bool ok = o < (long)a.B * a.Hq * a.T;
   float s = 0.f;
-#pragma unroll 2
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(orow + c * 8);
-    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(drow + c * 8);
-    s += lo_bf(ov.x) * lo_bf(dv.x) + hi_bf(ov.x) * hi_bf(dv.x) + lo_bf(ov.y) * lo_bf(dv.y) +
-         hi_bf(ov.y) * hi_bf(dv.y) + lo_bf(ov.z) * lo_bf(dv.z) + hi_bf(ov.z) * hi_bf(dv.z) +
-         lo_bf(ov.w) * lo_bf(dv.w) + hi_bf(ov.w) * hi_bf(dv.w);
+  if (ok) {
+    const int t = (int)(o % a.T);
+    const long bh = o / a.T;
+    const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const long tok = (long)b * a.T + t;
+    const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(a.o + tok * a.ldo + h * D + part * 8);
+    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(a.dout + tok * a.ldo + h * D + part * 8);
+    s = lo_bf(ov.x) * lo_bf(dv.x) + hi_bf(ov.x) * hi_bf(dv.x) + lo_bf(ov.y) * lo_bf(dv.y) +
+        hi_bf(ov.y) * hi_bf(dv.y) + lo_bf(ov.z) * lo_bf(dv.z) + hi_bf(ov.z) * hi_bf(dv.z) +
+        lo_bf(ov.w) * lo_bf(dv.w) + hi_bf(ov.w) * hi_bf(dv.w);
   }
-  const int b = (int)(tok / a.T), t = (int)(tok % a.T);
-  const_cast<float*>(a.delta)[((long)b * a.Hq + h) * a.T + t] = s;
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (ok && part == 0) const_cast<float*>(a.delta)[o] = s;
 }
 
 // ------------------------------------------------------------- dK and dV
@@ -1405,8 +1412,8 @@ hipError_t bwd_d(const AttnArgs& a, int stages, hipStream_t s) {
     attr = true;
   }
   if (stages & ATTN_BWD_DELTA) {
-    const long rows = (long)a.B * a.T * a.Hq;
-    hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+    const long threads = (long)a.B * a.T * a.Hq * (D / 8);
+    hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                        a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

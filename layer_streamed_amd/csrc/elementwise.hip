@@ -115,13 +115,24 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
     const long off = (long)row * cols;
     const float r = rstd[row];
     float dot = 0.f;
+    // bf16 rows stay in registers (the raw 16-byte chunks) between the two
+    // passes, so dy and x are read once; fp32 rows are read again
+    constexpr bool KEEP = std::is_same<E, uint16_t>::value;
+    u32x4_t kd[KEEP ? MAXC : 1], kx[KEEP ? MAXC : 1];
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
       const int c = lane + 64 * k;
       if (c < nch) {
         float fd[8], fx[8], fg[8];
-        St<E>::load8(dy + off + c * 8, fd);
-        St<E>::load8(x + off + c * 8, fx);
+        if constexpr (KEEP) {
+          kd[k] = *reinterpret_cast<const u32x4_t*>(dy + off + c * 8);
+          kx[k] = *reinterpret_cast<const u32x4_t*>(x + off + c * 8);
+          unpack8(kd[k], fd);
+          unpack8(kx[k], fx);
+        } else {
+          St<E>::load8(dy + off + c * 8, fd);
+          St<E>::load8(x + off + c * 8, fx);
+        }
         St<E>::load8(g + c * 8, fg);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -137,8 +148,13 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
       const int c = lane + 64 * k;
       if (c < nch) {
         float fd[8], fx[8], fg[8], fr[8];
-        St<E>::load8(dy + off + c * 8, fd);
-        St<E>::load8(x + off + c * 8, fx);
+        if constexpr (KEEP) {
+          unpack8(kd[k], fd);
+          unpack8(kx[k], fx);
+        } else {
+          St<E>::load8(dy + off + c * 8, fd);
+          St<E>::load8(x + off + c * 8, fx);
+        }
         St<E>::load8(g + c * 8, fg);
         if (resid) St<E>::load8(resid + off + c * 8, fr);
         else {
