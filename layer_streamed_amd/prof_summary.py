@@ -10,12 +10,18 @@
            SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and
            SQ_INSTS_VALU_MFMA_MOPS_BF16: busy SIMD cycles over active GPU
            cycles x SIMD_NUM, and the MFMA FLOPs those instructions did
+  lds      per kernel from one --pmc run of SQ_LDS_IDX_ACTIVE,
+           SQ_LDS_BANK_CONFLICT, SQ_VALU_MFMA_BUSY_CYCLES, TA_BUSY_avr and
+           GRBM_GUI_ACTIVE: LDS busy cycles over active cycles x CU count,
+           the share of those cycles stalled on bank conflicts, the texture
+           address unit's busy fraction and the MFMA-busy fraction
 
 Usage:
   python -m layer_streamed_amd.prof_summary stats STATS_CSV OUT_MD --title T --command C
   python -m layer_streamed_amd.prof_summary traffic FETCH_CSV WRITE_CSV OUT_MD \\
       --kernel NAME --flops-per-launch F --command-fetch C1 --command-write C2
   python -m layer_streamed_amd.prof_summary mfma PMC_CSV OUT_MD --title T --command C
+  python -m layer_streamed_amd.prof_summary lds PMC_CSV OUT_MD --title T --command C [--note N]
 """
 import argparse
 import csv
@@ -172,6 +178,45 @@ def mfma(args):
     open(args.out, "w").write("\n".join(out) + "\n")
 
 
+def lds(args):
+    keys = ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES", "TA_BUSY_avr",
+            "GRBM_GUI_ACTIVE")
+    val = defaultdict(lambda: defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(args.csv)):
+        key = int(r["Dispatch_Id"])
+        names[key] = short(r["Kernel_Name"])
+        if r["Counter_Name"] in keys:
+            val[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    xcc, simds = _gpu_agent(args.csv)
+    cus = simds // 4
+    by = defaultdict(lambda: defaultdict(float))
+    for key, n in names.items():
+        g = by[n]
+        g["n"] += 1
+        for k in keys:
+            g[k] += val[key][k]
+    rows = sorted(by.items(), key=lambda kv: -kv[1]["GRBM_GUI_ACTIVE"])
+    out = [f"# {args.title}", "", "Command (from the repository root):", "", f"    {args.command}", "",
+           f"Per kernel over its dispatches, with active cycles = GRBM_GUI_ACTIVE / {xcc} (the file "
+           f"sums it over the {xcc} XCDs): LDS busy = SQ_LDS_IDX_ACTIVE / (active cycles x {cus} "
+           "CUs) (indexed LDS operations, i.e. the reads; the direct global-to-LDS copies are not "
+           "counted); bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; TA busy = "
+           "TA_BUSY_avr (the mean over the texture address units) / active cycles; MFMA busy = "
+           f"SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x {simds} SIMDs).", ""]
+    if args.note:
+        out += [args.note, ""]
+    out += ["| kernel | dispatches | LDS busy | bank-conflict share | TA busy | MFMA busy |",
+            "|---|---|---|---|---|---|"]
+    for n, g in rows[: args.top]:
+        act = g["GRBM_GUI_ACTIVE"] / xcc
+        out.append(f"| {n[:72]} | {int(g['n'])} | {100 * g['SQ_LDS_IDX_ACTIVE'] / max(act * cus, 1):.1f}% | "
+                   f"{100 * g['SQ_LDS_BANK_CONFLICT'] / max(g['SQ_LDS_IDX_ACTIVE'], 1):.1f}% | "
+                   f"{100 * g['TA_BUSY_avr'] / max(act, 1):.1f}% | "
+                   f"{100 * g['SQ_VALU_MFMA_BUSY_CYCLES'] / max(act * simds, 1):.1f}% |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -197,8 +242,15 @@ def main():
     c.add_argument("--title", required=True)
     c.add_argument("--command", required=True)
     c.add_argument("--top", type=int, default=20)
+    d = sub.add_parser("lds")
+    d.add_argument("csv")
+    d.add_argument("out")
+    d.add_argument("--title", required=True)
+    d.add_argument("--command", required=True)
+    d.add_argument("--note", default="")
+    d.add_argument("--top", type=int, default=20)
     args = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "mfma": mfma}[args.cmd](args)
+    {"stats": stats, "traffic": traffic, "mfma": mfma, "lds": lds}[args.cmd](args)
 
 
 if __name__ == "__main__":
