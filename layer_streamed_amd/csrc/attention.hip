@@ -1194,12 +1194,22 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
-          float p = exp2_hw(sacc[kt][e] * a.scale_log2 - lse2);
-          if (kk > qrow || kk >= T) p = 0.f;
-          dpacc[kt][e] = p * (dpacc[kt][e] - del);
-        }
+        for (int e = 0; e < 16; ++e) sacc[kt][e] = exp2_hw(sacc[kt][e] * a.scale_log2 - lse2);
+      // the causal mask only where some key of the tile follows one of the
+      // wave's queries or lies past the end (a wave-uniform test)
+      if (!(kv0 + BKV - 1 <= q0 + 32 * w && kv0 + BKV <= T)) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (kk > qrow || kk >= T) sacc[kt][e] = 0.f;
+          }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dpacc[kt][e] = sacc[kt][e] * (dpacc[kt][e] - del);
       // dQ over steps i = (kt, jj, dt); the two transpose reads of step
       // i+1 go out before the MFMA of step i
       constexpr int NI = 2 * 2 * (D / 32);
