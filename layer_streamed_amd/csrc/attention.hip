@@ -60,6 +60,33 @@ struct AttnArgs {
   float scale_log2;  // scale * log2(e)
 };
 
+// Work of a query-block workgroup: query block qb, batch b, query head h.
+// Blocks run longest causal rows first.  The heads of one GQA group at one
+// query block read the same K/V tiles, and the hardware hands workgroup
+// ids to the 8 XCDs (each with its own L2) in turn, so ids are mapped to
+// place every such set of heads on one XCD, where the first head's tile
+// reads fill the L2 for the others: in whole rounds of 8 sets, XCD x
+// (id % 8) takes sets x, x + 8, ... and their heads in order; the sets of a
+// last partial round keep the plain order.  A bijection of [0, nqb B Hq).
+struct QWork {
+  int qb, b, h;
+};
+__device__ __forceinline__ QWork q_work(int id, int nqb, int B, int Hq, int Hkv) {
+  const int grp = Hq / Hkv, sets = nqb * B * Hkv;
+  const int whole = (sets >> 3) * 8 * grp;
+  int set, hg;
+  if (id < whole) {
+    const int s = id >> 3;
+    set = (s / grp) * 8 + (id & 7);
+    hg = s % grp;
+  } else {
+    set = (sets >> 3) * 8 + (id - whole) / grp;
+    hg = (id - whole) % grp;
+  }
+  const int per = B * Hkv, rest = set % per;
+  return {nqb - 1 - set / per, rest / Hkv, (rest % Hkv) * grp + hg};
+}
+
 // Row r(s) of the 8-row set (group G of 16 rows, half hs) whose slot order
 // matches the MFMA accumulator: slots 0-3 -> rows 4hs..4hs+3, slots 4-7 ->
 // rows 8+4hs..8+4hs+3 of the group.
@@ -182,11 +209,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
 
   const int T = a.T;
   const int nqb = (T + BQ - 1) / BQ;
-  const int per = a.Hq * a.B;
-  const int id = blockIdx.x;
-  const int qb = nqb - 1 - id / per;  // longest causal rows first
-  const int rest = id % per;
-  const int h = rest % a.Hq, b = rest / a.Hq;
+  const QWork wk = q_work(blockIdx.x, nqb, a.B, a.Hq, a.Hkv);
+  const int qb = wk.qb, b = wk.b, h = wk.h;
   const int g = (h * a.Hkv) / a.Hq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int q0 = qb * BQ;
@@ -577,11 +601,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
 
   const int T = a.T;
   const int nqb = (T + BQ - 1) / BQ;
-  const int per = a.Hq * a.B;
-  const int id = blockIdx.x;
-  const int qb = nqb - 1 - id / per;  // longest causal rows first
-  const int rest = id % per;
-  const int h = rest % a.Hq, b = rest / a.Hq;
+  const QWork wk = q_work(blockIdx.x, nqb, a.B, a.Hq, a.Hkv);
+  const int qb = wk.qb, b = wk.b, h = wk.h;
   const int g = (h * a.Hkv) / a.Hq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int q0 = qb * BQ;
@@ -1091,10 +1112,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_dl_kernel(const AttnArgs a) {
 
   const int T = a.T;
   const int nqb = (T + BQ - 1) / BQ;
-  const int per = a.Hq * a.B;
-  const int qb = nqb - 1 - (int)blockIdx.x / per;
-  const int rest = blockIdx.x % per;
-  const int h = rest % a.Hq, b = rest / a.Hq;
+  const QWork wk = q_work(blockIdx.x, nqb, a.B, a.Hq, a.Hkv);
+  const int qb = wk.qb, b = wk.b, h = wk.h;
   const int g = (h * a.Hkv) / a.Hq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int q0 = qb * BQ;
@@ -1268,10 +1287,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const AttnArgs a) {
 
   const int T = a.T;
   const int nqb = (T + BQ - 1) / BQ;
-  const int per = a.Hq * a.B;
-  const int qb = nqb - 1 - (int)blockIdx.x / per;
-  const int rest = blockIdx.x % per;
-  const int h = rest % a.Hq, b = rest / a.Hq;
+  const QWork wk = q_work(blockIdx.x, nqb, a.B, a.Hq, a.Hkv);
+  const int qb = wk.qb, b = wk.b, h = wk.h;
   const int g = (h * a.Hkv) / a.Hq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int q0 = qb * BQ;
