@@ -23,7 +23,7 @@
 // queries and loops over key tiles up to the diagonal.  For head_dim 128
 // the forward and both backward kernels take their streamed tiles (keys and
 // values, or queries and dO for dK/dV) straight into LDS and read the
-// transposed operands with LDS transpose reads (attn_fwd_dl_kernel,
+// transposed operands with LDS transpose reads (attn_fwd_pp_kernel,
 // attn_dkdv_dl_kernel, attn_dq_dl_kernel); the register-staged forms serve
 // head_dim 64.
 #include <mutex>
@@ -282,7 +282,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
         scores(std::false_type{});
       else
         scores(std::true_type{});
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      {
+        const f32x2_t mp = lane_pair32(mx);
+        mx = fmaxf(mp.x, mp.y);
+      }
       const float mnew = fmaxf(m, mx);
       const float alpha = exp2_hw(m - mnew);
       float rs = 0.f;
@@ -294,7 +297,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
           sacc[kt][e] = p;
           rs += p;
         }
-      rs += __shfl_xor(rs, 32, 64);
+      {
+        const f32x2_t rp = lane_pair32(rs);
+        rs = rp.x + rp.y;
+      }
       l = l * alpha + rs;
       m = mnew;
 #pragma unroll
@@ -584,239 +590,6 @@ __device__ __forceinline__ u32x4_t lds_tr_pair(const char* p, const int o0, cons
 __device__ __forceinline__ u32x4_t lds_tr_pair2(const char* p, const char* p8, const int o) {
   const u32x2_t v0 = lds_tr16(p + o), v1 = lds_tr16(p8 + o);
   return u32x4_t{v0.x, v0.y, v1.x, v1.y};
-}
-
-// The forward for head_dim 128 in the dK/dV kernel's form: K and V tiles of
-// 64 keys go straight into LDS (global_load_lds, double-buffered, one
-// barrier per tile) in natural [key][d] layout; K rows for S^T are one
-// ds_read_b128 per lane, and the V^T fragments for O^T = V^T P^T two
-// ds_read_b64_tr_b16 at immediate offsets.  Products, k-slot order and
-// summation order are those of attn_fwd_kernel.
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_dl_kernel(const AttnArgs a) {
-  static_assert(D == 128, "rows of 16 chunks");
-  constexpr int BQ = 128, BKV = 64, CH = D / 8, TILE = BKV * D * 2, STAGE = 2 * TILE;
-  constexpr int PER = BKV * CH / 256;  // 16-byte load instructions per lane per operand
-  extern __shared__ __attribute__((aligned(16))) char dsm[];
-
-  const int T = a.T;
-  const int nqb = (T + BQ - 1) / BQ;
-  const QWork wk = q_work(blockIdx.x, nqb, a.B, a.Hq, a.Hkv);
-  const int qb = wk.qb, b = wk.b, h = wk.h;
-  const int g = (h * a.Hkv) / a.Hq;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
-  const int q0 = qb * BQ;
-  const int qrow = q0 + 32 * w + n;
-  const long ldq = a.ldq;
-  const uint16_t* base = a.qkv + (long)b * T * ldq;
-  const uint16_t* kbase = base + (long)(a.Hq + g) * D;
-  const uint16_t* vbase = base + (long)(a.Hq + a.Hkv + g) * D;
-
-  u32x4_t qf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    qf[ks] = qrow < T ? *reinterpret_cast<const u32x4_t*>(base + (long)qrow * ldq + h * D + ks * 16 + hh * 8)
-                      : u32x4_t{0, 0, 0, 0};
-
-  f32x16_t oacc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) zero16(oacc[dt]);
-  float m = NEG, l = 0.f;
-
-  const int kv_end = min(q0 + BQ, T);
-  const int ntiles = (kv_end + BKV - 1) / BKV;
-  const int wave_qmax = q0 + 32 * w + 31;
-  // Loop-invariant address parts, so that the tile loop (unrolled by two,
-  // the stage a constant in each half) spends no vector instructions on
-  // addresses: the wave index as a scalar; per copy slot the source row
-  // and chunk (K and V tiles share the layout); per K fragment the LDS
-  // byte offset within a stage.
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  int crow[PER], ccol[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int slot = (wu * PER + p) * 64 + lane;
-    const int row = slot / CH, pos = slot % CH;
-    crow[p] = row;
-    ccol[p] = row * (int)ldq + ((pos ^ tile_swz(row)) << 3);
-  }
-  // tile t -> stage BUF: K and V rows clamped to T - 1 past the end (those
-  // keys are masked)
-  auto issue = [&](int t, auto BUF) {
-    constexpr int buf = decltype(BUF)::value;
-    const int kv0 = t * BKV;
-    char* sk = dsm + buf * STAGE;
-    if (kv0 + BKV <= T) {
-      const uint16_t* kt0 = kbase + (long)kv0 * ldq;
-      const uint16_t* vt0 = vbase + (long)kv0 * ldq;
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        lds_dma16(kt0 + ccol[p], sk + (wu * PER + p) * 1024);
-        lds_dma16(vt0 + ccol[p], sk + TILE + (wu * PER + p) * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const long gk = min(kv0 + crow[p], T - 1);
-        const int c8 = ccol[p] - crow[p] * (int)ldq;
-        lds_dma16(kbase + gk * ldq + c8, sk + (wu * PER + p) * 1024);
-        lds_dma16(vbase + gk * ldq + c8, sk + TILE + (wu * PER + p) * 1024);
-      }
-    }
-  };
-  // K row fragments: key row n of each 32-key block at chunk 2 ks + hh
-  int kro[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) kro[ks] = n * 256 + (((2 * ks + hh) ^ tile_swz(n)) << 4);
-  // V^T read addresses, as the dK/dV kernel's Q^T reads, and the offset
-  // from a read at row r to its partner at row r + 8: 8 rows, and the
-  // chunk's position with bit 0 flipped (the same for every dt: bit 0 of
-  // the chunk is (i >> 1) & 1)
-  uint32_t trb[D / 32];
-  int d8;
-  {
-    const int i = lane & 15, r = 4 * hh + (i >> 2);
-    const int sw = tile_swz(r);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      trb[dt] = r * 256 + (((4 * dt + 2 * ((lane >> 4) & 1) + ((i >> 1) & 1)) ^ sw) << 4) + (i & 1) * 8;
-    const int c0 = 2 * ((lane >> 4) & 1) + ((i >> 1) & 1);
-    d8 = 8 * 256 + (((c0 ^ tile_swz(r + 8)) - (c0 ^ sw)) << 4);
-  }
-  uint32_t trb8[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) trb8[dt] = trb[dt] + d8;
-
-  issue(0, std::integral_constant<int, 0>{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // the Q fragments are complete here; tying them to this point keeps the
-  // compiler, which does not track the copies, from waiting for them (and
-  // so for every copy in flight) inside the loop
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
-  __syncthreads();
-  auto tile = [&](int t, auto BUF) {
-    constexpr int buf = decltype(BUF)::value;
-    if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, buf ^ 1>{});
-    const int kv0 = t * BKV;
-    const char* sk = dsm + buf * STAGE;
-    if (kv0 <= wave_qmax) {
-      f32x16_t sacc[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        zero16(sacc[kt]);
-        u32x4_t Ak[2];
-        Ak[0] = *reinterpret_cast<const u32x4_t*>(sk + kt * 32 * 256 + kro[0]);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const int c = ks & 1;
-          if (ks + 1 < D / 16) {
-            Ak[c ^ 1] = *reinterpret_cast<const u32x4_t*>(sk + kt * 32 * 256 + kro[ks + 1]);
-          }
-          asm volatile("" : "+v"(Ak[c]));
-          sacc[kt] = mfma32(Ak[c], qf[ks], sacc[kt]);
-        }
-      }
-      // scores stay unscaled: the scale (positive) commutes with the max
-      // (rounding is monotonic, so m is the max of the rounded scaled
-      // scores), and each exponent is one fused multiply-add
-      float mx = NEG;
-      auto scores = [&](auto masked) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (decltype(masked)::value && (key > qrow || key >= T)) sacc[kt][e] = NEG;
-            mx = fmaxf(mx, sacc[kt][e]);
-          }
-      };
-      // a tile whose keys all precede the wave's first query and lie in the
-      // sequence masks nothing (a wave-uniform test)
-      if (kv0 + BKV - 1 <= q0 + 32 * w && kv0 + BKV <= T)
-        scores(std::false_type{});
-      else
-        scores(std::true_type{});
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m, mx * a.scale_log2);
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2_hw(fmaf(sacc[kt][e], a.scale_log2, -mnew));
-          sacc[kt][e] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 32, 64);
-      // where no query's running max moved, the rescale factor is exactly 1
-      // (2^0): the rescale of l and O is skipped for the whole wave (after
-      // the first few tiles, the usual case)
-      if (__ballot(mnew != m)) {
-        const float alpha = exp2_hw(m - mnew);
-        l = l * alpha + rs;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-      } else {
-        l = l + rs;
-      }
-      m = mnew;
-      u32x4_t pf[2][2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) pf[kt][jj] = pack_p(sacc[kt], jj);
-      // O^T over steps i = (dt, kt, jj); the two transpose reads of step
-      // i+1 go out before the MFMA of step i
-      constexpr int NI = (D / 32) * 2 * 2;
-      const char* sva = sk + TILE;
-      u32x4_t Vt[2];
-      auto reads = [&](int i, int slot) {
-        const int dt = i / 4, kt = (i >> 1) & 1, jj = i & 1;
-        const int ro = (32 * kt + 16 * jj) * 256;
-        Vt[slot] = lds_tr_pair2(sva + trb[dt], sva + trb8[dt], ro);
-      };
-      reads(0, 0);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int dt = i / 4, kt = (i >> 1) & 1, jj = i & 1;
-        const int c = i & 1;
-        if (i + 1 < NI) {
-          reads(i + 1, c ^ 1);
-        }
-        asm volatile("" : "+v"(Vt[c]));
-        oacc[dt] = mfma32(Vt[c], pf[kt][jj], oacc[dt]);
-      }
-    }
-    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-  {
-    int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
-      tile(t, std::integral_constant<int, 0>{});
-      tile(t + 1, std::integral_constant<int, 1>{});
-    }
-    if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
-  }
-
-  if (qrow < T) {
-    const float linv = 1.f / l;
-    uint16_t* orow = a.o + ((long)b * T + qrow) * a.ldo + h * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * dt + 8 * j + 4 * hh;
-        u32x2_t v;
-        v.x = pack_bf(oacc[dt][4 * j] * linv, oacc[dt][4 * j + 1] * linv);
-        v.y = pack_bf(oacc[dt][4 * j + 2] * linv, oacc[dt][4 * j + 3] * linv);
-        *reinterpret_cast<u32x2_t*>(orow + d) = v;
-      }
-    if (hh == 0) a.lse[((long)b * a.Hq + h) * T + qrow] = (m + log2f(l)) * LN2;
-  }
 }
 
 // dK and dV for head_dim 128 on v_mfma_f32_16x16x32_bf16: a workgroup of 8
@@ -1390,6 +1163,280 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const AttnArgs a) {
   }
 }
 
+// The forward for head_dim 128 as two wave groups in ping-pong.  A
+// workgroup of 8 waves takes 256 queries, 32 per wave: group 0 (waves 0-3)
+// the first 128, group 1 (waves 4-7) the rest; waves w and w + 4 share a
+// SIMD.  Each wave alternates two phases per 64-key tile t, separated by
+// workgroup barriers: an MFMA phase (O^T += V^T P^T of tile t - 1, then
+// S^T of tile t) and a vector phase (the softmax of tile t).  Group 1 runs
+// the same code one phase behind group 0 (one extra barrier at its start,
+// one at group 0's end), so on every SIMD one wave's exponentials and
+// packing run under the other wave's matrix products, instead of the two
+// waves drifting into the same phase.  The K and V tiles go straight into
+// LDS (global_load_lds) through a ring of 4 stages, issued by group 0 three
+// tiles ahead: tile t + 1 is complete at the barrier that ends group 0's
+// vector phase of tile t, and only after that barrier is the stage of tile
+// t - 1 (whose V group 1 read in the phase just ended) refilled.  Per query
+// the operations and their order are those of attn_fwd_kernel.
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const AttnArgs a) {
+  static_assert(D == 128, "rows of 16 chunks");
+  constexpr int BQ = 256, BKV = 64, CH = D / 8, TILE = BKV * D * 2, STAGE = 2 * TILE, NS = 4;
+  constexpr int PER = BKV * CH / 256;  // 16-byte copies per group-0 lane per operand
+  static_assert(2 * PER == 8, "the vmcnt immediates below count 8 copies per tile");
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+
+  const int T = a.T;
+  const int nqb = (T + BQ - 1) / BQ;
+  const QWork wk = q_work(blockIdx.x, nqb, a.B, a.Hq, a.Hkv);
+  const int qb = wk.qb, b = wk.b, h = wk.h;
+  const int g = (h * a.Hkv) / a.Hq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int grp = wu >> 2;
+  const int q0 = qb * BQ;
+  const int wq0 = q0 + 32 * wu;  // the wave's first query (a scalar)
+  const int qrow = wq0 + n;
+  const int wave_qmax = wq0 + 31;
+  const long ldq = a.ldq;
+  const uint16_t* base = a.qkv + (long)b * T * ldq;
+  const uint16_t* kbase = base + (long)(a.Hq + g) * D;
+  const uint16_t* vbase = base + (long)(a.Hq + a.Hkv + g) * D;
+
+  u32x4_t qf[D / 16];
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) zero16(oacc[dt]);
+  float m = NEG, l = 0.f;
+
+  const int kv_end = min(q0 + BQ, T);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  // copy slots of group 0's lanes: source row and chunk (K and V tiles
+  // share the layout)
+  int crow[PER], ccol[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int slot = (wu * PER + p) * 64 + lane;
+    const int row = slot / CH, pos = slot % CH;
+    crow[p] = row;
+    ccol[p] = row * (int)ldq + ((pos ^ tile_swz(row)) << 3);
+  }
+  // tile t -> stage t % NS: K and V rows clamped to T - 1 past the end
+  // (those keys are masked)
+  auto issue = [&](int t) {
+    const int kv0 = t * BKV;
+    char* sk = dsm + (t % NS) * STAGE;
+    if (kv0 + BKV <= T) {
+      const uint16_t* kt0 = kbase + (long)kv0 * ldq;
+      const uint16_t* vt0 = vbase + (long)kv0 * ldq;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        lds_dma16(kt0 + ccol[p], sk + (wu * PER + p) * 1024);
+        lds_dma16(vt0 + ccol[p], sk + TILE + (wu * PER + p) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const long gk = min(kv0 + crow[p], T - 1);
+        const int c8 = ccol[p] - crow[p] * (int)ldq;
+        lds_dma16(kbase + gk * ldq + c8, sk + (wu * PER + p) * 1024);
+        lds_dma16(vbase + gk * ldq + c8, sk + TILE + (wu * PER + p) * 1024);
+      }
+    }
+  };
+  // K row fragments: key row n of each 32-key block at chunk 2 ks + hh
+  int kro[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kro[ks] = n * 256 + (((2 * ks + hh) ^ tile_swz(n)) << 4);
+  // V^T read addresses, as the dK/dV kernel's Q^T reads, and the offset
+  // from a read at row r to its partner at row r + 8: 8 rows, and the
+  // chunk's position with bit 0 flipped (the same for every dt: bit 0 of
+  // the chunk is (i >> 1) & 1)
+  uint32_t trb[D / 32];
+  int d8;
+  {
+    const int i = lane & 15, r = 4 * hh + (i >> 2);
+    const int sw = tile_swz(r);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      trb[dt] = r * 256 + (((4 * dt + 2 * ((lane >> 4) & 1) + ((i >> 1) & 1)) ^ sw) << 4) + (i & 1) * 8;
+    const int c0 = 2 * ((lane >> 4) & 1) + ((i >> 1) & 1);
+    d8 = 8 * 256 + (((c0 ^ tile_swz(r + 8)) - (c0 ^ sw)) << 4);
+  }
+  uint32_t trb8[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) trb8[dt] = trb[dt] + d8;
+
+  f32x16_t sacc[2];
+  u32x4_t pf[2][2];
+  // S^T of tile t for both 32-key blocks: the two products alternate, and
+  // the K row reads run two k-steps ahead of their MFMAs
+  auto s_phase = [&](int t) {
+    const char* sk = dsm + (t % NS) * STAGE;
+    zero16(sacc[0]);
+    zero16(sacc[1]);
+    u32x4_t Ak[3][2];
+    auto kread = [&](int ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        Ak[ks % 3][kt] = *reinterpret_cast<const u32x4_t*>(sk + kt * 32 * 256 + kro[ks]);
+    };
+    kread(0);
+    kread(1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      if (ks + 2 < D / 16) kread(ks + 2);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        asm volatile("" : "+v"(Ak[ks % 3][kt]));
+        sacc[kt] = mfma32(Ak[ks % 3][kt], qf[ks], sacc[kt]);
+      }
+    }
+  };
+  // online softmax of tile t's scores (left unscaled in S: the positive
+  // scale commutes with the max), the running max and sum, the rescale of
+  // O when some query's max moved, and P packed to bf16
+  auto softmax = [&](int t) {
+    const int kv0 = t * BKV;
+    float mx = NEG;
+    auto scores = [&](auto masked) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          if (decltype(masked)::value && (key > qrow || key >= T)) sacc[kt][e] = NEG;
+          mx = fmaxf(mx, sacc[kt][e]);
+        }
+    };
+    // a tile whose keys all precede the wave's first query and lie in the
+    // sequence masks nothing (a wave-uniform test)
+    if (kv0 + BKV - 1 <= wq0 && kv0 + BKV <= T)
+      scores(std::false_type{});
+    else
+      scores(std::true_type{});
+    {
+      const f32x2_t mp = lane_pair32(mx);
+      mx = fmaxf(mp.x, mp.y);
+    }
+    const float mnew = fmaxf(m, mx * a.scale_log2);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2_hw(fmaf(sacc[kt][e], a.scale_log2, -mnew));
+        sacc[kt][e] = p;
+        rs += p;
+      }
+    {
+      const f32x2_t rp = lane_pair32(rs);
+      rs = rp.x + rp.y;
+    }
+    // where no query's running max moved, the factor is exactly 1 (2^0)
+    if (__ballot(mnew != m)) {
+      const float alpha = exp2_hw(m - mnew);
+      l = l * alpha + rs;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+    } else {
+      l = l + rs;
+    }
+    m = mnew;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) pf[kt][jj] = pack_p(sacc[kt], jj);
+  };
+  // O^T += V^T P^T(t) over steps i = (kt, jj, dt), consecutive MFMAs into
+  // different accumulators; transpose reads two steps ahead
+  auto pv_phase = [&](int t) {
+    const char* sva = dsm + (t % NS) * STAGE + TILE;
+    constexpr int NI = (D / 32) * 2 * 2;
+    u32x4_t Vt[3];
+    auto reads = [&](int i) {
+      const int dt = i % (D / 32), kt = i / (D / 16), jj = (i / (D / 32)) & 1;
+      const int ro = (32 * kt + 16 * jj) * 256;
+      Vt[i % 3] = lds_tr_pair2(sva + trb[dt], sva + trb8[dt], ro);
+    };
+    reads(0);
+    reads(1);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int dt = i % (D / 32), kt = i / (D / 16), jj = (i / (D / 32)) & 1;
+      if (i + 2 < NI) reads(i + 2);
+      asm volatile("" : "+v"(Vt[i % 3]));
+      oacc[dt] = mfma32(Vt[i % 3], pf[kt][jj], oacc[dt]);
+    }
+  };
+
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = qrow < T ? *reinterpret_cast<const u32x4_t*>(base + (long)qrow * ldq + h * D + ks * 16 + hh * 8)
+                      : u32x4_t{0, 0, 0, 0};
+  if (grp == 0) {
+    issue(0);
+    if (1 < ntiles) issue(1);
+  }
+  // tiles 0 and 1 and the Q fragments complete; tying the fragments to
+  // this point keeps the compiler, which does not track the copies, from
+  // waiting for them (and so for every copy in flight) later on
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
+  if (grp == 0 && 2 < ntiles) issue(2);
+  __syncthreads();
+  // Every wave runs every iteration and its two barriers, and both groups
+  // pass 2 ntiles + 4 barriers in all; a wave whose queries all precede a
+  // tile skips that tile's work.
+  if (grp == 1) __syncthreads();
+  for (int t = 0; t <= ntiles; ++t) {
+    const bool prev = t >= 1 && (t - 1) * BKV <= wave_qmax;
+    const bool cur = t < ntiles && t * BKV <= wave_qmax;
+    // the MFMA phase at a raised wave priority, so that the wave's MFMAs
+    // and LDS reads issue ahead of its SIMD partner's softmax
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (prev) pv_phase(t - 1);
+    if (cur) s_phase(t);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    if (cur) softmax(t);
+    if (grp == 0) {
+      // tile t + 1 complete before group 0's next MFMA phase reads it (tile
+      // t + 2 may stay in flight)
+      if (t + 2 < ntiles)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (t + 1 < ntiles)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (grp == 0 && t + 3 < ntiles) issue(t + 3);
+  }
+  if (grp == 0) __syncthreads();
+
+  if (qrow < T) {
+    const float linv = 1.f / l;
+    uint16_t* orow = a.o + ((long)b * T + qrow) * a.ldo + h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * hh;
+        u32x2_t v;
+        v.x = pack_bf(oacc[dt][4 * j] * linv, oacc[dt][4 * j + 1] * linv);
+        v.y = pack_bf(oacc[dt][4 * j + 2] * linv, oacc[dt][4 * j + 3] * linv);
+        *reinterpret_cast<u32x2_t*>(orow + d) = v;
+      }
+    if (hh == 0) a.lse[((long)b * a.Hq + h) * T + qrow] = (m + log2f(l)) * LN2;
+  }
+}
+
 template <class K>
 hipError_t set_lds(K kern, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1399,22 +1446,21 @@ hipError_t set_lds(K kern, size_t bytes) {
 template <int D>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
   constexpr size_t lds = 2 * (64 * (D + 8) + D * (64 + 8)) * sizeof(uint16_t);
-  constexpr size_t lds_dl = 2 * 2 * 64 * D * sizeof(uint16_t);
+  constexpr size_t lds_pp = 4 * 2 * 64 * D * sizeof(uint16_t);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(attn_fwd_kernel<D>, lds);
     if (e != hipSuccess) return e;
     if constexpr (D == 128) {
-      e = set_lds(attn_fwd_dl_kernel<D>, lds_dl);
+      e = set_lds(attn_fwd_pp_kernel<D>, lds_pp);
       if (e != hipSuccess) return e;
     }
     attr = true;
   }
-  const int nqb = (a.T + 127) / 128;
   if constexpr (D == 128)
-    hipLaunchKernelGGL(attn_fwd_dl_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds_dl, s, a);
+    hipLaunchKernelGGL(attn_fwd_pp_kernel<D>, dim3((a.T + 255) / 256 * a.Hq * a.B), dim3(512), lds_pp, s, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqb * a.Hq * a.B), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((a.T + 127) / 128 * a.Hq * a.B), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1545,7 +1591,7 @@ hipError_t attn_bwd_static(const uint16_t* qkv, const uint16_t* o, const float* 
 }
 
 const char* attn_kernel_name(int head_dim, int which) {
-  static const char* n128[4] = {"attn_fwd_dl_kernel<128>", "attn_delta_kernel<128>",
+  static const char* n128[4] = {"attn_fwd_pp_kernel<128>", "attn_delta_kernel<128>",
                                 "attn_dkdv_dl_kernel<128>", "attn_dq_dl_kernel<128>"};
   static const char* n64[4] = {"attn_fwd_kernel<64>", "attn_delta_kernel<64>",
                                "attn_dkdv_kernel<64>", "attn_dq_kernel<64>"};

@@ -174,7 +174,7 @@ def test_no_inline_asm_load_returns_into_registers(src):
 @pytest.mark.parametrize("src,pattern", [("gemm.hip", "gemm_dl_kernel"),
                                          ("attention.hip", "attn_dkdv_dl_kernel"),
                                          ("attention.hip", "attn_dq_dl_kernel"),
-                                         ("attention.hip", "attn_fwd_dl_kernel")])
+                                         ("attention.hip", "attn_fwd_pp_kernel")])
 def test_no_compiler_vmcnt_wait_with_copies_in_flight(src, pattern):
     kernels = _kernels(_asm(src), pattern)
     with_copies = [(n, b) for n, b in kernels if any(c.startswith("global_load_lds") for _, c in _lines(b))]
