@@ -116,6 +116,16 @@ __device__ __forceinline__ u32x4_t col_of(const u32x2_t* r, int di) {
 // compare, an add, a select and a ldexp per element).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The values of lanes l and l ^ 32, in an order that depends on the half
+// (gfx950 v_permlane32_swap with v in both operands: one instruction instead
+// of an LDS permute and its lane arithmetic), for symmetric combinations:
+// max(p.x, p.y) or p.x + p.y is the same in both lanes of a pair.
+__device__ inline f32x2_t lane_pair32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return f32x2_t{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+
 __device__ __forceinline__ u32x4_t pack_p(const f32x16_t& acc, int jj) {
   u32x4_t v;
   v.x = pack_bf(acc[8 * jj + 0], acc[8 * jj + 1]);

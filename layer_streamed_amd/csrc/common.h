@@ -88,16 +88,6 @@ __device__ inline u32x2_t lds_tr16(const void* p) {
                    (__attribute__((address_space(3))) i16x4_t*)(const __attribute__((address_space(3))) char*)p));
 }
 
-// The values of lanes l and l ^ 32, in an order that depends on the half
-// (gfx950 v_permlane32_swap with v in both operands: one instruction instead
-// of an LDS permute and its lane arithmetic), for symmetric combinations:
-// max(p.x, p.y) or p.x + p.y is the same in both lanes of a pair.
-__device__ inline f32x2_t lane_pair32(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return f32x2_t{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
-}
-
 // Wave-level reductions over all 64 lanes (butterfly via ds_swizzle-free shuffles).
 __device__ inline float wave_sum(float v) {
 #pragma unroll
