@@ -261,6 +261,8 @@ ATTN_CASES = [
     (1, 200, 6, 2, 128),    # ragged T, group 3
     (2, 300, 10, 2, 64),    # ragged T, group 5
     (1, 1024, 28, 4, 128),  # 7B heads, group 7
+    (2, 700, 6, 2, 128),    # several 256-query blocks, the last ragged; 12 (block,
+                            # batch, KV group) sets: one whole XCD round and a partial one
     (3, 1, 4, 4, 128),      # single token
 ]
 
