@@ -240,8 +240,10 @@ def main():
     ap.add_argument("--clip-norm", type=float, default=0.0)
     # CPU threads for Adam and the embedding scatter (memory-bandwidth bound)
     ap.add_argument("--host-threads", type=int, default=16)
-    # the same model under the pages' schedule after the timed steps (0: skip)
-    ap.add_argument("--pages-steps", type=int, default=3)
+    # the same model under the pages' schedule after the timed steps (0: skip;
+    # the default, -1, runs 3 such steps up to 64K context and none beyond,
+    # where each step takes half a minute to several minutes)
+    ap.add_argument("--pages-steps", type=int, default=-1)
     # the listing page's Table 4 ablation on the same model
     ap.add_argument("--ablation", action="store_true")
     # after the timed steps, three plain 1 GiB device copies: the known-size
@@ -261,6 +263,8 @@ def main():
     from layer_streamed_amd import metrics, mt
 
     shape = synth.CONFIGS[args.config]
+    if args.pages_steps < 0:
+        args.pages_steps = 3 if shape.seq <= 65536 else 0
     if args.ckpt_interval:
         shape = shape.with_(ckpt_interval=args.ckpt_interval)
     if args.layers:
